@@ -1,0 +1,25 @@
+"""MI355X (gfx950) depthwise and dynamic-filter convolution.
+
+The computation runs in hand-written HIP kernels behind the C ABI of
+include/dwconv.h (libdwconv.so, built in-tree by ``build.build()``); this
+package only marshals torch tensors into that ABI.  The functions carry the
+ABI's names:
+
+    dwconv2d_fwd(x, w, bias=None, stride=1, padding=0, dilation=1)
+    dwconv2d_bwd_input(dy, w, x_shape, stride=1, padding=0, dilation=1)
+    dwconv2d_bwd_weight(x, dy, w_shape, stride=1, padding=0, dilation=1, with_bias=True)
+    dynconv_multidil_fwd(x, filters, dilations=(1, 3, 5))
+    dwconv2d_out_size(x_shape, w_shape, stride=1, padding=0, dilation=1)
+    dwconv2d_bwd_weight_workspace_bytes(x_shape, w_shape, stride, padding, dilation, dtype)
+"""
+from ._native import (  # noqa: F401
+    DwconvError,
+    dwconv2d_bwd_input,
+    dwconv2d_bwd_weight,
+    dwconv2d_bwd_weight_workspace_bytes,
+    dwconv2d_fwd,
+    dwconv2d_out_size,
+    dynconv_multidil_fwd,
+    lib,
+    status_str,
+)

@@ -1,0 +1,229 @@
+"""ctypes binding to libdwconv.so (the C ABI in include/dwconv.h).
+
+Argument marshalling only: tensor shapes become the ABI's integers, data
+pointers and torch's current HIP stream are passed through, and a nonzero
+status becomes an exception.  Every step of the computation runs in the HIP
+kernels behind the ABI; there is no CPU path.  When libdwconv.so is missing
+the first call raises, naming the build step.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdwconv.so")
+
+DW_F32, DW_F16, DW_BF16 = 0, 1, 2
+STATUS = {
+    0: "DW_OK", -1: "DW_EPTR", -2: "DW_ESHAPE", -3: "DW_EMULT", -4: "DW_EDTYPE",
+    -5: "DW_EWORKSPACE", -6: "DW_ETOOLARGE", -7: "DW_EALIAS", -8: "DW_EHIP",
+    -9: "DW_EDYN", -10: "DW_EUNSUPPORTED",
+}
+# every exported symbol the header declares
+EXPORTS = (
+    "dwconv2d_out_size", "dwconv2d_fwd", "dwconv2d_bwd_input",
+    "dwconv2d_bwd_weight_workspace_bytes", "dwconv2d_bwd_weight",
+    "dynconv_multidil_fwd", "dw_status_str",
+)
+
+_I64 = ctypes.c_int64
+_VP = ctypes.c_void_p
+_GEO = [_I64] * 13
+_lib = None
+
+
+class DwconvError(RuntimeError):
+    """A nonzero status returned by libdwconv."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s (%s)" % (where, STATUS.get(status, status), status_str(status)))
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libdwconv.so with argument types declared."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            "libdwconv.so is not built (%s); run `python -c 'import __graft_entry__ as g; g.build()'` "
+            "or `python dynamic_convolution_amd/build.py`" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    L.dwconv2d_out_size.argtypes = _GEO + [ctypes.POINTER(_I64), ctypes.POINTER(_I64)]
+    L.dwconv2d_out_size.restype = ctypes.c_int
+    L.dwconv2d_fwd.argtypes = [_VP, _VP, _VP, _VP] + _GEO + [ctypes.c_int, _VP]
+    L.dwconv2d_fwd.restype = ctypes.c_int
+    L.dwconv2d_bwd_input.argtypes = [_VP, _VP, _VP] + _GEO + [ctypes.c_int, _VP]
+    L.dwconv2d_bwd_input.restype = ctypes.c_int
+    L.dwconv2d_bwd_weight_workspace_bytes.argtypes = _GEO + [ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
+    L.dwconv2d_bwd_weight_workspace_bytes.restype = ctypes.c_int
+    L.dwconv2d_bwd_weight.argtypes = [_VP, _VP, _VP, _VP, _VP, ctypes.c_size_t] + _GEO + [ctypes.c_int, _VP]
+    L.dwconv2d_bwd_weight.restype = ctypes.c_int
+    L.dynconv_multidil_fwd.argtypes = [_VP, ctypes.POINTER(_VP), ctypes.POINTER(ctypes.c_int32),
+                                       ctypes.c_int32, _VP, _I64, _I64, _I64, _I64, _I64,
+                                       ctypes.c_int, _VP]
+    L.dynconv_multidil_fwd.restype = ctypes.c_int
+    L.dw_status_str.argtypes = [ctypes.c_int]
+    L.dw_status_str.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def status_str(status: int) -> str:
+    return lib().dw_status_str(int(status)).decode()
+
+
+def _check(rc: int, where: str):
+    if rc != 0:
+        raise DwconvError(rc, where)
+
+
+def _pair(v):
+    if isinstance(v, (tuple, list)):
+        return int(v[0]), int(v[1])
+    return int(v), int(v)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    codes = {torch.float32: DW_F32, torch.float16: DW_F16, torch.bfloat16: DW_BF16}
+    if t.dtype not in codes:
+        raise TypeError("unsupported dtype %s (float32, float16, bfloat16)" % t.dtype)
+    return codes[t.dtype]
+
+
+def _dev(t, name: str):
+    """Device pointer of a contiguous GPU tensor (raises for CPU or strided tensors)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor: there is no CPU path" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous (NCHW)" % name)
+    return t.data_ptr()
+
+
+def _stream(t):
+    import torch
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _geo(x_shape, w_shape, stride, padding, dilation):
+    n, ic, ih, iw = (int(s) for s in x_shape)
+    w_shape = tuple(int(s) for s in w_shape)
+    if len(w_shape) == 4 and w_shape[1] != 1:
+        raise ValueError("depthwise filters have shape (oc, kh, kw) or (oc, 1, kh, kw)")
+    oc, kh, kw = w_shape[0], w_shape[-2], w_shape[-1]
+    sh, sw = _pair(stride)
+    ph, pw = _pair(padding)
+    dh, dw = _pair(dilation)
+    return (n, ic, ih, iw, oc, kh, kw, sh, sw, ph, pw, dh, dw)
+
+
+def dwconv2d_out_size(x_shape, w_shape, stride=1, padding=0, dilation=1):
+    """(oh, ow) for the geometry, computed by the library."""
+    oh, ow = _I64(), _I64()
+    _check(lib().dwconv2d_out_size(*_geo(x_shape, w_shape, stride, padding, dilation),
+                                   ctypes.byref(oh), ctypes.byref(ow)), "dwconv2d_out_size")
+    return oh.value, ow.value
+
+
+def dwconv2d_bwd_weight_workspace_bytes(x_shape, w_shape, stride=1, padding=0, dilation=1, dtype=None):
+    import torch
+    code = _dtype_code(torch.empty(0, dtype=dtype or torch.float32))
+    nbytes = ctypes.c_size_t()
+    _check(lib().dwconv2d_bwd_weight_workspace_bytes(*_geo(x_shape, w_shape, stride, padding, dilation),
+                                                     code, ctypes.byref(nbytes)),
+           "dwconv2d_bwd_weight_workspace_bytes")
+    return nbytes.value
+
+
+def dwconv2d_fwd(x, w, bias=None, stride=1, padding=0, dilation=1, out=None):
+    """y = depthwise conv2d of x (n, ic, ih, iw) with w (oc, [1,] kh, kw) plus bias (oc)."""
+    import torch
+    geo = _geo(x.shape, w.shape, stride, padding, dilation)
+    oh, ow = dwconv2d_out_size(x.shape, w.shape, stride, padding, dilation)
+    if out is None:
+        out = torch.empty((geo[0], geo[4], oh, ow), dtype=x.dtype, device=x.device)
+    code = _dtype_code(x)
+    for t, nm in ((w, "w"), (bias, "bias"), (out, "out")):
+        if t is not None and t.dtype != x.dtype:
+            raise TypeError("%s dtype %s != x dtype %s" % (nm, t.dtype, x.dtype))
+    if tuple(out.shape) != (geo[0], geo[4], oh, ow):
+        raise ValueError("out has shape %s" % (tuple(out.shape),))
+    _check(lib().dwconv2d_fwd(_dev(x, "x"), _dev(w, "w"), _dev(bias, "bias"), _dev(out, "out"), *geo,
+                              code, _stream(x)), "dwconv2d_fwd")
+    return out
+
+
+def dwconv2d_bwd_input(dy, w, x_shape, stride=1, padding=0, dilation=1, out=None):
+    """dx (shape x_shape) of the forward above, given dy (n, oc, oh, ow)."""
+    import torch
+    geo = _geo(x_shape, w.shape, stride, padding, dilation)
+    if out is None:
+        out = torch.empty(tuple(int(s) for s in x_shape), dtype=dy.dtype, device=dy.device)
+    code = _dtype_code(dy)
+    for t, nm in ((w, "w"), (out, "out")):
+        if t.dtype != dy.dtype:
+            raise TypeError("%s dtype %s != dy dtype %s" % (nm, t.dtype, dy.dtype))
+    oh, ow = dwconv2d_out_size(x_shape, w.shape, stride, padding, dilation)
+    if tuple(dy.shape) != (geo[0], geo[4], oh, ow) or tuple(out.shape) != tuple(geo[:4]):
+        raise ValueError("dy %s / out %s do not match the geometry" % (tuple(dy.shape), tuple(out.shape)))
+    _check(lib().dwconv2d_bwd_input(_dev(dy, "dy"), _dev(w, "w"), _dev(out, "out"), *geo, code,
+                                    _stream(dy)), "dwconv2d_bwd_input")
+    return out
+
+
+def dwconv2d_bwd_weight(x, dy, w_shape, stride=1, padding=0, dilation=1, with_bias=True,
+                        out=None, out_bias=None, workspace=None):
+    """(dw of shape w_shape, db of shape (oc,) or None) of the forward above.
+
+    The workspace (uint8 GPU tensor) is allocated here when not given.
+    """
+    import torch
+    geo = _geo(x.shape, w_shape, stride, padding, dilation)
+    code = _dtype_code(x)
+    if dy.dtype != x.dtype:
+        raise TypeError("dy dtype %s != x dtype %s" % (dy.dtype, x.dtype))
+    oh, ow = dwconv2d_out_size(x.shape, w_shape, stride, padding, dilation)
+    if tuple(dy.shape) != (geo[0], geo[4], oh, ow):
+        raise ValueError("dy %s does not match the geometry" % (tuple(dy.shape),))
+    if out is None:
+        out = torch.empty(tuple(int(s) for s in w_shape), dtype=x.dtype, device=x.device)
+    if with_bias and out_bias is None:
+        out_bias = torch.empty((geo[4],), dtype=x.dtype, device=x.device)
+    nbytes = dwconv2d_bwd_weight_workspace_bytes(x.shape, w_shape, stride, padding, dilation, x.dtype)
+    if workspace is None:
+        workspace = torch.empty((nbytes,), dtype=torch.uint8, device=x.device)
+    _check(lib().dwconv2d_bwd_weight(_dev(x, "x"), _dev(dy, "dy"), _dev(out, "out"),
+                                     _dev(out_bias, "out_bias") if with_bias else None,
+                                     _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                                     *geo, code, _stream(x)), "dwconv2d_bwd_weight")
+    return out, (out_bias if with_bias else None)
+
+
+def dynconv_multidil_fwd(x, filters, dilations=(1, 3, 5), out=None):
+    """Branch-concatenated dynamic-filter output (n, nb*c, h, w); filters[b] is (n, c, k*k, h, w)."""
+    import torch
+    n, c, h, w = (int(s) for s in x.shape)
+    nb = len(filters)
+    if nb != len(dilations):
+        raise ValueError("one filter tensor per dilation")
+    kk = int(filters[0].shape[2])
+    k = int(round(kk ** 0.5))
+    if k * k != kk:
+        raise ValueError("filters must hold k*k taps")
+    for f in filters:
+        if tuple(f.shape) != (n, c, kk, h, w) or f.dtype != x.dtype:
+            raise ValueError("filter %s %s does not match x" % (tuple(f.shape), f.dtype))
+    if out is None:
+        out = torch.empty((n, nb * c, h, w), dtype=x.dtype, device=x.device)
+    if tuple(out.shape) != (n, nb * c, h, w) or out.dtype != x.dtype:
+        raise ValueError("out %s %s does not match" % (tuple(out.shape), out.dtype))
+    fptrs = (_VP * nb)(*[_dev(f, "filter") for f in filters])
+    dil = (ctypes.c_int32 * nb)(*[int(d) for d in dilations])
+    _check(lib().dynconv_multidil_fwd(_dev(x, "x"), fptrs, dil, nb, _dev(out, "out"), n, c, h, w, k,
+                                      _dtype_code(x), _stream(x)), "dynconv_multidil_fwd")
+    return out

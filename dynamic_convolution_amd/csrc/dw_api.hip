@@ -1,0 +1,229 @@
+// dw_api.hip -- the extern "C" entry points declared in include/dwconv.h.
+//
+// Every argument is validated on the host before any HIP call, so invalid
+// calls launch nothing and touch no output.  Valid calls plan the launch and
+// enqueue the kernels of dw_fwd / dw_bwd_input / dw_bwd_weight / dw_dynconv on
+// the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "dw_internal.hpp"
+#include "dwconv.h"
+
+namespace {
+
+constexpr int64_t kMaxElems = (int64_t{1} << 31) - 1;  // every tensor below 2^31 elements
+constexpr int64_t kMaxExtent = int64_t{1} << 30;        // keeps in-kernel index math in int32
+
+size_t elem_size(int dtype) { return dtype == DW_F32 ? 4 : 2; }
+
+// a * b * c * d < 2^31 without overflow (all factors >= 1).
+bool product_ok(int64_t a, int64_t b, int64_t c = 1, int64_t d = 1) {
+    int64_t p = a;
+    for (int64_t f : {b, c, d}) {
+        if (p > kMaxElems / f) return false;
+        p *= f;
+    }
+    return p <= kMaxElems;
+}
+
+bool aligned(const void *p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+
+// [a, a+na) and [b, b+nb) share a byte.
+bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+// Validates the 13 geometry integers and fills g.  Order of checks: size
+// ranges, multiplier, output size, element counts.
+int check_geometry(int64_t n, int64_t ic, int64_t ih, int64_t iw, int64_t oc, int64_t kh, int64_t kw,
+                   int64_t sh, int64_t sw, int64_t ph, int64_t pw, int64_t dh, int64_t dw_, dw::Geo *g) {
+    if (n < 1 || ic < 1 || ih < 1 || iw < 1 || oc < 1 || kh < 1 || kw < 1 || sh < 1 || sw < 1 || dh < 1 ||
+        dw_ < 1 || ph < 0 || pw < 0)
+        return DW_ESHAPE;
+    for (int64_t v : {n, ic, ih, iw, oc, kh, kw, sh, sw, ph, pw, dh, dw_})
+        if (v > kMaxExtent) return DW_ETOOLARGE;
+    if (oc % ic != 0) return DW_EMULT;
+    if (ih + 2 * ph > kMaxExtent || iw + 2 * pw > kMaxExtent || (kh - 1) * dh > kMaxExtent ||
+        (kw - 1) * dw_ > kMaxExtent)
+        return DW_ETOOLARGE;
+    const int64_t nh = ih + 2 * ph - dh * (kh - 1) - 1;
+    const int64_t nw = iw + 2 * pw - dw_ * (kw - 1) - 1;
+    if (nh < 0 || nw < 0) return DW_ESHAPE;
+    const int64_t oh = nh / sh + 1, ow = nw / sw + 1;
+    if (!product_ok(n, ic, ih, iw) || !product_ok(n, oc, oh, ow) || !product_ok(oc, kh, kw))
+        return DW_ETOOLARGE;
+    if (g) {
+        g->n = static_cast<int>(n);
+        g->ic = static_cast<int>(ic);
+        g->ih = static_cast<int>(ih);
+        g->iw = static_cast<int>(iw);
+        g->oc = static_cast<int>(oc);
+        g->kh = static_cast<int>(kh);
+        g->kw = static_cast<int>(kw);
+        g->sh = static_cast<int>(sh);
+        g->sw = static_cast<int>(sw);
+        g->ph = static_cast<int>(ph);
+        g->pw = static_cast<int>(pw);
+        g->dh = static_cast<int>(dh);
+        g->dw = static_cast<int>(dw_);
+        g->oh = static_cast<int>(oh);
+        g->ow = static_cast<int>(ow);
+        g->mult = static_cast<int>(oc / ic);
+    }
+    return DW_OK;
+}
+
+size_t x_bytes(const dw::Geo &g, size_t e) { return static_cast<size_t>(g.n) * g.ic * g.ih * g.iw * e; }
+size_t y_bytes(const dw::Geo &g, size_t e) { return static_cast<size_t>(g.n) * g.oc * g.oh * g.ow * e; }
+size_t w_bytes(const dw::Geo &g, size_t e) { return static_cast<size_t>(g.oc) * g.kh * g.kw * e; }
+size_t b_bytes(const dw::Geo &g, size_t e) { return static_cast<size_t>(g.oc) * e; }
+
+int map_launch(int rc) {
+    if (rc == dw::kOk) return DW_OK;
+    if (rc == dw::kErrUnsupported) return DW_EUNSUPPORTED;
+    return DW_EHIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dwconv2d_out_size(int64_t n, int64_t ic, int64_t ih, int64_t iw, int64_t oc, int64_t kh, int64_t kw,
+                      int64_t stride_h, int64_t stride_w, int64_t pad_h, int64_t pad_w, int64_t dil_h,
+                      int64_t dil_w, int64_t *oh, int64_t *ow) {
+    dw::Geo g;
+    const int rc = check_geometry(n, ic, ih, iw, oc, kh, kw, stride_h, stride_w, pad_h, pad_w, dil_h, dil_w, &g);
+    if (rc != DW_OK) return rc;
+    if (oh) *oh = g.oh;
+    if (ow) *ow = g.ow;
+    return DW_OK;
+}
+
+int dwconv2d_fwd(const void *x, const void *w, const void *bias, void *y, int64_t n, int64_t ic, int64_t ih,
+                 int64_t iw, int64_t oc, int64_t kh, int64_t kw, int64_t stride_h, int64_t stride_w,
+                 int64_t pad_h, int64_t pad_w, int64_t dil_h, int64_t dil_w, int dtype, void *stream) {
+    if (dtype != DW_F32 && dtype != DW_F16 && dtype != DW_BF16) return DW_EDTYPE;
+    dw::Geo g;
+    const int rc = check_geometry(n, ic, ih, iw, oc, kh, kw, stride_h, stride_w, pad_h, pad_w, dil_h, dil_w, &g);
+    if (rc != DW_OK) return rc;
+    const size_t e = elem_size(dtype);
+    if (!x || !w || !y) return DW_EPTR;
+    if (!aligned(x, e) || !aligned(w, e) || !aligned(y, e) || (bias && !aligned(bias, e))) return DW_EPTR;
+    const size_t yb = y_bytes(g, e);
+    if (overlap(y, yb, x, x_bytes(g, e)) || overlap(y, yb, w, w_bytes(g, e)) ||
+        (bias && overlap(y, yb, bias, b_bytes(g, e))))
+        return DW_EALIAS;
+    if (!dw::fwd_supported(g, dtype)) return DW_EUNSUPPORTED;
+    return map_launch(dw::launch_fwd(g, x, w, bias, y, dtype, static_cast<hipStream_t>(stream)));
+}
+
+int dwconv2d_bwd_input(const void *dy, const void *w, void *dx, int64_t n, int64_t ic, int64_t ih, int64_t iw,
+                       int64_t oc, int64_t kh, int64_t kw, int64_t stride_h, int64_t stride_w, int64_t pad_h,
+                       int64_t pad_w, int64_t dil_h, int64_t dil_w, int dtype, void *stream) {
+    if (dtype != DW_F32 && dtype != DW_F16 && dtype != DW_BF16) return DW_EDTYPE;
+    dw::Geo g;
+    const int rc = check_geometry(n, ic, ih, iw, oc, kh, kw, stride_h, stride_w, pad_h, pad_w, dil_h, dil_w, &g);
+    if (rc != DW_OK) return rc;
+    const size_t e = elem_size(dtype);
+    if (!dy || !w || !dx) return DW_EPTR;
+    if (!aligned(dy, e) || !aligned(w, e) || !aligned(dx, e)) return DW_EPTR;
+    const size_t xb = x_bytes(g, e);
+    if (overlap(dx, xb, dy, y_bytes(g, e)) || overlap(dx, xb, w, w_bytes(g, e))) return DW_EALIAS;
+    if (!dw::bwd_input_supported(g, dtype)) return DW_EUNSUPPORTED;
+    return map_launch(dw::launch_bwd_input(g, dy, w, dx, dtype, static_cast<hipStream_t>(stream)));
+}
+
+int dwconv2d_bwd_weight_workspace_bytes(int64_t n, int64_t ic, int64_t ih, int64_t iw, int64_t oc, int64_t kh,
+                                        int64_t kw, int64_t stride_h, int64_t stride_w, int64_t pad_h,
+                                        int64_t pad_w, int64_t dil_h, int64_t dil_w, int dtype, size_t *bytes) {
+    if (dtype != DW_F32 && dtype != DW_F16 && dtype != DW_BF16) return DW_EDTYPE;
+    dw::Geo g;
+    const int rc = check_geometry(n, ic, ih, iw, oc, kh, kw, stride_h, stride_w, pad_h, pad_w, dil_h, dil_w, &g);
+    if (rc != DW_OK) return rc;
+    const int64_t ws = dw::bwd_weight_workspace(g, dtype);
+    if (ws < 0) return DW_EUNSUPPORTED;
+    if (bytes) *bytes = static_cast<size_t>(ws);
+    return DW_OK;
+}
+
+int dwconv2d_bwd_weight(const void *x, const void *dy, void *dwt, void *db, void *workspace,
+                        size_t workspace_bytes, int64_t n, int64_t ic, int64_t ih, int64_t iw, int64_t oc,
+                        int64_t kh, int64_t kw, int64_t stride_h, int64_t stride_w, int64_t pad_h, int64_t pad_w,
+                        int64_t dil_h, int64_t dil_w, int dtype, void *stream) {
+    if (dtype != DW_F32 && dtype != DW_F16 && dtype != DW_BF16) return DW_EDTYPE;
+    dw::Geo g;
+    const int rc = check_geometry(n, ic, ih, iw, oc, kh, kw, stride_h, stride_w, pad_h, pad_w, dil_h, dil_w, &g);
+    if (rc != DW_OK) return rc;
+    const size_t e = elem_size(dtype);
+    if (!x || !dy || !dwt) return DW_EPTR;
+    if (!aligned(x, e) || !aligned(dy, e) || !aligned(dwt, e) || (db && !aligned(db, e))) return DW_EPTR;
+    const int64_t need = dw::bwd_weight_workspace(g, dtype);
+    if (need < 0) return DW_EUNSUPPORTED;
+    if (!workspace || workspace_bytes < static_cast<size_t>(need) || !aligned(workspace, 16))
+        return DW_EWORKSPACE;
+    const size_t xb = x_bytes(g, e), yb = y_bytes(g, e), wb = w_bytes(g, e), bb = b_bytes(g, e);
+    const size_t wsb = static_cast<size_t>(need);
+    if (overlap(dwt, wb, x, xb) || overlap(dwt, wb, dy, yb) || overlap(dwt, wb, workspace, wsb) ||
+        overlap(workspace, wsb, x, xb) || overlap(workspace, wsb, dy, yb) ||
+        (db && (overlap(db, bb, x, xb) || overlap(db, bb, dy, yb) || overlap(db, bb, dwt, wb) ||
+                overlap(db, bb, workspace, wsb))))
+        return DW_EALIAS;
+    return map_launch(dw::launch_bwd_weight(g, x, dy, dwt, db, workspace, dtype, static_cast<hipStream_t>(stream)));
+}
+
+int dynconv_multidil_fwd(const void *x, const void *const *filters, const int32_t *dilations, int32_t nb,
+                         void *y, int64_t n, int64_t c, int64_t h, int64_t w, int64_t k, int dtype, void *stream) {
+    if (dtype != DW_F32 && dtype != DW_F16 && dtype != DW_BF16) return DW_EDTYPE;
+    if (n < 1 || c < 1 || h < 1 || w < 1 || k < 1) return DW_ESHAPE;
+    for (int64_t v : {n, c, h, w, k})
+        if (v > kMaxExtent) return DW_ETOOLARGE;
+    if (nb < 1 || nb > 4 || (k % 2) == 0) return DW_EDYN;
+    if (!x || !y || !filters || !dilations) return DW_EPTR;
+    int maxdil = 1;
+    for (int b = 0; b < nb; ++b) {
+        if (dilations[b] < 1) return DW_EDYN;
+        if (!filters[b]) return DW_EPTR;
+        if ((k - 1) / 2 * static_cast<int64_t>(dilations[b]) > kMaxExtent) return DW_ETOOLARGE;
+        if (dilations[b] > maxdil) maxdil = dilations[b];
+    }
+    if (!product_ok(n, c, h, w) || !product_ok(n * nb, c, h, w) || !product_ok(n * c, k * k, h, w))
+        return DW_ETOOLARGE;
+    const size_t e = elem_size(dtype);
+    if (!aligned(x, e) || !aligned(y, e)) return DW_EPTR;
+    for (int b = 0; b < nb; ++b)
+        if (!aligned(filters[b], e)) return DW_EPTR;
+    const size_t xb = static_cast<size_t>(n * c * h * w) * e;
+    const size_t yb = xb * static_cast<size_t>(nb);
+    const size_t fb = static_cast<size_t>(n * c * k * k * h * w) * e;
+    if (overlap(y, yb, x, xb)) return DW_EALIAS;
+    for (int b = 0; b < nb; ++b)
+        if (overlap(y, yb, filters[b], fb)) return DW_EALIAS;
+    if (!dw::dynconv_supported(static_cast<int>(h), static_cast<int>(w), static_cast<int>(k), maxdil, dtype))
+        return DW_EUNSUPPORTED;
+    return map_launch(dw::launch_dynconv(x, filters, dilations, nb, y, static_cast<int>(n), static_cast<int>(c),
+                                         static_cast<int>(h), static_cast<int>(w), static_cast<int>(k), dtype,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+const char *dw_status_str(int status) {
+    switch (status) {
+        case DW_OK: return "ok";
+        case DW_EPTR: return "a required pointer is NULL or not aligned to its element size";
+        case DW_ESHAPE: return "invalid size, stride, dilation or padding, or empty output";
+        case DW_EMULT: return "output channels are not a multiple of input channels";
+        case DW_EDTYPE: return "unknown dtype";
+        case DW_EWORKSPACE: return "workspace missing, too small or not 16-byte aligned";
+        case DW_ETOOLARGE: return "a tensor has 2^31 elements or more, or an extent exceeds 2^30";
+        case DW_EALIAS: return "an output overlaps an input or another output";
+        case DW_EHIP: return "HIP kernel launch failed";
+        case DW_EDYN: return "dynamic filter: k must be odd, 1 <= nb <= 4, dilations >= 1";
+        case DW_EUNSUPPORTED: return "geometry needs more LDS per workgroup than this library stages";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

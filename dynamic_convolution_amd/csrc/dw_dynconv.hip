@@ -1,0 +1,224 @@
+// dw_dynconv.hip -- fused per-pixel dynamic filter at several dilations on gfx950.
+//
+//   y[n, b*C + c, h, w] = sum_{i,j<k} F_b[n, c, i*k + j, h, w] * x[n, c, h + (i-r)d_b, w + (j-r)d_b]
+// with r = (k-1)/2 and zero outside the image (lartpang/DynamicConvolutionOperator:
+// HDFNet's Dynamic Dilated Pyramid computation; its fused design gathers all
+// dilation branches in one program and stores each branch's pixels straight
+// into the concatenated output, so no unfolded copy and no concatenation).
+//
+// The op moves ~k*k*nb filter values per output pixel and does one FMA per
+// value, so it is bound by HBM bandwidth.  A workgroup owns a band of rows of
+// one (n, c) plane: the x rows of the band plus the largest dilation's halo
+// are staged in LDS once and serve every branch; each thread produces RW
+// adjacent pixels of one row for all branches, streaming every filter tap as
+// one 16-byte coalesced load and writing each branch's strip at its channel
+// offset b*C + c of the concatenated output.
+#include "dw_common.hpp"
+#include "dw_internal.hpp"
+
+namespace dw {
+namespace {
+
+constexpr int kMaxBranches = 4;
+constexpr int kLdsPref = 32 * 1024;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+template <typename T> struct DynArgs {
+    const T *x;
+    const T *f[kMaxBranches];
+    T *y;
+    int dil[kMaxBranches];
+    int nb;
+    int n, c, h, w, k;
+    int BH, nbands, NS;
+    FastDiv fNS;
+    int halo;   // r * max dilation
+    int vin;    // x 16-byte aligned
+    int vf;     // filters and y rows allow 16-byte strips
+};
+
+template <typename T, int RW>
+__device__ __forceinline__ void load_strip(const T *p, float *v, int valid, bool vec) {
+    if (vec && valid >= RW) {
+        static_assert(sizeof(T) * RW == 16, "strip is one 16-byte vector");
+        union {
+            u32x4 u;
+            T t[RW];
+        } b;
+        b.u = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+#pragma unroll
+        for (int q = 0; q < RW; ++q) v[q] = to_f32(b.t[q]);
+    } else {
+#pragma unroll
+        for (int q = 0; q < RW; ++q) v[q] = q < valid ? to_f32(p[q]) : 0.f;
+    }
+}
+
+template <typename T, int RW>
+__device__ __forceinline__ void store_strip(T *p, const float *acc, int valid, bool vec) {
+    if (vec && valid >= RW) {
+        union {
+            uint4 u;
+            T t[RW];
+        } b;
+#pragma unroll
+        for (int q = 0; q < RW; ++q) b.t[q] = from_f32<T>(acc[q]);
+        *reinterpret_cast<uint4 *>(p) = b.u;
+    } else {
+#pragma unroll
+        for (int q = 0; q < RW; ++q)
+            if (q < valid) p[q] = from_f32<T>(acc[q]);
+    }
+}
+
+template <typename T, int K_, int RW>
+__global__ __launch_bounds__(kThreads) void dynconv_kernel(DynArgs<T> a) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int K = K_ ? K_ : a.k;
+    const int KK = K * K;
+    const int rr = (K - 1) / 2;
+    const int tid = threadIdx.x;
+    const int plane = blockIdx.x / a.nbands;
+    const int band = blockIdx.x - plane * a.nbands;
+    const int nn = plane / a.c;
+    const int ch = plane - nn * a.c;
+    const int h0 = band * a.BH;
+    const int h1 = min(h0 + a.BH, a.h);
+    const int rlo = max(h0 - a.halo, 0);
+    const int rhi = min(h1 + a.halo, a.h);
+    const int64_t hw = static_cast<int64_t>(a.h) * a.w;
+
+    T *xs = reinterpret_cast<T *>(smem);
+    const int64_t gbeg = static_cast<int64_t>(plane) * hw + static_cast<int64_t>(rlo) * a.w;
+    const int64_t gend = gbeg + static_cast<int64_t>(rhi - rlo) * a.w;
+    const int off = a.vin ? lds_copy_range(xs, a.x, gbeg, gend, tid, kThreads)
+                          : lds_copy_range_scalar(xs, a.x, gbeg, gend, tid, kThreads);
+    __syncthreads();
+
+    const int items = a.BH * a.NS;
+    for (int u = tid; u < items; u += kThreads) {
+        const int r = static_cast<int>(fdiv(static_cast<uint32_t>(u), a.fNS));
+        const int s = u - r * a.NS;
+        const int hh = h0 + r;
+        if (hh >= h1) continue;
+        const int w0 = s * RW;
+        const int valid = a.w - w0;
+        const int64_t pix = static_cast<int64_t>(hh) * a.w + w0;
+        for (int b = 0; b < a.nb; ++b) {
+            const int d = a.dil[b];
+            const T *fb = a.f[b] + static_cast<int64_t>(plane) * KK * hw + pix;
+            float acc[RW];
+#pragma unroll
+            for (int q = 0; q < RW; ++q) acc[q] = 0.f;
+#pragma unroll
+            for (int i = 0; i < K; ++i) {
+                const int sy = hh + (i - rr) * d;
+                if (sy < 0 || sy >= a.h) continue;  // whole filter row multiplies zero padding
+                const T *rp = xs + off + (sy - rlo) * a.w;
+#pragma unroll
+                for (int j = 0; j < K; ++j) {
+                    float fv[RW];
+                    load_strip<T, RW>(fb + static_cast<int64_t>(i * K + j) * hw, fv, valid, a.vf != 0);
+                    const int sx0 = w0 + (j - rr) * d;
+#pragma unroll
+                    for (int q = 0; q < RW; ++q) {
+                        const int sx = sx0 + q;
+                        const float xv = (sx >= 0 && sx < a.w) ? to_f32(rp[sx]) : 0.f;
+                        acc[q] = fmaf(fv[q], xv, acc[q]);
+                    }
+                }
+            }
+            T *yp = a.y + (static_cast<int64_t>(nn * a.nb + b) * a.c + ch) * hw + pix;
+            store_strip<T, RW>(yp, acc, valid, a.vf != 0);
+        }
+    }
+}
+
+struct DynPlan {
+    int BH, nbands, lds_bytes;
+};
+
+template <typename T>
+bool plan_dyn(int n, int c, int h, int w, int k, int maxdil, DynPlan &p) {
+    constexpr int RW = Vec<T>::N;
+    const int NS = (w + RW - 1) / RW;
+    const int halo = (k - 1) / 2 * maxdil;
+    auto bytes = [&](int bh) -> int64_t {
+        const int64_t rows = std::min<int64_t>(static_cast<int64_t>(bh) + 2 * halo, h);
+        const int64_t cnt = rows * w;
+        if (cnt > (1 << 24)) return INT64_MAX;
+        return static_cast<int64_t>(lds_slots<T>(static_cast<int>(cnt))) * sizeof(T);
+    };
+    const int lim = bytes(1) <= kLdsPref ? kLdsPref : kLdsCap;
+    if (bytes(1) > lim) return false;
+    // about two strips per thread, within the LDS budget
+    int bh = std::max(1, (2 * kThreads + NS - 1) / NS);
+    bh = std::min(bh, h);
+    while (bh > 1 && bytes(bh) > lim) --bh;
+    // keep >= 1024 workgroups when the problem is big enough
+    const int64_t planes = static_cast<int64_t>(n) * c;
+    while (bh > 1 && planes * ((h + bh - 1) / bh) < 1024) bh = (bh + 1) / 2;
+    p.nbands = (h + bh - 1) / bh;
+    p.BH = (h + p.nbands - 1) / p.nbands;
+    p.lds_bytes = static_cast<int>(bytes(p.BH));
+    return true;
+}
+
+template <typename T>
+int run_dyn(const void *x, const void *const *filters, const int32_t *dil, int nb, void *y, int n, int c,
+            int h, int w, int k, hipStream_t s) {
+    constexpr int RW = Vec<T>::N;
+    int maxdil = 1;
+    for (int b = 0; b < nb; ++b) maxdil = std::max(maxdil, static_cast<int>(dil[b]));
+    DynPlan p;
+    if (!plan_dyn<T>(n, c, h, w, k, maxdil, p)) return kErrUnsupported;
+    DynArgs<T> a;
+    a.x = static_cast<const T *>(x);
+    bool fal = true;
+    for (int b = 0; b < kMaxBranches; ++b) {
+        a.f[b] = b < nb ? static_cast<const T *>(filters[b]) : nullptr;
+        a.dil[b] = b < nb ? dil[b] : 1;
+        if (b < nb) fal = fal && (reinterpret_cast<uintptr_t>(filters[b]) % 16 == 0);
+    }
+    a.y = static_cast<T *>(y);
+    a.nb = nb;
+    a.n = n;
+    a.c = c;
+    a.h = h;
+    a.w = w;
+    a.k = k;
+    a.BH = p.BH;
+    a.nbands = p.nbands;
+    a.NS = (w + RW - 1) / RW;
+    a.fNS = make_fastdiv(a.NS, static_cast<uint64_t>(p.BH) * a.NS);
+    a.halo = (k - 1) / 2 * maxdil;
+    a.vin = reinterpret_cast<uintptr_t>(x) % 16 == 0;
+    a.vf = fal && (w % RW == 0) && (reinterpret_cast<uintptr_t>(y) % 16 == 0);
+    const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(n) * c * p.nbands));
+    if (k == 3)
+        hipLaunchKernelGGL((dynconv_kernel<T, 3, RW>), grid, dim3(kThreads), p.lds_bytes, s, a);
+    else if (k == 5)
+        hipLaunchKernelGGL((dynconv_kernel<T, 5, RW>), grid, dim3(kThreads), p.lds_bytes, s, a);
+    else
+        hipLaunchKernelGGL((dynconv_kernel<T, 0, RW>), grid, dim3(kThreads), p.lds_bytes, s, a);
+    return hipGetLastError() == hipSuccess ? kOk : kErrHip;
+}
+
+}  // namespace
+
+bool dynconv_supported(int h, int w, int k, int maxdil, int dtype) {
+    DynPlan p;
+    return dtype == 0 ? plan_dyn<float>(1, 1, h, w, k, maxdil, p) : plan_dyn<__half>(1, 1, h, w, k, maxdil, p);
+}
+
+int launch_dynconv(const void *x, const void *const *filters, const int32_t *dil, int nb, void *y, int n, int c,
+                   int h, int w, int k, int dtype, hipStream_t s) {
+    switch (dtype) {
+        case 0: return run_dyn<float>(x, filters, dil, nb, y, n, c, h, w, k, s);
+        case 1: return run_dyn<__half>(x, filters, dil, nb, y, n, c, h, w, k, s);
+        default: return run_dyn<bf16_t>(x, filters, dil, nb, y, n, c, h, w, k, s);
+    }
+}
+
+}  // namespace dw

@@ -1,0 +1,45 @@
+// dw_internal.hpp -- host-side plan structures and kernel launchers shared by
+// the C ABI (dw_api.hip) and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dw {
+
+// Validated geometry in 32-bit ints (every tensor is below 2^31 elements).
+struct Geo {
+    int n, ic, ih, iw;
+    int oc, kh, kw;
+    int sh, sw, ph, pw, dh, dw;
+    int oh, ow, mult;
+};
+
+// Largest LDS a single workgroup may use for staged tiles (bytes).
+constexpr int kLdsCap = 64 * 1024;
+// Threads per workgroup of every kernel in this library.
+constexpr int kThreads = 256;
+
+// Status codes returned by launchers (subset of the public enum).
+constexpr int kOk = 0;
+constexpr int kErrHip = -8;
+constexpr int kErrUnsupported = -10;
+
+int launch_fwd(const Geo &g, const void *x, const void *w, const void *b, void *y, int dtype,
+               hipStream_t s);
+int launch_bwd_input(const Geo &g, const void *dy, const void *w, void *dx, int dtype,
+                     hipStream_t s);
+// Bytes of workspace launch_bwd_weight needs; -1 when the geometry is unsupported.
+int64_t bwd_weight_workspace(const Geo &g, int dtype);
+int launch_bwd_weight(const Geo &g, const void *x, const void *dy, void *dwt, void *db,
+                      void *ws, int dtype, hipStream_t s);
+int launch_dynconv(const void *x, const void *const *filters, const int32_t *dil, int nb, void *y,
+                   int n, int c, int h, int w, int k, int dtype, hipStream_t s);
+
+// Shape checks the launchers need beyond argument validation (LDS fit).
+bool fwd_supported(const Geo &g, int dtype);
+bool bwd_input_supported(const Geo &g, int dtype);
+bool dynconv_supported(int h, int w, int k, int maxdil, int dtype);
+
+}  // namespace dw

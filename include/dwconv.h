@@ -1,0 +1,176 @@
+/*
+ * dwconv.h -- C ABI of the MI355X (gfx950) depthwise and dynamic-filter
+ * convolution library (libdwconv.so).
+ *
+ * Problem statement (MegEngine large-kernel depthwise article, section on
+ * going from convolution to matrix multiplication): input x is (n, ic, ih, iw),
+ * the kernel is (oc, ic, kh, kw) and the output is (n, oc, oh, ow).  In the
+ * depthwise case each output channel sees one input channel only, so the
+ * kernel is stored as (oc, kh, kw) -- bitwise the same as (oc, 1, kh, kw).
+ *
+ * Features (PyTorch PR #3057 "Spatial Depthwise Convolution on the GPU": its
+ * TODO list and commit history): zero padding, stride, dilation, a depth
+ * multiplier M = oc / ic (output channel o reads input channel o / M, so the
+ * M filters of one input channel are adjacent), an optional bias and its
+ * gradient, and half precision with a wider accumulation type.
+ *
+ * Shared conventions
+ * ------------------
+ *  - Every tensor pointer is a DEVICE pointer to a dense, row-major (NCHW)
+ *    array owned by the caller.  The library never allocates or frees device
+ *    memory, never synchronises and keeps no pointer after a call returns.
+ *    Host arrays (filters[], dilations[]) are read during the call only.
+ *  - dtype selects the element type of every tensor of the call: DW_F32,
+ *    DW_F16 (IEEE binary16) or DW_BF16 (bfloat16).  Arithmetic is fp32;
+ *    16-bit results are rounded to nearest-even on the final store.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *    and the call returns without waiting for it.
+ *  - Every pointer must be aligned to its element size.
+ *  - Geometry: cross-correlation (no kernel flip); symmetric zero padding per
+ *    axis; oh = floor((ih + 2*pad_h - dil_h*(kh-1) - 1) / stride_h) + 1 and
+ *    likewise ow.  All sizes, strides and dilations >= 1, pads >= 0,
+ *    oc % ic == 0, oh >= 1, ow >= 1, and every tensor below 2^31 elements.
+ *  - Errors: a negative status code, never an abort, exception or print.
+ *    All argument checks run before any HIP call; when one fails nothing is
+ *    launched and no output is touched.  DW_EHIP reports a failed launch.
+ *  - Thread safety: the library is stateless; concurrent calls on different
+ *    streams with disjoint outputs are safe.
+ */
+#ifndef DWCONV_H
+#define DWCONV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum dw_dtype { DW_F32 = 0, DW_F16 = 1, DW_BF16 = 2 };
+
+enum dw_status {
+    DW_OK = 0,
+    DW_EPTR = -1,       /* a required pointer is NULL or not aligned to its element size */
+    DW_ESHAPE = -2,     /* a size/stride/dilation < 1, a pad < 0, or an empty output */
+    DW_EMULT = -3,      /* oc is not a multiple of ic */
+    DW_EDTYPE = -4,     /* dtype is not one of enum dw_dtype */
+    DW_EWORKSPACE = -5, /* workspace NULL or smaller than dwconv2d_bwd_weight_workspace_bytes */
+    DW_ETOOLARGE = -6,  /* some tensor has 2^31 elements or more, or an extent
+                           (size, stride, pad, dilated kernel span) exceeds 2^30 */
+    DW_EALIAS = -7,     /* an output overlaps an input or another output */
+    DW_EHIP = -8,       /* a HIP launch failed (hipGetLastError after the launch) */
+    DW_EDYN = -9,       /* dynamic filter: k even, nb outside [1, 4], or a dilation < 1 */
+    DW_EUNSUPPORTED = -10 /* valid geometry whose minimal row band (rows one output row
+                             reads, times the row width) exceeds the 64 KiB of LDS a
+                             workgroup stages; nothing is launched */
+};
+
+/*
+ * Output spatial size for the geometry above.  Writes *oh and *ow (either may
+ * be NULL) and returns DW_OK, or returns DW_ESHAPE / DW_EMULT / DW_ETOOLARGE
+ * exactly as the compute calls would for the same geometry.  Host only.
+ */
+int dwconv2d_out_size(int64_t n, int64_t ic, int64_t ih, int64_t iw,
+                      int64_t oc, int64_t kh, int64_t kw,
+                      int64_t stride_h, int64_t stride_w, int64_t pad_h, int64_t pad_w,
+                      int64_t dil_h, int64_t dil_w, int64_t *oh, int64_t *ow);
+
+/*
+ * Forward (PR #3057: depthwise forward kernel with padding, stride,
+ * dilation, multiplier and bias):
+ *   y[n, o, p, q] = bias[o]
+ *       + sum_{i<kh, j<kw} w[o, i, j] * x[n, o/M, p*stride_h - pad_h + i*dil_h,
+ *                                             q*stride_w - pad_w + j*dil_w]
+ * with out-of-image taps contributing zero.
+ *   x    (n, ic, ih, iw)   input
+ *   w    (oc, kh, kw)      filters
+ *   bias (oc) or NULL      added after accumulation, before rounding
+ *   y    (n, oc, oh, ow)   output, fully overwritten
+ */
+int dwconv2d_fwd(const void *x, const void *w, const void *bias, void *y,
+                 int64_t n, int64_t ic, int64_t ih, int64_t iw,
+                 int64_t oc, int64_t kh, int64_t kw,
+                 int64_t stride_h, int64_t stride_w, int64_t pad_h, int64_t pad_w,
+                 int64_t dil_h, int64_t dil_w, int dtype, void *stream);
+
+/*
+ * Gradient with respect to the input (PR #3057: the grad-input kernel of the
+ * depthwise convolution): the adjoint of the forward in x,
+ *   dx[n, g, h, c] = sum over (m < M, i, j, p, q) with
+ *                    p*stride_h - pad_h + i*dil_h == h and
+ *                    q*stride_w - pad_w + j*dil_w == c
+ *                    of w[g*M + m, i, j] * dy[n, g*M + m, p, q].
+ *   dy (n, oc, oh, ow)   incoming gradient
+ *   w  (oc, kh, kw)      filters
+ *   dx (n, ic, ih, iw)   output, fully overwritten (elements no tap reaches are 0)
+ */
+int dwconv2d_bwd_input(const void *dy, const void *w, void *dx,
+                       int64_t n, int64_t ic, int64_t ih, int64_t iw,
+                       int64_t oc, int64_t kh, int64_t kw,
+                       int64_t stride_h, int64_t stride_w, int64_t pad_h, int64_t pad_w,
+                       int64_t dil_h, int64_t dil_w, int dtype, void *stream);
+
+/*
+ * Bytes of device workspace dwconv2d_bwd_weight needs for this geometry and
+ * dtype (always > 0).  Writes *bytes; returns a status as dwconv2d_out_size.
+ */
+int dwconv2d_bwd_weight_workspace_bytes(int64_t n, int64_t ic, int64_t ih, int64_t iw,
+                                        int64_t oc, int64_t kh, int64_t kw,
+                                        int64_t stride_h, int64_t stride_w,
+                                        int64_t pad_h, int64_t pad_w,
+                                        int64_t dil_h, int64_t dil_w, int dtype,
+                                        size_t *bytes);
+
+/*
+ * Gradient with respect to the filters and the bias (PR #3057: the
+ * grad-weight kernel, later extended to padding, stride and dilation, and
+ * the bias gradient added with it):
+ *   dw[o, i, j] = sum_{n, p, q} dy[n, o, p, q] * x[n, o/M, p*stride_h - pad_h + i*dil_h,
+ *                                                       q*stride_w - pad_w + j*dil_w]
+ *   db[o]       = sum_{n, p, q} dy[n, o, p, q]
+ *   x         (n, ic, ih, iw)   forward input
+ *   dy        (n, oc, oh, ow)   incoming gradient
+ *   dw        (oc, kh, kw)      output, overwritten
+ *   db        (oc) or NULL      output, overwritten when non-NULL
+ *   workspace device scratch of at least dwconv2d_bwd_weight_workspace_bytes
+ *             bytes, aligned to 16 bytes, owned by the caller; its contents on
+ *             entry do not matter and are garbage on exit.
+ * Two kernels run in stream order (per-block partial sums, then a fixed-order
+ * reduction); no atomics, so results are bitwise reproducible run to run.
+ */
+int dwconv2d_bwd_weight(const void *x, const void *dy, void *dw, void *db,
+                        void *workspace, size_t workspace_bytes,
+                        int64_t n, int64_t ic, int64_t ih, int64_t iw,
+                        int64_t oc, int64_t kh, int64_t kw,
+                        int64_t stride_h, int64_t stride_w, int64_t pad_h, int64_t pad_w,
+                        int64_t dil_h, int64_t dil_w, int dtype, void *stream);
+
+/*
+ * Fused per-pixel dynamic filter at several dilations, written straight into
+ * the channel-concatenated result (lartpang/DynamicConvolutionOperator: the
+ * Dynamic Dilated Pyramid computation of HDFNet, sections on the
+ * optimisation analysis and the solution -- no unfold buffer, no concat copy):
+ *   y[n, b*c + ch, h, w] = sum_{i, j < k} F_b[n, ch, i*k + j, h, w]
+ *                          * x[n, ch, h + (i - r)*d_b, w + (j - r)*d_b]
+ * for every branch b < nb, with r = (k - 1)/2, d_b = dilations[b] and zero
+ * outside the image (i.e. zero padding r*d_b, stride 1, output h x w).
+ *   x          (n, c, h, w)            input
+ *   filters    host array of nb device pointers; filters[b] is (n, c, k*k, h, w)
+ *   dilations  host array of nb dilations (e.g. {1, 3, 5})
+ *   nb         number of branches, 1..4
+ *   y          (n, nb*c, h, w)         output, fully overwritten, branch-major
+ *   k          odd window size
+ */
+int dynconv_multidil_fwd(const void *x, const void *const *filters,
+                         const int32_t *dilations, int32_t nb, void *y,
+                         int64_t n, int64_t c, int64_t h, int64_t w, int64_t k,
+                         int dtype, void *stream);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char *dw_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DWCONV_H */

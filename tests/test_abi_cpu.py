@@ -1,0 +1,159 @@
+"""C ABI checks that need no GPU: exports, geometry helper, argument validation.
+
+Validation runs before any HIP call, so invalid calls return their status here
+without a device.  These tests pass fake addresses only to calls that must be
+rejected; they are skipped where a GPU is visible so that a validation bug
+could never turn into a launch on a fake pointer.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from dynamic_convolution_amd import _native as N
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "dwconv.h")
+
+no_gpu = pytest.mark.skipif(torch.cuda.is_available(), reason="fake-pointer validation only without a GPU")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_abi():
+    assert declared_functions() == sorted(N.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = N.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for code in N.STATUS:
+        s = N.status_str(code)
+        assert s and s != "unknown status"
+    assert N.status_str(12345) == "unknown status"
+
+
+def _geo(n=2, ic=3, ih=9, iw=7, oc=3, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1):
+    return [n, ic, ih, iw, oc, kh, kw, sh, sw, ph, pw, dh, dw]
+
+
+def out_size(*geo):
+    oh, ow = ctypes.c_int64(-1), ctypes.c_int64(-1)
+    rc = N.lib().dwconv2d_out_size(*geo, ctypes.byref(oh), ctypes.byref(ow))
+    return rc, oh.value, ow.value
+
+
+def test_out_size_matches_oracle(orc):
+    import itertools
+    for ih, kh, sh, ph, dh in itertools.product((1, 2, 5, 8, 13), (1, 2, 3, 5, 7), (1, 2, 3), (0, 1, 3), (1, 2, 3)):
+        rc, oh, ow = out_size(*_geo(ih=ih, iw=ih + 1, kh=kh, kw=kh, sh=sh, sw=sh, ph=ph, pw=ph, dh=dh, dw=dh))
+        want_h = orc.out_size(ih, kh, sh, ph, dh)
+        want_w = orc.out_size(ih + 1, kh, sh, ph, dh)
+        if want_h < 1 or want_w < 1:
+            assert rc == -2
+        else:
+            assert (rc, oh, ow) == (0, want_h, want_w)
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(n=0), -2), (dict(ic=0), -2), (dict(kh=0), -2), (dict(sh=0), -2), (dict(dw=0), -2),
+    (dict(ph=-1), -2), (dict(ih=2, kh=5, ph=0), -2), (dict(oc=4), -3), (dict(oc=7, ic=3), -3),
+    (dict(n=1 << 31), -6), (dict(n=4096, ic=4096, ih=512, iw=512, oc=4096), -6),
+])
+def test_out_size_rejects(bad, code):
+    assert out_size(*_geo(**bad))[0] == code
+
+
+FAKE = 1 << 40  # never dereferenced: every call below must fail validation
+
+
+@no_gpu
+def test_fwd_validation():
+    L = N.lib()
+    g = _geo()
+    assert L.dwconv2d_fwd(FAKE, FAKE, None, FAKE + 4096, *g, 7, None) == -4      # dtype
+    assert L.dwconv2d_fwd(None, FAKE, None, FAKE + 4096, *g, 0, None) == -1      # null x
+    assert L.dwconv2d_fwd(FAKE, FAKE, None, None, *g, 0, None) == -1             # null y
+    assert L.dwconv2d_fwd(FAKE + 2, FAKE, None, FAKE + 4096, *g, 0, None) == -1  # misaligned f32
+    assert L.dwconv2d_fwd(FAKE, FAKE + 1, None, FAKE + 4096, *g, 1, None) == -1  # misaligned f16
+    assert L.dwconv2d_fwd(FAKE, FAKE, None, FAKE, *g, 0, None) == -7             # y aliases x
+    assert L.dwconv2d_fwd(FAKE, FAKE + 4096, FAKE + 8, FAKE + 4096 - 8, *g, 0, None) == -7  # y overlaps w
+    assert L.dwconv2d_fwd(FAKE, FAKE, None, FAKE + 4096, *_geo(oc=4), 0, None) == -3
+    assert L.dwconv2d_fwd(FAKE, FAKE, None, FAKE + 4096, *_geo(ih=1, ph=0), 0, None) == -2
+
+
+@no_gpu
+def test_bwd_input_validation():
+    L = N.lib()
+    g = _geo()
+    assert L.dwconv2d_bwd_input(FAKE, FAKE, FAKE + 4096, *g, 3, None) == -4
+    assert L.dwconv2d_bwd_input(None, FAKE, FAKE + 4096, *g, 0, None) == -1
+    assert L.dwconv2d_bwd_input(FAKE, FAKE, FAKE, *g, 0, None) == -7
+    assert L.dwconv2d_bwd_input(FAKE, FAKE, FAKE + 4096, *_geo(n=-1), 0, None) == -2
+
+
+@no_gpu
+def test_bwd_weight_validation():
+    L = N.lib()
+    g = _geo()
+    need = ctypes.c_size_t()
+    assert L.dwconv2d_bwd_weight_workspace_bytes(*g, 0, ctypes.byref(need)) == 0
+    assert need.value > 0
+    ws = FAKE + (1 << 20)
+    assert L.dwconv2d_bwd_weight(FAKE, FAKE, FAKE + 8192, None, ws, need.value, *g, 9, None) == -4
+    assert L.dwconv2d_bwd_weight(FAKE, FAKE, None, None, ws, need.value, *g, 0, None) == -1
+    assert L.dwconv2d_bwd_weight(FAKE, FAKE, FAKE + 8192, None, None, need.value, *g, 0, None) == -5
+    assert L.dwconv2d_bwd_weight(FAKE, FAKE, FAKE + 8192, None, ws, need.value - 1, *g, 0, None) == -5
+    assert L.dwconv2d_bwd_weight(FAKE, FAKE, FAKE + 8192, None, ws + 4, need.value, *g, 0, None) == -5
+    assert L.dwconv2d_bwd_weight(FAKE, FAKE, FAKE, None, ws, need.value, *g, 0, None) == -7
+    assert L.dwconv2d_bwd_weight(FAKE, FAKE, FAKE + 8192, FAKE + 8192, ws, need.value, *g, 0, None) == -7
+    assert L.dwconv2d_bwd_weight(FAKE, FAKE, FAKE + 8192, None, FAKE, need.value, *g, 0, None) == -7
+
+
+def test_workspace_bytes_positive_and_valid(orc):
+    L = N.lib()
+    for g in (_geo(), _geo(n=128, ic=32, ih=112, iw=112, oc=32), _geo(n=64, ic=384, ih=64, iw=64, oc=384,
+                                                                      kh=31, kw=31, ph=15, pw=15),
+              _geo(n=128, ic=256, ih=56, iw=56, oc=512, kh=5, kw=5, sh=2, sw=2, ph=4, pw=4, dh=2, dw=2)):
+        for dt in (0, 1, 2):
+            need = ctypes.c_size_t()
+            assert L.dwconv2d_bwd_weight_workspace_bytes(*g, dt, ctypes.byref(need)) == 0
+            assert 0 < need.value < (64 << 20)
+    assert L.dwconv2d_bwd_weight_workspace_bytes(*_geo(oc=4), 0, ctypes.byref(need)) == -3
+
+
+@no_gpu
+def test_dynconv_validation():
+    L = N.lib()
+    f3 = (ctypes.c_void_p * 3)(FAKE + (1 << 24), FAKE + (2 << 24), FAKE + (3 << 24))
+    d3 = (ctypes.c_int32 * 3)(1, 3, 5)
+    y = FAKE + (8 << 24)
+    dyn = L.dynconv_multidil_fwd
+    assert dyn(FAKE, f3, d3, 3, y, 1, 4, 8, 8, 3, 5, None) == -4
+    assert dyn(FAKE, f3, d3, 3, y, 1, 4, 8, 8, 4, 0, None) == -9        # even k
+    assert dyn(FAKE, f3, d3, 0, y, 1, 4, 8, 8, 3, 0, None) == -9        # nb = 0
+    assert dyn(FAKE, f3, d3, 5, y, 1, 4, 8, 8, 3, 0, None) == -9        # nb > 4
+    bad = (ctypes.c_int32 * 3)(1, 0, 5)
+    assert dyn(FAKE, f3, bad, 3, y, 1, 4, 8, 8, 3, 0, None) == -9       # dilation 0
+    assert dyn(None, f3, d3, 3, y, 1, 4, 8, 8, 3, 0, None) == -1
+    fnull = (ctypes.c_void_p * 3)(FAKE + (1 << 24), None, FAKE + (3 << 24))
+    assert dyn(FAKE, fnull, d3, 3, y, 1, 4, 8, 8, 3, 0, None) == -1
+    assert dyn(FAKE, f3, d3, 3, FAKE, 1, 4, 8, 8, 3, 0, None) == -7     # y aliases x
+    assert dyn(FAKE, f3, d3, 3, FAKE + (1 << 24), 1, 4, 8, 8, 3, 0, None) == -7  # y aliases a filter
+    assert dyn(FAKE, f3, d3, 3, y, 0, 4, 8, 8, 3, 0, None) == -2
+
+
+def test_binding_refuses_cpu_tensors():
+    x = torch.zeros(1, 2, 5, 5)
+    w = torch.zeros(2, 3, 3)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        N.dwconv2d_fwd(x, w, None, 1, 1, 1)
