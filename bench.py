@@ -1,0 +1,367 @@
+"""Benchmark of the depthwise / dynamic-filter hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload mobilenet|multdil|largek|dynamic]
+
+Prints ONE JSON line.  A step is one pass of every entry point the workload
+uses over every case of the workload, with inputs resident in HBM:
+
+  mobilenet (default)  3x3 depthwise layers of MobileNet, N in {1, 64, 128},
+                       (C, H) in {(32,112), (64,112), (128,56), (256,28), (512,14),
+                       (1024,7)}, stride 1 and 2, pad 1, fp32; forward, grad-input,
+                       grad-weight (36 cases x 3 passes)
+  multdil              multiplier 2, dilation 2, stride 2, 5x5, pad 4,
+                       N=128, C=256->512, 56x56, bf16; the three passes
+  largek               N=64, C=384, H in {32,48,64}, k in {7,13,31}, pad k//2,
+                       fp32 and fp16; the three passes
+  dynamic              per-pixel 3x3 filters at dilations 1/3/5, N in {1,2}, C=64,
+                       H in {128,256}, fp32/fp16/bf16; output concatenated
+
+Passes run in pass-major order (every case's forward, then every grad-input,
+then every grad-weight) so a tensor is re-read only after gigabytes of other
+traffic, i.e. from HBM, not from the 256 MB last-level cache.
+
+value      whole-step algorithmic throughput: compulsory bytes (each input element
+           the result depends on once, each output once) per second for the
+           bandwidth-bound workloads; valid-tap flops (2 per in-bounds multiply-add)
+           per second for largek
+roofline   the dominant kernel (most time in the step): its algorithmic bytes or
+           flops over its average launch duration, measured with HIP events on the
+           launch stream during the timed steps, against the MI355X peak
+cpu_baseline  the fp64 CPU oracle on a bounded sample of the same workload
+           (a batch slice of the same host tensors), on this host's cores
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X published fp32 vector peak
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="mobilenet", choices=["mobilenet", "multdil", "largek", "dynamic"])
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline leg")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------- accounting
+def read_extent(in_n, out_n, k, s, p, d):
+    """How many input rows (or cols) some tap of some output position reads."""
+    seen = set()
+    for o in range(out_n):
+        for i in range(k):
+            h = o * s - p + i * d
+            if 0 <= h < in_n:
+                seen.add(h)
+    return len(seen)
+
+
+def valid_taps(in_n, out_n, k, s, p, d):
+    """Sum over output positions of the in-bounds tap count along one axis."""
+    tot = 0
+    for o in range(out_n):
+        for i in range(k):
+            h = o * s - p + i * d
+            tot += 0 <= h < in_n
+    return tot
+
+
+class Call:
+    """One entry-point call of the step with its algorithmic bytes and flops."""
+
+    def __init__(self, tag, fn, nbytes, flops):
+        self.tag, self.fn, self.nbytes, self.flops = tag, fn, nbytes, flops
+
+
+def static_calls(dc, case, dev, seed, passes=("fwd", "bwd_in", "bwd_w")):
+    import torch
+    from dynamic_convolution_amd import synth
+    n, c, h, M, k, s, p, d, dtype, dists, tagbase, with_bias = case
+    e = torch.empty(0, dtype=dtype).element_size()
+    x = synth.draw((n, c, h, h), dists["x"], seed, "x", dtype, device=dev)
+    w = synth.draw((c * M, k, k), dists["w"], seed, "w", dtype, device=dev)
+    b = synth.draw((c * M,), ("U", -0.1, 0.1), seed, "b", dtype, device=dev) if with_bias else None
+    oh, ow = dc.dwconv2d_out_size(x.shape, w.shape, s, p, d)
+    dy = synth.draw((n, c * M, oh, ow), dists["dy"], seed, "dy", dtype, device=dev)
+    y = torch.empty((n, c * M, oh, ow), dtype=dtype, device=dev)
+    dx = torch.empty_like(x)
+    gw = torch.empty_like(w)
+    gb = torch.empty((c * M,), dtype=dtype, device=dev) if with_bias else None
+    ws = torch.empty((dc.dwconv2d_bwd_weight_workspace_bytes(x.shape, w.shape, s, p, d, dtype),),
+                     dtype=torch.uint8, device=dev)
+    rows = read_extent(h, oh, k, s, p, d)
+    sx = n * c * rows * rows * e
+    X, W, B, Y = x.numel() * e, w.numel() * e, (c * M * e if with_bias else 0), y.numel() * e
+    macs = n * c * M * valid_taps(h, oh, k, s, p, d) ** 2
+    calls = []
+    if "fwd" in passes:
+        calls.append(Call(tagbase + "fwd", lambda: dc.dwconv2d_fwd(x, w, b, s, p, d, out=y), sx + W + B + Y, 2 * macs))
+    if "bwd_in" in passes:
+        calls.append(Call(tagbase + "bwd_input", lambda: dc.dwconv2d_bwd_input(dy, w, x.shape, s, p, d, out=dx),
+                          Y + W + X, 2 * macs))
+    if "bwd_w" in passes:
+        calls.append(Call(tagbase + "bwd_weight",
+                          lambda: dc.dwconv2d_bwd_weight(x, dy, w.shape, s, p, d, with_bias=with_bias, out=gw,
+                                                         out_bias=gb, workspace=ws),
+                          sx + Y + W + B, 2 * macs))
+    tensors = dict(x=x, w=w, b=b, dy=dy, y=y, dx=dx, gw=gw, gb=gb)
+    return calls, tensors
+
+
+def build_workload(name, dc, dev):
+    """(cases, pass-major list of calls, description, dtype string, value kind)."""
+    import torch
+    from dynamic_convolution_amd import synth
+    cases = []
+    if name == "mobilenet":
+        m = synth.MOBILENET
+        dists = dict(x=m["x"], w=m["w"], dy=m["dy"])
+        seed = 100
+        for n in m["batches"]:
+            for c, h in m["layers"]:
+                for s in m["strides"]:
+                    cases.append(((n, c, h, 1, 3, s, 1, 1, torch.float32, dists, "3x3_s%d_" % s, False), seed))
+                    seed += 1
+        desc = "mobilenet_dw3x3_sweep"
+        dt, kind = "f32", "bytes"
+        cfg = {"batches": list(m["batches"]), "layers_c_h": [list(l) for l in m["layers"]],
+               "strides": list(m["strides"]), "kernel": 3, "pad": 1, "passes": ["fwd", "bwd_input", "bwd_weight"]}
+    elif name == "multdil":
+        m = synth.MULT_DIL
+        dists = dict(x=m["x"], w=m["w"], dy=m["dy"])
+        cases.append(((m["n"], m["c"], m["h"], m["mult"], m["k"], m["stride"], m["pad"], m["dil"],
+                       torch.bfloat16, dists, "5x5_m2_d2_s2_", False), 200))
+        desc, dt, kind = "mult2_dil2_stride2_5x5", "bf16", "bytes"
+        cfg = {"n": m["n"], "c_in": m["c"], "c_out": m["c"] * m["mult"], "hw": m["h"], "kernel": 5, "stride": 2,
+               "pad": 4, "dilation": 2, "passes": ["fwd", "bwd_input", "bwd_weight"]}
+    elif name == "largek":
+        L = synth.LARGE_K
+        seed = 300
+        for h in L["hs"]:
+            for k in L["ks"]:
+                for dts in L["dtypes"]:
+                    dists = dict(x=L["x"], w=("N", 0.0, 1.0 / k ** 2), dy=L["dy"])
+                    cases.append(((L["n"], L["c"], h, 1, k, 1, k // 2, 1, synth.DTYPES[dts], dists,
+                                   "k%d_%s_" % (k, dts), False), seed))
+                    seed += 1
+        desc, dt, kind = "large_kernel_dw_n64_c384", "f32+f16", "flops"
+        cfg = {"n": L["n"], "c": L["c"], "hw": list(L["hs"]), "kernels": list(L["ks"]), "dtypes": list(L["dtypes"]),
+               "passes": ["fwd", "bwd_input", "bwd_weight"]}
+    else:
+        return build_dynamic(dc, dev)
+    per_case = [static_calls(dc, cs, dev, seed) for cs, seed in cases]
+    calls = [cl for pi in range(3) for (cls, _t) in per_case for cl in cls[pi:pi + 1]]
+    return dict(cases=cases, per_case=per_case, calls=calls, desc=desc, dtype=dt, kind=kind, cfg=cfg)
+
+
+def build_dynamic(dc, dev):
+    import torch
+    from dynamic_convolution_amd import synth
+    D = synth.DYNAMIC
+    calls, per_case, cases = [], [], []
+    seed = 400
+    for n in D["batches"]:
+        for h in D["hs"]:
+            for dts in D["dtypes"]:
+                dtype = synth.DTYPES[dts]
+                e = torch.empty(0, dtype=dtype).element_size()
+                x = synth.draw((n, D["c"], h, h), D["x"], seed, "x", dtype, device=dev)
+                fs = [synth.draw((n, D["c"], 9, h, h), D["f"], seed, "f%d" % i, dtype, device=dev)
+                      for i in range(3)]
+                y = torch.empty((n, 3 * D["c"], h, h), dtype=dtype, device=dev)
+                taps = sum(valid_taps(h, h, 3, 1, dd, dd) ** 2 for dd in D["dilations"])
+                nbytes = x.numel() * e + n * D["c"] * taps * e + y.numel() * e
+                cl = Call("dyn_%s_" % dts, (lambda x=x, fs=fs, y=y: dc.dynconv_multidil_fwd(x, fs, D["dilations"], out=y)),
+                          nbytes, 2 * n * D["c"] * taps)
+                calls.append(cl)
+                per_case.append(([cl], dict(x=x, fs=fs, y=y)))
+                cases.append(((n, h, dts), seed))
+                seed += 1
+    cfg = {"batches": list(D["batches"]), "c": D["c"], "hw": list(D["hs"]), "k": 3, "dilations": list(D["dilations"]),
+           "dtypes": list(D["dtypes"]), "passes": ["fwd"]}
+    return dict(cases=cases, per_case=per_case, calls=calls, desc="dynamic_multidil_3x3_d135", dtype="f32+f16+bf16",
+                kind="bytes", cfg=cfg)
+
+
+# ---------------------------------------------------------------- CPU baseline
+def cpu_baseline(wl, target_s):
+    """Time the oracle on a batch slice of the workload's own tensors."""
+    import numpy as np
+    import torch
+    from oracle import oracle as O
+
+    def f64(t):
+        return t.detach().to("cpu", torch.float64).numpy()
+
+    kind = wl["kind"]
+
+    def run_sample(ns):
+        tot_units, tot_t = 0.0, 0.0
+        for (cs, _seed), (calls, t) in zip(wl["cases"], wl["per_case"]):
+            if "fs" in t:  # dynamic
+                n = t["x"].shape[0]
+                sl = min(ns, n)
+                x = f64(t["x"][:sl])
+                fs = [f64(f[:sl]) for f in t["fs"]]
+                t0 = time.perf_counter()
+                O.dynconv_multidil_fwd(x, fs, (1, 3, 5))
+                tot_t += time.perf_counter() - t0
+                tot_units += (calls[0].nbytes if kind == "bytes" else calls[0].flops) * sl / n
+                continue
+            n, c, h, M, k, s, p, d = cs[:8]
+            sl = min(ns, n)
+            x, w, dy = f64(t["x"][:sl]), f64(t["w"]), f64(t["dy"][:sl])
+            for cl in calls:
+                t0 = time.perf_counter()
+                if cl.tag.endswith("fwd"):
+                    O.dwconv2d_fwd(x, w, None, s, p, d)
+                elif cl.tag.endswith("bwd_input"):
+                    O.dwconv2d_bwd_input(dy, w, x.shape, s, p, d)
+                else:
+                    O.dwconv2d_bwd_weight(x, dy, w.shape, s, p, d, with_bias=False)
+                tot_t += time.perf_counter() - t0
+                tot_units += (cl.nbytes if kind == "bytes" else cl.flops) * sl / n
+        return tot_units, tot_t
+
+    u1, t1 = run_sample(1)
+    ns = 1
+    if t1 > 0 and t1 < target_s:
+        ns = max(1, min(128, int(target_s / t1)))
+        if ns > 1:
+            u1, t1 = run_sample(ns)
+    if kind == "bytes":
+        val, unit = u1 / t1 / 1e9, "GB/s"
+    else:
+        val, unit = u1 / t1 / 1e9, "GFLOP/s"
+    return {"value": round(val, 4), "unit": unit, "cores": O.num_threads(), "kind": "oracle",
+            "sample": "first %d image(s) of every case's batch, every pass, same host tensors; %.1f s of oracle time"
+                      % (ns, t1)}
+
+
+# ---------------------------------------------------------------- traffic from committed counters
+def committed_traffic(tag, kernel_src):
+    """HBM bytes per launch from profiles/traffic_<tag>.json when the kernel source is unchanged."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % tag)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    h = hashlib.sha256(open(os.path.join(ROOT, kernel_src), "rb").read()).hexdigest()
+    if rec.get("source_sha256") != h:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+KERNEL_SRC = {"fwd": "dynamic_convolution_amd/csrc/dw_fwd.hip",
+              "bwd_input": "dynamic_convolution_amd/csrc/dw_bwd_input.hip",
+              "bwd_weight": "dynamic_convolution_amd/csrc/dw_bwd_weight.hip",
+              "dyn": "dynamic_convolution_amd/csrc/dw_dynconv.hip"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import dynamic_convolution_amd as dc
+
+    if not os.path.exists(dc._native.LIB_PATH):
+        from dynamic_convolution_amd import build as hb
+        hb.build()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = build_workload(args.workload, dc, dev)
+    calls = wl["calls"]
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        for cl in calls:
+            cl.fn()
+    torch.cuda.synchronize()
+
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for st in range(args.steps):
+        for ci, cl in enumerate(calls):
+            ev[st][ci][0].record(stream)
+            cl.fn()
+            ev[st][ci][1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    step_bytes = sum(cl.nbytes for cl in calls)
+    step_flops = sum(cl.flops for cl in calls)
+    ms_step = elapsed / args.steps * 1e3
+    # per-tag event time (a tag = one entry point at one kernel geometry = one kernel symbol,
+    # except grad-weight whose call also runs the small fixed-order reduction kernel)
+    per_tag = {}
+    for st in range(args.steps):
+        for ci, cl in enumerate(calls):
+            ms = ev[st][ci][0].elapsed_time(ev[st][ci][1])
+            r = per_tag.setdefault(cl.tag, {"ms": 0.0, "launches": 0, "bytes": 0, "flops": 0})
+            r["ms"] += ms
+            r["launches"] += 1
+            r["bytes"] += cl.nbytes
+            r["flops"] += cl.flops
+    dom_tag = max(per_tag, key=lambda t: per_tag[t]["ms"])
+    dom = per_tag[dom_tag]
+    avg_s = dom["ms"] / dom["launches"] / 1e3
+    if wl["kind"] == "bytes":
+        value = step_bytes / (elapsed / args.steps) / 1e9
+        unit = "GB/s"
+        achieved = dom["bytes"] / dom["launches"] / avg_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    else:
+        value = step_flops / (elapsed / args.steps) / 1e9
+        unit = "GFLOP/s"
+        achieved = dom["flops"] / dom["launches"] / avg_s / 1e12
+        roof = {"bound": "alu", "achieved": round(achieved, 2), "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / FP32_VALU_PEAK_TFLOPS, 4)}
+    src_key = next(k for k in KERNEL_SRC if k in dom_tag)
+    roof["traffic"] = committed_traffic(dom_tag.rstrip("_"), KERNEL_SRC[src_key])
+    roof["kernel"] = dom_tag.rstrip("_")
+    roof["avg_launch_us"] = round(avg_s * 1e6, 2)
+
+    out = {
+        "metric": "dwconv fwd+bwd GFLOP/s and HBM GB/s at 1 GPU, % of roofline, vs CPU oracle",
+        "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": wl["dtype"], "data": "synthetic (seeded, shapes and distributions of the workload)",
+        "config": dict({"workload": wl["desc"]}, **wl["cfg"]),
+        "step_gbytes": round(step_bytes / 1e9, 4), "step_gflop": round(step_flops / 1e9, 4),
+        "gbs": round(step_bytes / (elapsed / args.steps) / 1e9, 2),
+        "gflops": round(step_flops / (elapsed / args.steps) / 1e9, 2),
+        "roofline": roof,
+        "per_kernel": {t.rstrip("_"): {"avg_us": round(r["ms"] / r["launches"] * 1e3, 2),
+                                       "share": round(r["ms"] / sum(v["ms"] for v in per_tag.values()), 4),
+                                       "gbs": round(r["bytes"] / (r["ms"] / 1e3) / 1e9, 1),
+                                       "gflops": round(r["flops"] / (r["ms"] / 1e3) / 1e9, 1)}
+                       for t, r in sorted(per_tag.items())},
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
