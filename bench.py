@@ -24,9 +24,13 @@ value      whole-step algorithmic throughput: compulsory bytes (each input eleme
            the result depends on once, each output once) per second for the
            bandwidth-bound workloads; valid-tap flops (2 per in-bounds multiply-add)
            per second for largek
+launches   the calls of one kernel geometry (a "tag") are captured once into a HIP
+           graph; a step replays the tags' graphs in pass order (--eager launches
+           call by call instead)
 roofline   the dominant kernel (most time in the step): its algorithmic bytes or
-           flops over its average launch duration, measured with HIP events on the
-           launch stream during the timed steps, against the MI355X peak
+           flops over its average launch duration, measured with HIP events recorded
+           on the launch stream around each tag's replay during the timed steps,
+           against the MI355X peak
 cpu_baseline  the fp64 CPU oracle on a bounded sample of the same workload
            (a batch slice of the same host tensors), on this host's cores
 """
@@ -55,6 +59,7 @@ def parse():
     ap.add_argument("--workload", default="mobilenet", choices=["mobilenet", "multdil", "largek", "dynamic"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline leg")
+    ap.add_argument("--eager", action="store_true", help="launch call by call instead of replaying HIP graphs")
     return ap.parse_args()
 
 
@@ -164,7 +169,15 @@ def build_workload(name, dc, dev):
     else:
         return build_dynamic(dc, dev)
     per_case = [static_calls(dc, cs, dev, seed) for cs, seed in cases]
-    calls = [cl for pi in range(3) for (cls, _t) in per_case for cl in cls[pi:pi + 1]]
+    # pass-major; within a pass, calls of one kernel geometry (tag) are adjacent
+    calls = []
+    for pi in range(3):
+        tags = {}
+        for cls, _t in per_case:
+            for cl in cls[pi:pi + 1]:
+                tags.setdefault(cl.tag, []).append(cl)
+        for cl_list in tags.values():
+            calls.extend(cl_list)
     return dict(cases=cases, per_case=per_case, calls=calls, desc=desc, dtype=dt, kind=kind, cfg=cfg)
 
 
@@ -291,20 +304,44 @@ def main():
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
 
-    for _ in range(args.warmup):
+    # one group of consecutive calls per tag (= one kernel geometry)
+    groups = []
+    for cl in calls:
+        if groups and groups[-1][0] == cl.tag:
+            groups[-1][1].append(cl)
+        else:
+            groups.append((cl.tag, [cl]))
+    for _ in range(max(1, args.warmup)):
         for cl in calls:
             cl.fn()
     torch.cuda.synchronize()
+    if args.eager:
+        runners = [(tag, (lambda cls=cls: [c.fn() for c in cls])) for tag, cls in groups]
+    else:
+        # each group captured once into a HIP graph and replayed: the step's
+        # launches cost no host time, as a fixed training step would run
+        runners = []
+        for tag, cls in groups:
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                for c in cls:
+                    c.fn()
+            runners.append((tag, gr.replay))
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            for _tag, run in runners:
+                run()
+        torch.cuda.synchronize()
 
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in runners]
           for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for st in range(args.steps):
-        for ci, cl in enumerate(calls):
-            ev[st][ci][0].record(stream)
-            cl.fn()
-            ev[st][ci][1].record(stream)
+        for gi, (_tag, run) in enumerate(runners):
+            ev[st][gi][0].record(stream)
+            run()
+            ev[st][gi][1].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
@@ -312,16 +349,17 @@ def main():
     step_flops = sum(cl.flops for cl in calls)
     ms_step = elapsed / args.steps * 1e3
     # per-tag event time (a tag = one entry point at one kernel geometry = one kernel symbol,
-    # except grad-weight whose call also runs the small fixed-order reduction kernel)
+    # except grad-weight whose call also runs the small fixed-order reduction kernel);
+    # events bracket each tag's graph replay on the launch stream
     per_tag = {}
     for st in range(args.steps):
-        for ci, cl in enumerate(calls):
-            ms = ev[st][ci][0].elapsed_time(ev[st][ci][1])
-            r = per_tag.setdefault(cl.tag, {"ms": 0.0, "launches": 0, "bytes": 0, "flops": 0})
+        for gi, (tag, cls) in enumerate(groups):
+            ms = ev[st][gi][0].elapsed_time(ev[st][gi][1])
+            r = per_tag.setdefault(tag, {"ms": 0.0, "launches": 0, "bytes": 0, "flops": 0})
             r["ms"] += ms
-            r["launches"] += 1
-            r["bytes"] += cl.nbytes
-            r["flops"] += cl.flops
+            r["launches"] += len(cls)
+            r["bytes"] += sum(c.nbytes for c in cls)
+            r["flops"] += sum(c.flops for c in cls)
     dom_tag = max(per_tag, key=lambda t: per_tag[t]["ms"])
     dom = per_tag[dom_tag]
     avg_s = dom["ms"] / dom["launches"] / 1e3
@@ -347,7 +385,8 @@ def main():
         "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": wl["dtype"], "data": "synthetic (seeded, shapes and distributions of the workload)",
-        "config": dict({"workload": wl["desc"]}, **wl["cfg"]),
+        "config": dict({"workload": wl["desc"], "launch": "eager" if args.eager else "hip_graph_per_kernel"},
+                       **wl["cfg"]),
         "step_gbytes": round(step_bytes / 1e9, 4), "step_gflop": round(step_flops / 1e9, 4),
         "gbs": round(step_bytes / (elapsed / args.steps) / 1e9, 2),
         "gflops": round(step_flops / (elapsed / args.steps) / 1e9, 2),

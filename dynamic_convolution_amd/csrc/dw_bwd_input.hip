@@ -15,6 +15,8 @@
 #include "dw_common.hpp"
 #include "dw_internal.hpp"
 
+#include <type_traits>
+
 namespace dw {
 namespace {
 
@@ -238,6 +240,8 @@ int run_bwd_input(const Geo &g, const BandPlan &bp, int seg_slots, const void *d
 
 template <typename T>
 int dispatch_bwd_input(const Geo &g, const void *dy, const void *w, void *dx, hipStream_t s) {
+    const int dt = sizeof(T) == 4 ? 0 : (std::is_same<T, __half>::value ? 1 : 2);
+    if (rowwalk_fits(g, dt, 1)) return rowwalk_bwd_input(g, dy, w, dx, dt, s);
     BandPlan bp;
     int seg_slots = 0;
     if (!plan_bwd_input<T>(g, bp, seg_slots)) return kErrUnsupported;
@@ -252,6 +256,7 @@ int dispatch_bwd_input(const Geo &g, const void *dy, const void *w, void *dx, hi
 }  // namespace
 
 bool bwd_input_supported(const Geo &g, int dtype) {
+    if (rowwalk_fits(g, dtype, 1)) return true;
     BandPlan bp;
     int ss;
     return dtype == 0 ? plan_bwd_input<float>(g, bp, ss) : plan_bwd_input<__half>(g, bp, ss);

@@ -19,6 +19,8 @@
 #include "dw_common.hpp"
 #include "dw_internal.hpp"
 
+#include <type_traits>
+
 namespace dw {
 namespace {
 
@@ -393,9 +395,23 @@ int run_small(const Geo &g, const BwPlan &p, const void *x, const void *dy, void
 template <typename T>
 int dispatch_bwd_weight(const Geo &g, const void *x, const void *dy, void *dwt, void *db, void *ws,
                         hipStream_t s) {
+    const int dt = sizeof(T) == 4 ? 0 : (std::is_same<T, __half>::value ? 1 : 2);
+    const int kk = g.kh * g.kw;
+    int NC, nslots, rc;
+    if (rowwalk_fits(g, dt, 2)) {
+        // streaming pass 1 (3x3, pad 1): workspace [ic][NC][M*10]
+        NC = rowwalk_bwd_weight_chunks(g, dt);
+        nslots = g.mult * (kk + 1);
+        rc = rowwalk_bwd_weight(g, x, dy, ws, dt, s);
+        if (rc != kOk) return rc;
+        const int total = g.oc * (kk + 1);
+        hipLaunchKernelGGL((bwd_weight_reduce_kernel<T>), dim3((total + kThreads - 1) / kThreads), dim3(kThreads),
+                           0, s, static_cast<const float *>(ws), static_cast<T *>(dwt), static_cast<T *>(db), g.oc,
+                           g.mult, kk, NC, nslots);
+        return hipGetLastError() == hipSuccess ? kOk : kErrHip;
+    }
     BwPlan p;
     if (!plan_bwd_weight(g, sizeof(T), p)) return kErrUnsupported;
-    int rc;
     if (p.small) {
         if (g.kh == 3 && g.sh == 1) rc = run_small<T, 3, 3, 1, 1>(g, p, x, dy, ws, s);
         else if (g.kh == 3) rc = run_small<T, 3, 3, 2, 1>(g, p, x, dy, ws, s);
@@ -414,7 +430,6 @@ int dispatch_bwd_weight(const Geo &g, const void *x, const void *dy, void *dwt, 
         rc = hipGetLastError() == hipSuccess ? kOk : kErrHip;
     }
     if (rc != kOk) return rc;
-    const int kk = g.kh * g.kw;
     const int total = g.oc * (kk + 1);
     hipLaunchKernelGGL((bwd_weight_reduce_kernel<T>), dim3((total + kThreads - 1) / kThreads), dim3(kThreads), 0,
                        s, static_cast<const float *>(ws), static_cast<T *>(dwt), static_cast<T *>(db), g.oc,
@@ -425,6 +440,10 @@ int dispatch_bwd_weight(const Geo &g, const void *x, const void *dy, void *dwt, 
 }  // namespace
 
 int64_t bwd_weight_workspace(const Geo &g, int dtype) {
+    if (rowwalk_fits(g, dtype, 2)) {
+        const int NC = rowwalk_bwd_weight_chunks(g, dtype);
+        return std::max<int64_t>(static_cast<int64_t>(g.ic) * NC * g.mult * 10 * 4, 16);
+    }
     BwPlan p;
     if (!plan_bwd_weight(g, dtype == 0 ? 4 : 2, p)) return -1;
     return std::max<int64_t>(p.ws_bytes, 16);

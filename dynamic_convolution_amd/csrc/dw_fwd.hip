@@ -17,6 +17,8 @@
 #include "dw_common.hpp"
 #include "dw_internal.hpp"
 
+#include <type_traits>
+
 namespace dw {
 namespace {
 
@@ -238,6 +240,8 @@ int run_fwd(const Geo &g, const BandPlan &bp, const void *x, const void *w, cons
 
 template <typename T>
 int dispatch_fwd(const Geo &g, const void *x, const void *w, const void *b, void *y, hipStream_t s) {
+    const int dt = sizeof(T) == 4 ? 0 : (std::is_same<T, __half>::value ? 1 : 2);
+    if (rowwalk_fits(g, dt, 0)) return rowwalk_fwd(g, x, w, b, y, dt, s);
     BandPlan bp;
     if (!plan_fwd<T>(g, bp)) return kErrUnsupported;
     const bool sq = g.kh == g.kw && g.sh == g.sw && g.dh == g.dw;
@@ -251,6 +255,7 @@ int dispatch_fwd(const Geo &g, const void *x, const void *w, const void *b, void
 }  // namespace
 
 bool fwd_supported(const Geo &g, int dtype) {
+    if (rowwalk_fits(g, dtype, 0)) return true;
     BandPlan bp;
     switch (dtype) {
         case 0: return plan_fwd<float>(g, bp);

@@ -37,6 +37,16 @@ int launch_bwd_weight(const Geo &g, const void *x, const void *dy, void *dwt, vo
 int launch_dynconv(const void *x, const void *const *filters, const int32_t *dil, int nb, void *y,
                    int n, int c, int h, int w, int k, int dtype, hipStream_t s);
 
+// Streaming kernels for 3x3 / pad 1 / dilation 1 / stride 1-2 / multiplier <= 2
+// (dw_rowwalk.hip).  The launchers return kErrUnsupported when the row is
+// wider than one wave of 16-byte strips; callers then use the band kernels.
+bool rowwalk_applicable(const Geo &g, int pass);
+bool rowwalk_fits(const Geo &g, int dtype, int pass);  // pass: 0 fwd, 1 grad-input, 2 grad-weight
+int rowwalk_fwd(const Geo &g, const void *x, const void *w, const void *b, void *y, int dtype, hipStream_t s);
+int rowwalk_bwd_input(const Geo &g, const void *dy, const void *w, void *dx, int dtype, hipStream_t s);
+int rowwalk_bwd_weight_chunks(const Geo &g, int dtype);
+int rowwalk_bwd_weight(const Geo &g, const void *x, const void *dy, void *ws, int dtype, hipStream_t s);
+
 // Shape checks the launchers need beyond argument validation (LDS fit).
 bool fwd_supported(const Geo &g, int dtype);
 bool bwd_input_supported(const Geo &g, int dtype);

@@ -322,3 +322,67 @@ def test_full_size_dynamic_sampled(dtype):
                                           [f[nn:nn + 1, ch:ch + 1].cpu() for f in fs], D["dilations"])
             got = torch.stack([y[nn, b * c + ch] for b in range(3)]).unsqueeze(0)
             assert_close(got, want, 9, DT[dtype], "dynamic-full n%d c%d" % (nn, ch))
+
+
+# ------------------------------------------------------------------ streaming 3x3 path edges
+@pytest.mark.parametrize("n,c,h,w,mult,s,dt", [
+    (2, 3, 9, 13, 1, 1, "f32"), (2, 3, 9, 13, 1, 2, "f32"),     # odd sizes, scalar loads
+    (1, 4, 17, 256, 1, 1, "f32"),                               # 64 strips: widest row of one wave
+    (1, 2, 10, 257, 1, 1, "f32"),                               # one column too wide: band kernels
+    (1, 2, 12, 512, 1, 2, "f32"),                               # stride 2, 64 output strips
+    (3, 5, 23, 40, 2, 1, "f32"), (3, 5, 23, 40, 2, 2, "f32"),   # multiplier 2
+    (2, 3, 31, 64, 1, 1, "f16"), (2, 3, 31, 64, 2, 2, "bf16"),  # 16-bit strips of 8
+    (1, 2, 6, 512, 1, 1, "bf16"), (1, 2, 5, 1030, 1, 2, "f16"),
+    (4, 1, 1, 1, 1, 1, "f32"), (2, 2, 2, 3, 1, 2, "f32"),       # degenerate planes
+])
+def test_streaming_3x3_shapes(n, c, h, w, mult, s, dt):
+    x, wt, b, dy = static_case(n, c, h, w, mult, 3, s, 1, 1, DT[dt], 600 + h * 7 + w)
+    check_static(x, wt, b, dy, s, 1, 1, "stream3x3 n%d c%d %dx%d m%d s%d %s" % (n, c, h, w, mult, s, dt))
+
+
+# ------------------------------------------------------------------ HIP graph replay
+def test_graph_replay_matches_eager():
+    """Every entry point captured in a HIP graph: each of several replays, with eager
+    work and synchronisation in between, reproduces the eager result bitwise."""
+    cases = [(4, 8, 112, 112, 1, 1), (4, 8, 56, 56, 2, 2), (3, 5, 14, 14, 1, 2)]  # streaming and band paths
+    work = []
+    for n, c, h, w, mult, s in cases:
+        x, wt, b, dy = static_case(n, c, h, w, mult, 3, s, 1, 1, torch.float32, 17 + h)
+        xd, wd, bd, dyd = x.to(DEV), wt.to(DEV), b.to(DEV), dy.to(DEV)
+        y = torch.empty((n, c * mult) + tuple(dy.shape[2:]), device=DEV)
+        dx, gw, gb = torch.empty_like(xd), torch.empty_like(wd), torch.empty_like(bd)
+        ws = torch.empty((dc.dwconv2d_bwd_weight_workspace_bytes(x.shape, wt.shape, s, 1, 1),),
+                         dtype=torch.uint8, device=DEV)
+        work.append(lambda xd=xd, wd=wd, bd=bd, dyd=dyd, y=y, dx=dx, gw=gw, gb=gb, ws=ws, s=s: (
+            dc.dwconv2d_fwd(xd, wd, bd, s, 1, 1, out=y),
+            dc.dwconv2d_bwd_input(dyd, wd, xd.shape, s, 1, 1, out=dx),
+            dc.dwconv2d_bwd_weight(xd, dyd, wd.shape, s, 1, 1, out=gw, out_bias=gb, workspace=ws)))
+        work[-1].outs = (y, dx, gw, gb)
+    xq, fs = dyn_inputs(1, 4, 64, 64, 3, (1, 3, 5), torch.float32, 19)
+    xqd, fsd = xq.to(DEV), [f.to(DEV) for f in fs]
+    yq = torch.empty((1, 12, 64, 64), device=DEV)
+    dynf = lambda: dc.dynconv_multidil_fwd(xqd, fsd, (1, 3, 5), out=yq)
+    note("graph eager")
+    for fn in work:
+        fn()
+    dynf()
+    torch.cuda.synchronize()
+    ref = [tuple(t.clone() for t in fn.outs) for fn in work] + [(yq.clone(),)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for fn in work:
+            fn()
+        dynf()
+    for rep in range(4):
+        for fn in work:  # poison outputs eagerly between replays
+            for t in fn.outs:
+                t.fill_(float("nan"))
+        yq.fill_(float("nan"))
+        torch.cuda.synchronize()
+        note("graph replay %d" % rep)
+        g.replay()
+        torch.cuda.synchronize()
+        got = [fn.outs for fn in work] + [(yq,)]
+        for a_, b_ in zip(got, ref):
+            for t1, t2 in zip(a_, b_):
+                assert torch.equal(t1, t2), "replay %d differs from eager" % rep
