@@ -398,11 +398,12 @@ int dispatch_bwd_weight(const Geo &g, const void *x, const void *dy, void *dwt, 
     const int dt = sizeof(T) == 4 ? 0 : (std::is_same<T, __half>::value ? 1 : 2);
     const int kk = g.kh * g.kw;
     int NC, nslots, rc;
-    if (rowwalk_fits(g, dt, 2)) {
-        // streaming pass 1 (3x3, pad 1): workspace [ic][NC][M*10]
-        NC = rowwalk_bwd_weight_chunks(g, dt);
+    const bool small = small_fits(g, dt, 2);
+    if (small || rowwalk_fits(g, dt, 2)) {
+        // whole-plane (small planes) or streaming (3x3, pad 1) pass 1: workspace [ic][NC][M*(kk+1)]
+        NC = small ? small_bwd_weight_chunks(g, dt) : rowwalk_bwd_weight_chunks(g, dt);
         nslots = g.mult * (kk + 1);
-        rc = rowwalk_bwd_weight(g, x, dy, ws, dt, s);
+        rc = small ? small_bwd_weight(g, x, dy, ws, dt, s) : rowwalk_bwd_weight(g, x, dy, ws, dt, s);
         if (rc != kOk) return rc;
         const int total = g.oc * (kk + 1);
         hipLaunchKernelGGL((bwd_weight_reduce_kernel<T>), dim3((total + kThreads - 1) / kThreads), dim3(kThreads),
@@ -440,6 +441,10 @@ int dispatch_bwd_weight(const Geo &g, const void *x, const void *dy, void *dwt, 
 }  // namespace
 
 int64_t bwd_weight_workspace(const Geo &g, int dtype) {
+    if (small_fits(g, dtype, 2)) {
+        const int NC = small_bwd_weight_chunks(g, dtype);
+        return std::max<int64_t>(static_cast<int64_t>(g.ic) * NC * g.mult * (g.kh * g.kw + 1) * 4, 16);
+    }
     if (rowwalk_fits(g, dtype, 2)) {
         const int NC = rowwalk_bwd_weight_chunks(g, dtype);
         return std::max<int64_t>(static_cast<int64_t>(g.ic) * NC * g.mult * 10 * 4, 16);

@@ -72,22 +72,40 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t u, FastDiv f) {
 // vectors aligned in global memory (src must be 16-byte aligned), so element e
 // lands at lds[e - (gbeg rounded down to a vector)]; the return value is the
 // LDS index of element gbeg.  Partially covered end vectors are read one
-// element at a time so nothing outside [gbeg, gend) is touched.
+// element at a time so nothing outside [gbeg, gend) is touched.  Each thread
+// issues up to kCopyBatch loads before its LDS stores, to keep several
+// 16-byte requests per lane in flight.
+constexpr int kCopyBatch = 4;
+
 template <typename T>
 __device__ __forceinline__ int lds_copy_range(T *lds, const T *__restrict__ src, int64_t gbeg,
                                               int64_t gend, int tid, int nthreads) {
     constexpr int VE = Vec<T>::N;
     const int64_t base = gbeg & ~static_cast<int64_t>(VE - 1);
     const int nvec = static_cast<int>((gend - base + VE - 1) / VE);
-    for (int v = tid; v < nvec; v += nthreads) {
-        const int64_t e0 = base + static_cast<int64_t>(v) * VE;
-        if (e0 >= gbeg && e0 + VE <= gend) {
-            *reinterpret_cast<uint4 *>(lds + v * VE) = *reinterpret_cast<const uint4 *>(src + e0);
-        } else {
+    for (int v0 = tid; v0 < nvec; v0 += nthreads * kCopyBatch) {
+        uint4 r[kCopyBatch];
 #pragma unroll
-            for (int k = 0; k < VE; ++k) {
-                const int64_t e = e0 + k;
-                lds[v * VE + k] = (e >= gbeg && e < gend) ? src[e] : T{};
+        for (int u = 0; u < kCopyBatch; ++u) r[u] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < kCopyBatch; ++u) {
+            const int v = v0 + u * nthreads;
+            const int64_t e0 = base + static_cast<int64_t>(v) * VE;
+            if (v < nvec && e0 >= gbeg && e0 + VE <= gend) r[u] = *reinterpret_cast<const uint4 *>(src + e0);
+        }
+#pragma unroll
+        for (int u = 0; u < kCopyBatch; ++u) {
+            const int v = v0 + u * nthreads;
+            if (v >= nvec) continue;
+            const int64_t e0 = base + static_cast<int64_t>(v) * VE;
+            if (e0 >= gbeg && e0 + VE <= gend) {
+                *reinterpret_cast<uint4 *>(lds + v * VE) = r[u];
+            } else {
+#pragma unroll
+                for (int k = 0; k < VE; ++k) {
+                    const int64_t e = e0 + k;
+                    lds[v * VE + k] = (e >= gbeg && e < gend) ? src[e] : T{};
+                }
             }
         }
     }

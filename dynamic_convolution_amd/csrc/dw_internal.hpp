@@ -47,6 +47,12 @@ int rowwalk_bwd_input(const Geo &g, const void *dy, const void *w, void *dx, int
 int rowwalk_bwd_weight_chunks(const Geo &g, int dtype);
 int rowwalk_bwd_weight(const Geo &g, const void *x, const void *dy, void *ws, int dtype, hipStream_t s);
 
+// Grad-weight for small planes over groups of adjacent channels (dw_small.hip);
+// small_fits is true only for pass 2 (grad-weight) geometries it handles.
+bool small_fits(const Geo &g, int dtype, int pass);
+int small_bwd_weight_chunks(const Geo &g, int dtype);
+int small_bwd_weight(const Geo &g, const void *x, const void *dy, void *ws, int dtype, hipStream_t s);
+
 // Shape checks the launchers need beyond argument validation (LDS fit).
 bool fwd_supported(const Geo &g, int dtype);
 bool bwd_input_supported(const Geo &g, int dtype);

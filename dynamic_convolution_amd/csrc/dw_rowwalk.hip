@@ -488,6 +488,7 @@ bool rowwalk_fits(const Geo &g, int dtype, int pass) {
     if ((width + ve - 1) / ve > 64) return false;
     // narrow rows leave most lanes of a slot idle; the LDS band kernels measure
     // faster there for the forward and grad-input (grad-weight streams always)
+    if (pass == 1 && g.sh == 2) return false;  // the band kernel measured faster for stride-2 grad-input
     return pass == 2 || width >= 56;
 }
 
