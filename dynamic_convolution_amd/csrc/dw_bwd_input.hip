@@ -242,6 +242,7 @@ template <typename T>
 int dispatch_bwd_input(const Geo &g, const void *dy, const void *w, void *dx, hipStream_t s) {
     const int dt = sizeof(T) == 4 ? 0 : (std::is_same<T, __half>::value ? 1 : 2);
     if (rowwalk_fits(g, dt, 1)) return rowwalk_bwd_input(g, dy, w, dx, dt, s);
+    if (largek_fits(g, 1)) return largek_bwd_input(g, dy, w, dx, dt, s);
     BandPlan bp;
     int seg_slots = 0;
     if (!plan_bwd_input<T>(g, bp, seg_slots)) return kErrUnsupported;
@@ -256,7 +257,7 @@ int dispatch_bwd_input(const Geo &g, const void *dy, const void *w, void *dx, hi
 }  // namespace
 
 bool bwd_input_supported(const Geo &g, int dtype) {
-    if (rowwalk_fits(g, dtype, 1)) return true;
+    if (rowwalk_fits(g, dtype, 1) || largek_fits(g, 1)) return true;
     BandPlan bp;
     int ss;
     return dtype == 0 ? plan_bwd_input<float>(g, bp, ss) : plan_bwd_input<__half>(g, bp, ss);

@@ -399,11 +399,14 @@ int dispatch_bwd_weight(const Geo &g, const void *x, const void *dy, void *dwt, 
     const int kk = g.kh * g.kw;
     int NC, nslots, rc;
     const bool small = small_fits(g, dt, 2);
-    if (small || rowwalk_fits(g, dt, 2)) {
-        // whole-plane (small planes) or streaming (3x3, pad 1) pass 1: workspace [ic][NC][M*(kk+1)]
-        NC = small ? small_bwd_weight_chunks(g, dt) : rowwalk_bwd_weight_chunks(g, dt);
+    const bool large = !small && largek_bwdw_fits(g);
+    if (small || large || rowwalk_fits(g, dt, 2)) {
+        // channel-group (small planes), register-tile (large k) or streaming (3x3, pad 1)
+        // pass 1: workspace [ic][NC][M*(kk+1)]
+        NC = small ? small_bwd_weight_chunks(g, dt) : large ? largek_bwd_weight_chunks(g) : rowwalk_bwd_weight_chunks(g, dt);
         nslots = g.mult * (kk + 1);
-        rc = small ? small_bwd_weight(g, x, dy, ws, dt, s) : rowwalk_bwd_weight(g, x, dy, ws, dt, s);
+        rc = small ? small_bwd_weight(g, x, dy, ws, dt, s)
+                   : large ? largek_bwd_weight(g, x, dy, ws, dt, s) : rowwalk_bwd_weight(g, x, dy, ws, dt, s);
         if (rc != kOk) return rc;
         const int total = g.oc * (kk + 1);
         hipLaunchKernelGGL((bwd_weight_reduce_kernel<T>), dim3((total + kThreads - 1) / kThreads), dim3(kThreads),
@@ -444,6 +447,10 @@ int64_t bwd_weight_workspace(const Geo &g, int dtype) {
     if (small_fits(g, dtype, 2)) {
         const int NC = small_bwd_weight_chunks(g, dtype);
         return std::max<int64_t>(static_cast<int64_t>(g.ic) * NC * g.mult * (g.kh * g.kw + 1) * 4, 16);
+    }
+    if (largek_bwdw_fits(g)) {
+        const int NC = largek_bwd_weight_chunks(g);
+        return std::max<int64_t>(static_cast<int64_t>(g.ic) * NC * (g.kh * g.kw + 1) * 4, 16);
     }
     if (rowwalk_fits(g, dtype, 2)) {
         const int NC = rowwalk_bwd_weight_chunks(g, dtype);

@@ -242,6 +242,7 @@ template <typename T>
 int dispatch_fwd(const Geo &g, const void *x, const void *w, const void *b, void *y, hipStream_t s) {
     const int dt = sizeof(T) == 4 ? 0 : (std::is_same<T, __half>::value ? 1 : 2);
     if (rowwalk_fits(g, dt, 0)) return rowwalk_fwd(g, x, w, b, y, dt, s);
+    if (largek_fits(g, 0)) return largek_fwd(g, x, w, b, y, dt, s);
     BandPlan bp;
     if (!plan_fwd<T>(g, bp)) return kErrUnsupported;
     const bool sq = g.kh == g.kw && g.sh == g.sw && g.dh == g.dw;
@@ -255,7 +256,7 @@ int dispatch_fwd(const Geo &g, const void *x, const void *w, const void *b, void
 }  // namespace
 
 bool fwd_supported(const Geo &g, int dtype) {
-    if (rowwalk_fits(g, dtype, 0)) return true;
+    if (rowwalk_fits(g, dtype, 0) || largek_fits(g, 0)) return true;
     BandPlan bp;
     switch (dtype) {
         case 0: return plan_fwd<float>(g, bp);

@@ -53,6 +53,15 @@ bool small_fits(const Geo &g, int dtype, int pass);
 int small_bwd_weight_chunks(const Geo &g, int dtype);
 int small_bwd_weight(const Geo &g, const void *x, const void *dy, void *ws, int dtype, hipStream_t s);
 
+// Large-kernel (k = 7, 13, 31; stride 1, dilation 1) register-tile kernels
+// (dw_largek.hip).  pass: 0 forward, 1 grad-input.
+bool largek_fits(const Geo &g, int pass);
+int largek_fwd(const Geo &g, const void *x, const void *w, const void *b, void *y, int dtype, hipStream_t s);
+int largek_bwd_input(const Geo &g, const void *dy, const void *w, void *dx, int dtype, hipStream_t s);
+bool largek_bwdw_fits(const Geo &g);
+int largek_bwd_weight_chunks(const Geo &g);
+int largek_bwd_weight(const Geo &g, const void *x, const void *dy, void *ws, int dtype, hipStream_t s);
+
 // Shape checks the launchers need beyond argument validation (LDS fit).
 bool fwd_supported(const Geo &g, int dtype);
 bool bwd_input_supported(const Geo &g, int dtype);

@@ -1,0 +1,440 @@
+// dw_largek.hip -- large-kernel depthwise forward and grad-input on gfx950
+// (k = 7, 13, 31; stride 1, dilation 1).
+//
+// With a k x k filter each input element feeds k*k multiply-adds, so for
+// k >= 13 these passes are bound by fp32 VALU throughput, not by HBM (the
+// MegEngine large-kernel depthwise article: batch 64, 384 channels, kernels up
+// to 31x31; its DirectConv splits kernel columns over 4 lanes and reduces with
+// a shuffle butterfly).  On CDNA the filter of a plane is uniform across the
+// workgroup, so here it is read with scalar loads into SGPRs and used directly
+// as an FMA operand, and each lane keeps a whole TR x TC output tile in VGPRs
+// -- no cross-lane reduction is needed:
+//   1. the workgroup stages its plane (or a band of rows) into LDS as fp32 with
+//      the zero padding written out, so the inner loop has no bounds tests;
+//   2. a lane walks the TR + k - 1 padded input rows its tile reads; each row
+//      segment of TC + k - 1 values is read from LDS once and feeds up to
+//      TR*k*TC FMAs (0.08 LDS words per FMA at k = 31);
+//   3. grad-input is the same correlation of dy with the kernel flipped in
+//      both axes and padding k - 1 - pad (stride 1, dilation 1, multiplier 1).
+#include "dw_common.hpp"
+#include "dw_internal.hpp"
+
+namespace dw {
+namespace {
+
+template <typename T> struct LkArgs {
+    const T *in;   // forward: x; grad-input: dy
+    const T *w;
+    const T *b;
+    T *out;        // y or dx
+    int IH, IW;    // input plane of this pass
+    int OH, OW;    // output plane of this pass
+    int P;         // top/left zero padding of this pass
+    int C;         // output channels of this pass (planes per image)
+    int mult;      // forward: output channels per input channel
+    int pitch;     // LDS row pitch (floats)
+    int BH;        // output rows per band
+    int nbands;
+    int NCB, NRB;  // column / row blocks of output tiles in a band
+    FastDiv fpitch;
+};
+
+template <typename T, int K, int TR, int TC, bool FLIP>
+__global__ __launch_bounds__(256) void lk_conv_kernel(LkArgs<T> a) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    float *xs = reinterpret_cast<float *>(smem);
+    constexpr int WW4 = (TC + K - 1 + 3) / 4 * 4;
+    static_assert(TC % 4 == 0, "column tile is whole 16-byte vectors");
+    const int tid = threadIdx.x;
+    const int nthr = blockDim.x;
+    const int plane = blockIdx.x / a.nbands;  // output plane (n, c)
+    const int band = blockIdx.x - plane * a.nbands;
+    const int n = plane / a.C;
+    const int c = plane - n * a.C;
+    const int cin = FLIP ? c : c / a.mult;  // input plane channel
+    const int oh0 = band * a.BH;
+    const int rows = min(a.BH, a.OH - oh0) + K - 1;  // padded input rows of this band
+    const T *src = a.in + (static_cast<int64_t>(n) * (FLIP ? a.C : a.C / a.mult) + cin) * a.IH * a.IW;
+
+    // 1. stage padded rows [oh0 - P, oh0 - P + rows) x cols [-P, pitch - P)
+    const int total = rows * a.pitch;
+    for (int e = tid; e < total; e += nthr) {
+        const int r = static_cast<int>(fdiv(static_cast<uint32_t>(e), a.fpitch));
+        const int col = e - r * a.pitch;
+        const int ih = oh0 - a.P + r, iw = col - a.P;
+        xs[e] = (ih >= 0 && ih < a.IH && iw >= 0 && iw < a.IW) ? to_f32(src[ih * a.IW + iw]) : 0.f;
+    }
+    __syncthreads();
+
+    const T *__restrict__ wk = a.w + static_cast<int64_t>(c) * K * K;
+    const float bias = (!FLIP && a.b) ? to_f32(a.b[c]) : 0.f;
+    const int items = a.NRB * a.NCB;
+    for (int it = tid; it < items; it += nthr) {
+        const int rb = it / a.NCB;
+        const int cb = it - rb * a.NCB;
+        float acc[TR][TC];
+#pragma unroll
+        for (int tr = 0; tr < TR; ++tr)
+#pragma unroll
+            for (int q = 0; q < TC; ++q) acc[tr][q] = bias;
+        const float *base = xs + (rb * TR) * a.pitch + cb * TC;
+#pragma unroll 1
+        for (int r = 0; r < TR + K - 1; ++r) {
+            // TC and the pitch are multiples of 4: the window is read as 16-byte vectors
+            float win[WW4];
+            const float4 *rp = reinterpret_cast<const float4 *>(base + r * a.pitch);
+#pragma unroll
+            for (int e = 0; e < WW4 / 4; ++e) {
+                const float4 v = rp[e];
+                win[4 * e] = v.x;
+                win[4 * e + 1] = v.y;
+                win[4 * e + 2] = v.z;
+                win[4 * e + 3] = v.w;
+            }
+#pragma unroll
+            for (int tr = 0; tr < TR; ++tr) {
+                const int i = r - tr;  // kernel row; uniform across the workgroup
+                if (i < 0 || i >= K) continue;
+                const T *wrow = wk + (FLIP ? (K - 1 - i) : i) * K;
+#pragma unroll
+                for (int j = 0; j < K; ++j) {
+                    const float wv = to_f32(wrow[FLIP ? K - 1 - j : j]);
+#pragma unroll
+                    for (int q = 0; q < TC; ++q) acc[tr][q] = fmaf(wv, win[q + j], acc[tr][q]);
+                }
+            }
+        }
+        T *op = a.out + (static_cast<int64_t>(plane) * a.OH + oh0 + rb * TR) * a.OW + cb * TC;
+#pragma unroll
+        for (int tr = 0; tr < TR; ++tr) {
+            if (oh0 + rb * TR + tr >= min(oh0 + a.BH, a.OH)) continue;
+#pragma unroll
+            for (int q = 0; q < TC; ++q)
+                if (cb * TC + q < a.OW) op[tr * a.OW + q] = from_f32<T>(acc[tr][q]);
+        }
+    }
+}
+
+struct LkPlan {
+    int TC, BH, nbands, NCB, NRB, pitch, threads, lds_bytes;
+};
+
+constexpr int kTR = 2;
+
+bool plan_lk(int OH, int OW, int K, LkPlan &p) {
+    // column tile 8 unless that wastes more than a quarter of the row, else 4
+    p.TC = 8;
+    if (((OW + 7) / 8) * 8 - OW > OW / 4) p.TC = 4;
+    p.NCB = (OW + p.TC - 1) / p.TC;
+    p.pitch = p.NCB * p.TC + K - 1;
+    p.pitch = (p.pitch + 3) & ~3;
+    // rows per band: whole plane while the tile count fits 256 lanes and LDS fits 64 KiB
+    int bh = OH;
+    auto lds = [&](int b) { return static_cast<int64_t>(b + K - 1) * p.pitch * 4; };
+    while (bh > kTR && (((bh + kTR - 1) / kTR) * p.NCB > 256 || lds(bh) > 64 * 1024)) bh = (bh + 1) / 2;
+    if (lds(bh) > 64 * 1024) return false;
+    p.nbands = (OH + bh - 1) / bh;
+    p.BH = (OH + p.nbands - 1) / p.nbands;
+    p.BH = (p.BH + kTR - 1) / kTR * kTR;
+    p.nbands = (OH + p.BH - 1) / p.BH;
+    p.NRB = p.BH / kTR;
+    p.threads = std::min(256, ((p.NRB * p.NCB + 63) / 64) * 64);
+    if (lds(p.BH) > 64 * 1024) return false;
+    p.lds_bytes = static_cast<int>(lds(p.BH));
+    return true;
+}
+
+template <typename T, int K, int TC, bool FLIP>
+int run_lk(const LkArgs<T> &a0, const LkPlan &p, int planes, hipStream_t s) {
+    LkArgs<T> a = a0;
+    a.pitch = p.pitch;
+    a.BH = p.BH;
+    a.nbands = p.nbands;
+    a.NCB = p.NCB;
+    a.NRB = p.NRB;
+    a.fpitch = make_fastdiv(p.pitch, static_cast<uint64_t>(p.BH + K) * p.pitch);
+    hipLaunchKernelGGL((lk_conv_kernel<T, K, kTR, TC, FLIP>), dim3(planes * p.nbands), dim3(p.threads), p.lds_bytes, s, a);
+    return hipGetLastError() == hipSuccess ? kOk : kErrHip;
+}
+
+template <typename T, bool FLIP>
+int run_k(const LkArgs<T> &a, const LkPlan &p, int K, int planes, hipStream_t s) {
+    if (p.TC == 8) {
+        if (K == 7) return run_lk<T, 7, 8, FLIP>(a, p, planes, s);
+        if (K == 13) return run_lk<T, 13, 8, FLIP>(a, p, planes, s);
+        return run_lk<T, 31, 8, FLIP>(a, p, planes, s);
+    }
+    if (K == 7) return run_lk<T, 7, 4, FLIP>(a, p, planes, s);
+    if (K == 13) return run_lk<T, 13, 4, FLIP>(a, p, planes, s);
+    return run_lk<T, 31, 4, FLIP>(a, p, planes, s);
+}
+
+template <typename T>
+int lk_fwd_t(const Geo &g, const void *x, const void *w, const void *b, void *y, hipStream_t s) {
+    LkPlan p;
+    if (!plan_lk(g.oh, g.ow, g.kh, p)) return kErrUnsupported;
+    LkArgs<T> a{};
+    a.in = static_cast<const T *>(x);
+    a.w = static_cast<const T *>(w);
+    a.b = static_cast<const T *>(b);
+    a.out = static_cast<T *>(y);
+    a.IH = g.ih;
+    a.IW = g.iw;
+    a.OH = g.oh;
+    a.OW = g.ow;
+    a.P = g.ph;
+    a.C = g.oc;
+    a.mult = g.mult;
+    return run_k<T, false>(a, p, g.kh, g.n * g.oc, s);
+}
+
+template <typename T>
+int lk_bwdin_t(const Geo &g, const void *dy, const void *w, void *dx, hipStream_t s) {
+    LkPlan p;
+    if (!plan_lk(g.ih, g.iw, g.kh, p)) return kErrUnsupported;
+    LkArgs<T> a{};
+    a.in = static_cast<const T *>(dy);
+    a.w = static_cast<const T *>(w);
+    a.out = static_cast<T *>(dx);
+    a.IH = g.oh;
+    a.IW = g.ow;
+    a.OH = g.ih;
+    a.OW = g.iw;
+    a.P = g.kh - 1 - g.ph;
+    a.C = g.ic;
+    a.mult = 1;
+    return run_k<T, true>(a, p, g.kh, g.n * g.ic, s);
+}
+
+
+// ---------------------------------------------------------------- grad-weight
+// dw[c,i,j] = sum_{n,oh,ow} dy[n,c,oh,ow] * xpad[n,c,oh+i,ow+j]: the same sliding
+// correlation with the roles swapped (dy is the long "filter", dw the small
+// output).  A workgroup owns (channel, image chunk); a lane holds a TR x TC
+// tile of dw; the ceil(k/TR)*ceil(k/TC) tiles are replicated over NG lane groups
+// that take every NG-th dy row, and the groups are summed at the end in a
+// fixed order.  Per image the padded x plane and the dy plane are staged in
+// LDS as fp32; a lane reads a 16-byte-vector x window and the dy values (the
+// same for all lanes of a group, so the reads broadcast).
+template <typename T> struct LkwArgs {
+    const T *x;
+    const T *dy;
+    float *ws;     // [c][NC][k*k+1]
+    int C, IH, IW, OH, OW, P;
+    int N, NC, npc;
+    int xpitch;    // LDS pitch of the padded x plane
+    int xrows;     // OH + k - 1
+    int dpitch;    // LDS pitch of the dy plane (multiple of 8)
+    FastDiv fxp, fdp;
+};
+
+template <typename T, int K, int TR, int TC>
+__global__ __launch_bounds__(256) void lk_bwdw_kernel(LkwArgs<T> a) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    constexpr int NRB = (K + TR - 1) / TR, NCB = (K + TC - 1) / TC, NT = NRB * NCB;
+    constexpr int NG = 256 / NT;  // lane groups
+    constexpr int SEG = 8;        // dy columns per step
+    constexpr int XW = SEG + TC - 1, XW4 = (XW + 3) / 4 * 4;
+    float *xs = reinterpret_cast<float *>(smem);
+    float *ds = xs + a.xrows * a.xpitch;
+    const int tid = threadIdx.x;
+    const int c = blockIdx.x / a.NC;
+    const int chunk = blockIdx.x - c * a.NC;
+    const int grp = tid / NT;
+    const int tile = tid - grp * NT;
+    const int rb = tile / NCB, cb = tile - (tile / NCB) * NCB;
+    const bool lane_ok = grp < NG;
+    float acc[TR][TC];
+#pragma unroll
+    for (int tr = 0; tr < TR; ++tr)
+#pragma unroll
+        for (int q = 0; q < TC; ++q) acc[tr][q] = 0.f;
+    float dbs = 0.f;
+    const int n0 = chunk * a.npc, n1 = min(n0 + a.npc, a.N);
+    const int xtot = a.xrows * a.xpitch, dtot = a.OH * a.dpitch;
+    for (int n = n0; n < n1; ++n) {
+        __syncthreads();
+        const T *xp = a.x + (static_cast<int64_t>(n) * a.C + c) * a.IH * a.IW;
+        const T *dp = a.dy + (static_cast<int64_t>(n) * a.C + c) * a.OH * a.OW;
+        for (int e = tid; e < xtot; e += 256) {
+            const int r = static_cast<int>(fdiv(static_cast<uint32_t>(e), a.fxp));
+            const int col = e - r * a.xpitch;
+            const int ih = r - a.P, iw = col - a.P;
+            xs[e] = (ih >= 0 && ih < a.IH && iw >= 0 && iw < a.IW) ? to_f32(xp[ih * a.IW + iw]) : 0.f;
+        }
+        for (int e = tid; e < dtot; e += 256) {
+            const int r = static_cast<int>(fdiv(static_cast<uint32_t>(e), a.fdp));
+            const int col = e - r * a.dpitch;
+            ds[e] = col < a.OW ? to_f32(dp[r * a.OW + col]) : 0.f;
+        }
+        __syncthreads();
+        if (!lane_ok) continue;
+        for (int oh = grp; oh < a.OH; oh += NG) {
+            const float *drow = ds + oh * a.dpitch;
+            for (int s0 = 0; s0 < a.OW; s0 += SEG) {
+                float dv[SEG];
+                const float4 *d4 = reinterpret_cast<const float4 *>(drow + s0);
+#pragma unroll
+                for (int e = 0; e < SEG / 4; ++e) {
+                    const float4 v = d4[e];
+                    dv[4 * e] = v.x;
+                    dv[4 * e + 1] = v.y;
+                    dv[4 * e + 2] = v.z;
+                    dv[4 * e + 3] = v.w;
+                }
+                if (tile == 0) {
+#pragma unroll
+                    for (int u = 0; u < SEG; ++u) dbs += dv[u];
+                }
+#pragma unroll
+                for (int tr = 0; tr < TR; ++tr) {
+                    const int i = rb * TR + tr;
+                    if (i >= K) continue;
+                    float xv[XW4];
+                    const float4 *x4 = reinterpret_cast<const float4 *>(xs + (oh + i) * a.xpitch + cb * TC + s0);
+#pragma unroll
+                    for (int e = 0; e < XW4 / 4; ++e) {
+                        const float4 v = x4[e];
+                        xv[4 * e] = v.x;
+                        xv[4 * e + 1] = v.y;
+                        xv[4 * e + 2] = v.z;
+                        xv[4 * e + 3] = v.w;
+                    }
+#pragma unroll
+                    for (int u = 0; u < SEG; ++u)
+#pragma unroll
+                        for (int q = 0; q < TC; ++q) acc[tr][q] = fmaf(dv[u], xv[u + q], acc[tr][q]);
+                }
+            }
+        }
+    }
+    // fixed-order sum over the lane groups
+    __syncthreads();
+    float *red = xs;  // reuse: [256][TR*TC + 1]
+    constexpr int RS = TR * TC + 1;
+#pragma unroll
+    for (int tr = 0; tr < TR; ++tr)
+#pragma unroll
+        for (int q = 0; q < TC; ++q) red[tid * RS + tr * TC + q] = acc[tr][q];
+    red[tid * RS + TR * TC] = dbs;
+    __syncthreads();
+    float *dst = a.ws + (static_cast<int64_t>(c) * a.NC + chunk) * (K * K + 1);
+    for (int e = tid; e < NT * RS; e += 256) {
+        const int t = e / RS, k = e - (e / RS) * RS;
+        float v = 0.f;
+        for (int gq = 0; gq < NG; ++gq) v += red[(gq * NT + t) * RS + k];
+        if (k == TR * TC) {
+            if (t == 0) dst[K * K] = v;
+            continue;
+        }
+        const int i = (t / NCB) * TR + k / TC, j = (t - (t / NCB) * NCB) * TC + k % TC;
+        if (i < K && j < K) dst[i * K + j] = v;
+    }
+}
+
+struct LkwPlan {
+    int NC, npc, xpitch, xrows, dpitch, lds_bytes;
+};
+
+bool plan_lkw(const Geo &g, int K, LkwPlan &p) {
+    constexpr int TC = 8, SEG = 8;
+    const int owr = (g.ow + SEG - 1) / SEG * SEG;  // dy columns walked (zero beyond ow)
+    p.xrows = g.oh + K - 1;
+    // x window of the last segment and tile: owr + ceil(k/TC)*TC + 3 columns at most
+    p.xpitch = (owr + (K + TC - 1) / TC * TC + 3 + 3) & ~3;
+    p.dpitch = owr;
+    const int64_t bytes = (static_cast<int64_t>(p.xrows) * p.xpitch + static_cast<int64_t>(g.oh) * p.dpitch) * 4;
+    const int64_t red = 256 * (2 * TC + 1) * 4;
+    p.lds_bytes = static_cast<int>(std::max(bytes, red));
+    if (p.lds_bytes > 64 * 1024) return false;
+    // image chunks: about 4 workgroups per CU in total
+    int NC = std::max(1, (1024 + g.ic - 1) / g.ic);
+    NC = std::min(NC, g.n);
+    p.npc = (g.n + NC - 1) / NC;
+    p.NC = (g.n + p.npc - 1) / p.npc;
+    return true;
+}
+
+template <typename T, int K>
+int run_lkw(const Geo &g, const LkwPlan &p, const void *x, const void *dy, void *ws, hipStream_t s) {
+    LkwArgs<T> a{};
+    a.x = static_cast<const T *>(x);
+    a.dy = static_cast<const T *>(dy);
+    a.ws = static_cast<float *>(ws);
+    a.C = g.ic;
+    a.IH = g.ih;
+    a.IW = g.iw;
+    a.OH = g.oh;
+    a.OW = g.ow;
+    a.P = g.ph;
+    a.N = g.n;
+    a.NC = p.NC;
+    a.npc = p.npc;
+    a.xpitch = p.xpitch;
+    a.xrows = p.xrows;
+    a.dpitch = p.dpitch;
+    a.fxp = make_fastdiv(p.xpitch, static_cast<uint64_t>(p.xrows) * p.xpitch + 256);
+    a.fdp = make_fastdiv(p.dpitch, static_cast<uint64_t>(g.oh) * p.dpitch + 256);
+    hipLaunchKernelGGL((lk_bwdw_kernel<T, K, kTR, 8>), dim3(g.ic * p.NC), dim3(256), p.lds_bytes, s, a);
+    return hipGetLastError() == hipSuccess ? kOk : kErrHip;
+}
+
+template <typename T>
+int lk_bwdw_t(const Geo &g, const void *x, const void *dy, void *ws, hipStream_t s) {
+    LkwPlan p;
+    if (!plan_lkw(g, g.kh, p)) return kErrUnsupported;
+    if (g.kh == 7) return run_lkw<T, 7>(g, p, x, dy, ws, s);
+    if (g.kh == 13) return run_lkw<T, 13>(g, p, x, dy, ws, s);
+    return run_lkw<T, 31>(g, p, x, dy, ws, s);
+}
+
+}  // namespace
+
+bool largek_bwdw_fits(const Geo &g) {
+    if (g.kh != g.kw || (g.kh != 7 && g.kh != 13 && g.kh != 31)) return false;
+    if (g.sh != 1 || g.sw != 1 || g.dh != 1 || g.dw != 1 || g.ph != g.pw || g.mult != 1) return false;
+    LkwPlan p;
+    return plan_lkw(g, g.kh, p);
+}
+
+int largek_bwd_weight_chunks(const Geo &g) {
+    LkwPlan p;
+    return plan_lkw(g, g.kh, p) ? p.NC : 0;
+}
+
+int largek_bwd_weight(const Geo &g, const void *x, const void *dy, void *ws, int dtype, hipStream_t s) {
+    switch (dtype) {
+        case 0: return lk_bwdw_t<float>(g, x, dy, ws, s);
+        case 1: return lk_bwdw_t<__half>(g, x, dy, ws, s);
+        default: return lk_bwdw_t<bf16_t>(g, x, dy, ws, s);
+    }
+}
+
+namespace {
+}  // namespace
+
+bool largek_fits(const Geo &g, int pass) {
+    if (g.kh != g.kw || (g.kh != 7 && g.kh != 13 && g.kh != 31)) return false;
+    if (g.sh != 1 || g.sw != 1 || g.dh != 1 || g.dw != 1 || g.ph != g.pw) return false;
+    if (pass == 1 && (g.mult != 1 || g.ph > g.kh - 1)) return false;
+    LkPlan p;
+    return pass == 1 ? plan_lk(g.ih, g.iw, g.kh, p) : plan_lk(g.oh, g.ow, g.kh, p);
+}
+
+int largek_fwd(const Geo &g, const void *x, const void *w, const void *b, void *y, int dtype, hipStream_t s) {
+    switch (dtype) {
+        case 0: return lk_fwd_t<float>(g, x, w, b, y, s);
+        case 1: return lk_fwd_t<__half>(g, x, w, b, y, s);
+        default: return lk_fwd_t<bf16_t>(g, x, w, b, y, s);
+    }
+}
+
+int largek_bwd_input(const Geo &g, const void *dy, const void *w, void *dx, int dtype, hipStream_t s) {
+    switch (dtype) {
+        case 0: return lk_bwdin_t<float>(g, dy, w, dx, s);
+        case 1: return lk_bwdin_t<__half>(g, dy, w, dx, s);
+        default: return lk_bwdin_t<bf16_t>(g, dy, w, dx, s);
+    }
+}
+
+}  // namespace dw

@@ -386,3 +386,18 @@ def test_graph_replay_matches_eager():
         for a_, b_ in zip(got, ref):
             for t1, t2 in zip(a_, b_):
                 assert torch.equal(t1, t2), "replay %d differs from eager" % rep
+
+
+# ------------------------------------------------------------------ large-kernel path edges
+@pytest.mark.parametrize("n,c,h,w,mult,k,p,dt", [
+    (2, 3, 37, 50, 1, 7, 3, "f32"),      # ragged sizes, column tile of 4
+    (1, 2, 20, 70, 1, 13, 0, "f32"),     # no padding
+    (1, 2, 40, 33, 1, 13, 12, "f32"),    # pad k-1: grad-input pad 0
+    (1, 2, 64, 64, 2, 31, 15, "f32"),    # multiplier 2 (forward register tiles, others fall back)
+    (1, 3, 48, 48, 1, 31, 15, "bf16"),
+    (2, 2, 9, 9, 1, 31, 15, "f16"),      # kernel wider than the image
+    (1, 1, 130, 24, 1, 7, 3, "f32"),     # several row bands
+])
+def test_large_kernel_shapes(n, c, h, w, mult, k, p, dt):
+    x, wt, b, dy = static_case(n, c, h, w, mult, k, 1, p, 1, DT[dt], 650 + h + w + k)
+    check_static(x, wt, b, dy, 1, p, 1, "largek n%d c%d %dx%d m%d k%d p%d %s" % (n, c, h, w, mult, k, p, dt))
