@@ -60,6 +60,13 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline leg")
     ap.add_argument("--eager", action="store_true", help="launch call by call instead of replaying HIP graphs")
+    ap.add_argument("--only-tag", default=None, help="run only the calls of this kernel tag (for counter runs)")
+    ap.add_argument("--copy-ref", action="store_true",
+                    help="also run a plain 256 MiB device copy (counter calibration)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
+                    help="write profiles/traffic_<--only-tag>.json from two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--launches", type=int, default=0, help="calls of the tag in the counter runs")
+    ap.add_argument("--cmd", default="", help="command recorded with the traffic figures")
     return ap.parse_args()
 
 
@@ -95,7 +102,7 @@ class Call:
 def static_calls(dc, case, dev, seed, passes=("fwd", "bwd_in", "bwd_w")):
     import torch
     from dynamic_convolution_amd import synth
-    n, c, h, M, k, s, p, d, dtype, dists, tagbase, with_bias = case
+    n, c, h, M, k, s, p, d, dtype, dists, _label, with_bias = case
     e = torch.empty(0, dtype=dtype).element_size()
     x = synth.draw((n, c, h, h), dists["x"], seed, "x", dtype, device=dev)
     w = synth.draw((c * M, k, k), dists["w"], seed, "w", dtype, device=dev)
@@ -113,13 +120,21 @@ def static_calls(dc, case, dev, seed, passes=("fwd", "bwd_in", "bwd_w")):
     X, W, B, Y = x.numel() * e, w.numel() * e, (c * M * e if with_bias else 0), y.numel() * e
     macs = n * c * M * valid_taps(h, oh, k, s, p, d) ** 2
     calls = []
+    dts = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}[dtype]
+
+    def tag(pi, name):
+        # one tag = one kernel instantiation: the library's algorithm for this geometry,
+        # plus the template parameters it is specialised on
+        algo = dc.dwconv2d_algo(pi, x.shape, w.shape, s, p, d, dtype)
+        return "%s.%s.k%d_s%d_m%d_%s" % (name, algo, k, s, M, dts)
+
     if "fwd" in passes:
-        calls.append(Call(tagbase + "fwd", lambda: dc.dwconv2d_fwd(x, w, b, s, p, d, out=y), sx + W + B + Y, 2 * macs))
+        calls.append(Call(tag(0, "fwd"), lambda: dc.dwconv2d_fwd(x, w, b, s, p, d, out=y), sx + W + B + Y, 2 * macs))
     if "bwd_in" in passes:
-        calls.append(Call(tagbase + "bwd_input", lambda: dc.dwconv2d_bwd_input(dy, w, x.shape, s, p, d, out=dx),
+        calls.append(Call(tag(1, "bwd_input"), lambda: dc.dwconv2d_bwd_input(dy, w, x.shape, s, p, d, out=dx),
                           Y + W + X, 2 * macs))
     if "bwd_w" in passes:
-        calls.append(Call(tagbase + "bwd_weight",
+        calls.append(Call(tag(2, "bwd_weight"),
                           lambda: dc.dwconv2d_bwd_weight(x, dy, w.shape, s, p, d, with_bias=with_bias, out=gw,
                                                          out_bias=gb, workspace=ws),
                           sx + Y + W + B, 2 * macs))
@@ -198,7 +213,7 @@ def build_dynamic(dc, dev):
                 y = torch.empty((n, 3 * D["c"], h, h), dtype=dtype, device=dev)
                 taps = sum(valid_taps(h, h, 3, 1, dd, dd) ** 2 for dd in D["dilations"])
                 nbytes = x.numel() * e + n * D["c"] * taps * e + y.numel() * e
-                cl = Call("dyn_%s_" % dts, (lambda x=x, fs=fs, y=y: dc.dynconv_multidil_fwd(x, fs, D["dilations"], out=y)),
+                cl = Call("dyn.fused.k3_%s" % dts, (lambda x=x, fs=fs, y=y: dc.dynconv_multidil_fwd(x, fs, D["dilations"], out=y)),
                           nbytes, 2 * n * D["c"] * taps)
                 calls.append(cl)
                 per_case.append(([cl], dict(x=x, fs=fs, y=y)))
@@ -240,9 +255,9 @@ def cpu_baseline(wl, target_s):
             x, w, dy = f64(t["x"][:sl]), f64(t["w"]), f64(t["dy"][:sl])
             for cl in calls:
                 t0 = time.perf_counter()
-                if cl.tag.endswith("fwd"):
+                if cl.tag.startswith("fwd."):
                     O.dwconv2d_fwd(x, w, None, s, p, d)
-                elif cl.tag.endswith("bwd_input"):
+                elif cl.tag.startswith("bwd_input."):
                     O.dwconv2d_bwd_input(dy, w, x.shape, s, p, d)
                 else:
                     O.dwconv2d_bwd_weight(x, dy, w.shape, s, p, d, with_bias=False)
@@ -266,27 +281,75 @@ def cpu_baseline(wl, target_s):
 
 
 # ---------------------------------------------------------------- traffic from committed counters
-def committed_traffic(tag, kernel_src):
-    """HBM bytes per launch from profiles/traffic_<tag>.json when the kernel source is unchanged."""
-    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % tag)
+COPY_REF_BYTES = 256 << 20  # bytes read (and written) by one reference copy
+
+
+def kernel_sources_sha256():
+    """Hash of every kernel source: counters are valid only for the code they were taken on."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "dynamic_convolution_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def traffic_path(tag):
+    return os.path.join(ROOT, "profiles", "traffic_%s.json" % tag.replace("/", "_"))
+
+
+def committed_traffic(tag):
+    """HBM bytes per launch from profiles/traffic_<tag>.json when the kernel sources are unchanged."""
+    path = traffic_path(tag)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    h = hashlib.sha256(open(os.path.join(ROOT, kernel_src), "rb").read()).hexdigest()
-    if rec.get("source_sha256") != h:
+    if rec.get("source_sha256") != kernel_sources_sha256():
         return None
     return rec.get("bytes_per_launch")
 
 
-KERNEL_SRC = {"fwd": "dynamic_convolution_amd/csrc/dw_fwd.hip",
-              "bwd_input": "dynamic_convolution_amd/csrc/dw_bwd_input.hip",
-              "bwd_weight": "dynamic_convolution_amd/csrc/dw_bwd_weight.hip",
-              "dyn": "dynamic_convolution_amd/csrc/dw_dynconv.hip"}
+def read_counter_csv(path, counter):
+    """Per-dispatch (kernel name, value) of one counter from a rocprofv3 counter_collection.csv."""
+    import csv
+    rows = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r.get("Counter_Name") == counter:
+                rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def traffic_from(fetch_csv, write_csv, tag, launches, cmd):
+    """Scale FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of this library's kernels by the
+    reference copy's reading and write profiles/traffic_<tag>.json."""
+    out = {"tag": tag, "source_sha256": kernel_sources_sha256(), "command": cmd}
+    for key, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
+        rows = read_counter_csv(path, counter)
+        mine = [v for name, v in rows if "dw::" in name]
+        # the reference copy is torch's elementwise copy kernel; the largest such dispatches
+        refs = sorted((v for name, v in rows if "dw::" not in name and "copy" in name.lower()), reverse=True)[:3]
+        if not mine or not refs:
+            raise SystemExit("no %s rows for this library or the reference copy in %s" % (counter, path))
+        ref_kib = sum(refs) / len(refs)
+        scale = (COPY_REF_BYTES / 1024.0) / ref_kib
+        out[key + "_kib_raw"] = sum(mine)
+        out[key + "_ref_copy_kib"] = ref_kib
+        out[key + "_scale"] = scale
+        out[key + "_bytes_per_launch"] = sum(mine) * 1024.0 * scale / launches
+    out["launches"] = launches
+    out["bytes_per_launch"] = out["fetch_bytes_per_launch"] + out["write_bytes_per_launch"]
+    with open(traffic_path(tag), "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
 
 
 def main():
     args = parse()
+    if args.traffic_from:
+        traffic_from(args.traffic_from[0], args.traffic_from[1], args.only_tag, args.launches, args.cmd)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
@@ -301,6 +364,10 @@ def main():
     torch.cuda.set_device(dev)
     wl = build_workload(args.workload, dc, dev)
     calls = wl["calls"]
+    if args.only_tag:
+        calls = [cl for cl in calls if cl.tag == args.only_tag]
+        if not calls:
+            raise SystemExit("no call has tag %r; tags: %s" % (args.only_tag, sorted({c.tag for c in wl["calls"]})))
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
 
@@ -345,6 +412,15 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
+    executed = len(calls) * (max(1, args.warmup) + (0 if args.eager else args.warmup) + args.steps)
+    if args.copy_ref:
+        src = torch.empty(COPY_REF_BYTES // 4, dtype=torch.float32, device=dev).normal_()
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     step_bytes = sum(cl.nbytes for cl in calls)
     step_flops = sum(cl.flops for cl in calls)
     ms_step = elapsed / args.steps * 1e3
@@ -375,9 +451,8 @@ def main():
         achieved = dom["flops"] / dom["launches"] / avg_s / 1e12
         roof = {"bound": "alu", "achieved": round(achieved, 2), "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / FP32_VALU_PEAK_TFLOPS, 4)}
-    src_key = next(k for k in KERNEL_SRC if k in dom_tag)
-    roof["traffic"] = committed_traffic(dom_tag.rstrip("_"), KERNEL_SRC[src_key])
-    roof["kernel"] = dom_tag.rstrip("_")
+    roof["traffic"] = committed_traffic(dom_tag)
+    roof["kernel"] = dom_tag
     roof["avg_launch_us"] = round(avg_s * 1e6, 2)
 
     out = {
@@ -391,7 +466,8 @@ def main():
         "gbs": round(step_bytes / (elapsed / args.steps) / 1e9, 2),
         "gflops": round(step_flops / (elapsed / args.steps) / 1e9, 2),
         "roofline": roof,
-        "per_kernel": {t.rstrip("_"): {"avg_us": round(r["ms"] / r["launches"] * 1e3, 2),
+        "launches_executed": executed,
+        "per_kernel": {t: {"avg_us": round(r["ms"] / r["launches"] * 1e3, 2),
                                        "share": round(r["ms"] / sum(v["ms"] for v in per_tag.values()), 4),
                                        "gbs": round(r["bytes"] / (r["ms"] / 1e3) / 1e9, 1),
                                        "gflops": round(r["flops"] / (r["ms"] / 1e3) / 1e9, 1)}

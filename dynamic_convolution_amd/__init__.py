@@ -14,6 +14,7 @@ ABI's names:
 """
 from ._native import (  # noqa: F401
     DwconvError,
+    dwconv2d_algo,
     dwconv2d_bwd_input,
     dwconv2d_bwd_weight,
     dwconv2d_bwd_weight_workspace_bytes,

@@ -24,7 +24,7 @@ STATUS = {
 EXPORTS = (
     "dwconv2d_out_size", "dwconv2d_fwd", "dwconv2d_bwd_input",
     "dwconv2d_bwd_weight_workspace_bytes", "dwconv2d_bwd_weight",
-    "dynconv_multidil_fwd", "dw_status_str",
+    "dynconv_multidil_fwd", "dwconv2d_algo", "dw_status_str",
 )
 
 _I64 = ctypes.c_int64
@@ -65,6 +65,8 @@ def lib() -> ctypes.CDLL:
                                        ctypes.c_int32, _VP, _I64, _I64, _I64, _I64, _I64,
                                        ctypes.c_int, _VP]
     L.dynconv_multidil_fwd.restype = ctypes.c_int
+    L.dwconv2d_algo.argtypes = [ctypes.c_int] + _GEO + [ctypes.c_int]
+    L.dwconv2d_algo.restype = ctypes.c_char_p
     L.dw_status_str.argtypes = [ctypes.c_int]
     L.dw_status_str.restype = ctypes.c_char_p
     _lib = L
@@ -128,6 +130,16 @@ def dwconv2d_out_size(x_shape, w_shape, stride=1, padding=0, dilation=1):
     _check(lib().dwconv2d_out_size(*_geo(x_shape, w_shape, stride, padding, dilation),
                                    ctypes.byref(oh), ctypes.byref(ow)), "dwconv2d_out_size")
     return oh.value, ow.value
+
+
+def dwconv2d_algo(pass_, x_shape, w_shape, stride=1, padding=0, dilation=1, dtype=None):
+    """Kernel family pass_ (0 fwd, 1 grad-input, 2 grad-weight) launches for this geometry."""
+    import torch
+    code = _dtype_code(torch.empty(0, dtype=dtype or torch.float32))
+    r = lib().dwconv2d_algo(int(pass_), *_geo(x_shape, w_shape, stride, padding, dilation), code)
+    if r is None:
+        raise ValueError("invalid pass, dtype or geometry")
+    return r.decode()
 
 
 def dwconv2d_bwd_weight_workspace_bytes(x_shape, w_shape, stride=1, padding=0, dilation=1, dtype=None):

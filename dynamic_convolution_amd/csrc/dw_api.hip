@@ -209,6 +209,21 @@ int dynconv_multidil_fwd(const void *x, const void *const *filters, const int32_
                                          static_cast<hipStream_t>(stream)));
 }
 
+const char *dwconv2d_algo(int pass, int64_t n, int64_t ic, int64_t ih, int64_t iw, int64_t oc, int64_t kh,
+                          int64_t kw, int64_t stride_h, int64_t stride_w, int64_t pad_h, int64_t pad_w,
+                          int64_t dil_h, int64_t dil_w, int dtype) {
+    if (dtype != DW_F32 && dtype != DW_F16 && dtype != DW_BF16) return nullptr;
+    dw::Geo g;
+    if (check_geometry(n, ic, ih, iw, oc, kh, kw, stride_h, stride_w, pad_h, pad_w, dil_h, dil_w, &g) != DW_OK)
+        return nullptr;
+    switch (pass) {
+        case 0: return dw::fwd_supported(g, dtype) ? dw::fwd_algo_name(g, dtype) : nullptr;
+        case 1: return dw::bwd_input_supported(g, dtype) ? dw::bwd_input_algo_name(g, dtype) : nullptr;
+        case 2: return dw::bwd_weight_workspace(g, dtype) >= 0 ? dw::bwd_weight_algo_name(g, dtype) : nullptr;
+        default: return nullptr;
+    }
+}
+
 const char *dw_status_str(int status) {
     switch (status) {
         case DW_OK: return "ok";

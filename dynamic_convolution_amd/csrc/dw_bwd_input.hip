@@ -238,23 +238,45 @@ int run_bwd_input(const Geo &g, const BandPlan &bp, int seg_slots, const void *d
     return hipGetLastError() == hipSuccess ? kOk : kErrHip;
 }
 
+enum BinAlgo { kBinRowwalk = 0, kBinLargek, kBinBand33s1, kBinBand33s2, kBinBand55s1, kBinBand55s2d2, kBinBandGeneric };
+
+// The kernel family a grad-input call launches.
+int select_bwd_input(const Geo &g, int dt) {
+    if (rowwalk_fits(g, dt, 1)) return kBinRowwalk;
+    if (largek_fits(g, 1)) return kBinLargek;
+    const bool sq = g.kh == g.kw && g.sh == g.sw && g.dh == g.dw;
+    if (sq && g.kh == 3 && g.sh == 1 && g.dh == 1) return kBinBand33s1;
+    if (sq && g.kh == 3 && g.sh == 2 && g.dh == 1) return kBinBand33s2;
+    if (sq && g.kh == 5 && g.sh == 1 && g.dh == 1) return kBinBand55s1;
+    if (sq && g.kh == 5 && g.sh == 2 && g.dh == 2) return kBinBand55s2d2;
+    return kBinBandGeneric;
+}
+
 template <typename T>
 int dispatch_bwd_input(const Geo &g, const void *dy, const void *w, void *dx, hipStream_t s) {
     const int dt = sizeof(T) == 4 ? 0 : (std::is_same<T, __half>::value ? 1 : 2);
-    if (rowwalk_fits(g, dt, 1)) return rowwalk_bwd_input(g, dy, w, dx, dt, s);
-    if (largek_fits(g, 1)) return largek_bwd_input(g, dy, w, dx, dt, s);
+    const int algo = select_bwd_input(g, dt);
+    if (algo == kBinRowwalk) return rowwalk_bwd_input(g, dy, w, dx, dt, s);
+    if (algo == kBinLargek) return largek_bwd_input(g, dy, w, dx, dt, s);
     BandPlan bp;
     int seg_slots = 0;
     if (!plan_bwd_input<T>(g, bp, seg_slots)) return kErrUnsupported;
-    const bool sq = g.kh == g.kw && g.sh == g.sw && g.dh == g.dw;
-    if (sq && g.kh == 3 && g.sh == 1 && g.dh == 1) return run_bwd_input<T, 3, 3, 1, 1>(g, bp, seg_slots, dy, w, dx, s);
-    if (sq && g.kh == 3 && g.sh == 2 && g.dh == 1) return run_bwd_input<T, 3, 3, 2, 1>(g, bp, seg_slots, dy, w, dx, s);
-    if (sq && g.kh == 5 && g.sh == 1 && g.dh == 1) return run_bwd_input<T, 5, 5, 1, 1>(g, bp, seg_slots, dy, w, dx, s);
-    if (sq && g.kh == 5 && g.sh == 2 && g.dh == 2) return run_bwd_input<T, 5, 5, 2, 2>(g, bp, seg_slots, dy, w, dx, s);
-    return run_bwd_input<T, 0, 0, 0, 0>(g, bp, seg_slots, dy, w, dx, s);
+    switch (algo) {
+        case kBinBand33s1: return run_bwd_input<T, 3, 3, 1, 1>(g, bp, seg_slots, dy, w, dx, s);
+        case kBinBand33s2: return run_bwd_input<T, 3, 3, 2, 1>(g, bp, seg_slots, dy, w, dx, s);
+        case kBinBand55s1: return run_bwd_input<T, 5, 5, 1, 1>(g, bp, seg_slots, dy, w, dx, s);
+        case kBinBand55s2d2: return run_bwd_input<T, 5, 5, 2, 2>(g, bp, seg_slots, dy, w, dx, s);
+        default: return run_bwd_input<T, 0, 0, 0, 0>(g, bp, seg_slots, dy, w, dx, s);
+    }
 }
 
 }  // namespace
+
+const char *bwd_input_algo_name(const Geo &g, int dtype) {
+    static const char *names[] = {"rowwalk_3x3",    "largek_regtile", "band_3x3_s1",   "band_3x3_s2",
+                                  "band_5x5_s1",    "band_5x5_s2_d2", "band_generic"};
+    return names[select_bwd_input(g, dtype)];
+}
 
 bool bwd_input_supported(const Geo &g, int dtype) {
     if (rowwalk_fits(g, dtype, 1) || largek_fits(g, 1)) return true;

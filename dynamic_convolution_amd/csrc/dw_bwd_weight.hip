@@ -392,15 +392,27 @@ int run_small(const Geo &g, const BwPlan &p, const void *x, const void *dy, void
     return hipGetLastError() == hipSuccess ? kOk : kErrHip;
 }
 
+enum BwAlgo { kBwChannelGroup = 0, kBwLargek, kBwRowwalk, kBwBandPixel, kBwBandTaps };
+
+// The pass-1 kernel family a grad-weight call launches (pass 2 is always the
+// fixed-order chunk reduction).
+int select_bwd_weight(const Geo &g, int dt) {
+    if (small_fits(g, dt, 2)) return kBwChannelGroup;
+    if (largek_bwdw_fits(g)) return kBwLargek;
+    if (rowwalk_fits(g, dt, 2)) return kBwRowwalk;
+    return small_variant(g) ? kBwBandPixel : kBwBandTaps;
+}
+
 template <typename T>
 int dispatch_bwd_weight(const Geo &g, const void *x, const void *dy, void *dwt, void *db, void *ws,
                         hipStream_t s) {
     const int dt = sizeof(T) == 4 ? 0 : (std::is_same<T, __half>::value ? 1 : 2);
     const int kk = g.kh * g.kw;
     int NC, nslots, rc;
-    const bool small = small_fits(g, dt, 2);
-    const bool large = !small && largek_bwdw_fits(g);
-    if (small || large || rowwalk_fits(g, dt, 2)) {
+    const int algo = select_bwd_weight(g, dt);
+    const bool small = algo == kBwChannelGroup;
+    const bool large = algo == kBwLargek;
+    if (small || large || algo == kBwRowwalk) {
         // channel-group (small planes), register-tile (large k) or streaming (3x3, pad 1)
         // pass 1: workspace [ic][NC][M*(kk+1)]
         NC = small ? small_bwd_weight_chunks(g, dt) : large ? largek_bwd_weight_chunks(g) : rowwalk_bwd_weight_chunks(g, dt);
@@ -443,19 +455,17 @@ int dispatch_bwd_weight(const Geo &g, const void *x, const void *dy, void *dwt, 
 
 }  // namespace
 
+const char *bwd_weight_algo_name(const Geo &g, int dtype) {
+    static const char *names[] = {"channelgroup_small", "largek_regtile", "rowwalk_3x3", "band_pixel", "band_taps"};
+    return names[select_bwd_weight(g, dtype)];
+}
+
 int64_t bwd_weight_workspace(const Geo &g, int dtype) {
-    if (small_fits(g, dtype, 2)) {
-        const int NC = small_bwd_weight_chunks(g, dtype);
-        return std::max<int64_t>(static_cast<int64_t>(g.ic) * NC * g.mult * (g.kh * g.kw + 1) * 4, 16);
-    }
-    if (largek_bwdw_fits(g)) {
-        const int NC = largek_bwd_weight_chunks(g);
-        return std::max<int64_t>(static_cast<int64_t>(g.ic) * NC * (g.kh * g.kw + 1) * 4, 16);
-    }
-    if (rowwalk_fits(g, dtype, 2)) {
-        const int NC = rowwalk_bwd_weight_chunks(g, dtype);
-        return std::max<int64_t>(static_cast<int64_t>(g.ic) * NC * g.mult * 10 * 4, 16);
-    }
+    const int algo = select_bwd_weight(g, dtype);
+    const int64_t slots = static_cast<int64_t>(g.mult) * (g.kh * g.kw + 1);
+    if (algo == kBwChannelGroup) return std::max<int64_t>(g.ic * small_bwd_weight_chunks(g, dtype) * slots * 4, 16);
+    if (algo == kBwLargek) return std::max<int64_t>(g.ic * largek_bwd_weight_chunks(g) * slots * 4, 16);
+    if (algo == kBwRowwalk) return std::max<int64_t>(g.ic * rowwalk_bwd_weight_chunks(g, dtype) * slots * 4, 16);
     BwPlan p;
     if (!plan_bwd_weight(g, dtype == 0 ? 4 : 2, p)) return -1;
     return std::max<int64_t>(p.ws_bytes, 16);

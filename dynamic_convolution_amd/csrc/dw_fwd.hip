@@ -238,22 +238,45 @@ int run_fwd(const Geo &g, const BandPlan &bp, const void *x, const void *w, cons
     return hipGetLastError() == hipSuccess ? kOk : kErrHip;
 }
 
+enum FwdAlgo { kFwdRowwalk = 0, kFwdLargek, kFwdBand33s1, kFwdBand33s2, kFwdBand55s1, kFwdBand55s2d2, kFwdBandGeneric };
+
+// The kernel family a forward call launches (the dispatcher and the
+// introspection helper both use this one decision).
+int select_fwd(const Geo &g, int dt) {
+    if (rowwalk_fits(g, dt, 0)) return kFwdRowwalk;
+    if (largek_fits(g, 0)) return kFwdLargek;
+    const bool sq = g.kh == g.kw && g.sh == g.sw && g.dh == g.dw;
+    if (sq && g.kh == 3 && g.sh == 1 && g.dh == 1) return kFwdBand33s1;
+    if (sq && g.kh == 3 && g.sh == 2 && g.dh == 1) return kFwdBand33s2;
+    if (sq && g.kh == 5 && g.sh == 1 && g.dh == 1) return kFwdBand55s1;
+    if (sq && g.kh == 5 && g.sh == 2 && g.dh == 2) return kFwdBand55s2d2;
+    return kFwdBandGeneric;
+}
+
 template <typename T>
 int dispatch_fwd(const Geo &g, const void *x, const void *w, const void *b, void *y, hipStream_t s) {
     const int dt = sizeof(T) == 4 ? 0 : (std::is_same<T, __half>::value ? 1 : 2);
-    if (rowwalk_fits(g, dt, 0)) return rowwalk_fwd(g, x, w, b, y, dt, s);
-    if (largek_fits(g, 0)) return largek_fwd(g, x, w, b, y, dt, s);
+    const int algo = select_fwd(g, dt);
+    if (algo == kFwdRowwalk) return rowwalk_fwd(g, x, w, b, y, dt, s);
+    if (algo == kFwdLargek) return largek_fwd(g, x, w, b, y, dt, s);
     BandPlan bp;
     if (!plan_fwd<T>(g, bp)) return kErrUnsupported;
-    const bool sq = g.kh == g.kw && g.sh == g.sw && g.dh == g.dw;
-    if (sq && g.kh == 3 && g.sh == 1 && g.dh == 1) return run_fwd<T, 3, 3, 1, 1, 1, 1>(g, bp, x, w, b, y, s);
-    if (sq && g.kh == 3 && g.sh == 2 && g.dh == 1) return run_fwd<T, 3, 3, 2, 2, 1, 1>(g, bp, x, w, b, y, s);
-    if (sq && g.kh == 5 && g.sh == 1 && g.dh == 1) return run_fwd<T, 5, 5, 1, 1, 1, 1>(g, bp, x, w, b, y, s);
-    if (sq && g.kh == 5 && g.sh == 2 && g.dh == 2) return run_fwd<T, 5, 5, 2, 2, 2, 2>(g, bp, x, w, b, y, s);
-    return run_fwd<T, 0, 0, 0, 0, 0, 0>(g, bp, x, w, b, y, s);
+    switch (algo) {
+        case kFwdBand33s1: return run_fwd<T, 3, 3, 1, 1, 1, 1>(g, bp, x, w, b, y, s);
+        case kFwdBand33s2: return run_fwd<T, 3, 3, 2, 2, 1, 1>(g, bp, x, w, b, y, s);
+        case kFwdBand55s1: return run_fwd<T, 5, 5, 1, 1, 1, 1>(g, bp, x, w, b, y, s);
+        case kFwdBand55s2d2: return run_fwd<T, 5, 5, 2, 2, 2, 2>(g, bp, x, w, b, y, s);
+        default: return run_fwd<T, 0, 0, 0, 0, 0, 0>(g, bp, x, w, b, y, s);
+    }
 }
 
 }  // namespace
+
+const char *fwd_algo_name(const Geo &g, int dtype) {
+    static const char *names[] = {"rowwalk_3x3",    "largek_regtile", "band_3x3_s1",   "band_3x3_s2",
+                                  "band_5x5_s1",    "band_5x5_s2_d2", "band_generic"};
+    return names[select_fwd(g, dtype)];
+}
 
 bool fwd_supported(const Geo &g, int dtype) {
     if (rowwalk_fits(g, dtype, 0) || largek_fits(g, 0)) return true;

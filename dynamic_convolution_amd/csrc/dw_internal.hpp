@@ -62,6 +62,11 @@ bool largek_bwdw_fits(const Geo &g);
 int largek_bwd_weight_chunks(const Geo &g);
 int largek_bwd_weight(const Geo &g, const void *x, const void *dy, void *ws, int dtype, hipStream_t s);
 
+// Name of the kernel family each pass would launch for this geometry.
+const char *fwd_algo_name(const Geo &g, int dtype);
+const char *bwd_input_algo_name(const Geo &g, int dtype);
+const char *bwd_weight_algo_name(const Geo &g, int dtype);
+
 // Shape checks the launchers need beyond argument validation (LDS fit).
 bool fwd_supported(const Geo &g, int dtype);
 bool bwd_input_supported(const Geo &g, int dtype);

@@ -166,6 +166,18 @@ int dynconv_multidil_fwd(const void *x, const void *const *filters,
                          int64_t n, int64_t c, int64_t h, int64_t w, int64_t k,
                          int dtype, void *stream);
 
+/*
+ * Kernel family a call would launch for this geometry and dtype (for
+ * profiling and per-shape tuning; the same decision the compute calls make).
+ * pass: 0 = dwconv2d_fwd, 1 = dwconv2d_bwd_input, 2 = dwconv2d_bwd_weight.
+ * Returns a static string, or NULL for an invalid pass, dtype or geometry.
+ * Host only; launches nothing.
+ */
+const char *dwconv2d_algo(int pass, int64_t n, int64_t ic, int64_t ih, int64_t iw,
+                          int64_t oc, int64_t kh, int64_t kw,
+                          int64_t stride_h, int64_t stride_w, int64_t pad_h, int64_t pad_w,
+                          int64_t dil_h, int64_t dil_w, int dtype);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char *dw_status_str(int status);
 
