@@ -234,11 +234,37 @@ __global__ __launch_bounds__(kThreads) void rw_conv3_kernel(RwArgs<T> a) {
 //   dx[2r+1][2c  ] = w01 dy[r+1][c] + w21 dy[r][c]
 //   dx[2r+1][2c+1] = w00 dy[r+1][c+1] + w02 dy[r+1][c] + w20 dy[r][c+1] + w22 dy[r][c]
 // (summed over the M output planes of the input channel; dy outside its plane
-// is zero).  A lane owns dy columns [c0, c0+RW) and writes dx columns
-// [2c0, 2c0+2RW) of dx rows 2r and 2r+1 while walking dy rows r.
+// is zero).  dx is four times dy, so the kernel is store-bound: a lane owns the
+// DRW = RW/2 dy columns [c0, c0+DRW) and writes the RW dx columns [2c0, 2c0+RW)
+// of dx rows 2r and 2r+1 as one 16-byte store each, so every store instruction
+// of a wave covers one contiguous run of dx.
+template <typename T, int DRW>
+__device__ __forceinline__ void load_half(const T *plane, int r, int H, int W, int c0, bool vec, bool act,
+                                          float (&v)[DRW]) {
+    static_assert(sizeof(T) * DRW == 8, "half strip is 8 bytes");
+#pragma unroll
+    for (int e = 0; e < DRW; ++e) v[e] = 0.f;
+    if (!act || r < 0 || r >= H) return;
+    const T *p = plane + static_cast<int64_t>(r) * W + c0;
+    if (vec && c0 + DRW <= W) {
+        union {
+            uint2 u;
+            T t[DRW];
+        } b;
+        b.u = *reinterpret_cast<const uint2 *>(p);
+#pragma unroll
+        for (int e = 0; e < DRW; ++e) v[e] = to_f32(b.t[e]);
+    } else {
+#pragma unroll
+        for (int e = 0; e < DRW; ++e)
+            if (c0 + e < W) v[e] = to_f32(p[e]);
+    }
+}
+
 template <typename T, int MM>
 __global__ __launch_bounds__(kThreads) void rw_bwdin3_s2_kernel(RwArgs<T> a) {
     constexpr int RW = Vec<T>::N;
+    constexpr int DRW = RW / 2;
     const Geo &g = a.g;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -248,7 +274,7 @@ __global__ __launch_bounds__(kThreads) void rw_bwdin3_s2_kernel(RwArgs<T> a) {
     const bool act = slot < a.SPW && unit < a.nunits;
     const int P = act ? unit / a.nbands : 0;
     const int band = act ? unit - P * a.nbands : 0;
-    const int c0 = s * RW;
+    const int c0 = s * DRW;
     const bool has_right = s < a.NS - 1;
     const int ic = P % g.ic;
     float wt[MM][9];
@@ -263,41 +289,41 @@ __global__ __launch_bounds__(kThreads) void rw_bwdin3_s2_kernel(RwArgs<T> a) {
     const int r0 = band * a.BH;
     // dy row r (cur) and r+1 (nxt), each with the right neighbour column; the
     // raw segment of row r+2 is loaded one step ahead (pre)
-    float cur[MM][RW + 1], nxt[MM][RW + 1], pre[MM][RW];
+    float cur[MM][DRW + 1], nxt[MM][DRW + 1], pre[MM][DRW];
     const bool vin = a.vin != 0;
 #pragma unroll
     for (int m = 0; m < MM; ++m) {
-        float v[RW];
-        load_seg<T, RW>(dp[m], r0, g.oh, g.ow, c0, vin, act, v);
+        float v[DRW];
+        load_half<T, DRW>(dp[m], r0, g.oh, g.ow, c0, vin, act, v);
         const float rr = __shfl(v[0], lane + 1, 64);
 #pragma unroll
-        for (int e = 0; e < RW; ++e) cur[m][e] = v[e];
-        cur[m][RW] = has_right ? rr : 0.f;
-        load_seg<T, RW>(dp[m], r0 + 1, g.oh, g.ow, c0, vin, act, pre[m]);
+        for (int e = 0; e < DRW; ++e) cur[m][e] = v[e];
+        cur[m][DRW] = has_right ? rr : 0.f;
+        load_half<T, DRW>(dp[m], r0 + 1, g.oh, g.ow, c0, vin, act, pre[m]);
     }
     // dx rows 2r and 2r+1 for r in the band; the band covers dx rows [2*r0, 2*(r0+BH))
     for (int step = 0; step < a.BH; ++step) {
         const int r = r0 + step;
 #pragma unroll
         for (int m = 0; m < MM; ++m) {
-            float v[RW];
+            float v[DRW];
 #pragma unroll
-            for (int e = 0; e < RW; ++e) v[e] = pre[m][e];
-            load_seg<T, RW>(dp[m], r + 2, g.oh, g.ow, c0, vin, act, pre[m]);
+            for (int e = 0; e < DRW; ++e) v[e] = pre[m][e];
+            load_half<T, DRW>(dp[m], r + 2, g.oh, g.ow, c0, vin, act, pre[m]);
             const float rr = __shfl(v[0], lane + 1, 64);
 #pragma unroll
-            for (int e = 0; e < RW; ++e) nxt[m][e] = v[e];
-            nxt[m][RW] = has_right ? rr : 0.f;
+            for (int e = 0; e < DRW; ++e) nxt[m][e] = v[e];
+            nxt[m][DRW] = has_right ? rr : 0.f;
         }
         if (act && 2 * r < g.ih) {
-            float e0[2 * RW], e1[2 * RW];  // dx rows 2r and 2r+1, columns 2c0 ...
+            float e0[RW], e1[RW];  // dx rows 2r and 2r+1, columns 2c0 .. 2c0+RW-1
 #pragma unroll
-            for (int q = 0; q < 2 * RW; ++q) e0[q] = e1[q] = 0.f;
+            for (int q = 0; q < RW; ++q) e0[q] = e1[q] = 0.f;
 #pragma unroll
             for (int m = 0; m < MM; ++m) {
                 const float *w = wt[m];
 #pragma unroll
-                for (int q = 0; q < RW; ++q) {
+                for (int q = 0; q < DRW; ++q) {
                     e0[2 * q] = fmaf(w[4], cur[m][q], e0[2 * q]);
                     e0[2 * q + 1] = fmaf(w[3], cur[m][q + 1], fmaf(w[5], cur[m][q], e0[2 * q + 1]));
                     e1[2 * q] = fmaf(w[1], nxt[m][q], fmaf(w[7], cur[m][q], e1[2 * q]));
@@ -308,16 +334,12 @@ __global__ __launch_bounds__(kThreads) void rw_bwdin3_s2_kernel(RwArgs<T> a) {
             T *xp = a.out + (static_cast<int64_t>(P) * g.ih + 2 * r) * g.iw + 2 * c0;
             const int valid = g.iw - 2 * c0;
             store_seg<T, RW>(xp, e0, valid, a.vout != 0);
-            store_seg<T, RW>(xp + RW, e0 + RW, valid - RW, a.vout != 0);
-            if (2 * r + 1 < g.ih) {
-                store_seg<T, RW>(xp + g.iw, e1, valid, a.vout != 0);
-                store_seg<T, RW>(xp + g.iw + RW, e1 + RW, valid - RW, a.vout != 0);
-            }
+            if (2 * r + 1 < g.ih) store_seg<T, RW>(xp + g.iw, e1, valid, a.vout != 0);
         }
 #pragma unroll
         for (int m = 0; m < MM; ++m)
 #pragma unroll
-            for (int e = 0; e <= RW; ++e) cur[m][e] = nxt[m][e];
+            for (int e = 0; e <= DRW; ++e) cur[m][e] = nxt[m][e];
     }
 }
 
@@ -485,10 +507,10 @@ bool rowwalk_fits(const Geo &g, int dtype, int pass) {
     // strip-defining width: output rows (forward, grad-weight), dx rows (grad-input
     // stride 1) or dy rows (grad-input stride 2)
     const int width = pass == 1 ? (g.sh == 1 ? g.iw : g.ow) : g.ow;
+    if (pass == 1 && g.sh == 2) return (width + ve / 2 - 1) / (ve / 2) <= 64 && width >= 28;  // half strips of dy
     if ((width + ve - 1) / ve > 64) return false;
     // narrow rows leave most lanes of a slot idle; the LDS band kernels measure
     // faster there for the forward and grad-input (grad-weight streams always)
-    if (pass == 1 && g.sh == 2) return false;  // the band kernel measured faster for stride-2 grad-input
     return pass == 2 || width >= 56;
 }
 
@@ -535,8 +557,11 @@ int launch_conv3(const Geo &g, const void *in, const void *w, const void *b, voi
 template <typename T, int MM>
 int launch_bwdin_s2(const Geo &g, const void *dy, const void *w, void *dx, hipStream_t st) {
     constexpr int RW = Vec<T>::N;
+    constexpr int DRW = RW / 2;
     RwPlan p;
-    if (!rw_strip_layout<T>(g.ow, p)) return kErrUnsupported;
+    p.NS = (g.ow + DRW - 1) / DRW;  // half strips of dy columns
+    if (p.NS > 64) return kErrUnsupported;
+    p.SPW = 64 / p.NS;
     // dx must be covered by dy rows/cols: 2*oh >= ih and 2*ow >= iw hold for pad 1, k 3, stride 2
     const int64_t planes = static_cast<int64_t>(g.n) * g.ic;
     p.BH = pick_bh(planes, g.oh, p.SPW, 2);
@@ -554,7 +579,7 @@ int launch_bwdin_s2(const Geo &g, const void *dy, const void *w, void *dx, hipSt
     a.BH = p.BH;
     a.nbands = p.nbands;
     a.nunits = p.nunits;
-    a.vin = (g.ow % RW == 0) && (reinterpret_cast<uintptr_t>(dy) % 16 == 0);
+    a.vin = (g.ow % DRW == 0) && (reinterpret_cast<uintptr_t>(dy) % 8 == 0);
     a.vout = (g.iw % RW == 0) && (reinterpret_cast<uintptr_t>(dx) % 16 == 0);
     hipLaunchKernelGGL((rw_bwdin3_s2_kernel<T, MM>), dim3(p.grid), dim3(kThreads), 0, st, a);
     return hipGetLastError() == hipSuccess ? kOk : kErrHip;
