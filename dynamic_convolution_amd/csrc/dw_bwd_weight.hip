@@ -392,7 +392,7 @@ int run_small(const Geo &g, const BwPlan &p, const void *x, const void *dy, void
     return hipGetLastError() == hipSuccess ? kOk : kErrHip;
 }
 
-enum BwAlgo { kBwChannelGroup = 0, kBwLargek, kBwRowwalk, kBwBandPixel, kBwBandTaps };
+enum BwAlgo { kBwChannelGroup = 0, kBwLargek, kBwRowwalk, kBwDecim, kBwBandPixel, kBwBandTaps };
 
 // The pass-1 kernel family a grad-weight call launches (pass 2 is always the
 // fixed-order chunk reduction).
@@ -400,6 +400,7 @@ int select_bwd_weight(const Geo &g, int dt) {
     if (small_fits(g, dt, 2)) return kBwChannelGroup;
     if (largek_bwdw_fits(g)) return kBwLargek;
     if (rowwalk_fits(g, dt, 2)) return kBwRowwalk;
+    if (decim_fits(g, 2)) return kBwDecim;
     return small_variant(g) ? kBwBandPixel : kBwBandTaps;
 }
 
@@ -412,13 +413,18 @@ int dispatch_bwd_weight(const Geo &g, const void *x, const void *dy, void *dwt, 
     const int algo = select_bwd_weight(g, dt);
     const bool small = algo == kBwChannelGroup;
     const bool large = algo == kBwLargek;
-    if (small || large || algo == kBwRowwalk) {
+    const bool decim = algo == kBwDecim;
+    if (small || large || decim || algo == kBwRowwalk) {
         // channel-group (small planes), register-tile (large k) or streaming (3x3, pad 1)
         // pass 1: workspace [ic][NC][M*(kk+1)]
-        NC = small ? small_bwd_weight_chunks(g, dt) : large ? largek_bwd_weight_chunks(g) : rowwalk_bwd_weight_chunks(g, dt);
+        NC = small ? small_bwd_weight_chunks(g, dt)
+                   : large ? largek_bwd_weight_chunks(g)
+                           : decim ? decim_bwd_weight_chunks(g) : rowwalk_bwd_weight_chunks(g, dt);
         nslots = g.mult * (kk + 1);
-        rc = small ? small_bwd_weight(g, x, dy, ws, dt, s)
-                   : large ? largek_bwd_weight(g, x, dy, ws, dt, s) : rowwalk_bwd_weight(g, x, dy, ws, dt, s);
+        rc = small   ? small_bwd_weight(g, x, dy, ws, dt, s)
+             : large ? largek_bwd_weight(g, x, dy, ws, dt, s)
+             : decim ? decim_bwd_weight(g, x, dy, ws, dt, s)
+                     : rowwalk_bwd_weight(g, x, dy, ws, dt, s);
         if (rc != kOk) return rc;
         const int total = g.oc * (kk + 1);
         hipLaunchKernelGGL((bwd_weight_reduce_kernel<T>), dim3((total + kThreads - 1) / kThreads), dim3(kThreads),
@@ -456,7 +462,8 @@ int dispatch_bwd_weight(const Geo &g, const void *x, const void *dy, void *dwt, 
 }  // namespace
 
 const char *bwd_weight_algo_name(const Geo &g, int dtype) {
-    static const char *names[] = {"channelgroup_small", "largek_regtile", "rowwalk_3x3", "band_pixel", "band_taps"};
+    static const char *names[] = {"channelgroup_small", "largek_regtile", "rowwalk_3x3", "decimated_s2d2", "band_pixel",
+                                  "band_taps"};
     return names[select_bwd_weight(g, dtype)];
 }
 
@@ -466,6 +473,7 @@ int64_t bwd_weight_workspace(const Geo &g, int dtype) {
     if (algo == kBwChannelGroup) return std::max<int64_t>(g.ic * small_bwd_weight_chunks(g, dtype) * slots * 4, 16);
     if (algo == kBwLargek) return std::max<int64_t>(g.ic * largek_bwd_weight_chunks(g) * slots * 4, 16);
     if (algo == kBwRowwalk) return std::max<int64_t>(g.ic * rowwalk_bwd_weight_chunks(g, dtype) * slots * 4, 16);
+    if (algo == kBwDecim) return std::max<int64_t>(g.ic * decim_bwd_weight_chunks(g) * slots * 4, 16);
     BwPlan p;
     if (!plan_bwd_weight(g, dtype == 0 ? 4 : 2, p)) return -1;
     return std::max<int64_t>(p.ws_bytes, 16);

@@ -1,0 +1,669 @@
+// dw_decim.hip -- depthwise passes with stride 2, dilation 2 and pad k-1
+// (k = 3, 5; multiplier 1 or 2) on gfx950.
+//
+// With stride s = 2, dilation d = 2 and pad p = k - 1 every tap of every output
+// reads an input element at an even row and an even column:
+//   x[2*oh - p + 2*i][2*ow - p + 2*j] = xe[oh - h + i][ow - h + j],   h = (k-1)/2,
+// where xe[r][c] = x[2r][2c] is the decimated input.  So all three passes are
+// stride-1, dilation-1 "same" convolutions on the decimated grid (this is the
+// multiplier-2 / dilation-2 / stride-2 layer of PyTorch PR #3057's feature set):
+//   forward      y = sum_ij w[i][j] xe[oh-h+i][ow-h+j]  -- only even x rows are read;
+//   grad-input   dx[2r][2c] = sum_m sum_ij w_m[i][j] dy_m[r+h-i][c+h-j], and every
+//                other dx element is a structural zero (75 % of dx), written as such;
+//   grad-weight  dw_m[i][j] = sum dy_m[oh][ow] xe[oh-h+i][ow-h+j].
+//
+// Each lane owns RO = 4 decimated columns of a plane and walks a band of rows:
+// the lane's x segment [2c0, 2c0+8) is one 16-byte load (two for fp32) whose
+// even elements are kept, the column halo of h values on each side comes from
+// the neighbouring lanes by shuffle, and the k rows of the window stay in
+// registers as a ring indexed at compile time (the row loop is unrolled by k).
+// Rows are loaded kPF rows ahead and kept as raw 32-bit words until they enter
+// the window, so those loads stay in flight across the arithmetic of the rows
+// before them; rows outside the plane are read from a clamped address and
+// replaced by zeros on conversion, which keeps the loads branch-free.
+// Forward and grad-input waves each serve one channel (several images or row
+// bands of it), so the filter taps are wave-uniform and live in scalar registers.
+#include "dw_common.hpp"
+#include "dw_internal.hpp"
+
+#include <type_traits>
+
+namespace dw {
+namespace {
+
+constexpr int kWaves = kThreads / 64;
+constexpr int RO = 4;   // decimated columns per lane
+constexpr int kPF = 2;  // raw rows loaded ahead of the row entering the window
+
+// 32-bit words of a lane's x segment (2*RO elements) and of a dy / y strip (RO elements).
+template <typename T> constexpr int kXWords = 2 * RO * static_cast<int>(sizeof(T)) / 4;
+template <typename T> constexpr int kDWords = RO * static_cast<int>(sizeof(T)) / 4;
+template <typename T> constexpr int kPerWord = 4 / static_cast<int>(sizeof(T));
+
+__device__ __forceinline__ uint32_t bits_of(float v) { return __float_as_uint(v); }
+__device__ __forceinline__ uint32_t bits_of(__half v) { return __half_as_ushort(v); }
+__device__ __forceinline__ uint32_t bits_of(bf16_t v) { return v.bits; }
+
+template <typename T> __device__ __forceinline__ T from_bits(uint32_t b);
+template <> __device__ __forceinline__ float from_bits<float>(uint32_t b) { return __uint_as_float(b); }
+template <> __device__ __forceinline__ __half from_bits<__half>(uint32_t b) {
+    return __ushort_as_half(static_cast<unsigned short>(b));
+}
+template <> __device__ __forceinline__ bf16_t from_bits<bf16_t>(uint32_t b) {
+    bf16_t r;
+    r.bits = static_cast<uint16_t>(b);
+    return r;
+}
+
+// Element e of a packed run of words, as fp32 (e is a constant after unrolling).
+template <typename T, int NW>
+__device__ __forceinline__ float word_elem(const uint32_t (&w)[NW], int e) {
+    if constexpr (sizeof(T) == 4) {
+        return __uint_as_float(w[e]);
+    } else {
+        const uint32_t h = (e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xffffu);
+        if constexpr (std::is_same<T, bf16_t>::value)
+            return __uint_as_float(h << 16);
+        else
+            return __half2float(__ushort_as_half(static_cast<unsigned short>(h)));
+    }
+}
+
+// NW words from NW * kPerWord<T> fp32 values, each rounded to T.
+template <typename T, int NW>
+__device__ __forceinline__ void pack_words(const float *v, uint32_t (&w)[NW]) {
+#pragma unroll
+    for (int k = 0; k < NW; ++k) {
+        if constexpr (sizeof(T) == 4)
+            w[k] = __float_as_uint(v[k]);
+        else
+            w[k] = bits_of(from_f32<T>(v[2 * k])) | (bits_of(from_f32<T>(v[2 * k + 1])) << 16);
+    }
+}
+
+template <int NW>
+__device__ __forceinline__ void load_words(const void *p, uint32_t (&w)[NW]) {
+    if constexpr (NW == 2) {
+        const uint2 u = *reinterpret_cast<const uint2 *>(p);
+        w[0] = u.x;
+        w[1] = u.y;
+    } else {
+        static_assert(NW % 4 == 0, "whole 16-byte vectors");
+#pragma unroll
+        for (int k = 0; k < NW / 4; ++k) {
+            const uint4 u = reinterpret_cast<const uint4 *>(p)[k];
+            w[4 * k] = u.x;
+            w[4 * k + 1] = u.y;
+            w[4 * k + 2] = u.z;
+            w[4 * k + 3] = u.w;
+        }
+    }
+}
+
+template <int NW>
+__device__ __forceinline__ void store_words(void *p, const uint32_t (&w)[NW]) {
+    if constexpr (NW == 2) {
+        *reinterpret_cast<uint2 *>(p) = make_uint2(w[0], w[1]);
+    } else {
+        static_assert(NW % 4 == 0, "whole 16-byte vectors");
+#pragma unroll
+        for (int k = 0; k < NW / 4; ++k)
+            reinterpret_cast<uint4 *>(p)[k] = make_uint4(w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]);
+    }
+}
+
+// The same words assembled element by element; elements at index >= avail read as zero.
+template <typename T, int NW>
+__device__ __forceinline__ void load_words_tail(const T *p, int avail, uint32_t (&w)[NW]) {
+    constexpr int PW = kPerWord<T>;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int e = 0; e < PW; ++e)
+            if (k * PW + e < avail) v |= bits_of(p[k * PW + e]) << (16 * e);
+        w[k] = v;
+    }
+}
+
+template <typename T, int NW>
+__device__ __forceinline__ void store_words_tail(T *p, int avail, const uint32_t (&w)[NW]) {
+    constexpr int PW = kPerWord<T>;
+#pragma unroll
+    for (int k = 0; k < NW; ++k)
+#pragma unroll
+        for (int e = 0; e < PW; ++e)
+            if (k * PW + e < avail) p[k * PW + e] = from_bits<T>(PW == 1 ? w[k] : (w[k] >> (16 * e)) & 0xffffu);
+}
+
+// Raw x segment of decimated row r (x row 2r, columns [2c0, 2c0 + 2*RO)).
+template <typename T, bool FULL>
+__device__ __forceinline__ void load_xrow(const T *plane, int r, int XH, int IW, int c0, bool act,
+                                          uint32_t (&w)[kXWords<T>], bool &ok) {
+    ok = act && r >= 0 && r < XH;
+    const int rc = min(max(r, 0), XH - 1);
+    const T *p = plane + static_cast<int64_t>(2 * rc) * IW + 2 * c0;
+    if constexpr (FULL)
+        load_words<kXWords<T>>(p, w);
+    else
+        load_words_tail<T, kXWords<T>>(p, IW - 2 * c0, w);
+}
+
+// Raw strip [c0, c0 + RO) of row r of a plane of H rows and W columns.
+template <typename T, bool FULL>
+__device__ __forceinline__ void load_drow(const T *plane, int r, int H, int W, int c0, bool act,
+                                          uint32_t (&w)[kDWords<T>], bool &ok) {
+    ok = act && r >= 0 && r < H;
+    const int rc = min(max(r, 0), H - 1);
+    const T *p = plane + static_cast<int64_t>(rc) * W + c0;
+    if constexpr (FULL)
+        load_words<kDWords<T>>(p, w);
+    else
+        load_words_tail<T, kDWords<T>>(p, W - c0, w);
+}
+
+// win[0..H) = the left lane's last H values, win[H..H+RO) = own, then the right lane's first H.
+template <int HH>
+__device__ __forceinline__ void halo_window(const float (&v)[RO], int lane, bool has_left, bool has_right,
+                                            float (&win)[RO + 2 * HH]) {
+#pragma unroll
+    for (int e = 0; e < HH; ++e) {
+        const float l = __shfl(v[RO - HH + e], lane - 1, 64);
+        win[e] = has_left ? l : 0.f;
+        const float r = __shfl(v[e], lane + 1, 64);
+        win[HH + RO + e] = has_right ? r : 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < RO; ++e) win[HH + e] = v[e];
+}
+
+// Window row from a raw x segment: its even elements, zero when the row is outside the plane.
+template <typename T, int HH>
+__device__ __forceinline__ void xrow_window(const uint32_t (&w)[kXWords<T>], bool ok, int lane, bool hl, bool hr,
+                                            float (&row)[RO + 2 * HH]) {
+    float v[RO];
+#pragma unroll
+    for (int e = 0; e < RO; ++e) v[e] = ok ? word_elem<T>(w, 2 * e) : 0.f;
+    halo_window<HH>(v, lane, hl, hr, row);
+}
+
+template <typename T>
+__device__ __forceinline__ void drow_values(const uint32_t (&w)[kDWords<T>], bool ok, float (&v)[RO]) {
+#pragma unroll
+    for (int e = 0; e < RO; ++e) v[e] = ok ? word_elem<T>(w, e) : 0.f;
+}
+
+// Wave-uniform value kept in a scalar register (the filter taps of a channel).
+__device__ __forceinline__ float uniform(float v) {
+    return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+}
+
+template <int NW>
+__device__ __forceinline__ void ring_pop(uint32_t (&q)[kPF][NW], bool (&ok)[kPF]) {
+#pragma unroll
+    for (int f = 0; f + 1 < kPF; ++f) {
+#pragma unroll
+        for (int k = 0; k < NW; ++k) q[f][k] = q[f + 1][k];
+        ok[f] = ok[f + 1];
+    }
+}
+
+template <typename T> struct DcArgs {
+    const T *in;
+    const T *in2;   // grad-weight: dy
+    const T *w;
+    const T *b;
+    T *out;
+    float *ws;
+    Geo g;
+    int XH, XW;     // decimated input plane: ceil(ih/2) x ceil(iw/2)
+    int NS, SPW, BH, nbands;
+    int wpc;        // forward / grad-input: waves per channel
+    int nunits;     // units (image, band) per channel
+    int NC, upc;    // grad-weight chunking
+};
+
+// One wave serves one channel: wave wv of the grid takes units
+// [j*SPW, (j+1)*SPW) of channel wv / wpc (j = wv % wpc), a unit being one
+// (image, row band) pair; slot = lane / NS picks the unit, s its column strip.
+struct WaveUnit {
+    int ic, n, band, lane, s;
+    bool act;
+};
+
+template <typename T>
+__device__ __forceinline__ WaveUnit wave_unit(const DcArgs<T> &a) {
+    WaveUnit u;
+    const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x) * kWaves +
+                                                  static_cast<int>(threadIdx.x >> 6));
+    int ic = wv / a.wpc;
+    const int jw = wv - ic * a.wpc;
+    const bool wave_ok = ic < a.g.ic;
+    u.ic = wave_ok ? ic : a.g.ic - 1;
+    u.lane = threadIdx.x & 63;
+    const int slot = u.lane / a.NS;
+    u.s = u.lane - slot * a.NS;
+    const int ul = jw * a.SPW + slot;
+    u.act = wave_ok && slot < a.SPW && ul < a.nunits;
+    u.n = u.act ? ul / a.nbands : 0;
+    u.band = u.act ? ul - u.n * a.nbands : 0;
+    return u;
+}
+
+// ---------------------------------------------------------------- forward
+template <typename T, int K, int MM, bool FULL>
+__global__ __launch_bounds__(kThreads) void dec_fwd_kernel(DcArgs<T> a) {
+    constexpr int HH = (K - 1) / 2, WW = RO + 2 * HH, NX = kXWords<T>, ND = kDWords<T>;
+    const Geo &g = a.g;
+    const WaveUnit u = wave_unit(a);
+    float wt[MM][K * K], bias[MM];
+#pragma unroll
+    for (int m = 0; m < MM; ++m) {
+#pragma unroll
+        for (int t = 0; t < K * K; ++t) wt[m][t] = uniform(to_f32(a.w[(u.ic * MM + m) * K * K + t]));
+        bias[m] = a.b ? uniform(to_f32(a.b[u.ic * MM + m])) : 0.f;
+    }
+    const int P = u.n * g.ic + u.ic;  // input plane (n, ic)
+    const T *xp = a.in + static_cast<int64_t>(P) * g.ih * g.iw;
+    const int c0 = u.s * RO;
+    const bool hl = u.s > 0, hr = u.s < a.NS - 1;
+    const int oh0 = u.band * a.BH, oh_end = min(oh0 + a.BH, g.oh);
+    // relative row j (absolute decimated row oh0 - HH + j) lives in window slot j % K
+    float win[K][WW];
+    uint32_t rq[kPF][NX];
+    bool rk[kPF];
+#pragma unroll
+    for (int j = 0; j < K - 1; ++j) {
+        uint32_t w[NX];
+        bool ok;
+        load_xrow<T, FULL>(xp, oh0 - HH + j, a.XH, g.iw, c0, u.act, w, ok);
+        xrow_window<T, HH>(w, ok, u.lane, hl, hr, win[j]);
+    }
+#pragma unroll
+    for (int f = 0; f < kPF; ++f) load_xrow<T, FULL>(xp, oh0 - HH + K - 1 + f, a.XH, g.iw, c0, u.act, rq[f], rk[f]);
+    for (int t0 = 0; t0 < a.BH; t0 += K) {
+#pragma unroll
+        for (int uu = 0; uu < K; ++uu) {
+            const int t = t0 + uu;
+            if (t < a.BH) {
+                xrow_window<T, HH>(rq[0], rk[0], u.lane, hl, hr, win[(uu + K - 1) % K]);
+                ring_pop<NX>(rq, rk);
+                load_xrow<T, FULL>(xp, oh0 - HH + t + K - 1 + kPF, a.XH, g.iw, c0, u.act, rq[kPF - 1], rk[kPF - 1]);
+                const int oh = oh0 + t;
+                if (u.act && oh < oh_end) {
+#pragma unroll
+                    for (int m = 0; m < MM; ++m) {
+                        float acc[RO];
+#pragma unroll
+                        for (int q = 0; q < RO; ++q) acc[q] = bias[m];
+#pragma unroll
+                        for (int i = 0; i < K; ++i)
+#pragma unroll
+                            for (int j = 0; j < K; ++j)
+#pragma unroll
+                                for (int q = 0; q < RO; ++q)
+                                    acc[q] = fmaf(wt[m][i * K + j], win[(uu + i) % K][q + j], acc[q]);
+                        T *yp = a.out + ((static_cast<int64_t>(P) * MM + m) * g.oh + oh) * g.ow + c0;
+                        if constexpr (FULL) {
+                            uint32_t w[ND];
+                            pack_words<T, ND>(acc, w);
+                            store_words<ND>(yp, w);
+                        } else {
+#pragma unroll
+                            for (int q = 0; q < RO; ++q)
+                                if (q < g.ow - c0) yp[q] = from_f32<T>(acc[q]);
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- grad-input
+template <typename T, int K, int MM, bool FULL>
+__global__ __launch_bounds__(kThreads) void dec_bwdin_kernel(DcArgs<T> a) {
+    constexpr int HH = (K - 1) / 2, WW = RO + 2 * HH, ND = kDWords<T>, NX = kXWords<T>;
+    const Geo &g = a.g;
+    const WaveUnit u = wave_unit(a);
+    // flipped taps: dxe[r][c] = sum_m sum_ij wf_m[i][j] dy_m[r-h+i][c-h+j]
+    float wf[MM][K * K];
+#pragma unroll
+    for (int m = 0; m < MM; ++m)
+#pragma unroll
+        for (int i = 0; i < K; ++i)
+#pragma unroll
+            for (int j = 0; j < K; ++j)
+                wf[m][i * K + j] = uniform(to_f32(a.w[(u.ic * MM + m) * K * K + (K - 1 - i) * K + (K - 1 - j)]));
+    const int P = u.n * g.ic + u.ic;  // dx plane (n, ic)
+    const int64_t dplane = static_cast<int64_t>(g.oh) * g.ow;
+    const T *dp[MM];
+#pragma unroll
+    for (int m = 0; m < MM; ++m) dp[m] = a.in + (static_cast<int64_t>(P) * MM + m) * dplane;
+    const int c0 = u.s * RO;  // decimated dx columns [c0, c0+RO) = dy columns of the same index
+    const bool hl = u.s > 0, hr = u.s < a.NS - 1;
+    const int r0 = u.band * a.BH, r_end = min(r0 + a.BH, a.XH);
+    // relative row j (dy row r0 - HH + j) lives in window slot j % K
+    float win[MM][K][WW];
+    uint32_t rq[MM][kPF][ND];
+    bool rk[MM][kPF];
+#pragma unroll
+    for (int m = 0; m < MM; ++m) {
+#pragma unroll
+        for (int j = 0; j < K - 1; ++j) {
+            uint32_t w[ND];
+            bool ok;
+            float v[RO];
+            load_drow<T, FULL>(dp[m], r0 - HH + j, g.oh, g.ow, c0, u.act, w, ok);
+            drow_values<T>(w, ok, v);
+            halo_window<HH>(v, u.lane, hl, hr, win[m][j]);
+        }
+#pragma unroll
+        for (int f = 0; f < kPF; ++f)
+            load_drow<T, FULL>(dp[m], r0 - HH + K - 1 + f, g.oh, g.ow, c0, u.act, rq[m][f], rk[m][f]);
+    }
+    for (int t0 = 0; t0 < a.BH; t0 += K) {
+#pragma unroll
+        for (int uu = 0; uu < K; ++uu) {
+            const int t = t0 + uu;
+            if (t < a.BH) {
+#pragma unroll
+                for (int m = 0; m < MM; ++m) {
+                    float v[RO];
+                    drow_values<T>(rq[m][0], rk[m][0], v);
+                    halo_window<HH>(v, u.lane, hl, hr, win[m][(uu + K - 1) % K]);
+                    ring_pop<ND>(rq[m], rk[m]);
+                    load_drow<T, FULL>(dp[m], r0 - HH + t + K - 1 + kPF, g.oh, g.ow, c0, u.act, rq[m][kPF - 1],
+                                       rk[m][kPF - 1]);
+                }
+                const int r = r0 + t;
+                if (u.act && r < r_end) {
+                    float acc[RO];
+#pragma unroll
+                    for (int q = 0; q < RO; ++q) acc[q] = 0.f;
+#pragma unroll
+                    for (int m = 0; m < MM; ++m)
+#pragma unroll
+                        for (int i = 0; i < K; ++i)
+#pragma unroll
+                            for (int j = 0; j < K; ++j)
+#pragma unroll
+                                for (int q = 0; q < RO; ++q)
+                                    acc[q] = fmaf(wf[m][i * K + j], win[m][(uu + i) % K][q + j], acc[q]);
+                    // dx row 2r: values at even columns, zeros at odd; dx row 2r+1: zeros
+                    float e0[2 * RO];
+#pragma unroll
+                    for (int q = 0; q < RO; ++q) {
+                        e0[2 * q] = acc[q];
+                        e0[2 * q + 1] = 0.f;
+                    }
+                    uint32_t we[NX], wz[NX];
+                    pack_words<T, NX>(e0, we);
+#pragma unroll
+                    for (int k = 0; k < NX; ++k) wz[k] = 0u;
+                    T *xq = a.out + (static_cast<int64_t>(P) * g.ih + 2 * r) * g.iw + 2 * c0;
+                    if constexpr (FULL) {
+                        store_words<NX>(xq, we);
+                        if (2 * r + 1 < g.ih) store_words<NX>(xq + g.iw, wz);
+                    } else {
+                        store_words_tail<T, NX>(xq, g.iw - 2 * c0, we);
+                        if (2 * r + 1 < g.ih) store_words_tail<T, NX>(xq + g.iw, g.iw - 2 * c0, wz);
+                    }
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- grad-weight
+// Sums of N <= 64 per-lane values over the wave, by recursive halving: at the
+// step with lane offset o every lane keeps one half of its current vector,
+// sends the other half to lane ^ o and adds what it receives, so after six
+// steps lane l holds the total of value l (63 shuffles instead of 6 per value).
+template <int N>
+__device__ __forceinline__ float wave_transpose_sum(const float (&v)[N], int lane) {
+    static_assert(N <= 64, "one value per lane");
+    float c[64];
+#pragma unroll
+    for (int i = 0; i < 64; ++i) c[i] = i < N ? v[i] : 0.f;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        const bool upper = (lane & o) != 0;  // this lane keeps indices [o, 2o) of the current vector
+#pragma unroll
+        for (int i = 0; i < o; ++i) {
+            const float keep = upper ? c[i + o] : c[i];
+            const float send = upper ? c[i] : c[i + o];
+            c[i] = keep + __shfl_xor(send, o, 64);
+        }
+    }
+    return c[0];
+}
+
+template <typename T, int K, int MM, bool FULL>
+__global__ __launch_bounds__(kThreads) void dec_bwdw_kernel(DcArgs<T> a) {
+    constexpr int HH = (K - 1) / 2, WW = RO + 2 * HH, KK = K * K, A = MM * (KK + 1);
+    constexpr int NX = kXWords<T>, ND = kDWords<T>;
+    __shared__ float red[kWaves][A];
+    const Geo &g = a.g;
+    const int ic = blockIdx.x / a.NC;
+    const int chunk = blockIdx.x - ic * a.NC;
+    float acc[MM][KK + 1];
+#pragma unroll
+    for (int m = 0; m < MM; ++m)
+#pragma unroll
+        for (int t = 0; t <= KK; ++t) acc[m][t] = 0.f;
+    const int ubeg = chunk * a.upc, uend = min(ubeg + a.upc, a.nunits);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int slot = lane / a.NS, s = lane - slot * a.NS;
+    const int c0 = s * RO;
+    const bool hl = s > 0, hr = s < a.NS - 1;
+    const int64_t dplane = static_cast<int64_t>(g.oh) * g.ow;
+    for (int base = ubeg; base < uend; base += kWaves * a.SPW) {
+        const int unit = base + wave * a.SPW + slot;
+        const bool act = slot < a.SPW && unit < uend;
+        const int n = act ? unit / a.nbands : 0;
+        const int band = act ? unit - n * a.nbands : 0;
+        const T *xp = a.in + (static_cast<int64_t>(n) * g.ic + ic) * g.ih * g.iw;
+        const T *dyp = a.in2 + (static_cast<int64_t>(n) * g.oc + static_cast<int64_t>(ic) * MM) * dplane;
+        const int oh0 = band * a.BH, oh_end = min(oh0 + a.BH, g.oh);
+        // relative x row j (decimated row oh0 - HH + j) lives in window slot j % K;
+        // dy row oh0 + t is used at step t
+        float win[K][WW];
+        uint32_t rq[kPF][NX], gq[MM][kPF][ND];
+        bool rk[kPF], gk[MM][kPF];
+#pragma unroll
+        for (int j = 0; j < K - 1; ++j) {
+            uint32_t w[NX];
+            bool ok;
+            load_xrow<T, FULL>(xp, oh0 - HH + j, a.XH, g.iw, c0, act, w, ok);
+            xrow_window<T, HH>(w, ok, lane, hl, hr, win[j]);
+        }
+#pragma unroll
+        for (int f = 0; f < kPF; ++f) {
+            load_xrow<T, FULL>(xp, oh0 - HH + K - 1 + f, a.XH, g.iw, c0, act, rq[f], rk[f]);
+#pragma unroll
+            for (int m = 0; m < MM; ++m)
+                load_drow<T, FULL>(dyp + m * dplane, oh0 + f, oh_end, g.ow, c0, act, gq[m][f], gk[m][f]);
+        }
+        for (int t0 = 0; t0 < a.BH; t0 += K) {
+#pragma unroll
+            for (int uu = 0; uu < K; ++uu) {
+                const int t = t0 + uu;
+                if (t < a.BH) {
+                    xrow_window<T, HH>(rq[0], rk[0], lane, hl, hr, win[(uu + K - 1) % K]);
+                    ring_pop<NX>(rq, rk);
+                    load_xrow<T, FULL>(xp, oh0 - HH + t + K - 1 + kPF, a.XH, g.iw, c0, act, rq[kPF - 1],
+                                       rk[kPF - 1]);
+#pragma unroll
+                    for (int m = 0; m < MM; ++m) {
+                        float gy[RO];
+                        drow_values<T>(gq[m][0], gk[m][0], gy);
+                        ring_pop<ND>(gq[m], gk[m]);
+                        load_drow<T, FULL>(dyp + m * dplane, oh0 + t + kPF, oh_end, g.ow, c0, act, gq[m][kPF - 1],
+                                           gk[m][kPF - 1]);
+#pragma unroll
+                        for (int q = 0; q < RO; ++q) {
+                            acc[m][KK] += gy[q];
+#pragma unroll
+                            for (int i = 0; i < K; ++i)
+#pragma unroll
+                                for (int j = 0; j < K; ++j)
+                                    acc[m][i * K + j] = fmaf(gy[q], win[(uu + i) % K][q + j], acc[m][i * K + j]);
+                        }
+                    }
+                }
+            }
+        }
+    }
+    {
+        float flat[A];
+#pragma unroll
+        for (int m = 0; m < MM; ++m)
+#pragma unroll
+            for (int t = 0; t <= KK; ++t) flat[m * (KK + 1) + t] = acc[m][t];
+        const float v = wave_transpose_sum<A>(flat, lane);
+        if (lane < A) red[wave][lane] = v;
+    }
+    __syncthreads();
+    if (threadIdx.x < A) {
+        float v = red[0][threadIdx.x];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) v += red[w][threadIdx.x];
+        a.ws[(static_cast<int64_t>(ic) * a.NC + chunk) * A + threadIdx.x] = v;
+    }
+}
+
+// ---------------------------------------------------------------- planning
+struct DcPlan {
+    int NS, SPW, BH, nbands, nunits, wpc, grid, NC, upc;
+};
+
+bool plan_dec(const Geo &g, int pass, DcPlan &p) {
+    // strips of RO decimated columns over the output width (= decimated width)
+    p.NS = (g.ow + RO - 1) / RO;
+    if (p.NS > 64) return false;
+    p.SPW = 64 / p.NS;
+    const int rows = pass == 1 ? (g.ih + 1) / 2 : g.oh;  // rows walked: decimated dx rows or output rows
+    const int64_t planes = static_cast<int64_t>(g.n) * g.ic;
+    int bh = rows;
+    while (bh > 4 && planes * ((rows + bh - 1) / bh) < int64_t{8192} * p.SPW / 2) bh = (bh + 1) / 2;
+    p.nbands = (rows + bh - 1) / bh;
+    p.BH = (rows + p.nbands - 1) / p.nbands;
+    p.nbands = (rows + p.BH - 1) / p.BH;
+    p.nunits = g.n * p.nbands;  // units per channel
+    if (pass == 2) {
+        const int per_round = kWaves * p.SPW;
+        const int rounds = (p.nunits + per_round - 1) / per_round;
+        const int nc = std::min(rounds, std::max(1, (2048 + g.ic - 1) / g.ic));
+        p.upc = ((rounds + nc - 1) / nc) * per_round;
+        p.NC = (p.nunits + p.upc - 1) / p.upc;
+        p.wpc = 0;
+        p.grid = g.ic * p.NC;
+    } else {
+        p.wpc = (p.nunits + p.SPW - 1) / p.SPW;
+        p.NC = p.upc = 0;
+        const int64_t waves = static_cast<int64_t>(g.ic) * p.wpc;
+        if (waves > int64_t{1} << 30) return false;
+        p.grid = static_cast<int>((waves + kWaves - 1) / kWaves);
+    }
+    return true;
+}
+
+template <typename T>
+DcArgs<T> dec_args(const Geo &g, const DcPlan &p) {
+    DcArgs<T> a{};
+    a.g = g;
+    a.XH = (g.ih + 1) / 2;
+    a.XW = (g.iw + 1) / 2;
+    a.NS = p.NS;
+    a.SPW = p.SPW;
+    a.BH = p.BH;
+    a.nbands = p.nbands;
+    a.wpc = p.wpc;
+    a.nunits = p.nunits;
+    a.NC = p.NC;
+    a.upc = p.upc;
+    return a;
+}
+
+bool aligned16(const void *p) { return p == nullptr || reinterpret_cast<uintptr_t>(p) % 16 == 0; }
+
+template <typename T, int K, int MM, bool FULL>
+void launch_dec(int pass, int grid, const DcArgs<T> &a, hipStream_t s) {
+    if (pass == 0)
+        hipLaunchKernelGGL((dec_fwd_kernel<T, K, MM, FULL>), dim3(grid), dim3(kThreads), 0, s, a);
+    else if (pass == 1)
+        hipLaunchKernelGGL((dec_bwdin_kernel<T, K, MM, FULL>), dim3(grid), dim3(kThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL((dec_bwdw_kernel<T, K, MM, FULL>), dim3(grid), dim3(kThreads), 0, s, a);
+}
+
+template <typename T, int K, int MM>
+int run_dec(int pass, const Geo &g, const void *in, const void *in2, const void *w, const void *b, void *out,
+            void *ws, hipStream_t s) {
+    DcPlan p;
+    if (!plan_dec(g, pass, p)) return kErrUnsupported;
+    DcArgs<T> a = dec_args<T>(g, p);
+    a.in = static_cast<const T *>(in);
+    a.in2 = static_cast<const T *>(in2);
+    a.w = static_cast<const T *>(w);
+    a.b = static_cast<const T *>(b);
+    a.out = static_cast<T *>(out);
+    a.ws = static_cast<float *>(ws);
+    // Whole-vector path: every lane's x segment [2c0, 2c0+8) and strip [c0, c0+4)
+    // lie inside their rows (iw a multiple of 8 makes ow = iw/2 a multiple of 4),
+    // and every row starts 16-byte aligned.
+    const bool full = g.iw % 8 == 0 && aligned16(in) && aligned16(in2) && aligned16(out);
+    if (full)
+        launch_dec<T, K, MM, true>(pass, p.grid, a, s);
+    else
+        launch_dec<T, K, MM, false>(pass, p.grid, a, s);
+    return hipGetLastError() == hipSuccess ? kOk : kErrHip;
+}
+
+template <typename T>
+int dec_t(int pass, const Geo &g, const void *in, const void *in2, const void *w, const void *b, void *out, void *ws,
+          hipStream_t s) {
+    if (g.kh == 3) return g.mult == 1 ? run_dec<T, 3, 1>(pass, g, in, in2, w, b, out, ws, s)
+                                      : run_dec<T, 3, 2>(pass, g, in, in2, w, b, out, ws, s);
+    return g.mult == 1 ? run_dec<T, 5, 1>(pass, g, in, in2, w, b, out, ws, s)
+                       : run_dec<T, 5, 2>(pass, g, in, in2, w, b, out, ws, s);
+}
+
+int dec_dispatch(int pass, const Geo &g, const void *in, const void *in2, const void *w, const void *b, void *out,
+                 void *ws, int dtype, hipStream_t s) {
+    switch (dtype) {
+        case 0: return dec_t<float>(pass, g, in, in2, w, b, out, ws, s);
+        case 1: return dec_t<__half>(pass, g, in, in2, w, b, out, ws, s);
+        default: return dec_t<bf16_t>(pass, g, in, in2, w, b, out, ws, s);
+    }
+}
+
+}  // namespace
+
+bool decim_fits(const Geo &g, int pass) {
+    if (g.kh != g.kw || (g.kh != 3 && g.kh != 5)) return false;
+    if (g.sh != 2 || g.sw != 2 || g.dh != 2 || g.dw != 2) return false;
+    if (g.ph != g.kh - 1 || g.pw != g.kw - 1 || g.mult > 2) return false;
+    DcPlan p;
+    return plan_dec(g, pass, p);
+}
+
+int decim_bwd_weight_chunks(const Geo &g) {
+    DcPlan p;
+    return plan_dec(g, 2, p) ? p.NC : 0;
+}
+
+int decim_fwd(const Geo &g, const void *x, const void *w, const void *b, void *y, int dtype, hipStream_t s) {
+    return dec_dispatch(0, g, x, nullptr, w, b, y, nullptr, dtype, s);
+}
+
+int decim_bwd_input(const Geo &g, const void *dy, const void *w, void *dx, int dtype, hipStream_t s) {
+    return dec_dispatch(1, g, dy, nullptr, w, nullptr, dx, nullptr, dtype, s);
+}
+
+int decim_bwd_weight(const Geo &g, const void *x, const void *dy, void *ws, int dtype, hipStream_t s) {
+    return dec_dispatch(2, g, x, dy, nullptr, nullptr, nullptr, ws, dtype, s);
+}
+
+}  // namespace dw

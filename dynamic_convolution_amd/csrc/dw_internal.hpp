@@ -62,6 +62,13 @@ bool largek_bwdw_fits(const Geo &g);
 int largek_bwd_weight_chunks(const Geo &g);
 int largek_bwd_weight(const Geo &g, const void *x, const void *dy, void *ws, int dtype, hipStream_t s);
 
+// Stride 2, dilation 2, pad k-1 (k = 3, 5) as stride-1 passes on the even grid (dw_decim.hip).
+bool decim_fits(const Geo &g, int pass);
+int decim_fwd(const Geo &g, const void *x, const void *w, const void *b, void *y, int dtype, hipStream_t s);
+int decim_bwd_input(const Geo &g, const void *dy, const void *w, void *dx, int dtype, hipStream_t s);
+int decim_bwd_weight_chunks(const Geo &g);
+int decim_bwd_weight(const Geo &g, const void *x, const void *dy, void *ws, int dtype, hipStream_t s);
+
 // Name of the kernel family each pass would launch for this geometry.
 const char *fwd_algo_name(const Geo &g, int dtype);
 const char *bwd_input_algo_name(const Geo &g, int dtype);

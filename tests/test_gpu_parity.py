@@ -401,3 +401,20 @@ def test_graph_replay_matches_eager():
 def test_large_kernel_shapes(n, c, h, w, mult, k, p, dt):
     x, wt, b, dy = static_case(n, c, h, w, mult, k, 1, p, 1, DT[dt], 650 + h + w + k)
     check_static(x, wt, b, dy, 1, p, 1, "largek n%d c%d %dx%d m%d k%d p%d %s" % (n, c, h, w, mult, k, p, dt))
+
+
+# ------------------------------------------------------------------ stride 2 / dilation 2 / pad k-1 (even-grid) path
+@pytest.mark.parametrize("n,c,h,w,mult,k,dt", [
+    (2, 3, 29, 31, 2, 5, "bf16"), (2, 3, 29, 31, 1, 5, "f32"),   # odd sizes
+    (1, 2, 20, 22, 1, 3, "f32"), (2, 2, 17, 9, 2, 3, "f16"),
+    (1, 2, 6, 512, 2, 5, "bf16"),                                # 64 strips of decimated columns
+    (1, 2, 6, 514, 1, 5, "f32"),                                 # one strip too many: band kernels
+    (3, 1, 1, 1, 1, 3, "f32"), (1, 2, 2, 3, 2, 5, "f32"),        # tiny planes
+    # width a multiple of 8: whole-vector loads and stores
+    (2, 5, 24, 40, 2, 5, "bf16"), (3, 3, 15, 16, 1, 3, "f16"),   # odd height: last dx row has no zero row
+    (2, 4, 16, 24, 2, 3, "f32"), (1, 2, 9, 8, 2, 5, "bf16"),
+    (5, 7, 20, 56, 1, 5, "bf16"),                                # images x bands not a multiple of a wave's units
+])
+def test_even_grid_shapes(n, c, h, w, mult, k, dt):
+    x, wt, b, dy = static_case(n, c, h, w, mult, k, 2, k - 1, 2, DT[dt], 670 + h + w + k)
+    check_static(x, wt, b, dy, 2, k - 1, 2, "evengrid n%d c%d %dx%d m%d k%d %s" % (n, c, h, w, mult, k, dt))
