@@ -23,10 +23,8 @@
 // replaced by zeros on conversion, which keeps the loads branch-free.
 // Forward and grad-input waves each serve one channel (several images or row
 // bands of it), so the filter taps are wave-uniform and live in scalar registers.
-#include "dw_common.hpp"
 #include "dw_internal.hpp"
-
-#include <type_traits>
+#include "dw_stream.hpp"
 
 namespace dw {
 namespace {
@@ -38,103 +36,6 @@ constexpr int kPF = 2;  // raw rows loaded ahead of the row entering the window
 // 32-bit words of a lane's x segment (2*RO elements) and of a dy / y strip (RO elements).
 template <typename T> constexpr int kXWords = 2 * RO * static_cast<int>(sizeof(T)) / 4;
 template <typename T> constexpr int kDWords = RO * static_cast<int>(sizeof(T)) / 4;
-template <typename T> constexpr int kPerWord = 4 / static_cast<int>(sizeof(T));
-
-__device__ __forceinline__ uint32_t bits_of(float v) { return __float_as_uint(v); }
-__device__ __forceinline__ uint32_t bits_of(__half v) { return __half_as_ushort(v); }
-__device__ __forceinline__ uint32_t bits_of(bf16_t v) { return v.bits; }
-
-template <typename T> __device__ __forceinline__ T from_bits(uint32_t b);
-template <> __device__ __forceinline__ float from_bits<float>(uint32_t b) { return __uint_as_float(b); }
-template <> __device__ __forceinline__ __half from_bits<__half>(uint32_t b) {
-    return __ushort_as_half(static_cast<unsigned short>(b));
-}
-template <> __device__ __forceinline__ bf16_t from_bits<bf16_t>(uint32_t b) {
-    bf16_t r;
-    r.bits = static_cast<uint16_t>(b);
-    return r;
-}
-
-// Element e of a packed run of words, as fp32 (e is a constant after unrolling).
-template <typename T, int NW>
-__device__ __forceinline__ float word_elem(const uint32_t (&w)[NW], int e) {
-    if constexpr (sizeof(T) == 4) {
-        return __uint_as_float(w[e]);
-    } else {
-        const uint32_t h = (e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xffffu);
-        if constexpr (std::is_same<T, bf16_t>::value)
-            return __uint_as_float(h << 16);
-        else
-            return __half2float(__ushort_as_half(static_cast<unsigned short>(h)));
-    }
-}
-
-// NW words from NW * kPerWord<T> fp32 values, each rounded to T.
-template <typename T, int NW>
-__device__ __forceinline__ void pack_words(const float *v, uint32_t (&w)[NW]) {
-#pragma unroll
-    for (int k = 0; k < NW; ++k) {
-        if constexpr (sizeof(T) == 4)
-            w[k] = __float_as_uint(v[k]);
-        else
-            w[k] = bits_of(from_f32<T>(v[2 * k])) | (bits_of(from_f32<T>(v[2 * k + 1])) << 16);
-    }
-}
-
-template <int NW>
-__device__ __forceinline__ void load_words(const void *p, uint32_t (&w)[NW]) {
-    if constexpr (NW == 2) {
-        const uint2 u = *reinterpret_cast<const uint2 *>(p);
-        w[0] = u.x;
-        w[1] = u.y;
-    } else {
-        static_assert(NW % 4 == 0, "whole 16-byte vectors");
-#pragma unroll
-        for (int k = 0; k < NW / 4; ++k) {
-            const uint4 u = reinterpret_cast<const uint4 *>(p)[k];
-            w[4 * k] = u.x;
-            w[4 * k + 1] = u.y;
-            w[4 * k + 2] = u.z;
-            w[4 * k + 3] = u.w;
-        }
-    }
-}
-
-template <int NW>
-__device__ __forceinline__ void store_words(void *p, const uint32_t (&w)[NW]) {
-    if constexpr (NW == 2) {
-        *reinterpret_cast<uint2 *>(p) = make_uint2(w[0], w[1]);
-    } else {
-        static_assert(NW % 4 == 0, "whole 16-byte vectors");
-#pragma unroll
-        for (int k = 0; k < NW / 4; ++k)
-            reinterpret_cast<uint4 *>(p)[k] = make_uint4(w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]);
-    }
-}
-
-// The same words assembled element by element; elements at index >= avail read as zero.
-template <typename T, int NW>
-__device__ __forceinline__ void load_words_tail(const T *p, int avail, uint32_t (&w)[NW]) {
-    constexpr int PW = kPerWord<T>;
-#pragma unroll
-    for (int k = 0; k < NW; ++k) {
-        uint32_t v = 0;
-#pragma unroll
-        for (int e = 0; e < PW; ++e)
-            if (k * PW + e < avail) v |= bits_of(p[k * PW + e]) << (16 * e);
-        w[k] = v;
-    }
-}
-
-template <typename T, int NW>
-__device__ __forceinline__ void store_words_tail(T *p, int avail, const uint32_t (&w)[NW]) {
-    constexpr int PW = kPerWord<T>;
-#pragma unroll
-    for (int k = 0; k < NW; ++k)
-#pragma unroll
-        for (int e = 0; e < PW; ++e)
-            if (k * PW + e < avail) p[k * PW + e] = from_bits<T>(PW == 1 ? w[k] : (w[k] >> (16 * e)) & 0xffffu);
-}
 
 // Raw x segment of decimated row r (x row 2r, columns [2c0, 2c0 + 2*RO)).
 template <typename T, bool FULL>
@@ -193,21 +94,6 @@ __device__ __forceinline__ void drow_values(const uint32_t (&w)[kDWords<T>], boo
     for (int e = 0; e < RO; ++e) v[e] = ok ? word_elem<T>(w, e) : 0.f;
 }
 
-// Wave-uniform value kept in a scalar register (the filter taps of a channel).
-__device__ __forceinline__ float uniform(float v) {
-    return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
-}
-
-template <int NW>
-__device__ __forceinline__ void ring_pop(uint32_t (&q)[kPF][NW], bool (&ok)[kPF]) {
-#pragma unroll
-    for (int f = 0; f + 1 < kPF; ++f) {
-#pragma unroll
-        for (int k = 0; k < NW; ++k) q[f][k] = q[f + 1][k];
-        ok[f] = ok[f + 1];
-    }
-}
-
 template <typename T> struct DcArgs {
     const T *in;
     const T *in2;   // grad-weight: dy
@@ -223,39 +109,12 @@ template <typename T> struct DcArgs {
     int NC, upc;    // grad-weight chunking
 };
 
-// One wave serves one channel: wave wv of the grid takes units
-// [j*SPW, (j+1)*SPW) of channel wv / wpc (j = wv % wpc), a unit being one
-// (image, row band) pair; slot = lane / NS picks the unit, s its column strip.
-struct WaveUnit {
-    int ic, n, band, lane, s;
-    bool act;
-};
-
-template <typename T>
-__device__ __forceinline__ WaveUnit wave_unit(const DcArgs<T> &a) {
-    WaveUnit u;
-    const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x) * kWaves +
-                                                  static_cast<int>(threadIdx.x >> 6));
-    int ic = wv / a.wpc;
-    const int jw = wv - ic * a.wpc;
-    const bool wave_ok = ic < a.g.ic;
-    u.ic = wave_ok ? ic : a.g.ic - 1;
-    u.lane = threadIdx.x & 63;
-    const int slot = u.lane / a.NS;
-    u.s = u.lane - slot * a.NS;
-    const int ul = jw * a.SPW + slot;
-    u.act = wave_ok && slot < a.SPW && ul < a.nunits;
-    u.n = u.act ? ul / a.nbands : 0;
-    u.band = u.act ? ul - u.n * a.nbands : 0;
-    return u;
-}
-
 // ---------------------------------------------------------------- forward
 template <typename T, int K, int MM, bool FULL>
 __global__ __launch_bounds__(kThreads) void dec_fwd_kernel(DcArgs<T> a) {
     constexpr int HH = (K - 1) / 2, WW = RO + 2 * HH, NX = kXWords<T>, ND = kDWords<T>;
     const Geo &g = a.g;
-    const WaveUnit u = wave_unit(a);
+    const WaveUnit u = wave_unit(a.wpc, a.NS, a.SPW, a.nunits, a.nbands, g.ic);
     float wt[MM][K * K], bias[MM];
 #pragma unroll
     for (int m = 0; m < MM; ++m) {
@@ -287,7 +146,7 @@ __global__ __launch_bounds__(kThreads) void dec_fwd_kernel(DcArgs<T> a) {
             const int t = t0 + uu;
             if (t < a.BH) {
                 xrow_window<T, HH>(rq[0], rk[0], u.lane, hl, hr, win[(uu + K - 1) % K]);
-                ring_pop<NX>(rq, rk);
+                ring_pop<kPF, NX>(rq, rk);
                 load_xrow<T, FULL>(xp, oh0 - HH + t + K - 1 + kPF, a.XH, g.iw, c0, u.act, rq[kPF - 1], rk[kPF - 1]);
                 const int oh = oh0 + t;
                 if (u.act && oh < oh_end) {
@@ -325,7 +184,7 @@ template <typename T, int K, int MM, bool FULL>
 __global__ __launch_bounds__(kThreads) void dec_bwdin_kernel(DcArgs<T> a) {
     constexpr int HH = (K - 1) / 2, WW = RO + 2 * HH, ND = kDWords<T>, NX = kXWords<T>;
     const Geo &g = a.g;
-    const WaveUnit u = wave_unit(a);
+    const WaveUnit u = wave_unit(a.wpc, a.NS, a.SPW, a.nunits, a.nbands, g.ic);
     // flipped taps: dxe[r][c] = sum_m sum_ij wf_m[i][j] dy_m[r-h+i][c-h+j]
     float wf[MM][K * K];
 #pragma unroll
@@ -372,7 +231,7 @@ __global__ __launch_bounds__(kThreads) void dec_bwdin_kernel(DcArgs<T> a) {
                     float v[RO];
                     drow_values<T>(rq[m][0], rk[m][0], v);
                     halo_window<HH>(v, u.lane, hl, hr, win[m][(uu + K - 1) % K]);
-                    ring_pop<ND>(rq[m], rk[m]);
+                    ring_pop<kPF, ND>(rq[m], rk[m]);
                     load_drow<T, FULL>(dp[m], r0 - HH + t + K - 1 + kPF, g.oh, g.ow, c0, u.act, rq[m][kPF - 1],
                                        rk[m][kPF - 1]);
                 }
@@ -416,29 +275,6 @@ __global__ __launch_bounds__(kThreads) void dec_bwdin_kernel(DcArgs<T> a) {
 }
 
 // ---------------------------------------------------------------- grad-weight
-// Sums of N <= 64 per-lane values over the wave, by recursive halving: at the
-// step with lane offset o every lane keeps one half of its current vector,
-// sends the other half to lane ^ o and adds what it receives, so after six
-// steps lane l holds the total of value l (63 shuffles instead of 6 per value).
-template <int N>
-__device__ __forceinline__ float wave_transpose_sum(const float (&v)[N], int lane) {
-    static_assert(N <= 64, "one value per lane");
-    float c[64];
-#pragma unroll
-    for (int i = 0; i < 64; ++i) c[i] = i < N ? v[i] : 0.f;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        const bool upper = (lane & o) != 0;  // this lane keeps indices [o, 2o) of the current vector
-#pragma unroll
-        for (int i = 0; i < o; ++i) {
-            const float keep = upper ? c[i + o] : c[i];
-            const float send = upper ? c[i] : c[i + o];
-            c[i] = keep + __shfl_xor(send, o, 64);
-        }
-    }
-    return c[0];
-}
-
 template <typename T, int K, int MM, bool FULL>
 __global__ __launch_bounds__(kThreads) void dec_bwdw_kernel(DcArgs<T> a) {
     constexpr int HH = (K - 1) / 2, WW = RO + 2 * HH, KK = K * K, A = MM * (KK + 1);
@@ -491,14 +327,14 @@ __global__ __launch_bounds__(kThreads) void dec_bwdw_kernel(DcArgs<T> a) {
                 const int t = t0 + uu;
                 if (t < a.BH) {
                     xrow_window<T, HH>(rq[0], rk[0], lane, hl, hr, win[(uu + K - 1) % K]);
-                    ring_pop<NX>(rq, rk);
+                    ring_pop<kPF, NX>(rq, rk);
                     load_xrow<T, FULL>(xp, oh0 - HH + t + K - 1 + kPF, a.XH, g.iw, c0, act, rq[kPF - 1],
                                        rk[kPF - 1]);
 #pragma unroll
                     for (int m = 0; m < MM; ++m) {
                         float gy[RO];
                         drow_values<T>(gq[m][0], gk[m][0], gy);
-                        ring_pop<ND>(gq[m], gk[m]);
+                        ring_pop<kPF, ND>(gq[m], gk[m]);
                         load_drow<T, FULL>(dyp + m * dplane, oh0 + t + kPF, oh_end, g.ow, c0, act, gq[m][kPF - 1],
                                            gk[m][kPF - 1]);
 #pragma unroll

@@ -6,17 +6,22 @@
 // Convolution on the GPU" is this case).  Instead of staging tiles in LDS
 // behind barriers, every lane owns one 16-byte column strip of a plane and
 // walks down a band of rows:
-//   - each input row segment is read once with a 16-byte load and converted
-//     to fp32 registers; the column halo (one element left/right) comes from
-//     the neighbouring lanes with a shuffle, the row halo from a rolling window
-//     of the previous rows kept in registers;
+//   - each input row segment is read with one 16-byte load (two for a stride-2
+//     forward segment) several rows ahead of its use and kept as raw words
+//     until it enters the window, so those loads stay in flight across the
+//     arithmetic of the rows before it; rows outside the plane are read from
+//     a clamped row and zeroed on conversion, so the loads need no branch;
+//   - the column halo (one element left/right) comes from the neighbouring
+//     lanes by shuffle, the row halo from a ring of the last three rows kept
+//     in registers and indexed at compile time (the row loop is unrolled by 3);
 //   - each output strip is written with one 16-byte store;
 //   - no LDS tile and no barrier, so waves stream independently.
-// A wave holds 64 / NS strips-of-a-row "slots" (NS = strips per row), each slot
-// walking one (plane, band) unit; all slots of a wave take the same number of
-// steps so the shuffles always see every lane active.
-#include "dw_common.hpp"
+// A wave serves one channel (its taps are wave-uniform, in scalar registers)
+// and holds 64 / NS slots (NS = strips per row), each slot walking one
+// (image, band) unit; all slots of a wave take the same number of steps so the
+// shuffles always see every lane active.
 #include "dw_internal.hpp"
+#include "dw_stream.hpp"
 
 namespace dw {
 namespace {
@@ -35,59 +40,11 @@ template <typename T> struct RwArgs {
     int SPW;        // slots per wave
     int BH;         // rows walked per unit
     int nbands;     // bands per plane
-    int nunits;     // forward/grad-input: units in total; grad-weight: units per channel
+    int nunits;     // units (image, band) per channel
+    int wpc;        // forward / grad-input: waves per channel
     int NC;         // grad-weight: chunks per channel
     int upc;        // grad-weight: units per chunk
-    int vin, vout;  // 16-byte loads / stores allowed
 };
-
-// Lane's IRW consecutive elements [c0, c0 + IRW) of row r (zero outside the image).
-template <typename T, int IRW>
-__device__ __forceinline__ void load_seg(const T *plane, int r, int H, int W, int c0, bool vec, bool act,
-                                         float (&v)[IRW]) {
-    constexpr int VE = Vec<T>::N;
-    static_assert(IRW % VE == 0, "segment is whole vectors");
-#pragma unroll
-    for (int e = 0; e < IRW; ++e) v[e] = 0.f;
-    if (!act || r < 0 || r >= H) return;
-    const T *p = plane + static_cast<int64_t>(r) * W + c0;
-    if (vec) {
-#pragma unroll
-        for (int k = 0; k < IRW / VE; ++k) {
-            if (c0 + (k + 1) * VE <= W) {
-                union {
-                    uint4 u;
-                    T t[VE];
-                } b;
-                b.u = *reinterpret_cast<const uint4 *>(p + k * VE);
-#pragma unroll
-                for (int e = 0; e < VE; ++e) v[k * VE + e] = to_f32(b.t[e]);
-            }
-        }
-    } else {
-#pragma unroll
-        for (int e = 0; e < IRW; ++e)
-            if (c0 + e < W) v[e] = to_f32(p[e]);
-    }
-}
-
-template <typename T, int RW>
-__device__ __forceinline__ void store_seg(T *p, const float *acc, int valid, bool vec) {
-    if (vec && valid >= RW) {
-        union {
-            uint4 u;
-            T t[RW];
-        } b;
-        static_assert(sizeof(T) * RW == 16, "strip is one 16-byte vector");
-#pragma unroll
-        for (int q = 0; q < RW; ++q) b.t[q] = from_f32<T>(acc[q]);
-        *reinterpret_cast<uint4 *>(p) = b.u;
-    } else {
-#pragma unroll
-        for (int q = 0; q < RW; ++q)
-            if (q < valid) p[q] = from_f32<T>(acc[q]);
-    }
-}
 
 // Window of one input row for a strip: win[0] = column c0 - 1 (from the left
 // lane), win[1..IRW] = the lane's own segment, and for stride 1 win[IRW+1] =
@@ -105,125 +62,113 @@ __device__ __forceinline__ void make_window(const float (&v)[IRW], int lane, boo
     }
 }
 
+// Steps of rows loaded ahead of use: stride 1 keeps 3 rows in flight, stride 2
+// (two rows per step) 4.
+template <int S> constexpr int kAhead = S == 1 ? 3 : 2;
+
 // ---------------------------------------------------------------- forward / grad-input (stride 1)
 // FWD: one input plane x[P] -> MM output planes y[P*MM+m].
 // BWD (stride 1 only): MM input planes dy[P*MM+m] -> one output plane dx[P],
 // with the kernel flipped (for stride 1, pad 1 the adjoint is the same
 // stencil with w[2-i][2-j]).
-template <typename T, int S, int MM, bool BWD>
+// Relative input row j (row S*oh0 - 1 + j of the band) lives in window slot
+// j % 3; output step t reads rows S*t .. S*t + 2 and brings in the S rows
+// S*t + 3 - S .. S*t + 2.
+template <typename T, int S, int MM, bool BWD, bool FULL>
 __global__ __launch_bounds__(kThreads) void rw_conv3_kernel(RwArgs<T> a) {
     constexpr int RW = Vec<T>::N;
     constexpr int IRW = RW * S;
     constexpr int WW = IRW + (S == 1 ? 2 : 1);
-    constexpr int NIN = BWD ? MM : 1;   // input planes per unit
-    constexpr int NOUT = BWD ? 1 : MM;  // output planes per unit
+    constexpr int NWI = IRW / kPerWord<T>;  // raw words of an input segment
+    constexpr int R = S * kAhead<S>;        // raw rows in flight
+    constexpr int NIN = BWD ? MM : 1;       // input planes per unit
+    constexpr int NOUT = BWD ? 1 : MM;      // output planes per unit
     static_assert(!BWD || S == 1, "stride-2 grad-input has its own kernel");
     const Geo &g = a.g;
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int slot = lane / a.NS;
-    const int s = lane - slot * a.NS;
-    const int unit = (blockIdx.x * kWaves + wave) * a.SPW + slot;
-    const bool act = slot < a.SPW && unit < a.nunits;
-    const int P = act ? unit / a.nbands : 0;
-    const int band = act ? unit - P * a.nbands : 0;
-    const int IH = BWD ? g.oh : g.ih, IW = BWD ? g.ow : g.iw;  // rows/cols of the input planes
-    const int OH = BWD ? g.ih : g.oh, OW = BWD ? g.iw : g.ow;
-    const int c_in = s * IRW;
-    const int c_out = s * RW;
-    const bool has_left = s > 0;
-    const bool has_right = s < a.NS - 1;
-    const int ic = P % g.ic;
-
+    const WaveUnit u = wave_unit(a.wpc, a.NS, a.SPW, a.nunits, a.nbands, g.ic);
     float wt[MM][9];
     float bias[NOUT];
 #pragma unroll
     for (int m = 0; m < MM; ++m)
 #pragma unroll
-        for (int t = 0; t < 9; ++t)
-            wt[m][t] = act ? to_f32(a.w[(ic * MM + m) * 9 + (BWD ? 8 - t : t)]) : 0.f;
+        for (int t = 0; t < 9; ++t) wt[m][t] = uniform(to_f32(a.w[(u.ic * MM + m) * 9 + (BWD ? 8 - t : t)]));
 #pragma unroll
-    for (int o = 0; o < NOUT; ++o) bias[o] = (!BWD && act && a.b) ? to_f32(a.b[ic * MM + o]) : 0.f;
+    for (int o = 0; o < NOUT; ++o) bias[o] = (!BWD && a.b) ? uniform(to_f32(a.b[u.ic * MM + o])) : 0.f;
 
+    const int P = u.n * g.ic + u.ic;  // plane (n, ic)
+    const int IH = BWD ? g.oh : g.ih, IW = BWD ? g.ow : g.iw;  // rows/cols of the input planes
+    const int OH = BWD ? g.ih : g.oh, OW = BWD ? g.iw : g.ow;
+    const int c_in = u.s * IRW, c_out = u.s * RW;
+    const bool hl = u.s > 0, hr = u.s < a.NS - 1;
     const int64_t in_plane = static_cast<int64_t>(IH) * IW;
     const T *inp[NIN];
 #pragma unroll
     for (int k = 0; k < NIN; ++k) inp[k] = a.in + (static_cast<int64_t>(P) * NIN + k) * in_plane;
-
-    const int oh0 = band * a.BH;
+    const int oh0 = u.band * a.BH;
     const int oh_end = min(oh0 + a.BH, OH);
-    const bool vin = a.vin != 0;
-    // rolling window: rows S*oh - 1 (w0, carried), S*oh (w1), S*oh + 1 (w2); the
-    // raw segments of the next step's rows are loaded one step ahead (nx*)
-    float w0[NIN][WW], w1[NIN][WW], w2[NIN][WW];
-    float nxa[NIN][IRW], nxb[NIN][IRW];  // next step: row S*oh+S (stride 2: and S*oh+1 of next)
+    const int rb = S * oh0 - 1;             // input row of relative row 0
+    const int jlast = S * (a.BH - 1) + 2;   // last relative row any step reads
+
+    float win[NIN][3][WW];
+    uint32_t rq[NIN][R][NWI];
+    bool rk[NIN][R];
 #pragma unroll
     for (int k = 0; k < NIN; ++k) {
-        float v[IRW];
-        load_seg<T, IRW>(inp[k], S * oh0 - 1, IH, IW, c_in, vin, act, v);
-        make_window<IRW, S>(v, lane, has_left, has_right, w0[k]);
-        if constexpr (S == 1) {
-            load_seg<T, IRW>(inp[k], oh0, IH, IW, c_in, vin, act, v);
-            make_window<IRW, S>(v, lane, has_left, has_right, w1[k]);
-            load_seg<T, IRW>(inp[k], oh0 + 1, IH, IW, c_in, vin, act, nxb[k]);
-        } else {
-            load_seg<T, IRW>(inp[k], 2 * oh0, IH, IW, c_in, vin, act, nxa[k]);
-            load_seg<T, IRW>(inp[k], 2 * oh0 + 1, IH, IW, c_in, vin, act, nxb[k]);
+#pragma unroll
+        for (int j = 0; j < 3 - S; ++j) {
+            uint32_t w[NWI];
+            bool ok;
+            float v[IRW];
+            load_row<T, NWI, FULL>(inp[k], rb + j, IH, IW, c_in, u.act, w, ok);
+            row_values<T>(w, ok, v);
+            make_window<IRW, S>(v, u.lane, hl, hr, win[k][j]);
         }
+#pragma unroll
+        for (int f = 0; f < R; ++f) load_row<T, NWI, FULL>(inp[k], rb + 3 - S + f, IH, IW, c_in, u.act, rq[k][f], rk[k][f]);
     }
-    for (int step = 0; step < a.BH; ++step) {
-        const int oh = oh0 + step;
+    for (int t0 = 0; t0 < a.BH; t0 += 3) {
 #pragma unroll
-        for (int k = 0; k < NIN; ++k) {
-            float cb[IRW];
+        for (int uu = 0; uu < 3; ++uu) {
+            const int t = t0 + uu;
+            if (t < a.BH) {
 #pragma unroll
-            for (int e = 0; e < IRW; ++e) cb[e] = nxb[k][e];
-            if constexpr (S == 2) {
-                float ca[IRW];
+                for (int k = 0; k < NIN; ++k)
 #pragma unroll
-                for (int e = 0; e < IRW; ++e) ca[e] = nxa[k][e];
-                load_seg<T, IRW>(inp[k], 2 * oh + 2, IH, IW, c_in, vin, act, nxa[k]);
-                load_seg<T, IRW>(inp[k], 2 * oh + 3, IH, IW, c_in, vin, act, nxb[k]);
-                make_window<IRW, S>(ca, lane, has_left, has_right, w1[k]);
-            } else {
-                load_seg<T, IRW>(inp[k], oh + 2, IH, IW, c_in, vin, act, nxb[k]);
-            }
-            make_window<IRW, S>(cb, lane, has_left, has_right, w2[k]);
-        }
-        if (act && oh < oh_end) {
+                    for (int e = 0; e < S; ++e) {
+                        float v[IRW];
+                        row_values<T>(rq[k][0], rk[k][0], v);
+                        make_window<IRW, S>(v, u.lane, hl, hr, win[k][(S * uu + 3 - S + e) % 3]);
+                        ring_pop<R, NWI>(rq[k], rk[k]);
+                        // refill with relative row S*t + 3 - S + e + R; past the last row a
+                        // step reads, re-read that row (a cache hit, never used) so the
+                        // load stays unconditional
+                        const int jn = min(S * t + 3 - S + e + R, jlast);
+                        load_row<T, NWI, FULL>(inp[k], rb + jn, IH, IW, c_in, u.act, rq[k][R - 1], rk[k][R - 1]);
+                    }
+                const int oh = oh0 + t;
+                if (u.act && oh < oh_end) {
 #pragma unroll
-            for (int o = 0; o < NOUT; ++o) {
-                float acc[RW];
+                    for (int o = 0; o < NOUT; ++o) {
+                        float acc[RW];
 #pragma unroll
-                for (int q = 0; q < RW; ++q) acc[q] = bias[o];
+                        for (int q = 0; q < RW; ++q) acc[q] = bias[o];
 #pragma unroll
-                for (int k = 0; k < NIN; ++k) {
-                    const float *wk = wt[BWD ? k : o];
+                        for (int k = 0; k < NIN; ++k) {
+                            const float *wk = wt[BWD ? k : o];
 #pragma unroll
-                    for (int j = 0; j < 3; ++j)
+                            for (int i = 0; i < 3; ++i)
 #pragma unroll
-                        for (int q = 0; q < RW; ++q) {
-                            acc[q] = fmaf(wk[j], w0[k][q * S + j], acc[q]);
-                            acc[q] = fmaf(wk[3 + j], w1[k][q * S + j], acc[q]);
-                            acc[q] = fmaf(wk[6 + j], w2[k][q * S + j], acc[q]);
+                                for (int j = 0; j < 3; ++j)
+#pragma unroll
+                                    for (int q = 0; q < RW; ++q)
+                                        acc[q] = fmaf(wk[3 * i + j], win[k][(S * uu + i) % 3][q * S + j], acc[q]);
                         }
+                        T *op = a.out + ((static_cast<int64_t>(P) * NOUT + o) * OH + oh) * OW + c_out;
+                        store_values<T, RW, FULL>(op, acc, OW - c_out);
+                    }
                 }
-                T *op = a.out + ((static_cast<int64_t>(P) * NOUT + o) * OH + oh) * OW + c_out;
-                store_seg<T, RW>(op, acc, OW - c_out, a.vout != 0);
             }
         }
-        // slide the window down
-#pragma unroll
-        for (int k = 0; k < NIN; ++k)
-#pragma unroll
-            for (int e = 0; e < WW; ++e) {
-                if constexpr (S == 1) {
-                    w0[k][e] = w1[k][e];
-                    w1[k][e] = w2[k][e];
-                } else {
-                    w0[k][e] = w2[k][e];
-                }
-            }
     }
 }
 
@@ -238,84 +183,60 @@ __global__ __launch_bounds__(kThreads) void rw_conv3_kernel(RwArgs<T> a) {
 // DRW = RW/2 dy columns [c0, c0+DRW) and writes the RW dx columns [2c0, 2c0+RW)
 // of dx rows 2r and 2r+1 as one 16-byte store each, so every store instruction
 // of a wave covers one contiguous run of dx.
-template <typename T, int DRW>
-__device__ __forceinline__ void load_half(const T *plane, int r, int H, int W, int c0, bool vec, bool act,
-                                          float (&v)[DRW]) {
-    static_assert(sizeof(T) * DRW == 8, "half strip is 8 bytes");
-#pragma unroll
-    for (int e = 0; e < DRW; ++e) v[e] = 0.f;
-    if (!act || r < 0 || r >= H) return;
-    const T *p = plane + static_cast<int64_t>(r) * W + c0;
-    if (vec && c0 + DRW <= W) {
-        union {
-            uint2 u;
-            T t[DRW];
-        } b;
-        b.u = *reinterpret_cast<const uint2 *>(p);
-#pragma unroll
-        for (int e = 0; e < DRW; ++e) v[e] = to_f32(b.t[e]);
-    } else {
-#pragma unroll
-        for (int e = 0; e < DRW; ++e)
-            if (c0 + e < W) v[e] = to_f32(p[e]);
-    }
-}
-
-template <typename T, int MM>
+template <typename T, int MM, bool FULL>
 __global__ __launch_bounds__(kThreads) void rw_bwdin3_s2_kernel(RwArgs<T> a) {
     constexpr int RW = Vec<T>::N;
     constexpr int DRW = RW / 2;
+    constexpr int ND = DRW / kPerWord<T>;  // raw words of a half strip (8 bytes)
+    constexpr int R = 3;                   // dy rows in flight
     const Geo &g = a.g;
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int slot = lane / a.NS;
-    const int s = lane - slot * a.NS;
-    const int unit = (blockIdx.x * kWaves + wave) * a.SPW + slot;
-    const bool act = slot < a.SPW && unit < a.nunits;
-    const int P = act ? unit / a.nbands : 0;
-    const int band = act ? unit - P * a.nbands : 0;
-    const int c0 = s * DRW;
-    const bool has_right = s < a.NS - 1;
-    const int ic = P % g.ic;
+    const WaveUnit u = wave_unit(a.wpc, a.NS, a.SPW, a.nunits, a.nbands, g.ic);
+    const int c0 = u.s * DRW;
+    const bool has_right = u.s < a.NS - 1;
     float wt[MM][9];
 #pragma unroll
     for (int m = 0; m < MM; ++m)
 #pragma unroll
-        for (int t = 0; t < 9; ++t) wt[m][t] = act ? to_f32(a.w[(ic * MM + m) * 9 + t]) : 0.f;
+        for (int t = 0; t < 9; ++t) wt[m][t] = uniform(to_f32(a.w[(u.ic * MM + m) * 9 + t]));
+    const int P = u.n * g.ic + u.ic;
     const int64_t dplane = static_cast<int64_t>(g.oh) * g.ow;
     const T *dp[MM];
 #pragma unroll
     for (int m = 0; m < MM; ++m) dp[m] = a.in + (static_cast<int64_t>(P) * MM + m) * dplane;
-    const int r0 = band * a.BH;
-    // dy row r (cur) and r+1 (nxt), each with the right neighbour column; the
-    // raw segment of row r+2 is loaded one step ahead (pre)
-    float cur[MM][DRW + 1], nxt[MM][DRW + 1], pre[MM][DRW];
-    const bool vin = a.vin != 0;
+    const int r0 = u.band * a.BH;
+    const int rlast = r0 + a.BH;  // last dy row any step reads (later refills re-read it)
+    // dy row r (cur) and r+1 (nxt), each with the right neighbour column
+    float cur[MM][DRW + 1], nxt[MM][DRW + 1];
+    uint32_t rq[MM][R][ND];
+    bool rk[MM][R];
 #pragma unroll
     for (int m = 0; m < MM; ++m) {
+        uint32_t w[ND];
+        bool ok;
         float v[DRW];
-        load_half<T, DRW>(dp[m], r0, g.oh, g.ow, c0, vin, act, v);
-        const float rr = __shfl(v[0], lane + 1, 64);
+        load_row<T, ND, FULL>(dp[m], r0, g.oh, g.ow, c0, u.act, w, ok);
+        row_values<T>(w, ok, v);
+        const float rr = __shfl(v[0], u.lane + 1, 64);
 #pragma unroll
         for (int e = 0; e < DRW; ++e) cur[m][e] = v[e];
         cur[m][DRW] = has_right ? rr : 0.f;
-        load_half<T, DRW>(dp[m], r0 + 1, g.oh, g.ow, c0, vin, act, pre[m]);
+#pragma unroll
+        for (int f = 0; f < R; ++f) load_row<T, ND, FULL>(dp[m], r0 + 1 + f, g.oh, g.ow, c0, u.act, rq[m][f], rk[m][f]);
     }
-    // dx rows 2r and 2r+1 for r in the band; the band covers dx rows [2*r0, 2*(r0+BH))
     for (int step = 0; step < a.BH; ++step) {
         const int r = r0 + step;
 #pragma unroll
         for (int m = 0; m < MM; ++m) {
             float v[DRW];
-#pragma unroll
-            for (int e = 0; e < DRW; ++e) v[e] = pre[m][e];
-            load_half<T, DRW>(dp[m], r + 2, g.oh, g.ow, c0, vin, act, pre[m]);
-            const float rr = __shfl(v[0], lane + 1, 64);
+            row_values<T>(rq[m][0], rk[m][0], v);
+            ring_pop<R, ND>(rq[m], rk[m]);
+            load_row<T, ND, FULL>(dp[m], min(r + 1 + R, rlast), g.oh, g.ow, c0, u.act, rq[m][R - 1], rk[m][R - 1]);
+            const float rr = __shfl(v[0], u.lane + 1, 64);
 #pragma unroll
             for (int e = 0; e < DRW; ++e) nxt[m][e] = v[e];
             nxt[m][DRW] = has_right ? rr : 0.f;
         }
-        if (act && 2 * r < g.ih) {
+        if (u.act && 2 * r < g.ih) {
             float e0[RW], e1[RW];  // dx rows 2r and 2r+1, columns 2c0 .. 2c0+RW-1
 #pragma unroll
             for (int q = 0; q < RW; ++q) e0[q] = e1[q] = 0.f;
@@ -333,8 +254,8 @@ __global__ __launch_bounds__(kThreads) void rw_bwdin3_s2_kernel(RwArgs<T> a) {
             }
             T *xp = a.out + (static_cast<int64_t>(P) * g.ih + 2 * r) * g.iw + 2 * c0;
             const int valid = g.iw - 2 * c0;
-            store_seg<T, RW>(xp, e0, valid, a.vout != 0);
-            if (2 * r + 1 < g.ih) store_seg<T, RW>(xp + g.iw, e1, valid, a.vout != 0);
+            store_values<T, RW, FULL>(xp, e0, valid);
+            if (2 * r + 1 < g.ih) store_values<T, RW, FULL>(xp + g.iw, e1, valid);
         }
 #pragma unroll
         for (int m = 0; m < MM; ++m)
@@ -344,20 +265,20 @@ __global__ __launch_bounds__(kThreads) void rw_bwdin3_s2_kernel(RwArgs<T> a) {
 }
 
 // ---------------------------------------------------------------- grad-weight
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
-}
-
 // Workgroup (ic, chunk): its lanes walk units (n, band) of input channel ic,
 // accumulating for each of the MM output channels the 9 taps and the bias sum;
-// one fixed-order workgroup reduction writes the chunk's partials.
-template <typename T, int S, int MM>
+// one fixed-order workgroup reduction writes the chunk's partials.  The x rows
+// move through the same window ring as the forward; dy rows are loaded ahead
+// as raw words too.
+template <typename T, int S, int MM, bool FULL>
 __global__ __launch_bounds__(kThreads) void rw_bwdw3_kernel(RwArgs<T> a) {
     constexpr int RW = Vec<T>::N;
     constexpr int IRW = RW * S;
     constexpr int WW = IRW + (S == 1 ? 2 : 1);
+    constexpr int NWI = IRW / kPerWord<T>;
+    constexpr int NWO = RW / kPerWord<T>;
+    constexpr int R = S * kAhead<S>;
+    constexpr int RD = kAhead<S>;  // dy rows in flight
     constexpr int A = MM * 10;
     __shared__ float red[kWaves][A];
     const Geo &g = a.g;
@@ -369,10 +290,11 @@ __global__ __launch_bounds__(kThreads) void rw_bwdw3_kernel(RwArgs<T> a) {
     const int chunk = blockIdx.x - ic * a.NC;
     const int c_in = s * IRW;
     const int c_out = s * RW;
-    const bool has_left = s > 0;
-    const bool has_right = s < a.NS - 1;
+    const bool hl = s > 0;
+    const bool hr = s < a.NS - 1;
     const int64_t xplane = static_cast<int64_t>(g.ih) * g.iw;
     const int64_t dplane = static_cast<int64_t>(g.oh) * g.ow;
+    const int jlast = S * (a.BH - 1) + 2;
 
     float acc[MM][10];
 #pragma unroll
@@ -391,79 +313,73 @@ __global__ __launch_bounds__(kThreads) void rw_bwdw3_kernel(RwArgs<T> a) {
         const T *dyp = a.in2 + (static_cast<int64_t>(n) * g.oc + ic * MM) * dplane;
         const int oh0 = band * a.BH;
         const int oh_end = min(oh0 + a.BH, g.oh);
-        const bool vin = a.vin != 0, vdy = a.vout != 0;
-        float w0[WW], w1[WW], w2[WW];
-        float nxa[IRW], nxb[IRW], ndy[MM][RW];  // next step's raw rows, loaded one step ahead
-        {
+        const int rb = S * oh0 - 1;
+        float win[3][WW];
+        uint32_t rq[R][NWI], gq[MM][RD][NWO];
+        bool rk[R], gk[MM][RD];
+#pragma unroll
+        for (int j = 0; j < 3 - S; ++j) {
+            uint32_t w[NWI];
+            bool ok;
             float v[IRW];
-            load_seg<T, IRW>(xp, S * oh0 - 1, g.ih, g.iw, c_in, vin, act, v);
-            make_window<IRW, S>(v, lane, has_left, has_right, w0);
-            if constexpr (S == 1) {
-                load_seg<T, IRW>(xp, oh0, g.ih, g.iw, c_in, vin, act, v);
-                make_window<IRW, S>(v, lane, has_left, has_right, w1);
-                load_seg<T, IRW>(xp, oh0 + 1, g.ih, g.iw, c_in, vin, act, nxb);
-            } else {
-                load_seg<T, IRW>(xp, 2 * oh0, g.ih, g.iw, c_in, vin, act, nxa);
-                load_seg<T, IRW>(xp, 2 * oh0 + 1, g.ih, g.iw, c_in, vin, act, nxb);
-            }
-#pragma unroll
-            for (int m = 0; m < MM; ++m)
-                load_seg<T, RW>(dyp + m * dplane, oh0, g.oh, g.ow, c_out, vdy, act && oh0 < oh_end, ndy[m]);
+            load_row<T, NWI, FULL>(xp, rb + j, g.ih, g.iw, c_in, act, w, ok);
+            row_values<T>(w, ok, v);
+            make_window<IRW, S>(v, lane, hl, hr, win[j]);
         }
-        for (int step = 0; step < a.BH; ++step) {
-            const int oh = oh0 + step;
-            float cb[IRW], gy[MM][RW];
 #pragma unroll
-            for (int e = 0; e < IRW; ++e) cb[e] = nxb[e];
+        for (int f = 0; f < R; ++f) load_row<T, NWI, FULL>(xp, rb + 3 - S + f, g.ih, g.iw, c_in, act, rq[f], rk[f]);
 #pragma unroll
-            for (int m = 0; m < MM; ++m)
+        for (int m = 0; m < MM; ++m)
 #pragma unroll
-                for (int q = 0; q < RW; ++q) gy[m][q] = ndy[m][q];
-            if constexpr (S == 2) {
-                float ca[IRW];
+            for (int f = 0; f < RD; ++f)
+                load_row<T, NWO, FULL>(dyp + m * dplane, oh0 + f, oh_end, g.ow, c_out, act, gq[m][f], gk[m][f]);
+        for (int t0 = 0; t0 < a.BH; t0 += 3) {
 #pragma unroll
-                for (int e = 0; e < IRW; ++e) ca[e] = nxa[e];
-                load_seg<T, IRW>(xp, 2 * oh + 2, g.ih, g.iw, c_in, vin, act, nxa);
-                load_seg<T, IRW>(xp, 2 * oh + 3, g.ih, g.iw, c_in, vin, act, nxb);
-                make_window<IRW, S>(ca, lane, has_left, has_right, w1);
-            } else {
-                load_seg<T, IRW>(xp, oh + 2, g.ih, g.iw, c_in, vin, act, nxb);
-            }
+            for (int uu = 0; uu < 3; ++uu) {
+                const int t = t0 + uu;
+                if (t < a.BH) {
 #pragma unroll
-            for (int m = 0; m < MM; ++m)
-                load_seg<T, RW>(dyp + m * dplane, oh + 1, g.oh, g.ow, c_out, vdy, act && oh + 1 < oh_end, ndy[m]);
-            make_window<IRW, S>(cb, lane, has_left, has_right, w2);
-#pragma unroll
-            for (int m = 0; m < MM; ++m) {
-#pragma unroll
-                for (int q = 0; q < RW; ++q) {
-                    acc[m][9] += gy[m][q];
-#pragma unroll
-                    for (int j = 0; j < 3; ++j) {
-                        acc[m][j] = fmaf(gy[m][q], w0[q * S + j], acc[m][j]);
-                        acc[m][3 + j] = fmaf(gy[m][q], w1[q * S + j], acc[m][3 + j]);
-                        acc[m][6 + j] = fmaf(gy[m][q], w2[q * S + j], acc[m][6 + j]);
+                    for (int e = 0; e < S; ++e) {
+                        float v[IRW];
+                        row_values<T>(rq[0], rk[0], v);
+                        make_window<IRW, S>(v, lane, hl, hr, win[(S * uu + 3 - S + e) % 3]);
+                        ring_pop<R, NWI>(rq, rk);
+                        const int jn = min(S * t + 3 - S + e + R, jlast);
+                        load_row<T, NWI, FULL>(xp, rb + jn, g.ih, g.iw, c_in, act, rq[R - 1], rk[R - 1]);
                     }
-                }
-            }
+                    float gy[MM][RW];
 #pragma unroll
-            for (int e = 0; e < WW; ++e) {
-                if constexpr (S == 1) {
-                    w0[e] = w1[e];
-                    w1[e] = w2[e];
-                } else {
-                    w0[e] = w2[e];
+                    for (int m = 0; m < MM; ++m) {
+                        row_values<T>(gq[m][0], gk[m][0], gy[m]);
+                        ring_pop<RD, NWO>(gq[m], gk[m]);
+                        load_row<T, NWO, FULL>(dyp + m * dplane, oh0 + min(t + RD, a.BH - 1), oh_end, g.ow, c_out, act,
+                                               gq[m][RD - 1], gk[m][RD - 1]);
+                    }
+#pragma unroll
+                    for (int m = 0; m < MM; ++m)
+#pragma unroll
+                        for (int q = 0; q < RW; ++q) {
+                            acc[m][9] += gy[m][q];
+#pragma unroll
+                            for (int i = 0; i < 3; ++i)
+#pragma unroll
+                                for (int j = 0; j < 3; ++j)
+                                    acc[m][3 * i + j] =
+                                        fmaf(gy[m][q], win[(S * uu + i) % 3][q * S + j], acc[m][3 * i + j]);
+                        }
                 }
             }
         }
     }
+    {
+        float flat[A];
 #pragma unroll
-    for (int m = 0; m < MM; ++m)
+        for (int m = 0; m < MM; ++m)
 #pragma unroll
-        for (int t = 0; t < 10; ++t) {
-            const float v = wave_sum(acc[m][t]);
-            if (lane == 0) red[wave][m * 10 + t] = v;
-        }
+            for (int t = 0; t < 10; ++t) flat[m * 10 + t] = acc[m][t];
+        const float v = wave_transpose_sum<A>(flat, lane);
+        if (lane < A) red[wave][lane] = v;
+    }
     __syncthreads();
     if (threadIdx.x < A) {
         float v = red[0][threadIdx.x];
@@ -475,7 +391,7 @@ __global__ __launch_bounds__(kThreads) void rw_bwdw3_kernel(RwArgs<T> a) {
 
 // ---------------------------------------------------------------- planning
 struct RwPlan {
-    int NS, SPW, BH, nbands, nunits, grid, NC, upc;
+    int NS, SPW, BH, nbands, nunits, wpc, grid, NC, upc;
 };
 
 // Strips of 16 bytes per row of the strip-defining tensor (output rows for the
@@ -490,6 +406,8 @@ inline int pick_bh(int64_t planes, int rows, int SPW, int min_bh) {
     const int nb = (rows + bh - 1) / bh;
     return (rows + nb - 1) / nb;
 }
+
+bool aligned16(const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
 
 }  // namespace
 
@@ -524,33 +442,54 @@ bool rw_strip_layout(int width, RwPlan &p) {
     return true;
 }
 
-template <typename T, int S, int MM, bool BWD>
-int launch_conv3(const Geo &g, const void *in, const void *w, const void *b, void *out, hipStream_t st) {
-    constexpr int RW = Vec<T>::N;
-    RwPlan p;
-    const int OW = BWD ? g.iw : g.ow, OH = BWD ? g.ih : g.oh;
-    const int IW = BWD ? g.ow : g.iw;
-    if (!rw_strip_layout<T>(OW, p)) return kErrUnsupported;
+// Channel-uniform waves over units (image, band): wpc waves per channel.
+inline bool finish_plan(const Geo &g, RwPlan &p, int rows, int min_bh) {
     const int64_t planes = static_cast<int64_t>(g.n) * g.ic;
-    p.BH = pick_bh(planes, OH, p.SPW, 4);
-    p.nbands = (OH + p.BH - 1) / p.BH;
-    p.nunits = static_cast<int>(planes * p.nbands);
-    const int per_wg = kWaves * p.SPW;
-    p.grid = (p.nunits + per_wg - 1) / per_wg;
+    p.BH = pick_bh(planes, rows, p.SPW, min_bh);
+    p.nbands = (rows + p.BH - 1) / p.BH;
+    p.nunits = g.n * p.nbands;
+    p.wpc = (p.nunits + p.SPW - 1) / p.SPW;
+    const int64_t waves = static_cast<int64_t>(g.ic) * p.wpc;
+    if (waves > (int64_t{1} << 30)) return false;
+    p.grid = static_cast<int>((waves + kWaves - 1) / kWaves);
+    return true;
+}
+
+template <typename T>
+RwArgs<T> rw_args(const Geo &g, const RwPlan &p) {
     RwArgs<T> a{};
-    a.in = static_cast<const T *>(in);
-    a.w = static_cast<const T *>(w);
-    a.b = static_cast<const T *>(b);
-    a.out = static_cast<T *>(out);
     a.g = g;
     a.NS = p.NS;
     a.SPW = p.SPW;
     a.BH = p.BH;
     a.nbands = p.nbands;
     a.nunits = p.nunits;
-    a.vin = (IW % RW == 0) && (reinterpret_cast<uintptr_t>(in) % 16 == 0);
-    a.vout = (OW % RW == 0) && (reinterpret_cast<uintptr_t>(out) % 16 == 0);
-    hipLaunchKernelGGL((rw_conv3_kernel<T, S, MM, BWD>), dim3(p.grid), dim3(kThreads), 0, st, a);
+    a.wpc = p.wpc;
+    a.NC = p.NC;
+    a.upc = p.upc;
+    return a;
+}
+
+template <typename T, int S, int MM, bool BWD>
+int launch_conv3(const Geo &g, const void *in, const void *w, const void *b, void *out, hipStream_t st) {
+    constexpr int RW = Vec<T>::N;
+    RwPlan p{};
+    const int OW = BWD ? g.iw : g.ow, OH = BWD ? g.ih : g.oh;
+    const int IW = BWD ? g.ow : g.iw;
+    if (!rw_strip_layout<T>(OW, p)) return kErrUnsupported;
+    if (!finish_plan(g, p, OH, 4)) return kErrUnsupported;
+    RwArgs<T> a = rw_args<T>(g, p);
+    a.in = static_cast<const T *>(in);
+    a.w = static_cast<const T *>(w);
+    a.b = static_cast<const T *>(b);
+    a.out = static_cast<T *>(out);
+    // whole vectors: every strip [c_out, c_out+RW) and segment [S*c_out, S*c_out + S*RW)
+    // lies inside its row and every row starts 16-byte aligned
+    const bool full = OW % RW == 0 && IW == S * OW && aligned16(in) && aligned16(out);
+    if (full)
+        hipLaunchKernelGGL((rw_conv3_kernel<T, S, MM, BWD, true>), dim3(p.grid), dim3(kThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL((rw_conv3_kernel<T, S, MM, BWD, false>), dim3(p.grid), dim3(kThreads), 0, st, a);
     return hipGetLastError() == hipSuccess ? kOk : kErrHip;
 }
 
@@ -558,30 +497,23 @@ template <typename T, int MM>
 int launch_bwdin_s2(const Geo &g, const void *dy, const void *w, void *dx, hipStream_t st) {
     constexpr int RW = Vec<T>::N;
     constexpr int DRW = RW / 2;
-    RwPlan p;
+    RwPlan p{};
     p.NS = (g.ow + DRW - 1) / DRW;  // half strips of dy columns
     if (p.NS > 64) return kErrUnsupported;
     p.SPW = 64 / p.NS;
     // dx must be covered by dy rows/cols: 2*oh >= ih and 2*ow >= iw hold for pad 1, k 3, stride 2
-    const int64_t planes = static_cast<int64_t>(g.n) * g.ic;
-    p.BH = pick_bh(planes, g.oh, p.SPW, 2);
-    p.nbands = (g.oh + p.BH - 1) / p.BH;
-    p.nunits = static_cast<int>(planes * p.nbands);
-    const int per_wg = kWaves * p.SPW;
-    p.grid = (p.nunits + per_wg - 1) / per_wg;
-    RwArgs<T> a{};
+    if (!finish_plan(g, p, g.oh, 2)) return kErrUnsupported;
+    RwArgs<T> a = rw_args<T>(g, p);
     a.in = static_cast<const T *>(dy);
     a.w = static_cast<const T *>(w);
     a.out = static_cast<T *>(dx);
-    a.g = g;
-    a.NS = p.NS;
-    a.SPW = p.SPW;
-    a.BH = p.BH;
-    a.nbands = p.nbands;
-    a.nunits = p.nunits;
-    a.vin = (g.ow % DRW == 0) && (reinterpret_cast<uintptr_t>(dy) % 8 == 0);
-    a.vout = (g.iw % RW == 0) && (reinterpret_cast<uintptr_t>(dx) % 16 == 0);
-    hipLaunchKernelGGL((rw_bwdin3_s2_kernel<T, MM>), dim3(p.grid), dim3(kThreads), 0, st, a);
+    // whole vectors: dy half strips inside their rows (8-byte aligned) and dx
+    // runs [2c0, 2c0+RW) inside theirs (16-byte aligned)
+    const bool full = g.ow % DRW == 0 && g.iw == 2 * g.ow && aligned16(dy) && aligned16(dx);
+    if (full)
+        hipLaunchKernelGGL((rw_bwdin3_s2_kernel<T, MM, true>), dim3(p.grid), dim3(kThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL((rw_bwdin3_s2_kernel<T, MM, false>), dim3(p.grid), dim3(kThreads), 0, st, a);
     return hipGetLastError() == hipSuccess ? kOk : kErrHip;
 }
 
@@ -606,21 +538,15 @@ bool plan_bwdw(const Geo &g, RwPlan &p) {
 template <typename T, int S, int MM>
 int launch_bwdw(const Geo &g, const RwPlan &p, const void *x, const void *dy, void *ws, hipStream_t st) {
     constexpr int RW = Vec<T>::N;
-    RwArgs<T> a{};
+    RwArgs<T> a = rw_args<T>(g, p);
     a.in = static_cast<const T *>(x);
     a.in2 = static_cast<const T *>(dy);
     a.ws = static_cast<float *>(ws);
-    a.g = g;
-    a.NS = p.NS;
-    a.SPW = p.SPW;
-    a.BH = p.BH;
-    a.nbands = p.nbands;
-    a.nunits = p.nunits;
-    a.NC = p.NC;
-    a.upc = p.upc;
-    a.vin = (g.iw % RW == 0) && (reinterpret_cast<uintptr_t>(x) % 16 == 0);
-    a.vout = (g.ow % RW == 0) && (reinterpret_cast<uintptr_t>(dy) % 16 == 0);
-    hipLaunchKernelGGL((rw_bwdw3_kernel<T, S, MM>), dim3(p.grid), dim3(kThreads), 0, st, a);
+    const bool full = g.ow % RW == 0 && g.iw == S * g.ow && aligned16(x) && aligned16(dy);
+    if (full)
+        hipLaunchKernelGGL((rw_bwdw3_kernel<T, S, MM, true>), dim3(p.grid), dim3(kThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL((rw_bwdw3_kernel<T, S, MM, false>), dim3(p.grid), dim3(kThreads), 0, st, a);
     return hipGetLastError() == hipSuccess ? kOk : kErrHip;
 }
 

@@ -1,0 +1,220 @@
+// dw_stream.hpp -- device helpers of the streaming (row-walk) kernels:
+// rows moved as raw 32-bit words so that loads issued ahead stay in flight
+// until the row is used, element access and rounding on those words, and
+// wave-level reductions.
+#pragma once
+
+#include "dw_common.hpp"
+#include "dw_internal.hpp"
+
+#include <type_traits>
+
+namespace dw {
+
+// Elements of T per 32-bit word.
+template <typename T> constexpr int kPerWord = 4 / static_cast<int>(sizeof(T));
+
+__device__ __forceinline__ uint32_t bits_of(float v) { return __float_as_uint(v); }
+__device__ __forceinline__ uint32_t bits_of(__half v) { return __half_as_ushort(v); }
+__device__ __forceinline__ uint32_t bits_of(bf16_t v) { return v.bits; }
+
+template <typename T> __device__ __forceinline__ T from_bits(uint32_t b);
+template <> __device__ __forceinline__ float from_bits<float>(uint32_t b) { return __uint_as_float(b); }
+template <> __device__ __forceinline__ __half from_bits<__half>(uint32_t b) {
+    return __ushort_as_half(static_cast<unsigned short>(b));
+}
+template <> __device__ __forceinline__ bf16_t from_bits<bf16_t>(uint32_t b) {
+    bf16_t r;
+    r.bits = static_cast<uint16_t>(b);
+    return r;
+}
+
+// Element e of a packed run of words, as fp32 (e is a constant after unrolling).
+template <typename T, int NW>
+__device__ __forceinline__ float word_elem(const uint32_t (&w)[NW], int e) {
+    if constexpr (sizeof(T) == 4) {
+        return __uint_as_float(w[e]);
+    } else {
+        const uint32_t h = (e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xffffu);
+        if constexpr (std::is_same<T, bf16_t>::value)
+            return __uint_as_float(h << 16);
+        else
+            return __half2float(__ushort_as_half(static_cast<unsigned short>(h)));
+    }
+}
+
+// NW words from NW * kPerWord<T> fp32 values, each rounded to T.
+template <typename T, int NW>
+__device__ __forceinline__ void pack_words(const float *v, uint32_t (&w)[NW]) {
+#pragma unroll
+    for (int k = 0; k < NW; ++k) {
+        if constexpr (sizeof(T) == 4)
+            w[k] = __float_as_uint(v[k]);
+        else
+            w[k] = bits_of(from_f32<T>(v[2 * k])) | (bits_of(from_f32<T>(v[2 * k + 1])) << 16);
+    }
+}
+
+template <int NW>
+__device__ __forceinline__ void load_words(const void *p, uint32_t (&w)[NW]) {
+    if constexpr (NW == 2) {
+        const uint2 u = *reinterpret_cast<const uint2 *>(p);
+        w[0] = u.x;
+        w[1] = u.y;
+    } else {
+        static_assert(NW % 4 == 0, "whole 16-byte vectors");
+#pragma unroll
+        for (int k = 0; k < NW / 4; ++k) {
+            const uint4 u = reinterpret_cast<const uint4 *>(p)[k];
+            w[4 * k] = u.x;
+            w[4 * k + 1] = u.y;
+            w[4 * k + 2] = u.z;
+            w[4 * k + 3] = u.w;
+        }
+    }
+}
+
+template <int NW>
+__device__ __forceinline__ void store_words(void *p, const uint32_t (&w)[NW]) {
+    if constexpr (NW == 2) {
+        *reinterpret_cast<uint2 *>(p) = make_uint2(w[0], w[1]);
+    } else {
+        static_assert(NW % 4 == 0, "whole 16-byte vectors");
+#pragma unroll
+        for (int k = 0; k < NW / 4; ++k)
+            reinterpret_cast<uint4 *>(p)[k] = make_uint4(w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]);
+    }
+}
+
+// The same words assembled element by element; elements at index >= avail read as zero.
+template <typename T, int NW>
+__device__ __forceinline__ void load_words_tail(const T *p, int avail, uint32_t (&w)[NW]) {
+    constexpr int PW = kPerWord<T>;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int e = 0; e < PW; ++e)
+            if (k * PW + e < avail) v |= bits_of(p[k * PW + e]) << (16 * e);
+        w[k] = v;
+    }
+}
+
+template <typename T, int NW>
+__device__ __forceinline__ void store_words_tail(T *p, int avail, const uint32_t (&w)[NW]) {
+    constexpr int PW = kPerWord<T>;
+#pragma unroll
+    for (int k = 0; k < NW; ++k)
+#pragma unroll
+        for (int e = 0; e < PW; ++e)
+            if (k * PW + e < avail) p[k * PW + e] = from_bits<T>(PW == 1 ? w[k] : (w[k] >> (16 * e)) & 0xffffu);
+}
+
+// Wave-uniform value kept in a scalar register (the filter taps of a channel).
+__device__ __forceinline__ float uniform(float v) {
+    return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+}
+
+// Sums of N <= 64 per-lane values over the wave, by recursive halving: at the
+// step with lane offset o every lane keeps one half of its current vector,
+// sends the other half to lane ^ o and adds what it receives, so after six
+// steps lane l holds the total of value l (63 shuffles instead of 6 per value).
+template <int N>
+__device__ __forceinline__ float wave_transpose_sum(const float (&v)[N], int lane) {
+    static_assert(N <= 64, "one value per lane");
+    float c[64];
+#pragma unroll
+    for (int i = 0; i < 64; ++i) c[i] = i < N ? v[i] : 0.f;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        const bool upper = (lane & o) != 0;  // this lane keeps indices [o, 2o) of the current vector
+#pragma unroll
+        for (int i = 0; i < o; ++i) {
+            const float keep = upper ? c[i + o] : c[i];
+            const float send = upper ? c[i] : c[i + o];
+            c[i] = keep + __shfl_xor(send, o, 64);
+        }
+    }
+    return c[0];
+}
+
+// Drops the front of a ring of R raw rows: q[f] = q[f + 1]; the back slot is refilled by the caller.
+template <int R, int NW>
+__device__ __forceinline__ void ring_pop(uint32_t (&q)[R][NW], bool (&ok)[R]) {
+#pragma unroll
+    for (int f = 0; f + 1 < R; ++f) {
+#pragma unroll
+        for (int k = 0; k < NW; ++k) q[f][k] = q[f + 1][k];
+        ok[f] = ok[f + 1];
+    }
+}
+
+// Raw words of columns [c0, c0 + NW * kPerWord<T>) of row r of a plane with H
+// rows of W elements.  Rows outside [0, H) are read from the nearest row and
+// flagged !ok, so the load needs no branch; FULL promises the columns lie
+// inside the row and the address is aligned for whole-vector loads.
+template <typename T, int NW, bool FULL>
+__device__ __forceinline__ void load_row(const T *plane, int r, int H, int W, int c0, bool act, uint32_t (&w)[NW],
+                                         bool &ok) {
+    ok = act && r >= 0 && r < H;
+    const int rc = min(max(r, 0), H - 1);
+    const T *p = plane + static_cast<int64_t>(rc) * W + c0;
+    if constexpr (FULL)
+        load_words<NW>(p, w);
+    else
+        load_words_tail<T, NW>(p, W - c0, w);
+}
+
+// The N elements held in a raw row as fp32, zero when the row is flagged !ok.
+template <typename T, int N, int NW>
+__device__ __forceinline__ void row_values(const uint32_t (&w)[NW], bool ok, float (&v)[N]) {
+    static_assert(N <= NW * kPerWord<T>, "elements held in the words");
+#pragma unroll
+    for (int e = 0; e < N; ++e) v[e] = ok ? word_elem<T>(w, e) : 0.f;
+}
+
+// N fp32 values rounded to T and stored at p: whole vectors when FULL, else
+// element by element for the first `avail`.
+template <typename T, int N, bool FULL>
+__device__ __forceinline__ void store_values(T *p, const float (&v)[N], int avail) {
+    constexpr int NW = N / kPerWord<T>;
+    static_assert(NW * kPerWord<T> == N, "whole words");
+    if constexpr (FULL) {
+        uint32_t w[NW];
+        pack_words<T, NW>(v, w);
+        store_words<NW>(p, w);
+    } else {
+#pragma unroll
+        for (int q = 0; q < N; ++q)
+            if (q < avail) p[q] = from_f32<T>(v[q]);
+    }
+}
+
+// Wave -> work of the streaming kernels: wave wv of the grid serves channel
+// wv / wpc and its units [j*SPW, (j+1)*SPW), j = wv % wpc, a unit being one
+// (image, row band) pair; within the wave, slot = lane / NS picks the unit
+// and s = lane % NS the column strip.  Waves past the last channel are idle.
+struct WaveUnit {
+    int ic, n, band, lane, s;
+    bool act;
+};
+
+__device__ __forceinline__ WaveUnit wave_unit(int wpc, int NS, int SPW, int nunits, int nbands, int nch) {
+    WaveUnit u;
+    const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x) * (kThreads / 64) +
+                                                  static_cast<int>(threadIdx.x >> 6));
+    const int ic = wv / wpc;
+    const int jw = wv - ic * wpc;
+    const bool wave_ok = ic < nch;
+    u.ic = wave_ok ? ic : nch - 1;
+    u.lane = threadIdx.x & 63;
+    const int slot = u.lane / NS;
+    u.s = u.lane - slot * NS;
+    const int ul = jw * SPW + slot;
+    u.act = wave_ok && slot < SPW && ul < nunits;
+    u.n = u.act ? ul / nbands : 0;
+    u.band = u.act ? ul - u.n * nbands : 0;
+    return u;
+}
+
+}  // namespace dw
