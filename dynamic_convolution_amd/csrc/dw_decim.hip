@@ -140,11 +140,11 @@ __global__ __launch_bounds__(kThreads) void dec_fwd_kernel(DcArgs<T> a) {
     }
 #pragma unroll
     for (int f = 0; f < kPF; ++f) load_xrow<T, FULL>(xp, oh0 - HH + K - 1 + f, a.XH, g.iw, c0, u.act, rq[f], rk[f]);
-    for (int t0 = 0; t0 < a.BH; t0 += K) {
+    for (int t0 = 0; t0 < a.BH; t0 += K) {  // BH is a multiple of K
 #pragma unroll
         for (int uu = 0; uu < K; ++uu) {
             const int t = t0 + uu;
-            if (t < a.BH) {
+            {
                 xrow_window<T, HH>(rq[0], rk[0], u.lane, hl, hr, win[(uu + K - 1) % K]);
                 ring_pop<kPF, NX>(rq, rk);
                 load_xrow<T, FULL>(xp, oh0 - HH + t + K - 1 + kPF, a.XH, g.iw, c0, u.act, rq[kPF - 1], rk[kPF - 1]);
@@ -221,11 +221,11 @@ __global__ __launch_bounds__(kThreads) void dec_bwdin_kernel(DcArgs<T> a) {
         for (int f = 0; f < kPF; ++f)
             load_drow<T, FULL>(dp[m], r0 - HH + K - 1 + f, g.oh, g.ow, c0, u.act, rq[m][f], rk[m][f]);
     }
-    for (int t0 = 0; t0 < a.BH; t0 += K) {
+    for (int t0 = 0; t0 < a.BH; t0 += K) {  // BH is a multiple of K
 #pragma unroll
         for (int uu = 0; uu < K; ++uu) {
             const int t = t0 + uu;
-            if (t < a.BH) {
+            {
 #pragma unroll
                 for (int m = 0; m < MM; ++m) {
                     float v[RO];
@@ -321,11 +321,11 @@ __global__ __launch_bounds__(kThreads) void dec_bwdw_kernel(DcArgs<T> a) {
             for (int m = 0; m < MM; ++m)
                 load_drow<T, FULL>(dyp + m * dplane, oh0 + f, oh_end, g.ow, c0, act, gq[m][f], gk[m][f]);
         }
-        for (int t0 = 0; t0 < a.BH; t0 += K) {
+        for (int t0 = 0; t0 < a.BH; t0 += K) {  // BH is a multiple of K
 #pragma unroll
             for (int uu = 0; uu < K; ++uu) {
                 const int t = t0 + uu;
-                if (t < a.BH) {
+                {
                     xrow_window<T, HH>(rq[0], rk[0], lane, hl, hr, win[(uu + K - 1) % K]);
                     ring_pop<kPF, NX>(rq, rk);
                     load_xrow<T, FULL>(xp, oh0 - HH + t + K - 1 + kPF, a.XH, g.iw, c0, act, rq[kPF - 1],
@@ -384,7 +384,9 @@ bool plan_dec(const Geo &g, int pass, DcPlan &p) {
     int bh = rows;
     while (bh > 4 && planes * ((rows + bh - 1) / bh) < int64_t{8192} * p.SPW / 2) bh = (bh + 1) / 2;
     p.nbands = (rows + bh - 1) / bh;
-    p.BH = (rows + p.nbands - 1) / p.nbands;
+    // rows per band, a multiple of k (the row loop's unroll factor; steps past
+    // the band's last row store nothing and read dy as zero)
+    p.BH = ((rows + p.nbands - 1) / p.nbands + g.kh - 1) / g.kh * g.kh;
     p.nbands = (rows + p.BH - 1) / p.BH;
     p.nunits = g.n * p.nbands;  // units per channel
     if (pass == 2) {

@@ -126,11 +126,11 @@ __global__ __launch_bounds__(kThreads) void rw_conv3_kernel(RwArgs<T> a) {
 #pragma unroll
         for (int f = 0; f < R; ++f) load_row<T, NWI, FULL>(inp[k], rb + 3 - S + f, IH, IW, c_in, u.act, rq[k][f], rk[k][f]);
     }
-    for (int t0 = 0; t0 < a.BH; t0 += 3) {
+    for (int t0 = 0; t0 < a.BH; t0 += 3) {  // BH is a multiple of 3
 #pragma unroll
         for (int uu = 0; uu < 3; ++uu) {
             const int t = t0 + uu;
-            if (t < a.BH) {
+            {
 #pragma unroll
                 for (int k = 0; k < NIN; ++k)
 #pragma unroll
@@ -333,11 +333,11 @@ __global__ __launch_bounds__(kThreads) void rw_bwdw3_kernel(RwArgs<T> a) {
 #pragma unroll
             for (int f = 0; f < RD; ++f)
                 load_row<T, NWO, FULL>(dyp + m * dplane, oh0 + f, oh_end, g.ow, c_out, act, gq[m][f], gk[m][f]);
-        for (int t0 = 0; t0 < a.BH; t0 += 3) {
+        for (int t0 = 0; t0 < a.BH; t0 += 3) {  // BH is a multiple of 3
 #pragma unroll
             for (int uu = 0; uu < 3; ++uu) {
                 const int t = t0 + uu;
-                if (t < a.BH) {
+                {
 #pragma unroll
                     for (int e = 0; e < S; ++e) {
                         float v[IRW];
@@ -443,9 +443,11 @@ bool rw_strip_layout(int width, RwPlan &p) {
 }
 
 // Channel-uniform waves over units (image, band): wpc waves per channel.
-inline bool finish_plan(const Geo &g, RwPlan &p, int rows, int min_bh) {
+// Bands of BH rows, BH rounded up to a multiple of `step` (the row loop's
+// unroll factor: steps past the band's last row compute nothing that is stored).
+inline bool finish_plan(const Geo &g, RwPlan &p, int rows, int min_bh, int step) {
     const int64_t planes = static_cast<int64_t>(g.n) * g.ic;
-    p.BH = pick_bh(planes, rows, p.SPW, min_bh);
+    p.BH = (pick_bh(planes, rows, p.SPW, min_bh) + step - 1) / step * step;
     p.nbands = (rows + p.BH - 1) / p.BH;
     p.nunits = g.n * p.nbands;
     p.wpc = (p.nunits + p.SPW - 1) / p.SPW;
@@ -477,7 +479,7 @@ int launch_conv3(const Geo &g, const void *in, const void *w, const void *b, voi
     const int OW = BWD ? g.iw : g.ow, OH = BWD ? g.ih : g.oh;
     const int IW = BWD ? g.ow : g.iw;
     if (!rw_strip_layout<T>(OW, p)) return kErrUnsupported;
-    if (!finish_plan(g, p, OH, 4)) return kErrUnsupported;
+    if (!finish_plan(g, p, OH, 4, 3)) return kErrUnsupported;
     RwArgs<T> a = rw_args<T>(g, p);
     a.in = static_cast<const T *>(in);
     a.w = static_cast<const T *>(w);
@@ -502,7 +504,7 @@ int launch_bwdin_s2(const Geo &g, const void *dy, const void *w, void *dx, hipSt
     if (p.NS > 64) return kErrUnsupported;
     p.SPW = 64 / p.NS;
     // dx must be covered by dy rows/cols: 2*oh >= ih and 2*ow >= iw hold for pad 1, k 3, stride 2
-    if (!finish_plan(g, p, g.oh, 2)) return kErrUnsupported;
+    if (!finish_plan(g, p, g.oh, 2, 1)) return kErrUnsupported;
     RwArgs<T> a = rw_args<T>(g, p);
     a.in = static_cast<const T *>(dy);
     a.w = static_cast<const T *>(w);
@@ -520,7 +522,7 @@ int launch_bwdin_s2(const Geo &g, const void *dy, const void *w, void *dx, hipSt
 template <typename T>
 bool plan_bwdw(const Geo &g, RwPlan &p) {
     if (!rw_strip_layout<T>(g.ow, p)) return false;
-    p.BH = pick_bh(static_cast<int64_t>(g.n) * g.ic, g.oh, p.SPW, 4);
+    p.BH = (pick_bh(static_cast<int64_t>(g.n) * g.ic, g.oh, p.SPW, 4) + 2) / 3 * 3;  // unroll factor 3
     p.nbands = (g.oh + p.BH - 1) / p.BH;
     p.nunits = g.n * p.nbands;  // per channel
     const int per_round = kWaves * p.SPW;

@@ -138,7 +138,11 @@ __device__ __forceinline__ float wave_transpose_sum(const float (&v)[N], int lan
     return c[0];
 }
 
-// Drops the front of a ring of R raw rows: q[f] = q[f + 1]; the back slot is refilled by the caller.
+// Drops the front of a ring of R raw rows: q[f] = q[f + 1]; the back slot is
+// refilled by the caller.  Call it after the front row has been used: the
+// scheduling barrier keeps the refill load below that use, so the register
+// allocator can give each refill the registers of the row it replaces and the
+// ring needs no copies (a copy of a row still in flight would wait for it).
 template <int R, int NW>
 __device__ __forceinline__ void ring_pop(uint32_t (&q)[R][NW], bool (&ok)[R]) {
 #pragma unroll
@@ -147,6 +151,7 @@ __device__ __forceinline__ void ring_pop(uint32_t (&q)[R][NW], bool (&ok)[R]) {
         for (int k = 0; k < NW; ++k) q[f][k] = q[f + 1][k];
         ok[f] = ok[f + 1];
     }
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 // Raw words of columns [c0, c0 + NW * kPerWord<T>) of row r of a plane with H
