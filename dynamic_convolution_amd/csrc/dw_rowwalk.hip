@@ -74,7 +74,7 @@ template <int S> constexpr int kAhead = S == 1 ? 3 : 2;
 // Relative input row j (row S*oh0 - 1 + j of the band) lives in window slot
 // j % 3; output step t reads rows S*t .. S*t + 2 and brings in the S rows
 // S*t + 3 - S .. S*t + 2.
-template <typename T, int S, int MM, bool BWD, bool FULL>
+template <typename T, int S, int MM, bool BWD, int VB>
 __global__ __launch_bounds__(kThreads) void rw_conv3_kernel(RwArgs<T> a) {
     constexpr int RW = Vec<T>::N;
     constexpr int IRW = RW * S;
@@ -99,6 +99,7 @@ __global__ __launch_bounds__(kThreads) void rw_conv3_kernel(RwArgs<T> a) {
     const int IH = BWD ? g.oh : g.ih, IW = BWD ? g.ow : g.iw;  // rows/cols of the input planes
     const int OH = BWD ? g.ih : g.oh, OW = BWD ? g.iw : g.ow;
     const int c_in = u.s * IRW, c_out = u.s * RW;
+    const int nin = VB == 16 ? IRW : IW - c_in;  // valid columns of the lane's input segment
     const bool hl = u.s > 0, hr = u.s < a.NS - 1;
     const int64_t in_plane = static_cast<int64_t>(IH) * IW;
     const T *inp[NIN];
@@ -119,12 +120,12 @@ __global__ __launch_bounds__(kThreads) void rw_conv3_kernel(RwArgs<T> a) {
             uint32_t w[NWI];
             bool ok;
             float v[IRW];
-            load_row<T, NWI, FULL>(inp[k], rb + j, IH, IW, c_in, u.act, w, ok);
-            row_values<T>(w, ok, v);
+            load_row<T, NWI, VB>(inp[k], rb + j, IH, IW, c_in, u.act, w, ok);
+            row_values<T>(w, ok, nin, v);
             make_window<IRW, S>(v, u.lane, hl, hr, win[k][j]);
         }
 #pragma unroll
-        for (int f = 0; f < R; ++f) load_row<T, NWI, FULL>(inp[k], rb + 3 - S + f, IH, IW, c_in, u.act, rq[k][f], rk[k][f]);
+        for (int f = 0; f < R; ++f) load_row<T, NWI, VB>(inp[k], rb + 3 - S + f, IH, IW, c_in, u.act, rq[k][f], rk[k][f]);
     }
     for (int t0 = 0; t0 < a.BH; t0 += 3) {  // BH is a multiple of 3
 #pragma unroll
@@ -136,14 +137,14 @@ __global__ __launch_bounds__(kThreads) void rw_conv3_kernel(RwArgs<T> a) {
 #pragma unroll
                     for (int e = 0; e < S; ++e) {
                         float v[IRW];
-                        row_values<T>(rq[k][0], rk[k][0], v);
+                        row_values<T>(rq[k][0], rk[k][0], nin, v);
                         make_window<IRW, S>(v, u.lane, hl, hr, win[k][(S * uu + 3 - S + e) % 3]);
                         ring_pop<R, NWI>(rq[k], rk[k]);
                         // refill with relative row S*t + 3 - S + e + R; past the last row a
                         // step reads, re-read that row (a cache hit, never used) so the
                         // load stays unconditional
                         const int jn = min(S * t + 3 - S + e + R, jlast);
-                        load_row<T, NWI, FULL>(inp[k], rb + jn, IH, IW, c_in, u.act, rq[k][R - 1], rk[k][R - 1]);
+                        load_row<T, NWI, VB>(inp[k], rb + jn, IH, IW, c_in, u.act, rq[k][R - 1], rk[k][R - 1]);
                     }
                 const int oh = oh0 + t;
                 if (u.act && oh < oh_end) {
@@ -164,7 +165,7 @@ __global__ __launch_bounds__(kThreads) void rw_conv3_kernel(RwArgs<T> a) {
                                         acc[q] = fmaf(wk[3 * i + j], win[k][(S * uu + i) % 3][q * S + j], acc[q]);
                         }
                         T *op = a.out + ((static_cast<int64_t>(P) * NOUT + o) * OH + oh) * OW + c_out;
-                        store_values<T, RW, FULL>(op, acc, OW - c_out);
+                        store_values<T, RW, VB>(op, acc, OW - c_out);
                     }
                 }
             }
@@ -183,15 +184,17 @@ __global__ __launch_bounds__(kThreads) void rw_conv3_kernel(RwArgs<T> a) {
 // DRW = RW/2 dy columns [c0, c0+DRW) and writes the RW dx columns [2c0, 2c0+RW)
 // of dx rows 2r and 2r+1 as one 16-byte store each, so every store instruction
 // of a wave covers one contiguous run of dx.
-template <typename T, int MM, bool FULL>
+template <typename T, int MM, int VB>
 __global__ __launch_bounds__(kThreads) void rw_bwdin3_s2_kernel(RwArgs<T> a) {
     constexpr int RW = Vec<T>::N;
     constexpr int DRW = RW / 2;
     constexpr int ND = DRW / kPerWord<T>;  // raw words of a half strip (8 bytes)
     constexpr int R = 3;                   // dy rows in flight
+    constexpr int VD = VB < 8 ? VB : 8;    // vector bytes of the dy loads
     const Geo &g = a.g;
     const WaveUnit u = wave_unit(a.wpc, a.NS, a.SPW, a.nunits, a.nbands, g.ic);
     const int c0 = u.s * DRW;
+    const int nd = VB == 16 ? DRW : g.ow - c0;  // valid dy columns of the half strip
     const bool has_right = u.s < a.NS - 1;
     float wt[MM][9];
 #pragma unroll
@@ -214,23 +217,23 @@ __global__ __launch_bounds__(kThreads) void rw_bwdin3_s2_kernel(RwArgs<T> a) {
         uint32_t w[ND];
         bool ok;
         float v[DRW];
-        load_row<T, ND, FULL>(dp[m], r0, g.oh, g.ow, c0, u.act, w, ok);
-        row_values<T>(w, ok, v);
+        load_row<T, ND, VD>(dp[m], r0, g.oh, g.ow, c0, u.act, w, ok);
+        row_values<T>(w, ok, nd, v);
         const float rr = __shfl(v[0], u.lane + 1, 64);
 #pragma unroll
         for (int e = 0; e < DRW; ++e) cur[m][e] = v[e];
         cur[m][DRW] = has_right ? rr : 0.f;
 #pragma unroll
-        for (int f = 0; f < R; ++f) load_row<T, ND, FULL>(dp[m], r0 + 1 + f, g.oh, g.ow, c0, u.act, rq[m][f], rk[m][f]);
+        for (int f = 0; f < R; ++f) load_row<T, ND, VD>(dp[m], r0 + 1 + f, g.oh, g.ow, c0, u.act, rq[m][f], rk[m][f]);
     }
     for (int step = 0; step < a.BH; ++step) {
         const int r = r0 + step;
 #pragma unroll
         for (int m = 0; m < MM; ++m) {
             float v[DRW];
-            row_values<T>(rq[m][0], rk[m][0], v);
+            row_values<T>(rq[m][0], rk[m][0], nd, v);
             ring_pop<R, ND>(rq[m], rk[m]);
-            load_row<T, ND, FULL>(dp[m], min(r + 1 + R, rlast), g.oh, g.ow, c0, u.act, rq[m][R - 1], rk[m][R - 1]);
+            load_row<T, ND, VD>(dp[m], min(r + 1 + R, rlast), g.oh, g.ow, c0, u.act, rq[m][R - 1], rk[m][R - 1]);
             const float rr = __shfl(v[0], u.lane + 1, 64);
 #pragma unroll
             for (int e = 0; e < DRW; ++e) nxt[m][e] = v[e];
@@ -254,8 +257,8 @@ __global__ __launch_bounds__(kThreads) void rw_bwdin3_s2_kernel(RwArgs<T> a) {
             }
             T *xp = a.out + (static_cast<int64_t>(P) * g.ih + 2 * r) * g.iw + 2 * c0;
             const int valid = g.iw - 2 * c0;
-            store_values<T, RW, FULL>(xp, e0, valid);
-            if (2 * r + 1 < g.ih) store_values<T, RW, FULL>(xp + g.iw, e1, valid);
+            store_values<T, RW, VB>(xp, e0, valid);
+            if (2 * r + 1 < g.ih) store_values<T, RW, VB>(xp + g.iw, e1, valid);
         }
 #pragma unroll
         for (int m = 0; m < MM; ++m)
@@ -270,8 +273,8 @@ __global__ __launch_bounds__(kThreads) void rw_bwdin3_s2_kernel(RwArgs<T> a) {
 // one fixed-order workgroup reduction writes the chunk's partials.  The x rows
 // move through the same window ring as the forward; dy rows are loaded ahead
 // as raw words too.
-template <typename T, int S, int MM, bool FULL>
-__global__ __launch_bounds__(kThreads) void rw_bwdw3_kernel(RwArgs<T> a) {
+template <typename T, int S, int MM, int VB>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu((sizeof(T) == 4 && S == 1 && MM == 1 && VB == 16) ? 6 : 1))) void rw_bwdw3_kernel(RwArgs<T> a) {
     constexpr int RW = Vec<T>::N;
     constexpr int IRW = RW * S;
     constexpr int WW = IRW + (S == 1 ? 2 : 1);
@@ -290,6 +293,8 @@ __global__ __launch_bounds__(kThreads) void rw_bwdw3_kernel(RwArgs<T> a) {
     const int chunk = blockIdx.x - ic * a.NC;
     const int c_in = s * IRW;
     const int c_out = s * RW;
+    const int nin = VB == 16 ? IRW : g.iw - c_in;   // valid columns of the x segment
+    const int nout = VB == 16 ? RW : g.ow - c_out;  // valid columns of the dy strip
     const bool hl = s > 0;
     const bool hr = s < a.NS - 1;
     const int64_t xplane = static_cast<int64_t>(g.ih) * g.iw;
@@ -322,17 +327,17 @@ __global__ __launch_bounds__(kThreads) void rw_bwdw3_kernel(RwArgs<T> a) {
             uint32_t w[NWI];
             bool ok;
             float v[IRW];
-            load_row<T, NWI, FULL>(xp, rb + j, g.ih, g.iw, c_in, act, w, ok);
-            row_values<T>(w, ok, v);
+            load_row<T, NWI, VB>(xp, rb + j, g.ih, g.iw, c_in, act, w, ok);
+            row_values<T>(w, ok, nin, v);
             make_window<IRW, S>(v, lane, hl, hr, win[j]);
         }
 #pragma unroll
-        for (int f = 0; f < R; ++f) load_row<T, NWI, FULL>(xp, rb + 3 - S + f, g.ih, g.iw, c_in, act, rq[f], rk[f]);
+        for (int f = 0; f < R; ++f) load_row<T, NWI, VB>(xp, rb + 3 - S + f, g.ih, g.iw, c_in, act, rq[f], rk[f]);
 #pragma unroll
         for (int m = 0; m < MM; ++m)
 #pragma unroll
             for (int f = 0; f < RD; ++f)
-                load_row<T, NWO, FULL>(dyp + m * dplane, oh0 + f, oh_end, g.ow, c_out, act, gq[m][f], gk[m][f]);
+                load_row<T, NWO, VB>(dyp + m * dplane, oh0 + f, oh_end, g.ow, c_out, act, gq[m][f], gk[m][f]);
         for (int t0 = 0; t0 < a.BH; t0 += 3) {  // BH is a multiple of 3
 #pragma unroll
             for (int uu = 0; uu < 3; ++uu) {
@@ -341,18 +346,18 @@ __global__ __launch_bounds__(kThreads) void rw_bwdw3_kernel(RwArgs<T> a) {
 #pragma unroll
                     for (int e = 0; e < S; ++e) {
                         float v[IRW];
-                        row_values<T>(rq[0], rk[0], v);
+                        row_values<T>(rq[0], rk[0], nin, v);
                         make_window<IRW, S>(v, lane, hl, hr, win[(S * uu + 3 - S + e) % 3]);
                         ring_pop<R, NWI>(rq, rk);
                         const int jn = min(S * t + 3 - S + e + R, jlast);
-                        load_row<T, NWI, FULL>(xp, rb + jn, g.ih, g.iw, c_in, act, rq[R - 1], rk[R - 1]);
+                        load_row<T, NWI, VB>(xp, rb + jn, g.ih, g.iw, c_in, act, rq[R - 1], rk[R - 1]);
                     }
                     float gy[MM][RW];
 #pragma unroll
                     for (int m = 0; m < MM; ++m) {
-                        row_values<T>(gq[m][0], gk[m][0], gy[m]);
+                        row_values<T>(gq[m][0], gk[m][0], nout, gy[m]);
                         ring_pop<RD, NWO>(gq[m], gk[m]);
-                        load_row<T, NWO, FULL>(dyp + m * dplane, oh0 + min(t + RD, a.BH - 1), oh_end, g.ow, c_out, act,
+                        load_row<T, NWO, VB>(dyp + m * dplane, oh0 + min(t + RD, a.BH - 1), oh_end, g.ow, c_out, act,
                                                gq[m][RD - 1], gk[m][RD - 1]);
                     }
 #pragma unroll
@@ -407,8 +412,6 @@ inline int pick_bh(int64_t planes, int rows, int SPW, int min_bh) {
     return (rows + nb - 1) / nb;
 }
 
-bool aligned16(const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
-
 }  // namespace
 
 bool rowwalk_applicable(const Geo &g, int pass) {
@@ -425,7 +428,7 @@ bool rowwalk_fits(const Geo &g, int dtype, int pass) {
     // strip-defining width: output rows (forward, grad-weight), dx rows (grad-input
     // stride 1) or dy rows (grad-input stride 2)
     const int width = pass == 1 ? (g.sh == 1 ? g.iw : g.ow) : g.ow;
-    if (pass == 1 && g.sh == 2) return (width + ve / 2 - 1) / (ve / 2) <= 64 && width >= 28;  // half strips of dy
+    if (pass == 1 && g.sh == 2) return (width + ve / 2 - 1) / (ve / 2) <= 64 && width >= 14;  // half strips of dy
     if ((width + ve - 1) / ve > 64) return false;
     // narrow rows leave most lanes of a slot idle; the LDS band kernels measure
     // faster there for the forward and grad-input (grad-weight streams always)
@@ -485,14 +488,13 @@ int launch_conv3(const Geo &g, const void *in, const void *w, const void *b, voi
     a.w = static_cast<const T *>(w);
     a.b = static_cast<const T *>(b);
     a.out = static_cast<T *>(out);
-    // whole vectors: every strip [c_out, c_out+RW) and segment [S*c_out, S*c_out + S*RW)
-    // lies inside its row and every row starts 16-byte aligned
-    const bool full = OW % RW == 0 && IW == S * OW && aligned16(in) && aligned16(out);
-    if (full)
-        hipLaunchKernelGGL((rw_conv3_kernel<T, S, MM, BWD, true>), dim3(p.grid), dim3(kThreads), 0, st, a);
-    else
-        hipLaunchKernelGGL((rw_conv3_kernel<T, S, MM, BWD, false>), dim3(p.grid), dim3(kThreads), 0, st, a);
-    return hipGetLastError() == hipSuccess ? kOk : kErrHip;
+    // vector width of the row accesses: 16 bytes means every strip [c_out, c_out+RW)
+    // and segment [S*c_out, S*(c_out+RW)) lies inside its row
+    const int vb = row_vector_bytes<T>({IW, OW}, {in, out});
+    return with_vector_bytes<T>(vb, [&](auto V) {
+        hipLaunchKernelGGL((rw_conv3_kernel<T, S, MM, BWD, decltype(V)::value>), dim3(p.grid), dim3(kThreads), 0, st, a);
+        return hipGetLastError() == hipSuccess ? kOk : kErrHip;
+    });
 }
 
 template <typename T, int MM>
@@ -509,14 +511,12 @@ int launch_bwdin_s2(const Geo &g, const void *dy, const void *w, void *dx, hipSt
     a.in = static_cast<const T *>(dy);
     a.w = static_cast<const T *>(w);
     a.out = static_cast<T *>(dx);
-    // whole vectors: dy half strips inside their rows (8-byte aligned) and dx
-    // runs [2c0, 2c0+RW) inside theirs (16-byte aligned)
-    const bool full = g.ow % DRW == 0 && g.iw == 2 * g.ow && aligned16(dy) && aligned16(dx);
-    if (full)
-        hipLaunchKernelGGL((rw_bwdin3_s2_kernel<T, MM, true>), dim3(p.grid), dim3(kThreads), 0, st, a);
-    else
-        hipLaunchKernelGGL((rw_bwdin3_s2_kernel<T, MM, false>), dim3(p.grid), dim3(kThreads), 0, st, a);
-    return hipGetLastError() == hipSuccess ? kOk : kErrHip;
+    // vector width of the row accesses (dy loads use at most 8 bytes, a half strip)
+    const int vb = row_vector_bytes<T>({g.ow, g.iw}, {dy, dx});
+    return with_vector_bytes<T>(vb, [&](auto V) {
+        hipLaunchKernelGGL((rw_bwdin3_s2_kernel<T, MM, decltype(V)::value>), dim3(p.grid), dim3(kThreads), 0, st, a);
+        return hipGetLastError() == hipSuccess ? kOk : kErrHip;
+    });
 }
 
 template <typename T>
@@ -544,12 +544,11 @@ int launch_bwdw(const Geo &g, const RwPlan &p, const void *x, const void *dy, vo
     a.in = static_cast<const T *>(x);
     a.in2 = static_cast<const T *>(dy);
     a.ws = static_cast<float *>(ws);
-    const bool full = g.ow % RW == 0 && g.iw == S * g.ow && aligned16(x) && aligned16(dy);
-    if (full)
-        hipLaunchKernelGGL((rw_bwdw3_kernel<T, S, MM, true>), dim3(p.grid), dim3(kThreads), 0, st, a);
-    else
-        hipLaunchKernelGGL((rw_bwdw3_kernel<T, S, MM, false>), dim3(p.grid), dim3(kThreads), 0, st, a);
-    return hipGetLastError() == hipSuccess ? kOk : kErrHip;
+    const int vb = row_vector_bytes<T>({g.iw, g.ow}, {x, dy});
+    return with_vector_bytes<T>(vb, [&](auto V) {
+        hipLaunchKernelGGL((rw_bwdw3_kernel<T, S, MM, decltype(V)::value>), dim3(p.grid), dim3(kThreads), 0, st, a);
+        return hipGetLastError() == hipSuccess ? kOk : kErrHip;
+    });
 }
 
 template <typename T>

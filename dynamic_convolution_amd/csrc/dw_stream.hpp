@@ -7,6 +7,7 @@
 #include "dw_common.hpp"
 #include "dw_internal.hpp"
 
+#include <initializer_list>
 #include <type_traits>
 
 namespace dw {
@@ -155,43 +156,82 @@ __device__ __forceinline__ void ring_pop(uint32_t (&q)[R][NW], bool (&ok)[R]) {
 }
 
 // Raw words of columns [c0, c0 + NW * kPerWord<T>) of row r of a plane with H
-// rows of W elements.  Rows outside [0, H) are read from the nearest row and
-// flagged !ok, so the load needs no branch; FULL promises the columns lie
-// inside the row and the address is aligned for whole-vector loads.
-template <typename T, int NW, bool FULL>
+// rows of W elements, read as vectors of VB bytes.  Rows outside [0, H) are
+// read from the nearest row and flagged !ok, so the load needs no branch.
+// VB == 16: the caller guarantees the columns lie inside the row (and the
+// alignment).  VB < 16: each vector's start is clamped to the row's last whole
+// vector, so the read stays inside the row; the caller masks the columns at
+// and beyond W when converting (row_values with nvalid = W - c0).  Requires
+// W * sizeof(T) to be a multiple of VB, at least VB, and a VB-aligned plane.
+template <typename T, int NW, int VB>
 __device__ __forceinline__ void load_row(const T *plane, int r, int H, int W, int c0, bool act, uint32_t (&w)[NW],
                                          bool &ok) {
+    static_assert(VB == 16 || VB == 8 || VB == 4 || VB == 2, "vector width");
+    static_assert(VB >= static_cast<int>(sizeof(T)), "whole elements");
     ok = act && r >= 0 && r < H;
     const int rc = min(max(r, 0), H - 1);
-    const T *p = plane + static_cast<int64_t>(rc) * W + c0;
-    if constexpr (FULL)
-        load_words<NW>(p, w);
-    else
-        load_words_tail<T, NW>(p, W - c0, w);
+    const T *row = plane + static_cast<int64_t>(rc) * W;
+    if constexpr (VB == 16) {
+        load_words<NW>(row + c0, w);
+    } else {
+        constexpr int VE = VB / static_cast<int>(sizeof(T));  // elements per vector
+        constexpr int NV = NW * 4 / VB;                         // vectors per segment
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            const T *q = row + min(c0 + k * VE, W - VE);
+            if constexpr (VB == 8) {
+                const uint2 u = *reinterpret_cast<const uint2 *>(q);
+                w[2 * k] = u.x;
+                w[2 * k + 1] = u.y;
+            } else if constexpr (VB == 4) {
+                w[k] = *reinterpret_cast<const uint32_t *>(q);
+            } else {
+                const uint32_t h = *reinterpret_cast<const uint16_t *>(q);
+                if (k & 1)
+                    w[k >> 1] |= h << 16;
+                else
+                    w[k >> 1] = h;
+            }
+        }
+    }
 }
 
-// The N elements held in a raw row as fp32, zero when the row is flagged !ok.
+// The N elements held in a raw row as fp32; zero when the row is flagged !ok
+// and for elements at index >= nvalid (columns past the end of the row).
 template <typename T, int N, int NW>
-__device__ __forceinline__ void row_values(const uint32_t (&w)[NW], bool ok, float (&v)[N]) {
+__device__ __forceinline__ void row_values(const uint32_t (&w)[NW], bool ok, int nvalid, float (&v)[N]) {
     static_assert(N <= NW * kPerWord<T>, "elements held in the words");
 #pragma unroll
-    for (int e = 0; e < N; ++e) v[e] = ok ? word_elem<T>(w, e) : 0.f;
+    for (int e = 0; e < N; ++e) v[e] = (ok && e < nvalid) ? word_elem<T>(w, e) : 0.f;
 }
 
-// N fp32 values rounded to T and stored at p: whole vectors when FULL, else
-// element by element for the first `avail`.
-template <typename T, int N, bool FULL>
+// N fp32 values rounded to T and stored at p as vectors of VB bytes: all of
+// them when VB == 16 (the caller guarantees the strip lies inside the row),
+// else only the vectors that start before `avail` (W * sizeof(T) a multiple
+// of VB, so a vector that starts inside the row ends inside it).
+template <typename T, int N, int VB>
 __device__ __forceinline__ void store_values(T *p, const float (&v)[N], int avail) {
     constexpr int NW = N / kPerWord<T>;
     static_assert(NW * kPerWord<T> == N, "whole words");
-    if constexpr (FULL) {
-        uint32_t w[NW];
-        pack_words<T, NW>(v, w);
+    uint32_t w[NW];
+    pack_words<T, NW>(v, w);
+    if constexpr (VB == 16) {
         store_words<NW>(p, w);
     } else {
+        constexpr int VE = VB / static_cast<int>(sizeof(T));
+        constexpr int NV = NW * 4 / VB;
 #pragma unroll
-        for (int q = 0; q < N; ++q)
-            if (q < avail) p[q] = from_f32<T>(v[q]);
+        for (int k = 0; k < NV; ++k) {
+            if (k * VE < avail) {
+                T *q = p + k * VE;
+                if constexpr (VB == 8)
+                    *reinterpret_cast<uint2 *>(q) = make_uint2(w[2 * k], w[2 * k + 1]);
+                else if constexpr (VB == 4)
+                    *reinterpret_cast<uint32_t *>(q) = w[k];
+                else
+                    *reinterpret_cast<uint16_t *>(q) = static_cast<uint16_t>((k & 1) ? w[k >> 1] >> 16 : w[k >> 1]);
+            }
+        }
     }
 }
 
@@ -220,6 +260,41 @@ __device__ __forceinline__ WaveUnit wave_unit(int wpc, int NS, int SPW, int nuni
     u.n = u.act ? ul / nbands : 0;
     u.band = u.act ? ul - u.n * nbands : 0;
     return u;
+}
+
+// Widest vector (16, 8, 4 or 2 bytes, at least one element of T) that divides
+// the byte length of every listed row width and every listed base address: the
+// VB for load_row / store_values on those rows (a row vector never straddles
+// two rows).  Never 0 for element-aligned bases, as 2- or 4-byte vectors fit.
+template <typename T>
+inline int row_vector_bytes(std::initializer_list<int> widths, std::initializer_list<const void *> bases) {
+    for (int vb = 16; vb >= static_cast<int>(sizeof(T)); vb /= 2) {
+        bool ok = true;
+        for (int w : widths) {
+            const int64_t bytes = static_cast<int64_t>(w) * static_cast<int64_t>(sizeof(T));
+            ok = ok && bytes % vb == 0 && bytes >= vb;
+        }
+        for (const void *p : bases) ok = ok && reinterpret_cast<uintptr_t>(p) % vb == 0;
+        if (ok) return vb;
+    }
+    return 0;
+}
+
+// Calls f(std::integral_constant<int, VB>) for the runtime vector width vb.
+template <typename T, typename F>
+int with_vector_bytes(int vb, F &&f) {
+    switch (vb) {
+        case 16: return f(std::integral_constant<int, 16>{});
+        case 8: return f(std::integral_constant<int, 8>{});
+        case 4:
+            if constexpr (sizeof(T) <= 4) return f(std::integral_constant<int, 4>{});
+            break;
+        case 2:
+            if constexpr (sizeof(T) <= 2) return f(std::integral_constant<int, 2>{});
+            break;
+        default: break;
+    }
+    return kErrUnsupported;
 }
 
 }  // namespace dw

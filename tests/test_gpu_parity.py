@@ -334,6 +334,13 @@ def test_full_size_dynamic_sampled(dtype):
     (2, 3, 31, 64, 1, 1, "f16"), (2, 3, 31, 64, 2, 2, "bf16"),  # 16-bit strips of 8
     (1, 2, 6, 512, 1, 1, "bf16"), (1, 2, 5, 1030, 1, 2, "f16"),
     (4, 1, 1, 1, 1, 1, "f32"), (2, 2, 2, 3, 1, 2, "f32"),       # degenerate planes
+    # rows whose byte length is not a multiple of 16: narrower clamped vector accesses
+    (2, 3, 19, 58, 1, 1, "f32"), (2, 3, 19, 58, 1, 2, "f32"),   # 232-byte rows: 8-byte vectors
+    (2, 2, 15, 57, 1, 1, "f32"), (2, 2, 15, 57, 2, 2, "f32"),   # 228-byte rows: 4-byte vectors
+    (2, 3, 14, 58, 1, 1, "bf16"), (2, 3, 14, 60, 2, 1, "f16"),  # 116 / 120-byte rows
+    (2, 2, 13, 57, 1, 1, "bf16"), (2, 2, 13, 57, 1, 2, "f16"),  # odd 16-bit rows: 2-byte vectors
+    (3, 4, 14, 14, 1, 1, "f32"), (3, 4, 28, 28, 1, 2, "f32"),   # narrow planes (grad-weight, grad-input s2)
+    (3, 4, 14, 14, 2, 2, "bf16"), (2, 3, 7, 7, 1, 1, "f32"),
 ])
 def test_streaming_3x3_shapes(n, c, h, w, mult, s, dt):
     x, wt, b, dy = static_case(n, c, h, w, mult, 3, s, 1, 1, DT[dt], 600 + h * 7 + w)
