@@ -74,7 +74,7 @@ template <int S> constexpr int kAhead = S == 1 ? 3 : 2;
 // Relative input row j (row S*oh0 - 1 + j of the band) lives in window slot
 // j % 3; output step t reads rows S*t .. S*t + 2 and brings in the S rows
 // S*t + 3 - S .. S*t + 2.
-template <typename T, int S, int MM, bool BWD, int VB>
+template <typename T, int S, int MM, bool BWD, int VB, bool CS>
 __global__ __launch_bounds__(kThreads) void rw_conv3_kernel(RwArgs<T> a) {
     constexpr int RW = Vec<T>::N;
     constexpr int IRW = RW * S;
@@ -85,15 +85,24 @@ __global__ __launch_bounds__(kThreads) void rw_conv3_kernel(RwArgs<T> a) {
     constexpr int NOUT = BWD ? 1 : MM;      // output planes per unit
     static_assert(!BWD || S == 1, "stride-2 grad-input has its own kernel");
     const Geo &g = a.g;
-    const WaveUnit u = wave_unit(a.wpc, a.NS, a.SPW, a.nunits, a.nbands, g.ic);
+    // CS: slots are consecutive channels of one image (taps per lane); else
+    // slots are (image, band) units of one channel (taps wave-uniform, in SGPRs)
+    const WaveUnit u = CS ? chan_unit(a.wpc, a.NS, a.SPW, g.ic, g.n)
+                          : wave_unit(a.wpc, a.NS, a.SPW, a.nunits, a.nbands, g.ic);
     float wt[MM][9];
     float bias[NOUT];
 #pragma unroll
     for (int m = 0; m < MM; ++m)
 #pragma unroll
-        for (int t = 0; t < 9; ++t) wt[m][t] = uniform(to_f32(a.w[(u.ic * MM + m) * 9 + (BWD ? 8 - t : t)]));
+        for (int t = 0; t < 9; ++t) {
+            const float v = to_f32(a.w[(u.ic * MM + m) * 9 + (BWD ? 8 - t : t)]);
+            wt[m][t] = CS ? v : uniform(v);
+        }
 #pragma unroll
-    for (int o = 0; o < NOUT; ++o) bias[o] = (!BWD && a.b) ? uniform(to_f32(a.b[u.ic * MM + o])) : 0.f;
+    for (int o = 0; o < NOUT; ++o) {
+        const float v = (!BWD && a.b) ? to_f32(a.b[u.ic * MM + o]) : 0.f;
+        bias[o] = CS ? v : uniform(v);
+    }
 
     const int P = u.n * g.ic + u.ic;  // plane (n, ic)
     const int IH = BWD ? g.oh : g.ih, IW = BWD ? g.ow : g.iw;  // rows/cols of the input planes
@@ -184,7 +193,7 @@ __global__ __launch_bounds__(kThreads) void rw_conv3_kernel(RwArgs<T> a) {
 // DRW = RW/2 dy columns [c0, c0+DRW) and writes the RW dx columns [2c0, 2c0+RW)
 // of dx rows 2r and 2r+1 as one 16-byte store each, so every store instruction
 // of a wave covers one contiguous run of dx.
-template <typename T, int MM, int VB>
+template <typename T, int MM, int VB, bool CS>
 __global__ __launch_bounds__(kThreads) void rw_bwdin3_s2_kernel(RwArgs<T> a) {
     constexpr int RW = Vec<T>::N;
     constexpr int DRW = RW / 2;
@@ -192,7 +201,8 @@ __global__ __launch_bounds__(kThreads) void rw_bwdin3_s2_kernel(RwArgs<T> a) {
     constexpr int R = 3;                   // dy rows in flight
     constexpr int VD = VB < 8 ? VB : 8;    // vector bytes of the dy loads
     const Geo &g = a.g;
-    const WaveUnit u = wave_unit(a.wpc, a.NS, a.SPW, a.nunits, a.nbands, g.ic);
+    const WaveUnit u = CS ? chan_unit(a.wpc, a.NS, a.SPW, g.ic, g.n)
+                          : wave_unit(a.wpc, a.NS, a.SPW, a.nunits, a.nbands, g.ic);
     const int c0 = u.s * DRW;
     const int nd = VB == 16 ? DRW : g.ow - c0;  // valid dy columns of the half strip
     const bool has_right = u.s < a.NS - 1;
@@ -200,7 +210,10 @@ __global__ __launch_bounds__(kThreads) void rw_bwdin3_s2_kernel(RwArgs<T> a) {
 #pragma unroll
     for (int m = 0; m < MM; ++m)
 #pragma unroll
-        for (int t = 0; t < 9; ++t) wt[m][t] = uniform(to_f32(a.w[(u.ic * MM + m) * 9 + t]));
+        for (int t = 0; t < 9; ++t) {
+            const float v = to_f32(a.w[(u.ic * MM + m) * 9 + t]);
+            wt[m][t] = CS ? v : uniform(v);
+        }
     const int P = u.n * g.ic + u.ic;
     const int64_t dplane = static_cast<int64_t>(g.oh) * g.ow;
     const T *dp[MM];
@@ -394,10 +407,135 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu((sizeo
     }
 }
 
+// Grad-weight for small planes with channel slots: workgroup (channel group,
+// image chunk); each of its waves walks whole planes of one image at a time
+// (images chunk*upc + wave, + 4, ...), its slots on SPW consecutive channels,
+// so each lane accumulates the taps of its own channel.  The partials of a
+// channel's NS strips and 4 waves are summed in a fixed order through LDS.
+template <typename T, int S, int MM, int VB>
+__global__ __launch_bounds__(kThreads) void rw_bwdw3_cs_kernel(RwArgs<T> a) {
+    constexpr int RW = Vec<T>::N;
+    constexpr int IRW = RW * S;
+    constexpr int WW = IRW + (S == 1 ? 2 : 1);
+    constexpr int NWI = IRW / kPerWord<T>;
+    constexpr int NWO = RW / kPerWord<T>;
+    constexpr int R = S * kAhead<S>;
+    constexpr int RD = kAhead<S>;
+    constexpr int A = MM * 10;
+    __shared__ float red[kWaves][64][A + 1];
+    const Geo &g = a.g;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int slot = lane / a.NS;
+    const int s = lane - slot * a.NS;
+    const int cg = blockIdx.x / a.NC;
+    const int chunk = blockIdx.x - cg * a.NC;
+    const int c = cg * a.SPW + slot;
+    const bool act = slot < a.SPW && c < g.ic;
+    const int cc = act ? c : 0;
+    const int c_in = s * IRW;
+    const int c_out = s * RW;
+    const int nin = VB == 16 ? IRW : g.iw - c_in;
+    const int nout = VB == 16 ? RW : g.ow - c_out;
+    const bool hl = s > 0;
+    const bool hr = s < a.NS - 1;
+    const int64_t xplane = static_cast<int64_t>(g.ih) * g.iw;
+    const int64_t dplane = static_cast<int64_t>(g.oh) * g.ow;
+    const int jlast = S * (a.BH - 1) + 2;
+
+    float acc[MM][10];
+#pragma unroll
+    for (int m = 0; m < MM; ++m)
+#pragma unroll
+        for (int t = 0; t < 10; ++t) acc[m][t] = 0.f;
+
+    const int n_end = min((chunk + 1) * a.upc, g.n);
+    for (int n = chunk * a.upc + wave; n < n_end; n += kWaves) {
+        const T *xp = a.in + (static_cast<int64_t>(n) * g.ic + cc) * xplane;
+        const T *dyp = a.in2 + (static_cast<int64_t>(n) * g.oc + cc * MM) * dplane;
+        const int rb = -1;
+        float win[3][WW];
+        uint32_t rq[R][NWI], gq[MM][RD][NWO];
+        bool rk[R], gk[MM][RD];
+#pragma unroll
+        for (int j = 0; j < 3 - S; ++j) {
+            uint32_t w[NWI];
+            bool ok;
+            float v[IRW];
+            load_row<T, NWI, VB>(xp, rb + j, g.ih, g.iw, c_in, act, w, ok);
+            row_values<T>(w, ok, nin, v);
+            make_window<IRW, S>(v, lane, hl, hr, win[j]);
+        }
+#pragma unroll
+        for (int f = 0; f < R; ++f) load_row<T, NWI, VB>(xp, rb + 3 - S + f, g.ih, g.iw, c_in, act, rq[f], rk[f]);
+#pragma unroll
+        for (int m = 0; m < MM; ++m)
+#pragma unroll
+            for (int f = 0; f < RD; ++f)
+                load_row<T, NWO, VB>(dyp + m * dplane, f, g.oh, g.ow, c_out, act, gq[m][f], gk[m][f]);
+        for (int t0 = 0; t0 < a.BH; t0 += 3) {  // BH is a multiple of 3
+#pragma unroll
+            for (int uu = 0; uu < 3; ++uu) {
+                const int t = t0 + uu;
+#pragma unroll
+                for (int e = 0; e < S; ++e) {
+                    float v[IRW];
+                    row_values<T>(rq[0], rk[0], nin, v);
+                    make_window<IRW, S>(v, lane, hl, hr, win[(S * uu + 3 - S + e) % 3]);
+                    ring_pop<R, NWI>(rq, rk);
+                    const int jn = min(S * t + 3 - S + e + R, jlast);
+                    load_row<T, NWI, VB>(xp, rb + jn, g.ih, g.iw, c_in, act, rq[R - 1], rk[R - 1]);
+                }
+                float gy[MM][RW];
+#pragma unroll
+                for (int m = 0; m < MM; ++m) {
+                    row_values<T>(gq[m][0], gk[m][0], nout, gy[m]);
+                    ring_pop<RD, NWO>(gq[m], gk[m]);
+                    load_row<T, NWO, VB>(dyp + m * dplane, min(t + RD, a.BH - 1), g.oh, g.ow, c_out, act,
+                                         gq[m][RD - 1], gk[m][RD - 1]);
+                }
+#pragma unroll
+                for (int m = 0; m < MM; ++m)
+#pragma unroll
+                    for (int q = 0; q < RW; ++q) {
+                        acc[m][9] += gy[m][q];
+#pragma unroll
+                        for (int i = 0; i < 3; ++i)
+#pragma unroll
+                            for (int j = 0; j < 3; ++j)
+                                acc[m][3 * i + j] = fmaf(gy[m][q], win[(S * uu + i) % 3][q * S + j], acc[m][3 * i + j]);
+                    }
+            }
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < MM; ++m)
+#pragma unroll
+        for (int t = 0; t < 10; ++t) red[wave][lane][m * 10 + t] = acc[m][t];
+    __syncthreads();
+    for (int e = threadIdx.x; e < a.SPW * A; e += kThreads) {
+        const int j = e / A;
+        const int k = e - j * A;
+        const int cj = cg * a.SPW + j;
+        if (cj < g.ic) {
+            float v = 0.f;
+            for (int w = 0; w < kWaves; ++w)
+                for (int q = 0; q < a.NS; ++q) v += red[w][j * a.NS + q][k];
+            a.ws[(static_cast<int64_t>(cj) * a.NC + chunk) * A + k] = v;
+        }
+    }
+}
+
 // ---------------------------------------------------------------- planning
 struct RwPlan {
     int NS, SPW, BH, nbands, nunits, wpc, grid, NC, upc;
+    bool cs;  // channel slots (small planes)
 };
+
+// Planes of at most this many outputs are walked with channel slots: the
+// slots of a wave then read one contiguous run of planes instead of one row of
+// each of 64/NS planes that lie a whole image apart.
+constexpr int64_t kCsMaxOut = 1024;
 
 // Strips of 16 bytes per row of the strip-defining tensor (output rows for the
 // forward, dy rows for grad-input stride 2, output rows for grad-weight).
@@ -460,6 +598,20 @@ inline bool finish_plan(const Geo &g, RwPlan &p, int rows, int min_bh, int step)
     return true;
 }
 
+// Channel-slot plan: one wave per (image, group of SPW channels), whole planes
+// of `rows` rows, rounded up to a multiple of `step`.
+inline bool cs_plan(const Geo &g, RwPlan &p, int rows, int step) {
+    p.cs = true;
+    p.BH = (rows + step - 1) / step * step;
+    p.nbands = 1;
+    p.nunits = 0;
+    p.wpc = (g.ic + p.SPW - 1) / p.SPW;
+    const int64_t waves = static_cast<int64_t>(g.n) * p.wpc;
+    if (waves > (int64_t{1} << 30)) return false;
+    p.grid = static_cast<int>((waves + kWaves - 1) / kWaves);
+    return true;
+}
+
 template <typename T>
 RwArgs<T> rw_args(const Geo &g, const RwPlan &p) {
     RwArgs<T> a{};
@@ -482,7 +634,8 @@ int launch_conv3(const Geo &g, const void *in, const void *w, const void *b, voi
     const int OW = BWD ? g.iw : g.ow, OH = BWD ? g.ih : g.oh;
     const int IW = BWD ? g.ow : g.iw;
     if (!rw_strip_layout<T>(OW, p)) return kErrUnsupported;
-    if (!finish_plan(g, p, OH, 4, 3)) return kErrUnsupported;
+    if (static_cast<int64_t>(OH) * OW <= kCsMaxOut ? !cs_plan(g, p, OH, 3) : !finish_plan(g, p, OH, 4, 3))
+        return kErrUnsupported;
     RwArgs<T> a = rw_args<T>(g, p);
     a.in = static_cast<const T *>(in);
     a.w = static_cast<const T *>(w);
@@ -492,7 +645,12 @@ int launch_conv3(const Geo &g, const void *in, const void *w, const void *b, voi
     // and segment [S*c_out, S*(c_out+RW)) lies inside its row
     const int vb = row_vector_bytes<T>({IW, OW}, {in, out});
     return with_vector_bytes<T>(vb, [&](auto V) {
-        hipLaunchKernelGGL((rw_conv3_kernel<T, S, MM, BWD, decltype(V)::value>), dim3(p.grid), dim3(kThreads), 0, st, a);
+        if (p.cs)
+            hipLaunchKernelGGL((rw_conv3_kernel<T, S, MM, BWD, decltype(V)::value, true>), dim3(p.grid), dim3(kThreads),
+                               0, st, a);
+        else
+            hipLaunchKernelGGL((rw_conv3_kernel<T, S, MM, BWD, decltype(V)::value, false>), dim3(p.grid), dim3(kThreads),
+                               0, st, a);
         return hipGetLastError() == hipSuccess ? kOk : kErrHip;
     });
 }
@@ -506,7 +664,8 @@ int launch_bwdin_s2(const Geo &g, const void *dy, const void *w, void *dx, hipSt
     if (p.NS > 64) return kErrUnsupported;
     p.SPW = 64 / p.NS;
     // dx must be covered by dy rows/cols: 2*oh >= ih and 2*ow >= iw hold for pad 1, k 3, stride 2
-    if (!finish_plan(g, p, g.oh, 2, 1)) return kErrUnsupported;
+    if (static_cast<int64_t>(g.ih) * g.iw <= kCsMaxOut ? !cs_plan(g, p, g.oh, 1) : !finish_plan(g, p, g.oh, 2, 1))
+        return kErrUnsupported;
     RwArgs<T> a = rw_args<T>(g, p);
     a.in = static_cast<const T *>(dy);
     a.w = static_cast<const T *>(w);
@@ -514,7 +673,11 @@ int launch_bwdin_s2(const Geo &g, const void *dy, const void *w, void *dx, hipSt
     // vector width of the row accesses (dy loads use at most 8 bytes, a half strip)
     const int vb = row_vector_bytes<T>({g.ow, g.iw}, {dy, dx});
     return with_vector_bytes<T>(vb, [&](auto V) {
-        hipLaunchKernelGGL((rw_bwdin3_s2_kernel<T, MM, decltype(V)::value>), dim3(p.grid), dim3(kThreads), 0, st, a);
+        if (p.cs)
+            hipLaunchKernelGGL((rw_bwdin3_s2_kernel<T, MM, decltype(V)::value, true>), dim3(p.grid), dim3(kThreads), 0, st, a);
+        else
+            hipLaunchKernelGGL((rw_bwdin3_s2_kernel<T, MM, decltype(V)::value, false>), dim3(p.grid), dim3(kThreads), 0, st,
+                               a);
         return hipGetLastError() == hipSuccess ? kOk : kErrHip;
     });
 }
@@ -522,6 +685,22 @@ int launch_bwdin_s2(const Geo &g, const void *dy, const void *w, void *dx, hipSt
 template <typename T>
 bool plan_bwdw(const Geo &g, RwPlan &p) {
     if (!rw_strip_layout<T>(g.ow, p)) return false;
+    if (static_cast<int64_t>(g.oh) * g.ow <= kCsMaxOut) {
+        // channel slots: workgroup (channel group, chunk of upc images), one image per wave at a time
+        p.cs = true;
+        p.BH = (g.oh + 2) / 3 * 3;
+        p.nbands = 1;
+        p.nunits = 0;
+        p.wpc = (g.ic + p.SPW - 1) / p.SPW;
+        p.upc = kWaves;
+        while (p.upc < g.n && static_cast<int64_t>(p.wpc) * ((g.n + 2 * p.upc - 1) / (2 * p.upc)) >= 1024) p.upc *= 2;
+        p.NC = (g.n + p.upc - 1) / p.upc;
+        const int64_t grid = static_cast<int64_t>(p.wpc) * p.NC;
+        if (grid > (int64_t{1} << 30)) return false;
+        p.grid = static_cast<int>(grid);
+        return true;
+    }
+    p.cs = false;
     p.BH = (pick_bh(static_cast<int64_t>(g.n) * g.ic, g.oh, p.SPW, 4) + 2) / 3 * 3;  // unroll factor 3
     p.nbands = (g.oh + p.BH - 1) / p.BH;
     p.nunits = g.n * p.nbands;  // per channel
@@ -546,7 +725,10 @@ int launch_bwdw(const Geo &g, const RwPlan &p, const void *x, const void *dy, vo
     a.ws = static_cast<float *>(ws);
     const int vb = row_vector_bytes<T>({g.iw, g.ow}, {x, dy});
     return with_vector_bytes<T>(vb, [&](auto V) {
-        hipLaunchKernelGGL((rw_bwdw3_kernel<T, S, MM, decltype(V)::value>), dim3(p.grid), dim3(kThreads), 0, st, a);
+        if (p.cs)
+            hipLaunchKernelGGL((rw_bwdw3_cs_kernel<T, S, MM, decltype(V)::value>), dim3(p.grid), dim3(kThreads), 0, st, a);
+        else
+            hipLaunchKernelGGL((rw_bwdw3_kernel<T, S, MM, decltype(V)::value>), dim3(p.grid), dim3(kThreads), 0, st, a);
         return hipGetLastError() == hipSuccess ? kOk : kErrHip;
     });
 }

@@ -262,6 +262,28 @@ __device__ __forceinline__ WaveUnit wave_unit(int wpc, int NS, int SPW, int nuni
     return u;
 }
 
+// Channel-slot mapping for small planes: wave wv serves image wv / wpc and the
+// SPW consecutive channels of group wv % wpc, slot = lane / NS picking the
+// channel and s = lane % NS the column strip; every slot walks its whole
+// plane.  The planes a wave touches are one contiguous run of memory, and the
+// channel (so the taps) differs per slot.
+__device__ __forceinline__ WaveUnit chan_unit(int wpc, int NS, int SPW, int nch, int nimg) {
+    WaveUnit u;
+    const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x) * (kThreads / 64) +
+                                                  static_cast<int>(threadIdx.x >> 6));
+    const int n = wv / wpc;
+    const int cg = wv - n * wpc;
+    u.lane = threadIdx.x & 63;
+    const int slot = u.lane / NS;
+    u.s = u.lane - slot * NS;
+    const int c = cg * SPW + slot;
+    u.act = n < nimg && slot < SPW && c < nch;
+    u.ic = u.act ? c : 0;
+    u.n = u.act ? n : 0;
+    u.band = 0;
+    return u;
+}
+
 // Widest vector (16, 8, 4 or 2 bytes, at least one element of T) that divides
 // the byte length of every listed row width and every listed base address: the
 // VB for load_row / store_values on those rows (a row vector never straddles
