@@ -29,18 +29,27 @@ template <> __device__ __forceinline__ float from_f32<float>(float v) { return v
 template <> __device__ __forceinline__ __half from_f32<__half>(float v) {
     return __float2half_rn(v);  // v_cvt_f16_f32: round to nearest even
 }
-// Round to nearest, ties to even, on the 16 dropped mantissa bits; NaN stays a
-// (quiet) NaN, overflow rounds to +-inf as the rounding rule implies.
+// Round to nearest, ties to even (the hardware conversion, v_cvt_pk_bf16_f32
+// on gfx950): overflow rounds to +-inf, a NaN stays a quiet NaN.
 template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) {
-    uint32_t u = __float_as_uint(v);
     bf16_t r;
-    if ((u & 0x7fffffffu) > 0x7f800000u) {
-        r.bits = static_cast<uint16_t>((u >> 16) | 0x0040u);
-    } else {
-        u += 0x7fffu + ((u >> 16) & 1u);
-        r.bits = static_cast<uint16_t>(u >> 16);
-    }
+    r.bits = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
     return r;
+}
+
+// Two fp32 values rounded to nearest even into one word of 16-bit elements
+// (element 0 in the low half): one v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32.
+typedef float f32x2_v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_v __attribute__((ext_vector_type(2)));
+template <typename T> __device__ __forceinline__ uint32_t pack2(float lo, float hi);
+template <> __device__ __forceinline__ uint32_t pack2<bf16_t>(float lo, float hi) {
+    const f32x2_v v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_v));
+}
+template <> __device__ __forceinline__ uint32_t pack2<__half>(float lo, float hi) {
+    const f32x2_v v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_v));
 }
 
 // Elements per 16-byte vector.

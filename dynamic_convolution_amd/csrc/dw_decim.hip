@@ -382,7 +382,9 @@ bool plan_dec(const Geo &g, int pass, DcPlan &p) {
     const int rows = pass == 1 ? (g.ih + 1) / 2 : g.oh;  // rows walked: decimated dx rows or output rows
     const int64_t planes = static_cast<int64_t>(g.n) * g.ic;
     int bh = rows;
-    while (bh > 4 && planes * ((rows + bh - 1) / bh) < int64_t{8192} * p.SPW / 2) bh = (bh + 1) / 2;
+    // few long bands: the halo rows are re-read once per band, and longer
+    // streams per slot measure faster (8192 * SPW / 4 units is ~2000+ waves)
+    while (bh > 4 && planes * ((rows + bh - 1) / bh) < int64_t{8192} * p.SPW / 4) bh = (bh + 1) / 2;
     p.nbands = (rows + bh - 1) / bh;
     // rows per band, a multiple of k (the row loop's unroll factor; steps past
     // the band's last row store nothing and read dy as zero)

@@ -9,10 +9,11 @@
 // The op moves ~k*k*nb filter values per output pixel and does one FMA per
 // value, so it is bound by HBM bandwidth.  A workgroup owns a band of rows of
 // one (n, c) plane: the x rows of the band plus the largest dilation's halo
-// are staged in LDS once and serve every branch; each thread produces RW
-// adjacent pixels of one row for all branches, streaming every filter tap as
-// one 16-byte coalesced load and writing each branch's strip at its channel
-// offset b*C + c of the concatenated output.
+// are staged in LDS once, as fp32 with zero columns on both sides (so no tap
+// needs a column test and no conversion), and serve every branch; each thread
+// produces RW adjacent pixels of one row for all branches, streaming every
+// filter tap as one 16-byte coalesced load and writing each branch's strip at
+// its channel offset b*C + c of the concatenated output.
 #include "dw_common.hpp"
 #include "dw_internal.hpp"
 
@@ -34,7 +35,10 @@ template <typename T> struct DynArgs {
     int BH, nbands, NS;
     FastDiv fNS;
     int halo;   // r * max dilation
-    int vin;    // x 16-byte aligned
+    int hp;     // zero columns left of the staged rows: halo rounded up to 4
+    int LW;     // staged row pitch in floats (multiple of 4)
+    FastDiv fLW, fVPR, fPAD;
+    int vin;    // x 16-byte aligned and rows of whole 16-byte vectors
     int vf;     // filters and y rows allow 16-byte strips
 };
 
@@ -74,7 +78,7 @@ __device__ __forceinline__ void store_strip(T *p, const float *acc, int valid, b
 
 template <typename T, int K_, int RW>
 __global__ __launch_bounds__(kThreads) void dynconv_kernel(DynArgs<T> a) {
-    extern __shared__ __align__(16) unsigned char smem[];
+    extern __shared__ __align__(16) float xs[];
     const int K = K_ ? K_ : a.k;
     const int KK = K * K;
     const int rr = (K - 1) / 2;
@@ -88,12 +92,55 @@ __global__ __launch_bounds__(kThreads) void dynconv_kernel(DynArgs<T> a) {
     const int rlo = max(h0 - a.halo, 0);
     const int rhi = min(h1 + a.halo, a.h);
     const int64_t hw = static_cast<int64_t>(a.h) * a.w;
+    const int rows = rhi - rlo;
+    const int LW = a.LW, hp = a.hp;
 
-    T *xs = reinterpret_cast<T *>(smem);
-    const int64_t gbeg = static_cast<int64_t>(plane) * hw + static_cast<int64_t>(rlo) * a.w;
-    const int64_t gend = gbeg + static_cast<int64_t>(rhi - rlo) * a.w;
-    const int off = a.vin ? lds_copy_range(xs, a.x, gbeg, gend, tid, kThreads)
-                          : lds_copy_range_scalar(xs, a.x, gbeg, gend, tid, kThreads);
+    // stage x rows [rlo, rhi) as fp32: row r at xs[r*LW + hp ...], zeros elsewhere in the row
+    const T *src = a.x + static_cast<int64_t>(plane) * hw + static_cast<int64_t>(rlo) * a.w;
+    if (a.vin) {
+        constexpr int VE = Vec<T>::N;
+        constexpr int NB = 4;  // 16-byte loads in flight per thread
+        const int vpr = a.w / VE;
+        const int nvec = rows * vpr;
+        for (int v0 = tid; v0 < nvec; v0 += NB * kThreads) {
+            uint4 raw[NB];
+#pragma unroll
+            for (int k = 0; k < NB; ++k) {
+                raw[k] = make_uint4(0u, 0u, 0u, 0u);
+                const int v = v0 + k * kThreads;
+                if (v < nvec) raw[k] = *reinterpret_cast<const uint4 *>(src + static_cast<int64_t>(v) * VE);
+            }
+#pragma unroll
+            for (int k = 0; k < NB; ++k) {
+                const int v = v0 + k * kThreads;
+                if (v < nvec) {
+                    const int r = static_cast<int>(fdiv(static_cast<uint32_t>(v), a.fVPR));
+                    float *d = xs + r * LW + hp + (v - r * vpr) * VE;
+                    union {
+                        uint4 u;
+                        T t[VE];
+                    } b;
+                    b.u = raw[k];
+#pragma unroll
+                    for (int e = 0; e < VE; e += 4)
+                        *reinterpret_cast<float4 *>(d + e) =
+                            make_float4(to_f32(b.t[e]), to_f32(b.t[e + 1]), to_f32(b.t[e + 2]), to_f32(b.t[e + 3]));
+                }
+            }
+        }
+        const int padw = LW - a.w;
+        for (int e = tid; e < rows * padw; e += kThreads) {
+            const int r = static_cast<int>(fdiv(static_cast<uint32_t>(e), a.fPAD));
+            const int j = e - r * padw;
+            xs[r * LW + (j < hp ? j : a.w + j)] = 0.f;
+        }
+    } else {
+        for (int e = tid; e < rows * LW; e += kThreads) {
+            const int r = static_cast<int>(fdiv(static_cast<uint32_t>(e), a.fLW));
+            const int col = e - r * LW - hp;
+            xs[e] = (col >= 0 && col < a.w) ? to_f32(src[static_cast<int64_t>(r) * a.w + col]) : 0.f;
+        }
+    }
     __syncthreads();
 
     const int items = a.BH * a.NS;
@@ -115,18 +162,28 @@ __global__ __launch_bounds__(kThreads) void dynconv_kernel(DynArgs<T> a) {
             for (int i = 0; i < K; ++i) {
                 const int sy = hh + (i - rr) * d;
                 if (sy < 0 || sy >= a.h) continue;  // whole filter row multiplies zero padding
-                const T *rp = xs + off + (sy - rlo) * a.w;
+                const float *rp = xs + (sy - rlo) * LW + hp + w0;  // column w0 of row sy
 #pragma unroll
                 for (int j = 0; j < K; ++j) {
-                    float fv[RW];
+                    float fv[RW], xv[RW];
                     load_strip<T, RW>(fb + static_cast<int64_t>(i * K + j) * hw, fv, valid, a.vf != 0);
-                    const int sx0 = w0 + (j - rr) * d;
+                    if (K_ && j == rr) {
+                        // centre column: RW floats at a 16-byte aligned address
 #pragma unroll
-                    for (int q = 0; q < RW; ++q) {
-                        const int sx = sx0 + q;
-                        const float xv = (sx >= 0 && sx < a.w) ? to_f32(rp[sx]) : 0.f;
-                        acc[q] = fmaf(fv[q], xv, acc[q]);
+                        for (int q = 0; q < RW; q += 4) {
+                            const float4 v4 = *reinterpret_cast<const float4 *>(rp + q);
+                            xv[q] = v4.x;
+                            xv[q + 1] = v4.y;
+                            xv[q + 2] = v4.z;
+                            xv[q + 3] = v4.w;
+                        }
+                    } else {
+                        const int off = (j - rr) * d;
+#pragma unroll
+                        for (int q = 0; q < RW; ++q) xv[q] = rp[off + q];
                     }
+#pragma unroll
+                    for (int q = 0; q < RW; ++q) acc[q] = fmaf(fv[q], xv[q], acc[q]);
                 }
             }
             T *yp = a.y + (static_cast<int64_t>(nn * a.nb + b) * a.c + ch) * hw + pix;
@@ -139,16 +196,26 @@ struct DynPlan {
     int BH, nbands, lds_bytes;
 };
 
+// Staged tile geometry: hp zero columns left of each row (the largest
+// dilation's halo rounded up to 4, so the centre column of a strip is 16-byte
+// aligned) and a row pitch LW >= w + 2*hp, a multiple of 4.
+inline void dyn_tile(int w, int halo, int &hp, int &LW) {
+    hp = (halo + 3) / 4 * 4;
+    LW = (w + 2 * hp + 3) / 4 * 4;
+}
+
 template <typename T>
 bool plan_dyn(int n, int c, int h, int w, int k, int maxdil, DynPlan &p) {
     constexpr int RW = Vec<T>::N;
     const int NS = (w + RW - 1) / RW;
     const int halo = (k - 1) / 2 * maxdil;
+    int hp, LW;
+    dyn_tile(w, halo, hp, LW);
     auto bytes = [&](int bh) -> int64_t {
         const int64_t rows = std::min<int64_t>(static_cast<int64_t>(bh) + 2 * halo, h);
-        const int64_t cnt = rows * w;
+        const int64_t cnt = rows * LW + RW;  // + RW: a partial last strip may read past the last row
         if (cnt > (1 << 24)) return INT64_MAX;
-        return static_cast<int64_t>(lds_slots<T>(static_cast<int>(cnt))) * sizeof(T);
+        return cnt * static_cast<int64_t>(sizeof(float));
     };
     const int lim = bytes(1) <= kLdsPref ? kLdsPref : kLdsCap;
     if (bytes(1) > lim) return false;
@@ -193,7 +260,13 @@ int run_dyn(const void *x, const void *const *filters, const int32_t *dil, int n
     a.NS = (w + RW - 1) / RW;
     a.fNS = make_fastdiv(a.NS, static_cast<uint64_t>(p.BH) * a.NS);
     a.halo = (k - 1) / 2 * maxdil;
-    a.vin = reinterpret_cast<uintptr_t>(x) % 16 == 0;
+    dyn_tile(w, a.halo, a.hp, a.LW);
+    const int rows_max = std::min(p.BH + 2 * a.halo, h);
+    const int vpr = w / Vec<T>::N;
+    a.fLW = make_fastdiv(a.LW, static_cast<uint64_t>(rows_max) * a.LW);
+    a.fVPR = make_fastdiv(std::max(vpr, 1), static_cast<uint64_t>(rows_max) * std::max(vpr, 1));
+    a.fPAD = make_fastdiv(a.LW - w, static_cast<uint64_t>(rows_max) * (a.LW - w));
+    a.vin = reinterpret_cast<uintptr_t>(x) % 16 == 0 && w % Vec<T>::N == 0;
     a.vf = fal && (w % RW == 0) && (reinterpret_cast<uintptr_t>(y) % 16 == 0);
     const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(n) * c * p.nbands));
     if (k == 3)

@@ -52,7 +52,7 @@ __device__ __forceinline__ void pack_words(const float *v, uint32_t (&w)[NW]) {
         if constexpr (sizeof(T) == 4)
             w[k] = __float_as_uint(v[k]);
         else
-            w[k] = bits_of(from_f32<T>(v[2 * k])) | (bits_of(from_f32<T>(v[2 * k + 1])) << 16);
+            w[k] = pack2<T>(v[2 * k], v[2 * k + 1]);
     }
 }
 
