@@ -6,9 +6,9 @@
 // MegEngine large-kernel depthwise article: batch 64, 384 channels, kernels up
 // to 31x31; its DirectConv splits kernel columns over 4 lanes and reduces with
 // a shuffle butterfly).  On CDNA the filter of a plane is uniform across the
-// workgroup, so here it is read with scalar loads into SGPRs and used directly
-// as an FMA operand, and each lane keeps a whole TR x TC output tile in VGPRs
-// -- no cross-lane reduction is needed:
+// workgroup, so here it is staged once as fp32 in LDS and each tap is a
+// broadcast LDS read feeding TR*TC FMAs, and each lane keeps a whole TR x TC
+// output tile in VGPRs -- no cross-lane reduction is needed:
 //   1. the workgroup stages its plane (or a band of rows) into LDS as fp32 with
 //      the zero padding written out, so the inner loop has no bounds tests;
 //   2. a lane walks the TR + k - 1 padded input rows its tile reads; each row
@@ -36,6 +36,7 @@ template <typename T> struct LkArgs {
     int BH;        // output rows per band
     int nbands;
     int NCB, NRB;  // column / row blocks of output tiles in a band
+    int wsm_off;   // float offset of the fp32 filter copy in LDS
     FastDiv fpitch;
 };
 
@@ -64,9 +65,14 @@ __global__ __launch_bounds__(256) void lk_conv_kernel(LkArgs<T> a) {
         const int ih = oh0 - a.P + r, iw = col - a.P;
         xs[e] = (ih >= 0 && ih < a.IH && iw >= 0 && iw < a.IW) ? to_f32(src[ih * a.IW + iw]) : 0.f;
     }
+    // The filter is staged once as fp32 in LDS and each tap is read with a
+    // uniform-address (broadcast) LDS read right before its FMAs.  (Scalar
+    // loads of an fp32 filter measured slower: the scalar cache misses stall
+    // each row's FMAs; 16-bit taps at odd offsets cannot be scalar-loaded.)
+    float *wsm = xs + a.wsm_off;
+    for (int e = tid; e < K * K; e += nthr) wsm[e] = to_f32(a.w[static_cast<int64_t>(c) * K * K + e]);
     __syncthreads();
 
-    const T *__restrict__ wk = a.w + static_cast<int64_t>(c) * K * K;
     const float bias = (!FLIP && a.b) ? to_f32(a.b[c]) : 0.f;
     const int items = a.NRB * a.NCB;
     for (int it = tid; it < items; it += nthr) {
@@ -95,10 +101,11 @@ __global__ __launch_bounds__(256) void lk_conv_kernel(LkArgs<T> a) {
             for (int tr = 0; tr < TR; ++tr) {
                 const int i = r - tr;  // kernel row; uniform across the workgroup
                 if (i < 0 || i >= K) continue;
-                const T *wrow = wk + (FLIP ? (K - 1 - i) : i) * K;
+                const int wrow = (FLIP ? (K - 1 - i) : i) * K;
 #pragma unroll
                 for (int j = 0; j < K; ++j) {
-                    const float wv = to_f32(wrow[FLIP ? K - 1 - j : j]);
+                    const int t = wrow + (FLIP ? K - 1 - j : j);
+                    const float wv = wsm[t];
 #pragma unroll
                     for (int q = 0; q < TC; ++q) acc[tr][q] = fmaf(wv, win[q + j], acc[tr][q]);
                 }
@@ -130,7 +137,8 @@ bool plan_lk(int OH, int OW, int K, LkPlan &p) {
     p.pitch = (p.pitch + 3) & ~3;
     // rows per band: whole plane while the tile count fits 256 lanes and LDS fits 64 KiB
     int bh = OH;
-    auto lds = [&](int b) { return static_cast<int64_t>(b + K - 1) * p.pitch * 4; };
+    // padded input tile + an fp32 copy of the filter
+    auto lds = [&](int b) { return (static_cast<int64_t>(b + K - 1) * p.pitch + K * K) * 4; };
     while (bh > kTR && (((bh + kTR - 1) / kTR) * p.NCB > 256 || lds(bh) > 64 * 1024)) bh = (bh + 1) / 2;
     if (lds(bh) > 64 * 1024) return false;
     p.nbands = (OH + bh - 1) / bh;
@@ -153,6 +161,7 @@ int run_lk(const LkArgs<T> &a0, const LkPlan &p, int planes, hipStream_t s) {
     a.NCB = p.NCB;
     a.NRB = p.NRB;
     a.fpitch = make_fastdiv(p.pitch, static_cast<uint64_t>(p.BH + K) * p.pitch);
+    a.wsm_off = (p.BH + K - 1) * p.pitch;
     hipLaunchKernelGGL((lk_conv_kernel<T, K, kTR, TC, FLIP>), dim3(planes * p.nbands), dim3(p.threads), p.lds_bytes, s, a);
     return hipGetLastError() == hipSuccess ? kOk : kErrHip;
 }
@@ -222,9 +231,10 @@ template <typename T> struct LkwArgs {
     float *ws;     // [c][NC][k*k+1]
     int C, IH, IW, OH, OW, P;
     int N, NC, npc;
-    int xpitch;    // LDS pitch of the padded x plane
-    int xrows;     // OH + k - 1
-    int dpitch;    // LDS pitch of the dy plane (multiple of 8)
+    int BH, nbands;  // dy rows per band, bands per plane
+    int xpitch;    // LDS pitch of the padded x rows
+    int xrows;     // LDS rows reserved for x: BH + k - 1
+    int dpitch;    // LDS pitch of the dy rows (multiple of 8)
     FastDiv fxp, fdp;
 };
 
@@ -238,8 +248,13 @@ __global__ __launch_bounds__(256) void lk_bwdw_kernel(LkwArgs<T> a) {
     float *xs = reinterpret_cast<float *>(smem);
     float *ds = xs + a.xrows * a.xpitch;
     const int tid = threadIdx.x;
-    const int c = blockIdx.x / a.NC;
-    const int chunk = blockIdx.x - c * a.NC;
+    // workgroup (channel, image chunk, band of dy rows)
+    const int units = a.NC * a.nbands;
+    const int c = blockIdx.x / units;
+    const int rest = blockIdx.x - c * units;
+    const int chunk = rest / a.nbands;
+    const int band = rest - chunk * a.nbands;
+    const int oh0 = band * a.BH, oh1 = min(oh0 + a.BH, a.OH);
     const int grp = tid / NT;
     const int tile = tid - grp * NT;
     const int rb = tile / NCB, cb = tile - (tile / NCB) * NCB;
@@ -251,7 +266,8 @@ __global__ __launch_bounds__(256) void lk_bwdw_kernel(LkwArgs<T> a) {
         for (int q = 0; q < TC; ++q) acc[tr][q] = 0.f;
     float dbs = 0.f;
     const int n0 = chunk * a.npc, n1 = min(n0 + a.npc, a.N);
-    const int xtot = a.xrows * a.xpitch, dtot = a.OH * a.dpitch;
+    // padded x rows oh0 .. oh1 + k - 2 (image rows minus P) and dy rows oh0 .. oh1 - 1
+    const int xtot = (oh1 - oh0 + K - 1) * a.xpitch, dtot = (oh1 - oh0) * a.dpitch;
     for (int n = n0; n < n1; ++n) {
         __syncthreads();
         const T *xp = a.x + (static_cast<int64_t>(n) * a.C + c) * a.IH * a.IW;
@@ -259,17 +275,17 @@ __global__ __launch_bounds__(256) void lk_bwdw_kernel(LkwArgs<T> a) {
         for (int e = tid; e < xtot; e += 256) {
             const int r = static_cast<int>(fdiv(static_cast<uint32_t>(e), a.fxp));
             const int col = e - r * a.xpitch;
-            const int ih = r - a.P, iw = col - a.P;
+            const int ih = oh0 + r - a.P, iw = col - a.P;
             xs[e] = (ih >= 0 && ih < a.IH && iw >= 0 && iw < a.IW) ? to_f32(xp[ih * a.IW + iw]) : 0.f;
         }
         for (int e = tid; e < dtot; e += 256) {
             const int r = static_cast<int>(fdiv(static_cast<uint32_t>(e), a.fdp));
             const int col = e - r * a.dpitch;
-            ds[e] = col < a.OW ? to_f32(dp[r * a.OW + col]) : 0.f;
+            ds[e] = col < a.OW ? to_f32(dp[(oh0 + r) * a.OW + col]) : 0.f;
         }
         __syncthreads();
         if (!lane_ok) continue;
-        for (int oh = grp; oh < a.OH; oh += NG) {
+        for (int oh = grp; oh < oh1 - oh0; oh += NG) {  // band-relative dy row
             const float *drow = ds + oh * a.dpitch;
             for (int s0 = 0; s0 < a.OW; s0 += SEG) {
                 float dv[SEG];
@@ -318,7 +334,7 @@ __global__ __launch_bounds__(256) void lk_bwdw_kernel(LkwArgs<T> a) {
         for (int q = 0; q < TC; ++q) red[tid * RS + tr * TC + q] = acc[tr][q];
     red[tid * RS + TR * TC] = dbs;
     __syncthreads();
-    float *dst = a.ws + (static_cast<int64_t>(c) * a.NC + chunk) * (K * K + 1);
+    float *dst = a.ws + (static_cast<int64_t>(c) * units + rest) * (K * K + 1);
     for (int e = tid; e < NT * RS; e += 256) {
         const int t = e / RS, k = e - (e / RS) * RS;
         float v = 0.f;
@@ -333,22 +349,30 @@ __global__ __launch_bounds__(256) void lk_bwdw_kernel(LkwArgs<T> a) {
 }
 
 struct LkwPlan {
-    int NC, npc, xpitch, xrows, dpitch, lds_bytes;
+    int NC, npc, BH, nbands, xpitch, xrows, dpitch, lds_bytes;
 };
 
 bool plan_lkw(const Geo &g, int K, LkwPlan &p) {
     constexpr int TC = 8, SEG = 8;
     const int owr = (g.ow + SEG - 1) / SEG * SEG;  // dy columns walked (zero beyond ow)
-    p.xrows = g.oh + K - 1;
     // x window of the last segment and tile: owr + ceil(k/TC)*TC + 3 columns at most
     p.xpitch = (owr + (K + TC - 1) / TC * TC + 3 + 3) & ~3;
     p.dpitch = owr;
-    const int64_t bytes = (static_cast<int64_t>(p.xrows) * p.xpitch + static_cast<int64_t>(g.oh) * p.dpitch) * 4;
     const int64_t red = 256 * (2 * TC + 1) * 4;
-    p.lds_bytes = static_cast<int>(std::max(bytes, red));
-    if (p.lds_bytes > 64 * 1024) return false;
-    // image chunks: about 4 workgroups per CU in total
-    int NC = std::max(1, (1024 + g.ic - 1) / g.ic);
+    auto bytes = [&](int bh) {
+        return std::max((static_cast<int64_t>(bh + K - 1) * p.xpitch + static_cast<int64_t>(bh) * p.dpitch) * 4, red);
+    };
+    // bands of dy rows small enough for ~6 workgroups per CU (24 KiB of LDS each):
+    // the staging of one image overlaps the arithmetic of the other workgroups
+    int bh = g.oh;
+    while (bh > 8 && bytes(bh) > 24 * 1024) bh = (bh + 1) / 2;
+    if (bytes(bh) > 64 * 1024) return false;
+    p.nbands = (g.oh + bh - 1) / bh;
+    p.BH = (g.oh + p.nbands - 1) / p.nbands;
+    p.xrows = p.BH + K - 1;
+    p.lds_bytes = static_cast<int>(bytes(p.BH));
+    // image chunks: about 2048 workgroups in total
+    int NC = std::max(1, (2048 + g.ic * p.nbands - 1) / (g.ic * p.nbands));
     NC = std::min(NC, g.n);
     p.npc = (g.n + NC - 1) / NC;
     p.NC = (g.n + p.npc - 1) / p.npc;
@@ -370,12 +394,14 @@ int run_lkw(const Geo &g, const LkwPlan &p, const void *x, const void *dy, void 
     a.N = g.n;
     a.NC = p.NC;
     a.npc = p.npc;
+    a.BH = p.BH;
+    a.nbands = p.nbands;
     a.xpitch = p.xpitch;
     a.xrows = p.xrows;
     a.dpitch = p.dpitch;
     a.fxp = make_fastdiv(p.xpitch, static_cast<uint64_t>(p.xrows) * p.xpitch + 256);
-    a.fdp = make_fastdiv(p.dpitch, static_cast<uint64_t>(g.oh) * p.dpitch + 256);
-    hipLaunchKernelGGL((lk_bwdw_kernel<T, K, kTR, 8>), dim3(g.ic * p.NC), dim3(256), p.lds_bytes, s, a);
+    a.fdp = make_fastdiv(p.dpitch, static_cast<uint64_t>(p.BH) * p.dpitch + 256);
+    hipLaunchKernelGGL((lk_bwdw_kernel<T, K, kTR, 8>), dim3(g.ic * p.NC * p.nbands), dim3(256), p.lds_bytes, s, a);
     return hipGetLastError() == hipSuccess ? kOk : kErrHip;
 }
 
@@ -399,7 +425,7 @@ bool largek_bwdw_fits(const Geo &g) {
 
 int largek_bwd_weight_chunks(const Geo &g) {
     LkwPlan p;
-    return plan_lkw(g, g.kh, p) ? p.NC : 0;
+    return plan_lkw(g, g.kh, p) ? p.NC * p.nbands : 0;
 }
 
 int largek_bwd_weight(const Geo &g, const void *x, const void *dy, void *ws, int dtype, hipStream_t s) {
