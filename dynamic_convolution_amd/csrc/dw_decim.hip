@@ -141,6 +141,7 @@ __global__ __launch_bounds__(kThreads) void dec_fwd_kernel(DcArgs<T> a) {
 #pragma unroll
     for (int f = 0; f < kPF; ++f) load_xrow<T, FULL>(xp, oh0 - HH + K - 1 + f, a.XH, g.iw, c0, u.act, rq[f], rk[f]);
     for (int t0 = 0; t0 < a.BH; t0 += K) {  // BH is a multiple of K
+        uint32_t ybuf[K][MM][ND];  // packed outputs of this iteration's K rows
 #pragma unroll
         for (int uu = 0; uu < K; ++uu) {
             const int t = t0 + uu;
@@ -149,32 +150,43 @@ __global__ __launch_bounds__(kThreads) void dec_fwd_kernel(DcArgs<T> a) {
                 ring_pop<kPF, NX>(rq, rk);
                 load_xrow<T, FULL>(xp, oh0 - HH + t + K - 1 + kPF, a.XH, g.iw, c0, u.act, rq[kPF - 1], rk[kPF - 1]);
                 const int oh = oh0 + t;
-                if (u.act && oh < oh_end) {
 #pragma unroll
-                    for (int m = 0; m < MM; ++m) {
-                        float acc[RO];
+                for (int m = 0; m < MM; ++m) {
+                    float acc[RO];
 #pragma unroll
-                        for (int q = 0; q < RO; ++q) acc[q] = bias[m];
+                    for (int q = 0; q < RO; ++q) acc[q] = bias[m];
 #pragma unroll
-                        for (int i = 0; i < K; ++i)
+                    for (int i = 0; i < K; ++i)
 #pragma unroll
-                            for (int j = 0; j < K; ++j)
-#pragma unroll
-                                for (int q = 0; q < RO; ++q)
-                                    acc[q] = fmaf(wt[m][i * K + j], win[(uu + i) % K][q + j], acc[q]);
-                        T *yp = a.out + ((static_cast<int64_t>(P) * MM + m) * g.oh + oh) * g.ow + c0;
-                        if constexpr (FULL) {
-                            uint32_t w[ND];
-                            pack_words<T, ND>(acc, w);
-                            store_words<ND>(yp, w);
-                        } else {
+                        for (int j = 0; j < K; ++j)
 #pragma unroll
                             for (int q = 0; q < RO; ++q)
-                                if (q < g.ow - c0) yp[q] = from_f32<T>(acc[q]);
-                        }
+                                acc[q] = fmaf(wt[m][i * K + j], win[(uu + i) % K][q + j], acc[q]);
+                    if constexpr (FULL) {
+                        pack_words<T, ND>(acc, ybuf[uu][m]);
+                    } else if (u.act && oh < oh_end) {
+                        T *yp = a.out + ((static_cast<int64_t>(P) * MM + m) * g.oh + oh) * g.ow + c0;
+#pragma unroll
+                        for (int q = 0; q < RO; ++q)
+                            if (q < g.ow - c0) yp[q] = from_f32<T>(acc[q]);
                     }
                 }
             }
+        }
+        if constexpr (FULL) {
+            // the K rows of this iteration back to back: a slot's rows are adjacent
+            // in memory, so each cache line is completed by one burst of stores
+            // (rows written one step apart were evicted half-written and cost
+            // extra HBM writes and read-modify-writes)
+#pragma unroll
+            for (int m = 0; m < MM; ++m)
+#pragma unroll
+                for (int uu = 0; uu < K; ++uu) {
+                    const int oh = oh0 + t0 + uu;
+                    if (u.act && oh < oh_end)
+                        store_words<ND>(a.out + ((static_cast<int64_t>(P) * MM + m) * g.oh + oh) * g.ow + c0,
+                                        ybuf[uu][m]);
+                }
         }
     }
 }
@@ -204,8 +216,6 @@ __global__ __launch_bounds__(kThreads) void dec_bwdin_kernel(DcArgs<T> a) {
     const int r0 = u.band * a.BH, r_end = min(r0 + a.BH, a.XH);
     // relative row j (dy row r0 - HH + j) lives in window slot j % K
     float win[MM][K][WW];
-    uint32_t rq[MM][kPF][ND];
-    bool rk[MM][kPF];
 #pragma unroll
     for (int m = 0; m < MM; ++m) {
 #pragma unroll
@@ -217,60 +227,71 @@ __global__ __launch_bounds__(kThreads) void dec_bwdin_kernel(DcArgs<T> a) {
             drow_values<T>(w, ok, v);
             halo_window<HH>(v, u.lane, hl, hr, win[m][j]);
         }
-#pragma unroll
-        for (int f = 0; f < kPF; ++f)
-            load_drow<T, FULL>(dp[m], r0 - HH + K - 1 + f, g.oh, g.ow, c0, u.act, rq[m][f], rk[m][f]);
     }
-    for (int t0 = 0; t0 < a.BH; t0 += K) {  // BH is a multiple of K
+    // The K new dy rows of an iteration (relative rows t0+K-1 .. t0+2K-2) are
+    // loaded as one burst an iteration ahead, into two alternating buffers: a
+    // slot's consecutive dy rows share cache lines, and rows read one step
+    // apart were evicted and fetched again in between.
+    auto load_iter = [&](int jbase, uint32_t (&buf)[MM][K][ND], bool (&ok)[MM][K]) {
+#pragma unroll
+        for (int m = 0; m < MM; ++m)
+#pragma unroll
+            for (int uu = 0; uu < K; ++uu)
+                load_drow<T, FULL>(dp[m], r0 - HH + jbase + uu, g.oh, g.ow, c0, u.act, buf[m][uu], ok[m][uu]);
+    };
+    auto run_iter = [&](int t0, const uint32_t (&buf)[MM][K][ND], const bool (&ok)[MM][K]) {
 #pragma unroll
         for (int uu = 0; uu < K; ++uu) {
-            const int t = t0 + uu;
-            {
 #pragma unroll
-                for (int m = 0; m < MM; ++m) {
-                    float v[RO];
-                    drow_values<T>(rq[m][0], rk[m][0], v);
-                    halo_window<HH>(v, u.lane, hl, hr, win[m][(uu + K - 1) % K]);
-                    ring_pop<kPF, ND>(rq[m], rk[m]);
-                    load_drow<T, FULL>(dp[m], r0 - HH + t + K - 1 + kPF, g.oh, g.ow, c0, u.act, rq[m][kPF - 1],
-                                       rk[m][kPF - 1]);
+            for (int m = 0; m < MM; ++m) {
+                float v[RO];
+                drow_values<T>(buf[m][uu], ok[m][uu], v);
+                halo_window<HH>(v, u.lane, hl, hr, win[m][(uu + K - 1) % K]);
+            }
+            const int r = r0 + t0 + uu;
+            if (u.act && r < r_end) {
+                float acc[RO];
+#pragma unroll
+                for (int q = 0; q < RO; ++q) acc[q] = 0.f;
+#pragma unroll
+                for (int m = 0; m < MM; ++m)
+#pragma unroll
+                    for (int i = 0; i < K; ++i)
+#pragma unroll
+                        for (int j = 0; j < K; ++j)
+#pragma unroll
+                            for (int q = 0; q < RO; ++q)
+                                acc[q] = fmaf(wf[m][i * K + j], win[m][(uu + i) % K][q + j], acc[q]);
+                // dx row 2r: values at even columns, zeros at odd; dx row 2r+1: zeros
+                float e0[2 * RO];
+#pragma unroll
+                for (int q = 0; q < RO; ++q) {
+                    e0[2 * q] = acc[q];
+                    e0[2 * q + 1] = 0.f;
                 }
-                const int r = r0 + t;
-                if (u.act && r < r_end) {
-                    float acc[RO];
+                uint32_t we[NX], wz[NX];
+                pack_words<T, NX>(e0, we);
 #pragma unroll
-                    for (int q = 0; q < RO; ++q) acc[q] = 0.f;
-#pragma unroll
-                    for (int m = 0; m < MM; ++m)
-#pragma unroll
-                        for (int i = 0; i < K; ++i)
-#pragma unroll
-                            for (int j = 0; j < K; ++j)
-#pragma unroll
-                                for (int q = 0; q < RO; ++q)
-                                    acc[q] = fmaf(wf[m][i * K + j], win[m][(uu + i) % K][q + j], acc[q]);
-                    // dx row 2r: values at even columns, zeros at odd; dx row 2r+1: zeros
-                    float e0[2 * RO];
-#pragma unroll
-                    for (int q = 0; q < RO; ++q) {
-                        e0[2 * q] = acc[q];
-                        e0[2 * q + 1] = 0.f;
-                    }
-                    uint32_t we[NX], wz[NX];
-                    pack_words<T, NX>(e0, we);
-#pragma unroll
-                    for (int k = 0; k < NX; ++k) wz[k] = 0u;
-                    T *xq = a.out + (static_cast<int64_t>(P) * g.ih + 2 * r) * g.iw + 2 * c0;
-                    if constexpr (FULL) {
-                        store_words<NX>(xq, we);
-                        if (2 * r + 1 < g.ih) store_words<NX>(xq + g.iw, wz);
-                    } else {
-                        store_words_tail<T, NX>(xq, g.iw - 2 * c0, we);
-                        if (2 * r + 1 < g.ih) store_words_tail<T, NX>(xq + g.iw, g.iw - 2 * c0, wz);
-                    }
+                for (int k = 0; k < NX; ++k) wz[k] = 0u;
+                T *xq = a.out + (static_cast<int64_t>(P) * g.ih + 2 * r) * g.iw + 2 * c0;
+                if constexpr (FULL) {
+                    store_words<NX>(xq, we);
+                    if (2 * r + 1 < g.ih) store_words<NX>(xq + g.iw, wz);
+                } else {
+                    store_words_tail<T, NX>(xq, g.iw - 2 * c0, we);
+                    if (2 * r + 1 < g.ih) store_words_tail<T, NX>(xq + g.iw, g.iw - 2 * c0, wz);
                 }
             }
         }
+    };
+    uint32_t bA[MM][K][ND], bB[MM][K][ND];
+    bool kA[MM][K], kB[MM][K];
+    load_iter(K - 1, bA, kA);
+    for (int t0 = 0; t0 < a.BH; t0 += 2 * K) {  // BH is a multiple of 2K
+        load_iter(t0 + 2 * K - 1, bB, kB);
+        run_iter(t0, bA, kA);
+        load_iter(t0 + 3 * K - 1, bA, kA);
+        run_iter(t0 + K, bB, kB);
     }
 }
 
@@ -305,8 +326,8 @@ __global__ __launch_bounds__(kThreads) void dec_bwdw_kernel(DcArgs<T> a) {
         // relative x row j (decimated row oh0 - HH + j) lives in window slot j % K;
         // dy row oh0 + t is used at step t
         float win[K][WW];
-        uint32_t rq[kPF][NX], gq[MM][kPF][ND];
-        bool rk[kPF], gk[MM][kPF];
+        uint32_t rq[kPF][NX];
+        bool rk[kPF];
 #pragma unroll
         for (int j = 0; j < K - 1; ++j) {
             uint32_t w[NX];
@@ -315,40 +336,49 @@ __global__ __launch_bounds__(kThreads) void dec_bwdw_kernel(DcArgs<T> a) {
             xrow_window<T, HH>(w, ok, lane, hl, hr, win[j]);
         }
 #pragma unroll
-        for (int f = 0; f < kPF; ++f) {
-            load_xrow<T, FULL>(xp, oh0 - HH + K - 1 + f, a.XH, g.iw, c0, act, rq[f], rk[f]);
+        for (int f = 0; f < kPF; ++f) load_xrow<T, FULL>(xp, oh0 - HH + K - 1 + f, a.XH, g.iw, c0, act, rq[f], rk[f]);
+        // dy rows: the K rows of an iteration are loaded as one burst an
+        // iteration ahead into two alternating buffers (a slot's consecutive dy
+        // rows share cache lines; rows read one step apart were fetched twice)
+        auto load_dy = [&](int tbase, uint32_t (&buf)[MM][K][ND], bool (&ok)[MM][K]) {
 #pragma unroll
             for (int m = 0; m < MM; ++m)
-                load_drow<T, FULL>(dyp + m * dplane, oh0 + f, oh_end, g.ow, c0, act, gq[m][f], gk[m][f]);
-        }
-        for (int t0 = 0; t0 < a.BH; t0 += K) {  // BH is a multiple of K
+#pragma unroll
+                for (int uu = 0; uu < K; ++uu)
+                    load_drow<T, FULL>(dyp + m * dplane, oh0 + tbase + uu, oh_end, g.ow, c0, act, buf[m][uu],
+                                       ok[m][uu]);
+        };
+        auto run_iter = [&](int t0, const uint32_t (&buf)[MM][K][ND], const bool (&ok)[MM][K]) {
 #pragma unroll
             for (int uu = 0; uu < K; ++uu) {
                 const int t = t0 + uu;
-                {
-                    xrow_window<T, HH>(rq[0], rk[0], lane, hl, hr, win[(uu + K - 1) % K]);
-                    ring_pop<kPF, NX>(rq, rk);
-                    load_xrow<T, FULL>(xp, oh0 - HH + t + K - 1 + kPF, a.XH, g.iw, c0, act, rq[kPF - 1],
-                                       rk[kPF - 1]);
+                xrow_window<T, HH>(rq[0], rk[0], lane, hl, hr, win[(uu + K - 1) % K]);
+                ring_pop<kPF, NX>(rq, rk);
+                load_xrow<T, FULL>(xp, oh0 - HH + t + K - 1 + kPF, a.XH, g.iw, c0, act, rq[kPF - 1], rk[kPF - 1]);
 #pragma unroll
-                    for (int m = 0; m < MM; ++m) {
-                        float gy[RO];
-                        drow_values<T>(gq[m][0], gk[m][0], gy);
-                        ring_pop<kPF, ND>(gq[m], gk[m]);
-                        load_drow<T, FULL>(dyp + m * dplane, oh0 + t + kPF, oh_end, g.ow, c0, act, gq[m][kPF - 1],
-                                           gk[m][kPF - 1]);
+                for (int m = 0; m < MM; ++m) {
+                    float gy[RO];
+                    drow_values<T>(buf[m][uu], ok[m][uu], gy);
 #pragma unroll
-                        for (int q = 0; q < RO; ++q) {
-                            acc[m][KK] += gy[q];
+                    for (int q = 0; q < RO; ++q) {
+                        acc[m][KK] += gy[q];
 #pragma unroll
-                            for (int i = 0; i < K; ++i)
+                        for (int i = 0; i < K; ++i)
 #pragma unroll
-                                for (int j = 0; j < K; ++j)
-                                    acc[m][i * K + j] = fmaf(gy[q], win[(uu + i) % K][q + j], acc[m][i * K + j]);
-                        }
+                            for (int j = 0; j < K; ++j)
+                                acc[m][i * K + j] = fmaf(gy[q], win[(uu + i) % K][q + j], acc[m][i * K + j]);
                     }
                 }
             }
+        };
+        uint32_t dA[MM][K][ND], dB[MM][K][ND];
+        bool kA[MM][K], kB[MM][K];
+        load_dy(0, dA, kA);
+        for (int t0 = 0; t0 < a.BH; t0 += 2 * K) {  // BH is a multiple of 2K
+            load_dy(t0 + K, dB, kB);
+            run_iter(t0, dA, kA);
+            load_dy(t0 + 2 * K, dA, kA);
+            run_iter(t0 + K, dB, kB);
         }
     }
     {
@@ -386,9 +416,11 @@ bool plan_dec(const Geo &g, int pass, DcPlan &p) {
     // streams per slot measure faster (8192 * SPW / 4 units is ~2000+ waves)
     while (bh > 4 && planes * ((rows + bh - 1) / bh) < int64_t{8192} * p.SPW / 4) bh = (bh + 1) / 2;
     p.nbands = (rows + bh - 1) / bh;
-    // rows per band, a multiple of k (the row loop's unroll factor; steps past
-    // the band's last row store nothing and read dy as zero)
-    p.BH = ((rows + p.nbands - 1) / p.nbands + g.kh - 1) / g.kh * g.kh;
+    // rows per band, a multiple of the row loop's unroll factor (k; 2k for
+    // the backward passes, which alternate two dy row buffers): steps past the
+    // band's last row store nothing and read dy as zero
+    const int step = pass == 0 ? g.kh : 2 * g.kh;
+    p.BH = ((rows + p.nbands - 1) / p.nbands + step - 1) / step * step;
     p.nbands = (rows + p.BH - 1) / p.BH;
     p.nunits = g.n * p.nbands;  // units per channel
     if (pass == 2) {
