@@ -404,6 +404,7 @@ def test_graph_replay_matches_eager():
     (1, 3, 48, 48, 1, 31, 15, "bf16"),
     (2, 2, 9, 9, 1, 31, 15, "f16"),      # kernel wider than the image
     (1, 1, 130, 24, 1, 7, 3, "f32"),     # several row bands
+    (1, 2, 100, 64, 1, 13, 6, "f16"),    # several grad-weight bands, 16-bit filter staged as fp32
 ])
 def test_large_kernel_shapes(n, c, h, w, mult, k, p, dt):
     x, wt, b, dy = static_case(n, c, h, w, mult, k, 1, p, 1, DT[dt], 650 + h + w + k)
@@ -421,6 +422,8 @@ def test_large_kernel_shapes(n, c, h, w, mult, k, p, dt):
     (2, 5, 24, 40, 2, 5, "bf16"), (3, 3, 15, 16, 1, 3, "f16"),   # odd height: last dx row has no zero row
     (2, 4, 16, 24, 2, 3, "f32"), (1, 2, 9, 8, 2, 5, "bf16"),
     (5, 7, 20, 56, 1, 5, "bf16"),                                # images x bands not a multiple of a wave's units
+    # few planes of many rows: several row bands (band heights rounded to k or 2k rows)
+    (1, 2, 120, 40, 2, 5, "bf16"), (1, 3, 90, 24, 1, 3, "f32"), (2, 2, 64, 32, 1, 5, "f16"),
 ])
 def test_even_grid_shapes(n, c, h, w, mult, k, dt):
     x, wt, b, dy = static_case(n, c, h, w, mult, k, 2, k - 1, 2, DT[dt], 670 + h + w + k)
