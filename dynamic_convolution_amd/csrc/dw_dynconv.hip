@@ -76,7 +76,29 @@ __device__ __forceinline__ void store_strip(T *p, const float *acc, int valid, b
     }
 }
 
-template <typename T, int K_, int RW>
+// RW elements held in one 16-byte vector, as fp32.
+template <typename T, int RW>
+__device__ __forceinline__ void strip_values(const u32x4 &u, float *v) {
+    static_assert(sizeof(T) * RW == 16, "strip is one 16-byte vector");
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int q = 0; q < RW; ++q) {
+        if constexpr (sizeof(T) == 4) {
+            v[q] = __uint_as_float(w[q]);
+        } else {
+            const uint32_t h = (q & 1) ? (w[q >> 1] >> 16) : (w[q >> 1] & 0xffffu);
+            T t;
+            __builtin_memcpy(&t, &h, sizeof(T));
+            v[q] = to_f32(t);
+        }
+    }
+}
+
+// VF: every strip is a whole aligned 16-byte vector (w a multiple of RW), so
+// the filter loads of a branch are issued together, unconditionally, before
+// any of them is used (behind a per-strip branch each load was waited on at
+// once, serialising the nine loads).
+template <typename T, int K_, int RW, bool VF>
 __global__ __launch_bounds__(kThreads) void dynconv_kernel(DynArgs<T> a) {
     extern __shared__ __align__(16) float xs[];
     const int K = K_ ? K_ : a.k;
@@ -89,14 +111,15 @@ __global__ __launch_bounds__(kThreads) void dynconv_kernel(DynArgs<T> a) {
     const int ch = plane - nn * a.c;
     const int h0 = band * a.BH;
     const int h1 = min(h0 + a.BH, a.h);
-    const int rlo = max(h0 - a.halo, 0);
-    const int rhi = min(h1 + a.halo, a.h);
     const int64_t hw = static_cast<int64_t>(a.h) * a.w;
-    const int rows = rhi - rlo;
+    // LDS row r holds image row rbase + r (zeros outside the image), for every
+    // row a tap of the band can reach: no tap needs a row test
+    const int rbase = h0 - a.halo;
+    const int rows = (h1 - h0) + 2 * a.halo;
     const int LW = a.LW, hp = a.hp;
 
-    // stage x rows [rlo, rhi) as fp32: row r at xs[r*LW + hp ...], zeros elsewhere in the row
-    const T *src = a.x + static_cast<int64_t>(plane) * hw + static_cast<int64_t>(rlo) * a.w;
+    // stage x rows as fp32: row r at xs[r*LW + hp ...], zeros elsewhere in the row
+    const T *src = a.x + static_cast<int64_t>(plane) * hw;
     if (a.vin) {
         constexpr int VE = Vec<T>::N;
         constexpr int NB = 4;  // 16-byte loads in flight per thread
@@ -108,7 +131,11 @@ __global__ __launch_bounds__(kThreads) void dynconv_kernel(DynArgs<T> a) {
             for (int k = 0; k < NB; ++k) {
                 raw[k] = make_uint4(0u, 0u, 0u, 0u);
                 const int v = v0 + k * kThreads;
-                if (v < nvec) raw[k] = *reinterpret_cast<const uint4 *>(src + static_cast<int64_t>(v) * VE);
+                const int r = v < nvec ? static_cast<int>(fdiv(static_cast<uint32_t>(v), a.fVPR)) : 0;
+                const int ih = rbase + r;
+                if (v < nvec && ih >= 0 && ih < a.h)
+                    raw[k] = *reinterpret_cast<const uint4 *>(src + static_cast<int64_t>(ih) * a.w +
+                                                               static_cast<int64_t>(v - r * vpr) * VE);
             }
 #pragma unroll
             for (int k = 0; k < NB; ++k) {
@@ -138,7 +165,9 @@ __global__ __launch_bounds__(kThreads) void dynconv_kernel(DynArgs<T> a) {
         for (int e = tid; e < rows * LW; e += kThreads) {
             const int r = static_cast<int>(fdiv(static_cast<uint32_t>(e), a.fLW));
             const int col = e - r * LW - hp;
-            xs[e] = (col >= 0 && col < a.w) ? to_f32(src[static_cast<int64_t>(r) * a.w + col]) : 0.f;
+            const int ih = rbase + r;
+            xs[e] = (col >= 0 && col < a.w && ih >= 0 && ih < a.h)
+                        ? to_f32(src[static_cast<int64_t>(ih) * a.w + col]) : 0.f;
         }
     }
     __syncthreads();
@@ -158,11 +187,48 @@ __global__ __launch_bounds__(kThreads) void dynconv_kernel(DynArgs<T> a) {
             float acc[RW];
 #pragma unroll
             for (int q = 0; q < RW; ++q) acc[q] = 0.f;
+            if constexpr (VF && K_ > 0) {
+                constexpr int KK_ = K_ * K_;
+                u32x4 fr[KK_];
+#pragma unroll
+                for (int t = 0; t < KK_; ++t)
+                    fr[t] = __builtin_nontemporal_load(
+                        reinterpret_cast<const u32x4 *>(fb + static_cast<int64_t>(t) * hw));
+                __builtin_amdgcn_sched_barrier(0);  // all taps in flight before the first use
+#pragma unroll
+                for (int i = 0; i < K_; ++i) {
+                    const float *rp = xs + (hh + (i - rr) * d - rbase) * LW + hp + w0;
+#pragma unroll
+                    for (int j = 0; j < K_; ++j) {
+                        float fv[RW], xv[RW];
+                        strip_values<T, RW>(fr[i * K_ + j], fv);
+                        if (j == rr) {
+#pragma unroll
+                            for (int q = 0; q < RW; q += 4) {
+                                const float4 v4 = *reinterpret_cast<const float4 *>(rp + q);
+                                xv[q] = v4.x;
+                                xv[q + 1] = v4.y;
+                                xv[q + 2] = v4.z;
+                                xv[q + 3] = v4.w;
+                            }
+                        } else {
+                            const int off = (j - rr) * d;
+#pragma unroll
+                            for (int q = 0; q < RW; ++q) xv[q] = rp[off + q];
+                        }
+#pragma unroll
+                        for (int q = 0; q < RW; ++q) acc[q] = fmaf(fv[q], xv[q], acc[q]);
+                    }
+                }
+                T *yp = a.y + (static_cast<int64_t>(nn * a.nb + b) * a.c + ch) * hw + pix;
+                store_strip<T, RW>(yp, acc, RW, true);
+                continue;
+            }
 #pragma unroll
             for (int i = 0; i < K; ++i) {
                 const int sy = hh + (i - rr) * d;
                 if (sy < 0 || sy >= a.h) continue;  // whole filter row multiplies zero padding
-                const float *rp = xs + (sy - rlo) * LW + hp + w0;  // column w0 of row sy
+                const float *rp = xs + (sy - rbase) * LW + hp + w0;  // column w0 of row sy
 #pragma unroll
                 for (int j = 0; j < K; ++j) {
                     float fv[RW], xv[RW];
@@ -212,7 +278,7 @@ bool plan_dyn(int n, int c, int h, int w, int k, int maxdil, DynPlan &p) {
     int hp, LW;
     dyn_tile(w, halo, hp, LW);
     auto bytes = [&](int bh) -> int64_t {
-        const int64_t rows = std::min<int64_t>(static_cast<int64_t>(bh) + 2 * halo, h);
+        const int64_t rows = std::min<int64_t>(bh, h) + 2 * static_cast<int64_t>(halo);  // zero rows included
         const int64_t cnt = rows * LW + RW;  // + RW: a partial last strip may read past the last row
         if (cnt > (1 << 24)) return INT64_MAX;
         return cnt * static_cast<int64_t>(sizeof(float));
@@ -261,7 +327,7 @@ int run_dyn(const void *x, const void *const *filters, const int32_t *dil, int n
     a.fNS = make_fastdiv(a.NS, static_cast<uint64_t>(p.BH) * a.NS);
     a.halo = (k - 1) / 2 * maxdil;
     dyn_tile(w, a.halo, a.hp, a.LW);
-    const int rows_max = std::min(p.BH + 2 * a.halo, h);
+    const int rows_max = p.BH + 2 * a.halo;
     const int vpr = w / Vec<T>::N;
     a.fLW = make_fastdiv(a.LW, static_cast<uint64_t>(rows_max) * a.LW);
     a.fVPR = make_fastdiv(std::max(vpr, 1), static_cast<uint64_t>(rows_max) * std::max(vpr, 1));
@@ -269,12 +335,17 @@ int run_dyn(const void *x, const void *const *filters, const int32_t *dil, int n
     a.vin = reinterpret_cast<uintptr_t>(x) % 16 == 0 && w % Vec<T>::N == 0;
     a.vf = fal && (w % RW == 0) && (reinterpret_cast<uintptr_t>(y) % 16 == 0);
     const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(n) * c * p.nbands));
-    if (k == 3)
-        hipLaunchKernelGGL((dynconv_kernel<T, 3, RW>), grid, dim3(kThreads), p.lds_bytes, s, a);
+    const bool vf = a.vf != 0;
+    if (k == 3 && vf)
+        hipLaunchKernelGGL((dynconv_kernel<T, 3, RW, true>), grid, dim3(kThreads), p.lds_bytes, s, a);
+    else if (k == 3)
+        hipLaunchKernelGGL((dynconv_kernel<T, 3, RW, false>), grid, dim3(kThreads), p.lds_bytes, s, a);
+    else if (k == 5 && vf)
+        hipLaunchKernelGGL((dynconv_kernel<T, 5, RW, true>), grid, dim3(kThreads), p.lds_bytes, s, a);
     else if (k == 5)
-        hipLaunchKernelGGL((dynconv_kernel<T, 5, RW>), grid, dim3(kThreads), p.lds_bytes, s, a);
+        hipLaunchKernelGGL((dynconv_kernel<T, 5, RW, false>), grid, dim3(kThreads), p.lds_bytes, s, a);
     else
-        hipLaunchKernelGGL((dynconv_kernel<T, 0, RW>), grid, dim3(kThreads), p.lds_bytes, s, a);
+        hipLaunchKernelGGL((dynconv_kernel<T, 0, RW, false>), grid, dim3(kThreads), p.lds_bytes, s, a);
     return hipGetLastError() == hipSuccess ? kOk : kErrHip;
 }
 
