@@ -270,8 +270,9 @@ __global__ __launch_bounds__(kThreads) void rw_bwdin3_s2_kernel(RwArgs<T> a) {
             }
             T *xp = a.out + (static_cast<int64_t>(P) * g.ih + 2 * r) * g.iw + 2 * c0;
             const int valid = g.iw - 2 * c0;
-            store_values<T, RW, VB>(xp, e0, valid);
-            if (2 * r + 1 < g.ih) store_values<T, RW, VB>(xp + g.iw, e1, valid);
+            // dx is four times dy: streaming stores keep L2 for the dy rows
+            store_values<T, RW, VB, true>(xp, e0, valid);
+            if (2 * r + 1 < g.ih) store_values<T, RW, VB, true>(xp + g.iw, e1, valid);
         }
 #pragma unroll
         for (int m = 0; m < MM; ++m)

@@ -75,15 +75,23 @@ __device__ __forceinline__ void load_words(const void *p, uint32_t (&w)[NW]) {
     }
 }
 
-template <int NW>
+// NT: nontemporal (streaming) 16-byte stores, for outputs much larger than
+// the inputs of the kernel (they then leave L2 to the input rows).
+template <int NW, bool NT = false>
 __device__ __forceinline__ void store_words(void *p, const uint32_t (&w)[NW]) {
     if constexpr (NW == 2) {
         *reinterpret_cast<uint2 *>(p) = make_uint2(w[0], w[1]);
     } else {
         static_assert(NW % 4 == 0, "whole 16-byte vectors");
+        typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 #pragma unroll
-        for (int k = 0; k < NW / 4; ++k)
-            reinterpret_cast<uint4 *>(p)[k] = make_uint4(w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]);
+        for (int k = 0; k < NW / 4; ++k) {
+            const v4u t = {w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]};
+            if constexpr (NT)
+                __builtin_nontemporal_store(t, reinterpret_cast<v4u *>(p) + k);
+            else
+                reinterpret_cast<v4u *>(p)[k] = t;
+        }
     }
 }
 
@@ -209,14 +217,14 @@ __device__ __forceinline__ void row_values(const uint32_t (&w)[NW], bool ok, int
 // them when VB == 16 (the caller guarantees the strip lies inside the row),
 // else only the vectors that start before `avail` (W * sizeof(T) a multiple
 // of VB, so a vector that starts inside the row ends inside it).
-template <typename T, int N, int VB>
+template <typename T, int N, int VB, bool NT = false>
 __device__ __forceinline__ void store_values(T *p, const float (&v)[N], int avail) {
     constexpr int NW = N / kPerWord<T>;
     static_assert(NW * kPerWord<T> == N, "whole words");
     uint32_t w[NW];
     pack_words<T, NW>(v, w);
     if constexpr (VB == 16) {
-        store_words<NW>(p, w);
+        store_words<NW, NT>(p, w);
     } else {
         constexpr int VE = VB / static_cast<int>(sizeof(T));
         constexpr int NV = NW * 4 / VB;
