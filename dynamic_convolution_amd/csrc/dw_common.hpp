@@ -131,28 +131,10 @@ __device__ __forceinline__ int lds_copy_range_scalar(T *lds, const T *__restrict
     return 0;
 }
 
-// Copies nseg equal-length segments (len elements each, segment k starting at
-// element start(k) of src) densely into lds[k*len + e], one element per lane
-// and step; consecutive lanes read consecutive elements of a segment.
-template <typename T, typename StartFn>
-__device__ __forceinline__ void lds_copy_segments(T *lds, const T *__restrict__ src, int nseg,
-                                                  int len, FastDiv flen, StartFn start, int tid,
-                                                  int nthreads) {
-    const int total = nseg * len;
-    for (int e = tid; e < total; e += nthreads) {
-        const int k = static_cast<int>(fdiv(static_cast<uint32_t>(e), flen));
-        lds[e] = src[start(k) + (e - k * len)];
-    }
-}
-
 // LDS slots a copied range of `cnt` elements occupies (vector rounding on both ends).
 template <typename T> __host__ __device__ constexpr int lds_slots(int cnt) {
     return ((cnt + 2 * Vec<T>::N - 1) / Vec<T>::N + 1) * Vec<T>::N;
 }
-
-}  // namespace dw
-
-namespace dw {
 
 // ---------------------------------------------------------------- band planning
 // A workgroup either stages G whole input planes (full = 1, one band) or a

@@ -224,12 +224,10 @@ __global__ __launch_bounds__(kThreads) void dynconv_kernel(DynArgs<T> a) {
                 store_strip<T, RW>(yp, acc, RW, true);
                 continue;
             }
-#pragma unroll
-            for (int i = 0; i < K; ++i) {
+            for (int i = 0; i < K; ++i) {  // K is a constant unless k is a runtime size
                 const int sy = hh + (i - rr) * d;
                 if (sy < 0 || sy >= a.h) continue;  // whole filter row multiplies zero padding
                 const float *rp = xs + (sy - rbase) * LW + hp + w0;  // column w0 of row sy
-#pragma unroll
                 for (int j = 0; j < K; ++j) {
                     float fv[RW], xv[RW];
                     load_strip<T, RW>(fb + static_cast<int64_t>(i * K + j) * hw, fv, valid, a.vf != 0);

@@ -630,7 +630,6 @@ RwArgs<T> rw_args(const Geo &g, const RwPlan &p) {
 
 template <typename T, int S, int MM, bool BWD>
 int launch_conv3(const Geo &g, const void *in, const void *w, const void *b, void *out, hipStream_t st) {
-    constexpr int RW = Vec<T>::N;
     RwPlan p{};
     const int OW = BWD ? g.iw : g.ow, OH = BWD ? g.ih : g.oh;
     const int IW = BWD ? g.ow : g.iw;
@@ -719,7 +718,6 @@ bool plan_bwdw(const Geo &g, RwPlan &p) {
 
 template <typename T, int S, int MM>
 int launch_bwdw(const Geo &g, const RwPlan &p, const void *x, const void *dy, void *ws, hipStream_t st) {
-    constexpr int RW = Vec<T>::N;
     RwArgs<T> a = rw_args<T>(g, p);
     a.in = static_cast<const T *>(x);
     a.in2 = static_cast<const T *>(dy);
