@@ -37,8 +37,25 @@ template <typename T> struct LkArgs {
     int nbands;
     int NCB, NRB;  // column / row blocks of output tiles in a band
     int wsm_off;   // float offset of the fp32 filter copy in LDS
-    FastDiv fpitch;
+    int vin;       // input rows are whole 16-byte vectors (aligned): vector staging
+    int vout;      // output tiles are whole (OW % TC == 0) and aligned: vector stores
+    FastDiv fpitch, fvpr, fpad;
 };
+
+// TC fp32 values rounded to T and stored as 16-byte (or 8-byte) vectors.
+template <typename T, int TC>
+__device__ __forceinline__ void store_tile_row(T *p, const float (&v)[TC]) {
+    if constexpr (sizeof(T) == 4) {
+#pragma unroll
+        for (int q = 0; q < TC; q += 4)
+            *reinterpret_cast<float4 *>(p + q) = make_float4(v[q], v[q + 1], v[q + 2], v[q + 3]);
+    } else if constexpr (TC == 8) {
+        *reinterpret_cast<uint4 *>(p) =
+            make_uint4(pack2<T>(v[0], v[1]), pack2<T>(v[2], v[3]), pack2<T>(v[4], v[5]), pack2<T>(v[6], v[7]));
+    } else {
+        *reinterpret_cast<uint2 *>(p) = make_uint2(pack2<T>(v[0], v[1]), pack2<T>(v[2], v[3]));
+    }
+}
 
 template <typename T, int K, int TR, int TC, bool FLIP>
 __global__ __launch_bounds__(256) void lk_conv_kernel(LkArgs<T> a) {
@@ -58,12 +75,57 @@ __global__ __launch_bounds__(256) void lk_conv_kernel(LkArgs<T> a) {
     const T *src = a.in + (static_cast<int64_t>(n) * (FLIP ? a.C : a.C / a.mult) + cin) * a.IH * a.IW;
 
     // 1. stage padded rows [oh0 - P, oh0 - P + rows) x cols [-P, pitch - P)
-    const int total = rows * a.pitch;
-    for (int e = tid; e < total; e += nthr) {
-        const int r = static_cast<int>(fdiv(static_cast<uint32_t>(e), a.fpitch));
-        const int col = e - r * a.pitch;
-        const int ih = oh0 - a.P + r, iw = col - a.P;
-        xs[e] = (ih >= 0 && ih < a.IH && iw >= 0 && iw < a.IW) ? to_f32(src[ih * a.IW + iw]) : 0.f;
+    if (a.vin) {
+        // tile rows r_lo .. r_hi - 1 hold image rows; their image part is copied
+        // with 16-byte loads (4 in flight per lane), the rest of the tile is zeroed
+        constexpr int VE = Vec<T>::N;
+        constexpr int NB = 4;
+        const int r_lo = max(0, a.P - oh0), r_hi = min(rows, a.IH + a.P - oh0);
+        const int vpr = a.IW / VE;
+        const int nvec = max(r_hi - r_lo, 0) * vpr;
+        const T *s0 = src + static_cast<int64_t>(oh0 - a.P + r_lo) * a.IW;
+        for (int v0 = tid; v0 < nvec; v0 += NB * nthr) {
+            uint4 raw[NB];
+#pragma unroll
+            for (int k = 0; k < NB; ++k) {
+                raw[k] = make_uint4(0u, 0u, 0u, 0u);
+                const int v = v0 + k * nthr;
+                if (v < nvec) raw[k] = *reinterpret_cast<const uint4 *>(s0 + static_cast<int64_t>(v) * VE);
+            }
+#pragma unroll
+            for (int k = 0; k < NB; ++k) {
+                const int v = v0 + k * nthr;
+                if (v < nvec) {
+                    const int rr = static_cast<int>(fdiv(static_cast<uint32_t>(v), a.fvpr));
+                    float *d = xs + (r_lo + rr) * a.pitch + a.P + (v - rr * vpr) * VE;
+                    union {
+                        uint4 u;
+                        T t[VE];
+                    } b;
+                    b.u = raw[k];
+#pragma unroll
+                    for (int e = 0; e < VE; ++e) d[e] = to_f32(b.t[e]);
+                }
+            }
+        }
+        const int padw = a.pitch - a.IW;  // zero columns of an image row: P left, the rest right
+        for (int e = tid; e < max(r_hi - r_lo, 0) * padw; e += nthr) {
+            const int rr = static_cast<int>(fdiv(static_cast<uint32_t>(e), a.fpad));
+            const int j = e - rr * padw;
+            xs[(r_lo + rr) * a.pitch + (j < a.P ? j : a.IW + j)] = 0.f;
+        }
+        const int top = min(r_lo, rows) * a.pitch;  // whole zero rows above and below the image
+        for (int e = tid; e < top; e += nthr) xs[e] = 0.f;
+        const int bot0 = max(r_hi, r_lo) * a.pitch;
+        for (int e = bot0 + tid; e < rows * a.pitch; e += nthr) xs[e] = 0.f;
+    } else {
+        const int total = rows * a.pitch;
+        for (int e = tid; e < total; e += nthr) {
+            const int r = static_cast<int>(fdiv(static_cast<uint32_t>(e), a.fpitch));
+            const int col = e - r * a.pitch;
+            const int ih = oh0 - a.P + r, iw = col - a.P;
+            xs[e] = (ih >= 0 && ih < a.IH && iw >= 0 && iw < a.IW) ? to_f32(src[ih * a.IW + iw]) : 0.f;
+        }
     }
     // The filter is staged once as fp32 in LDS and each tap is read with a
     // uniform-address (broadcast) LDS read right before its FMAs.  (Scalar
@@ -115,9 +177,13 @@ __global__ __launch_bounds__(256) void lk_conv_kernel(LkArgs<T> a) {
 #pragma unroll
         for (int tr = 0; tr < TR; ++tr) {
             if (oh0 + rb * TR + tr >= min(oh0 + a.BH, a.OH)) continue;
+            if (a.vout) {
+                store_tile_row<T, TC>(op + tr * a.OW, acc[tr]);
+            } else {
 #pragma unroll
-            for (int q = 0; q < TC; ++q)
-                if (cb * TC + q < a.OW) op[tr * a.OW + q] = from_f32<T>(acc[tr][q]);
+                for (int q = 0; q < TC; ++q)
+                    if (cb * TC + q < a.OW) op[tr * a.OW + q] = from_f32<T>(acc[tr][q]);
+            }
         }
     }
 }
@@ -162,6 +228,11 @@ int run_lk(const LkArgs<T> &a0, const LkPlan &p, int planes, hipStream_t s) {
     a.NRB = p.NRB;
     a.fpitch = make_fastdiv(p.pitch, static_cast<uint64_t>(p.BH + K) * p.pitch);
     a.wsm_off = (p.BH + K - 1) * p.pitch;
+    const int rows_max = p.BH + K - 1;
+    a.vin = a.IW % Vec<T>::N == 0 && reinterpret_cast<uintptr_t>(a.in) % 16 == 0;
+    a.vout = a.OW % TC == 0 && reinterpret_cast<uintptr_t>(a.out) % 16 == 0;
+    a.fvpr = make_fastdiv(std::max(a.IW / Vec<T>::N, 1), static_cast<uint64_t>(rows_max) * (a.IW / Vec<T>::N + 1));
+    a.fpad = make_fastdiv(std::max(p.pitch - a.IW, 1), static_cast<uint64_t>(rows_max) * p.pitch);
     hipLaunchKernelGGL((lk_conv_kernel<T, K, kTR, TC, FLIP>), dim3(planes * p.nbands), dim3(p.threads), p.lds_bytes, s, a);
     return hipGetLastError() == hipSuccess ? kOk : kErrHip;
 }
