@@ -306,8 +306,45 @@ template <typename T> struct LkwArgs {
     int xpitch;    // LDS pitch of the padded x rows
     int xrows;     // LDS rows reserved for x: BH + k - 1
     int dpitch;    // LDS pitch of the dy rows (multiple of 8)
-    FastDiv fxp, fdp;
+    int vx, vd;    // x / dy rows are whole aligned 16-byte vectors: vector staging
+    FastDiv fxp, fdp, fxv, fdv;
 };
+
+// Copies `nrows` rows of `w` elements (whole 16-byte vectors, row stride w in
+// global memory) into fp32 LDS rows of `pitch` floats starting at column
+// col0; 4 loads in flight per lane.  fvpr divides by w / VE.
+template <typename T>
+__device__ __forceinline__ void stage_rows_vec(float *lds, int pitch, int col0, const T *src, int nrows, int w,
+                                               FastDiv fvpr, int tid, int nthr) {
+    constexpr int VE = Vec<T>::N;
+    constexpr int NB = 4;
+    const int vpr = w / VE;
+    const int nvec = nrows * vpr;
+    for (int v0 = tid; v0 < nvec; v0 += NB * nthr) {
+        uint4 raw[NB];
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+            raw[k] = make_uint4(0u, 0u, 0u, 0u);
+            const int v = v0 + k * nthr;
+            if (v < nvec) raw[k] = *reinterpret_cast<const uint4 *>(src + static_cast<int64_t>(v) * VE);
+        }
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+            const int v = v0 + k * nthr;
+            if (v < nvec) {
+                const int r = static_cast<int>(fdiv(static_cast<uint32_t>(v), fvpr));
+                float *d = lds + r * pitch + col0 + (v - r * vpr) * VE;
+                union {
+                    uint4 u;
+                    T t[VE];
+                } b;
+                b.u = raw[k];
+#pragma unroll
+                for (int e = 0; e < VE; ++e) d[e] = to_f32(b.t[e]);
+            }
+        }
+    }
+}
 
 template <typename T, int K, int TR, int TC>
 __global__ __launch_bounds__(256) void lk_bwdw_kernel(LkwArgs<T> a) {
@@ -339,20 +376,35 @@ __global__ __launch_bounds__(256) void lk_bwdw_kernel(LkwArgs<T> a) {
     const int n0 = chunk * a.npc, n1 = min(n0 + a.npc, a.N);
     // padded x rows oh0 .. oh1 + k - 2 (image rows minus P) and dy rows oh0 .. oh1 - 1
     const int xtot = (oh1 - oh0 + K - 1) * a.xpitch, dtot = (oh1 - oh0) * a.dpitch;
+    // tile rows r_lo .. r_hi - 1 hold image rows (at columns P .. P + IW - 1)
+    const int r_lo = max(0, a.P - oh0), r_hi = min(oh1 - oh0 + K - 1, a.IH + a.P - oh0);
+    if (a.vx && a.vd) {
+        // the zero padding is the same for every image: write the whole tile once,
+        // then each image overwrites only its data
+        for (int e = tid; e < xtot; e += 256) xs[e] = 0.f;
+        for (int e = tid; e < dtot; e += 256) ds[e] = 0.f;
+    }
     for (int n = n0; n < n1; ++n) {
         __syncthreads();
         const T *xp = a.x + (static_cast<int64_t>(n) * a.C + c) * a.IH * a.IW;
         const T *dp = a.dy + (static_cast<int64_t>(n) * a.C + c) * a.OH * a.OW;
-        for (int e = tid; e < xtot; e += 256) {
-            const int r = static_cast<int>(fdiv(static_cast<uint32_t>(e), a.fxp));
-            const int col = e - r * a.xpitch;
-            const int ih = oh0 + r - a.P, iw = col - a.P;
-            xs[e] = (ih >= 0 && ih < a.IH && iw >= 0 && iw < a.IW) ? to_f32(xp[ih * a.IW + iw]) : 0.f;
-        }
-        for (int e = tid; e < dtot; e += 256) {
-            const int r = static_cast<int>(fdiv(static_cast<uint32_t>(e), a.fdp));
-            const int col = e - r * a.dpitch;
-            ds[e] = col < a.OW ? to_f32(dp[(oh0 + r) * a.OW + col]) : 0.f;
+        if (a.vx && a.vd) {
+            if (r_hi > r_lo)
+                stage_rows_vec<T>(xs + r_lo * a.xpitch, a.xpitch, a.P, xp + static_cast<int64_t>(oh0 + r_lo - a.P) * a.IW,
+                                  r_hi - r_lo, a.IW, a.fxv, tid, 256);
+            stage_rows_vec<T>(ds, a.dpitch, 0, dp + static_cast<int64_t>(oh0) * a.OW, oh1 - oh0, a.OW, a.fdv, tid, 256);
+        } else {
+            for (int e = tid; e < xtot; e += 256) {
+                const int r = static_cast<int>(fdiv(static_cast<uint32_t>(e), a.fxp));
+                const int col = e - r * a.xpitch;
+                const int ih = oh0 + r - a.P, iw = col - a.P;
+                xs[e] = (ih >= 0 && ih < a.IH && iw >= 0 && iw < a.IW) ? to_f32(xp[ih * a.IW + iw]) : 0.f;
+            }
+            for (int e = tid; e < dtot; e += 256) {
+                const int r = static_cast<int>(fdiv(static_cast<uint32_t>(e), a.fdp));
+                const int col = e - r * a.dpitch;
+                ds[e] = col < a.OW ? to_f32(dp[(oh0 + r) * a.OW + col]) : 0.f;
+            }
         }
         __syncthreads();
         if (!lane_ok) continue;
@@ -472,6 +524,10 @@ int run_lkw(const Geo &g, const LkwPlan &p, const void *x, const void *dy, void 
     a.dpitch = p.dpitch;
     a.fxp = make_fastdiv(p.xpitch, static_cast<uint64_t>(p.xrows) * p.xpitch + 256);
     a.fdp = make_fastdiv(p.dpitch, static_cast<uint64_t>(p.BH) * p.dpitch + 256);
+    a.vx = g.iw % Vec<T>::N == 0 && reinterpret_cast<uintptr_t>(x) % 16 == 0;
+    a.vd = g.ow % Vec<T>::N == 0 && reinterpret_cast<uintptr_t>(dy) % 16 == 0;
+    a.fxv = make_fastdiv(std::max(g.iw / Vec<T>::N, 1), static_cast<uint64_t>(p.xrows) * (g.iw / Vec<T>::N + 1) + 1024);
+    a.fdv = make_fastdiv(std::max(g.ow / Vec<T>::N, 1), static_cast<uint64_t>(p.BH) * (g.ow / Vec<T>::N + 1) + 1024);
     hipLaunchKernelGGL((lk_bwdw_kernel<T, K, kTR, 8>), dim3(g.ic * p.NC * p.nbands), dim3(256), p.lds_bytes, s, a);
     return hipGetLastError() == hipSuccess ? kOk : kErrHip;
 }
