@@ -286,23 +286,46 @@ __global__ __launch_bounds__(kThreads) void bwd_weight_taps_kernel(BwArgs<T> a) 
 }
 
 // Pass 2: dw[o, t] (t < kk) and db[o] (t == kk) from the chunk partials.
+// 2^lrl adjacent lanes share one output slot: lane l adds chunks l, l + 2^lrl,
+// ... in order and the lanes are then combined by a fixed xor tree, so the
+// result does not depend on scheduling.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void bwd_weight_reduce_kernel(const float *__restrict__ ws, T *dwt,
                                                                      T *db, int oc, int mult, int kk,
-                                                                     int NC, int nslots) {
-    const int idx = blockIdx.x * kThreads + threadIdx.x;
-    if (idx >= oc * (kk + 1)) return;
-    const int o = idx / (kk + 1);
-    const int t = idx - o * (kk + 1);
-    if (t == kk && db == nullptr) return;
-    const int ic = o / mult, m = o - ic * mult;
-    const float *p = ws + static_cast<int64_t>(ic) * NC * nslots + m * (kk + 1) + t;
+                                                                     int NC, int nslots, int lrl) {
+    const int gid = blockIdx.x * kThreads + threadIdx.x;
+    const int RL = 1 << lrl;
+    const int idx = gid >> lrl, lane = gid & (RL - 1);
+    const bool valid = idx < oc * (kk + 1);
+    int o = 0, t = 0;
     float s = 0.f;
-    for (int c = 0; c < NC; ++c) s += p[static_cast<int64_t>(c) * nslots];
+    if (valid) {
+        o = idx / (kk + 1);
+        t = idx - o * (kk + 1);
+        const int ic = o / mult, m = o - ic * mult;
+        const float *p = ws + static_cast<int64_t>(ic) * NC * nslots + m * (kk + 1) + t;
+        for (int c = lane; c < NC; c += RL) s += p[static_cast<int64_t>(c) * nslots];
+    }
+    for (int off = RL >> 1; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+    if (!valid || lane != 0) return;
     if (t < kk)
         dwt[static_cast<int64_t>(o) * kk + t] = from_f32<T>(s);
-    else
+    else if (db != nullptr)
         db[o] = from_f32<T>(s);
+}
+
+// Launches pass 2 with about four chunks per lane (at most 64 lanes per slot).
+template <typename T>
+int launch_reduce(const Geo &g, const void *ws, void *dwt, void *db, int NC, int nslots, hipStream_t s) {
+    const int kk = g.kh * g.kw;
+    const int64_t total = static_cast<int64_t>(g.oc) * (kk + 1);
+    int lrl = 0;
+    while (lrl < 6 && (1 << (lrl + 2)) < NC && (total << (lrl + 1)) <= 0x7fff0000LL) ++lrl;
+    const int64_t threads = total << lrl;
+    hipLaunchKernelGGL((bwd_weight_reduce_kernel<T>), dim3(static_cast<unsigned>((threads + kThreads - 1) / kThreads)),
+                       dim3(kThreads), 0, s, static_cast<const float *>(ws), static_cast<T *>(dwt),
+                       static_cast<T *>(db), g.oc, g.mult, kk, NC, nslots, lrl);
+    return hipGetLastError() == hipSuccess ? kOk : kErrHip;
 }
 
 bool small_variant(const Geo &g) {
@@ -426,11 +449,7 @@ int dispatch_bwd_weight(const Geo &g, const void *x, const void *dy, void *dwt, 
              : decim ? decim_bwd_weight(g, x, dy, ws, dt, s)
                      : rowwalk_bwd_weight(g, x, dy, ws, dt, s);
         if (rc != kOk) return rc;
-        const int total = g.oc * (kk + 1);
-        hipLaunchKernelGGL((bwd_weight_reduce_kernel<T>), dim3((total + kThreads - 1) / kThreads), dim3(kThreads),
-                           0, s, static_cast<const float *>(ws), static_cast<T *>(dwt), static_cast<T *>(db), g.oc,
-                           g.mult, kk, NC, nslots);
-        return hipGetLastError() == hipSuccess ? kOk : kErrHip;
+        return launch_reduce<T>(g, ws, dwt, db, NC, nslots, s);
     }
     BwPlan p;
     if (!plan_bwd_weight(g, sizeof(T), p)) return kErrUnsupported;
@@ -452,11 +471,7 @@ int dispatch_bwd_weight(const Geo &g, const void *x, const void *dy, void *dwt, 
         rc = hipGetLastError() == hipSuccess ? kOk : kErrHip;
     }
     if (rc != kOk) return rc;
-    const int total = g.oc * (kk + 1);
-    hipLaunchKernelGGL((bwd_weight_reduce_kernel<T>), dim3((total + kThreads - 1) / kThreads), dim3(kThreads), 0,
-                       s, static_cast<const float *>(ws), static_cast<T *>(dwt), static_cast<T *>(db), g.oc,
-                       g.mult, kk, p.NC, p.nslots);
-    return hipGetLastError() == hipSuccess ? kOk : kErrHip;
+    return launch_reduce<T>(g, ws, dwt, db, p.NC, p.nslots, s);
 }
 
 }  // namespace

@@ -7,188 +7,186 @@
 // 200-800 byte piece per image, scattered with the stride of a whole image,
 // and a per-channel walk reads short rows from many places.  Here a workgroup
 // owns G adjacent channels instead: for a fixed image their x planes are one
-// contiguous range and their dy planes another.  Each iteration stages NI
-// images' worth of both ranges in LDS, every lane issuing all of its 16-byte
-// loads before any LDS store (2*NI requests in flight per lane).  Each
-// channel's output pixels are split over TPC lanes accumulating the kh*kw tap
-// sums and the bias sum; the TPC lanes of a channel are reduced with shuffles
-// in a fixed order and one lane writes the (channel, image chunk) partial to
-// the workspace [ic][chunk][M*(kh*kw+1)] that pass 2 adds up.
+// contiguous range and their dy planes another, and the workgroup walks a
+// chunk of images, staging one image's two ranges in LDS at a time.  When the
+// ranges are whole 16-byte vectors the next image's vectors are loaded into
+// registers while the current image is computed.
+//
+// Each lane owns one (channel, output row) for the whole chunk: per image it
+// reads its dy row and the kh input rows under it from LDS and accumulates the
+// kh*kw tap sums and the bias sum in registers, so the sum over images needs
+// no cross-lane step.  At the end the output rows of each channel are added
+// in a fixed order through LDS and one lane per (channel, slot) writes the
+// (channel, image chunk) partial to the workspace [ic][chunk][M*(kh*kw+1)]
+// that pass 2 adds up.
 #include "dw_common.hpp"
 #include "dw_internal.hpp"
 
 namespace dw {
 namespace {
 
-constexpr int kSmallLds = 32 * 1024;  // staged bytes per workgroup
-constexpr int kNI = 4;                // images staged per iteration
+constexpr int kStageCap = 32 * 1024;  // staged bytes per image and workgroup
+constexpr int kPV = kStageCap / (16 * kThreads);  // 16-byte vectors per lane and image
+constexpr int kRedCh = 16;            // accumulators per lane per reduction step
 
 template <typename T> struct SwArgs {
     const T *x;
     const T *dy;
     float *ws;
     Geo g;
-    int G;          // channels per workgroup
-    int NC, npc;    // image chunks, images per chunk
-    int TPC;        // lanes per channel (power of two <= 64)
-    FastDiv fPW;    // output width
-    int xslots, dslots;  // LDS elements per staged image (x, dy)
-    int vec;        // x and dy 16-byte aligned
+    int G;             // channels per workgroup
+    int NC, npc;       // image chunks, images per chunk
+    int gpre;          // LDS elements before the x planes (left-pad reads)
+    int dofs;          // LDS element index of the first dy plane
+    int vec;           // every staged range is whole, aligned 16-byte vectors
 };
 
-// Stages the x range and the dy range of images n0 .. n0+NI-1 (those < n1).
-template <typename T>
-__device__ __forceinline__ void stage_images(const SwArgs<T> &a, T *xs, T *ds, int c0, int Gc, int n0, int n1,
-                                             int (&xo)[kNI], int (&dof)[kNI], int tid) {
-    constexpr int VE = Vec<T>::N;
-    const Geo &g = a.g;
-    const int64_t iplane = static_cast<int64_t>(g.ih) * g.iw, oplane = static_cast<int64_t>(g.oh) * g.ow;
-    const int64_t xlen = Gc * iplane, dlen = Gc * g.mult * oplane;
-    int64_t xb[kNI], db[kNI];
-    int nvx = 0, nvd = 0;
-#pragma unroll
-    for (int u = 0; u < kNI; ++u) {
-        const int n = n0 + u;
-        xb[u] = (static_cast<int64_t>(n) * g.ic + c0) * iplane;
-        db[u] = (static_cast<int64_t>(n) * g.oc + static_cast<int64_t>(c0) * g.mult) * oplane;
-        xo[u] = static_cast<int>(xb[u] & (VE - 1));
-        dof[u] = static_cast<int>(db[u] & (VE - 1));
-        nvx = max(nvx, static_cast<int>((xo[u] + xlen + VE - 1) / VE));
-        nvd = max(nvd, static_cast<int>((dof[u] + dlen + VE - 1) / VE));
-    }
-    if (!a.vec) {  // base pointers not 16-byte aligned: element copies
-#pragma unroll
-        for (int u = 0; u < kNI; ++u) {
-            xo[u] = dof[u] = 0;
-            if (n0 + u >= n1) continue;
-            for (int e = tid; e < xlen; e += kThreads) xs[u * a.xslots + e] = a.x[xb[u] + e];
-            for (int e = tid; e < dlen; e += kThreads) ds[u * a.dslots + e] = a.dy[db[u] + e];
-        }
-        return;
-    }
-    const int nv = max(nvx, nvd);
-    for (int v = tid; v < nv; v += kThreads) {
-        uint4 rx[kNI], rd[kNI];
-#pragma unroll
-        for (int u = 0; u < kNI; ++u) rx[u] = rd[u] = make_uint4(0, 0, 0, 0);
-        // all loads of this lane first ...
-#pragma unroll
-        for (int u = 0; u < kNI; ++u) {
-            if (n0 + u >= n1) continue;
-            const int64_t ex = (xb[u] - xo[u]) + static_cast<int64_t>(v) * VE;
-            if (v < nvx && ex >= xb[u] && ex + VE <= xb[u] + xlen) rx[u] = *reinterpret_cast<const uint4 *>(a.x + ex);
-            const int64_t ed = (db[u] - dof[u]) + static_cast<int64_t>(v) * VE;
-            if (v < nvd && ed >= db[u] && ed + VE <= db[u] + dlen) rd[u] = *reinterpret_cast<const uint4 *>(a.dy + ed);
-        }
-        // ... then the LDS stores (partial end vectors element by element)
-#pragma unroll
-        for (int u = 0; u < kNI; ++u) {
-            if (n0 + u >= n1) continue;
-            const int64_t ex = (xb[u] - xo[u]) + static_cast<int64_t>(v) * VE;
-            T *lx = xs + u * a.xslots + v * VE;
-            if (v < nvx) {
-                if (ex >= xb[u] && ex + VE <= xb[u] + xlen) {
-                    *reinterpret_cast<uint4 *>(lx) = rx[u];
-                } else {
-#pragma unroll
-                    for (int k = 0; k < VE; ++k)
-                        lx[k] = (ex + k >= xb[u] && ex + k < xb[u] + xlen) ? a.x[ex + k] : T{};
-                }
-            }
-            const int64_t ed = (db[u] - dof[u]) + static_cast<int64_t>(v) * VE;
-            T *ld = ds + u * a.dslots + v * VE;
-            if (v < nvd) {
-                if (ed >= db[u] && ed + VE <= db[u] + dlen) {
-                    *reinterpret_cast<uint4 *>(ld) = rd[u];
-                } else {
-#pragma unroll
-                    for (int k = 0; k < VE; ++k)
-                        ld[k] = (ed + k >= db[u] && ed + k < db[u] + dlen) ? a.dy[ed + k] : T{};
-                }
-            }
-        }
-    }
-}
+// In-row positions a lane touches: q*S + j*D for q < OWM, j < K.
+template <int K, int S, int D, int OWM> struct RowSpan {
+    static constexpr int IWM = (OWM - 1) * S + (K - 1) * D + 1;
+};
 
-template <typename T, int KH, int KW, int S, int D, int MM>
+template <typename T, int K, int S, int D, int MM, int OWM>
 __global__ __launch_bounds__(kThreads) void sp_bwdw_kernel(SwArgs<T> a) {
     extern __shared__ __align__(16) unsigned char smem[];
-    constexpr int KK = KH * KW;
+    constexpr int KK = K * K;
+    constexpr int NT = MM * (KK + 1);
+    constexpr int IWM = RowSpan<K, S, D, OWM>::IWM;
+    constexpr int VE = Vec<T>::N;
     const Geo &g = a.g;
     const int tid = threadIdx.x;
-    const int cg = blockIdx.x / a.NC;
-    const int chunk = blockIdx.x - cg * a.NC;
+    // consecutive workgroups take adjacent channel groups of the same images,
+    // so the groups in flight read a few long stretches of memory
+    const int ngroups = (g.ic + a.G - 1) / a.G;
+    const int chunk = blockIdx.x / ngroups;
+    const int cg = blockIdx.x - chunk * ngroups;
     const int c0 = cg * a.G;
     const int Gc = min(a.G, g.ic - c0);
-    const int lch = tid / a.TPC;  // local channel of this lane
-    const int sub = tid - lch * a.TPC;
     const int iplane = g.ih * g.iw, oplane = g.oh * g.ow;
-    T *xs = reinterpret_cast<T *>(smem);
-    T *ds = xs + kNI * a.xslots;
+    const int ch = tid / g.oh;
+    const int r = tid - ch * g.oh;
+    const bool active = ch < Gc;
+    T *lds = reinterpret_cast<T *>(smem);
+    T *xs = lds + a.gpre;
+    T *ds = lds + a.dofs;
+    const int xlen = Gc * iplane, dlen = Gc * MM * oplane;
+    const int nvx = xlen / VE, nv = nvx + dlen / VE;
+
     float acc[MM][KK + 1];
 #pragma unroll
     for (int m = 0; m < MM; ++m)
 #pragma unroll
         for (int t = 0; t <= KK; ++t) acc[m][t] = 0.f;
+
     const int n_beg = chunk * a.npc;
     const int n_end = min(n_beg + a.npc, g.n);
-    for (int n0 = n_beg; n0 < n_end; n0 += kNI) {
-        int xo[kNI], dof[kNI];
-        __syncthreads();  // the previous images' LDS reads are done
-        stage_images(a, xs, ds, c0, Gc, n0, n_end, xo, dof, tid);
-        __syncthreads();
-        if (lch < Gc) {
+    auto xbase = [&](int n) { return (static_cast<int64_t>(n) * g.ic + c0) * iplane; };
+    auto dbase = [&](int n) { return (static_cast<int64_t>(n) * g.oc + static_cast<int64_t>(c0) * MM) * oplane; };
+
+    // register-staged 16-byte vectors of one image: lane vector k is flat
+    // vector tid + k*kThreads of [x range | dy range]; lanes past the end load
+    // the first x vector again (a valid address) and store nothing
+    typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+    v4u pf[kPV];
+    auto issue = [&](int n) {
+        const T *xb = a.x + xbase(n), *db = a.dy + dbase(n);
 #pragma unroll
-            for (int u = 0; u < kNI; ++u) {
-                if (n0 + u >= n_end) continue;
-                const T *xp = xs + u * a.xslots + xo[u] + lch * iplane;
-                const T *dp = ds + u * a.dslots + dof[u] + lch * MM * oplane;
-                for (int pix = sub; pix < oplane; pix += a.TPC) {
-                    const int oh = static_cast<int>(fdiv(static_cast<uint32_t>(pix), a.fPW));
-                    const int ow = pix - oh * g.ow;
-                    float gy[MM];
+        for (int k = 0; k < kPV; ++k) {
+            const int f = tid + k * kThreads;
+            const T *p = f < nvx ? xb + f * VE : (f < nv ? db + (f - nvx) * VE : xb);
+            pf[k] = *reinterpret_cast<const v4u *>(p);
+        }
+    };
+    auto commit = [&]() {
+#pragma unroll
+        for (int k = 0; k < kPV; ++k) {
+            const int f = tid + k * kThreads;
+            if (f < nv) {
+                T *q = f < nvx ? xs + f * VE : ds + (f - nvx) * VE;
+                *reinterpret_cast<v4u *>(q) = pf[k];
+            }
+        }
+    };
+
+    // uniform column masks: position p of a row window reads column p - pw
+    uint64_t colok = 0;
+#pragma unroll
+    for (int p = 0; p < IWM; ++p) {
+        const int c = p - g.pw;
+        if (c >= 0 && c < g.iw) colok |= 1ull << p;
+    }
+
+    if (a.vec && n_beg < n_end) issue(n_beg);
+    for (int n = n_beg; n < n_end; ++n) {
+        __syncthreads();  // the previous image's LDS reads are done
+        if (a.vec) {
+            commit();
+        } else {
+            const int64_t xb = xbase(n), db = dbase(n);
+            for (int e = tid; e < xlen; e += kThreads) xs[e] = a.x[xb + e];
+            for (int e = tid; e < dlen; e += kThreads) ds[e] = a.dy[db + e];
+        }
+        __syncthreads();
+        if (a.vec && n + 1 < n_end) issue(n + 1);
+        if (active) {
+            const T *dp = ds + ch * MM * oplane + r * g.ow;
+            float dv[MM][OWM];
+#pragma unroll
+            for (int m = 0; m < MM; ++m)
+#pragma unroll
+                for (int q = 0; q < OWM; ++q) {
+                    const float v = to_f32(dp[m * oplane + q]);
+                    dv[m][q] = q < g.ow ? v : 0.f;
+                    acc[m][KK] += dv[m][q];
+                }
+#pragma unroll
+            for (int i = 0; i < K; ++i) {
+                const int ih = r * S - g.ph + i * D;
+                const bool rowok = ih >= 0 && ih < g.ih;
+                const T *xr = xs + ch * iplane + (rowok ? ih : 0) * g.iw - g.pw;
+                float xv[IWM];
+#pragma unroll
+                for (int p = 0; p < IWM; ++p) {
+                    const float v = to_f32(xr[p]);
+                    xv[p] = (colok >> p) & 1 ? v : 0.f;
+                }
+#pragma unroll
+                for (int j = 0; j < K; ++j)
 #pragma unroll
                     for (int m = 0; m < MM; ++m) {
-                        gy[m] = to_f32(dp[m * oplane + pix]);
-                        acc[m][KK] += gy[m];
+                        float t = 0.f;
+#pragma unroll
+                        for (int q = 0; q < OWM; ++q) t = fmaf(dv[m][q], xv[q * S + j * D], t);
+                        acc[m][i * K + j] += rowok ? t : 0.f;
                     }
-#pragma unroll
-                    for (int i = 0; i < KH; ++i) {
-                        const int ih = oh * S - g.ph + i * D;
-                        if (ih < 0 || ih >= g.ih) continue;
-#pragma unroll
-                        for (int j = 0; j < KW; ++j) {
-                            const int iw = ow * S - g.pw + j * D;
-                            if (iw < 0 || iw >= g.iw) continue;
-                            const float xv = to_f32(xp[ih * g.iw + iw]);
-#pragma unroll
-                            for (int m = 0; m < MM; ++m) acc[m][i * KW + j] = fmaf(gy[m], xv, acc[m][i * KW + j]);
-                        }
-                    }
-                }
             }
         }
     }
-    // fixed-order reduction over the TPC lanes of each channel (aligned groups in one wave)
+
+    // fixed-order sum over the output rows of each channel, kRedCh slots at a time
+    float *red = reinterpret_cast<float *>(smem);
+    constexpr int RC = NT < kRedCh ? NT : kRedCh;
 #pragma unroll
-    for (int m = 0; m < MM; ++m)
+    for (int t0 = 0; t0 < NT; t0 += RC) {
+        __syncthreads();
 #pragma unroll
-        for (int t = 0; t <= KK; ++t) {
-            float v = acc[m][t];
-            for (int off = a.TPC >> 1; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-            acc[m][t] = v;
+        for (int tt = 0; tt < RC; ++tt) {
+            const int t = t0 + tt;
+            if (t < NT) red[tid * RC + tt] = acc[t / (KK + 1)][t % (KK + 1)];
         }
-    if (sub == 0 && lch < Gc) {
-        float *dst = a.ws + (static_cast<int64_t>(c0 + lch) * a.NC + chunk) * (MM * (KK + 1));
-#pragma unroll
-        for (int m = 0; m < MM; ++m)
-#pragma unroll
-            for (int t = 0; t <= KK; ++t) dst[m * (KK + 1) + t] = acc[m][t];
+        __syncthreads();
+        for (int idx = tid; idx < Gc * RC; idx += kThreads) {
+            const int c = idx / RC, tt = idx - c * RC;
+            if (t0 + tt >= NT) continue;
+            float s = 0.f;
+            for (int rr = 0; rr < g.oh; ++rr) s += red[(c * g.oh + rr) * RC + tt];
+            a.ws[(static_cast<int64_t>(c0 + c) * a.NC + chunk) * NT + t0 + tt] = s;
+        }
     }
 }
 
 struct SwPlan {
-    int G, TPC, NC, npc, grid, xslots, dslots, lds_bytes;
+    int G, NC, npc, grid, gpre, dofs, lds_bytes, vec, owm;
 };
 
 bool combo_ok(const Geo &g) {
@@ -197,45 +195,56 @@ bool combo_ok(const Geo &g) {
            ((g.kh == 3 && g.dh == 1 && g.sh <= 2) || (g.kh == 5 && ((g.sh == 1 && g.dh == 1) || (g.sh == 2 && g.dh == 2))));
 }
 
+int row_span(const Geo &g, int owm) { return (owm - 1) * g.sw + (g.kw - 1) * g.dw + 1; }
+
 template <typename T>
 bool plan_sp_bwdw(const Geo &g, SwPlan &p) {
     if (!combo_ok(g)) return false;
+    const int sz = sizeof(T), VE = 16 / sz;
     const int64_t iplane = static_cast<int64_t>(g.ih) * g.iw, oplane = static_cast<int64_t>(g.oh) * g.ow;
     // used for planes of at most 64 output pixels (7x7, and 14x14 at stride 2):
     // larger planes measured faster with the streaming row walk
-    if (oplane > 64) return false;
-    int tpc = 4;
-    while (tpc < 64 && tpc * 4 < oplane) tpc <<= 1;
-    int G = std::min(kThreads / tpc, g.ic);
-    auto bytes = [&](int Gx, int &xs, int &dsl) {
-        xs = lds_slots<T>(static_cast<int>(Gx * iplane));
-        dsl = lds_slots<T>(static_cast<int>(Gx * g.mult * oplane));
-        return static_cast<int64_t>(kNI) * (xs + dsl) * static_cast<int64_t>(sizeof(T));
-    };
-    int xs, dsl;
-    while (G > 1 && bytes(G, xs, dsl) > kSmallLds) --G;
-    if (bytes(G, xs, dsl) > kSmallLds) return false;
-    int t = 1;
-    while (t * 2 <= std::min(64, kThreads / G)) t *= 2;
-    tpc = t;
+    if (oplane > 64 || g.ow > 16 || g.oh > kThreads) return false;
+    p.owm = g.ow <= 4 ? 4 : (g.ow <= 8 ? 8 : 16);
+    const int64_t per_ch = (iplane + g.mult * oplane) * sz;
+    int G = std::min<int64_t>(kThreads / g.oh, g.ic);
+    while (G > 1 && G * per_ch > kStageCap) --G;
+    if (G * per_ch > kStageCap) return false;
+    // whole 16-byte vectors: every image's range of every channel group starts
+    // and ends on a vector boundary (base pointers are checked at launch)
+    bool vec = (g.ic * iplane) % VE == 0 && (static_cast<int64_t>(g.oc) * oplane) % VE == 0;
+    if (vec) {
+        int Gv = G;
+        while (Gv > 0 && ((Gv * iplane) % VE != 0 || (Gv * g.mult * oplane) % VE != 0)) --Gv;
+        if (Gv > 0) G = Gv; else vec = false;
+    }
     const int ngroups = (g.ic + G - 1) / G;
-    // image chunks: >= 2048 workgroups, each staging at least one full batch of kNI images
-    int NC = std::max(1, (2048 + ngroups - 1) / ngroups);
-    NC = std::min(NC, std::max(1, g.n / kNI));
+    // about 1536 workgroups (six per CU) with at least two images each when
+    // the batch allows, so loads of the next image overlap the current one
+    int NC = std::max(1, (1536 + ngroups - 1) / ngroups);
+    NC = std::min(NC, std::max(1, g.n / 2));
     const int npc = (g.n + NC - 1) / NC;
     NC = (g.n + npc - 1) / npc;
+    const int iwm = row_span(g, p.owm);
     p.G = G;
-    p.TPC = tpc;
     p.NC = NC;
     p.npc = npc;
     p.grid = ngroups * NC;
-    p.xslots = xs;
-    p.dslots = dsl;
-    p.lds_bytes = static_cast<int>(bytes(G, xs, dsl));
+    p.vec = vec;
+    // LDS: [left guard][x planes][pad][dy planes][right guard]; the guards and
+    // the pad keep every row-window read inside the allocation
+    p.gpre = (g.pw + VE - 1) / VE * VE;
+    const int xl = static_cast<int>(G * iplane), dl = static_cast<int>(G * g.mult * oplane);
+    p.dofs = p.gpre + (xl + VE - 1) / VE * VE;
+    const int post = std::max(iwm, p.owm) + VE;
+    const int stage = (p.dofs + dl + post) * sz;
+    const int NT = g.mult * (g.kh * g.kw + 1);
+    const int red = kThreads * std::min(NT, kRedCh) * 4;
+    p.lds_bytes = (std::max(stage, red) + 15) / 16 * 16;
     return true;
 }
 
-template <typename T, int KH, int KW, int S, int D, int MM>
+template <typename T, int K, int S, int D, int MM, int OWM>
 int run_sp_bwdw(const Geo &g, const SwPlan &p, const void *x, const void *dy, void *ws, hipStream_t s) {
     SwArgs<T> a{};
     a.x = static_cast<const T *>(x);
@@ -245,19 +254,23 @@ int run_sp_bwdw(const Geo &g, const SwPlan &p, const void *x, const void *dy, vo
     a.G = p.G;
     a.NC = p.NC;
     a.npc = p.npc;
-    a.TPC = p.TPC;
-    a.fPW = make_fastdiv(g.ow, static_cast<uint64_t>(g.oh) * g.ow + 64);
-    a.xslots = p.xslots;
-    a.dslots = p.dslots;
-    a.vec = reinterpret_cast<uintptr_t>(x) % 16 == 0 && reinterpret_cast<uintptr_t>(dy) % 16 == 0;
-    hipLaunchKernelGGL((sp_bwdw_kernel<T, KH, KW, S, D, MM>), dim3(p.grid), dim3(kThreads), p.lds_bytes, s, a);
+    a.gpre = p.gpre;
+    a.dofs = p.dofs;
+    a.vec = p.vec && reinterpret_cast<uintptr_t>(x) % 16 == 0 && reinterpret_cast<uintptr_t>(dy) % 16 == 0;
+    hipLaunchKernelGGL((sp_bwdw_kernel<T, K, S, D, MM, OWM>), dim3(p.grid), dim3(kThreads), p.lds_bytes, s, a);
     return hipGetLastError() == hipSuccess ? kOk : kErrHip;
 }
 
-template <typename T, int KH, int S, int D>
+template <typename T, int K, int S, int D, int MM>
+int run_w(const Geo &g, const SwPlan &p, const void *x, const void *dy, void *ws, hipStream_t s) {
+    if (p.owm == 4) return run_sp_bwdw<T, K, S, D, MM, 4>(g, p, x, dy, ws, s);
+    if (p.owm == 8) return run_sp_bwdw<T, K, S, D, MM, 8>(g, p, x, dy, ws, s);
+    return run_sp_bwdw<T, K, S, D, MM, 16>(g, p, x, dy, ws, s);
+}
+
+template <typename T, int K, int S, int D>
 int run_m(const Geo &g, const SwPlan &p, const void *x, const void *dy, void *ws, hipStream_t s) {
-    return g.mult == 2 ? run_sp_bwdw<T, KH, KH, S, D, 2>(g, p, x, dy, ws, s)
-                       : run_sp_bwdw<T, KH, KH, S, D, 1>(g, p, x, dy, ws, s);
+    return g.mult == 2 ? run_w<T, K, S, D, 2>(g, p, x, dy, ws, s) : run_w<T, K, S, D, 1>(g, p, x, dy, ws, s);
 }
 
 template <typename T>

@@ -428,3 +428,22 @@ def test_large_kernel_shapes(n, c, h, w, mult, k, p, dt):
 def test_even_grid_shapes(n, c, h, w, mult, k, dt):
     x, wt, b, dy = static_case(n, c, h, w, mult, k, 2, k - 1, 2, DT[dt], 670 + h + w + k)
     check_static(x, wt, b, dy, 2, k - 1, 2, "evengrid n%d c%d %dx%d m%d k%d %s" % (n, c, h, w, mult, k, dt))
+
+
+# ------------------------------------------------------------------ small planes (grad-weight by channel groups)
+@pytest.mark.parametrize("n,c,h,w,mult,k,s,p,d,dt", [
+    (6, 40, 7, 7, 1, 3, 1, 1, 1, "f32"),      # two channel groups, the second partial; two images per chunk
+    (9, 1024, 7, 7, 1, 3, 1, 1, 1, "f32"),    # 7x7 MobileNet plane, three images per chunk
+    (4, 512, 14, 14, 1, 3, 2, 1, 1, "f32"),   # 14x14 -> 7x7
+    (5, 72, 14, 14, 1, 3, 2, 1, 1, "bf16"),   # group size cut to whole 16-byte vectors of both ranges
+    (4, 24, 7, 7, 2, 3, 2, 1, 1, "f16"),      # 7x7 -> 4x4 with multiplier 2
+    (3, 20, 7, 9, 1, 5, 1, 2, 1, "f32"),      # 5x5, rows of 9 outputs
+    (4, 10, 11, 11, 1, 5, 2, 4, 2, "f32"),    # 5x5 stride 2 dilation 2; ranges not whole vectors
+    (3, 9, 4, 16, 1, 3, 1, 1, 1, "bf16"),     # rows of 16 outputs
+    (2, 7, 5, 5, 1, 3, 1, 1, 1, "f32"),       # element staging
+])
+def test_small_plane_shapes(n, c, h, w, mult, k, s, p, d, dt):
+    assert dc.dwconv2d_algo(2, (n, c, h, w), (c * mult, k, k), s, p, d, dtype=DT[dt]) == "channelgroup_small"
+    x, wt, b, dy = static_case(n, c, h, w, mult, k, s, p, d, DT[dt], 900 + c + h * 3 + k)
+    check_static(x, wt, b, dy, s, p, d, "smallplane n%d c%d %dx%d m%d k%d s%d %s" % (n, c, h, w, mult, k, s, dt),
+                 passes=("bwd_w",))
