@@ -288,7 +288,9 @@ __global__ __launch_bounds__(kThreads) void bwd_weight_taps_kernel(BwArgs<T> a) 
 // Pass 2: dw[o, t] (t < kk) and db[o] (t == kk) from the chunk partials.
 // 2^lrl adjacent lanes share one output slot: lane l adds chunks l, l + 2^lrl,
 // ... in order and the lanes are then combined by a fixed xor tree, so the
-// result does not depend on scheduling.
+// result does not depend on scheduling.  Each lane issues its (up to four per
+// round) loads before adding any of them: the partials were just written by
+// pass 1 and every load is a full memory round trip.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void bwd_weight_reduce_kernel(const float *__restrict__ ws, T *dwt,
                                                                      T *db, int oc, int mult, int kk,
@@ -304,7 +306,14 @@ __global__ __launch_bounds__(kThreads) void bwd_weight_reduce_kernel(const float
         t = idx - o * (kk + 1);
         const int ic = o / mult, m = o - ic * mult;
         const float *p = ws + static_cast<int64_t>(ic) * NC * nslots + m * (kk + 1) + t;
-        for (int c = lane; c < NC; c += RL) s += p[static_cast<int64_t>(c) * nslots];
+        for (int c0 = lane; c0 < NC; c0 += 4 * RL) {
+            float v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)  // clamped index: always a valid address, no branch around the load
+                v[u] = p[static_cast<int64_t>(min(c0 + u * RL, NC - 1)) * nslots];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) s += c0 + u * RL < NC ? v[u] : 0.f;
+        }
     }
     for (int off = RL >> 1; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
     if (!valid || lane != 0) return;

@@ -3,8 +3,8 @@
 //   dw[o,i,j] = sum_{n,p,q} dy[n,o,p,q] * x[n,o/M, p*s-pad+i*d, q*s-pad+j*d],  db[o] = sum dy
 // (PyTorch PR #3057: grad-weight and grad-bias of the depthwise convolution.)
 //
-// For small planes (7x7, or 14x14 at stride 2) one channel's data is a
-// 200-800 byte piece per image, scattered with the stride of a whole image,
+// For small planes (up to 14x14 outputs) one channel's data is a
+// 200-4000 byte piece per image, scattered with the stride of a whole image,
 // and a per-channel walk reads short rows from many places.  Here a workgroup
 // owns G adjacent channels instead: for a fixed image their x planes are one
 // contiguous range and their dy planes another, and the workgroup walks a
@@ -25,7 +25,7 @@
 namespace dw {
 namespace {
 
-constexpr int kStageCap = 32 * 1024;  // staged bytes per image and workgroup
+constexpr int kStageCap = 16 * 1024;  // staged bytes per image and workgroup
 constexpr int kPV = kStageCap / (16 * kThreads);  // 16-byte vectors per lane and image
 constexpr int kRedCh = 16;            // accumulators per lane per reduction step
 
@@ -202,9 +202,10 @@ bool plan_sp_bwdw(const Geo &g, SwPlan &p) {
     if (!combo_ok(g)) return false;
     const int sz = sizeof(T), VE = 16 / sz;
     const int64_t iplane = static_cast<int64_t>(g.ih) * g.iw, oplane = static_cast<int64_t>(g.oh) * g.ow;
-    // used for planes of at most 64 output pixels (7x7, and 14x14 at stride 2):
-    // larger planes measured faster with the streaming row walk
-    if (oplane > 64 || g.ow > 16 || g.oh > kThreads) return false;
+    // used for planes of at most 256 output pixels and rows of at most 16
+    // (7x7, 14x14, 28x28 at stride 2): larger planes measured faster with the
+    // streaming row walk
+    if (oplane > 256 || g.ow > 16 || g.oh > kThreads) return false;
     p.owm = g.ow <= 4 ? 4 : (g.ow <= 8 ? 8 : 16);
     const int64_t per_ch = (iplane + g.mult * oplane) * sz;
     int G = std::min<int64_t>(kThreads / g.oh, g.ic);
@@ -219,10 +220,10 @@ bool plan_sp_bwdw(const Geo &g, SwPlan &p) {
         if (Gv > 0) G = Gv; else vec = false;
     }
     const int ngroups = (g.ic + G - 1) / G;
-    // about 1536 workgroups (six per CU) with at least two images each when
+    // about 1536 workgroups (six per CU) with at least four images each when
     // the batch allows, so loads of the next image overlap the current one
     int NC = std::max(1, (1536 + ngroups - 1) / ngroups);
-    NC = std::min(NC, std::max(1, g.n / 2));
+    NC = std::min(NC, std::max(1, g.n / 4));
     const int npc = (g.n + NC - 1) / NC;
     NC = (g.n + npc - 1) / npc;
     const int iwm = row_span(g, p.owm);

@@ -339,7 +339,7 @@ def test_full_size_dynamic_sampled(dtype):
     (2, 2, 15, 57, 1, 1, "f32"), (2, 2, 15, 57, 2, 2, "f32"),   # 228-byte rows: 4-byte vectors
     (2, 3, 14, 58, 1, 1, "bf16"), (2, 3, 14, 60, 2, 1, "f16"),  # 116 / 120-byte rows
     (2, 2, 13, 57, 1, 1, "bf16"), (2, 2, 13, 57, 1, 2, "f16"),  # odd 16-bit rows: 2-byte vectors
-    (3, 4, 14, 14, 1, 1, "f32"), (3, 4, 28, 28, 1, 2, "f32"),   # narrow planes (grad-weight, grad-input s2)
+    (3, 4, 14, 14, 1, 1, "f32"), (3, 4, 28, 28, 1, 2, "f32"),   # narrow planes (grad-input s2)
     (3, 4, 14, 14, 2, 2, "bf16"), (2, 3, 7, 7, 1, 1, "f32"),
 ])
 def test_streaming_3x3_shapes(n, c, h, w, mult, s, dt):
@@ -441,6 +441,9 @@ def test_even_grid_shapes(n, c, h, w, mult, k, dt):
     (4, 10, 11, 11, 1, 5, 2, 4, 2, "f32"),    # 5x5 stride 2 dilation 2; ranges not whole vectors
     (3, 9, 4, 16, 1, 3, 1, 1, 1, "bf16"),     # rows of 16 outputs
     (2, 7, 5, 5, 1, 3, 1, 1, 1, "f32"),       # element staging
+    (5, 20, 14, 14, 1, 3, 1, 1, 1, "f32"),    # 14x14 outputs: rows of 14 in 16-wide windows
+    (4, 12, 28, 28, 1, 3, 2, 1, 1, "bf16"),   # 28x28 -> 14x14
+    (3, 8, 16, 16, 2, 5, 1, 2, 1, "f16"),     # 256 outputs per plane, multiplier 2, 5x5
 ])
 def test_small_plane_shapes(n, c, h, w, mult, k, s, p, d, dt):
     assert dc.dwconv2d_algo(2, (n, c, h, w), (c * mult, k, k), s, p, d, dtype=DT[dt]) == "channelgroup_small"
