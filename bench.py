@@ -24,13 +24,19 @@ value      whole-step algorithmic throughput: compulsory bytes (each input eleme
            the result depends on once, each output once) per second for the
            bandwidth-bound workloads; valid-tap flops (2 per in-bounds multiply-add)
            per second for largek
-launches   the calls of one kernel geometry (a "tag") are captured once into a HIP
-           graph; a step replays the tags' graphs in pass order (--eager launches
-           call by call instead)
-roofline   the dominant kernel (most time in the step): its algorithmic bytes or
-           flops over its average launch duration, measured with HIP events recorded
-           on the launch stream around each tag's replay during the timed steps,
-           against the MI355X peak
+launches   the whole step is captured once into a HIP graph and the timed steps
+           replay it (--eager launches call by call instead).  A workload whose
+           step moves less than 2 GiB gets identical copies of all its tensors
+           (one graph per copy) and step i uses copy i % copies, so no launch
+           finds its inputs still in the 256 MB last-level cache
+per_kernel per kernel geometry (a "tag"): HIP events on the launch stream around
+           a replay of a graph holding that tag's calls of one step, tags in step
+           order, as many rounds as timed steps (each figure includes one
+           graph-launch gap)
+roofline   the dominant tag (most event time): its algorithmic bytes or flops per
+           launch over its average launch duration, measured with HIP events on
+           the launch stream around a graph of back-to-back rounds of its calls
+           (at least 1 GiB of traffic per replay), against the MI355X peak
 cpu_baseline  the fp64 CPU oracle on a bounded sample of the same workload
            (a batch slice of the same host tensors), on this host's cores
 """
@@ -363,70 +369,80 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     wl = build_workload(args.workload, dc, dev)
-    calls = wl["calls"]
+    # rotating copies: a step whose traffic is under 2 GiB would find part of its
+    # inputs still in the 256 MB last-level cache when it runs again, so such
+    # workloads get identical copies of every tensor and step i uses copy i % ncopy
+    ncopy = int(min(8, max(1, math.ceil((2 << 30) / max(1, sum(cl.nbytes for cl in wl["calls"]))))))
+    copies = [wl] + [build_workload(args.workload, dc, dev) for _ in range(ncopy - 1)]
+    calls_by_copy = [w_["calls"] for w_ in copies]
     if args.only_tag:
-        calls = [cl for cl in calls if cl.tag == args.only_tag]
-        if not calls:
+        calls_by_copy = [[cl for cl in cc if cl.tag == args.only_tag] for cc in calls_by_copy]
+        if not calls_by_copy[0]:
             raise SystemExit("no call has tag %r; tags: %s" % (args.only_tag, sorted({c.tag for c in wl["calls"]})))
+    calls = calls_by_copy[0]
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
 
-    # one group of consecutive calls per tag (= one kernel geometry)
-    groups = []
-    for cl in calls:
-        if groups and groups[-1][0] == cl.tag:
-            groups[-1][1].append(cl)
-        else:
-            groups.append((cl.tag, [cl]))
-    for _ in range(max(1, args.warmup)):
-        for cl in calls:
+    # one group of consecutive calls per tag (= one kernel geometry); every copy
+    # has the same calls in the same order
+    def tag_groups(cc):
+        gs = []
+        for cl in cc:
+            if gs and gs[-1][0] == cl.tag:
+                gs[-1][1].append(cl)
+            else:
+                gs.append((cl.tag, [cl]))
+        return gs
+
+    groups_by_copy = [tag_groups(cc) for cc in calls_by_copy]
+    groups = groups_by_copy[0]
+    for cc in calls_by_copy:
+        for cl in cc:
             cl.fn()
     torch.cuda.synchronize()
-    if args.eager:
-        runners = [(tag, (lambda cls=cls: [c.fn() for c in cls])) for tag, cls in groups]
-    else:
-        # each group captured once into a HIP graph and replayed: the step's
-        # launches cost no host time, as a fixed training step would run
-        runners = []
-        for tag, cls in groups:
-            gr = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(gr):
-                for c in cls:
-                    c.fn()
-            runners.append((tag, gr.replay))
-        torch.cuda.synchronize()
-        for _ in range(args.warmup):
-            for _tag, run in runners:
-                run()
-        torch.cuda.synchronize()
 
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in runners]
-          for _ in range(args.steps)]
+    def runner(fns):
+        """A callable launching fns in order: replay of one HIP graph holding them (--eager: direct calls)."""
+        if args.eager:
+            return lambda: [f() for f in fns]
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for f in fns:
+                f()
+        graphs.append(gr)
+        return gr.replay
+
+    def event_pair():
+        return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    # the whole step is captured once into one HIP graph, so the step's launches
+    # cost no host time and no gap between graph launches, as a fixed training
+    # step would run
+    graphs = []
+    step_runs = [runner([cl.fn for cl in cc]) for cc in calls_by_copy]
     torch.cuda.synchronize()
+    for w_ in range(args.warmup):
+        step_runs[w_ % ncopy]()
+    torch.cuda.synchronize()
+
     t0 = time.perf_counter()
     for st in range(args.steps):
-        for gi, (_tag, run) in enumerate(runners):
+        step_runs[st % ncopy]()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    # per-tag event times: each tag's calls replayed from a graph of their own,
+    # tags in step order, HIP events recorded on the launch stream around each
+    # replay (each figure includes one graph-launch gap)
+    tag_runs = [[runner([c.fn for c in cls]) for _tag, cls in gs] for gs in groups_by_copy]
+    torch.cuda.synchronize()
+    ev = [[event_pair() for _ in groups] for _ in range(args.steps)]
+    for st in range(args.steps):
+        for gi, run in enumerate(tag_runs[st % ncopy]):
             ev[st][gi][0].record(stream)
             run()
             ev[st][gi][1].record(stream)
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-
-    executed = len(calls) * (max(1, args.warmup) + (0 if args.eager else args.warmup) + args.steps)
-    if args.copy_ref:
-        src = torch.empty(COPY_REF_BYTES // 4, dtype=torch.float32, device=dev).normal_()
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-
-    step_bytes = sum(cl.nbytes for cl in calls)
-    step_flops = sum(cl.flops for cl in calls)
-    ms_step = elapsed / args.steps * 1e3
-    # per-tag event time (a tag = one entry point at one kernel geometry = one kernel symbol,
-    # except grad-weight whose call also runs the small fixed-order reduction kernel);
-    # events bracket each tag's graph replay on the launch stream
     per_tag = {}
     for st in range(args.steps):
         for gi, (tag, cls) in enumerate(groups):
@@ -437,36 +453,69 @@ def main():
             r["bytes"] += sum(c.nbytes for c in cls)
             r["flops"] += sum(c.flops for c in cls)
     dom_tag = max(per_tag, key=lambda t: per_tag[t]["ms"])
-    dom = per_tag[dom_tag]
-    avg_s = dom["ms"] / dom["launches"] / 1e3
+
+    # the dominant tag's launch duration: HIP events around one graph of REP
+    # back-to-back rounds of its calls (at least 1 GiB of traffic per replay,
+    # so every round reads its inputs from HBM again), three replays
+    dom_calls = [cl for cl in calls if cl.tag == dom_tag]
+    dom_bytes = sum(cl.nbytes for cl in dom_calls)
+    rep = int(min(64, max(4, math.ceil((1 << 30) / max(dom_bytes, 1)))))
+    dom_run = runner([cl.fn for r in range(rep) for cl in calls_by_copy[r % ncopy] if cl.tag == dom_tag])
+    dom_run()
+    torch.cuda.synchronize()
+    e0, e1 = event_pair()
+    e0.record(stream)
+    for _ in range(3):
+        dom_run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    dom_launches = 3 * rep * len(dom_calls)
+    avg_s = e0.elapsed_time(e1) / 1e3 / dom_launches
+    executed = len(calls) * (ncopy + args.warmup + 2 * args.steps) + len(dom_calls) * rep * 4
+    if args.copy_ref:
+        src = torch.empty(COPY_REF_BYTES // 4, dtype=torch.float32, device=dev).normal_()
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    del graphs
+
+    step_bytes = sum(cl.nbytes for cl in calls)
+    step_flops = sum(cl.flops for cl in calls)
+    ms_step = elapsed / args.steps * 1e3
+    dom_nbytes = dom_bytes / len(dom_calls)
+    dom_nflops = sum(cl.flops for cl in dom_calls) / len(dom_calls)
     if wl["kind"] == "bytes":
         value = step_bytes / (elapsed / args.steps) / 1e9
         unit = "GB/s"
-        achieved = dom["bytes"] / dom["launches"] / avg_s / 1e9
+        achieved = dom_nbytes / avg_s / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4)}
     else:
         value = step_flops / (elapsed / args.steps) / 1e9
         unit = "GFLOP/s"
-        achieved = dom["flops"] / dom["launches"] / avg_s / 1e12
+        achieved = dom_nflops / avg_s / 1e12
         roof = {"bound": "alu", "achieved": round(achieved, 2), "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / FP32_VALU_PEAK_TFLOPS, 4)}
     roof["traffic"] = committed_traffic(dom_tag)
     roof["kernel"] = dom_tag
     roof["avg_launch_us"] = round(avg_s * 1e6, 2)
+    roof["timed_launches"] = dom_launches
 
     out = {
         "metric": "dwconv fwd+bwd GFLOP/s and HBM GB/s at 1 GPU, % of roofline, vs CPU oracle",
         "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": wl["dtype"], "data": "synthetic (seeded, shapes and distributions of the workload)",
-        "config": dict({"workload": wl["desc"], "launch": "eager" if args.eager else "hip_graph_per_kernel"},
+        "config": dict({"workload": wl["desc"], "launch": "eager" if args.eager else "hip_graph_per_step"},
                        **wl["cfg"]),
         "step_gbytes": round(step_bytes / 1e9, 4), "step_gflop": round(step_flops / 1e9, 4),
         "gbs": round(step_bytes / (elapsed / args.steps) / 1e9, 2),
         "gflops": round(step_flops / (elapsed / args.steps) / 1e9, 2),
         "roofline": roof,
         "launches_executed": executed,
+        "tensor_copies": ncopy,
         "per_kernel": {t: {"avg_us": round(r["ms"] / r["launches"] * 1e3, 2),
                                        "share": round(r["ms"] / sum(v["ms"] for v in per_tag.values()), 4),
                                        "gbs": round(r["bytes"] / (r["ms"] / 1e3) / 1e9, 1),
