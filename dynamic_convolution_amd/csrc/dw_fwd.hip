@@ -238,7 +238,7 @@ int run_fwd(const Geo &g, const BandPlan &bp, const void *x, const void *w, cons
     return hipGetLastError() == hipSuccess ? kOk : kErrHip;
 }
 
-enum FwdAlgo { kFwdRowwalk = 0, kFwdLargek, kFwdDecim, kFwdBand33s1, kFwdBand33s2, kFwdBand55s1, kFwdBand55s2d2, kFwdBandGeneric };
+enum FwdAlgo { kFwdRowwalk = 0, kFwdLargek, kFwdDecim, kFwdBand33s1, kFwdBand33s2, kFwdBand55s1, kFwdBand55s2d2, kFwdBandGeneric, kFwdChannelGroup };
 
 // The kernel family a forward call launches (the dispatcher and the
 // introspection helper both use this one decision).
@@ -246,6 +246,7 @@ int select_fwd(const Geo &g, int dt) {
     if (rowwalk_fits(g, dt, 0)) return kFwdRowwalk;
     if (largek_fits(g, 0)) return kFwdLargek;
     if (decim_fits(g, 0)) return kFwdDecim;
+    if (small_fwd_fits(g, dt)) return kFwdChannelGroup;
     const bool sq = g.kh == g.kw && g.sh == g.sw && g.dh == g.dw;
     if (sq && g.kh == 3 && g.sh == 1 && g.dh == 1) return kFwdBand33s1;
     if (sq && g.kh == 3 && g.sh == 2 && g.dh == 1) return kFwdBand33s2;
@@ -261,6 +262,7 @@ int dispatch_fwd(const Geo &g, const void *x, const void *w, const void *b, void
     if (algo == kFwdRowwalk) return rowwalk_fwd(g, x, w, b, y, dt, s);
     if (algo == kFwdLargek) return largek_fwd(g, x, w, b, y, dt, s);
     if (algo == kFwdDecim) return decim_fwd(g, x, w, b, y, dt, s);
+    if (algo == kFwdChannelGroup) return small_fwd(g, x, w, b, y, dt, s);
     BandPlan bp;
     if (!plan_fwd<T>(g, bp)) return kErrUnsupported;
     switch (algo) {
@@ -276,12 +278,12 @@ int dispatch_fwd(const Geo &g, const void *x, const void *w, const void *b, void
 
 const char *fwd_algo_name(const Geo &g, int dtype) {
     static const char *names[] = {"rowwalk_3x3",    "largek_regtile", "decimated_s2d2", "band_3x3_s1",   "band_3x3_s2",
-                                  "band_5x5_s1",    "band_5x5_s2_d2", "band_generic"};
+                                  "band_5x5_s1",    "band_5x5_s2_d2", "band_generic", "channelgroup_small"};
     return names[select_fwd(g, dtype)];
 }
 
 bool fwd_supported(const Geo &g, int dtype) {
-    if (rowwalk_fits(g, dtype, 0) || largek_fits(g, 0) || decim_fits(g, 0)) return true;
+    if (rowwalk_fits(g, dtype, 0) || largek_fits(g, 0) || decim_fits(g, 0) || small_fwd_fits(g, dtype)) return true;
     BandPlan bp;
     switch (dtype) {
         case 0: return plan_fwd<float>(g, bp);

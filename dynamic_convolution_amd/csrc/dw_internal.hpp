@@ -47,11 +47,16 @@ int rowwalk_bwd_input(const Geo &g, const void *dy, const void *w, void *dx, int
 int rowwalk_bwd_weight_chunks(const Geo &g, int dtype);
 int rowwalk_bwd_weight(const Geo &g, const void *x, const void *dy, void *ws, int dtype, hipStream_t s);
 
-// Grad-weight for small planes over groups of adjacent channels (dw_small.hip);
-// small_fits is true only for pass 2 (grad-weight) geometries it handles.
+// Small planes over groups of adjacent channels, one lane per (channel, row):
+// grad-weight (dw_small.hip; small_fits is true only for pass 2 geometries it
+// handles), forward (dw_small_fwd.hip) and grad-input (dw_small_bwdin.hip).
 bool small_fits(const Geo &g, int dtype, int pass);
 int small_bwd_weight_chunks(const Geo &g, int dtype);
 int small_bwd_weight(const Geo &g, const void *x, const void *dy, void *ws, int dtype, hipStream_t s);
+bool small_fwd_fits(const Geo &g, int dtype);
+int small_fwd(const Geo &g, const void *x, const void *w, const void *b, void *y, int dtype, hipStream_t s);
+bool small_bwd_input_fits(const Geo &g, int dtype);
+int small_bwd_input(const Geo &g, const void *dy, const void *w, void *dx, int dtype, hipStream_t s);
 
 // Large-kernel (k = 7, 13, 31; stride 1, dilation 1) register-tile kernels
 // (dw_largek.hip).  pass: 0 forward, 1 grad-input.

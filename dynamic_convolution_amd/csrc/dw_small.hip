@@ -3,14 +3,11 @@
 //   dw[o,i,j] = sum_{n,p,q} dy[n,o,p,q] * x[n,o/M, p*s-pad+i*d, q*s-pad+j*d],  db[o] = sum dy
 // (PyTorch PR #3057: grad-weight and grad-bias of the depthwise convolution.)
 //
-// For small planes (up to 14x14 outputs) one channel's data is a
-// 200-4000 byte piece per image, scattered with the stride of a whole image,
-// and a per-channel walk reads short rows from many places.  Here a workgroup
-// owns G adjacent channels instead: for a fixed image their x planes are one
-// contiguous range and their dy planes another, and the workgroup walks a
-// chunk of images, staging one image's two ranges in LDS at a time.  When the
-// ranges are whole 16-byte vectors the next image's vectors are loaded into
-// registers while the current image is computed.
+// For small planes (up to 16x16 outputs) one channel's data is a few hundred
+// bytes to 4 KB per image, scattered with the stride of a whole image, and a
+// per-channel walk reads short rows from many places.  Here a workgroup owns G
+// adjacent channels and walks a chunk of images, staging one image's x range
+// and dy range in LDS at a time (dw_small.hpp).
 //
 // Each lane owns one (channel, output row) for the whole chunk: per image it
 // reads its dy row and the kh input rows under it from LDS and accumulates the
@@ -19,15 +16,12 @@
 // in a fixed order through LDS and one lane per (channel, slot) writes the
 // (channel, image chunk) partial to the workspace [ic][chunk][M*(kh*kw+1)]
 // that pass 2 adds up.
-#include "dw_common.hpp"
-#include "dw_internal.hpp"
+#include "dw_small.hpp"
 
 namespace dw {
 namespace {
 
-constexpr int kStageCap = 16 * 1024;  // staged bytes per image and workgroup
-constexpr int kPV = kStageCap / (16 * kThreads);  // 16-byte vectors per lane and image
-constexpr int kRedCh = 16;            // accumulators per lane per reduction step
+constexpr int kRedCh = 16;  // accumulators per lane per reduction step
 
 template <typename T> struct SwArgs {
     const T *x;
@@ -83,48 +77,20 @@ __global__ __launch_bounds__(kThreads) void sp_bwdw_kernel(SwArgs<T> a) {
     auto xbase = [&](int n) { return (static_cast<int64_t>(n) * g.ic + c0) * iplane; };
     auto dbase = [&](int n) { return (static_cast<int64_t>(n) * g.oc + static_cast<int64_t>(c0) * MM) * oplane; };
 
-    // register-staged 16-byte vectors of one image: lane vector k is flat
-    // vector tid + k*kThreads of [x range | dy range]; lanes past the end load
-    // the first x vector again (a valid address) and store nothing
-    typedef unsigned int v4u __attribute__((ext_vector_type(4)));
-    v4u pf[kPV];
-    auto issue = [&](int n) {
-        const T *xb = a.x + xbase(n), *db = a.dy + dbase(n);
-#pragma unroll
-        for (int k = 0; k < kPV; ++k) {
-            const int f = tid + k * kThreads;
-            const T *p = f < nvx ? xb + f * VE : (f < nv ? db + (f - nvx) * VE : xb);
-            pf[k] = *reinterpret_cast<const v4u *>(p);
-        }
-    };
-    auto commit = [&]() {
-#pragma unroll
-        for (int k = 0; k < kPV; ++k) {
-            const int f = tid + k * kThreads;
-            if (f < nv) {
-                T *q = f < nvx ? xs + f * VE : ds + (f - nvx) * VE;
-                *reinterpret_cast<v4u *>(q) = pf[k];
-            }
-        }
-    };
+    cg_v4u pf[kCgPV];
+    auto issue = [&](int n) { cg_issue(pf, a.x + xbase(n), nvx, a.dy + dbase(n), nv, tid); };
 
-    // uniform column masks: position p of a row window reads column p - pw
-    uint64_t colok = 0;
-#pragma unroll
-    for (int p = 0; p < IWM; ++p) {
-        const int c = p - g.pw;
-        if (c >= 0 && c < g.iw) colok |= 1ull << p;
-    }
+    // uniform column mask: position p of a row window reads column p - pw
+    const uint64_t colok = cg_colmask<IWM>(-g.pw, g.iw);
 
     if (a.vec && n_beg < n_end) issue(n_beg);
     for (int n = n_beg; n < n_end; ++n) {
         __syncthreads();  // the previous image's LDS reads are done
         if (a.vec) {
-            commit();
+            cg_commit(pf, xs, nvx, ds, nv, tid);
         } else {
-            const int64_t xb = xbase(n), db = dbase(n);
-            for (int e = tid; e < xlen; e += kThreads) xs[e] = a.x[xb + e];
-            for (int e = tid; e < dlen; e += kThreads) ds[e] = a.dy[db + e];
+            cg_copy_elems(xs, a.x + xbase(n), xlen, tid);
+            cg_copy_elems(ds, a.dy + dbase(n), dlen, tid);
         }
         __syncthreads();
         if (a.vec && n + 1 < n_end) issue(n + 1);
@@ -186,56 +152,28 @@ __global__ __launch_bounds__(kThreads) void sp_bwdw_kernel(SwArgs<T> a) {
 }
 
 struct SwPlan {
-    int G, NC, npc, grid, gpre, dofs, lds_bytes, vec, owm;
+    CgPlan c;
+    int gpre, dofs, lds_bytes, owm;
 };
-
-bool combo_ok(const Geo &g) {
-    const bool sq = g.kh == g.kw && g.sh == g.sw && g.dh == g.dw;
-    return g.mult <= 2 && sq &&
-           ((g.kh == 3 && g.dh == 1 && g.sh <= 2) || (g.kh == 5 && ((g.sh == 1 && g.dh == 1) || (g.sh == 2 && g.dh == 2))));
-}
 
 int row_span(const Geo &g, int owm) { return (owm - 1) * g.sw + (g.kw - 1) * g.dw + 1; }
 
 template <typename T>
 bool plan_sp_bwdw(const Geo &g, SwPlan &p) {
-    if (!combo_ok(g)) return false;
+    if (!cg_combo_ok(g)) return false;
     const int sz = sizeof(T), VE = 16 / sz;
     const int64_t iplane = static_cast<int64_t>(g.ih) * g.iw, oplane = static_cast<int64_t>(g.oh) * g.ow;
     // used for planes of at most 256 output pixels and rows of at most 16
     // (7x7, 14x14, 28x28 at stride 2): larger planes measured faster with the
     // streaming row walk
-    if (oplane > 256 || g.ow > 16 || g.oh > kThreads) return false;
+    if (oplane > 256 || g.ow > 16) return false;
+    if (!cg_plan(g, g.oh, (iplane + g.mult * oplane) * sz, sz, p.c)) return false;
     p.owm = g.ow <= 4 ? 4 : (g.ow <= 8 ? 8 : 16);
-    const int64_t per_ch = (iplane + g.mult * oplane) * sz;
-    int G = std::min<int64_t>(kThreads / g.oh, g.ic);
-    while (G > 1 && G * per_ch > kStageCap) --G;
-    if (G * per_ch > kStageCap) return false;
-    // whole 16-byte vectors: every image's range of every channel group starts
-    // and ends on a vector boundary (base pointers are checked at launch)
-    bool vec = (g.ic * iplane) % VE == 0 && (static_cast<int64_t>(g.oc) * oplane) % VE == 0;
-    if (vec) {
-        int Gv = G;
-        while (Gv > 0 && ((Gv * iplane) % VE != 0 || (Gv * g.mult * oplane) % VE != 0)) --Gv;
-        if (Gv > 0) G = Gv; else vec = false;
-    }
-    const int ngroups = (g.ic + G - 1) / G;
-    // about 1536 workgroups (six per CU) with at least four images each when
-    // the batch allows, so loads of the next image overlap the current one
-    int NC = std::max(1, (1536 + ngroups - 1) / ngroups);
-    NC = std::min(NC, std::max(1, g.n / 4));
-    const int npc = (g.n + NC - 1) / NC;
-    NC = (g.n + npc - 1) / npc;
     const int iwm = row_span(g, p.owm);
-    p.G = G;
-    p.NC = NC;
-    p.npc = npc;
-    p.grid = ngroups * NC;
-    p.vec = vec;
     // LDS: [left guard][x planes][pad][dy planes][right guard]; the guards and
     // the pad keep every row-window read inside the allocation
     p.gpre = (g.pw + VE - 1) / VE * VE;
-    const int xl = static_cast<int>(G * iplane), dl = static_cast<int>(G * g.mult * oplane);
+    const int xl = static_cast<int>(p.c.G * iplane), dl = static_cast<int>(p.c.G * g.mult * oplane);
     p.dofs = p.gpre + (xl + VE - 1) / VE * VE;
     const int post = std::max(iwm, p.owm) + VE;
     const int stage = (p.dofs + dl + post) * sz;
@@ -252,13 +190,13 @@ int run_sp_bwdw(const Geo &g, const SwPlan &p, const void *x, const void *dy, vo
     a.dy = static_cast<const T *>(dy);
     a.ws = static_cast<float *>(ws);
     a.g = g;
-    a.G = p.G;
-    a.NC = p.NC;
-    a.npc = p.npc;
+    a.G = p.c.G;
+    a.NC = p.c.NC;
+    a.npc = p.c.npc;
     a.gpre = p.gpre;
     a.dofs = p.dofs;
-    a.vec = p.vec && reinterpret_cast<uintptr_t>(x) % 16 == 0 && reinterpret_cast<uintptr_t>(dy) % 16 == 0;
-    hipLaunchKernelGGL((sp_bwdw_kernel<T, K, S, D, MM, OWM>), dim3(p.grid), dim3(kThreads), p.lds_bytes, s, a);
+    a.vec = p.c.vec && reinterpret_cast<uintptr_t>(x) % 16 == 0 && reinterpret_cast<uintptr_t>(dy) % 16 == 0;
+    hipLaunchKernelGGL((sp_bwdw_kernel<T, K, S, D, MM, OWM>), dim3(p.c.grid), dim3(kThreads), p.lds_bytes, s, a);
     return hipGetLastError() == hipSuccess ? kOk : kErrHip;
 }
 
@@ -293,7 +231,7 @@ bool small_fits(const Geo &g, int dtype, int pass) {
 int small_bwd_weight_chunks(const Geo &g, int dtype) {
     SwPlan p;
     const bool ok = dtype == 0 ? plan_sp_bwdw<float>(g, p) : plan_sp_bwdw<__half>(g, p);
-    return ok ? p.NC : 0;
+    return ok ? p.c.NC : 0;
 }
 
 int small_bwd_weight(const Geo &g, const void *x, const void *dy, void *ws, int dtype, hipStream_t s) {

@@ -450,3 +450,27 @@ def test_small_plane_shapes(n, c, h, w, mult, k, s, p, d, dt):
     x, wt, b, dy = static_case(n, c, h, w, mult, k, s, p, d, DT[dt], 900 + c + h * 3 + k)
     check_static(x, wt, b, dy, s, p, d, "smallplane n%d c%d %dx%d m%d k%d s%d %s" % (n, c, h, w, mult, k, s, dt),
                  passes=("bwd_w",))
+
+
+# ------------------------------------------------------------------ small planes (forward and grad-input by channel groups)
+@pytest.mark.parametrize("n,c,h,w,mult,k,s,p,d,dt,fwd_cg", [
+    (6, 40, 7, 7, 1, 3, 1, 1, 1, "f32", True),       # two channel groups, the second partial
+    (9, 1024, 7, 7, 1, 3, 2, 1, 1, "f32", True),     # 7x7 -> 4x4, odd padding at stride 2
+    (4, 512, 14, 14, 1, 3, 2, 1, 1, "f32", True),    # 14x14 -> 7x7
+    (5, 72, 14, 14, 1, 3, 1, 1, 1, "bf16", True),    # group size cut to whole 16-byte vectors
+    (4, 24, 28, 28, 1, 3, 2, 1, 1, "f16", False),    # dx rows of 28 in 32-wide windows (grad-input only)
+    (3, 20, 7, 9, 2, 5, 1, 2, 1, "f32", True),       # 5x5, multiplier 2
+    (4, 10, 11, 11, 1, 5, 2, 2, 2, "f32", True),     # 5x5 stride 2 dilation 2, even padding; element staging
+    (3, 9, 12, 16, 1, 3, 2, 0, 1, "bf16", True),     # stride 2 without padding
+    (2, 7, 5, 5, 2, 3, 1, 1, 1, "f16", True),        # element staging, multiplier 2
+    (3, 6, 20, 30, 1, 5, 2, 3, 2, "f32", False),     # 5x5 stride 2 dilation 2, odd padding, dx rows of 30
+    (2, 3, 13, 15, 2, 3, 1, 1, 1, "f32", True),      # rows of 15 in 16-wide windows, multiplier 2
+    (2, 5, 8, 32, 1, 3, 1, 1, 1, "bf16", False),     # stride 1, dx rows of 32
+])
+def test_small_plane_fwd_bwd_input(n, c, h, w, mult, k, s, p, d, dt, fwd_cg):
+    geo = ((n, c, h, w), (c * mult, k, k), s, p, d)
+    assert dc.dwconv2d_algo(1, *geo, dtype=DT[dt]) == "channelgroup_small"
+    assert (dc.dwconv2d_algo(0, *geo, dtype=DT[dt]) == "channelgroup_small") == fwd_cg
+    x, wt, b, dy = static_case(n, c, h, w, mult, k, s, p, d, DT[dt], 950 + c + h * 3 + k + s)
+    check_static(x, wt, b, dy, s, p, d, "smallplane-fb n%d c%d %dx%d m%d k%d s%d p%d %s" % (n, c, h, w, mult, k, s, p, dt),
+                 passes=("fwd", "bwd_in"))
