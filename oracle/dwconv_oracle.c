@@ -204,3 +204,45 @@ void oracle_dynconv_multidil_fwd(const double *x, const double *const *filters,
             }
     }
 }
+
+/* Chain rule of oracle_dynconv_multidil_fwd (y is bilinear in x and the filters):
+ *   dF_b[n, c, i*k + j, py, px] = dy[n, b*C + c, py, px] * x[n, c, py + (i - r)*d_b, px + (j - r)*d_b]
+ *                                 (0 where that input pixel is outside the image)
+ *   dx[n, c, sy, sx] += F_b[n, c, i*k + j, py, px] * dy[n, b*C + c, py, px]
+ *                       for every in-image (sy, sx) = (py + (i - r)*d_b, px + (j - r)*d_b).
+ * dx may be NULL; dfilters may be NULL, and so may any entry of it.  The loop nest is
+ * the forward's, scattering into dx; each task owns one (n, c): its dx plane and its
+ * filter-gradient planes of every branch. */
+void oracle_dynconv_multidil_bwd(const double *x, const double *const *filters, const double *dy,
+                                 const int32_t *dilations, int32_t nb, double *dx,
+                                 double *const *dfilters, int64_t n, int64_t c, int64_t h,
+                                 int64_t w, int64_t k)
+{
+    const int64_t r = (k - 1) / 2;
+    int64_t task;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (task = 0; task < n * c; task++) {
+        const int64_t nn = task / c, ch = task % c;
+        const double *xp = x + task * h * w;
+        double *dxp = dx ? dx + task * h * w : NULL;
+        if (dxp) memset(dxp, 0, sizeof(double) * (size_t)(h * w));
+        for (int64_t br = 0; br < nb; br++) {
+            const int64_t d = dilations[br];
+            const double *fp = filters[br] + task * k * k * h * w;
+            const double *gp = dy + (nn * nb * c + br * c + ch) * h * w;
+            double *dfp = (dfilters && dfilters[br]) ? dfilters[br] + task * k * k * h * w : NULL;
+            for (int64_t py = 0; py < h; py++)
+                for (int64_t px = 0; px < w; px++) {
+                    const double g = gp[py * w + px];
+                    for (int64_t i = 0; i < k; i++)
+                        for (int64_t j = 0; j < k; j++) {
+                            const int64_t sy = py + (i - r) * d, sx = px + (j - r) * d;
+                            const int inside = sy >= 0 && sy < h && sx >= 0 && sx < w;
+                            const int64_t t = (i * k + j) * h * w + py * w + px;
+                            if (dfp) dfp[t] = inside ? g * xp[sy * w + sx] : 0.0;
+                            if (dxp && inside) dxp[sy * w + sx] += fp[t] * g;
+                        }
+                }
+        }
+    }
+}

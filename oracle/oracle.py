@@ -81,6 +81,10 @@ class Oracle:
             _DP, ctypes.POINTER(_DP), ctypes.POINTER(ctypes.c_int32), ctypes.c_int32, _DP,
             _I64, _I64, _I64, _I64, _I64]
         lib.oracle_dynconv_multidil_fwd.restype = None
+        lib.oracle_dynconv_multidil_bwd.argtypes = [
+            _DP, ctypes.POINTER(_DP), _DP, ctypes.POINTER(ctypes.c_int32), ctypes.c_int32, _DP,
+            ctypes.POINTER(_DP), _I64, _I64, _I64, _I64, _I64]
+        lib.oracle_dynconv_multidil_bwd.restype = None
         self._lib = lib
         self.path = path
 
@@ -167,6 +171,36 @@ class Oracle:
         self._lib.oracle_dynconv_multidil_fwd(_ptr(x), arr, dil, nb, _ptr(y), n, c, h, w, k)
         return y
 
+    def dynconv_multidil_bwd(self, x, filters, dy, dilations=(1, 3, 5), need_dx=True, need_df=True):
+        """(dx, [dF_b]) of the branch-concatenated dynamic filter for the output gradient dy
+        (n, nb*c, h, w); dx is (n, c, h, w), dF_b like filters[b].  Either part may be
+        skipped (returned as None)."""
+        x = _f64(x)
+        fs = [_f64(f) for f in filters]
+        dy = _f64(dy)
+        n, c, h, w = x.shape
+        nb = len(fs)
+        if nb < 1 or nb != len(dilations):
+            raise ValueError("one filter tensor per dilation")
+        kk = fs[0].shape[2]
+        k = int(round(kk ** 0.5))
+        if k * k != kk or k % 2 == 0:
+            raise ValueError("filters must hold an odd k*k taps")
+        for f in fs:
+            if tuple(f.shape) != (n, c, kk, h, w):
+                raise ValueError("filter shape %s does not match x" % (f.shape,))
+        if tuple(dy.shape) != (n, nb * c, h, w):
+            raise ValueError("dy shape %s does not match (n, nb*c, h, w)" % (dy.shape,))
+        if min(int(d) for d in dilations) < 1:
+            raise ValueError("dilations must be >= 1")
+        dx = np.empty((n, c, h, w), np.float64) if need_dx else None
+        dfs = [np.empty((n, c, kk, h, w), np.float64) for _ in fs] if need_df else None
+        arr = (_DP * nb)(*[_ptr(f) for f in fs])
+        darr = (_DP * nb)(*[_ptr(f) for f in dfs]) if need_df else None
+        dil = (ctypes.c_int32 * nb)(*[int(d) for d in dilations])
+        self._lib.oracle_dynconv_multidil_bwd(_ptr(x), arr, _ptr(dy), dil, nb, _ptr(dx), darr, n, c, h, w, k)
+        return dx, dfs
+
 
 _default = None
 
@@ -211,3 +245,7 @@ def dwconv2d_bwd_weight(*a, **k):
 
 def dynconv_multidil_fwd(*a, **k):
     return default().dynconv_multidil_fwd(*a, **k)
+
+
+def dynconv_multidil_bwd(*a, **k):
+    return default().dynconv_multidil_bwd(*a, **k)

@@ -12,7 +12,9 @@ AssertionError when the oracle disagrees with an independent fact:
   db is the plain sum of dy;
 * adjoint identities <dy, fwd(x, w)> = <bwd_input(dy, w), x> = <bwd_weight(x, dy), w>;
 * the dynamic filter equals the static depthwise convolution when every pixel
-  carries the same filter;
+  carries the same filter; its backward satisfies <dy, y> = <dx, x> =
+  sum_b <dF_b, F_b>, matches torch autograd of the unfold formulation and gives
+  shifted copies of dy (dx) and products dy * shifted x (dF) for one-hot filters;
 * the page-printed geometry chain in tests/golden/.
 
 The same checks run against builds of the oracle with planted mistakes
@@ -352,6 +354,101 @@ def check_dyn_ones_count(orc):
             p = (k - 1) // 2 * dd
             want = np.outer(_count(h, h, k, 1, p, dd), _count(w, w, k, 1, p, dd))
             assert np.array_equal(y[:, bi * c:(bi + 1) * c], np.broadcast_to(want, (n, c, h, w)))
+
+
+# ---------------------------------------------------------------- dynamic, backward
+def _dyn_bwd_case(case, seed):
+    n, c, h, w, k, dils = case
+    x, fs = _dyn_inputs(case, seed)
+    dy = _rng(seed + 1).normal(0, 1, (n, len(dils) * c, h, w))
+    return x, fs, dy
+
+
+def check_dyn_bwd_adjoint(orc):
+    """y is bilinear: <dy, y> = <dx, x> = sum_b <dF_b, F_b>."""
+    for ci, case in enumerate(DYN_CASES):
+        x, fs, dy = _dyn_bwd_case(case, 170 + ci)
+        dils = case[5]
+        y = orc.dynconv_multidil_fwd(x, fs, dils)
+        dx, dfs = orc.dynconv_multidil_bwd(x, fs, dy, dils)
+        ref = float(np.sum(dy * y))
+        lx = float(np.sum(dx * x))
+        lf = float(sum(np.sum(df * f) for df, f in zip(dfs, fs)))
+        tol = 1e-12 * max(1.0, abs(ref)) * y.size
+        assert abs(ref - lx) <= tol and abs(ref - lf) <= tol, (case, ref, lx, lf)
+
+
+def check_dyn_bwd_autograd(orc):
+    """torch autograd (float64, CPU) of the F.unfold formulation."""
+    torch, F = _torch()
+    for ci, case in enumerate(DYN_CASES):
+        n, c, h, w, k, dils = case
+        x, fs, dy = _dyn_bwd_case(case, 180 + ci)
+        xt = torch.from_numpy(x).requires_grad_(True)
+        ft = [torch.from_numpy(f).requires_grad_(True) for f in fs]
+        outs = []
+        for bi, dd in enumerate(dils):
+            cols = F.unfold(xt, k, dilation=dd, padding=(k - 1) // 2 * dd).view(n, c, k * k, h, w)
+            outs.append((cols * ft[bi]).sum(2))
+        torch.cat(outs, 1).backward(torch.from_numpy(dy))
+        dx, dfs = orc.dynconv_multidil_bwd(x, fs, dy, dils)
+        np.testing.assert_allclose(dx, xt.grad.numpy(), rtol=1e-11, atol=1e-11, err_msg=str(case))
+        for bi in range(len(dils)):
+            np.testing.assert_allclose(dfs[bi], ft[bi].grad.numpy(), rtol=1e-11, atol=1e-11,
+                                       err_msg="%s branch %d" % (case, bi))
+
+
+def check_dyn_bwd_one_hot(orc):
+    """Filters one-hot at tap t: dx is the sum over branches of dy_b shifted back by
+    ((i-r)d_b, (j-r)d_b), and dF_b at every tap is dy_b times x shifted forward, exactly."""
+    for case in DYN_CASES:
+        n, c, h, w, k, dils = case
+        x, _, dy = _dyn_bwd_case(case, 190)
+        rr = (k - 1) // 2
+        for t in range(k * k):
+            i, j = divmod(t, k)
+            fs = []
+            for _ in dils:
+                f = np.zeros((n, c, k * k, h, w))
+                f[:, :, t] = 1.0
+                fs.append(f)
+            dx, dfs = orc.dynconv_multidil_bwd(x, fs, dy, dils)
+            want = np.zeros((n, c, h, w))
+            for bi, dd in enumerate(dils):
+                g = dy[:, bi * c:(bi + 1) * c]
+                for py in range(h):
+                    for px in range(w):
+                        sy, sx = py + (i - rr) * dd, px + (j - rr) * dd
+                        if 0 <= sy < h and 0 <= sx < w:
+                            want[:, :, sy, sx] += g[:, :, py, px]
+            assert np.array_equal(dx, want), (case, t)
+        x, fs, dy = _dyn_bwd_case(case, 195)
+        _, dfs = orc.dynconv_multidil_bwd(x, fs, dy, dils)
+        for bi, dd in enumerate(dils):
+            g = dy[:, bi * c:(bi + 1) * c]
+            for t in range(k * k):
+                i, j = divmod(t, k)
+                want = np.zeros((n, c, h, w))
+                for py in range(h):
+                    for px in range(w):
+                        sy, sx = py + (i - rr) * dd, px + (j - rr) * dd
+                        if 0 <= sy < h and 0 <= sx < w:
+                            want[:, :, py, px] = g[:, :, py, px] * x[:, :, sy, sx]
+                assert np.array_equal(dfs[bi][:, :, t], want), (case, bi, t)
+
+
+def check_dyn_bwd_parts(orc):
+    """Asking for one part gives the same values as asking for both."""
+    for ci, case in enumerate(DYN_CASES):
+        x, fs, dy = _dyn_bwd_case(case, 200 + ci)
+        dils = case[5]
+        dx, dfs = orc.dynconv_multidil_bwd(x, fs, dy, dils)
+        dx1, none1 = orc.dynconv_multidil_bwd(x, fs, dy, dils, need_df=False)
+        none2, dfs2 = orc.dynconv_multidil_bwd(x, fs, dy, dils, need_dx=False)
+        assert none1 is None and none2 is None
+        assert np.array_equal(dx, dx1)
+        for a, b in zip(dfs, dfs2):
+            assert np.array_equal(a, b)
 
 
 ALL_CHECKS = [v for k_, v in sorted(globals().items()) if k_.startswith("check_")]

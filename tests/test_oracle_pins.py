@@ -44,6 +44,11 @@ MUTATIONS = [
     ("dyn_filter_spatial_transposed", r"h \* w \+ py \* w \+ px\]", "h * w + px * h + py]", 0),
     ("dyn_tap_order", r"\(i \* k \+ j\) \* h \* w", "(j * k + i) * h * w", 0),
     ("dyn_dilation_ignored", r"sx = px \+ \(j - r\) \* d", "sx = px + (j - r)", 0),
+    ("dynbwd_tap_flip", r"py \+ \(i - r\) \* d", "py + (r - i) * d", 1),
+    ("dynbwd_branch_offset", r"nn \* nb \* c \+ br \* c \+ ch", "nn * nb * c + ch * nb + br", 1),
+    ("dynbwd_df_reads_filter", r"g \* xp\[sy \* w \+ sx\]", "g * fp[t]", 0),
+    ("dynbwd_dx_drops_dy", r"\+= fp\[t\] \* g;", "+= fp[t];", 0),
+    ("dynbwd_dilation_ignored", r"sx = px \+ \(j - r\) \* d", "sx = px + (j - r)", 1),
 ]
 
 
