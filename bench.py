@@ -14,7 +14,8 @@ uses over every case of the workload, with inputs resident in HBM:
   largek               N=64, C=384, H in {32,48,64}, k in {7,13,31}, pad k//2,
                        fp32 and fp16; the three passes
   dynamic              per-pixel 3x3 filters at dilations 1/3/5, N in {1,2}, C=64,
-                       H in {128,256}, fp32/fp16/bf16; output concatenated
+                       H in {128,256}, fp32/fp16/bf16; output concatenated;
+                       forward, then backward (dx and the filter gradients)
 
 Passes run in pass-major order (every case's forward, then every grad-input,
 then every grad-weight) so a tensor is re-read only after gigabytes of other
@@ -203,31 +204,48 @@ def build_workload(name, dc, dev):
 
 
 def build_dynamic(dc, dev):
+    """Forward and backward of the fused dynamic filter over the workload's cases.
+
+    Compulsory bytes per call (each input element the result depends on once,
+    each output element once): forward |x| + in-bounds filter taps + |y|;
+    backward |x| + |dy| + in-bounds filter taps (read for dx) + |dx| + every
+    filter-gradient element (written, zero for taps outside the image).
+    """
     import torch
     from dynamic_convolution_amd import synth
     D = synth.DYNAMIC
-    calls, per_case, cases = [], [], []
+    fwd, bwd, per_case, cases = [], [], [], []
     seed = 400
     for n in D["batches"]:
         for h in D["hs"]:
             for dts in D["dtypes"]:
                 dtype = synth.DTYPES[dts]
                 e = torch.empty(0, dtype=dtype).element_size()
-                x = synth.draw((n, D["c"], h, h), D["x"], seed, "x", dtype, device=dev)
-                fs = [synth.draw((n, D["c"], 9, h, h), D["f"], seed, "f%d" % i, dtype, device=dev)
-                      for i in range(3)]
-                y = torch.empty((n, 3 * D["c"], h, h), dtype=dtype, device=dev)
+                c = D["c"]
+                x = synth.draw((n, c, h, h), D["x"], seed, "x", dtype, device=dev)
+                fs = [synth.draw((n, c, 9, h, h), D["f"], seed, "f%d" % i, dtype, device=dev) for i in range(3)]
+                dy = synth.draw((n, 3 * c, h, h), D["dy"], seed, "dy", dtype, device=dev)
+                y = torch.empty((n, 3 * c, h, h), dtype=dtype, device=dev)
+                dx = torch.empty_like(x)
+                dfs = [torch.empty_like(f) for f in fs]
                 taps = sum(valid_taps(h, h, 3, 1, dd, dd) ** 2 for dd in D["dilations"])
-                nbytes = x.numel() * e + n * D["c"] * taps * e + y.numel() * e
-                cl = Call("dyn.fused.k3_%s" % dts, (lambda x=x, fs=fs, y=y: dc.dynconv_multidil_fwd(x, fs, D["dilations"], out=y)),
-                          nbytes, 2 * n * D["c"] * taps)
-                calls.append(cl)
-                per_case.append(([cl], dict(x=x, fs=fs, y=y)))
+                X, Y, TF = x.numel() * e, y.numel() * e, n * c * taps * e
+                FF = sum(f.numel() for f in fs) * e
+                cf = Call("dyn.fused.k3_%s" % dts,
+                          (lambda x=x, fs=fs, y=y: dc.dynconv_multidil_fwd(x, fs, D["dilations"], out=y)),
+                          X + TF + Y, 2 * n * c * taps)
+                cb = Call("dyn_bwd.fused.k3_%s" % dts,
+                          (lambda x=x, fs=fs, dy=dy, dx=dx, dfs=dfs:
+                           dc.dynconv_multidil_bwd(x, fs, dy, D["dilations"], out_dx=dx, out_dfilters=dfs)),
+                          X + Y + TF + X + FF, 3 * n * c * taps)
+                fwd.append(cf)
+                bwd.append(cb)
+                per_case.append(([cf, cb], dict(x=x, fs=fs, y=y, dy=dy, dx=dx, dfs=dfs)))
                 cases.append(((n, h, dts), seed))
                 seed += 1
     cfg = {"batches": list(D["batches"]), "c": D["c"], "hw": list(D["hs"]), "k": 3, "dilations": list(D["dilations"]),
-           "dtypes": list(D["dtypes"]), "passes": ["fwd"]}
-    return dict(cases=cases, per_case=per_case, calls=calls, desc="dynamic_multidil_3x3_d135", dtype="f32+f16+bf16",
+           "dtypes": list(D["dtypes"]), "passes": ["fwd", "bwd (dx and filter gradients)"]}
+    return dict(cases=cases, per_case=per_case, calls=fwd + bwd, desc="dynamic_multidil_3x3_d135", dtype="f32+f16+bf16",
                 kind="bytes", cfg=cfg)
 
 
@@ -251,10 +269,12 @@ def cpu_baseline(wl, target_s):
                 sl = min(ns, n)
                 x = f64(t["x"][:sl])
                 fs = [f64(f[:sl]) for f in t["fs"]]
+                dy = f64(t["dy"][:sl])
                 t0 = time.perf_counter()
                 O.dynconv_multidil_fwd(x, fs, (1, 3, 5))
+                O.dynconv_multidil_bwd(x, fs, dy, (1, 3, 5))
                 tot_t += time.perf_counter() - t0
-                tot_units += (calls[0].nbytes if kind == "bytes" else calls[0].flops) * sl / n
+                tot_units += sum(cl.nbytes if kind == "bytes" else cl.flops for cl in calls) * sl / n
                 continue
             n, c, h, M, k, s, p, d = cs[:8]
             sl = min(ns, n)

@@ -9,6 +9,7 @@ ABI's names:
     dwconv2d_bwd_input(dy, w, x_shape, stride=1, padding=0, dilation=1)
     dwconv2d_bwd_weight(x, dy, w_shape, stride=1, padding=0, dilation=1, with_bias=True)
     dynconv_multidil_fwd(x, filters, dilations=(1, 3, 5))
+    dynconv_multidil_bwd(x, filters, dy, dilations=(1, 3, 5), need_dx=True, need_dfilters=True)
     dwconv2d_out_size(x_shape, w_shape, stride=1, padding=0, dilation=1)
     dwconv2d_bwd_weight_workspace_bytes(x_shape, w_shape, stride, padding, dilation, dtype)
 """
@@ -20,6 +21,7 @@ from ._native import (  # noqa: F401
     dwconv2d_bwd_weight_workspace_bytes,
     dwconv2d_fwd,
     dwconv2d_out_size,
+    dynconv_multidil_bwd,
     dynconv_multidil_fwd,
     lib,
     status_str,

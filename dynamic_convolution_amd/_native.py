@@ -24,7 +24,7 @@ STATUS = {
 EXPORTS = (
     "dwconv2d_out_size", "dwconv2d_fwd", "dwconv2d_bwd_input",
     "dwconv2d_bwd_weight_workspace_bytes", "dwconv2d_bwd_weight",
-    "dynconv_multidil_fwd", "dwconv2d_algo", "dw_status_str",
+    "dynconv_multidil_fwd", "dynconv_multidil_bwd", "dwconv2d_algo", "dw_status_str",
 )
 
 _I64 = ctypes.c_int64
@@ -65,6 +65,10 @@ def lib() -> ctypes.CDLL:
                                        ctypes.c_int32, _VP, _I64, _I64, _I64, _I64, _I64,
                                        ctypes.c_int, _VP]
     L.dynconv_multidil_fwd.restype = ctypes.c_int
+    L.dynconv_multidil_bwd.argtypes = [_VP, ctypes.POINTER(_VP), _VP, ctypes.POINTER(ctypes.c_int32),
+                                       ctypes.c_int32, _VP, ctypes.POINTER(_VP), _I64, _I64, _I64, _I64, _I64,
+                                       ctypes.c_int, _VP]
+    L.dynconv_multidil_bwd.restype = ctypes.c_int
     L.dwconv2d_algo.argtypes = [ctypes.c_int] + _GEO + [ctypes.c_int]
     L.dwconv2d_algo.restype = ctypes.c_char_p
     L.dw_status_str.argtypes = [ctypes.c_int]
@@ -239,3 +243,44 @@ def dynconv_multidil_fwd(x, filters, dilations=(1, 3, 5), out=None):
     _check(lib().dynconv_multidil_fwd(_dev(x, "x"), fptrs, dil, nb, _dev(out, "out"), n, c, h, w, k,
                                       _dtype_code(x), _stream(x)), "dynconv_multidil_fwd")
     return out
+
+
+def dynconv_multidil_bwd(x, filters, dy, dilations=(1, 3, 5), need_dx=True, need_dfilters=True,
+                         out_dx=None, out_dfilters=None):
+    """(dx, [dF_b]) of dynconv_multidil_fwd for the output gradient dy (n, nb*c, h, w).
+
+    dx has x's shape and dF_b filters[b]'s; a part not needed is returned as None.
+    """
+    import torch
+    n, c, h, w = (int(s) for s in x.shape)
+    nb = len(filters)
+    if nb != len(dilations):
+        raise ValueError("one filter tensor per dilation")
+    kk = int(filters[0].shape[2])
+    k = int(round(kk ** 0.5))
+    if k * k != kk:
+        raise ValueError("filters must hold k*k taps")
+    for f in filters:
+        if tuple(f.shape) != (n, c, kk, h, w) or f.dtype != x.dtype:
+            raise ValueError("filter %s %s does not match x" % (tuple(f.shape), f.dtype))
+    if tuple(dy.shape) != (n, nb * c, h, w) or dy.dtype != x.dtype:
+        raise ValueError("dy %s %s does not match (n, nb*c, h, w)" % (tuple(dy.shape), dy.dtype))
+    dx = None
+    if need_dx:
+        dx = out_dx if out_dx is not None else torch.empty_like(x)
+        if tuple(dx.shape) != tuple(x.shape) or dx.dtype != x.dtype:
+            raise ValueError("out_dx %s %s does not match x" % (tuple(dx.shape), dx.dtype))
+    dfs = None
+    if need_dfilters:
+        dfs = list(out_dfilters) if out_dfilters is not None else [torch.empty_like(f) for f in filters]
+        if len(dfs) != nb:
+            raise ValueError("one filter gradient per branch")
+        for g, f in zip(dfs, filters):
+            if g is not None and (tuple(g.shape) != tuple(f.shape) or g.dtype != f.dtype):
+                raise ValueError("filter gradient %s %s does not match" % (tuple(g.shape), g.dtype))
+    fptrs = (_VP * nb)(*[_dev(f, "filter") for f in filters])
+    dptrs = (_VP * nb)(*[_dev(g, "filter gradient") for g in dfs]) if dfs is not None else None
+    dil = (ctypes.c_int32 * nb)(*[int(d) for d in dilations])
+    _check(lib().dynconv_multidil_bwd(_dev(x, "x"), fptrs, _dev(dy, "dy"), dil, nb, _dev(dx, "dx"), dptrs,
+                                      n, c, h, w, k, _dtype_code(x), _stream(x)), "dynconv_multidil_bwd")
+    return dx, dfs

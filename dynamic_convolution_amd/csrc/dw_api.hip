@@ -2,8 +2,9 @@
 //
 // Every argument is validated on the host before any HIP call, so invalid
 // calls launch nothing and touch no output.  Valid calls plan the launch and
-// enqueue the kernels of dw_fwd / dw_bwd_input / dw_bwd_weight / dw_dynconv on
-// the caller's stream.
+// enqueue the kernels of dw_fwd / dw_bwd_input / dw_bwd_weight / dw_dynconv /
+// dw_dynbwd (and the specialised families they dispatch to) on the caller's
+// stream.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -86,6 +87,34 @@ int map_launch(int rc) {
     if (rc == dw::kOk) return DW_OK;
     if (rc == dw::kErrUnsupported) return DW_EUNSUPPORTED;
     return DW_EHIP;
+}
+
+// Validates the arguments the dynamic filter's forward and backward share:
+// dtype, sizes, branch count, dilations, x and the filter pointers, element
+// counts.  Writes the largest dilation.
+int check_dyn(const void *x, const void *const *filters, const int32_t *dilations, int32_t nb, int64_t n,
+              int64_t c, int64_t h, int64_t w, int64_t k, int dtype, int *maxdil) {
+    if (dtype != DW_F32 && dtype != DW_F16 && dtype != DW_BF16) return DW_EDTYPE;
+    if (n < 1 || c < 1 || h < 1 || w < 1 || k < 1) return DW_ESHAPE;
+    for (int64_t v : {n, c, h, w, k})
+        if (v > kMaxExtent) return DW_ETOOLARGE;
+    if (nb < 1 || nb > 4 || (k % 2) == 0) return DW_EDYN;
+    if (!x || !filters || !dilations) return DW_EPTR;
+    int md = 1;
+    for (int b = 0; b < nb; ++b) {
+        if (dilations[b] < 1) return DW_EDYN;
+        if (!filters[b]) return DW_EPTR;
+        if ((k - 1) / 2 * static_cast<int64_t>(dilations[b]) > kMaxExtent) return DW_ETOOLARGE;
+        if (dilations[b] > md) md = dilations[b];
+    }
+    if (!product_ok(n, c, h, w) || !product_ok(n * nb, c, h, w) || !product_ok(n * c, k * k, h, w))
+        return DW_ETOOLARGE;
+    const size_t e = elem_size(dtype);
+    if (!aligned(x, e)) return DW_EPTR;
+    for (int b = 0; b < nb; ++b)
+        if (!aligned(filters[b], e)) return DW_EPTR;
+    *maxdil = md;
+    return DW_OK;
 }
 
 }  // namespace
@@ -177,25 +206,12 @@ int dwconv2d_bwd_weight(const void *x, const void *dy, void *dwt, void *db, void
 
 int dynconv_multidil_fwd(const void *x, const void *const *filters, const int32_t *dilations, int32_t nb,
                          void *y, int64_t n, int64_t c, int64_t h, int64_t w, int64_t k, int dtype, void *stream) {
-    if (dtype != DW_F32 && dtype != DW_F16 && dtype != DW_BF16) return DW_EDTYPE;
-    if (n < 1 || c < 1 || h < 1 || w < 1 || k < 1) return DW_ESHAPE;
-    for (int64_t v : {n, c, h, w, k})
-        if (v > kMaxExtent) return DW_ETOOLARGE;
-    if (nb < 1 || nb > 4 || (k % 2) == 0) return DW_EDYN;
-    if (!x || !y || !filters || !dilations) return DW_EPTR;
     int maxdil = 1;
-    for (int b = 0; b < nb; ++b) {
-        if (dilations[b] < 1) return DW_EDYN;
-        if (!filters[b]) return DW_EPTR;
-        if ((k - 1) / 2 * static_cast<int64_t>(dilations[b]) > kMaxExtent) return DW_ETOOLARGE;
-        if (dilations[b] > maxdil) maxdil = dilations[b];
-    }
-    if (!product_ok(n, c, h, w) || !product_ok(n * nb, c, h, w) || !product_ok(n * c, k * k, h, w))
-        return DW_ETOOLARGE;
+    const int rc = check_dyn(x, filters, dilations, nb, n, c, h, w, k, dtype, &maxdil);
+    if (rc != DW_OK) return rc;
+    if (!y) return DW_EPTR;
     const size_t e = elem_size(dtype);
-    if (!aligned(x, e) || !aligned(y, e)) return DW_EPTR;
-    for (int b = 0; b < nb; ++b)
-        if (!aligned(filters[b], e)) return DW_EPTR;
+    if (!aligned(y, e)) return DW_EPTR;
     const size_t xb = static_cast<size_t>(n * c * h * w) * e;
     const size_t yb = xb * static_cast<size_t>(nb);
     const size_t fb = static_cast<size_t>(n * c * k * k * h * w) * e;
@@ -207,6 +223,48 @@ int dynconv_multidil_fwd(const void *x, const void *const *filters, const int32_
     return map_launch(dw::launch_dynconv(x, filters, dilations, nb, y, static_cast<int>(n), static_cast<int>(c),
                                          static_cast<int>(h), static_cast<int>(w), static_cast<int>(k), dtype,
                                          static_cast<hipStream_t>(stream)));
+}
+
+int dynconv_multidil_bwd(const void *x, const void *const *filters, const void *dy, const int32_t *dilations,
+                         int32_t nb, void *dx, void *const *dfilters, int64_t n, int64_t c, int64_t h, int64_t w,
+                         int64_t k, int dtype, void *stream) {
+    int maxdil = 1;
+    const int rc = check_dyn(x, filters, dilations, nb, n, c, h, w, k, dtype, &maxdil);
+    if (rc != DW_OK) return rc;
+    if (!dy) return DW_EPTR;
+    const size_t e = elem_size(dtype);
+    if (!aligned(dy, e) || (dx && !aligned(dx, e))) return DW_EPTR;
+    for (int b = 0; dfilters && b < nb; ++b)
+        if (dfilters[b] && !aligned(dfilters[b], e)) return DW_EPTR;
+    const size_t xb = static_cast<size_t>(n * c * h * w) * e;
+    const size_t yb = xb * static_cast<size_t>(nb);
+    const size_t fb = static_cast<size_t>(n * c * k * k * h * w) * e;
+    // every output against every input and every other output
+    const void *outs[1 + 4];
+    size_t osz[1 + 4];
+    int no = 0;
+    if (dx) {
+        outs[no] = dx;
+        osz[no++] = xb;
+    }
+    for (int b = 0; dfilters && b < nb; ++b)
+        if (dfilters[b]) {
+            outs[no] = dfilters[b];
+            osz[no++] = fb;
+        }
+    for (int o = 0; o < no; ++o) {
+        if (overlap(outs[o], osz[o], x, xb) || overlap(outs[o], osz[o], dy, yb)) return DW_EALIAS;
+        for (int b = 0; b < nb; ++b)
+            if (overlap(outs[o], osz[o], filters[b], fb)) return DW_EALIAS;
+        for (int q = o + 1; q < no; ++q)
+            if (overlap(outs[o], osz[o], outs[q], osz[q])) return DW_EALIAS;
+    }
+    if (!dw::dynconv_bwd_supported(static_cast<int>(h), static_cast<int>(w), static_cast<int>(k), maxdil, dtype))
+        return DW_EUNSUPPORTED;
+    if (no == 0) return DW_OK;  // nothing requested
+    return map_launch(dw::launch_dynconv_bwd(x, filters, dy, dilations, nb, dx, dfilters, static_cast<int>(n),
+                                             static_cast<int>(c), static_cast<int>(h), static_cast<int>(w),
+                                             static_cast<int>(k), dtype, static_cast<hipStream_t>(stream)));
 }
 
 const char *dwconv2d_algo(int pass, int64_t n, int64_t ic, int64_t ih, int64_t iw, int64_t oc, int64_t kh,

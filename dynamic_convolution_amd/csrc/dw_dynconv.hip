@@ -14,16 +14,12 @@
 // produces RW adjacent pixels of one row for all branches, streaming every
 // filter tap as one 16-byte coalesced load and writing each branch's strip at
 // its channel offset b*C + c of the concatenated output.
-#include "dw_common.hpp"
-#include "dw_internal.hpp"
+#include "dw_dyn.hpp"
 
 namespace dw {
 namespace {
 
-constexpr int kMaxBranches = 4;
-constexpr int kLdsPref = 32 * 1024;
-
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+using namespace dyn;
 
 template <typename T> struct DynArgs {
     const T *x;
@@ -41,58 +37,6 @@ template <typename T> struct DynArgs {
     int vin;    // x 16-byte aligned and rows of whole 16-byte vectors
     int vf;     // filters and y rows allow 16-byte strips
 };
-
-template <typename T, int RW>
-__device__ __forceinline__ void load_strip(const T *p, float *v, int valid, bool vec) {
-    if (vec && valid >= RW) {
-        static_assert(sizeof(T) * RW == 16, "strip is one 16-byte vector");
-        union {
-            u32x4 u;
-            T t[RW];
-        } b;
-        b.u = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
-#pragma unroll
-        for (int q = 0; q < RW; ++q) v[q] = to_f32(b.t[q]);
-    } else {
-#pragma unroll
-        for (int q = 0; q < RW; ++q) v[q] = q < valid ? to_f32(p[q]) : 0.f;
-    }
-}
-
-template <typename T, int RW>
-__device__ __forceinline__ void store_strip(T *p, const float *acc, int valid, bool vec) {
-    if (vec && valid >= RW) {
-        union {
-            uint4 u;
-            T t[RW];
-        } b;
-#pragma unroll
-        for (int q = 0; q < RW; ++q) b.t[q] = from_f32<T>(acc[q]);
-        *reinterpret_cast<uint4 *>(p) = b.u;
-    } else {
-#pragma unroll
-        for (int q = 0; q < RW; ++q)
-            if (q < valid) p[q] = from_f32<T>(acc[q]);
-    }
-}
-
-// RW elements held in one 16-byte vector, as fp32.
-template <typename T, int RW>
-__device__ __forceinline__ void strip_values(const u32x4 &u, float *v) {
-    static_assert(sizeof(T) * RW == 16, "strip is one 16-byte vector");
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int q = 0; q < RW; ++q) {
-        if constexpr (sizeof(T) == 4) {
-            v[q] = __uint_as_float(w[q]);
-        } else {
-            const uint32_t h = (q & 1) ? (w[q >> 1] >> 16) : (w[q >> 1] & 0xffffu);
-            T t;
-            __builtin_memcpy(&t, &h, sizeof(T));
-            v[q] = to_f32(t);
-        }
-    }
-}
 
 // VF: every strip is a whole aligned 16-byte vector (w a multiple of RW), so
 // the filter loads of a branch are issued together, unconditionally, before
@@ -120,56 +64,7 @@ __global__ __launch_bounds__(kThreads) void dynconv_kernel(DynArgs<T> a) {
 
     // stage x rows as fp32: row r at xs[r*LW + hp ...], zeros elsewhere in the row
     const T *src = a.x + static_cast<int64_t>(plane) * hw;
-    if (a.vin) {
-        constexpr int VE = Vec<T>::N;
-        constexpr int NB = 4;  // 16-byte loads in flight per thread
-        const int vpr = a.w / VE;
-        const int nvec = rows * vpr;
-        for (int v0 = tid; v0 < nvec; v0 += NB * kThreads) {
-            uint4 raw[NB];
-#pragma unroll
-            for (int k = 0; k < NB; ++k) {
-                raw[k] = make_uint4(0u, 0u, 0u, 0u);
-                const int v = v0 + k * kThreads;
-                const int r = v < nvec ? static_cast<int>(fdiv(static_cast<uint32_t>(v), a.fVPR)) : 0;
-                const int ih = rbase + r;
-                if (v < nvec && ih >= 0 && ih < a.h)
-                    raw[k] = *reinterpret_cast<const uint4 *>(src + static_cast<int64_t>(ih) * a.w +
-                                                               static_cast<int64_t>(v - r * vpr) * VE);
-            }
-#pragma unroll
-            for (int k = 0; k < NB; ++k) {
-                const int v = v0 + k * kThreads;
-                if (v < nvec) {
-                    const int r = static_cast<int>(fdiv(static_cast<uint32_t>(v), a.fVPR));
-                    float *d = xs + r * LW + hp + (v - r * vpr) * VE;
-                    union {
-                        uint4 u;
-                        T t[VE];
-                    } b;
-                    b.u = raw[k];
-#pragma unroll
-                    for (int e = 0; e < VE; e += 4)
-                        *reinterpret_cast<float4 *>(d + e) =
-                            make_float4(to_f32(b.t[e]), to_f32(b.t[e + 1]), to_f32(b.t[e + 2]), to_f32(b.t[e + 3]));
-                }
-            }
-        }
-        const int padw = LW - a.w;
-        for (int e = tid; e < rows * padw; e += kThreads) {
-            const int r = static_cast<int>(fdiv(static_cast<uint32_t>(e), a.fPAD));
-            const int j = e - r * padw;
-            xs[r * LW + (j < hp ? j : a.w + j)] = 0.f;
-        }
-    } else {
-        for (int e = tid; e < rows * LW; e += kThreads) {
-            const int r = static_cast<int>(fdiv(static_cast<uint32_t>(e), a.fLW));
-            const int col = e - r * LW - hp;
-            const int ih = rbase + r;
-            xs[e] = (col >= 0 && col < a.w && ih >= 0 && ih < a.h)
-                        ? to_f32(src[static_cast<int64_t>(ih) * a.w + col]) : 0.f;
-        }
-    }
+    stage_rows_f32<T>(xs, src, rbase, rows, a.h, a.w, LW, hp, a.fVPR, a.fPAD, a.fLW, a.vin != 0, tid);
     __syncthreads();
 
     const int items = a.BH * a.NS;
@@ -254,46 +149,6 @@ __global__ __launch_bounds__(kThreads) void dynconv_kernel(DynArgs<T> a) {
             store_strip<T, RW>(yp, acc, valid, a.vf != 0);
         }
     }
-}
-
-struct DynPlan {
-    int BH, nbands, lds_bytes;
-};
-
-// Staged tile geometry: hp zero columns left of each row (the largest
-// dilation's halo rounded up to 4, so the centre column of a strip is 16-byte
-// aligned) and a row pitch LW >= w + 2*hp, a multiple of 4.
-inline void dyn_tile(int w, int halo, int &hp, int &LW) {
-    hp = (halo + 3) / 4 * 4;
-    LW = (w + 2 * hp + 3) / 4 * 4;
-}
-
-template <typename T>
-bool plan_dyn(int n, int c, int h, int w, int k, int maxdil, DynPlan &p) {
-    constexpr int RW = Vec<T>::N;
-    const int NS = (w + RW - 1) / RW;
-    const int halo = (k - 1) / 2 * maxdil;
-    int hp, LW;
-    dyn_tile(w, halo, hp, LW);
-    auto bytes = [&](int bh) -> int64_t {
-        const int64_t rows = std::min<int64_t>(bh, h) + 2 * static_cast<int64_t>(halo);  // zero rows included
-        const int64_t cnt = rows * LW + RW;  // + RW: a partial last strip may read past the last row
-        if (cnt > (1 << 24)) return INT64_MAX;
-        return cnt * static_cast<int64_t>(sizeof(float));
-    };
-    const int lim = bytes(1) <= kLdsPref ? kLdsPref : kLdsCap;
-    if (bytes(1) > lim) return false;
-    // about two strips per thread, within the LDS budget
-    int bh = std::max(1, (2 * kThreads + NS - 1) / NS);
-    bh = std::min(bh, h);
-    while (bh > 1 && bytes(bh) > lim) --bh;
-    // keep >= 1024 workgroups when the problem is big enough
-    const int64_t planes = static_cast<int64_t>(n) * c;
-    while (bh > 1 && planes * ((h + bh - 1) / bh) < 1024) bh = (bh + 1) / 2;
-    p.nbands = (h + bh - 1) / bh;
-    p.BH = (h + p.nbands - 1) / p.nbands;
-    p.lds_bytes = static_cast<int>(bytes(p.BH));
-    return true;
 }
 
 template <typename T>

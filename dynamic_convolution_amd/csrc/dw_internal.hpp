@@ -36,6 +36,11 @@ int launch_bwd_weight(const Geo &g, const void *x, const void *dy, void *dwt, vo
                       void *ws, int dtype, hipStream_t s);
 int launch_dynconv(const void *x, const void *const *filters, const int32_t *dil, int nb, void *y,
                    int n, int c, int h, int w, int k, int dtype, hipStream_t s);
+// Backward of the dynamic filter (dw_dynbwd.hip): dx when non-NULL, dF_b for
+// every non-NULL dfilters[b] (dfilters itself may be NULL).
+int launch_dynconv_bwd(const void *x, const void *const *filters, const void *dy, const int32_t *dil, int nb,
+                       void *dx, void *const *dfilters, int n, int c, int h, int w, int k, int dtype,
+                       hipStream_t s);
 
 // Streaming kernels for 3x3 / pad 1 / dilation 1 / stride 1-2 / multiplier <= 2
 // (dw_rowwalk.hip).  The launchers return kErrUnsupported when the row is
@@ -83,5 +88,6 @@ const char *bwd_weight_algo_name(const Geo &g, int dtype);
 bool fwd_supported(const Geo &g, int dtype);
 bool bwd_input_supported(const Geo &g, int dtype);
 bool dynconv_supported(int h, int w, int k, int maxdil, int dtype);
+bool dynconv_bwd_supported(int h, int w, int k, int maxdil, int dtype);
 
 }  // namespace dw

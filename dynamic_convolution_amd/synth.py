@@ -48,6 +48,7 @@ LARGE_K = dict(n=64, c=384, hs=(32, 48, 64), ks=(7, 13, 31), dtypes=("f32", "f16
                x=("N", 0.0, 1.0), dy=("N", 0.0, 1.0))  # w ~ N(0, 1/k^2), pad k//2
 
 DYNAMIC = dict(batches=(1, 2), c=64, hs=(128, 256), k=3, dilations=(1, 3, 5),
-               dtypes=("f32", "f16", "bf16"), x=("N", 0.0, 1.0), f=("N", 0.0, 1.0 / 9))
+               dtypes=("f32", "f16", "bf16"), x=("N", 0.0, 1.0), f=("N", 0.0, 1.0 / 9),
+               dy=("N", 0.0, 1.0))  # dy: the output gradient of the backward
 
 DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}

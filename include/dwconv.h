@@ -167,6 +167,28 @@ int dynconv_multidil_fwd(const void *x, const void *const *filters,
                          int dtype, void *stream);
 
 /*
+ * Backward of dynconv_multidil_fwd (the page's benchmark of the fused
+ * operator times it together with its backward).  y is bilinear in x and
+ * the filters, so with dy the gradient of y:
+ *   dF_b[n, ch, i*k + j, h, w] = dy[n, b*c + ch, h, w] * x[n, ch, h + (i - r)*d_b, w + (j - r)*d_b]
+ *                                (0 where that pixel is outside the image)
+ *   dx[n, ch, sh, sw]          = sum over b, i, j of F_b[n, ch, i*k + j, h, w] * dy[n, b*c + ch, h, w]
+ *                                at (h, w) = (sh - (i - r)*d_b, sw - (j - r)*d_b) inside the image.
+ *   x, filters, dilations, nb, k   as for dynconv_multidil_fwd (all required)
+ *   dy         (n, nb*c, h, w)     gradient of the branch-concatenated output
+ *   dx         (n, c, h, w) or NULL: fully overwritten when non-NULL
+ *   dfilters   host array of nb device pointers, or NULL; dfilters[b] is
+ *              (n, c, k*k, h, w), fully overwritten, or NULL to skip branch b
+ * Each dx element is summed by one thread in a fixed order, so results are
+ * bitwise reproducible.  With dx NULL and no filter gradient requested the
+ * call validates its arguments, launches nothing and returns DW_OK.
+ */
+int dynconv_multidil_bwd(const void *x, const void *const *filters, const void *dy,
+                         const int32_t *dilations, int32_t nb, void *dx, void *const *dfilters,
+                         int64_t n, int64_t c, int64_t h, int64_t w, int64_t k,
+                         int dtype, void *stream);
+
+/*
  * Kernel family a call would launch for this geometry and dtype (for
  * profiling and per-shape tuning; the same decision the compute calls make).
  * pass: 0 = dwconv2d_fwd, 1 = dwconv2d_bwd_input, 2 = dwconv2d_bwd_weight.

@@ -152,6 +152,38 @@ def test_dynconv_validation():
     assert dyn(FAKE, f3, d3, 3, y, 0, 4, 8, 8, 3, 0, None) == -2
 
 
+@no_gpu
+def test_dynconv_bwd_validation():
+    L = N.lib()
+    f3 = (ctypes.c_void_p * 3)(FAKE + (1 << 24), FAKE + (2 << 24), FAKE + (3 << 24))
+    d3 = (ctypes.c_int32 * 3)(1, 3, 5)
+    dy = FAKE + (8 << 24)
+    dx = FAKE + (9 << 24)
+    g3 = (ctypes.c_void_p * 3)(FAKE + (10 << 24), FAKE + (11 << 24), FAKE + (12 << 24))
+    bwd = L.dynconv_multidil_bwd
+    geo = (1, 4, 8, 8, 3)
+    assert bwd(FAKE, f3, dy, d3, 3, dx, g3, *geo, 5, None) == -4              # dtype
+    assert bwd(FAKE, f3, dy, d3, 3, dx, g3, 1, 4, 8, 8, 2, 0, None) == -9     # even k
+    assert bwd(FAKE, f3, dy, d3, 0, dx, g3, *geo, 0, None) == -9              # nb = 0
+    bad = (ctypes.c_int32 * 3)(1, -3, 5)
+    assert bwd(FAKE, f3, dy, bad, 3, dx, g3, *geo, 0, None) == -9             # dilation < 1
+    assert bwd(FAKE, f3, None, d3, 3, dx, g3, *geo, 0, None) == -1            # null dy
+    assert bwd(None, f3, dy, d3, 3, dx, g3, *geo, 0, None) == -1              # null x
+    assert bwd(FAKE, f3, dy + 2, d3, 3, dx, g3, *geo, 0, None) == -1          # misaligned dy
+    assert bwd(FAKE, f3, dy, d3, 3, dx + 1, g3, *geo, 1, None) == -1          # misaligned dx (f16)
+    assert bwd(FAKE, f3, dy, d3, 3, FAKE, g3, *geo, 0, None) == -7            # dx aliases x
+    assert bwd(FAKE, f3, dy, d3, 3, dy, g3, *geo, 0, None) == -7              # dx aliases dy
+    assert bwd(FAKE, f3, dy, d3, 3, FAKE + (2 << 24), None, *geo, 0, None) == -7  # dx aliases a filter
+    galias = (ctypes.c_void_p * 3)(FAKE + (10 << 24), FAKE + (10 << 24) + 64, FAKE + (12 << 24))
+    assert bwd(FAKE, f3, dy, d3, 3, dx, galias, *geo, 0, None) == -7          # two filter gradients overlap
+    gx = (ctypes.c_void_p * 3)(None, dx, None)
+    assert bwd(FAKE, f3, dy, d3, 3, dx, gx, *geo, 0, None) == -7              # filter gradient aliases dx
+    assert bwd(FAKE, f3, dy, d3, 3, dx, g3, 0, 4, 8, 8, 3, 0, None) == -2     # n = 0
+    # nothing requested: validated, nothing launched (safe without a device)
+    none3 = (ctypes.c_void_p * 3)(None, None, None)
+    assert bwd(FAKE, f3, dy, d3, 3, None, None, *geo, 0, None) == 0
+    assert bwd(FAKE, f3, dy, d3, 3, None, none3, *geo, 0, None) == 0
+
 def test_binding_refuses_cpu_tensors():
     x = torch.zeros(1, 2, 5, 5)
     w = torch.zeros(2, 3, 3)

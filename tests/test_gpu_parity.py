@@ -148,6 +148,102 @@ def test_dynamic_shapes(shape, k, dils, dtype):
     check_dyn(x, fs, dils, "dynamic %s k%d %s %s" % (shape, k, dils, dtype))
 
 
+
+# ------------------------------------------------------------------ dynamic filter backward
+def check_dyn_bwd(x, fs, dy, dils, tag, need_dx=True, need_df=True, df_mask=None):
+    """dx and every requested dF_b against the oracle's chain rule; returns the device results."""
+    k = int(round(fs[0].shape[2] ** 0.5))
+    note(tag)
+    xd, fsd, dyd = x.to(DEV), [f.to(DEV) for f in fs], dy.to(DEV)
+    outs = None
+    if need_df and df_mask is not None:
+        outs = [torch.full_like(f, float("nan")) if m else None for f, m in zip(fsd, df_mask)]
+    dx, dfs = dc.dynconv_multidil_bwd(xd, fsd, dyd, dils, need_dx=need_dx, need_dfilters=need_df,
+                                      out_dfilters=outs)
+    torch.cuda.synchronize()
+    odx, odf = O.dynconv_multidil_bwd(x, fs, dy, dils)
+    if need_dx:
+        assert_close(dx, odx, len(dils) * k * k, x.dtype, tag + " dx")
+    else:
+        assert dx is None
+    if need_df:
+        for b, (g, o) in enumerate(zip(dfs, odf)):
+            if g is not None:
+                assert_close(g, o, 1, x.dtype, tag + " dF%d" % b)
+    return dx, dfs
+
+
+def dyn_bwd_inputs(n, c, h, w, k, dils, dtype, seed, fdist=("N", 0.0, 1.0 / 9)):
+    x, fs = dyn_inputs(n, c, h, w, k, dils, dtype, seed, fdist)
+    dy = synth.draw((n, len(dils) * c, h, w), ("N", 0.0, 1.0), seed, "dy", dtype)
+    return x, fs, dy
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("n,hw", [(1, 128), (2, 128), (1, 256)])
+def test_dynamic_bwd_workload(n, hw, dtype):
+    x, fs, dy = dyn_bwd_inputs(n, 4, hw, hw, 3, (1, 3, 5), DT[dtype], 420 + n + hw)
+    check_dyn_bwd(x, fs, dy, (1, 3, 5), "dynamic-bwd N%d H%d %s" % (n, hw, dtype))
+
+
+@pytest.mark.parametrize("shape,k,dils", [
+    ((1, 3, 37, 53), 3, (1, 3, 5)),     # ragged rows, width not a vector multiple: element paths
+    ((2, 2, 20, 16), 5, (1, 2)),        # k = 5 register path
+    ((2, 2, 13, 24), 5, (1, 3, 5)),     # k = 5, three branches, 16-bit strips of 8 fit 24
+    ((1, 2, 9, 130), 3, (2, 4, 6, 8)),  # four branches, halo wider than the image height
+    ((1, 1, 1, 1), 3, (1,)),            # single pixel
+    ((1, 2, 12, 12), 1, (1, 7)),        # k = 1
+    ((1, 2, 11, 14), 7, (3,)),          # runtime k
+    ((1, 2, 24, 64), 3, (1, 3, 5)),     # several row bands on the register path
+    ((1, 1, 40, 256), 3, (1, 3, 5)),    # one wave of strips per row
+    ((3, 2, 17, 40), 3, (1, 3, 5)),     # partial last band
+])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_dynamic_bwd_shapes(shape, k, dils, dtype):
+    x, fs, dy = dyn_bwd_inputs(*shape, k, dils, DT[dtype], 470 + sum(shape) + k,
+                               fdist=("N", 0.0, 1.0 / (k * k)))
+    check_dyn_bwd(x, fs, dy, dils, "dynamic-bwd %s k%d %s %s" % (shape, k, dils, dtype))
+
+
+@pytest.mark.parametrize("need_dx,need_df,mask", [
+    (True, False, None), (False, True, None), (True, True, (True, False, True)), (False, True, (False, True, False)),
+])
+def test_dynamic_bwd_partial_requests(need_dx, need_df, mask):
+    x, fs, dy = dyn_bwd_inputs(2, 3, 21, 32, 3, (1, 3, 5), torch.float32, 31)
+    dx, dfs = check_dyn_bwd(x, fs, dy, (1, 3, 5), "dynamic-bwd partial %s %s %s" % (need_dx, need_df, mask),
+                            need_dx, need_df, mask)
+    if mask is not None:
+        for g, m in zip(dfs, mask):
+            assert (g is not None) == m
+
+
+def test_dynamic_bwd_deterministic():
+    x, fs, dy = dyn_bwd_inputs(2, 4, 64, 64, 3, (1, 3, 5), torch.float32, 37)
+    xd, fsd, dyd = x.to(DEV), [f.to(DEV) for f in fs], dy.to(DEV)
+    note("dynamic-bwd determinism")
+    a = dc.dynconv_multidil_bwd(xd, fsd, dyd, (1, 3, 5))
+    b = dc.dynconv_multidil_bwd(xd, fsd, dyd, (1, 3, 5))
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0])
+    for g1, g2 in zip(a[1], b[1]):
+        assert torch.equal(g1, g2)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_dynamic_bwd_guard_bands(dtype):
+    margin = 64
+    n, c, h, w = 2, 3, 21, 24
+    x, fs, dy = dyn_bwd_inputs(n, c, h, w, 3, (1, 3, 5), DT[dtype], 41)
+    dxbuf, dx = _guarded((n, c, h, w), DT[dtype])
+    gb = [_guarded((n, c, 9, h, w), DT[dtype]) for _ in range(3)]
+    note("dynamic-bwd guard " + dtype)
+    dc.dynconv_multidil_bwd(x.to(DEV), [f.to(DEV) for f in fs], dy.to(DEV), (1, 3, 5), out_dx=dx,
+                            out_dfilters=[t for _, t in gb])
+    torch.cuda.synchronize()
+    for buf, t in [(dxbuf, dx)] + gb:
+        assert torch.isfinite(t).all(), "unwritten output element"
+        assert torch.all(buf[:margin] == 1024.0) and torch.all(buf[-margin:] == -2048.0), "guard band written"
+
 def fuzz_cases(count=48, seed=2024):
     r = random.Random(seed)
     out = []
@@ -323,6 +419,27 @@ def test_full_size_dynamic_sampled(dtype):
             got = torch.stack([y[nn, b * c + ch] for b in range(3)]).unsqueeze(0)
             assert_close(got, want, 9, DT[dtype], "dynamic-full n%d c%d" % (nn, ch))
 
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_full_size_dynamic_bwd_sampled(dtype):
+    D = synth.DYNAMIC
+    n, c, hw = 2, D["c"], 256
+    x = synth.draw((n, c, hw, hw), D["x"], 960, "x", DT[dtype], device=DEV)
+    fs = [synth.draw((n, c, 9, hw, hw), D["f"], 960, "f%d" % i, DT[dtype], device=DEV) for i in range(3)]
+    dy = synth.draw((n, 3 * c, hw, hw), D["dy"], 960, "dy", DT[dtype], device=DEV)
+    note("dynamic-bwd-full " + dtype)
+    dx, dfs = dc.dynconv_multidil_bwd(x, fs, dy, D["dilations"])
+    torch.cuda.synchronize()
+    for nn in range(n):
+        for ch in _sample_idx(c, 3, 961):
+            sl = lambda t: t[nn:nn + 1, ch:ch + 1].cpu()
+            dys = torch.stack([dy[nn, b * c + ch] for b in range(3)]).unsqueeze(0).cpu()
+            odx, odf = O.dynconv_multidil_bwd(sl(x), [sl(f) for f in fs], dys, D["dilations"])
+            assert_close(dx[nn:nn + 1, ch:ch + 1], odx, 27, DT[dtype], "dynamic-bwd-full dx n%d c%d" % (nn, ch))
+            for b in range(3):
+                assert_close(dfs[b][nn:nn + 1, ch:ch + 1], odf[b], 1, DT[dtype],
+                             "dynamic-bwd-full dF%d n%d c%d" % (b, nn, ch))
 
 # ------------------------------------------------------------------ streaming 3x3 path edges
 @pytest.mark.parametrize("n,c,h,w,mult,s,dt", [
