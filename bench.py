@@ -301,9 +301,11 @@ def cpu_baseline(wl, target_s):
         val, unit = u1 / t1 / 1e9, "GB/s"
     else:
         val, unit = u1 / t1 / 1e9, "GFLOP/s"
+    used = max(min(ns, t["x"].shape[0]) for _c, t in wl["per_case"])
+    whole = all(min(ns, t["x"].shape[0]) == t["x"].shape[0] for _c, t in wl["per_case"])
+    what = "every case's whole batch" if whole else "first %d image(s) of every case's batch" % used
     return {"value": round(val, 4), "unit": unit, "cores": O.num_threads(), "kind": "oracle",
-            "sample": "first %d image(s) of every case's batch, every pass, same host tensors; %.1f s of oracle time"
-                      % (ns, t1)}
+            "sample": "%s, every pass, same host tensors; %.1f s of oracle time" % (what, t1)}
 
 
 # ---------------------------------------------------------------- traffic from committed counters

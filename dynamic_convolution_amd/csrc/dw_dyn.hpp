@@ -33,28 +33,6 @@ __device__ __forceinline__ void load_strip(const T *p, float *v, int valid, bool
     }
 }
 
-// The same strip as raw bits (16-bit elements packed two per word, element 0
-// low), so a caller can keep the load in flight and convert later.
-template <typename T, int RW>
-__device__ __forceinline__ u32x4 load_raw(const T *p, int valid, bool vec) {
-    static_assert(sizeof(T) * RW == 16, "strip is one 16-byte vector");
-    if (vec && valid >= RW) return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
-    uint32_t wd[4] = {0u, 0u, 0u, 0u};
-    if constexpr (sizeof(T) == 4) {
-        const uint32_t *s = reinterpret_cast<const uint32_t *>(p);
-#pragma unroll
-        for (int q = 0; q < RW; ++q)
-            if (q < valid) wd[q] = s[q];
-    } else {
-        const uint16_t *s = reinterpret_cast<const uint16_t *>(p);
-#pragma unroll
-        for (int q = 0; q < RW; ++q)
-            if (q < valid) wd[q >> 1] |= static_cast<uint32_t>(s[q]) << ((q & 1) * 16);
-    }
-    u32x4 r = {wd[0], wd[1], wd[2], wd[3]};
-    return r;
-}
-
 template <typename T, int RW>
 __device__ __forceinline__ void store_strip(T *p, const float *acc, int valid, bool vec) {
     if (vec && valid >= RW) {
@@ -180,14 +158,14 @@ __device__ __forceinline__ void stage_rows_f32(float *xs, const T *src, int rbas
 }
 
 // Row bands over the planes of one (n, c) grid: band height BH so that each
-// thread gets about two strips, the tile (BH + 2*halo rows) within the LDS
-// budget, and >= 1024 workgroups when the problem allows.
+// thread gets about `per_thread` strips, the tile (BH + 2*halo rows) within
+// the LDS budget, and >= 1024 workgroups when the problem allows.
 struct DynPlan {
     int BH, nbands, lds_bytes;
 };
 
 template <typename T>
-bool plan_dyn(int n, int c, int h, int w, int k, int maxdil, DynPlan &p) {
+bool plan_dyn(int n, int c, int h, int w, int k, int maxdil, DynPlan &p, int per_thread = 2) {
     constexpr int RW = Vec<T>::N;
     const int NS = (w + RW - 1) / RW;
     const int halo = (k - 1) / 2 * maxdil;
@@ -201,7 +179,7 @@ bool plan_dyn(int n, int c, int h, int w, int k, int maxdil, DynPlan &p) {
     };
     const int lim = bytes(1) <= kLdsPref ? kLdsPref : kLdsCap;
     if (bytes(1) > lim) return false;
-    int bh = std::max(1, (2 * kThreads + NS - 1) / NS);
+    int bh = std::max(1, (per_thread * kThreads + NS - 1) / NS);
     bh = std::min(bh, h);
     while (bh > 1 && bytes(bh) > lim) --bh;
     const int64_t planes = static_cast<int64_t>(n) * c;

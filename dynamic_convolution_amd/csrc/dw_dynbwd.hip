@@ -121,15 +121,20 @@ __device__ __forceinline__ void zero_pad_columns(float *gs, int nrows, int w, in
     }
 }
 
-// Fast path: k = K_ at compile time, every strip a whole 16-byte vector, one
-// strip per thread per pair (BH * NS <= kThreads).  The loads of pair p + 1
-// are issued (from a clamped, always valid row, so they sit behind no branch)
-// before pair p is summed, then multiplied and written to the other buffer.
-template <typename T, int K_, int RW>
+// Fast path: k = K_ and the branch count NB_ at compile time, every strip a
+// whole 16-byte vector, one strip per thread per pair (BH * NS <= kThreads).
+// The pair loop is fully unrolled and free of branches around loads and LDS
+// writes (idle lanes repeat the last live lane's strip, writing the same
+// values to the same place), so the compiler tracks every load exactly: the
+// loads of pairs p + 1 and p + 2 stay in flight (issued from a clamped,
+// always valid row) while pair p is summed, and pair p + 1 is then
+// multiplied and written to the other buffer.
+template <typename T, int K_, int RW, int NB_>
 __global__ __launch_bounds__(kThreads) void dynbwd_input_kernel(DynBwdArgs<T> a) {
     extern __shared__ __align__(16) float gs[];
     constexpr int rr = (K_ - 1) / 2;
     constexpr int KK = K_ * K_;
+    constexpr int NP = NB_ * K_;  // (branch, tap row) pairs
     const int tid = threadIdx.x;
     const int plane = blockIdx.x / a.nbands;
     const int band = blockIdx.x - plane * a.nbands;
@@ -145,66 +150,74 @@ __global__ __launch_bounds__(kThreads) void dynbwd_input_kernel(DynBwdArgs<T> a)
     zero_pad_columns(gs, 2 * K_ * a.BH, a.w, LW, hp, a.fPAD, tid);
 
     const int items = a.BH * a.NS;
-    const bool live = tid < items;
-    const int u = live ? tid : items - 1;
+    const int u = min(tid, items - 1);
     const int row = static_cast<int>(fdiv(static_cast<uint32_t>(u), a.fNS));
     const int w0 = (u - row * a.NS) * RW;
-    const bool mine = live && h0 + row < h1;  // this thread owns dx strip (h0 + row, w0)
-    const int npairs = a.nb * K_;
+    const bool mine = tid < items && h0 + row < h1;  // this thread owns dx strip (h0 + row, w0)
 
-    u32x4 rg, rf[K_];
-    bool src_in = false;
-    auto issue = [&](int p) {
+    // one pair's loads: dy and the K filter strips of tap row i on the source row
+    struct Pend {
+        u32x4 g, f[K_];
+        bool in;
+    };
+    auto issue = [&](int p, Pend &r) {
         const int b = p / K_;
         const int i = p - b * K_;
         const int sr = h0 + row - (i - rr) * a.dil[b];
-        src_in = sr >= 0 && sr < a.h;
+        r.in = sr >= 0 && sr < a.h;
         const int64_t pix = static_cast<int64_t>(min(max(sr, 0), a.h - 1)) * a.w + w0;
-        rg = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
-            a.dy + (static_cast<int64_t>(nn * a.nb + b) * a.c + ch) * hw + pix));
+        r.g = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+            a.dy + (static_cast<int64_t>(nn * NB_ + b) * a.c + ch) * hw + pix));
         const T *fb = a.f[b] + (static_cast<int64_t>(plane) * KK + i * K_) * hw + pix;
 #pragma unroll
         for (int j = 0; j < K_; ++j)
-            rf[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(fb + static_cast<int64_t>(j) * hw));
+            r.f[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(fb + static_cast<int64_t>(j) * hw));
     };
-    auto put = [&](int p) {
-        if (!live) return;
+    auto put = [&](int p, const Pend &r) {
         float g[RW];
-        strip_values<T, RW>(rg, g);
+        strip_values<T, RW>(r.g, g);
+        const float m = r.in ? 1.f : 0.f;  // source row outside the image: the pair adds nothing
+#pragma unroll
+        for (int q = 0; q < RW; ++q) g[q] *= m;
         float *dst = gs + (p & 1) * bufsz + row * LW + hp + w0;
 #pragma unroll
         for (int j = 0; j < K_; ++j) {
             float fv[RW];
-            strip_values<T, RW>(rf[j], fv);
+            strip_values<T, RW>(r.f[j], fv);
 #pragma unroll
             for (int q = 0; q < RW; q += 4)
                 *reinterpret_cast<float4 *>(dst + j * slab + q) =
-                    src_in ? make_float4(fv[q] * g[q], fv[q + 1] * g[q + 1], fv[q + 2] * g[q + 2],
-                                         fv[q + 3] * g[q + 3])
-                           : make_float4(0.f, 0.f, 0.f, 0.f);
+                    make_float4(fv[q] * g[q], fv[q + 1] * g[q + 1], fv[q + 2] * g[q + 2], fv[q + 3] * g[q + 3]);
         }
     };
 
     float acc[RW];
 #pragma unroll
     for (int q = 0; q < RW; ++q) acc[q] = 0.f;
-
-    issue(0);
-    put(0);
-    __syncthreads();
-    for (int p = 0; p < npairs; ++p) {
-        if (p + 1 < npairs) issue(p + 1);
-        if (mine) {
-            const int d = a.dil[p / K_];
-            const float *src = gs + (p & 1) * bufsz + row * LW + hp + w0;
+    auto sum = [&](int p) {
+        const int d = a.dil[p / K_];
+        const float *src = gs + (p & 1) * bufsz + row * LW + hp + w0;
 #pragma unroll
-            for (int j = 0; j < K_; ++j) {
-                const float *sp = src + j * slab - (j - rr) * d;
+        for (int j = 0; j < K_; ++j) {
+            const float *sp = src + j * slab - (j - rr) * d;
 #pragma unroll
-                for (int q = 0; q < RW; ++q) acc[q] += sp[q];
-            }
+            for (int q = 0; q < RW; ++q) acc[q] += sp[q];
         }
-        if (p + 1 < npairs) put(p + 1);
+    };
+
+    Pend P[NP];
+    issue(0, P[0]);
+    if constexpr (NP > 1) issue(1, P[1]);
+    put(0, P[0]);
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        if (p + 2 < NP) issue(p + 2, P[p + 2]);
+        // all of pair p + 2's loads ahead of pair p + 1's uses: the in-order
+        // load counter then lets the waits for p + 1 leave them in flight
+        __builtin_amdgcn_sched_barrier(0);
+        sum(p);
+        if (p + 1 < NP) put(p + 1, P[p + 1]);
         __syncthreads();
     }
     if (mine) store_strip<T, RW>(a.dx + static_cast<int64_t>(plane) * hw + static_cast<int64_t>(h0 + row) * a.w + w0,
@@ -343,6 +356,16 @@ bool plan_dynbwd_input(int n, int c, int h, int w, int k, int maxdil, bool vf, I
     return true;
 }
 
+template <typename T, int K_, int RW>
+void launch_input_fast(int nb, dim3 grid, int lds, hipStream_t s, const DynBwdArgs<T> &g) {
+    switch (nb) {
+        case 1: hipLaunchKernelGGL((dynbwd_input_kernel<T, K_, RW, 1>), grid, dim3(kThreads), lds, s, g); break;
+        case 2: hipLaunchKernelGGL((dynbwd_input_kernel<T, K_, RW, 2>), grid, dim3(kThreads), lds, s, g); break;
+        case 3: hipLaunchKernelGGL((dynbwd_input_kernel<T, K_, RW, 3>), grid, dim3(kThreads), lds, s, g); break;
+        default: hipLaunchKernelGGL((dynbwd_input_kernel<T, K_, RW, 4>), grid, dim3(kThreads), lds, s, g); break;
+    }
+}
+
 template <typename T>
 int run_dynbwd(const void *x, const void *const *filters, const void *dy, const int32_t *dil, int nb, void *dx,
                void *const *dfilters, int n, int c, int h, int w, int k, hipStream_t s) {
@@ -381,7 +404,7 @@ int run_dynbwd(const void *x, const void *const *filters, const void *dy, const 
 
     if (want_df) {
         DynPlan p;
-        if (!plan_dyn<T>(n, c, h, w, k, maxdil, p)) return kErrUnsupported;
+        if (!plan_dyn<T>(n, c, h, w, k, maxdil, p, 1)) return kErrUnsupported;
         DynBwdArgs<T> f = a;
         f.BH = p.BH;
         f.nbands = p.nbands;
@@ -413,9 +436,9 @@ int run_dynbwd(const void *x, const void *const *filters, const void *dy, const 
         g.fPAD = make_fastdiv(a.LW - w, static_cast<uint64_t>(nrows) * (a.LW - w));
         const dim3 grid(static_cast<unsigned>(planes * p.nbands));
         if (p.fast && k == 3)
-            hipLaunchKernelGGL((dynbwd_input_kernel<T, 3, RW>), grid, dim3(kThreads), p.lds_bytes, s, g);
+            launch_input_fast<T, 3, RW>(nb, grid, p.lds_bytes, s, g);
         else if (p.fast)
-            hipLaunchKernelGGL((dynbwd_input_kernel<T, 5, RW>), grid, dim3(kThreads), p.lds_bytes, s, g);
+            launch_input_fast<T, 5, RW>(nb, grid, p.lds_bytes, s, g);
         else
             hipLaunchKernelGGL((dynbwd_input_generic_kernel<T, RW>), grid, dim3(kThreads), p.lds_bytes, s, g);
         if (hipGetLastError() != hipSuccess) return kErrHip;
