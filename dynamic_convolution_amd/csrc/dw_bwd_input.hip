@@ -238,13 +238,14 @@ int run_bwd_input(const Geo &g, const BandPlan &bp, int seg_slots, const void *d
     return hipGetLastError() == hipSuccess ? kOk : kErrHip;
 }
 
-enum BinAlgo { kBinRowwalk = 0, kBinLargek, kBinDecim, kBinBand33s1, kBinBand33s2, kBinBand55s1, kBinBand55s2d2, kBinBandGeneric, kBinChannelGroup };
+enum BinAlgo { kBinRowwalk = 0, kBinLargek, kBinDecim, kBinBand33s1, kBinBand33s2, kBinBand55s1, kBinBand55s2d2, kBinBandGeneric, kBinChannelGroup, kBinLargekMfma };
 
 // The kernel family a grad-input call launches.
 int select_bwd_input(const Geo &g, int dt) {
     if (decim_fits(g, 1)) return kBinDecim;
     if (small_bwd_input_fits(g, dt)) return kBinChannelGroup;
     if (rowwalk_fits(g, dt, 1)) return kBinRowwalk;
+    if (largek_mfma_fits(g, 1, dt)) return kBinLargekMfma;
     if (largek_fits(g, 1)) return kBinLargek;
     const bool sq = g.kh == g.kw && g.sh == g.sw && g.dh == g.dw;
     if (sq && g.kh == 3 && g.sh == 1 && g.dh == 1) return kBinBand33s1;
@@ -260,6 +261,7 @@ int dispatch_bwd_input(const Geo &g, const void *dy, const void *w, void *dx, hi
     const int algo = select_bwd_input(g, dt);
     if (algo == kBinRowwalk) return rowwalk_bwd_input(g, dy, w, dx, dt, s);
     if (algo == kBinLargek) return largek_bwd_input(g, dy, w, dx, dt, s);
+    if (algo == kBinLargekMfma) return largek_mfma_bwd_input(g, dy, w, dx, dt, s);
     if (algo == kBinDecim) return decim_bwd_input(g, dy, w, dx, dt, s);
     if (algo == kBinChannelGroup) return small_bwd_input(g, dy, w, dx, dt, s);
     BandPlan bp;
@@ -278,12 +280,14 @@ int dispatch_bwd_input(const Geo &g, const void *dy, const void *w, void *dx, hi
 
 const char *bwd_input_algo_name(const Geo &g, int dtype) {
     static const char *names[] = {"rowwalk_3x3",    "largek_regtile", "decimated_s2d2", "band_3x3_s1",   "band_3x3_s2",
-                                  "band_5x5_s1",    "band_5x5_s2_d2", "band_generic", "channelgroup_small"};
+                                  "band_5x5_s1",    "band_5x5_s2_d2", "band_generic", "channelgroup_small",
+                                  "largek_mfma"};
     return names[select_bwd_input(g, dtype)];
 }
 
 bool bwd_input_supported(const Geo &g, int dtype) {
-    if (small_bwd_input_fits(g, dtype) || rowwalk_fits(g, dtype, 1) || largek_fits(g, 1) || decim_fits(g, 1))
+    if (small_bwd_input_fits(g, dtype) || rowwalk_fits(g, dtype, 1) || largek_mfma_fits(g, 1, dtype) ||
+        largek_fits(g, 1) || decim_fits(g, 1))
         return true;
     BandPlan bp;
     int ss;

@@ -238,12 +238,13 @@ int run_fwd(const Geo &g, const BandPlan &bp, const void *x, const void *w, cons
     return hipGetLastError() == hipSuccess ? kOk : kErrHip;
 }
 
-enum FwdAlgo { kFwdRowwalk = 0, kFwdLargek, kFwdDecim, kFwdBand33s1, kFwdBand33s2, kFwdBand55s1, kFwdBand55s2d2, kFwdBandGeneric, kFwdChannelGroup };
+enum FwdAlgo { kFwdRowwalk = 0, kFwdLargek, kFwdDecim, kFwdBand33s1, kFwdBand33s2, kFwdBand55s1, kFwdBand55s2d2, kFwdBandGeneric, kFwdChannelGroup, kFwdLargekMfma };
 
 // The kernel family a forward call launches (the dispatcher and the
 // introspection helper both use this one decision).
 int select_fwd(const Geo &g, int dt) {
     if (rowwalk_fits(g, dt, 0)) return kFwdRowwalk;
+    if (largek_mfma_fits(g, 0, dt)) return kFwdLargekMfma;
     if (largek_fits(g, 0)) return kFwdLargek;
     if (decim_fits(g, 0)) return kFwdDecim;
     if (small_fwd_fits(g, dt)) return kFwdChannelGroup;
@@ -261,6 +262,7 @@ int dispatch_fwd(const Geo &g, const void *x, const void *w, const void *b, void
     const int algo = select_fwd(g, dt);
     if (algo == kFwdRowwalk) return rowwalk_fwd(g, x, w, b, y, dt, s);
     if (algo == kFwdLargek) return largek_fwd(g, x, w, b, y, dt, s);
+    if (algo == kFwdLargekMfma) return largek_mfma_fwd(g, x, w, b, y, dt, s);
     if (algo == kFwdDecim) return decim_fwd(g, x, w, b, y, dt, s);
     if (algo == kFwdChannelGroup) return small_fwd(g, x, w, b, y, dt, s);
     BandPlan bp;
@@ -278,12 +280,15 @@ int dispatch_fwd(const Geo &g, const void *x, const void *w, const void *b, void
 
 const char *fwd_algo_name(const Geo &g, int dtype) {
     static const char *names[] = {"rowwalk_3x3",    "largek_regtile", "decimated_s2d2", "band_3x3_s1",   "band_3x3_s2",
-                                  "band_5x5_s1",    "band_5x5_s2_d2", "band_generic", "channelgroup_small"};
+                                  "band_5x5_s1",    "band_5x5_s2_d2", "band_generic", "channelgroup_small",
+                                  "largek_mfma"};
     return names[select_fwd(g, dtype)];
 }
 
 bool fwd_supported(const Geo &g, int dtype) {
-    if (rowwalk_fits(g, dtype, 0) || largek_fits(g, 0) || decim_fits(g, 0) || small_fwd_fits(g, dtype)) return true;
+    if (rowwalk_fits(g, dtype, 0) || largek_mfma_fits(g, 0, dtype) || largek_fits(g, 0) || decim_fits(g, 0) ||
+        small_fwd_fits(g, dtype))
+        return true;
     BandPlan bp;
     switch (dtype) {
         case 0: return plan_fwd<float>(g, bp);

@@ -72,6 +72,13 @@ bool largek_bwdw_fits(const Geo &g);
 int largek_bwd_weight_chunks(const Geo &g);
 int largek_bwd_weight(const Geo &g, const void *x, const void *dy, void *ws, int dtype, hipStream_t s);
 
+// Large kernels (k = 7, 13, 31; stride 1, dilation 1) with 16-bit I/O on the
+// matrix cores, planes of at most 64 x 64 outputs (dw_largek_mfma.hip).
+// pass: 0 forward, 1 grad-input.
+bool largek_mfma_fits(const Geo &g, int pass, int dtype);
+int largek_mfma_fwd(const Geo &g, const void *x, const void *w, const void *b, void *y, int dtype, hipStream_t s);
+int largek_mfma_bwd_input(const Geo &g, const void *dy, const void *w, void *dx, int dtype, hipStream_t s);
+
 // Stride 2, dilation 2, pad k-1 (k = 3, 5) as stride-1 passes on the even grid (dw_decim.hip).
 bool decim_fits(const Geo &g, int pass);
 int decim_fwd(const Geo &g, const void *x, const void *w, const void *b, void *y, int dtype, hipStream_t s);

@@ -1,0 +1,326 @@
+// dw_largek_mfma.hip -- large-kernel depthwise forward and grad-input for
+// 16-bit I/O on the gfx950 matrix cores (k = 7, 13, 31; stride 1, dilation 1;
+// planes of at most 64 x 64 outputs).
+//
+// The MegEngine large-kernel depthwise article turns depthwise convolution
+// into an implicit batched GEMM (section on ImplicitBatchedGEMM) and notes
+// that its flop inflation shrinks as the kernel grows toward the input size.
+// Here the GEMM is built per plane from one kernel row at a time: with
+// zero-padded input rows X[r] (r = oh + i) the output tile is
+//   y[oh][ow] = sum_i sum_c T_i[ow][c] * X[oh + i][c],
+//   T_i[ow][c] = w[i][c - ow]   (0 <= c - ow < k, else 0),
+// a banded Toeplitz matrix of filter row i.  A 32 x 32 output tile reads the
+// 32 + k - 1 input columns of its window, padded to KP = 16 * KPS, so the
+// matrix cores do KP / k times the useful multiply-adds (2.06x at k = 31)
+// at 16x the fp32 vector rate.  Products of 16-bit values are exact and the
+// sums are fp32 (v_mfma_f32_32x32x16_{f16,bf16}).
+//
+// Roles in D = A * B (M = 32 output columns, N = 32 output rows, K = 16
+// window columns per instruction):
+//   A[m][kk] = T_i[m][kk]: lane l reads the 8 filter values
+//              w[i][16 s + 8 (l / 32) + e - l % 32], e < 8, from a zero-padded
+//              copy of filter row i in LDS (two copies shifted by one element,
+//              so every run of 8 starts on a 4-byte boundary);
+//   B[kk][n] = X[32 mt + n + i][32 nt + 16 s + kk]: lane l reads 8 adjacent
+//              columns of input row 32 mt + l % 32 + i -- one aligned 16-byte
+//              LDS read;
+//   D: register r of lane l is output (32 mt + l % 32, 32 nt + 8 (r / 4)
+//      + 4 (l / 32) + r % 4), so a lane stores runs of 4 adjacent outputs.
+// A workgroup serves one channel and one image per wave (4 waves, or 2 where
+// four input tiles would not fit 64 KiB of LDS): the filter table is built
+// once, each wave stages its own image's zero-padded plane in LDS and
+// accumulates its 2 x 2 (or fewer) output tiles over the k kernel rows.
+// Grad-input is the same correlation of dy with the filter flipped in both
+// axes and padding k - 1 - pad.
+#include "dw_common.hpp"
+#include "dw_internal.hpp"
+
+namespace dw {
+namespace {
+
+typedef _Float16 f16x8_v __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_v __attribute__((ext_vector_type(8)));
+typedef float f32x16_v __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4_v __attribute__((ext_vector_type(4)));
+
+constexpr int kZoff = 31;  // zero columns left of a filter row in the table (largest tile column)
+
+template <typename T> struct Mfma;
+template <> struct Mfma<__half> {
+    static __device__ __forceinline__ f32x16_v run(u32x4_v a, u32x4_v b, f32x16_v c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_v, a), __builtin_bit_cast(f16x8_v, b),
+                                                      c, 0, 0, 0);
+    }
+};
+template <> struct Mfma<bf16_t> {
+    static __device__ __forceinline__ f32x16_v run(u32x4_v a, u32x4_v b, f32x16_v c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_v, a),
+                                                       __builtin_bit_cast(bf16x8_v, b), c, 0, 0, 0);
+    }
+};
+
+template <typename T> struct LkmArgs {
+    const T *in;   // forward: x; grad-input: dy
+    const T *w;
+    const T *b;    // bias (forward) or NULL
+    T *out;        // y or dx
+    int N;         // images
+    int IH, IW;    // input plane of this pass
+    int OH, OW;    // output plane of this pass
+    int P;         // top/left zero padding of this pass
+    int C;         // output channels of this pass (planes per image)
+    int Cin;       // input channels of this pass
+    int mult;      // output channels per input channel
+    int ngroups;   // image groups (one image per wave of a workgroup)
+    int vin;       // input rows are whole 16-byte vectors (and aligned)
+    int vout;      // output rows are whole 4-element runs (and 8-byte aligned)
+};
+
+// LDS geometry of one (K, KPS, MT, NT) instance: the filter table plus one
+// input tile per wave, as many waves (up to 4) as fit the LDS budget.
+template <int K, int KPS, int MT, int NT> struct LkmGeo {
+    static constexpr int QD = 8 * KPS + 20;              // dwords per copy of a filter row (even)
+    static constexpr int XR = 32 * MT + K - 1;           // staged input rows
+    static constexpr int XC = 32 * (NT - 1) + 16 * KPS;  // staged input columns
+    static constexpr int XP = XC + 8;                    // row pitch (halves): an odd multiple of 16 bytes mod 32
+    static constexpr int table_bytes = 2 * K * QD * 4;
+    static constexpr int tile_halves = XR * XP;
+    static constexpr int WPG = (kLdsCap - table_bytes) / (tile_halves * 2) >= 4 ? 4 : 2;
+    static constexpr int lds_bytes = table_bytes + WPG * tile_halves * 2;
+    static_assert(lds_bytes <= kLdsCap, "tiles of two waves exceed the LDS budget");
+};
+
+template <typename T, int K, int KPS, int MT, int NT, bool FLIP>
+__global__ __launch_bounds__(256) void lk_mfma_kernel(LkmArgs<T> a) {
+    using G = LkmGeo<K, KPS, MT, NT>;
+    extern __shared__ __align__(16) unsigned char smem[];
+    uint32_t *wtab = reinterpret_cast<uint32_t *>(smem);  // [copy][i][QD]
+    uint16_t *tiles = reinterpret_cast<uint16_t *>(smem + G::table_bytes);
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int c = blockIdx.x / a.ngroups;  // output plane channel of this pass
+    const int n = (blockIdx.x - c * a.ngroups) * G::WPG + wave;
+    const bool active = n < a.N;
+
+    // 1. filter table: copy q (0, 1) of row i holds, in dword d, the 16-bit
+    //    values of padded positions 2d + q and 2d + q + 1, where padded
+    //    position p is w[i][p - kZoff] (flipped for grad-input), 0 outside.
+    const uint16_t *wr = reinterpret_cast<const uint16_t *>(a.w) + static_cast<int64_t>(c) * K * K;
+    for (int e = tid; e < 2 * K * G::QD; e += 64 * G::WPG) {
+        const int q = e / (K * G::QD);
+        const int rem = e - q * K * G::QD;
+        const int i = rem / G::QD;
+        const int d = rem - i * G::QD;
+        uint32_t v = 0;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int j = 2 * d + q + u - kZoff;
+            if (j >= 0 && j < K) {
+                const uint16_t bits = FLIP ? wr[(K - 1 - i) * K + (K - 1 - j)] : wr[i * K + j];
+                v |= static_cast<uint32_t>(bits) << (16 * u);
+            }
+        }
+        wtab[e] = v;
+    }
+
+    // 2. this wave's padded input plane: tile[r][col] = in[r - P][col - P], 0 outside
+    uint16_t *xt = tiles + wave * G::tile_halves;
+    {
+        uint4 *z = reinterpret_cast<uint4 *>(xt);
+        for (int e = lane; e < G::tile_halves / 8; e += 64) z[e] = make_uint4(0u, 0u, 0u, 0u);
+        if (active) {
+            const int cin = FLIP ? c : c / a.mult;
+            const uint16_t *src =
+                reinterpret_cast<const uint16_t *>(a.in) + (static_cast<int64_t>(n) * a.Cin + cin) * a.IH * a.IW;
+            if (a.vin) {
+                const int vpr = a.IW / 8;
+                const int nvec = a.IH * vpr;
+                for (int v = lane; v < nvec; v += 64) {
+                    const int r = v / vpr;
+                    const int c8 = (v - r * vpr) * 8;
+                    const uint4 raw = *reinterpret_cast<const uint4 *>(src + static_cast<int64_t>(r) * a.IW + c8);
+                    uint16_t *d = xt + (r + a.P) * G::XP + c8 + a.P;
+                    const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) d[e] = static_cast<uint16_t>(wd[e >> 1] >> ((e & 1) * 16));
+                }
+            } else {
+                for (int e = lane; e < a.IH * a.IW; e += 64) {
+                    const int r = e / a.IW;
+                    const int col = e - r * a.IW;
+                    xt[(r + a.P) * G::XP + col + a.P] = src[e];
+                }
+            }
+        }
+    }
+    __syncthreads();
+    if (!active) return;
+
+    // 3. k kernel rows x KPS window steps x (MT x NT) tiles of MFMAs
+    const int m = lane & 31;
+    const int h = lane >> 5;
+    f32x16_v acc[MT][NT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[mt][nt][r] = 0.f;
+
+#pragma unroll 1
+    for (int i = 0; i < K; ++i) {
+        u32x4_v af[KPS];
+#pragma unroll
+        for (int s = 0; s < KPS; ++s) {
+            const int t = 16 * s + 8 * h - m + kZoff;  // first padded position of this lane's run
+            const int q = t & 1;
+            const uint32_t *p = wtab + (q * K + i) * G::QD + ((t - q) >> 1);
+            af[s] = u32x4_v{p[0], p[1], p[2], p[3]};
+        }
+#pragma unroll
+        for (int sp = 0; sp < KPS + 2 * (NT - 1); ++sp) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const u32x4_v bf = *reinterpret_cast<const u32x4_v *>(xt + (32 * mt + m + i) * G::XP + 16 * sp + 8 * h);
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    const int s = sp - 2 * nt;
+                    if (s >= 0 && s < KPS) acc[mt][nt] = Mfma<T>::run(af[s], bf, acc[mt][nt]);
+                }
+            }
+        }
+    }
+
+    // 4. store: lane holds, per tile and r4, outputs (32 mt + m, 32 nt + 8 r4 + 4 h + 0..3)
+    const float bias = (!FLIP && a.b) ? to_f32(a.b[c]) : 0.f;
+    T *op = a.out + (static_cast<int64_t>(n) * a.C + c) * a.OH * a.OW;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int oh = 32 * mt + m;
+        if (oh >= a.OH) continue;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int ow = 32 * nt + 8 * r4 + 4 * h;
+                const float v0 = acc[mt][nt][4 * r4] + bias, v1 = acc[mt][nt][4 * r4 + 1] + bias;
+                const float v2 = acc[mt][nt][4 * r4 + 2] + bias, v3 = acc[mt][nt][4 * r4 + 3] + bias;
+                T *dst = op + oh * a.OW + ow;
+                if (a.vout && ow + 4 <= a.OW) {
+                    *reinterpret_cast<uint2 *>(dst) = make_uint2(pack2<T>(v0, v1), pack2<T>(v2, v3));
+                } else {
+                    const float vv[4] = {v0, v1, v2, v3};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        if (ow + q < a.OW) dst[q] = from_f32<T>(vv[q]);
+                }
+            }
+    }
+}
+
+// Window steps of 16 columns a 32-column output tile needs: 32 + K - 1 columns.
+constexpr int kps_of(int K) { return (32 + K - 1 + 15) / 16; }
+
+template <typename T, int K, bool FLIP, int MT, int NT>
+int run_lkm_t(const LkmArgs<T> &a, hipStream_t s) {
+    constexpr int KPS = kps_of(K);
+    using G = LkmGeo<K, KPS, MT, NT>;
+    LkmArgs<T> b = a;
+    b.ngroups = (a.N + G::WPG - 1) / G::WPG;
+    const dim3 grid(static_cast<unsigned>(a.C * b.ngroups));
+    hipLaunchKernelGGL((lk_mfma_kernel<T, K, KPS, MT, NT, FLIP>), grid, dim3(64 * G::WPG), G::lds_bytes, s, b);
+    return hipGetLastError() == hipSuccess ? kOk : kErrHip;
+}
+
+template <typename T, int K, bool FLIP>
+int run_lkm_k(const LkmArgs<T> &a, hipStream_t s) {
+    const int MT = (a.OH + 31) / 32, NT = (a.OW + 31) / 32;
+    if (MT == 1 && NT == 1) return run_lkm_t<T, K, FLIP, 1, 1>(a, s);
+    if (MT == 1) return run_lkm_t<T, K, FLIP, 1, 2>(a, s);
+    if (NT == 1) return run_lkm_t<T, K, FLIP, 2, 1>(a, s);
+    return run_lkm_t<T, K, FLIP, 2, 2>(a, s);
+}
+
+template <typename T, bool FLIP>
+int run_lkm(const LkmArgs<T> &a, int K, hipStream_t s) {
+    if (K == 7) return run_lkm_k<T, 7, FLIP>(a, s);
+    if (K == 13) return run_lkm_k<T, 13, FLIP>(a, s);
+    return run_lkm_k<T, 31, FLIP>(a, s);
+}
+
+template <typename T>
+void fill_io(LkmArgs<T> &a) {
+    a.vin = a.IW % 8 == 0 && reinterpret_cast<uintptr_t>(a.in) % 16 == 0;
+    a.vout = a.OW % 4 == 0 && reinterpret_cast<uintptr_t>(a.out) % 8 == 0;
+}
+
+template <typename T>
+int lkm_fwd_t(const Geo &g, const void *x, const void *w, const void *b, void *y, hipStream_t s) {
+    LkmArgs<T> a{};
+    a.in = static_cast<const T *>(x);
+    a.w = static_cast<const T *>(w);
+    a.b = static_cast<const T *>(b);
+    a.out = static_cast<T *>(y);
+    a.N = g.n;
+    a.IH = g.ih;
+    a.IW = g.iw;
+    a.OH = g.oh;
+    a.OW = g.ow;
+    a.P = g.ph;
+    a.C = g.oc;
+    a.Cin = g.ic;
+    a.mult = g.mult;
+    fill_io(a);
+    return run_lkm<T, false>(a, g.kh, s);
+}
+
+template <typename T>
+int lkm_bwdin_t(const Geo &g, const void *dy, const void *w, void *dx, hipStream_t s) {
+    LkmArgs<T> a{};
+    a.in = static_cast<const T *>(dy);
+    a.w = static_cast<const T *>(w);
+    a.out = static_cast<T *>(dx);
+    a.N = g.n;
+    a.IH = g.oh;
+    a.IW = g.ow;
+    a.OH = g.ih;
+    a.OW = g.iw;
+    a.P = g.kh - 1 - g.ph;
+    a.C = g.ic;
+    a.Cin = g.oc;
+    a.mult = 1;
+    fill_io(a);
+    return run_lkm<T, true>(a, g.kh, s);
+}
+
+}  // namespace
+
+// 16-bit I/O, k = 7 / 13 / 31 square, stride 1, dilation 1, symmetric padding,
+// an output plane of at most 64 x 64 and an input plane that fits the staged
+// tile (pad + input extent <= tile extent).  Grad-input needs multiplier 1 and
+// pad <= k - 1 (its own padding k - 1 - pad is then >= 0).
+bool largek_mfma_fits(const Geo &g, int pass, int dtype) {
+    if (dtype == 0) return false;
+    if (g.kh != g.kw || (g.kh != 7 && g.kh != 13 && g.kh != 31)) return false;
+    if (g.sh != 1 || g.sw != 1 || g.dh != 1 || g.dw != 1 || g.ph != g.pw) return false;
+    if (pass == 1 && (g.mult != 1 || g.ph > g.kh - 1)) return false;
+    const int OH = pass == 1 ? g.ih : g.oh, OW = pass == 1 ? g.iw : g.ow;
+    const int IH = pass == 1 ? g.oh : g.ih, IW = pass == 1 ? g.ow : g.iw;
+    const int P = pass == 1 ? g.kh - 1 - g.ph : g.ph;
+    if (OH > 64 || OW > 64) return false;
+    const int MT = (OH + 31) / 32, NT = (OW + 31) / 32;
+    const int XR = 32 * MT + g.kh - 1, XC = 32 * (NT - 1) + 16 * kps_of(g.kh);
+    // every staged input element lands inside the tile
+    return IH + P <= XR && IW + P <= XC;
+}
+
+int largek_mfma_fwd(const Geo &g, const void *x, const void *w, const void *b, void *y, int dtype, hipStream_t s) {
+    return dtype == 1 ? lkm_fwd_t<__half>(g, x, w, b, y, s) : lkm_fwd_t<bf16_t>(g, x, w, b, y, s);
+}
+
+int largek_mfma_bwd_input(const Geo &g, const void *dy, const void *w, void *dx, int dtype, hipStream_t s) {
+    return dtype == 1 ? lkm_bwdin_t<__half>(g, dy, w, dx, s) : lkm_bwdin_t<bf16_t>(g, dy, w, dx, s);
+}
+
+}  // namespace dw

@@ -528,6 +528,28 @@ def test_large_kernel_shapes(n, c, h, w, mult, k, p, dt):
     check_static(x, wt, b, dy, 1, p, 1, "largek n%d c%d %dx%d m%d k%d p%d %s" % (n, c, h, w, mult, k, p, dt))
 
 
+
+# ------------------------------------------------------------------ large kernels on the matrix cores (16-bit I/O)
+@pytest.mark.parametrize("n,c,h,w,mult,k,p,dt,fwd_mfma,bin_mfma", [
+    (5, 2, 64, 64, 1, 31, 15, "f16", True, True),     # 2 x 2 tiles, two images per workgroup: last group partial
+    (3, 3, 48, 48, 1, 31, 15, "bf16", True, True),    # 48 x 48 in 2 x 2 tiles (masked stores)
+    (6, 2, 32, 32, 1, 31, 15, "bf16", True, True),    # one tile, four images per workgroup: last group partial
+    (2, 2, 64, 64, 2, 31, 15, "f16", True, False),    # multiplier 2: forward on the matrix cores
+    (3, 2, 64, 40, 1, 13, 6, "f16", True, True),      # 2 x 2 tiles, ragged width (element staging and stores)
+    (2, 3, 33, 36, 1, 13, 0, "bf16", True, True),     # no padding (forward output 21 x 24)
+    (2, 2, 20, 22, 1, 13, 12, "f16", True, True),     # pad k - 1: grad-input pad 0
+    (4, 2, 47, 47, 1, 7, 2, "bf16", True, True),      # k = 7, odd sizes
+    (2, 2, 9, 9, 1, 31, 15, "f16", True, True),       # kernel wider than the image
+    (1, 2, 100, 64, 1, 13, 6, "f16", False, False),   # more than 64 rows: register-tile kernels
+])
+def test_large_kernel_mfma(n, c, h, w, mult, k, p, dt, fwd_mfma, bin_mfma):
+    geo = ((n, c, h, w), (c * mult, k, k), 1, p, 1)
+    assert (dc.dwconv2d_algo(0, *geo, dtype=DT[dt]) == "largek_mfma") == fwd_mfma
+    assert (dc.dwconv2d_algo(1, *geo, dtype=DT[dt]) == "largek_mfma") == bin_mfma
+    x, wt, b, dy = static_case(n, c, h, w, mult, k, 1, p, 1, DT[dt], 680 + h + w + k)
+    check_static(x, wt, b, dy, 1, p, 1, "largek-mfma n%d c%d %dx%d m%d k%d p%d %s" % (n, c, h, w, mult, k, p, dt),
+                 passes=("fwd", "bwd_in"))
+
 # ------------------------------------------------------------------ stride 2 / dilation 2 / pad k-1 (even-grid) path
 @pytest.mark.parametrize("n,c,h,w,mult,k,dt", [
     (2, 3, 29, 31, 2, 5, "bf16"), (2, 3, 29, 31, 1, 5, "f32"),   # odd sizes
