@@ -424,12 +424,13 @@ int run_small(const Geo &g, const BwPlan &p, const void *x, const void *dy, void
     return hipGetLastError() == hipSuccess ? kOk : kErrHip;
 }
 
-enum BwAlgo { kBwChannelGroup = 0, kBwLargek, kBwRowwalk, kBwDecim, kBwBandPixel, kBwBandTaps };
+enum BwAlgo { kBwChannelGroup = 0, kBwLargek, kBwRowwalk, kBwDecim, kBwBandPixel, kBwBandTaps, kBwLargekMfma };
 
 // The pass-1 kernel family a grad-weight call launches (pass 2 is always the
 // fixed-order chunk reduction).
 int select_bwd_weight(const Geo &g, int dt) {
     if (small_fits(g, dt, 2)) return kBwChannelGroup;
+    if (largek_mfma_bwdw_fits(g, dt)) return kBwLargekMfma;
     if (largek_bwdw_fits(g)) return kBwLargek;
     if (rowwalk_fits(g, dt, 2)) return kBwRowwalk;
     if (decim_fits(g, 2)) return kBwDecim;
@@ -446,6 +447,11 @@ int dispatch_bwd_weight(const Geo &g, const void *x, const void *dy, void *dwt, 
     const bool small = algo == kBwChannelGroup;
     const bool large = algo == kBwLargek;
     const bool decim = algo == kBwDecim;
+    if (algo == kBwLargekMfma) {
+        rc = largek_mfma_bwd_weight(g, x, dy, ws, dt, s);
+        if (rc != kOk) return rc;
+        return launch_reduce<T>(g, ws, dwt, db, largek_mfma_bwd_weight_chunks(g), kk + 1, s);
+    }
     if (small || large || decim || algo == kBwRowwalk) {
         // channel-group (small planes), register-tile (large k) or streaming (3x3, pad 1)
         // pass 1: workspace [ic][NC][M*(kk+1)]
@@ -487,7 +493,7 @@ int dispatch_bwd_weight(const Geo &g, const void *x, const void *dy, void *dwt, 
 
 const char *bwd_weight_algo_name(const Geo &g, int dtype) {
     static const char *names[] = {"channelgroup_small", "largek_regtile", "rowwalk_3x3", "decimated_s2d2", "band_pixel",
-                                  "band_taps"};
+                                  "band_taps",          "largek_mfma"};
     return names[select_bwd_weight(g, dtype)];
 }
 
@@ -496,6 +502,7 @@ int64_t bwd_weight_workspace(const Geo &g, int dtype) {
     const int64_t slots = static_cast<int64_t>(g.mult) * (g.kh * g.kw + 1);
     if (algo == kBwChannelGroup) return std::max<int64_t>(g.ic * small_bwd_weight_chunks(g, dtype) * slots * 4, 16);
     if (algo == kBwLargek) return std::max<int64_t>(g.ic * largek_bwd_weight_chunks(g) * slots * 4, 16);
+    if (algo == kBwLargekMfma) return std::max<int64_t>(g.ic * largek_mfma_bwd_weight_chunks(g) * slots * 4, 16);
     if (algo == kBwRowwalk) return std::max<int64_t>(g.ic * rowwalk_bwd_weight_chunks(g, dtype) * slots * 4, 16);
     if (algo == kBwDecim) return std::max<int64_t>(g.ic * decim_bwd_weight_chunks(g) * slots * 4, 16);
     BwPlan p;

@@ -323,4 +323,258 @@ int largek_mfma_bwd_input(const Geo &g, const void *dy, const void *w, void *dx,
     return dtype == 1 ? lkm_bwdin_t<__half>(g, dy, w, dx, s) : lkm_bwdin_t<bf16_t>(g, dy, w, dx, s);
 }
 
+
+// ---------------------------------------------------------------- grad-weight
+// dw[i][j] = sum_{n, oh, c} X[oh + i][c] * dz[oh][c - j], with X the
+// zero-padded input rows and dz[oh][u] = dy[oh][u] for 0 <= u < ow, else 0:
+// a contraction over (image, dy row, window column) with M = kernel row i and
+// N = kernel column j, one 32 x 32 output tile (k <= 32).  Per dy row and
+// window step of 16 columns one v_mfma_f32_32x32x16:
+//   A[i][kk] = X[oh + i][16 s + kk]: lane l reads 8 adjacent columns of input
+//              row oh + l % 32 -- one aligned 16-byte LDS read;
+//   B[kk][j] = dz[oh][16 s + kk - j]: lane l reads the run of 8 dy values
+//              starting at column 16 s + 8 (l / 32) - l % 32 from a zero-padded
+//              copy of dy row oh (two copies shifted by one element, so every
+//              run starts on a 4-byte boundary);
+//   D: register r of lane l is dw[8 (r / 4) + 4 (l / 32) + r % 4][l % 32].
+// A workgroup (4 waves) serves one channel and a chunk of images: per image
+// and band of BH dy rows it stages the BH + k - 1 padded input rows and the dy
+// rows in LDS, each wave takes every 4th dy row of the band, and at the end
+// the waves' tiles (and the dy sums for the bias gradient) are added in a
+// fixed order into the chunk's partial [k*k + 1] of the workspace, which the
+// fixed-order pass 2 reduces over chunks.
+namespace {
+
+constexpr int kDzOff = 32;  // zero columns left of a dy row in the table (even: copy 0 is dword aligned)
+
+template <typename T> struct LkmwArgs {
+    const T *x, *dy;
+    float *ws;           // [c][NC][k*k + 1]
+    int C, N, IH, IW, OH, OW, P;
+    int NC, npc, nbands;
+    int vx, vd;          // x / dy rows are whole aligned 16-byte vectors
+};
+
+template <int K, int CS, int BH> struct LkmwGeo {
+    static constexpr int QD = 8 * CS + 20;          // dwords per copy of a dy row (multiple of 4)
+    static constexpr int XR = BH + K - 1;           // staged input rows
+    static constexpr int XP = 16 * CS + 8;          // input row pitch (halves)
+    static constexpr int dz_bytes = 2 * BH * QD * 4;
+    static constexpr int x_bytes = XR * XP * 2;
+    static constexpr int red_bytes = 4 * 64 * 17 * 4;  // per-wave tiles and dy sums for the final sum
+    static constexpr int lds_bytes = (dz_bytes + x_bytes) > red_bytes ? dz_bytes + x_bytes : red_bytes;
+    static_assert(lds_bytes <= kLdsCap, "band tiles exceed the LDS budget");
+};
+
+template <typename T, int K, int CS, int BH>
+__global__ __launch_bounds__(256) void lk_mfma_bwdw_kernel(LkmwArgs<T> a) {
+    using G = LkmwGeo<K, CS, BH>;
+    extern __shared__ __align__(16) unsigned char smem[];
+    uint32_t *dz = reinterpret_cast<uint32_t *>(smem);                    // [copy][BH][QD]
+    uint16_t *xt = reinterpret_cast<uint16_t *>(smem + G::dz_bytes);      // [XR][XP]
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int m = lane & 31, h = lane >> 5;
+    const int c = blockIdx.x / a.NC;
+    const int chunk = blockIdx.x - c * a.NC;
+    const int n0 = chunk * a.npc, n1 = min(n0 + a.npc, a.N);
+
+    // zero padding that never changes: every x column and every dy column
+    // outside the image (the image part is rewritten per band)
+    for (int e = tid; e < G::x_bytes / 16; e += 256) reinterpret_cast<uint4 *>(xt)[e] = make_uint4(0u, 0u, 0u, 0u);
+    for (int e = tid; e < G::dz_bytes / 16; e += 256) reinterpret_cast<uint4 *>(dz)[e] = make_uint4(0u, 0u, 0u, 0u);
+
+    f32x16_v acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    float dsum = 0.f;
+
+    for (int n = n0; n < n1; ++n) {
+        const uint16_t *xp = reinterpret_cast<const uint16_t *>(a.x) + (static_cast<int64_t>(n) * a.C + c) * a.IH * a.IW;
+        const uint16_t *dp = reinterpret_cast<const uint16_t *>(a.dy) + (static_cast<int64_t>(n) * a.C + c) * a.OH * a.OW;
+        for (int band = 0; band < a.nbands; ++band) {
+            const int oh0 = band * BH;
+            const int rows = min(BH, a.OH - oh0);
+            __syncthreads();  // the previous band's reads are done
+            // input rows oh0 .. oh0 + rows + k - 2 of the padded plane (image row = that - P)
+            const int xrows = rows + K - 1;
+            if (a.vx) {
+                const int vpr = a.IW / 8;
+                for (int v = tid; v < xrows * vpr; v += 256) {
+                    const int r = v / vpr;
+                    const int c8 = (v - r * vpr) * 8;
+                    const int ih = oh0 + r - a.P;
+                    uint4 raw = make_uint4(0u, 0u, 0u, 0u);
+                    if (ih >= 0 && ih < a.IH) raw = *reinterpret_cast<const uint4 *>(xp + static_cast<int64_t>(ih) * a.IW + c8);
+                    uint16_t *d = xt + r * G::XP + a.P + c8;
+                    const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) d[e] = static_cast<uint16_t>(wd[e >> 1] >> ((e & 1) * 16));
+                }
+            } else {
+                for (int e = tid; e < xrows * a.IW; e += 256) {
+                    const int r = e / a.IW;
+                    const int col = e - r * a.IW;
+                    const int ih = oh0 + r - a.P;
+                    xt[r * G::XP + a.P + col] = (ih >= 0 && ih < a.IH) ? xp[static_cast<int64_t>(ih) * a.IW + col] : 0;
+                }
+            }
+            // dy rows oh0 .. oh0 + rows - 1 into copy 0: dword d holds columns 2d - kDzOff, 2d + 1 - kDzOff
+            if (a.vd) {
+                const int vpr = a.OW / 8;
+                for (int v = tid; v < rows * vpr; v += 256) {
+                    const int r = v / vpr;
+                    const int c8 = (v - r * vpr) * 8;
+                    const uint4 raw = *reinterpret_cast<const uint4 *>(dp + static_cast<int64_t>(oh0 + r) * a.OW + c8);
+                    *reinterpret_cast<uint4 *>(dz + r * G::QD + (kDzOff + c8) / 2) = raw;
+                    const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const uint16_t bits = static_cast<uint16_t>(wd[e >> 1] >> ((e & 1) * 16));
+                        T t;
+                        __builtin_memcpy(&t, &bits, 2);
+                        dsum += to_f32(t);
+                    }
+                }
+            } else {
+                uint16_t *dz16 = reinterpret_cast<uint16_t *>(dz);
+                for (int e = tid; e < rows * a.OW; e += 256) {
+                    const int r = e / a.OW;
+                    const int col = e - r * a.OW;
+                    const uint16_t bits = dp[static_cast<int64_t>(oh0 + r) * a.OW + col];
+                    dz16[2 * r * G::QD + kDzOff + col] = bits;
+                    T t;
+                    __builtin_memcpy(&t, &bits, 2);
+                    dsum += to_f32(t);
+                }
+            }
+            __syncthreads();
+            // copy 1: dword d holds copy-0 positions 2d + 1 and 2d + 2
+            uint32_t *dz1 = dz + BH * G::QD;
+            for (int e = tid; e < rows * G::QD; e += 256) {
+                const int r = e / G::QD;
+                const int d = e - r * G::QD;
+                const uint32_t lo = dz[r * G::QD + d];
+                const uint32_t hi = d + 1 < G::QD ? dz[r * G::QD + d + 1] : 0u;
+                dz1[r * G::QD + d] = (lo >> 16) | (hi << 16);
+            }
+            __syncthreads();
+            // kernel rows i >= k (lanes m >= k) are not part of dw: they read row k - 1
+            // instead, so every read stays inside the staged rows
+            const int mi = min(m, K - 1);
+            for (int oh = wave; oh < rows; oh += 4) {
+#pragma unroll
+                for (int s = 0; s < CS; ++s) {
+                    const u32x4_v af = *reinterpret_cast<const u32x4_v *>(xt + (oh + mi) * G::XP + 16 * s + 8 * h);
+                    const int t = 16 * s + 8 * h - m + kDzOff;  // first padded position of this lane's dy run
+                    const int q = t & 1;
+                    const uint32_t *p = dz + (q * BH + oh) * G::QD + ((t - q) >> 1);
+                    const u32x4_v bf = u32x4_v{p[0], p[1], p[2], p[3]};
+                    acc = Mfma<T>::run(af, bf, acc);
+                }
+            }
+        }
+    }
+
+    // fixed-order sum of the 4 waves' tiles and of the 256 dy partial sums
+    __syncthreads();
+    float *red = reinterpret_cast<float *>(smem);  // [wave][lane][17]
+#pragma unroll
+    for (int r = 0; r < 16; ++r) red[(wave * 64 + lane) * 17 + r] = acc[r];
+    red[(wave * 64 + lane) * 17 + 16] = dsum;
+    __syncthreads();
+    float *dst = a.ws + (static_cast<int64_t>(c) * a.NC + chunk) * (K * K + 1);
+    for (int e = tid; e < K * K + 1; e += 256) {
+        float v = 0.f;
+        if (e < K * K) {
+            const int i = e / K, j = e - (e / K) * K;
+            const int ln = 32 * ((i & 7) >> 2) + j, r = 4 * (i >> 3) + (i & 3);
+            for (int w = 0; w < 4; ++w) v += red[(w * 64 + ln) * 17 + r];
+        } else {
+            for (int t2 = 0; t2 < 256; ++t2) v += red[t2 * 17 + 16];
+        }
+        dst[e] = v;
+    }
+}
+
+constexpr int kBwBH = 32;  // dy rows per band
+
+struct LkmwPlan {
+    int NC, npc, nbands;
+};
+
+inline bool plan_lkmw(const Geo &g, LkmwPlan &p) {
+    p.nbands = (g.oh + kBwBH - 1) / kBwBH;
+    // image chunks: about 2048 workgroups in total
+    int NC = std::max(1, (2048 + g.ic - 1) / g.ic);
+    NC = std::min(NC, g.n);
+    p.npc = (g.n + NC - 1) / NC;
+    p.NC = (g.n + p.npc - 1) / p.npc;
+    return true;
+}
+
+template <typename T, int K, int CS>
+int run_lkmw_cs(const Geo &g, const LkmwPlan &p, const void *x, const void *dy, void *ws, hipStream_t s) {
+    using G = LkmwGeo<K, CS, kBwBH>;
+    LkmwArgs<T> a{};
+    a.x = static_cast<const T *>(x);
+    a.dy = static_cast<const T *>(dy);
+    a.ws = static_cast<float *>(ws);
+    a.C = g.ic;
+    a.N = g.n;
+    a.IH = g.ih;
+    a.IW = g.iw;
+    a.OH = g.oh;
+    a.OW = g.ow;
+    a.P = g.ph;
+    a.NC = p.NC;
+    a.npc = p.npc;
+    a.nbands = p.nbands;
+    a.vx = g.iw % 8 == 0 && reinterpret_cast<uintptr_t>(x) % 16 == 0;
+    a.vd = g.ow % 8 == 0 && reinterpret_cast<uintptr_t>(dy) % 16 == 0;
+    hipLaunchKernelGGL((lk_mfma_bwdw_kernel<T, K, CS, kBwBH>), dim3(g.ic * p.NC), dim3(256), G::lds_bytes, s, a);
+    return hipGetLastError() == hipSuccess ? kOk : kErrHip;
+}
+
+template <typename T, int K>
+int run_lkmw(const Geo &g, const LkmwPlan &p, const void *x, const void *dy, void *ws, hipStream_t s) {
+    switch ((g.ow + K - 1 + 15) / 16) {
+        case 1: return run_lkmw_cs<T, K, 1>(g, p, x, dy, ws, s);
+        case 2: return run_lkmw_cs<T, K, 2>(g, p, x, dy, ws, s);
+        case 3: return run_lkmw_cs<T, K, 3>(g, p, x, dy, ws, s);
+        case 4: return run_lkmw_cs<T, K, 4>(g, p, x, dy, ws, s);
+        case 5: return run_lkmw_cs<T, K, 5>(g, p, x, dy, ws, s);
+        default: return run_lkmw_cs<T, K, 6>(g, p, x, dy, ws, s);
+    }
+}
+
+}  // namespace
+
+// 16-bit I/O, k = 13 or 31 square, stride 1, dilation 1, multiplier 1,
+// symmetric padding, dy rows of at most 64 (so the window, ow + k - 1 <= 94
+// columns, is at most six 16-column steps) and an input that fits the staged
+// columns.
+bool largek_mfma_bwdw_fits(const Geo &g, int dtype) {
+    if (dtype == 0) return false;
+    if (g.kh != g.kw || (g.kh != 13 && g.kh != 31)) return false;
+    if (g.sh != 1 || g.sw != 1 || g.dh != 1 || g.dw != 1 || g.ph != g.pw || g.mult != 1) return false;
+    if (g.ow > 64) return false;
+    const int XC = 16 * ((g.ow + g.kh - 1 + 15) / 16);
+    return g.iw + g.ph <= XC;
+}
+
+int largek_mfma_bwd_weight_chunks(const Geo &g) {
+    LkmwPlan p;
+    plan_lkmw(g, p);
+    return p.NC;
+}
+
+int largek_mfma_bwd_weight(const Geo &g, const void *x, const void *dy, void *ws, int dtype, hipStream_t s) {
+    LkmwPlan p;
+    plan_lkmw(g, p);
+    if (dtype == 1) return g.kh == 13 ? run_lkmw<__half, 13>(g, p, x, dy, ws, s) : run_lkmw<__half, 31>(g, p, x, dy, ws, s);
+    return g.kh == 13 ? run_lkmw<bf16_t, 13>(g, p, x, dy, ws, s) : run_lkmw<bf16_t, 31>(g, p, x, dy, ws, s);
+}
+
 }  // namespace dw

@@ -550,6 +550,26 @@ def test_large_kernel_mfma(n, c, h, w, mult, k, p, dt, fwd_mfma, bin_mfma):
     check_static(x, wt, b, dy, 1, p, 1, "largek-mfma n%d c%d %dx%d m%d k%d p%d %s" % (n, c, h, w, mult, k, p, dt),
                  passes=("fwd", "bwd_in"))
 
+
+@pytest.mark.parametrize("n,c,h,w,k,p,dt,bw_mfma", [
+    (5, 2, 64, 64, 31, 15, "f16", True),     # two 32-row bands, chunks of images
+    (3, 3, 48, 48, 31, 15, "bf16", True),    # a full band and a partial band
+    (6, 2, 32, 32, 31, 15, "f16", True),     # one band
+    (3, 2, 64, 40, 13, 6, "bf16", True),     # ragged width: element staging
+    (2, 3, 33, 36, 13, 0, "f16", True),      # no padding
+    (2, 2, 20, 22, 13, 12, "bf16", True),    # pad k - 1
+    (2, 2, 9, 9, 31, 15, "f16", True),       # kernel wider than the image
+    (3, 2, 70, 40, 13, 6, "f16", True),      # 70 dy rows: three bands
+    (2, 2, 47, 47, 7, 2, "bf16", False),     # k = 7: register tiles
+    (1, 2, 40, 100, 13, 6, "f16", False),    # rows of 100: register tiles
+])
+def test_large_kernel_mfma_grad_weight(n, c, h, w, k, p, dt, bw_mfma):
+    geo = ((n, c, h, w), (c, k, k), 1, p, 1)
+    assert (dc.dwconv2d_algo(2, *geo, dtype=DT[dt]) == "largek_mfma") == bw_mfma
+    x, wt, b, dy = static_case(n, c, h, w, 1, k, 1, p, 1, DT[dt], 690 + h + w + k)
+    check_static(x, wt, b, dy, 1, p, 1, "largek-mfma-bw n%d c%d %dx%d k%d p%d %s" % (n, c, h, w, k, p, dt),
+                 passes=("bwd_w",))
+
 # ------------------------------------------------------------------ stride 2 / dilation 2 / pad k-1 (even-grid) path
 @pytest.mark.parametrize("n,c,h,w,mult,k,dt", [
     (2, 3, 29, 31, 2, 5, "bf16"), (2, 3, 29, 31, 1, 5, "f32"),   # odd sizes
