@@ -10,6 +10,8 @@ ABI's names:
     dwconv2d_bwd_weight(x, dy, w_shape, stride=1, padding=0, dilation=1, with_bias=True)
     dynconv_multidil_fwd(x, filters, dilations=(1, 3, 5))
     dynconv_multidil_bwd(x, filters, dy, dilations=(1, 3, 5), need_dx=True, need_dfilters=True)
+    dynconv_multidil_fwd_into(x, filters, y, channel_offset, dilations=(1, 3, 5))
+    dynconv_multidil_bwd_from(x, filters, dy, channel_offset, dilations=(1, 3, 5))
     dwconv2d_out_size(x_shape, w_shape, stride=1, padding=0, dilation=1)
     dwconv2d_bwd_weight_workspace_bytes(x_shape, w_shape, stride, padding, dilation, dtype)
 """
@@ -22,7 +24,9 @@ from ._native import (  # noqa: F401
     dwconv2d_fwd,
     dwconv2d_out_size,
     dynconv_multidil_bwd,
+    dynconv_multidil_bwd_from,
     dynconv_multidil_fwd,
+    dynconv_multidil_fwd_into,
     lib,
     status_str,
 )

@@ -24,7 +24,8 @@ STATUS = {
 EXPORTS = (
     "dwconv2d_out_size", "dwconv2d_fwd", "dwconv2d_bwd_input",
     "dwconv2d_bwd_weight_workspace_bytes", "dwconv2d_bwd_weight",
-    "dynconv_multidil_fwd", "dynconv_multidil_bwd", "dwconv2d_algo", "dw_status_str",
+    "dynconv_multidil_fwd", "dynconv_multidil_bwd", "dynconv_multidil_fwd_into",
+    "dynconv_multidil_bwd_from", "dwconv2d_algo", "dw_status_str",
 )
 
 _I64 = ctypes.c_int64
@@ -69,6 +70,14 @@ def lib() -> ctypes.CDLL:
                                        ctypes.c_int32, _VP, ctypes.POINTER(_VP), _I64, _I64, _I64, _I64, _I64,
                                        ctypes.c_int, _VP]
     L.dynconv_multidil_bwd.restype = ctypes.c_int
+    L.dynconv_multidil_fwd_into.argtypes = [_VP, ctypes.POINTER(_VP), ctypes.POINTER(ctypes.c_int32),
+                                            ctypes.c_int32, _VP, _I64, _I64, _I64, _I64, _I64, _I64, _I64,
+                                            ctypes.c_int, _VP]
+    L.dynconv_multidil_fwd_into.restype = ctypes.c_int
+    L.dynconv_multidil_bwd_from.argtypes = [_VP, ctypes.POINTER(_VP), _VP, _I64, _I64, ctypes.POINTER(ctypes.c_int32),
+                                            ctypes.c_int32, _VP, ctypes.POINTER(_VP), _I64, _I64, _I64, _I64, _I64,
+                                            ctypes.c_int, _VP]
+    L.dynconv_multidil_bwd_from.restype = ctypes.c_int
     L.dwconv2d_algo.argtypes = [ctypes.c_int] + _GEO + [ctypes.c_int]
     L.dwconv2d_algo.restype = ctypes.c_char_p
     L.dw_status_str.argtypes = [ctypes.c_int]
@@ -283,4 +292,52 @@ def dynconv_multidil_bwd(x, filters, dy, dilations=(1, 3, 5), need_dx=True, need
     dil = (ctypes.c_int32 * nb)(*[int(d) for d in dilations])
     _check(lib().dynconv_multidil_bwd(_dev(x, "x"), fptrs, _dev(dy, "dy"), dil, nb, _dev(dx, "dx"), dptrs,
                                       n, c, h, w, k, _dtype_code(x), _stream(x)), "dynconv_multidil_bwd")
+    return dx, dfs
+
+
+def _dyn_shapes(x, filters, dilations):
+    n, c, h, w = (int(s) for s in x.shape)
+    nb = len(filters)
+    if nb != len(dilations):
+        raise ValueError("one filter tensor per dilation")
+    kk = int(filters[0].shape[2])
+    k = int(round(kk ** 0.5))
+    if k * k != kk:
+        raise ValueError("filters must hold k*k taps")
+    for f in filters:
+        if tuple(f.shape) != (n, c, kk, h, w) or f.dtype != x.dtype:
+            raise ValueError("filter %s %s does not match x" % (tuple(f.shape), f.dtype))
+    return n, c, h, w, nb, k
+
+
+def dynconv_multidil_fwd_into(x, filters, y, channel_offset, dilations=(1, 3, 5)):
+    """Write the branch outputs into channels [channel_offset, channel_offset + nb*c) of
+    the caller's (n, C_total, h, w) tensor y; returns y."""
+    n, c, h, w, nb, k = _dyn_shapes(x, filters, dilations)
+    if y.dim() != 4 or (int(y.shape[0]), int(y.shape[2]), int(y.shape[3])) != (n, h, w) or y.dtype != x.dtype:
+        raise ValueError("y %s %s does not match x" % (tuple(y.shape), y.dtype))
+    fptrs = (_VP * nb)(*[_dev(f, "filter") for f in filters])
+    dil = (ctypes.c_int32 * nb)(*[int(d) for d in dilations])
+    _check(lib().dynconv_multidil_fwd_into(_dev(x, "x"), fptrs, dil, nb, _dev(y, "y"), int(y.shape[1]),
+                                           int(channel_offset), n, c, h, w, k, _dtype_code(x), _stream(x)),
+           "dynconv_multidil_fwd_into")
+    return y
+
+
+def dynconv_multidil_bwd_from(x, filters, dy, channel_offset, dilations=(1, 3, 5), need_dx=True,
+                              need_dfilters=True):
+    """(dx, [dF_b]) with the branch gradients read from channels
+    [channel_offset, channel_offset + nb*c) of the caller's (n, C_total, h, w) tensor dy."""
+    import torch
+    n, c, h, w, nb, k = _dyn_shapes(x, filters, dilations)
+    if dy.dim() != 4 or (int(dy.shape[0]), int(dy.shape[2]), int(dy.shape[3])) != (n, h, w) or dy.dtype != x.dtype:
+        raise ValueError("dy %s %s does not match x" % (tuple(dy.shape), dy.dtype))
+    dx = torch.empty_like(x) if need_dx else None
+    dfs = [torch.empty_like(f) for f in filters] if need_dfilters else None
+    fptrs = (_VP * nb)(*[_dev(f, "filter") for f in filters])
+    dptrs = (_VP * nb)(*[_dev(g, "filter gradient") for g in dfs]) if dfs is not None else None
+    dil = (ctypes.c_int32 * nb)(*[int(d) for d in dilations])
+    _check(lib().dynconv_multidil_bwd_from(_dev(x, "x"), fptrs, _dev(dy, "dy"), int(dy.shape[1]),
+                                           int(channel_offset), dil, nb, _dev(dx, "dx"), dptrs, n, c, h, w, k,
+                                           _dtype_code(x), _stream(x)), "dynconv_multidil_bwd_from")
     return dx, dfs

@@ -204,40 +204,54 @@ int dwconv2d_bwd_weight(const void *x, const void *dy, void *dwt, void *db, void
     return map_launch(dw::launch_bwd_weight(g, x, dy, dwt, db, workspace, dtype, static_cast<hipStream_t>(stream)));
 }
 
-int dynconv_multidil_fwd(const void *x, const void *const *filters, const int32_t *dilations, int32_t nb,
-                         void *y, int64_t n, int64_t c, int64_t h, int64_t w, int64_t k, int dtype, void *stream) {
+int dynconv_multidil_fwd_into(const void *x, const void *const *filters, const int32_t *dilations, int32_t nb,
+                              void *y, int64_t y_channels, int64_t y_offset, int64_t n, int64_t c, int64_t h,
+                              int64_t w, int64_t k, int dtype, void *stream) {
     int maxdil = 1;
     const int rc = check_dyn(x, filters, dilations, nb, n, c, h, w, k, dtype, &maxdil);
     if (rc != DW_OK) return rc;
     if (!y) return DW_EPTR;
+    if (y_channels < 1 || y_offset < 0 || y_offset + nb * c > y_channels) return DW_ESHAPE;
+    if (y_channels > kMaxExtent || !product_ok(n, y_channels, h, w)) return DW_ETOOLARGE;
     const size_t e = elem_size(dtype);
     if (!aligned(y, e)) return DW_EPTR;
     const size_t xb = static_cast<size_t>(n * c * h * w) * e;
-    const size_t yb = xb * static_cast<size_t>(nb);
+    const size_t yb = static_cast<size_t>(n * y_channels * h * w) * e;
     const size_t fb = static_cast<size_t>(n * c * k * k * h * w) * e;
     if (overlap(y, yb, x, xb)) return DW_EALIAS;
     for (int b = 0; b < nb; ++b)
         if (overlap(y, yb, filters[b], fb)) return DW_EALIAS;
     if (!dw::dynconv_supported(static_cast<int>(h), static_cast<int>(w), static_cast<int>(k), maxdil, dtype))
         return DW_EUNSUPPORTED;
-    return map_launch(dw::launch_dynconv(x, filters, dilations, nb, y, static_cast<int>(n), static_cast<int>(c),
+    return map_launch(dw::launch_dynconv(x, filters, dilations, nb, y, static_cast<int>(y_channels),
+                                         static_cast<int>(y_offset), static_cast<int>(n), static_cast<int>(c),
                                          static_cast<int>(h), static_cast<int>(w), static_cast<int>(k), dtype,
                                          static_cast<hipStream_t>(stream)));
 }
 
-int dynconv_multidil_bwd(const void *x, const void *const *filters, const void *dy, const int32_t *dilations,
-                         int32_t nb, void *dx, void *const *dfilters, int64_t n, int64_t c, int64_t h, int64_t w,
-                         int64_t k, int dtype, void *stream) {
+int dynconv_multidil_fwd(const void *x, const void *const *filters, const int32_t *dilations, int32_t nb,
+                         void *y, int64_t n, int64_t c, int64_t h, int64_t w, int64_t k, int dtype, void *stream) {
+    // the branch-concatenated output alone: nb*c channels, branch 0 at channel 0
+    const int64_t ych = (nb >= 1 && nb <= 4) ? nb * c : 1;
+    return dynconv_multidil_fwd_into(x, filters, dilations, nb, y, ych, 0, n, c, h, w, k, dtype, stream);
+}
+
+int dynconv_multidil_bwd_from(const void *x, const void *const *filters, const void *dy, int64_t dy_channels,
+                              int64_t dy_offset, const int32_t *dilations, int32_t nb, void *dx,
+                              void *const *dfilters, int64_t n, int64_t c, int64_t h, int64_t w, int64_t k,
+                              int dtype, void *stream) {
     int maxdil = 1;
     const int rc = check_dyn(x, filters, dilations, nb, n, c, h, w, k, dtype, &maxdil);
     if (rc != DW_OK) return rc;
     if (!dy) return DW_EPTR;
+    if (dy_channels < 1 || dy_offset < 0 || dy_offset + nb * c > dy_channels) return DW_ESHAPE;
+    if (dy_channels > kMaxExtent || !product_ok(n, dy_channels, h, w)) return DW_ETOOLARGE;
     const size_t e = elem_size(dtype);
     if (!aligned(dy, e) || (dx && !aligned(dx, e))) return DW_EPTR;
     for (int b = 0; dfilters && b < nb; ++b)
         if (dfilters[b] && !aligned(dfilters[b], e)) return DW_EPTR;
     const size_t xb = static_cast<size_t>(n * c * h * w) * e;
-    const size_t yb = xb * static_cast<size_t>(nb);
+    const size_t yb = static_cast<size_t>(n * dy_channels * h * w) * e;
     const size_t fb = static_cast<size_t>(n * c * k * k * h * w) * e;
     // every output against every input and every other output
     const void *outs[1 + 4];
@@ -262,9 +276,18 @@ int dynconv_multidil_bwd(const void *x, const void *const *filters, const void *
     if (!dw::dynconv_bwd_supported(static_cast<int>(h), static_cast<int>(w), static_cast<int>(k), maxdil, dtype))
         return DW_EUNSUPPORTED;
     if (no == 0) return DW_OK;  // nothing requested
-    return map_launch(dw::launch_dynconv_bwd(x, filters, dy, dilations, nb, dx, dfilters, static_cast<int>(n),
-                                             static_cast<int>(c), static_cast<int>(h), static_cast<int>(w),
-                                             static_cast<int>(k), dtype, static_cast<hipStream_t>(stream)));
+    return map_launch(dw::launch_dynconv_bwd(x, filters, dy, static_cast<int>(dy_channels), static_cast<int>(dy_offset),
+                                             dilations, nb, dx, dfilters, static_cast<int>(n), static_cast<int>(c),
+                                             static_cast<int>(h), static_cast<int>(w), static_cast<int>(k), dtype,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int dynconv_multidil_bwd(const void *x, const void *const *filters, const void *dy, const int32_t *dilations,
+                         int32_t nb, void *dx, void *const *dfilters, int64_t n, int64_t c, int64_t h, int64_t w,
+                         int64_t k, int dtype, void *stream) {
+    const int64_t dych = (nb >= 1 && nb <= 4) ? nb * c : 1;
+    return dynconv_multidil_bwd_from(x, filters, dy, dych, 0, dilations, nb, dx, dfilters, n, c, h, w, k, dtype,
+                                     stream);
 }
 
 const char *dwconv2d_algo(int pass, int64_t n, int64_t ic, int64_t ih, int64_t iw, int64_t oc, int64_t kh,

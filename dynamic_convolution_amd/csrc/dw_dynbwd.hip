@@ -35,12 +35,13 @@ using namespace dyn;
 template <typename T> struct DynBwdArgs {
     const T *x;
     const T *f[kMaxBranches];
-    const T *dy;              // (n, nb*c, h, w)
+    const T *dy;              // (n, dych, h, w): branch b, channel ch at plane dyoff + b*c + ch
     T *dx;                    // (n, c, h, w)
     T *df[kMaxBranches];      // (n, c, k*k, h, w) each; NULL: not wanted
     int dil[kMaxBranches];
     int nb;
     int n, c, h, w, k;
+    int dych, dyoff;
     int BH, nbands, NS;       // row bands of the launched kernel, strips per row
     FastDiv fNS;
     int halo;                 // r * max dilation
@@ -88,7 +89,7 @@ __global__ __launch_bounds__(kThreads) void dynbwd_filter_kernel(DynBwdArgs<T> a
             if (!ob) continue;
             const int d = a.dil[b];
             float g[RW];
-            load_strip<T, RW>(a.dy + (static_cast<int64_t>(nn * a.nb + b) * a.c + ch) * hw + pix, g, valid, vec);
+            load_strip<T, RW>(a.dy + (static_cast<int64_t>(nn) * a.dych + a.dyoff + b * a.c + ch) * hw + pix, g, valid, vec);
             ob += static_cast<int64_t>(plane) * KK * hw + pix;
             // LDS holds every row a tap of the band reaches (zeros outside the
             // image) and zero columns on both sides: no bounds test per tap
@@ -167,7 +168,7 @@ __global__ __launch_bounds__(kThreads) void dynbwd_input_kernel(DynBwdArgs<T> a)
         r.in = sr >= 0 && sr < a.h;
         const int64_t pix = static_cast<int64_t>(min(max(sr, 0), a.h - 1)) * a.w + w0;
         r.g = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
-            a.dy + (static_cast<int64_t>(nn * NB_ + b) * a.c + ch) * hw + pix));
+            a.dy + (static_cast<int64_t>(nn) * a.dych + a.dyoff + b * a.c + ch) * hw + pix));
         const T *fb = a.f[b] + (static_cast<int64_t>(plane) * KK + i * K_) * hw + pix;
 #pragma unroll
         for (int j = 0; j < K_; ++j)
@@ -256,7 +257,7 @@ __global__ __launch_bounds__(kThreads) void dynbwd_input_generic_kernel(DynBwdAr
 
     for (int b = 0; b < a.nb; ++b) {
         const int d = a.dil[b];
-        const T *dyb = a.dy + (static_cast<int64_t>(nn * a.nb + b) * a.c + ch) * hw;
+        const T *dyb = a.dy + (static_cast<int64_t>(nn) * a.dych + a.dyoff + b * a.c + ch) * hw;
         for (int i = 0; i < K; ++i) {
             const T *fb = a.f[b] + (static_cast<int64_t>(plane) * KK + i * K) * hw;
             for (int u = tid; u < items; u += kThreads) {
@@ -367,8 +368,8 @@ void launch_input_fast(int nb, dim3 grid, int lds, hipStream_t s, const DynBwdAr
 }
 
 template <typename T>
-int run_dynbwd(const void *x, const void *const *filters, const void *dy, const int32_t *dil, int nb, void *dx,
-               void *const *dfilters, int n, int c, int h, int w, int k, hipStream_t s) {
+int run_dynbwd(const void *x, const void *const *filters, const void *dy, int dych, int dyoff, const int32_t *dil,
+               int nb, void *dx, void *const *dfilters, int n, int c, int h, int w, int k, hipStream_t s) {
     constexpr int RW = Vec<T>::N;
     int maxdil = 1;
     for (int b = 0; b < nb; ++b) maxdil = std::max(maxdil, static_cast<int>(dil[b]));
@@ -378,6 +379,8 @@ int run_dynbwd(const void *x, const void *const *filters, const void *dy, const 
     DynBwdArgs<T> a;
     a.x = static_cast<const T *>(x);
     a.dy = static_cast<const T *>(dy);
+    a.dych = dych;
+    a.dyoff = dyoff;
     a.dx = static_cast<T *>(dx);
     bool al = reinterpret_cast<uintptr_t>(dy) % 16 == 0 && (!dx || reinterpret_cast<uintptr_t>(dx) % 16 == 0);
     for (int b = 0; b < kMaxBranches; ++b) {
@@ -459,13 +462,13 @@ bool dynconv_bwd_supported(int h, int w, int k, int maxdil, int dtype) {
     return dtype == 0 ? dynbwd_fits<float>(h, w, k, maxdil) : dynbwd_fits<__half>(h, w, k, maxdil);
 }
 
-int launch_dynconv_bwd(const void *x, const void *const *filters, const void *dy, const int32_t *dil, int nb,
-                       void *dx, void *const *dfilters, int n, int c, int h, int w, int k, int dtype,
-                       hipStream_t s) {
+int launch_dynconv_bwd(const void *x, const void *const *filters, const void *dy, int dych, int dyoff,
+                       const int32_t *dil, int nb, void *dx, void *const *dfilters, int n, int c, int h, int w,
+                       int k, int dtype, hipStream_t s) {
     switch (dtype) {
-        case 0: return run_dynbwd<float>(x, filters, dy, dil, nb, dx, dfilters, n, c, h, w, k, s);
-        case 1: return run_dynbwd<__half>(x, filters, dy, dil, nb, dx, dfilters, n, c, h, w, k, s);
-        default: return run_dynbwd<bf16_t>(x, filters, dy, dil, nb, dx, dfilters, n, c, h, w, k, s);
+        case 0: return run_dynbwd<float>(x, filters, dy, dych, dyoff, dil, nb, dx, dfilters, n, c, h, w, k, s);
+        case 1: return run_dynbwd<__half>(x, filters, dy, dych, dyoff, dil, nb, dx, dfilters, n, c, h, w, k, s);
+        default: return run_dynbwd<bf16_t>(x, filters, dy, dych, dyoff, dil, nb, dx, dfilters, n, c, h, w, k, s);
     }
 }
 

@@ -13,7 +13,8 @@
 // needs a column test and no conversion), and serve every branch; each thread
 // produces RW adjacent pixels of one row for all branches, streaming every
 // filter tap as one 16-byte coalesced load and writing each branch's strip at
-// its channel offset b*C + c of the concatenated output.
+// its channel offset b*C + c of the concatenated output (or, for a caller's
+// larger concatenation, at channel yoff + b*C + c of an output of ych channels).
 #include "dw_dyn.hpp"
 
 namespace dw {
@@ -28,6 +29,7 @@ template <typename T> struct DynArgs {
     int dil[kMaxBranches];
     int nb;
     int n, c, h, w, k;
+    int ych, yoff;  // channels of the output tensor, channel of branch 0's first plane
     int BH, nbands, NS;
     FastDiv fNS;
     int halo;   // r * max dilation
@@ -115,7 +117,7 @@ __global__ __launch_bounds__(kThreads) void dynconv_kernel(DynArgs<T> a) {
                         for (int q = 0; q < RW; ++q) acc[q] = fmaf(fv[q], xv[q], acc[q]);
                     }
                 }
-                T *yp = a.y + (static_cast<int64_t>(nn * a.nb + b) * a.c + ch) * hw + pix;
+                T *yp = a.y + (static_cast<int64_t>(nn) * a.ych + a.yoff + b * a.c + ch) * hw + pix;
                 store_strip<T, RW>(yp, acc, RW, true);
                 continue;
             }
@@ -145,15 +147,15 @@ __global__ __launch_bounds__(kThreads) void dynconv_kernel(DynArgs<T> a) {
                     for (int q = 0; q < RW; ++q) acc[q] = fmaf(fv[q], xv[q], acc[q]);
                 }
             }
-            T *yp = a.y + (static_cast<int64_t>(nn * a.nb + b) * a.c + ch) * hw + pix;
+            T *yp = a.y + (static_cast<int64_t>(nn) * a.ych + a.yoff + b * a.c + ch) * hw + pix;
             store_strip<T, RW>(yp, acc, valid, a.vf != 0);
         }
     }
 }
 
 template <typename T>
-int run_dyn(const void *x, const void *const *filters, const int32_t *dil, int nb, void *y, int n, int c,
-            int h, int w, int k, hipStream_t s) {
+int run_dyn(const void *x, const void *const *filters, const int32_t *dil, int nb, void *y, int ych, int yoff,
+            int n, int c, int h, int w, int k, hipStream_t s) {
     constexpr int RW = Vec<T>::N;
     int maxdil = 1;
     for (int b = 0; b < nb; ++b) maxdil = std::max(maxdil, static_cast<int>(dil[b]));
@@ -168,6 +170,8 @@ int run_dyn(const void *x, const void *const *filters, const int32_t *dil, int n
         if (b < nb) fal = fal && (reinterpret_cast<uintptr_t>(filters[b]) % 16 == 0);
     }
     a.y = static_cast<T *>(y);
+    a.ych = ych;
+    a.yoff = yoff;
     a.nb = nb;
     a.n = n;
     a.c = c;
@@ -209,12 +213,12 @@ bool dynconv_supported(int h, int w, int k, int maxdil, int dtype) {
     return dtype == 0 ? plan_dyn<float>(1, 1, h, w, k, maxdil, p) : plan_dyn<__half>(1, 1, h, w, k, maxdil, p);
 }
 
-int launch_dynconv(const void *x, const void *const *filters, const int32_t *dil, int nb, void *y, int n, int c,
-                   int h, int w, int k, int dtype, hipStream_t s) {
+int launch_dynconv(const void *x, const void *const *filters, const int32_t *dil, int nb, void *y, int ych,
+                   int yoff, int n, int c, int h, int w, int k, int dtype, hipStream_t s) {
     switch (dtype) {
-        case 0: return run_dyn<float>(x, filters, dil, nb, y, n, c, h, w, k, s);
-        case 1: return run_dyn<__half>(x, filters, dil, nb, y, n, c, h, w, k, s);
-        default: return run_dyn<bf16_t>(x, filters, dil, nb, y, n, c, h, w, k, s);
+        case 0: return run_dyn<float>(x, filters, dil, nb, y, ych, yoff, n, c, h, w, k, s);
+        case 1: return run_dyn<__half>(x, filters, dil, nb, y, ych, yoff, n, c, h, w, k, s);
+        default: return run_dyn<bf16_t>(x, filters, dil, nb, y, ych, yoff, n, c, h, w, k, s);
     }
 }
 

@@ -34,13 +34,16 @@ int launch_bwd_input(const Geo &g, const void *dy, const void *w, void *dx, int 
 int64_t bwd_weight_workspace(const Geo &g, int dtype);
 int launch_bwd_weight(const Geo &g, const void *x, const void *dy, void *dwt, void *db,
                       void *ws, int dtype, hipStream_t s);
-int launch_dynconv(const void *x, const void *const *filters, const int32_t *dil, int nb, void *y,
-                   int n, int c, int h, int w, int k, int dtype, hipStream_t s);
+// Dynamic filter forward: branch b, channel ch is written to plane
+// (n, yoff + b*c + ch) of an output with ych channels.
+int launch_dynconv(const void *x, const void *const *filters, const int32_t *dil, int nb, void *y, int ych,
+                   int yoff, int n, int c, int h, int w, int k, int dtype, hipStream_t s);
 // Backward of the dynamic filter (dw_dynbwd.hip): dx when non-NULL, dF_b for
-// every non-NULL dfilters[b] (dfilters itself may be NULL).
-int launch_dynconv_bwd(const void *x, const void *const *filters, const void *dy, const int32_t *dil, int nb,
-                       void *dx, void *const *dfilters, int n, int c, int h, int w, int k, int dtype,
-                       hipStream_t s);
+// every non-NULL dfilters[b] (dfilters itself may be NULL); dy is read at
+// plane (n, dyoff + b*c + ch) of a gradient with dych channels.
+int launch_dynconv_bwd(const void *x, const void *const *filters, const void *dy, int dych, int dyoff,
+                       const int32_t *dil, int nb, void *dx, void *const *dfilters, int n, int c, int h, int w,
+                       int k, int dtype, hipStream_t s);
 
 // Streaming kernels for 3x3 / pad 1 / dilation 1 / stride 1-2 / multiplier <= 2
 // (dw_rowwalk.hip).  The launchers return kErrUnsupported when the row is

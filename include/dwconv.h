@@ -189,6 +189,36 @@ int dynconv_multidil_bwd(const void *x, const void *const *filters, const void *
                          int dtype, void *stream);
 
 /*
+ * dynconv_multidil_fwd into a caller-owned larger concatenation: the page's
+ * fused operator stores each branch straight into the tensor the downstream
+ * aggregation reads.  Branch b, channel ch is written to channel
+ * y_offset + b*c + ch of y, an (n, y_channels, h, w) tensor; its other
+ * channels are not touched.  Requires y_offset >= 0 and
+ * y_offset + nb*c <= y_channels (else DW_ESHAPE); the whole of y must not
+ * overlap x or a filter (DW_EALIAS).  dynconv_multidil_fwd is this call with
+ * y_channels = nb*c and y_offset = 0.
+ */
+int dynconv_multidil_fwd_into(const void *x, const void *const *filters,
+                              const int32_t *dilations, int32_t nb, void *y,
+                              int64_t y_channels, int64_t y_offset,
+                              int64_t n, int64_t c, int64_t h, int64_t w, int64_t k,
+                              int dtype, void *stream);
+
+/*
+ * dynconv_multidil_bwd with dy taken from a larger gradient tensor: the
+ * gradient of branch b, channel ch is read from channel dy_offset + b*c + ch
+ * of dy, an (n, dy_channels, h, w) tensor (the gradient of the concatenation
+ * that dynconv_multidil_fwd_into wrote into).  Same requirements on the
+ * channel range as above; dynconv_multidil_bwd is this call with
+ * dy_channels = nb*c and dy_offset = 0.
+ */
+int dynconv_multidil_bwd_from(const void *x, const void *const *filters, const void *dy,
+                              int64_t dy_channels, int64_t dy_offset,
+                              const int32_t *dilations, int32_t nb, void *dx, void *const *dfilters,
+                              int64_t n, int64_t c, int64_t h, int64_t w, int64_t k,
+                              int dtype, void *stream);
+
+/*
  * Kernel family a call would launch for this geometry and dtype (for
  * profiling and per-shape tuning; the same decision the compute calls make).
  * pass: 0 = dwconv2d_fwd, 1 = dwconv2d_bwd_input, 2 = dwconv2d_bwd_weight.

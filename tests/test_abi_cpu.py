@@ -184,6 +184,30 @@ def test_dynconv_bwd_validation():
     assert bwd(FAKE, f3, dy, d3, 3, None, None, *geo, 0, None) == 0
     assert bwd(FAKE, f3, dy, d3, 3, None, none3, *geo, 0, None) == 0
 
+
+@no_gpu
+def test_dynconv_into_validation():
+    L = N.lib()
+    f3 = (ctypes.c_void_p * 3)(FAKE + (1 << 24), FAKE + (2 << 24), FAKE + (3 << 24))
+    d3 = (ctypes.c_int32 * 3)(1, 3, 5)
+    y = FAKE + (8 << 24)
+    into = L.dynconv_multidil_fwd_into
+    geo = (1, 4, 8, 8, 3)
+    assert into(FAKE, f3, d3, 3, y, 12, -1, *geo, 0, None) == -2       # negative offset
+    assert into(FAKE, f3, d3, 3, y, 12, 1, *geo, 0, None) == -2        # offset + nb*c past the channels
+    assert into(FAKE, f3, d3, 3, y, 0, 0, *geo, 0, None) == -2         # no channels
+    assert into(FAKE, f3, d3, 3, None, 20, 4, *geo, 0, None) == -1     # null y
+    assert into(FAKE, f3, d3, 3, y + 2, 20, 4, *geo, 0, None) == -1    # misaligned y
+    assert into(FAKE, f3, d3, 3, FAKE - 4096, 20, 4, *geo, 0, None) == -7  # larger y reaches x
+    assert into(FAKE, f3, d3, 3, y, 20, 4, *geo, 9, None) == -4        # dtype
+    frm = L.dynconv_multidil_bwd_from
+    dx = FAKE + (9 << 24)
+    assert frm(FAKE, f3, y, 12, 1, d3, 3, dx, None, *geo, 0, None) == -2
+    assert frm(FAKE, f3, y, 20, -2, d3, 3, dx, None, *geo, 0, None) == -2
+    assert frm(FAKE, f3, None, 20, 4, d3, 3, dx, None, *geo, 0, None) == -1
+    assert frm(FAKE, f3, y, 20, 4, d3, 3, y + 64, None, *geo, 0, None) == -7   # dx inside the larger dy
+    assert frm(FAKE, f3, y, 20, 4, d3, 3, None, None, *geo, 0, None) == 0      # nothing requested
+
 def test_binding_refuses_cpu_tensors():
     x = torch.zeros(1, 2, 5, 5)
     w = torch.zeros(2, 3, 3)

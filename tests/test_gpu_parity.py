@@ -244,6 +244,42 @@ def test_dynamic_bwd_guard_bands(dtype):
         assert torch.isfinite(t).all(), "unwritten output element"
         assert torch.all(buf[:margin] == 1024.0) and torch.all(buf[-margin:] == -2048.0), "guard band written"
 
+
+@pytest.mark.parametrize("shape,k,dils,off,extra,dtype", [
+    ((2, 3, 21, 24), 3, (1, 3, 5), 5, 2, "f32"),     # branches in the middle of a larger concatenation
+    ((1, 4, 32, 32), 5, (1, 3, 5), 0, 3, "bf16"),    # k = 5, offset 0, channels after
+    ((2, 2, 20, 16), 5, (1, 2), 7, 0, "f16"),        # k = 5, the last channels of the tensor
+    ((1, 3, 37, 53), 3, (1, 3, 5), 4, 1, "bf16"),    # ragged rows
+])
+def test_dynamic_into_larger_concat(shape, k, dils, off, extra, dtype):
+    n, c, h, w = shape
+    nb = len(dils)
+    ctot = off + nb * c + extra
+    x, fs, dy = dyn_bwd_inputs(*shape, k, dils, DT[dtype], 520 + sum(shape) + k + off,
+                               fdist=("N", 0.0, 1.0 / (k * k)))
+    note("dynamic-into %s k%d off%d of %d %s" % (shape, k, off, ctot, dtype))
+    xd, fsd = x.to(DEV), [f.to(DEV) for f in fs]
+    y = torch.full((n, ctot, h, w), 777.0, dtype=DT[dtype], device=DEV)
+    dc.dynconv_multidil_fwd_into(xd, fsd, y, off, dils)
+    # the gradient of the larger tensor: this op's branches at the same channels
+    gbig = torch.full((n, ctot, h, w), 555.0, dtype=DT[dtype], device=DEV)
+    gbig[:, off:off + nb * c] = dy.to(DEV)
+    dx, dfs = dc.dynconv_multidil_bwd_from(xd, fsd, gbig, off, dils)
+    torch.cuda.synchronize()
+    assert torch.all(y[:, :off] == 777.0) and torch.all(y[:, off + nb * c:] == 777.0), "channel outside the slice written"
+    assert_close(y[:, off:off + nb * c], O.dynconv_multidil_fwd(x, fs, dils), k * k, DT[dtype], "dynamic-into y")
+    odx, odf = O.dynconv_multidil_bwd(x, fs, dy, dils)
+    assert_close(dx, odx, nb * k * k, DT[dtype], "dynamic-from dx")
+    for b in range(nb):
+        assert_close(dfs[b], odf[b], 1, DT[dtype], "dynamic-from dF%d" % b)
+    # the plain entry points are the special case offset 0, channels nb*c: identical results
+    y0 = dc.dynconv_multidil_fwd(xd, fsd, dils)
+    dx0, dfs0 = dc.dynconv_multidil_bwd(xd, fsd, dy.to(DEV), dils)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y[:, off:off + nb * c]) and torch.equal(dx0, dx)
+    for a_, b_ in zip(dfs0, dfs):
+        assert torch.equal(a_, b_)
+
 def fuzz_cases(count=48, seed=2024):
     r = random.Random(seed)
     out = []
