@@ -72,7 +72,8 @@ def parse():
                     help="also run a plain 256 MiB device copy (counter calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
                     help="write profiles/traffic_<--only-tag>.json from two rocprofv3 --pmc runs and exit")
-    ap.add_argument("--launches", type=int, default=0, help="calls of the tag in the counter runs")
+    ap.add_argument("--launches", type=int, default=0,
+                    help="calls of the tag in the counter runs (0: the dispatch count of its kernels)")
     ap.add_argument("--cmd", default="", help="command recorded with the traffic figures")
     return ap.parse_args()
 
@@ -339,14 +340,16 @@ def committed_traffic(tag):
 
 
 def read_counter_csv(path, counter):
-    """Per-dispatch (kernel name, value) of one counter from a rocprofv3 counter_collection.csv."""
+    """Per-dispatch (kernel name, value) of one counter from a rocprofv3 counter_collection.csv,
+    in dispatch order."""
     import csv
     rows = []
     with open(path) as f:
         for r in csv.DictReader(f):
             if r.get("Counter_Name") == counter:
-                rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
-    return rows
+                rows.append((int(r.get("Dispatch_Id") or 0), r["Kernel_Name"], float(r["Counter_Value"])))
+    rows.sort(key=lambda t: t[0])
+    return [(name, v) for _d, name, v in rows]
 
 
 def traffic_from(fetch_csv, write_csv, tag, launches, cmd):
@@ -356,10 +359,19 @@ def traffic_from(fetch_csv, write_csv, tag, launches, cmd):
     for key, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
         rows = read_counter_csv(path, counter)
         mine = [v for name, v in rows if "dw::" in name]
-        # the reference copy is torch's elementwise copy kernel; the largest such dispatches
-        refs = sorted((v for name, v in rows if "dw::" not in name and "copy" in name.lower()), reverse=True)[:3]
+        # the reference copies are the run's last three copy dispatches (--copy-ref runs
+        # them after everything else; earlier copies are the inputs' dtype conversions)
+        refs = [v for name, v in rows if "dw::" not in name and "copy" in name.lower()][-3:]
         if not mine or not refs:
             raise SystemExit("no %s rows for this library or the reference copy in %s" % (counter, path))
+        if launches <= 0:
+            # each call of a tag launches each of its kernels once: the number of
+            # calls is the dispatch count of any of this library's kernels
+            counts = {}
+            for name, _v in rows:
+                if "dw::" in name:
+                    counts[name] = counts.get(name, 0) + 1
+            launches = max(counts.values())
         ref_kib = sum(refs) / len(refs)
         scale = (COPY_REF_BYTES / 1024.0) / ref_kib
         out[key + "_kib_raw"] = sum(mine)
