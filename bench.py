@@ -67,6 +67,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline leg")
     ap.add_argument("--eager", action="store_true", help="launch call by call instead of replaying HIP graphs")
+    ap.add_argument("--tune", action="store_true",
+                    help="before timing, let the library time every kernel family that can run each call's "
+                         "geometry and keep the fastest (its selection table)")
     ap.add_argument("--only-tag", default=None, help="run only the calls of this kernel tag (for counter runs)")
     ap.add_argument("--copy-ref", action="store_true",
                     help="also run a plain 256 MiB device copy (counter calibration)")
@@ -101,10 +104,12 @@ def valid_taps(in_n, out_n, k, s, p, d):
 
 
 class Call:
-    """One entry-point call of the step with its algorithmic bytes and flops."""
+    """One entry-point call of the step with its algorithmic bytes and flops; tune, when
+    given, times the kernel families that can run the call's geometry and records the
+    fastest in the library's selection table."""
 
-    def __init__(self, tag, fn, nbytes, flops):
-        self.tag, self.fn, self.nbytes, self.flops = tag, fn, nbytes, flops
+    def __init__(self, tag, fn, nbytes, flops, tune=None):
+        self.tag, self.fn, self.nbytes, self.flops, self.tune = tag, fn, nbytes, flops, tune
 
 
 def static_calls(dc, case, dev, seed, passes=("fwd", "bwd_in", "bwd_w")):
@@ -137,15 +142,18 @@ def static_calls(dc, case, dev, seed, passes=("fwd", "bwd_in", "bwd_w")):
         return "%s.%s.k%d_s%d_m%d_%s" % (name, algo, k, s, M, dts)
 
     if "fwd" in passes:
-        calls.append(Call(tag(0, "fwd"), lambda: dc.dwconv2d_fwd(x, w, b, s, p, d, out=y), sx + W + B + Y, 2 * macs))
+        calls.append(Call(tag(0, "fwd"), lambda: dc.dwconv2d_fwd(x, w, b, s, p, d, out=y), sx + W + B + Y, 2 * macs,
+                          lambda: dc.dwconv2d_tune_fwd(x, w, b, s, p, d, out=y, reps=5)))
     if "bwd_in" in passes:
         calls.append(Call(tag(1, "bwd_input"), lambda: dc.dwconv2d_bwd_input(dy, w, x.shape, s, p, d, out=dx),
-                          Y + W + X, 2 * macs))
+                          Y + W + X, 2 * macs,
+                          lambda: dc.dwconv2d_tune_bwd_input(dy, w, x.shape, s, p, d, out=dx, reps=5)))
     if "bwd_w" in passes:
         calls.append(Call(tag(2, "bwd_weight"),
                           lambda: dc.dwconv2d_bwd_weight(x, dy, w.shape, s, p, d, with_bias=with_bias, out=gw,
                                                          out_bias=gb, workspace=ws),
-                          sx + Y + W + B, 2 * macs))
+                          sx + Y + W + B, 2 * macs,
+                          lambda: dc.dwconv2d_tune_bwd_weight(x, dy, w.shape, s, p, d, with_bias=with_bias, reps=5)))
     tensors = dict(x=x, w=w, b=b, dy=dy, y=y, dx=dx, gw=gw, gb=gb)
     return calls, tensors
 
@@ -403,6 +411,16 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     wl = build_workload(args.workload, dc, dev)
+    if args.tune:
+        # the library times the families each call's geometry allows and keeps the
+        # fastest; the workload is then rebuilt so its tags name the chosen families
+        for cl in wl["calls"]:
+            if cl.tune is not None:
+                cl.tune()
+        torch.cuda.synchronize()
+        del wl
+        torch.cuda.empty_cache()
+        wl = build_workload(args.workload, dc, dev)
     # rotating copies: a step whose traffic is under 2 GiB would find part of its
     # inputs still in the 256 MB last-level cache when it runs again, so such
     # workloads get identical copies of every tensor and step i uses copy i % ncopy
@@ -542,7 +560,8 @@ def main():
         "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": wl["dtype"], "data": "synthetic (seeded, shapes and distributions of the workload)",
-        "config": dict({"workload": wl["desc"], "launch": "eager" if args.eager else "hip_graph_per_step"},
+        "config": dict({"workload": wl["desc"], "launch": "eager" if args.eager else "hip_graph_per_step",
+                        "kernel_selection": "tuned on this device" if args.tune else "built-in rules"},
                        **wl["cfg"]),
         "step_gbytes": round(step_bytes / 1e9, 4), "step_gflop": round(step_flops / 1e9, 4),
         "gbs": round(step_bytes / (elapsed / args.steps) / 1e9, 2),

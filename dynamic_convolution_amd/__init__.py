@@ -14,15 +14,22 @@ ABI's names:
     dynconv_multidil_bwd_from(x, filters, dy, channel_offset, dilations=(1, 3, 5))
     dwconv2d_out_size(x_shape, w_shape, stride=1, padding=0, dilation=1)
     dwconv2d_bwd_weight_workspace_bytes(x_shape, w_shape, stride, padding, dilation, dtype)
+    dwconv2d_algo_candidates / dwconv2d_set_algo / dwconv2d_tune_{fwd,bwd_input,bwd_weight}
+        (per-geometry kernel selection, measured on the device)
 """
 from ._native import (  # noqa: F401
     DwconvError,
     dwconv2d_algo,
+    dwconv2d_algo_candidates,
     dwconv2d_bwd_input,
     dwconv2d_bwd_weight,
     dwconv2d_bwd_weight_workspace_bytes,
     dwconv2d_fwd,
     dwconv2d_out_size,
+    dwconv2d_set_algo,
+    dwconv2d_tune_bwd_input,
+    dwconv2d_tune_bwd_weight,
+    dwconv2d_tune_fwd,
     dynconv_multidil_bwd,
     dynconv_multidil_bwd_from,
     dynconv_multidil_fwd,

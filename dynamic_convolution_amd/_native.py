@@ -26,6 +26,8 @@ EXPORTS = (
     "dwconv2d_bwd_weight_workspace_bytes", "dwconv2d_bwd_weight",
     "dynconv_multidil_fwd", "dynconv_multidil_bwd", "dynconv_multidil_fwd_into",
     "dynconv_multidil_bwd_from", "dwconv2d_algo", "dw_status_str",
+    "dwconv2d_algo_candidates", "dwconv2d_set_algo", "dwconv2d_tune_fwd", "dwconv2d_tune_bwd_input",
+    "dwconv2d_tune_bwd_weight",
 )
 
 _I64 = ctypes.c_int64
@@ -80,6 +82,20 @@ def lib() -> ctypes.CDLL:
     L.dynconv_multidil_bwd_from.restype = ctypes.c_int
     L.dwconv2d_algo.argtypes = [ctypes.c_int] + _GEO + [ctypes.c_int]
     L.dwconv2d_algo.restype = ctypes.c_char_p
+    _CP = ctypes.c_char_p
+    L.dwconv2d_algo_candidates.argtypes = [ctypes.c_int] + _GEO + [ctypes.c_int, ctypes.POINTER(_CP), ctypes.c_int]
+    L.dwconv2d_algo_candidates.restype = ctypes.c_int
+    L.dwconv2d_set_algo.argtypes = [ctypes.c_int] + _GEO + [ctypes.c_int, _CP]
+    L.dwconv2d_set_algo.restype = ctypes.c_int
+    L.dwconv2d_tune_fwd.argtypes = [_VP, _VP, _VP, _VP] + _GEO + [ctypes.c_int, ctypes.c_int, _VP,
+                                                                  ctypes.POINTER(_CP)]
+    L.dwconv2d_tune_fwd.restype = ctypes.c_int
+    L.dwconv2d_tune_bwd_input.argtypes = [_VP, _VP, _VP] + _GEO + [ctypes.c_int, ctypes.c_int, _VP,
+                                                                   ctypes.POINTER(_CP)]
+    L.dwconv2d_tune_bwd_input.restype = ctypes.c_int
+    L.dwconv2d_tune_bwd_weight.argtypes = [_VP, _VP, _VP, _VP, _VP, ctypes.c_size_t] + _GEO + [
+        ctypes.c_int, ctypes.c_int, _VP, ctypes.POINTER(_CP)]
+    L.dwconv2d_tune_bwd_weight.restype = ctypes.c_int
     L.dw_status_str.argtypes = [ctypes.c_int]
     L.dw_status_str.restype = ctypes.c_char_p
     _lib = L
@@ -341,3 +357,64 @@ def dynconv_multidil_bwd_from(x, filters, dy, channel_offset, dilations=(1, 3, 5
                                            int(channel_offset), dil, nb, _dev(dx, "dx"), dptrs, n, c, h, w, k,
                                            _dtype_code(x), _stream(x)), "dynconv_multidil_bwd_from")
     return dx, dfs
+
+
+# ---------------------------------------------------------------- kernel selection
+def dwconv2d_algo_candidates(pass_, x_shape, w_shape, stride=1, padding=0, dilation=1, dtype=None):
+    """Names of the kernel families that can run pass_ (0 fwd, 1 grad-input, 2 grad-weight)."""
+    import torch
+    code = _dtype_code(torch.empty(0, dtype=dtype or torch.float32))
+    geo = _geo(x_shape, w_shape, stride, padding, dilation)
+    names = (ctypes.c_char_p * 16)()
+    cnt = lib().dwconv2d_algo_candidates(int(pass_), *geo, code, names, 16)
+    if cnt < 0:
+        _check(cnt, "dwconv2d_algo_candidates")
+    return [names[i].decode() for i in range(min(cnt, 16))]
+
+
+def dwconv2d_set_algo(pass_, x_shape, w_shape, stride=1, padding=0, dilation=1, dtype=None, algo=None):
+    """Record family `algo` for this geometry (None: back to the built-in choice)."""
+    import torch
+    code = _dtype_code(torch.empty(0, dtype=dtype or torch.float32))
+    geo = _geo(x_shape, w_shape, stride, padding, dilation)
+    _check(lib().dwconv2d_set_algo(int(pass_), *geo, code, algo.encode() if algo else None), "dwconv2d_set_algo")
+
+
+def dwconv2d_tune_fwd(x, w, bias=None, stride=1, padding=0, dilation=1, out=None, reps=10):
+    """Time every forward family on these tensors, record the fastest; returns its name."""
+    import torch
+    geo = _geo(x.shape, w.shape, stride, padding, dilation)
+    oh, ow = dwconv2d_out_size(x.shape, w.shape, stride, padding, dilation)
+    if out is None:
+        out = torch.empty((geo[0], geo[4], oh, ow), dtype=x.dtype, device=x.device)
+    chosen = ctypes.c_char_p()
+    _check(lib().dwconv2d_tune_fwd(_dev(x, "x"), _dev(w, "w"), _dev(bias, "bias"), _dev(out, "out"), *geo,
+                                   _dtype_code(x), int(reps), _stream(x), ctypes.byref(chosen)), "dwconv2d_tune_fwd")
+    return chosen.value.decode()
+
+
+def dwconv2d_tune_bwd_input(dy, w, x_shape, stride=1, padding=0, dilation=1, out=None, reps=10):
+    """Time every grad-input family on these tensors, record the fastest; returns its name."""
+    import torch
+    geo = _geo(x_shape, w.shape, stride, padding, dilation)
+    if out is None:
+        out = torch.empty(tuple(int(s) for s in x_shape), dtype=dy.dtype, device=dy.device)
+    chosen = ctypes.c_char_p()
+    _check(lib().dwconv2d_tune_bwd_input(_dev(dy, "dy"), _dev(w, "w"), _dev(out, "out"), *geo, _dtype_code(dy),
+                                         int(reps), _stream(dy), ctypes.byref(chosen)), "dwconv2d_tune_bwd_input")
+    return chosen.value.decode()
+
+
+def dwconv2d_tune_bwd_weight(x, dy, w_shape, stride=1, padding=0, dilation=1, with_bias=True, reps=10):
+    """Time every grad-weight family on these tensors, record the fastest; returns its name."""
+    import torch
+    geo = _geo(x.shape, w_shape, stride, padding, dilation)
+    out = torch.empty(tuple(int(s) for s in w_shape), dtype=x.dtype, device=x.device)
+    ob = torch.empty((geo[4],), dtype=x.dtype, device=x.device) if with_bias else None
+    nbytes = dwconv2d_bwd_weight_workspace_bytes(x.shape, w_shape, stride, padding, dilation, x.dtype)
+    ws = torch.empty((nbytes,), dtype=torch.uint8, device=x.device)
+    chosen = ctypes.c_char_p()
+    _check(lib().dwconv2d_tune_bwd_weight(_dev(x, "x"), _dev(dy, "dy"), _dev(out, "out"), _dev(ob, "out_bias"),
+                                          _dev(ws, "workspace"), nbytes, *geo, _dtype_code(x), int(reps), _stream(x),
+                                          ctypes.byref(chosen)), "dwconv2d_tune_bwd_weight")
+    return chosen.value.decode()

@@ -9,6 +9,8 @@
 
 #include <stdint.h>
 
+#include <cstring>
+
 #include "dw_internal.hpp"
 #include "dwconv.h"
 
@@ -114,6 +116,68 @@ int check_dyn(const void *x, const void *const *filters, const int32_t *dilation
     for (int b = 0; b < nb; ++b)
         if (!aligned(filters[b], e)) return DW_EPTR;
     *maxdil = md;
+    return DW_OK;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- kernel selection
+namespace {
+
+struct PassFns {
+    int (*count)();
+    const char *(*name_of)(int);
+    bool (*feasible)(int, const dw::Geo &, int);
+};
+const PassFns kPassFns[3] = {{dw::fwd_algo_count, dw::fwd_algo_name_of, dw::fwd_algo_feasible},
+                             {dw::bwd_input_algo_count, dw::bwd_input_algo_name_of, dw::bwd_input_algo_feasible},
+                             {dw::bwd_weight_algo_count, dw::bwd_weight_algo_name_of, dw::bwd_weight_algo_feasible}};
+
+// Times every family that can run (pass, g, dtype) with `run` (one compute
+// call) and records the fastest; on an error the previous entry is restored.
+template <class Run>
+int tune_pass(int pass, const dw::Geo &g, int dtype, int reps, hipStream_t s, Run run, const char **chosen) {
+    const PassFns &f = kPassFns[pass];
+    const int prev = dw::tuned_algo(pass, g, dtype);
+    reps = reps < 1 ? 1 : (reps > 1000 ? 1000 : reps);
+    hipEvent_t e0, e1;
+    if (hipEventCreate(&e0) != hipSuccess) return DW_EHIP;
+    if (hipEventCreate(&e1) != hipSuccess) {
+        (void)hipEventDestroy(e0);
+        return DW_EHIP;
+    }
+    int best = -1, rc = DW_OK;
+    float best_ms = 0.f;
+    for (int a = 0; a < f.count() && rc == DW_OK; ++a) {
+        if (!f.feasible(a, g, dtype)) continue;
+        dw::set_tuned_algo(pass, g, dtype, a);
+        rc = run();  // warm-up, and the first error stops the search
+        if (rc != DW_OK) break;
+        if (hipEventRecord(e0, s) != hipSuccess) {
+            rc = DW_EHIP;
+            break;
+        }
+        for (int r = 0; r < reps && rc == DW_OK; ++r) rc = run();
+        if (rc != DW_OK) break;
+        float ms = 0.f;
+        if (hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+            hipEventElapsedTime(&ms, e0, e1) != hipSuccess) {
+            rc = DW_EHIP;
+            break;
+        }
+        if (best < 0 || ms < best_ms) {
+            best = a;
+            best_ms = ms;
+        }
+    }
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    if (rc != DW_OK || best < 0) {
+        dw::set_tuned_algo(pass, g, dtype, prev);
+        return rc != DW_OK ? rc : DW_EUNSUPPORTED;
+    }
+    dw::set_tuned_algo(pass, g, dtype, best);
+    if (chosen) *chosen = f.name_of(best);
     return DW_OK;
 }
 
@@ -303,6 +367,92 @@ const char *dwconv2d_algo(int pass, int64_t n, int64_t ic, int64_t ih, int64_t i
         case 2: return dw::bwd_weight_workspace(g, dtype) >= 0 ? dw::bwd_weight_algo_name(g, dtype) : nullptr;
         default: return nullptr;
     }
+}
+
+int dwconv2d_algo_candidates(int pass, int64_t n, int64_t ic, int64_t ih, int64_t iw, int64_t oc, int64_t kh,
+                             int64_t kw, int64_t stride_h, int64_t stride_w, int64_t pad_h, int64_t pad_w,
+                             int64_t dil_h, int64_t dil_w, int dtype, const char **names, int cap) {
+    if (dtype != DW_F32 && dtype != DW_F16 && dtype != DW_BF16) return DW_EDTYPE;
+    if (pass < 0 || pass > 2) return DW_ESHAPE;
+    dw::Geo g;
+    const int rc = check_geometry(n, ic, ih, iw, oc, kh, kw, stride_h, stride_w, pad_h, pad_w, dil_h, dil_w, &g);
+    if (rc != DW_OK) return rc;
+    if (cap > 0 && !names) return DW_EPTR;
+    const PassFns &f = kPassFns[pass];
+    int cnt = 0;
+    for (int a = 0; a < f.count(); ++a) {
+        if (!f.feasible(a, g, dtype)) continue;
+        if (cnt < cap) names[cnt] = f.name_of(a);
+        ++cnt;
+    }
+    return cnt;
+}
+
+int dwconv2d_set_algo(int pass, int64_t n, int64_t ic, int64_t ih, int64_t iw, int64_t oc, int64_t kh, int64_t kw,
+                      int64_t stride_h, int64_t stride_w, int64_t pad_h, int64_t pad_w, int64_t dil_h,
+                      int64_t dil_w, int dtype, const char *algo) {
+    if (dtype != DW_F32 && dtype != DW_F16 && dtype != DW_BF16) return DW_EDTYPE;
+    if (pass < 0 || pass > 2) return DW_ESHAPE;
+    dw::Geo g;
+    const int rc = check_geometry(n, ic, ih, iw, oc, kh, kw, stride_h, stride_w, pad_h, pad_w, dil_h, dil_w, &g);
+    if (rc != DW_OK) return rc;
+    if (!algo) {
+        dw::set_tuned_algo(pass, g, dtype, -1);
+        return DW_OK;
+    }
+    const PassFns &f = kPassFns[pass];
+    for (int a = 0; a < f.count(); ++a) {
+        if (std::strcmp(f.name_of(a), algo) == 0 && f.feasible(a, g, dtype)) {
+            dw::set_tuned_algo(pass, g, dtype, a);
+            return DW_OK;
+        }
+    }
+    return DW_EUNSUPPORTED;
+}
+
+int dwconv2d_tune_fwd(const void *x, const void *w, const void *bias, void *y, int64_t n, int64_t ic, int64_t ih,
+                      int64_t iw, int64_t oc, int64_t kh, int64_t kw, int64_t stride_h, int64_t stride_w,
+                      int64_t pad_h, int64_t pad_w, int64_t dil_h, int64_t dil_w, int dtype, int reps, void *stream,
+                      const char **chosen) {
+    auto run = [&] {
+        return dwconv2d_fwd(x, w, bias, y, n, ic, ih, iw, oc, kh, kw, stride_h, stride_w, pad_h, pad_w, dil_h, dil_w,
+                            dtype, stream);
+    };
+    const int rc = run();  // full validation with the current choice
+    if (rc != DW_OK) return rc;
+    dw::Geo g;
+    check_geometry(n, ic, ih, iw, oc, kh, kw, stride_h, stride_w, pad_h, pad_w, dil_h, dil_w, &g);
+    return tune_pass(0, g, dtype, reps, static_cast<hipStream_t>(stream), run, chosen);
+}
+
+int dwconv2d_tune_bwd_input(const void *dy, const void *w, void *dx, int64_t n, int64_t ic, int64_t ih, int64_t iw,
+                            int64_t oc, int64_t kh, int64_t kw, int64_t stride_h, int64_t stride_w, int64_t pad_h,
+                            int64_t pad_w, int64_t dil_h, int64_t dil_w, int dtype, int reps, void *stream,
+                            const char **chosen) {
+    auto run = [&] {
+        return dwconv2d_bwd_input(dy, w, dx, n, ic, ih, iw, oc, kh, kw, stride_h, stride_w, pad_h, pad_w, dil_h,
+                                  dil_w, dtype, stream);
+    };
+    const int rc = run();
+    if (rc != DW_OK) return rc;
+    dw::Geo g;
+    check_geometry(n, ic, ih, iw, oc, kh, kw, stride_h, stride_w, pad_h, pad_w, dil_h, dil_w, &g);
+    return tune_pass(1, g, dtype, reps, static_cast<hipStream_t>(stream), run, chosen);
+}
+
+int dwconv2d_tune_bwd_weight(const void *x, const void *dy, void *dwt, void *db, void *workspace,
+                             size_t workspace_bytes, int64_t n, int64_t ic, int64_t ih, int64_t iw, int64_t oc,
+                             int64_t kh, int64_t kw, int64_t stride_h, int64_t stride_w, int64_t pad_h, int64_t pad_w,
+                             int64_t dil_h, int64_t dil_w, int dtype, int reps, void *stream, const char **chosen) {
+    auto run = [&] {
+        return dwconv2d_bwd_weight(x, dy, dwt, db, workspace, workspace_bytes, n, ic, ih, iw, oc, kh, kw, stride_h,
+                                   stride_w, pad_h, pad_w, dil_h, dil_w, dtype, stream);
+    };
+    const int rc = run();
+    if (rc != DW_OK) return rc;
+    dw::Geo g;
+    check_geometry(n, ic, ih, iw, oc, kh, kw, stride_h, stride_w, pad_h, pad_w, dil_h, dil_w, &g);
+    return tune_pass(2, g, dtype, reps, static_cast<hipStream_t>(stream), run, chosen);
 }
 
 const char *dw_status_str(int status) {

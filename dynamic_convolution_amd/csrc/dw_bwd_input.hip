@@ -238,10 +238,41 @@ int run_bwd_input(const Geo &g, const BandPlan &bp, int seg_slots, const void *d
     return hipGetLastError() == hipSuccess ? kOk : kErrHip;
 }
 
-enum BinAlgo { kBinRowwalk = 0, kBinLargek, kBinDecim, kBinBand33s1, kBinBand33s2, kBinBand55s1, kBinBand55s2d2, kBinBandGeneric, kBinChannelGroup, kBinLargekMfma };
+enum BinAlgo { kBinRowwalk = 0, kBinLargek, kBinDecim, kBinBand33s1, kBinBand33s2, kBinBand55s1, kBinBand55s2d2, kBinBandGeneric, kBinChannelGroup, kBinLargekMfma, kBinCount };
 
-// The kernel family a grad-input call launches.
+const char *const kBinNames[kBinCount] = {"rowwalk_3x3",    "largek_regtile", "decimated_s2d2",
+                                          "band_3x3_s1",    "band_3x3_s2",    "band_5x5_s1",
+                                          "band_5x5_s2_d2", "band_generic",   "channelgroup_small",
+                                          "largek_mfma"};
+
+bool band_bin_plans(const Geo &g, int dt) {
+    BandPlan bp;
+    int ss;
+    return dt == 0 ? plan_bwd_input<float>(g, bp, ss) : plan_bwd_input<__half>(g, bp, ss);
+}
+
+bool feasible_bin(int algo, const Geo &g, int dt) {
+    const bool sq = g.kh == g.kw && g.sh == g.sw && g.dh == g.dw;
+    switch (algo) {
+        case kBinRowwalk: return rowwalk_fits(g, dt, 1);
+        case kBinLargek: return largek_fits(g, 1);
+        case kBinDecim: return decim_fits(g, 1);
+        case kBinChannelGroup: return small_bwd_input_fits(g, dt);
+        case kBinLargekMfma: return largek_mfma_fits(g, 1, dt);
+        case kBinBand33s1: return sq && g.kh == 3 && g.sh == 1 && g.dh == 1 && band_bin_plans(g, dt);
+        case kBinBand33s2: return sq && g.kh == 3 && g.sh == 2 && g.dh == 1 && band_bin_plans(g, dt);
+        case kBinBand55s1: return sq && g.kh == 5 && g.sh == 1 && g.dh == 1 && band_bin_plans(g, dt);
+        case kBinBand55s2d2: return sq && g.kh == 5 && g.sh == 2 && g.dh == 2 && band_bin_plans(g, dt);
+        case kBinBandGeneric: return band_bin_plans(g, dt);
+        default: return false;
+    }
+}
+
+// The kernel family a grad-input call launches: the selection table's entry
+// for this geometry, else the built-in rules.
 int select_bwd_input(const Geo &g, int dt) {
+    const int tuned = tuned_algo(1, g, dt);
+    if (tuned >= 0 && feasible_bin(tuned, g, dt)) return tuned;
     if (decim_fits(g, 1)) return kBinDecim;
     if (small_bwd_input_fits(g, dt)) return kBinChannelGroup;
     if (rowwalk_fits(g, dt, 1)) return kBinRowwalk;
@@ -278,12 +309,11 @@ int dispatch_bwd_input(const Geo &g, const void *dy, const void *w, void *dx, hi
 
 }  // namespace
 
-const char *bwd_input_algo_name(const Geo &g, int dtype) {
-    static const char *names[] = {"rowwalk_3x3",    "largek_regtile", "decimated_s2d2", "band_3x3_s1",   "band_3x3_s2",
-                                  "band_5x5_s1",    "band_5x5_s2_d2", "band_generic", "channelgroup_small",
-                                  "largek_mfma"};
-    return names[select_bwd_input(g, dtype)];
-}
+const char *bwd_input_algo_name(const Geo &g, int dtype) { return kBinNames[select_bwd_input(g, dtype)]; }
+
+int bwd_input_algo_count() { return kBinCount; }
+const char *bwd_input_algo_name_of(int algo) { return algo >= 0 && algo < kBinCount ? kBinNames[algo] : nullptr; }
+bool bwd_input_algo_feasible(int algo, const Geo &g, int dtype) { return feasible_bin(algo, g, dtype); }
 
 bool bwd_input_supported(const Geo &g, int dtype) {
     if (small_bwd_input_fits(g, dtype) || rowwalk_fits(g, dtype, 1) || largek_mfma_fits(g, 1, dtype) ||

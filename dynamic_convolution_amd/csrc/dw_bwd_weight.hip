@@ -424,17 +424,59 @@ int run_small(const Geo &g, const BwPlan &p, const void *x, const void *dy, void
     return hipGetLastError() == hipSuccess ? kOk : kErrHip;
 }
 
-enum BwAlgo { kBwChannelGroup = 0, kBwLargek, kBwRowwalk, kBwDecim, kBwBandPixel, kBwBandTaps, kBwLargekMfma };
+enum BwAlgo { kBwChannelGroup = 0, kBwLargek, kBwRowwalk, kBwDecim, kBwBandPixel, kBwBandTaps, kBwLargekMfma, kBwCount };
+
+const char *const kBwNames[kBwCount] = {"channelgroup_small", "largek_regtile", "rowwalk_3x3", "decimated_s2d2",
+                                        "band_pixel",         "band_taps",      "largek_mfma"};
+
+bool band_bw_plans(const Geo &g, int dt) {
+    BwPlan p;
+    return plan_bwd_weight(g, dt == 0 ? 4 : 2, p);
+}
+
+// Whether pass-1 family `algo` can run this geometry (the band kernel's
+// pixel and taps variants are decided by the geometry, not alternatives).
+bool feasible_bw(int algo, const Geo &g, int dt) {
+    switch (algo) {
+        case kBwChannelGroup: return small_fits(g, dt, 2);
+        case kBwLargek: return largek_bwdw_fits(g);
+        case kBwRowwalk: return rowwalk_fits(g, dt, 2);
+        case kBwDecim: return decim_fits(g, 2);
+        case kBwLargekMfma: return largek_mfma_bwdw_fits(g, dt);
+        case kBwBandPixel: return small_variant(g) && band_bw_plans(g, dt);
+        case kBwBandTaps: return !small_variant(g) && band_bw_plans(g, dt);
+        default: return false;
+    }
+}
 
 // The pass-1 kernel family a grad-weight call launches (pass 2 is always the
-// fixed-order chunk reduction).
+// fixed-order chunk reduction): the selection table's entry, else the rules.
 int select_bwd_weight(const Geo &g, int dt) {
+    const int tuned = tuned_algo(2, g, dt);
+    if (tuned >= 0 && feasible_bw(tuned, g, dt)) return tuned;
     if (small_fits(g, dt, 2)) return kBwChannelGroup;
     if (largek_mfma_bwdw_fits(g, dt)) return kBwLargekMfma;
     if (largek_bwdw_fits(g)) return kBwLargek;
     if (rowwalk_fits(g, dt, 2)) return kBwRowwalk;
     if (decim_fits(g, 2)) return kBwDecim;
     return small_variant(g) ? kBwBandPixel : kBwBandTaps;
+}
+
+// Workspace bytes family `algo` needs for this geometry (-1: cannot run it).
+int64_t ws_for(int algo, const Geo &g, int dtype) {
+    const int64_t slots = static_cast<int64_t>(g.mult) * (g.kh * g.kw + 1);
+    switch (algo) {
+        case kBwChannelGroup: return std::max<int64_t>(g.ic * small_bwd_weight_chunks(g, dtype) * slots * 4, 16);
+        case kBwLargek: return std::max<int64_t>(g.ic * largek_bwd_weight_chunks(g) * slots * 4, 16);
+        case kBwLargekMfma: return std::max<int64_t>(g.ic * largek_mfma_bwd_weight_chunks(g) * slots * 4, 16);
+        case kBwRowwalk: return std::max<int64_t>(g.ic * rowwalk_bwd_weight_chunks(g, dtype) * slots * 4, 16);
+        case kBwDecim: return std::max<int64_t>(g.ic * decim_bwd_weight_chunks(g) * slots * 4, 16);
+        default: {
+            BwPlan p;
+            if (!plan_bwd_weight(g, dtype == 0 ? 4 : 2, p)) return -1;
+            return std::max<int64_t>(p.ws_bytes, 16);
+        }
+    }
 }
 
 template <typename T>
@@ -491,23 +533,20 @@ int dispatch_bwd_weight(const Geo &g, const void *x, const void *dy, void *dwt, 
 
 }  // namespace
 
-const char *bwd_weight_algo_name(const Geo &g, int dtype) {
-    static const char *names[] = {"channelgroup_small", "largek_regtile", "rowwalk_3x3", "decimated_s2d2", "band_pixel",
-                                  "band_taps",          "largek_mfma"};
-    return names[select_bwd_weight(g, dtype)];
-}
+const char *bwd_weight_algo_name(const Geo &g, int dtype) { return kBwNames[select_bwd_weight(g, dtype)]; }
 
+int bwd_weight_algo_count() { return kBwCount; }
+const char *bwd_weight_algo_name_of(int algo) { return algo >= 0 && algo < kBwCount ? kBwNames[algo] : nullptr; }
+bool bwd_weight_algo_feasible(int algo, const Geo &g, int dtype) { return feasible_bw(algo, g, dtype); }
+
+// The largest workspace any family that can run this geometry needs, so a
+// buffer sized by it serves whichever family the selection table picks
+// (-1 when no family can run it).
 int64_t bwd_weight_workspace(const Geo &g, int dtype) {
-    const int algo = select_bwd_weight(g, dtype);
-    const int64_t slots = static_cast<int64_t>(g.mult) * (g.kh * g.kw + 1);
-    if (algo == kBwChannelGroup) return std::max<int64_t>(g.ic * small_bwd_weight_chunks(g, dtype) * slots * 4, 16);
-    if (algo == kBwLargek) return std::max<int64_t>(g.ic * largek_bwd_weight_chunks(g) * slots * 4, 16);
-    if (algo == kBwLargekMfma) return std::max<int64_t>(g.ic * largek_mfma_bwd_weight_chunks(g) * slots * 4, 16);
-    if (algo == kBwRowwalk) return std::max<int64_t>(g.ic * rowwalk_bwd_weight_chunks(g, dtype) * slots * 4, 16);
-    if (algo == kBwDecim) return std::max<int64_t>(g.ic * decim_bwd_weight_chunks(g) * slots * 4, 16);
-    BwPlan p;
-    if (!plan_bwd_weight(g, dtype == 0 ? 4 : 2, p)) return -1;
-    return std::max<int64_t>(p.ws_bytes, 16);
+    int64_t need = -1;
+    for (int a = 0; a < kBwCount; ++a)
+        if (feasible_bw(a, g, dtype)) need = std::max(need, ws_for(a, g, dtype));
+    return need;
 }
 
 int launch_bwd_weight(const Geo &g, const void *x, const void *dy, void *dwt, void *db, void *ws, int dtype,

@@ -238,11 +238,43 @@ int run_fwd(const Geo &g, const BandPlan &bp, const void *x, const void *w, cons
     return hipGetLastError() == hipSuccess ? kOk : kErrHip;
 }
 
-enum FwdAlgo { kFwdRowwalk = 0, kFwdLargek, kFwdDecim, kFwdBand33s1, kFwdBand33s2, kFwdBand55s1, kFwdBand55s2d2, kFwdBandGeneric, kFwdChannelGroup, kFwdLargekMfma };
+enum FwdAlgo { kFwdRowwalk = 0, kFwdLargek, kFwdDecim, kFwdBand33s1, kFwdBand33s2, kFwdBand55s1, kFwdBand55s2d2, kFwdBandGeneric, kFwdChannelGroup, kFwdLargekMfma, kFwdCount };
+
+const char *const kFwdNames[kFwdCount] = {"rowwalk_3x3",    "largek_regtile", "decimated_s2d2",
+                                          "band_3x3_s1",    "band_3x3_s2",    "band_5x5_s1",
+                                          "band_5x5_s2_d2", "band_generic",   "channelgroup_small",
+                                          "largek_mfma"};
+
+bool band_fwd_plans(const Geo &g, int dt) {
+    BandPlan bp;
+    return dt == 0 ? plan_fwd<float>(g, bp) : plan_fwd<__half>(g, bp);
+}
+
+// Whether family `algo` can run this geometry (each family's own fit test;
+// the specialised band variants need their exact geometry).
+bool feasible_fwd(int algo, const Geo &g, int dt) {
+    const bool sq = g.kh == g.kw && g.sh == g.sw && g.dh == g.dw;
+    switch (algo) {
+        case kFwdRowwalk: return rowwalk_fits(g, dt, 0);
+        case kFwdLargek: return largek_fits(g, 0);
+        case kFwdDecim: return decim_fits(g, 0);
+        case kFwdChannelGroup: return small_fwd_fits(g, dt);
+        case kFwdLargekMfma: return largek_mfma_fits(g, 0, dt);
+        case kFwdBand33s1: return sq && g.kh == 3 && g.sh == 1 && g.dh == 1 && band_fwd_plans(g, dt);
+        case kFwdBand33s2: return sq && g.kh == 3 && g.sh == 2 && g.dh == 1 && band_fwd_plans(g, dt);
+        case kFwdBand55s1: return sq && g.kh == 5 && g.sh == 1 && g.dh == 1 && band_fwd_plans(g, dt);
+        case kFwdBand55s2d2: return sq && g.kh == 5 && g.sh == 2 && g.dh == 2 && band_fwd_plans(g, dt);
+        case kFwdBandGeneric: return band_fwd_plans(g, dt);
+        default: return false;
+    }
+}
 
 // The kernel family a forward call launches (the dispatcher and the
-// introspection helper both use this one decision).
+// introspection helper both use this one decision): a family recorded in the
+// selection table for this geometry, else the built-in rules.
 int select_fwd(const Geo &g, int dt) {
+    const int tuned = tuned_algo(0, g, dt);
+    if (tuned >= 0 && feasible_fwd(tuned, g, dt)) return tuned;
     if (rowwalk_fits(g, dt, 0)) return kFwdRowwalk;
     if (largek_mfma_fits(g, 0, dt)) return kFwdLargekMfma;
     if (largek_fits(g, 0)) return kFwdLargek;
@@ -278,12 +310,11 @@ int dispatch_fwd(const Geo &g, const void *x, const void *w, const void *b, void
 
 }  // namespace
 
-const char *fwd_algo_name(const Geo &g, int dtype) {
-    static const char *names[] = {"rowwalk_3x3",    "largek_regtile", "decimated_s2d2", "band_3x3_s1",   "band_3x3_s2",
-                                  "band_5x5_s1",    "band_5x5_s2_d2", "band_generic", "channelgroup_small",
-                                  "largek_mfma"};
-    return names[select_fwd(g, dtype)];
-}
+const char *fwd_algo_name(const Geo &g, int dtype) { return kFwdNames[select_fwd(g, dtype)]; }
+
+int fwd_algo_count() { return kFwdCount; }
+const char *fwd_algo_name_of(int algo) { return algo >= 0 && algo < kFwdCount ? kFwdNames[algo] : nullptr; }
+bool fwd_algo_feasible(int algo, const Geo &g, int dtype) { return feasible_fwd(algo, g, dtype); }
 
 bool fwd_supported(const Geo &g, int dtype) {
     if (rowwalk_fits(g, dtype, 0) || largek_mfma_fits(g, 0, dtype) || largek_fits(g, 0) || decim_fits(g, 0) ||

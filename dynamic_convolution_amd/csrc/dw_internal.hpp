@@ -99,6 +99,22 @@ const char *fwd_algo_name(const Geo &g, int dtype);
 const char *bwd_input_algo_name(const Geo &g, int dtype);
 const char *bwd_weight_algo_name(const Geo &g, int dtype);
 
+// Every family of a pass, by index: its name and whether it can run a geometry.
+int fwd_algo_count();
+const char *fwd_algo_name_of(int algo);
+bool fwd_algo_feasible(int algo, const Geo &g, int dtype);
+int bwd_input_algo_count();
+const char *bwd_input_algo_name_of(int algo);
+bool bwd_input_algo_feasible(int algo, const Geo &g, int dtype);
+int bwd_weight_algo_count();
+const char *bwd_weight_algo_name_of(int algo);
+bool bwd_weight_algo_feasible(int algo, const Geo &g, int dtype);
+
+// Selection table (dw_tune.hip): the family recorded for (pass, geometry,
+// dtype), or -1; set_tuned_algo records one (algo < 0 removes the entry).
+int tuned_algo(int pass, const Geo &g, int dtype);
+void set_tuned_algo(int pass, const Geo &g, int dtype, int algo);
+
 // Shape checks the launchers need beyond argument validation (LDS fit).
 bool fwd_supported(const Geo &g, int dtype);
 bool bwd_input_supported(const Geo &g, int dtype);

@@ -18,7 +18,8 @@
  * ------------------
  *  - Every tensor pointer is a DEVICE pointer to a dense, row-major (NCHW)
  *    array owned by the caller.  The library never allocates or frees device
- *    memory, never synchronises and keeps no pointer after a call returns.
+ *    memory, never synchronises (the dwconv2d_tune_* calls excepted) and
+ *    keeps no pointer after a call returns.
  *    Host arrays (filters[], dilations[]) are read during the call only.
  *  - dtype selects the element type of every tensor of the call: DW_F32,
  *    DW_F16 (IEEE binary16) or DW_BF16 (bfloat16).  Arithmetic is fp32;
@@ -33,8 +34,11 @@
  *  - Errors: a negative status code, never an abort, exception or print.
  *    All argument checks run before any HIP call; when one fails nothing is
  *    launched and no output is touched.  DW_EHIP reports a failed launch.
- *  - Thread safety: the library is stateless; concurrent calls on different
- *    streams with disjoint outputs are safe.
+ *  - Thread safety: concurrent calls on different streams with disjoint
+ *    outputs are safe.  The only state is the kernel-selection table
+ *    (dwconv2d_set_algo / dwconv2d_tune_*), guarded by a mutex; it changes
+ *    which kernel family runs, never the values a call may produce beyond
+ *    fp32 rounding order.
  */
 #ifndef DWCONV_H
 #define DWCONV_H
@@ -112,7 +116,9 @@ int dwconv2d_bwd_input(const void *dy, const void *w, void *dx,
 
 /*
  * Bytes of device workspace dwconv2d_bwd_weight needs for this geometry and
- * dtype (always > 0).  Writes *bytes; returns a status as dwconv2d_out_size.
+ * dtype (always > 0): the largest any kernel family that can run the
+ * geometry needs, so the buffer serves whichever family is selected.
+ * Writes *bytes; returns a status as dwconv2d_out_size.
  */
 int dwconv2d_bwd_weight_workspace_bytes(int64_t n, int64_t ic, int64_t ih, int64_t iw,
                                         int64_t oc, int64_t kh, int64_t kw,
@@ -229,6 +235,65 @@ const char *dwconv2d_algo(int pass, int64_t n, int64_t ic, int64_t ih, int64_t i
                           int64_t oc, int64_t kh, int64_t kw,
                           int64_t stride_h, int64_t stride_w, int64_t pad_h, int64_t pad_w,
                           int64_t dil_h, int64_t dil_w, int dtype);
+
+/*
+ * Kernel selection per geometry (the MegEngine large-kernel depthwise article
+ * chooses among its algorithms automatically; here the choice is measured on
+ * the device the library runs on).  Several kernel families can often run one
+ * geometry -- the names dwconv2d_algo returns.  A process-wide table, keyed by
+ * (pass, dtype, the 13 geometry integers), overrides the built-in choice; the
+ * compute calls and dwconv2d_algo consult it.  Every family computes the same
+ * sums (fp32 accumulation in its own order), so the table affects speed, not
+ * the tolerance results meet.
+ *
+ * dwconv2d_algo_candidates: writes the names (static strings) of the families
+ *   that can run `pass` for this geometry and dtype into names[0..cap) and
+ *   returns how many there are (which may exceed cap; names may be NULL when
+ *   cap is 0), or a negative status.  Host only.
+ * dwconv2d_set_algo: records family `algo` (one of the candidates' names) for
+ *   this key, or removes the key's entry when algo is NULL.  Returns
+ *   DW_EUNSUPPORTED for a name that cannot run the geometry.  Host only.
+ * dwconv2d_tune_fwd / _bwd_input / _bwd_weight: take exactly the arguments of
+ *   the matching compute call (outputs are overwritten, several times), plus
+ *   `reps` (timed calls per candidate, clamped to 1..1000) and `chosen`
+ *   (NULL, or where to write the winner's name).  After one validating call
+ *   they run every candidate once, then `reps` times between two HIP events
+ *   on `stream`, and record the fastest for this key.  They synchronise on
+ *   the events and must not be called during stream capture.  For
+ *   grad-weight, dwconv2d_bwd_weight_workspace_bytes already covers every
+ *   candidate.  On error the key's previous entry is restored.
+ */
+int dwconv2d_algo_candidates(int pass, int64_t n, int64_t ic, int64_t ih, int64_t iw,
+                             int64_t oc, int64_t kh, int64_t kw,
+                             int64_t stride_h, int64_t stride_w, int64_t pad_h, int64_t pad_w,
+                             int64_t dil_h, int64_t dil_w, int dtype, const char **names, int cap);
+
+int dwconv2d_set_algo(int pass, int64_t n, int64_t ic, int64_t ih, int64_t iw,
+                      int64_t oc, int64_t kh, int64_t kw,
+                      int64_t stride_h, int64_t stride_w, int64_t pad_h, int64_t pad_w,
+                      int64_t dil_h, int64_t dil_w, int dtype, const char *algo);
+
+int dwconv2d_tune_fwd(const void *x, const void *w, const void *bias, void *y,
+                      int64_t n, int64_t ic, int64_t ih, int64_t iw,
+                      int64_t oc, int64_t kh, int64_t kw,
+                      int64_t stride_h, int64_t stride_w, int64_t pad_h, int64_t pad_w,
+                      int64_t dil_h, int64_t dil_w, int dtype, int reps, void *stream,
+                      const char **chosen);
+
+int dwconv2d_tune_bwd_input(const void *dy, const void *w, void *dx,
+                            int64_t n, int64_t ic, int64_t ih, int64_t iw,
+                            int64_t oc, int64_t kh, int64_t kw,
+                            int64_t stride_h, int64_t stride_w, int64_t pad_h, int64_t pad_w,
+                            int64_t dil_h, int64_t dil_w, int dtype, int reps, void *stream,
+                            const char **chosen);
+
+int dwconv2d_tune_bwd_weight(const void *x, const void *dy, void *dw, void *db,
+                             void *workspace, size_t workspace_bytes,
+                             int64_t n, int64_t ic, int64_t ih, int64_t iw,
+                             int64_t oc, int64_t kh, int64_t kw,
+                             int64_t stride_h, int64_t stride_w, int64_t pad_h, int64_t pad_w,
+                             int64_t dil_h, int64_t dil_w, int dtype, int reps, void *stream,
+                             const char **chosen);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char *dw_status_str(int status);

@@ -208,6 +208,61 @@ def test_dynconv_into_validation():
     assert frm(FAKE, f3, y, 20, 4, d3, 3, y + 64, None, *geo, 0, None) == -7   # dx inside the larger dy
     assert frm(FAKE, f3, y, 20, 4, d3, 3, None, None, *geo, 0, None) == 0      # nothing requested
 
+
+@pytest.mark.parametrize("pass_,geo,dtype,must", [
+    (0, ((128, 128, 56, 56), (128, 3, 3), 1, 1, 1), torch.float32, {"rowwalk_3x3", "band_3x3_s1", "band_generic"}),
+    (1, ((128, 128, 56, 56), (128, 3, 3), 2, 1, 1), torch.float32, {"rowwalk_3x3", "band_generic"}),
+    (2, ((128, 1024, 7, 7), (1024, 3, 3), 2, 1, 1), torch.float32, {"channelgroup_small"}),
+    (0, ((64, 384, 64, 64), (384, 31, 31), 1, 15, 1), torch.float16, {"largek_mfma", "largek_regtile"}),
+    (2, ((64, 384, 64, 64), (384, 31, 31), 1, 15, 1), torch.bfloat16, {"largek_mfma", "largek_regtile"}),
+    (1, ((128, 256, 56, 56), (512, 5, 5), 2, 4, 2), torch.bfloat16, {"decimated_s2d2", "band_generic"}),
+])
+def test_algo_candidates_and_selection_table(pass_, geo, dtype, must):
+    cands = N.dwconv2d_algo_candidates(pass_, *geo, dtype=dtype)
+    assert must <= set(cands), cands
+    default = N.dwconv2d_algo(pass_, *geo, dtype=dtype)
+    assert default in cands
+    try:
+        for name in cands:
+            N.dwconv2d_set_algo(pass_, *geo, dtype=dtype, algo=name)
+            assert N.dwconv2d_algo(pass_, *geo, dtype=dtype) == name
+        with pytest.raises(N.DwconvError):
+            N.dwconv2d_set_algo(pass_, *geo, dtype=dtype, algo="no_such_family")
+        # another dtype or pass of the same geometry is a different key
+        other = 0 if pass_ else 1
+        assert N.dwconv2d_algo(other, *geo, dtype=dtype) == N.dwconv2d_algo(other, *geo, dtype=dtype)
+    finally:
+        N.dwconv2d_set_algo(pass_, *geo, dtype=dtype, algo=None)
+    assert N.dwconv2d_algo(pass_, *geo, dtype=dtype) == default
+
+
+def test_algo_candidates_validation():
+    L = N.lib()
+    names = (ctypes.c_char_p * 4)()
+    g = _geo()
+    assert L.dwconv2d_algo_candidates(3, *g, 0, names, 4) == -2       # no such pass
+    assert L.dwconv2d_algo_candidates(0, *g, 7, names, 4) == -4       # dtype
+    assert L.dwconv2d_algo_candidates(0, *g, 0, None, 4) == -1        # names needed when cap > 0
+    cnt = L.dwconv2d_algo_candidates(0, *g, 0, None, 0)               # count only
+    assert cnt >= 1 and L.dwconv2d_algo_candidates(0, *g, 0, names, 1) == cnt
+    assert L.dwconv2d_algo_candidates(0, *_geo(oc=4), 0, names, 4) == -3
+    assert L.dwconv2d_set_algo(0, *g, 0, b"band_generic") == 0
+    assert L.dwconv2d_set_algo(0, *g, 0, None) == 0
+    assert L.dwconv2d_set_algo(0, *g, 0, b"largek_mfma") == -10        # cannot run a 3x3 fp32 layer
+
+
+def test_workspace_covers_every_candidate():
+    import torch as T
+    for geo, dt in ((((64, 384, 64, 64), (384, 31, 31), 1, 15, 1), T.float16),
+                    (((128, 32, 112, 112), (32, 3, 3), 1, 1, 1), T.float32)):
+        need = N.dwconv2d_bwd_weight_workspace_bytes(*geo, dt)
+        try:
+            for name in N.dwconv2d_algo_candidates(2, *geo, dtype=dt):
+                N.dwconv2d_set_algo(2, *geo, dtype=dt, algo=name)
+                assert N.dwconv2d_bwd_weight_workspace_bytes(*geo, dt) == need
+        finally:
+            N.dwconv2d_set_algo(2, *geo, dtype=dt, algo=None)
+
 def test_binding_refuses_cpu_tensors():
     x = torch.zeros(1, 2, 5, 5)
     w = torch.zeros(2, 3, 3)

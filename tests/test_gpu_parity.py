@@ -280,6 +280,55 @@ def test_dynamic_into_larger_concat(shape, k, dils, off, extra, dtype):
     for a_, b_ in zip(dfs0, dfs):
         assert torch.equal(a_, b_)
 
+
+# ------------------------------------------------------------------ every kernel family a geometry can run
+SELECT_CASES = [
+    (2, 6, 20, 24, 1, 3, 1, 1, 1, "f32"),      # 3x3 stride 1: row-walk, band 3x3, band generic
+    (2, 6, 28, 28, 1, 3, 2, 1, 1, "f32"),      # 3x3 stride 2
+    (2, 3, 20, 22, 2, 5, 2, 4, 2, "bf16"),     # multiplier 2, dilation 2, stride 2: even grid and band kernels
+    (1, 2, 40, 40, 1, 31, 1, 15, 1, "f16"),    # 31x31: matrix cores, register tiles, band kernels
+    (3, 20, 7, 7, 1, 3, 1, 1, 1, "f32"),       # small planes: channel groups, row-walk, band
+    (1, 2, 33, 36, 1, 13, 1, 6, 1, "bf16"),    # 13x13
+]
+
+
+@pytest.mark.parametrize("n,c,h,w,mult,k,s,p,d,dt", SELECT_CASES)
+def test_every_candidate_family_matches_oracle(n, c, h, w, mult, k, s, p, d, dt):
+    x, wt, b, dy = static_case(n, c, h, w, mult, k, s, p, d, DT[dt], 1100 + h + w + k)
+    geo = (x.shape, wt.shape, s, p, d)
+    passes = {0: "fwd", 1: "bwd_in", 2: "bwd_w"}
+    try:
+        for pi, pname in passes.items():
+            cands = dc.dwconv2d_algo_candidates(pi, *geo, dtype=DT[dt])
+            assert len(cands) >= 1
+            for name in cands:
+                dc.dwconv2d_set_algo(pi, *geo, dtype=DT[dt], algo=name)
+                check_static(x, wt, b, dy, s, p, d, "family %s %s n%d c%d %dx%d k%d s%d %s"
+                             % (pname, name, n, c, h, w, k, s, dt), passes=(pname,))
+            dc.dwconv2d_set_algo(pi, *geo, dtype=DT[dt], algo=None)
+    finally:
+        for pi in passes:
+            dc.dwconv2d_set_algo(pi, *geo, dtype=DT[dt], algo=None)
+
+
+@pytest.mark.parametrize("n,c,h,w,mult,k,s,p,d,dt", [SELECT_CASES[0], SELECT_CASES[3]])
+def test_tuned_selection_is_used_and_correct(n, c, h, w, mult, k, s, p, d, dt):
+    x, wt, b, dy = static_case(n, c, h, w, mult, k, s, p, d, DT[dt], 1200 + h + k)
+    xd, wd, bd, dyd = x.to(DEV), wt.to(DEV), b.to(DEV), dy.to(DEV)
+    geo = (x.shape, wt.shape, s, p, d)
+    note("tune n%d c%d %dx%d k%d %s" % (n, c, h, w, k, dt))
+    try:
+        got = [dc.dwconv2d_tune_fwd(xd, wd, bd, s, p, d, reps=3),
+               dc.dwconv2d_tune_bwd_input(dyd, wd, x.shape, s, p, d, reps=3),
+               dc.dwconv2d_tune_bwd_weight(xd, dyd, wt.shape, s, p, d, reps=3)]
+        for pi, name in enumerate(got):
+            assert name in dc.dwconv2d_algo_candidates(pi, *geo, dtype=DT[dt])
+            assert dc.dwconv2d_algo(pi, *geo, dtype=DT[dt]) == name
+        check_static(x, wt, b, dy, s, p, d, "tuned %s" % (got,))
+    finally:
+        for pi in range(3):
+            dc.dwconv2d_set_algo(pi, *geo, dtype=DT[dt], algo=None)
+
 def fuzz_cases(count=48, seed=2024):
     r = random.Random(seed)
     out = []
