@@ -553,30 +553,39 @@ def test_streaming_3x3_shapes(n, c, h, w, mult, s, dt):
 def test_graph_replay_matches_eager():
     """Every entry point captured in a HIP graph: each of several replays, with eager
     work and synchronisation in between, reproduces the eager result bitwise."""
-    cases = [(4, 8, 112, 112, 1, 1), (4, 8, 56, 56, 2, 2), (3, 5, 14, 14, 1, 2)]  # streaming and band paths
+    # streaming and band paths (fp32 3x3), and the 16-bit 31x31 matrix-core path
+    cases = [(4, 8, 112, 112, 1, 3, 1, 1, torch.float32), (4, 8, 56, 56, 2, 3, 2, 1, torch.float32),
+             (3, 5, 14, 14, 1, 3, 2, 1, torch.float32), (5, 2, 64, 64, 1, 31, 1, 15, torch.float16)]
     work = []
-    for n, c, h, w, mult, s in cases:
-        x, wt, b, dy = static_case(n, c, h, w, mult, 3, s, 1, 1, torch.float32, 17 + h)
+    for n, c, h, w, mult, k, s, p, dt in cases:
+        x, wt, b, dy = static_case(n, c, h, w, mult, k, s, p, 1, dt, 17 + h + k)
         xd, wd, bd, dyd = x.to(DEV), wt.to(DEV), b.to(DEV), dy.to(DEV)
-        y = torch.empty((n, c * mult) + tuple(dy.shape[2:]), device=DEV)
+        y = torch.empty((n, c * mult) + tuple(dy.shape[2:]), device=DEV, dtype=dt)
         dx, gw, gb = torch.empty_like(xd), torch.empty_like(wd), torch.empty_like(bd)
-        ws = torch.empty((dc.dwconv2d_bwd_weight_workspace_bytes(x.shape, wt.shape, s, 1, 1),),
+        ws = torch.empty((dc.dwconv2d_bwd_weight_workspace_bytes(x.shape, wt.shape, s, p, 1, dt),),
                          dtype=torch.uint8, device=DEV)
-        work.append(lambda xd=xd, wd=wd, bd=bd, dyd=dyd, y=y, dx=dx, gw=gw, gb=gb, ws=ws, s=s: (
-            dc.dwconv2d_fwd(xd, wd, bd, s, 1, 1, out=y),
-            dc.dwconv2d_bwd_input(dyd, wd, xd.shape, s, 1, 1, out=dx),
-            dc.dwconv2d_bwd_weight(xd, dyd, wd.shape, s, 1, 1, out=gw, out_bias=gb, workspace=ws)))
+        work.append(lambda xd=xd, wd=wd, bd=bd, dyd=dyd, y=y, dx=dx, gw=gw, gb=gb, ws=ws, s=s, p=p: (
+            dc.dwconv2d_fwd(xd, wd, bd, s, p, 1, out=y),
+            dc.dwconv2d_bwd_input(dyd, wd, xd.shape, s, p, 1, out=dx),
+            dc.dwconv2d_bwd_weight(xd, dyd, wd.shape, s, p, 1, out=gw, out_bias=gb, workspace=ws)))
         work[-1].outs = (y, dx, gw, gb)
     xq, fs = dyn_inputs(1, 4, 64, 64, 3, (1, 3, 5), torch.float32, 19)
     xqd, fsd = xq.to(DEV), [f.to(DEV) for f in fs]
+    gq = synth.draw((1, 12, 64, 64), ("N", 0.0, 1.0), 19, "dy", device=DEV)
     yq = torch.empty((1, 12, 64, 64), device=DEV)
-    dynf = lambda: dc.dynconv_multidil_fwd(xqd, fsd, (1, 3, 5), out=yq)
+    dxq = torch.empty_like(xqd)
+    dfq = [torch.empty_like(f) for f in fsd]
+
+    def dynf():
+        dc.dynconv_multidil_fwd(xqd, fsd, (1, 3, 5), out=yq)
+        dc.dynconv_multidil_bwd(xqd, fsd, gq, (1, 3, 5), out_dx=dxq, out_dfilters=dfq)
+    dyn_outs = (yq, dxq) + tuple(dfq)
     note("graph eager")
     for fn in work:
         fn()
     dynf()
     torch.cuda.synchronize()
-    ref = [tuple(t.clone() for t in fn.outs) for fn in work] + [(yq.clone(),)]
+    ref = [tuple(t.clone() for t in fn.outs) for fn in work] + [tuple(t.clone() for t in dyn_outs)]
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for fn in work:
@@ -586,15 +595,35 @@ def test_graph_replay_matches_eager():
         for fn in work:  # poison outputs eagerly between replays
             for t in fn.outs:
                 t.fill_(float("nan"))
-        yq.fill_(float("nan"))
+        for t in dyn_outs:
+            t.fill_(float("nan"))
         torch.cuda.synchronize()
         note("graph replay %d" % rep)
         g.replay()
         torch.cuda.synchronize()
-        got = [fn.outs for fn in work] + [(yq,)]
+        got = [fn.outs for fn in work] + [dyn_outs]
         for a_, b_ in zip(got, ref):
             for t1, t2 in zip(a_, b_):
                 assert torch.equal(t1, t2), "replay %d differs from eager" % rep
+
+
+@pytest.mark.parametrize("n,c,h,k,p,dt", [(5, 3, 64, 31, 15, "f16"), (4, 2, 48, 13, 6, "bf16"),
+                                          (3, 2, 32, 7, 3, "f16")])
+def test_large_kernel_matrix_core_deterministic(n, c, h, k, p, dt):
+    """The matrix-core passes give bitwise identical results run to run."""
+    x, wt, b, dy = static_case(n, c, h, h, 1, k, 1, p, 1, DT[dt], 1300 + h + k)
+    xd, wd, bd, dyd = x.to(DEV), wt.to(DEV), b.to(DEV), dy.to(DEV)
+    note("mfma determinism k%d %s" % (k, dt))
+    runs = []
+    for _ in range(3):
+        y = dc.dwconv2d_fwd(xd, wd, bd, 1, p, 1)
+        dx = dc.dwconv2d_bwd_input(dyd, wd, xd.shape, 1, p, 1)
+        gw, gb = dc.dwconv2d_bwd_weight(xd, dyd, wd.shape, 1, p, 1)
+        torch.cuda.synchronize()
+        runs.append((y, dx, gw, gb))
+    for r in runs[1:]:
+        for t1, t2 in zip(runs[0], r):
+            assert torch.equal(t1, t2)
 
 
 # ------------------------------------------------------------------ large-kernel path edges
