@@ -17,10 +17,13 @@
 // even elements are kept, the column halo of h values on each side comes from
 // the neighbouring lanes by shuffle, and the k rows of the window stay in
 // registers as a ring indexed at compile time (the row loop is unrolled by k).
-// Rows are loaded kPF rows ahead and kept as raw 32-bit words until they enter
-// the window, so those loads stay in flight across the arithmetic of the rows
-// before them; rows outside the plane are read from a clamped address and
-// replaced by zeros on conversion, which keeps the loads branch-free.
+// Rows are loaded k rows ahead and kept as raw 32-bit words until they enter
+// the window, in k buffers indexed by the row's step modulo k (a compile-time
+// index in the row loop unrolled by k, so no buffer is ever copied to another:
+// a copy would make the compiler wait for that buffer's load and leave one
+// load in flight); those loads stay in flight across the arithmetic of the
+// rows before them.  Rows outside the plane are read from a clamped address
+// and replaced by zeros on conversion, which keeps the loads branch-free.
 // Forward and grad-input waves each serve one channel (several images or row
 // bands of it), so the filter taps are wave-uniform and live in scalar registers.
 #include "dw_internal.hpp"
@@ -30,8 +33,7 @@ namespace dw {
 namespace {
 
 constexpr int kWaves = kThreads / 64;
-constexpr int RO = 4;   // decimated columns per lane
-constexpr int kPF = 2;  // raw rows loaded ahead of the row entering the window
+constexpr int RO = 4;  // decimated columns per lane
 
 // 32-bit words of a lane's x segment (2*RO elements) and of a dy / y strip (RO elements).
 template <typename T> constexpr int kXWords = 2 * RO * static_cast<int>(sizeof(T)) / 4;
@@ -129,8 +131,10 @@ __global__ __launch_bounds__(kThreads) void dec_fwd_kernel(DcArgs<T> a) {
     const int oh0 = u.band * a.BH, oh_end = min(oh0 + a.BH, g.oh);
     // relative row j (absolute decimated row oh0 - HH + j) lives in window slot j % K
     float win[K][WW];
-    uint32_t rq[kPF][NX];
-    bool rk[kPF];
+    // rq[f]: raw relative row K-1+f, +K per pass of the row loop (it enters the
+    // window at step f of the pass)
+    uint32_t rq[K][NX];
+    bool rk[K];
 #pragma unroll
     for (int j = 0; j < K - 1; ++j) {
         uint32_t w[NX];
@@ -139,16 +143,20 @@ __global__ __launch_bounds__(kThreads) void dec_fwd_kernel(DcArgs<T> a) {
         xrow_window<T, HH>(w, ok, u.lane, hl, hr, win[j]);
     }
 #pragma unroll
-    for (int f = 0; f < kPF; ++f) load_xrow<T, FULL>(xp, oh0 - HH + K - 1 + f, a.XH, g.iw, c0, u.act, rq[f], rk[f]);
+    for (int f = 0; f < K; ++f) load_xrow<T, FULL>(xp, oh0 - HH + K - 1 + f, a.XH, g.iw, c0, u.act, rq[f], rk[f]);
     for (int t0 = 0; t0 < a.BH; t0 += K) {  // BH is a multiple of K
         uint32_t ybuf[K][MM][ND];  // packed outputs of this iteration's K rows
 #pragma unroll
         for (int uu = 0; uu < K; ++uu) {
             const int t = t0 + uu;
             {
-                xrow_window<T, HH>(rq[0], rk[0], u.lane, hl, hr, win[(uu + K - 1) % K]);
-                ring_pop<kPF, NX>(rq, rk);
-                load_xrow<T, FULL>(xp, oh0 - HH + t + K - 1 + kPF, a.XH, g.iw, c0, u.act, rq[kPF - 1], rk[kPF - 1]);
+                {
+                    uint32_t cw[NX];
+                    take_words<T>(rq[uu], cw);
+                    xrow_window<T, HH>(cw, rk[uu], u.lane, hl, hr, win[(uu + K - 1) % K]);
+                }
+                load_xrow<T, FULL>(xp, oh0 - HH + t + 2 * K - 1, a.XH, g.iw, c0, u.act, rq[uu], rk[uu]);
+                __builtin_amdgcn_sched_barrier(0);
                 const int oh = oh0 + t;
 #pragma unroll
                 for (int m = 0; m < MM; ++m) {
@@ -326,8 +334,9 @@ __global__ __launch_bounds__(kThreads) void dec_bwdw_kernel(DcArgs<T> a) {
         // relative x row j (decimated row oh0 - HH + j) lives in window slot j % K;
         // dy row oh0 + t is used at step t
         float win[K][WW];
-        uint32_t rq[kPF][NX];
-        bool rk[kPF];
+        // rq[f]: raw relative x row K-1+f, +K per K steps (as in the forward)
+        uint32_t rq[K][NX];
+        bool rk[K];
 #pragma unroll
         for (int j = 0; j < K - 1; ++j) {
             uint32_t w[NX];
@@ -336,7 +345,7 @@ __global__ __launch_bounds__(kThreads) void dec_bwdw_kernel(DcArgs<T> a) {
             xrow_window<T, HH>(w, ok, lane, hl, hr, win[j]);
         }
 #pragma unroll
-        for (int f = 0; f < kPF; ++f) load_xrow<T, FULL>(xp, oh0 - HH + K - 1 + f, a.XH, g.iw, c0, act, rq[f], rk[f]);
+        for (int f = 0; f < K; ++f) load_xrow<T, FULL>(xp, oh0 - HH + K - 1 + f, a.XH, g.iw, c0, act, rq[f], rk[f]);
         // dy rows: the K rows of an iteration are loaded as one burst an
         // iteration ahead into two alternating buffers (a slot's consecutive dy
         // rows share cache lines; rows read one step apart were fetched twice)
@@ -352,9 +361,13 @@ __global__ __launch_bounds__(kThreads) void dec_bwdw_kernel(DcArgs<T> a) {
 #pragma unroll
             for (int uu = 0; uu < K; ++uu) {
                 const int t = t0 + uu;
-                xrow_window<T, HH>(rq[0], rk[0], lane, hl, hr, win[(uu + K - 1) % K]);
-                ring_pop<kPF, NX>(rq, rk);
-                load_xrow<T, FULL>(xp, oh0 - HH + t + K - 1 + kPF, a.XH, g.iw, c0, act, rq[kPF - 1], rk[kPF - 1]);
+                {
+                    uint32_t cw[NX];
+                    take_words<T>(rq[uu], cw);
+                    xrow_window<T, HH>(cw, rk[uu], lane, hl, hr, win[(uu + K - 1) % K]);
+                }
+                load_xrow<T, FULL>(xp, oh0 - HH + t + 2 * K - 1, a.XH, g.iw, c0, act, rq[uu], rk[uu]);
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int m = 0; m < MM; ++m) {
                     float gy[RO];

@@ -7,10 +7,13 @@
 // behind barriers, every lane owns one 16-byte column strip of a plane and
 // walks down a band of rows:
 //   - each input row segment is read with one 16-byte load (two for a stride-2
-//     forward segment) several rows ahead of its use and kept as raw words
+//     forward segment) three steps ahead of its use and kept as raw words
 //     until it enters the window, so those loads stay in flight across the
-//     arithmetic of the rows before it; rows outside the plane are read from
-//     a clamped row and zeroed on conversion, so the loads need no branch;
+//     arithmetic of the rows before it; the raw rows sit in one buffer per
+//     row of an unrolled pass of the row loop, indexed at compile time (a
+//     buffer copied into another would make the compiler wait for its load);
+//     rows outside the plane are read from a clamped row and zeroed on
+//     conversion, so the loads need no branch;
 //   - the column halo (one element left/right) comes from the neighbouring
 //     lanes by shuffle, the row halo from a ring of the last three rows kept
 //     in registers and indexed at compile time (the row loop is unrolled by 3);
@@ -62,9 +65,9 @@ __device__ __forceinline__ void make_window(const float (&v)[IRW], int lane, boo
     }
 }
 
-// Steps of rows loaded ahead of use: stride 1 keeps 3 rows in flight, stride 2
-// (two rows per step) 4.
-template <int S> constexpr int kAhead = S == 1 ? 3 : 2;
+// Rows are loaded three steps (one unrolled pass of the row loop) ahead of use:
+// S input rows and one dy row per step.
+constexpr int kAhead = 3;
 
 // ---------------------------------------------------------------- forward / grad-input (stride 1)
 // FWD: one input plane x[P] -> MM output planes y[P*MM+m].
@@ -80,7 +83,7 @@ __global__ __launch_bounds__(kThreads) void rw_conv3_kernel(RwArgs<T> a) {
     constexpr int IRW = RW * S;
     constexpr int WW = IRW + (S == 1 ? 2 : 1);
     constexpr int NWI = IRW / kPerWord<T>;  // raw words of an input segment
-    constexpr int R = S * kAhead<S>;        // raw rows in flight
+    constexpr int R = S * kAhead;           // raw rows in flight, buffer S*uu+e at step uu
     constexpr int NIN = BWD ? MM : 1;       // input planes per unit
     constexpr int NOUT = BWD ? 1 : MM;      // output planes per unit
     static_assert(!BWD || S == 1, "stride-2 grad-input has its own kernel");
@@ -133,8 +136,19 @@ __global__ __launch_bounds__(kThreads) void rw_conv3_kernel(RwArgs<T> a) {
             row_values<T>(w, ok, nin, v);
             make_window<IRW, S>(v, u.lane, hl, hr, win[k][j]);
         }
+    }
+    // first refills in the loop's own order (step, input plane, row), so the
+    // wait counts at the loop's head are the same on entry as around the loop
 #pragma unroll
-        for (int f = 0; f < R; ++f) load_row<T, NWI, VB>(inp[k], rb + 3 - S + f, IH, IW, c_in, u.act, rq[k][f], rk[k][f]);
+    for (int uu = 0; uu < 3; ++uu) {
+#pragma unroll
+        for (int k = 0; k < NIN; ++k)
+#pragma unroll
+            for (int e = 0; e < S; ++e) {
+                const int f = S * uu + e;
+                load_row<T, NWI, VB>(inp[k], rb + 3 - S + f, IH, IW, c_in, u.act, rq[k][f], rk[k][f]);
+            }
+        __builtin_amdgcn_sched_barrier(0);
     }
     for (int t0 = 0; t0 < a.BH; t0 += 3) {  // BH is a multiple of 3
 #pragma unroll
@@ -146,15 +160,18 @@ __global__ __launch_bounds__(kThreads) void rw_conv3_kernel(RwArgs<T> a) {
 #pragma unroll
                     for (int e = 0; e < S; ++e) {
                         float v[IRW];
-                        row_values<T>(rq[k][0], rk[k][0], nin, v);
+                        const int f = S * uu + e;
+                        uint32_t cw[NWI];
+                        take_words<T>(rq[k][f], cw);
+                        row_values<T>(cw, rk[k][f], nin, v);
                         make_window<IRW, S>(v, u.lane, hl, hr, win[k][(S * uu + 3 - S + e) % 3]);
-                        ring_pop<R, NWI>(rq[k], rk[k]);
                         // refill with relative row S*t + 3 - S + e + R; past the last row a
                         // step reads, re-read that row (a cache hit, never used) so the
                         // load stays unconditional
                         const int jn = min(S * t + 3 - S + e + R, jlast);
-                        load_row<T, NWI, VB>(inp[k], rb + jn, IH, IW, c_in, u.act, rq[k][R - 1], rk[k][R - 1]);
+                        load_row<T, NWI, VB>(inp[k], rb + jn, IH, IW, c_in, u.act, rq[k][f], rk[k][f]);
                     }
+                __builtin_amdgcn_sched_barrier(0);
                 const int oh = oh0 + t;
                 if (u.act && oh < oh_end) {
 #pragma unroll
@@ -294,8 +311,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu((sizeo
     constexpr int WW = IRW + (S == 1 ? 2 : 1);
     constexpr int NWI = IRW / kPerWord<T>;
     constexpr int NWO = RW / kPerWord<T>;
-    constexpr int R = S * kAhead<S>;
-    constexpr int RD = kAhead<S>;  // dy rows in flight
+    constexpr int R = S * kAhead;  // x rows in flight, buffer S*uu+e at step uu
+    constexpr int RD = kAhead;     // dy rows in flight, buffer uu at step uu
     constexpr int A = MM * 10;
     __shared__ float red[kWaves][A];
     const Geo &g = a.g;
@@ -345,13 +362,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu((sizeo
             row_values<T>(w, ok, nin, v);
             make_window<IRW, S>(v, lane, hl, hr, win[j]);
         }
+        // first loads in the loop's own order (step: x rows, then dy rows), so
+        // the wait counts at the loop's head are the same on entry as around it
 #pragma unroll
-        for (int f = 0; f < R; ++f) load_row<T, NWI, VB>(xp, rb + 3 - S + f, g.ih, g.iw, c_in, act, rq[f], rk[f]);
+        for (int uu = 0; uu < 3; ++uu) {
 #pragma unroll
-        for (int m = 0; m < MM; ++m)
+            for (int e = 0; e < S; ++e)
+                load_row<T, NWI, VB>(xp, rb + 3 - S + S * uu + e, g.ih, g.iw, c_in, act, rq[S * uu + e],
+                                     rk[S * uu + e]);
 #pragma unroll
-            for (int f = 0; f < RD; ++f)
-                load_row<T, NWO, VB>(dyp + m * dplane, oh0 + f, oh_end, g.ow, c_out, act, gq[m][f], gk[m][f]);
+            for (int m = 0; m < MM; ++m)
+                load_row<T, NWO, VB>(dyp + m * dplane, oh0 + uu, oh_end, g.ow, c_out, act, gq[m][uu], gk[m][uu]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         for (int t0 = 0; t0 < a.BH; t0 += 3) {  // BH is a multiple of 3
 #pragma unroll
             for (int uu = 0; uu < 3; ++uu) {
@@ -360,20 +383,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu((sizeo
 #pragma unroll
                     for (int e = 0; e < S; ++e) {
                         float v[IRW];
-                        row_values<T>(rq[0], rk[0], nin, v);
+                        const int f = S * uu + e;
+                        uint32_t cw[NWI];
+                        take_words<T>(rq[f], cw);
+                        row_values<T>(cw, rk[f], nin, v);
                         make_window<IRW, S>(v, lane, hl, hr, win[(S * uu + 3 - S + e) % 3]);
-                        ring_pop<R, NWI>(rq, rk);
                         const int jn = min(S * t + 3 - S + e + R, jlast);
-                        load_row<T, NWI, VB>(xp, rb + jn, g.ih, g.iw, c_in, act, rq[R - 1], rk[R - 1]);
+                        load_row<T, NWI, VB>(xp, rb + jn, g.ih, g.iw, c_in, act, rq[f], rk[f]);
                     }
                     float gy[MM][RW];
 #pragma unroll
                     for (int m = 0; m < MM; ++m) {
-                        row_values<T>(gq[m][0], gk[m][0], nout, gy[m]);
-                        ring_pop<RD, NWO>(gq[m], gk[m]);
+                        uint32_t cw[NWO];
+                        take_words<T>(gq[m][uu], cw);
+                        row_values<T>(cw, gk[m][uu], nout, gy[m]);
                         load_row<T, NWO, VB>(dyp + m * dplane, oh0 + min(t + RD, a.BH - 1), oh_end, g.ow, c_out, act,
-                                               gq[m][RD - 1], gk[m][RD - 1]);
+                                               gq[m][uu], gk[m][uu]);
                     }
+                    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                     for (int m = 0; m < MM; ++m)
 #pragma unroll
@@ -420,8 +447,8 @@ __global__ __launch_bounds__(kThreads) void rw_bwdw3_cs_kernel(RwArgs<T> a) {
     constexpr int WW = IRW + (S == 1 ? 2 : 1);
     constexpr int NWI = IRW / kPerWord<T>;
     constexpr int NWO = RW / kPerWord<T>;
-    constexpr int R = S * kAhead<S>;
-    constexpr int RD = kAhead<S>;
+    constexpr int R = S * kAhead;
+    constexpr int RD = kAhead;
     constexpr int A = MM * 10;
     __shared__ float red[kWaves][64][A + 1];
     const Geo &g = a.g;
@@ -467,13 +494,18 @@ __global__ __launch_bounds__(kThreads) void rw_bwdw3_cs_kernel(RwArgs<T> a) {
             row_values<T>(w, ok, nin, v);
             make_window<IRW, S>(v, lane, hl, hr, win[j]);
         }
+        // first loads in the loop's own order (as in rw_bwdw3_kernel)
 #pragma unroll
-        for (int f = 0; f < R; ++f) load_row<T, NWI, VB>(xp, rb + 3 - S + f, g.ih, g.iw, c_in, act, rq[f], rk[f]);
+        for (int uu = 0; uu < 3; ++uu) {
 #pragma unroll
-        for (int m = 0; m < MM; ++m)
+            for (int e = 0; e < S; ++e)
+                load_row<T, NWI, VB>(xp, rb + 3 - S + S * uu + e, g.ih, g.iw, c_in, act, rq[S * uu + e],
+                                     rk[S * uu + e]);
 #pragma unroll
-            for (int f = 0; f < RD; ++f)
-                load_row<T, NWO, VB>(dyp + m * dplane, f, g.oh, g.ow, c_out, act, gq[m][f], gk[m][f]);
+            for (int m = 0; m < MM; ++m)
+                load_row<T, NWO, VB>(dyp + m * dplane, uu, g.oh, g.ow, c_out, act, gq[m][uu], gk[m][uu]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         for (int t0 = 0; t0 < a.BH; t0 += 3) {  // BH is a multiple of 3
 #pragma unroll
             for (int uu = 0; uu < 3; ++uu) {
@@ -481,20 +513,24 @@ __global__ __launch_bounds__(kThreads) void rw_bwdw3_cs_kernel(RwArgs<T> a) {
 #pragma unroll
                 for (int e = 0; e < S; ++e) {
                     float v[IRW];
-                    row_values<T>(rq[0], rk[0], nin, v);
+                    const int f = S * uu + e;
+                    uint32_t cw[NWI];
+                    take_words<T>(rq[f], cw);
+                    row_values<T>(cw, rk[f], nin, v);
                     make_window<IRW, S>(v, lane, hl, hr, win[(S * uu + 3 - S + e) % 3]);
-                    ring_pop<R, NWI>(rq, rk);
                     const int jn = min(S * t + 3 - S + e + R, jlast);
-                    load_row<T, NWI, VB>(xp, rb + jn, g.ih, g.iw, c_in, act, rq[R - 1], rk[R - 1]);
+                    load_row<T, NWI, VB>(xp, rb + jn, g.ih, g.iw, c_in, act, rq[f], rk[f]);
                 }
                 float gy[MM][RW];
 #pragma unroll
                 for (int m = 0; m < MM; ++m) {
-                    row_values<T>(gq[m][0], gk[m][0], nout, gy[m]);
-                    ring_pop<RD, NWO>(gq[m], gk[m]);
-                    load_row<T, NWO, VB>(dyp + m * dplane, min(t + RD, a.BH - 1), g.oh, g.ow, c_out, act,
-                                         gq[m][RD - 1], gk[m][RD - 1]);
+                    uint32_t cw[NWO];
+                    take_words<T>(gq[m][uu], cw);
+                    row_values<T>(cw, gk[m][uu], nout, gy[m]);
+                    load_row<T, NWO, VB>(dyp + m * dplane, min(t + RD, a.BH - 1), g.oh, g.ow, c_out, act, gq[m][uu],
+                                         gk[m][uu]);
                 }
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int m = 0; m < MM; ++m)
 #pragma unroll

@@ -147,6 +147,25 @@ __device__ __forceinline__ float wave_transpose_sum(const float (&v)[N], int lan
     return c[0];
 }
 
+// Raw words moved out of a prefetch buffer before the buffer is refilled.
+// 32-bit elements are used as they are, so the compiler would otherwise keep
+// them in the buffer's registers for the whole step, load the refill into
+// other registers and copy it back at the loop's back edge, which makes every
+// pass wait for the loads it has just issued.  The copy is opaque to the
+// compiler (one v_mov_b32 per word), so the buffer's registers are free for
+// the refill as soon as it has run.  16-bit words are unpacked into new
+// registers anyway and are passed through.
+template <typename T, int NW>
+__device__ __forceinline__ void take_words(const uint32_t (&src)[NW], uint32_t (&dst)[NW]) {
+#pragma unroll
+    for (int k = 0; k < NW; ++k) {
+        if constexpr (sizeof(T) == 4)
+            asm("v_mov_b32 %0, %1" : "=v"(dst[k]) : "v"(src[k]));
+        else
+            dst[k] = src[k];
+    }
+}
+
 // Drops the front of a ring of R raw rows: q[f] = q[f + 1]; the back slot is
 // refilled by the caller.  Call it after the front row has been used: the
 // scheduling barrier keeps the refill load below that use, so the register
