@@ -37,7 +37,10 @@ per_kernel per kernel geometry (a "tag"): HIP events on the launch stream around
 roofline   the dominant tag (most event time): its algorithmic bytes or flops per
            launch over its average launch duration, measured with HIP events on
            the launch stream around a graph of back-to-back rounds of its calls
-           (at least 1 GiB of traffic per replay), against the MI355X peak
+           (at least 1 GiB of traffic per replay), against the MI355X peak;
+           roofline.secondary relates it to what this machine reaches on a plain
+           device-to-device copy measured in the same run (bandwidth-bound
+           workloads) or to the unpacked v_fma_f32 rate (vector-bound ones)
 cpu_baseline  the fp64 CPU oracle on a bounded sample of the same workload
            (a batch slice of the same host tensors), on this host's cores
 """
@@ -56,6 +59,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X published fp32 vector peak
+FP32_UNPACKED_FMA_TFLOPS = 78.6  # one v_fma_f32 per lane and clock: 256 CUs x 64 lanes x 2.4 GHz x 2
 
 
 def parse():
@@ -256,6 +260,25 @@ def build_dynamic(dc, dev):
            "dtypes": list(D["dtypes"]), "passes": ["fwd", "bwd (dx and filter gradients)"]}
     return dict(cases=cases, per_case=per_case, calls=fwd + bwd, desc="dynamic_multidil_3x3_d135", dtype="f32+f16+bf16",
                 kind="bytes", cfg=cfg)
+
+
+def device_copy_gbs(dev, nbytes=1 << 30, reps=5):
+    """Device-to-device copy rate (read + write bytes per second, GB/s) of torch's
+    copy kernel over two buffers of `nbytes`, timed with HIP events."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3 / reps
+    del src, dst
+    return 2 * nbytes / sec / 1e9
 
 
 # ---------------------------------------------------------------- CPU baseline
@@ -551,6 +574,15 @@ def main():
         roof = {"bound": "alu", "achieved": round(achieved, 2), "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / FP32_VALU_PEAK_TFLOPS, 4)}
     roof["traffic"] = committed_traffic(dom_tag)
+    # secondary ratios: the on-box device-to-device copy rate (bytes read plus
+    # bytes written, over buffers four times the last-level cache) measured in
+    # this run, and for vector-bound kernels the unpacked v_fma_f32 rate
+    if wl["kind"] == "bytes":
+        copy_gbs = device_copy_gbs(dev)
+        roof["secondary"] = {"copy_gbs": round(copy_gbs, 1), "frac_of_copy": round(achieved / copy_gbs, 4)}
+    else:
+        roof["secondary"] = {"unpacked_fma_tflops": FP32_UNPACKED_FMA_TFLOPS,
+                             "frac_of_unpacked": round(achieved / FP32_UNPACKED_FMA_TFLOPS, 4)}
     roof["kernel"] = dom_tag
     roof["avg_launch_us"] = round(avg_s * 1e6, 2)
     roof["timed_launches"] = dom_launches

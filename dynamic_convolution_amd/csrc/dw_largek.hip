@@ -407,9 +407,15 @@ __global__ __launch_bounds__(256, 3) void lk_bwdw_kernel(LkwArgs<T> a) {
         }
         __syncthreads();
         if (!lane_ok) continue;
-        for (int oh = grp; oh < oh1 - oh0; oh += NG) {  // band-relative dy row
+        // lane groups take (dy row, segment) items in turn, so a band with fewer
+        // rows than lane groups still keeps every group busy
+        const int nseg = (a.OW + SEG - 1) / SEG;
+        const int items = (oh1 - oh0) * nseg;
+        for (int it = grp; it < items; it += NG) {
+            const int oh = it / nseg;  // band-relative dy row
+            const int s0 = (it - oh * nseg) * SEG;
             const float *drow = ds + oh * a.dpitch;
-            for (int s0 = 0; s0 < a.OW; s0 += SEG) {
+            {
                 float dv[SEG];
                 const float4 *d4 = reinterpret_cast<const float4 *>(drow + s0);
 #pragma unroll
@@ -479,14 +485,17 @@ struct LkwPlan {
 
 // Tile shape of the grad-weight lanes: TR x TC taps per lane over dy segments
 // of SEG columns.  Each segment reads a TC + SEG - 1 wide x window per tile
-// row from LDS; at k = 31 16 x 16 halves the LDS bytes per FMA of 8 x 8
-// (1.1-1.25x faster; the kernel is held to 168 VGPRs so three waves share a
-// SIMD, which measured faster than two waves with more registers).
+// row from LDS, so the LDS bytes per FMA fall as the segment and the tile
+// widen: at k = 31 a 16 x 16 tile halves them against 8 x 8 (1.1-1.25x
+// faster; the kernel is held to 168 VGPRs so three waves share a SIMD, which
+// measured faster than two waves with more registers), and at k = 7 and 13
+// (8 tap columns per lane) 16-column segments measured 1.1-1.2x faster than
+// 8-column ones.
 constexpr int lkw_tc(int K) { return K == 31 ? 16 : 8; }
-constexpr int lkw_seg(int K) { return K == 31 ? 16 : 8; }
+constexpr int kLkwSeg = 16;
 
 bool plan_lkw(const Geo &g, int K, LkwPlan &p) {
-    const int TC = lkw_tc(K), SEG = lkw_seg(K);
+    const int TC = lkw_tc(K), SEG = kLkwSeg;
     const int owr = (g.ow + SEG - 1) / SEG * SEG;  // dy columns walked (zero beyond ow)
     // x window of the last segment and tile: owr + ceil(k/TC)*TC + 3 columns at most
     p.xpitch = (owr + (K + TC - 1) / TC * TC + 3 + 3) & ~3;
@@ -538,7 +547,7 @@ int run_lkw(const Geo &g, const LkwPlan &p, const void *x, const void *dy, void 
     a.vd = g.ow % Vec<T>::N == 0 && reinterpret_cast<uintptr_t>(dy) % 16 == 0;
     a.fxv = make_fastdiv(std::max(g.iw / Vec<T>::N, 1), static_cast<uint64_t>(p.xrows) * (g.iw / Vec<T>::N + 1) + 1024);
     a.fdv = make_fastdiv(std::max(g.ow / Vec<T>::N, 1), static_cast<uint64_t>(p.BH) * (g.ow / Vec<T>::N + 1) + 1024);
-    hipLaunchKernelGGL((lk_bwdw_kernel<T, K, kTR, lkw_tc(K), lkw_seg(K)>), dim3(g.ic * p.NC * p.nbands), dim3(256),
+    hipLaunchKernelGGL((lk_bwdw_kernel<T, K, kTR, lkw_tc(K), kLkwSeg>), dim3(g.ic * p.NC * p.nbands), dim3(256),
                        p.lds_bytes, s, a);
     return hipGetLastError() == hipSuccess ? kOk : kErrHip;
 }
