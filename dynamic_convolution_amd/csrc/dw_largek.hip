@@ -6,9 +6,10 @@
 // MegEngine large-kernel depthwise article: batch 64, 384 channels, kernels up
 // to 31x31; its DirectConv splits kernel columns over 4 lanes and reduces with
 // a shuffle butterfly).  On CDNA the filter of a plane is uniform across the
-// workgroup, so here it is staged once as fp32 in LDS and each tap is a
-// broadcast LDS read feeding TR*TC FMAs, and each lane keeps a whole TR x TC
-// output tile in VGPRs -- no cross-lane reduction is needed:
+// workgroup, so here it is staged once as fp32 in LDS, each kernel row is
+// read into VGPRs with broadcast 16-byte LDS reads and feeds TR*k*TC FMAs per
+// input row, and each lane keeps a whole TR x TC output tile in VGPRs -- no
+// cross-lane reduction is needed:
 //   1. the workgroup stages its plane (or a band of rows) into LDS as fp32 with
 //      the zero padding written out, so the inner loop has no bounds tests;
 //   2. a lane walks the TR + k - 1 padded input rows its tile reads; each row
@@ -127,12 +128,19 @@ __global__ __launch_bounds__(256) void lk_conv_kernel(LkArgs<T> a) {
             xs[e] = (ih >= 0 && ih < a.IH && iw >= 0 && iw < a.IW) ? to_f32(src[ih * a.IW + iw]) : 0.f;
         }
     }
-    // The filter is staged once as fp32 in LDS and each tap is read with a
-    // uniform-address (broadcast) LDS read right before its FMAs.  (Scalar
-    // loads of an fp32 filter measured slower: the scalar cache misses stall
-    // each row's FMAs; 16-bit taps at odd offsets cannot be scalar-loaded.)
+    // The filter is staged once as fp32 in LDS, one row per KP floats (16-byte
+    // aligned, zero past k).  A kernel row is read into VGPRs with KP/4
+    // uniform-address (broadcast) 16-byte LDS reads when the row walk first
+    // needs it and stays there for the TR steps that use it, so the FMAs take
+    // both multiplicands from VGPRs and wait for no LDS read of their own.
+    // (Scalar loads of an fp32 filter measured slower: the scalar cache misses
+    // stall each row's FMAs; 16-bit taps at odd offsets cannot be scalar-loaded.)
+    constexpr int KP = (K + 3) / 4 * 4;
     float *wsm = xs + a.wsm_off;
-    for (int e = tid; e < K * K; e += nthr) wsm[e] = to_f32(a.w[static_cast<int64_t>(c) * K * K + e]);
+    for (int e = tid; e < K * KP; e += nthr) {
+        const int i = e / KP, j = e - (e / KP) * KP;
+        wsm[e] = j < K ? to_f32(a.w[(static_cast<int64_t>(c) * K + i) * K + j]) : 0.f;
+    }
     __syncthreads();
 
     const float bias = (!FLIP && a.b) ? to_f32(a.b[c]) : 0.f;
@@ -146,30 +154,46 @@ __global__ __launch_bounds__(256) void lk_conv_kernel(LkArgs<T> a) {
 #pragma unroll
             for (int q = 0; q < TC; ++q) acc[tr][q] = bias;
         const float *base = xs + (rb * TR) * a.pitch + cb * TC;
+        // wr[u]: kernel row r of the step r = r0 + u that loaded it; tile row tr
+        // at step r uses kernel row r - tr, loaded tr steps earlier
+        float wr[TR][KP];
+        static_assert((TR + K - 1) % TR == 0, "the row walk is whole passes of TR steps");
 #pragma unroll 1
-        for (int r = 0; r < TR + K - 1; ++r) {
-            // TC and the pitch are multiples of 4: the window is read as 16-byte vectors
-            float win[WW4];
-            const float4 *rp = reinterpret_cast<const float4 *>(base + r * a.pitch);
+        for (int r0 = 0; r0 < TR + K - 1; r0 += TR) {
 #pragma unroll
-            for (int e = 0; e < WW4 / 4; ++e) {
-                const float4 v = rp[e];
-                win[4 * e] = v.x;
-                win[4 * e + 1] = v.y;
-                win[4 * e + 2] = v.z;
-                win[4 * e + 3] = v.w;
-            }
+            for (int u = 0; u < TR; ++u) {
+                const int r = r0 + u;
+                if (r < K) {
+                    const float4 *wp = reinterpret_cast<const float4 *>(wsm + (FLIP ? K - 1 - r : r) * KP);
 #pragma unroll
-            for (int tr = 0; tr < TR; ++tr) {
-                const int i = r - tr;  // kernel row; uniform across the workgroup
-                if (i < 0 || i >= K) continue;
-                const int wrow = (FLIP ? (K - 1 - i) : i) * K;
+                    for (int e = 0; e < KP / 4; ++e) {
+                        const float4 v = wp[e];
+                        wr[u][4 * e] = v.x;
+                        wr[u][4 * e + 1] = v.y;
+                        wr[u][4 * e + 2] = v.z;
+                        wr[u][4 * e + 3] = v.w;
+                    }
+                }
+                // TC and the pitch are multiples of 4: the window is read as 16-byte vectors
+                float win[WW4];
+                const float4 *rp = reinterpret_cast<const float4 *>(base + r * a.pitch);
 #pragma unroll
-                for (int j = 0; j < K; ++j) {
-                    const int t = wrow + (FLIP ? K - 1 - j : j);
-                    const float wv = wsm[t];
+                for (int e = 0; e < WW4 / 4; ++e) {
+                    const float4 v = rp[e];
+                    win[4 * e] = v.x;
+                    win[4 * e + 1] = v.y;
+                    win[4 * e + 2] = v.z;
+                    win[4 * e + 3] = v.w;
+                }
 #pragma unroll
-                    for (int q = 0; q < TC; ++q) acc[tr][q] = fmaf(wv, win[q + j], acc[tr][q]);
+                for (int tr = 0; tr < TR; ++tr) {
+                    const int i = r - tr;  // kernel row; uniform across the workgroup
+                    if (i < 0 || i >= K) continue;
+                    const float *wv = wr[(u - tr + TR) % TR];
+#pragma unroll
+                    for (int j = 0; j < K; ++j)
+#pragma unroll
+                        for (int q = 0; q < TC; ++q) acc[tr][q] = fmaf(wv[FLIP ? K - 1 - j : j], win[q + j], acc[tr][q]);
                 }
             }
         }
@@ -204,7 +228,7 @@ bool plan_lk(int OH, int OW, int K, LkPlan &p) {
     // rows per band: whole plane while the tile count fits 256 lanes and LDS fits 64 KiB
     int bh = OH;
     // padded input tile + an fp32 copy of the filter
-    auto lds = [&](int b) { return (static_cast<int64_t>(b + K - 1) * p.pitch + K * K) * 4; };
+    auto lds = [&](int b) { return (static_cast<int64_t>(b + K - 1) * p.pitch + K * ((K + 3) / 4 * 4)) * 4; };
     while (bh > kTR && (((bh + kTR - 1) / kTR) * p.NCB > 256 || lds(bh) > 64 * 1024)) bh = (bh + 1) / 2;
     if (lds(bh) > 64 * 1024) return false;
     p.nbands = (OH + bh - 1) / bh;
