@@ -528,10 +528,13 @@ bool plan_lkw(const Geo &g, int K, LkwPlan &p) {
     auto bytes = [&](int bh) {
         return std::max((static_cast<int64_t>(bh + K - 1) * p.xpitch + static_cast<int64_t>(bh) * p.dpitch) * 4, red);
     };
-    // bands of dy rows small enough for ~6 workgroups per CU (24 KiB of LDS each):
-    // the staging of one image overlaps the arithmetic of the other workgroups
+    // bands of dy rows within 48 KiB of LDS: the kernel's 168 VGPRs allow three
+    // workgroups per CU, and three such bands still fit its 160 KiB, so the
+    // staging of one image overlaps the arithmetic of the other workgroups
+    // (larger bands also re-stage fewer halo rows; 24 KiB bands measured
+    // 3-9 % slower at 48 x 48 and 64 x 64)
     int bh = g.oh;
-    while (bh > 8 && bytes(bh) > 24 * 1024) bh = (bh + 1) / 2;
+    while (bh > 8 && bytes(bh) > 48 * 1024) bh = (bh + 1) / 2;
     if (bytes(bh) > 64 * 1024) return false;
     p.nbands = (g.oh + bh - 1) / bh;
     p.BH = (g.oh + p.nbands - 1) / p.nbands;
