@@ -390,9 +390,11 @@ def traffic_from(fetch_csv, write_csv, tag, launches, cmd):
     for key, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
         rows = read_counter_csv(path, counter)
         mine = [v for name, v in rows if "dw::" in name]
-        # the reference copies are the run's last three copy dispatches (--copy-ref runs
-        # them after everything else; earlier copies are the inputs' dtype conversions)
-        refs = [v for name, v in rows if "dw::" not in name and "copy" in name.lower()][-3:]
+        # the reference copies are the first three copy dispatches after this library's
+        # last kernel (--copy-ref runs them after everything else; earlier copies are the
+        # inputs' dtype conversions)
+        last = max((i for i, (name, _v) in enumerate(rows) if "dw::" in name), default=-1)
+        refs = [v for name, v in rows[last + 1:] if "dw::" not in name and "copy" in name.lower()][:3]
         if not mine or not refs:
             raise SystemExit("no %s rows for this library or the reference copy in %s" % (counter, path))
         if launches <= 0:
@@ -578,8 +580,11 @@ def main():
     # bytes written, over buffers four times the last-level cache) measured in
     # this run, and for vector-bound kernels the unpacked v_fma_f32 rate
     if wl["kind"] == "bytes":
-        copy_gbs = device_copy_gbs(dev)
-        roof["secondary"] = {"copy_gbs": round(copy_gbs, 1), "frac_of_copy": round(achieved / copy_gbs, 4)}
+        if args.copy_ref:  # counter runs: their own reference copy must stay the last copy
+            roof["secondary"] = None
+        else:
+            copy_gbs = device_copy_gbs(dev)
+            roof["secondary"] = {"copy_gbs": round(copy_gbs, 1), "frac_of_copy": round(achieved / copy_gbs, 4)}
     else:
         roof["secondary"] = {"unpacked_fma_tflops": FP32_UNPACKED_FMA_TFLOPS,
                              "frac_of_unpacked": round(achieved / FP32_UNPACKED_FMA_TFLOPS, 4)}
