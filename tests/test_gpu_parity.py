@@ -674,7 +674,9 @@ def test_large_kernel_mfma(n, c, h, w, mult, k, p, dt, fwd_mfma, bin_mfma):
     (2, 2, 20, 22, 13, 12, "bf16", True),    # pad k - 1
     (2, 2, 9, 9, 31, 15, "f16", True),       # kernel wider than the image
     (3, 2, 70, 40, 13, 6, "f16", True),      # 70 dy rows: three bands
-    (2, 2, 47, 47, 7, 2, "bf16", False),     # k = 7: register tiles
+    (2, 2, 47, 47, 7, 2, "bf16", False),     # k = 7: register tiles (the matrix cores measured slower)
+    (3, 2, 64, 64, 7, 3, "f16", False),      # k = 7, 64 x 64
+    (2, 2, 20, 18, 7, 6, "bf16", False),     # k = 7, pad k - 1
     (1, 2, 40, 100, 13, 6, "f16", False),    # rows of 100: register tiles
 ])
 def test_large_kernel_mfma_grad_weight(n, c, h, w, k, p, dt, bw_mfma):
