@@ -329,13 +329,23 @@ def cpu_baseline(wl, target_s):
         ns = max(1, min(128, int(target_s / t1)))
         if ns > 1:
             u1, t1 = run_sample(ns)
+    used = max(min(ns, t["x"].shape[0]) for _c, t in wl["per_case"])
+    whole = all(min(ns, t["x"].shape[0]) == t["x"].shape[0] for _c, t in wl["per_case"])
+    # a whole workload that the oracle finishes well inside the target is run
+    # again, so the rate comes from about target_s of oracle time
+    reps = 1
+    if whole and 0 < t1 < target_s / 2:
+        reps = min(20, max(1, int(target_s / t1)))
+        for _ in range(reps - 1):
+            u, t_ = run_sample(ns)
+            u1, t1 = u1 + u, t1 + t_
     if kind == "bytes":
         val, unit = u1 / t1 / 1e9, "GB/s"
     else:
         val, unit = u1 / t1 / 1e9, "GFLOP/s"
-    used = max(min(ns, t["x"].shape[0]) for _c, t in wl["per_case"])
-    whole = all(min(ns, t["x"].shape[0]) == t["x"].shape[0] for _c, t in wl["per_case"])
     what = "every case's whole batch" if whole else "first %d image(s) of every case's batch" % used
+    if reps > 1:
+        what += " (%d passes over it)" % reps
     return {"value": round(val, 4), "unit": unit, "cores": O.num_threads(), "kind": "oracle",
             "sample": "%s, every pass, same host tensors; %.1f s of oracle time" % (what, t1)}
 
