@@ -129,3 +129,16 @@ def test_dynamic_at_element_offsets(dts, off):
     assert_guards(dxbuf, off, dx.numel(), tag + " dx")
     for i, (bf, v) in enumerate(dfb):
         assert_guards(bf, off, v.numel(), tag + " dF%d" % i)
+
+
+def test_strided_views_are_refused():
+    x = torch.randn(2, 3, 16, 16, device=DEV)
+    w = torch.randn(3, 3, 3, device=DEV)
+    with pytest.raises(ValueError, match="contiguous"):
+        dc.dwconv2d_fwd(x.transpose(2, 3), w, None, 1, 1, 1)
+    y = torch.empty(2, 3, 16, 32, device=DEV)[..., ::2]
+    with pytest.raises(ValueError, match="contiguous"):
+        dc.dwconv2d_fwd(x, w, None, 1, 1, 1, out=y)
+    fs = [torch.randn(2, 3, 9, 16, 16, device=DEV) for _ in range(3)]
+    with pytest.raises(ValueError, match="contiguous"):
+        dc.dynconv_multidil_fwd(x, [fs[0], fs[1].transpose(3, 4), fs[2]], (1, 3, 5))
