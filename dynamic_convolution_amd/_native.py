@@ -136,6 +136,17 @@ def _dev(t, name: str):
     return t.data_ptr()
 
 
+def _match(t, name: str, shape, ref):
+    """Raises unless tensor t has exactly `shape`, ref's dtype and ref's device (the
+    library writes or reads that many elements of that type through t's pointer)."""
+    if tuple(int(v) for v in t.shape) != tuple(int(v) for v in shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if t.dtype != ref.dtype:
+        raise TypeError("%s dtype %s != %s" % (name, t.dtype, ref.dtype))
+    if t.device != ref.device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, ref.device))
+
+
 def _stream(t):
     import torch
     return torch.cuda.current_stream(t.device).cuda_stream
@@ -189,11 +200,10 @@ def dwconv2d_fwd(x, w, bias=None, stride=1, padding=0, dilation=1, out=None):
     if out is None:
         out = torch.empty((geo[0], geo[4], oh, ow), dtype=x.dtype, device=x.device)
     code = _dtype_code(x)
-    for t, nm in ((w, "w"), (bias, "bias"), (out, "out")):
-        if t is not None and t.dtype != x.dtype:
-            raise TypeError("%s dtype %s != x dtype %s" % (nm, t.dtype, x.dtype))
-    if tuple(out.shape) != (geo[0], geo[4], oh, ow):
-        raise ValueError("out has shape %s" % (tuple(out.shape),))
+    _match(w, "w", w.shape, x)
+    if bias is not None:
+        _match(bias, "bias", (geo[4],), x)
+    _match(out, "out", (geo[0], geo[4], oh, ow), x)
     _check(lib().dwconv2d_fwd(_dev(x, "x"), _dev(w, "w"), _dev(bias, "bias"), _dev(out, "out"), *geo,
                               code, _stream(x)), "dwconv2d_fwd")
     return out
@@ -206,12 +216,10 @@ def dwconv2d_bwd_input(dy, w, x_shape, stride=1, padding=0, dilation=1, out=None
     if out is None:
         out = torch.empty(tuple(int(s) for s in x_shape), dtype=dy.dtype, device=dy.device)
     code = _dtype_code(dy)
-    for t, nm in ((w, "w"), (out, "out")):
-        if t.dtype != dy.dtype:
-            raise TypeError("%s dtype %s != dy dtype %s" % (nm, t.dtype, dy.dtype))
     oh, ow = dwconv2d_out_size(x_shape, w.shape, stride, padding, dilation)
-    if tuple(dy.shape) != (geo[0], geo[4], oh, ow) or tuple(out.shape) != tuple(geo[:4]):
-        raise ValueError("dy %s / out %s do not match the geometry" % (tuple(dy.shape), tuple(out.shape)))
+    _match(dy, "dy", (geo[0], geo[4], oh, ow), dy)
+    _match(w, "w", w.shape, dy)
+    _match(out, "out", geo[:4], dy)
     _check(lib().dwconv2d_bwd_input(_dev(dy, "dy"), _dev(w, "w"), _dev(out, "out"), *geo, code,
                                     _stream(dy)), "dwconv2d_bwd_input")
     return out
@@ -226,18 +234,20 @@ def dwconv2d_bwd_weight(x, dy, w_shape, stride=1, padding=0, dilation=1, with_bi
     import torch
     geo = _geo(x.shape, w_shape, stride, padding, dilation)
     code = _dtype_code(x)
-    if dy.dtype != x.dtype:
-        raise TypeError("dy dtype %s != x dtype %s" % (dy.dtype, x.dtype))
     oh, ow = dwconv2d_out_size(x.shape, w_shape, stride, padding, dilation)
-    if tuple(dy.shape) != (geo[0], geo[4], oh, ow):
-        raise ValueError("dy %s does not match the geometry" % (tuple(dy.shape),))
+    _match(dy, "dy", (geo[0], geo[4], oh, ow), x)
     if out is None:
         out = torch.empty(tuple(int(s) for s in w_shape), dtype=x.dtype, device=x.device)
-    if with_bias and out_bias is None:
-        out_bias = torch.empty((geo[4],), dtype=x.dtype, device=x.device)
+    _match(out, "out", w_shape, x)
+    if with_bias:
+        if out_bias is None:
+            out_bias = torch.empty((geo[4],), dtype=x.dtype, device=x.device)
+        _match(out_bias, "out_bias", (geo[4],), x)
     nbytes = dwconv2d_bwd_weight_workspace_bytes(x.shape, w_shape, stride, padding, dilation, x.dtype)
     if workspace is None:
         workspace = torch.empty((nbytes,), dtype=torch.uint8, device=x.device)
+    if workspace.device != x.device:
+        raise ValueError("workspace is on %s, expected %s" % (workspace.device, x.device))
     _check(lib().dwconv2d_bwd_weight(_dev(x, "x"), _dev(dy, "dy"), _dev(out, "out"),
                                      _dev(out_bias, "out_bias") if with_bias else None,
                                      _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
@@ -259,10 +269,12 @@ def dynconv_multidil_fwd(x, filters, dilations=(1, 3, 5), out=None):
     for f in filters:
         if tuple(f.shape) != (n, c, kk, h, w) or f.dtype != x.dtype:
             raise ValueError("filter %s %s does not match x" % (tuple(f.shape), f.dtype))
+        _match(f, "filter", (n, c, kk, h, w), x)
     if out is None:
         out = torch.empty((n, nb * c, h, w), dtype=x.dtype, device=x.device)
     if tuple(out.shape) != (n, nb * c, h, w) or out.dtype != x.dtype:
         raise ValueError("out %s %s does not match" % (tuple(out.shape), out.dtype))
+    _match(out, "out", (n, nb * c, h, w), x)
     fptrs = (_VP * nb)(*[_dev(f, "filter") for f in filters])
     dil = (ctypes.c_int32 * nb)(*[int(d) for d in dilations])
     _check(lib().dynconv_multidil_fwd(_dev(x, "x"), fptrs, dil, nb, _dev(out, "out"), n, c, h, w, k,
@@ -288,13 +300,16 @@ def dynconv_multidil_bwd(x, filters, dy, dilations=(1, 3, 5), need_dx=True, need
     for f in filters:
         if tuple(f.shape) != (n, c, kk, h, w) or f.dtype != x.dtype:
             raise ValueError("filter %s %s does not match x" % (tuple(f.shape), f.dtype))
+        _match(f, "filter", (n, c, kk, h, w), x)
     if tuple(dy.shape) != (n, nb * c, h, w) or dy.dtype != x.dtype:
         raise ValueError("dy %s %s does not match (n, nb*c, h, w)" % (tuple(dy.shape), dy.dtype))
+    _match(dy, "dy", (n, nb * c, h, w), x)
     dx = None
     if need_dx:
         dx = out_dx if out_dx is not None else torch.empty_like(x)
         if tuple(dx.shape) != tuple(x.shape) or dx.dtype != x.dtype:
             raise ValueError("out_dx %s %s does not match x" % (tuple(dx.shape), dx.dtype))
+        _match(dx, "out_dx", x.shape, x)
     dfs = None
     if need_dfilters:
         dfs = list(out_dfilters) if out_dfilters is not None else [torch.empty_like(f) for f in filters]
@@ -303,6 +318,8 @@ def dynconv_multidil_bwd(x, filters, dy, dilations=(1, 3, 5), need_dx=True, need
         for g, f in zip(dfs, filters):
             if g is not None and (tuple(g.shape) != tuple(f.shape) or g.dtype != f.dtype):
                 raise ValueError("filter gradient %s %s does not match" % (tuple(g.shape), g.dtype))
+            if g is not None:
+                _match(g, "filter gradient", f.shape, x)
     fptrs = (_VP * nb)(*[_dev(f, "filter") for f in filters])
     dptrs = (_VP * nb)(*[_dev(g, "filter gradient") for g in dfs]) if dfs is not None else None
     dil = (ctypes.c_int32 * nb)(*[int(d) for d in dilations])
@@ -323,6 +340,7 @@ def _dyn_shapes(x, filters, dilations):
     for f in filters:
         if tuple(f.shape) != (n, c, kk, h, w) or f.dtype != x.dtype:
             raise ValueError("filter %s %s does not match x" % (tuple(f.shape), f.dtype))
+        _match(f, "filter", (n, c, kk, h, w), x)
     return n, c, h, w, nb, k
 
 
@@ -332,6 +350,7 @@ def dynconv_multidil_fwd_into(x, filters, y, channel_offset, dilations=(1, 3, 5)
     n, c, h, w, nb, k = _dyn_shapes(x, filters, dilations)
     if y.dim() != 4 or (int(y.shape[0]), int(y.shape[2]), int(y.shape[3])) != (n, h, w) or y.dtype != x.dtype:
         raise ValueError("y %s %s does not match x" % (tuple(y.shape), y.dtype))
+    _match(y, "y", y.shape, x)
     fptrs = (_VP * nb)(*[_dev(f, "filter") for f in filters])
     dil = (ctypes.c_int32 * nb)(*[int(d) for d in dilations])
     _check(lib().dynconv_multidil_fwd_into(_dev(x, "x"), fptrs, dil, nb, _dev(y, "y"), int(y.shape[1]),
@@ -348,6 +367,7 @@ def dynconv_multidil_bwd_from(x, filters, dy, channel_offset, dilations=(1, 3, 5
     n, c, h, w, nb, k = _dyn_shapes(x, filters, dilations)
     if dy.dim() != 4 or (int(dy.shape[0]), int(dy.shape[2]), int(dy.shape[3])) != (n, h, w) or dy.dtype != x.dtype:
         raise ValueError("dy %s %s does not match x" % (tuple(dy.shape), dy.dtype))
+    _match(dy, "dy", dy.shape, x)
     dx = torch.empty_like(x) if need_dx else None
     dfs = [torch.empty_like(f) for f in filters] if need_dfilters else None
     fptrs = (_VP * nb)(*[_dev(f, "filter") for f in filters])
@@ -387,6 +407,10 @@ def dwconv2d_tune_fwd(x, w, bias=None, stride=1, padding=0, dilation=1, out=None
     oh, ow = dwconv2d_out_size(x.shape, w.shape, stride, padding, dilation)
     if out is None:
         out = torch.empty((geo[0], geo[4], oh, ow), dtype=x.dtype, device=x.device)
+    _match(w, "w", w.shape, x)
+    if bias is not None:
+        _match(bias, "bias", (geo[4],), x)
+    _match(out, "out", (geo[0], geo[4], oh, ow), x)
     chosen = ctypes.c_char_p()
     _check(lib().dwconv2d_tune_fwd(_dev(x, "x"), _dev(w, "w"), _dev(bias, "bias"), _dev(out, "out"), *geo,
                                    _dtype_code(x), int(reps), _stream(x), ctypes.byref(chosen)), "dwconv2d_tune_fwd")
@@ -399,6 +423,10 @@ def dwconv2d_tune_bwd_input(dy, w, x_shape, stride=1, padding=0, dilation=1, out
     geo = _geo(x_shape, w.shape, stride, padding, dilation)
     if out is None:
         out = torch.empty(tuple(int(s) for s in x_shape), dtype=dy.dtype, device=dy.device)
+    oh, ow = dwconv2d_out_size(x_shape, w.shape, stride, padding, dilation)
+    _match(dy, "dy", (geo[0], geo[4], oh, ow), dy)
+    _match(w, "w", w.shape, dy)
+    _match(out, "out", geo[:4], dy)
     chosen = ctypes.c_char_p()
     _check(lib().dwconv2d_tune_bwd_input(_dev(dy, "dy"), _dev(w, "w"), _dev(out, "out"), *geo, _dtype_code(dy),
                                          int(reps), _stream(dy), ctypes.byref(chosen)), "dwconv2d_tune_bwd_input")
@@ -409,6 +437,8 @@ def dwconv2d_tune_bwd_weight(x, dy, w_shape, stride=1, padding=0, dilation=1, wi
     """Time every grad-weight family on these tensors, record the fastest; returns its name."""
     import torch
     geo = _geo(x.shape, w_shape, stride, padding, dilation)
+    oh, ow = dwconv2d_out_size(x.shape, w_shape, stride, padding, dilation)
+    _match(dy, "dy", (geo[0], geo[4], oh, ow), x)
     out = torch.empty(tuple(int(s) for s in w_shape), dtype=x.dtype, device=x.device)
     ob = torch.empty((geo[4],), dtype=x.dtype, device=x.device) if with_bias else None
     nbytes = dwconv2d_bwd_weight_workspace_bytes(x.shape, w_shape, stride, padding, dilation, x.dtype)

@@ -238,7 +238,10 @@ int run_bwd_input(const Geo &g, const BandPlan &bp, int seg_slots, const void *d
     return hipGetLastError() == hipSuccess ? kOk : kErrHip;
 }
 
-enum BinAlgo { kBinRowwalk = 0, kBinLargek, kBinDecim, kBinBand33s1, kBinBand33s2, kBinBand55s1, kBinBand55s2d2, kBinBandGeneric, kBinChannelGroup, kBinLargekMfma, kBinCount };
+enum BinAlgo {
+    kBinRowwalk = 0, kBinLargek, kBinDecim, kBinBand33s1, kBinBand33s2, kBinBand55s1, kBinBand55s2d2, kBinBandGeneric,
+    kBinChannelGroup, kBinLargekMfma, kBinCount
+};
 
 const char *const kBinNames[kBinCount] = {"rowwalk_3x3",    "largek_regtile", "decimated_s2d2",
                                           "band_3x3_s1",    "band_3x3_s2",    "band_5x5_s1",

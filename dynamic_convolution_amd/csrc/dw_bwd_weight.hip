@@ -424,10 +424,13 @@ int run_small(const Geo &g, const BwPlan &p, const void *x, const void *dy, void
     return hipGetLastError() == hipSuccess ? kOk : kErrHip;
 }
 
-enum BwAlgo { kBwChannelGroup = 0, kBwLargek, kBwRowwalk, kBwDecim, kBwBandPixel, kBwBandTaps, kBwLargekMfma, kBwCount };
+enum BwAlgo {
+    kBwChannelGroup = 0, kBwLargek, kBwRowwalk, kBwDecim, kBwBandPixel, kBwBandTaps, kBwLargekMfma, kBwLargekMfma32,
+    kBwCount
+};
 
 const char *const kBwNames[kBwCount] = {"channelgroup_small", "largek_regtile", "rowwalk_3x3", "decimated_s2d2",
-                                        "band_pixel",         "band_taps",      "largek_mfma"};
+                                        "band_pixel",         "band_taps",      "largek_mfma",  "largek_mfma_f32"};
 
 bool band_bw_plans(const Geo &g, int dt) {
     BwPlan p;
@@ -443,6 +446,7 @@ bool feasible_bw(int algo, const Geo &g, int dt) {
         case kBwRowwalk: return rowwalk_fits(g, dt, 2);
         case kBwDecim: return decim_fits(g, 2);
         case kBwLargekMfma: return largek_mfma_bwdw_fits(g, dt);
+        case kBwLargekMfma32: return largek_wgrad32_fits(g, dt);
         case kBwBandPixel: return small_variant(g) && band_bw_plans(g, dt);
         case kBwBandTaps: return !small_variant(g) && band_bw_plans(g, dt);
         default: return false;
@@ -456,6 +460,7 @@ int select_bwd_weight(const Geo &g, int dt) {
     if (tuned >= 0 && feasible_bw(tuned, g, dt)) return tuned;
     if (small_fits(g, dt, 2)) return kBwChannelGroup;
     if (largek_mfma_bwdw_fits(g, dt)) return kBwLargekMfma;
+    if (largek_wgrad32_fits(g, dt)) return kBwLargekMfma32;
     if (largek_bwdw_fits(g)) return kBwLargek;
     if (rowwalk_fits(g, dt, 2)) return kBwRowwalk;
     if (decim_fits(g, 2)) return kBwDecim;
@@ -469,6 +474,7 @@ int64_t ws_for(int algo, const Geo &g, int dtype) {
         case kBwChannelGroup: return std::max<int64_t>(g.ic * small_bwd_weight_chunks(g, dtype) * slots * 4, 16);
         case kBwLargek: return std::max<int64_t>(g.ic * largek_bwd_weight_chunks(g) * slots * 4, 16);
         case kBwLargekMfma: return std::max<int64_t>(g.ic * largek_mfma_bwd_weight_chunks(g) * slots * 4, 16);
+        case kBwLargekMfma32: return std::max<int64_t>(g.ic * largek_wgrad32_chunks(g) * slots * 4, 16);
         case kBwRowwalk: return std::max<int64_t>(g.ic * rowwalk_bwd_weight_chunks(g, dtype) * slots * 4, 16);
         case kBwDecim: return std::max<int64_t>(g.ic * decim_bwd_weight_chunks(g) * slots * 4, 16);
         default: {
@@ -493,6 +499,11 @@ int dispatch_bwd_weight(const Geo &g, const void *x, const void *dy, void *dwt, 
         rc = largek_mfma_bwd_weight(g, x, dy, ws, dt, s);
         if (rc != kOk) return rc;
         return launch_reduce<T>(g, ws, dwt, db, largek_mfma_bwd_weight_chunks(g), kk + 1, s);
+    }
+    if (algo == kBwLargekMfma32) {
+        rc = largek_wgrad32(g, x, dy, ws, s);
+        if (rc != kOk) return rc;
+        return launch_reduce<T>(g, ws, dwt, db, largek_wgrad32_chunks(g), kk + 1, s);
     }
     if (small || large || decim || algo == kBwRowwalk) {
         // channel-group (small planes), register-tile (large k) or streaming (3x3, pad 1)

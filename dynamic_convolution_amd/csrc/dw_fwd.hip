@@ -238,7 +238,10 @@ int run_fwd(const Geo &g, const BandPlan &bp, const void *x, const void *w, cons
     return hipGetLastError() == hipSuccess ? kOk : kErrHip;
 }
 
-enum FwdAlgo { kFwdRowwalk = 0, kFwdLargek, kFwdDecim, kFwdBand33s1, kFwdBand33s2, kFwdBand55s1, kFwdBand55s2d2, kFwdBandGeneric, kFwdChannelGroup, kFwdLargekMfma, kFwdCount };
+enum FwdAlgo {
+    kFwdRowwalk = 0, kFwdLargek, kFwdDecim, kFwdBand33s1, kFwdBand33s2, kFwdBand55s1, kFwdBand55s2d2, kFwdBandGeneric,
+    kFwdChannelGroup, kFwdLargekMfma, kFwdCount
+};
 
 const char *const kFwdNames[kFwdCount] = {"rowwalk_3x3",    "largek_regtile", "decimated_s2d2",
                                           "band_3x3_s1",    "band_3x3_s2",    "band_5x5_s1",

@@ -87,6 +87,12 @@ bool largek_mfma_bwdw_fits(const Geo &g, int dtype);
 int largek_mfma_bwd_weight_chunks(const Geo &g);
 int largek_mfma_bwd_weight(const Geo &g, const void *x, const void *dy, void *ws, int dtype, hipStream_t s);
 
+// Grad-weight pass 1 of the 31 x 31 filter with fp32 I/O on the matrix cores
+// (dw_largek_wgrad32.hip): workspace [ic][chunks][k*k + 1].
+bool largek_wgrad32_fits(const Geo &g, int dtype);
+int largek_wgrad32_chunks(const Geo &g);
+int largek_wgrad32(const Geo &g, const void *x, const void *dy, void *ws, hipStream_t s);
+
 // Stride 2, dilation 2, pad k-1 (k = 3, 5) as stride-1 passes on the even grid (dw_decim.hip).
 bool decim_fits(const Geo &g, int pass);
 int decim_fwd(const Geo &g, const void *x, const void *w, const void *b, void *y, int dtype, hipStream_t s);

@@ -268,3 +268,36 @@ def test_binding_refuses_cpu_tensors():
     w = torch.zeros(2, 3, 3)
     with pytest.raises(ValueError, match="GPU tensor"):
         N.dwconv2d_fwd(x, w, None, 1, 1, 1)
+
+
+def test_binding_checks_caller_buffers():
+    """Caller-supplied outputs, bias and workspace must match the geometry, dtype and device
+    before any pointer reaches the library (which writes that many elements of that type)."""
+    x = torch.zeros(1, 2, 5, 5)
+    w = torch.zeros(2, 3, 3)
+    dy = torch.zeros(1, 2, 5, 5)
+    with pytest.raises(ValueError, match="bias has shape"):
+        N.dwconv2d_fwd(x, w, torch.zeros(3), 1, 1, 1)
+    with pytest.raises(TypeError, match="bias dtype"):
+        N.dwconv2d_fwd(x, w, torch.zeros(2, dtype=torch.float16), 1, 1, 1)
+    with pytest.raises(ValueError, match="out has shape"):
+        N.dwconv2d_fwd(x, w, None, 1, 1, 1, out=torch.zeros(1, 2, 4, 5))
+    with pytest.raises(ValueError, match="out has shape"):
+        N.dwconv2d_bwd_input(dy, w, x.shape, 1, 1, 1, out=torch.zeros(1, 2, 5, 4))
+    with pytest.raises(ValueError, match="dy has shape"):
+        N.dwconv2d_bwd_input(torch.zeros(1, 2, 4, 4), w, x.shape, 1, 1, 1)
+    with pytest.raises(ValueError, match="out has shape"):
+        N.dwconv2d_bwd_weight(x, dy, w.shape, 1, 1, 1, out=torch.zeros(2, 3, 2))
+    with pytest.raises(TypeError, match="out dtype"):
+        N.dwconv2d_bwd_weight(x, dy, w.shape, 1, 1, 1, out=torch.zeros(2, 3, 3, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="out_bias has shape"):
+        N.dwconv2d_bwd_weight(x, dy, w.shape, 1, 1, 1, out=torch.zeros(2, 3, 3), out_bias=torch.zeros(1))
+    with pytest.raises(TypeError, match="out_bias dtype"):
+        N.dwconv2d_bwd_weight(x, dy, w.shape, 1, 1, 1, out=torch.zeros(2, 3, 3),
+                              out_bias=torch.zeros(2, dtype=torch.float16))
+    with pytest.raises(ValueError, match="dy has shape"):
+        N.dwconv2d_bwd_weight(x, torch.zeros(1, 2, 5, 6), w.shape, 1, 1, 1)
+    with pytest.raises(ValueError, match="dy has shape"):
+        N.dwconv2d_tune_bwd_weight(x, torch.zeros(1, 2, 5, 6), w.shape, 1, 1, 1)
+    with pytest.raises(ValueError, match="bias has shape"):
+        N.dwconv2d_tune_fwd(x, w, torch.zeros(5), 1, 1, 1)

@@ -749,3 +749,21 @@ def test_small_plane_fwd_bwd_input(n, c, h, w, mult, k, s, p, d, dt, fwd_cg):
     x, wt, b, dy = static_case(n, c, h, w, mult, k, s, p, d, DT[dt], 950 + c + h * 3 + k + s)
     check_static(x, wt, b, dy, s, p, d, "smallplane-fb n%d c%d %dx%d m%d k%d s%d p%d %s" % (n, c, h, w, mult, k, s, p, dt),
                  passes=("fwd", "bwd_in"))
+
+
+# ------------------------------------------------------------------ 31 x 31 fp32 grad-weight on the matrix cores
+@pytest.mark.parametrize("n,c,h,w,p", [
+    (5, 2, 64, 64, 15),     # two 32-row bands, chunks of images
+    (3, 3, 48, 48, 15),     # a full band and a partial band
+    (6, 2, 32, 32, 15),     # one band
+    (2, 2, 9, 9, 15),       # kernel wider than the image; rows not whole 16-byte vectors
+    (2, 2, 40, 36, 0),      # no padding: 6 x 10 dy
+    (2, 2, 20, 22, 30),     # pad k - 1
+    (2, 2, 70, 40, 15),     # three bands
+    (1, 1, 33, 17, 7),      # odd sizes, asymmetric output
+])
+def test_large_kernel_grad_weight_f32_matrix(n, c, h, w, p):
+    geo = ((n, c, h, w), (c, 31, 31), 1, p, 1)
+    assert dc.dwconv2d_algo(2, *geo, dtype=torch.float32) == "largek_mfma_f32"
+    x, wt, b, dy = static_case(n, c, h, w, 1, 31, 1, p, 1, torch.float32, 1500 + h + w + p)
+    check_static(x, wt, b, dy, 1, p, 1, "largek-mfma32-bw n%d c%d %dx%d p%d" % (n, c, h, w, p), passes=("bwd_w",))
