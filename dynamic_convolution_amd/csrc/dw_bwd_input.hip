@@ -240,13 +240,13 @@ int run_bwd_input(const Geo &g, const BandPlan &bp, int seg_slots, const void *d
 
 enum BinAlgo {
     kBinRowwalk = 0, kBinLargek, kBinDecim, kBinBand33s1, kBinBand33s2, kBinBand55s1, kBinBand55s2d2, kBinBandGeneric,
-    kBinChannelGroup, kBinLargekMfma, kBinCount
+    kBinChannelGroup, kBinLargekMfma, kBinLargekMfma32, kBinCount
 };
 
 const char *const kBinNames[kBinCount] = {"rowwalk_3x3",    "largek_regtile", "decimated_s2d2",
                                           "band_3x3_s1",    "band_3x3_s2",    "band_5x5_s1",
                                           "band_5x5_s2_d2", "band_generic",   "channelgroup_small",
-                                          "largek_mfma"};
+                                          "largek_mfma",    "largek_mfma_f32"};
 
 bool band_bin_plans(const Geo &g, int dt) {
     BandPlan bp;
@@ -262,6 +262,7 @@ bool feasible_bin(int algo, const Geo &g, int dt) {
         case kBinDecim: return decim_fits(g, 1);
         case kBinChannelGroup: return small_bwd_input_fits(g, dt);
         case kBinLargekMfma: return largek_mfma_fits(g, 1, dt);
+        case kBinLargekMfma32: return largek_fwd32_fits(g, 1, dt);
         case kBinBand33s1: return sq && g.kh == 3 && g.sh == 1 && g.dh == 1 && band_bin_plans(g, dt);
         case kBinBand33s2: return sq && g.kh == 3 && g.sh == 2 && g.dh == 1 && band_bin_plans(g, dt);
         case kBinBand55s1: return sq && g.kh == 5 && g.sh == 1 && g.dh == 1 && band_bin_plans(g, dt);
@@ -280,6 +281,7 @@ int select_bwd_input(const Geo &g, int dt) {
     if (small_bwd_input_fits(g, dt)) return kBinChannelGroup;
     if (rowwalk_fits(g, dt, 1)) return kBinRowwalk;
     if (largek_mfma_fits(g, 1, dt)) return kBinLargekMfma;
+    if (largek_fwd32_fits(g, 1, dt) && largek_fwd32_preferred(g, 1)) return kBinLargekMfma32;
     if (largek_fits(g, 1)) return kBinLargek;
     const bool sq = g.kh == g.kw && g.sh == g.sw && g.dh == g.dw;
     if (sq && g.kh == 3 && g.sh == 1 && g.dh == 1) return kBinBand33s1;
@@ -296,6 +298,7 @@ int dispatch_bwd_input(const Geo &g, const void *dy, const void *w, void *dx, hi
     if (algo == kBinRowwalk) return rowwalk_bwd_input(g, dy, w, dx, dt, s);
     if (algo == kBinLargek) return largek_bwd_input(g, dy, w, dx, dt, s);
     if (algo == kBinLargekMfma) return largek_mfma_bwd_input(g, dy, w, dx, dt, s);
+    if (algo == kBinLargekMfma32) return largek_bwd_input32(g, dy, w, dx, s);
     if (algo == kBinDecim) return decim_bwd_input(g, dy, w, dx, dt, s);
     if (algo == kBinChannelGroup) return small_bwd_input(g, dy, w, dx, dt, s);
     BandPlan bp;
@@ -319,7 +322,7 @@ const char *bwd_input_algo_name_of(int algo) { return algo >= 0 && algo < kBinCo
 bool bwd_input_algo_feasible(int algo, const Geo &g, int dtype) { return feasible_bin(algo, g, dtype); }
 
 bool bwd_input_supported(const Geo &g, int dtype) {
-    if (small_bwd_input_fits(g, dtype) || rowwalk_fits(g, dtype, 1) || largek_mfma_fits(g, 1, dtype) ||
+    if (small_bwd_input_fits(g, dtype) || rowwalk_fits(g, dtype, 1) || largek_mfma_fits(g, 1, dtype) || largek_fwd32_fits(g, 1, dtype) ||
         largek_fits(g, 1) || decim_fits(g, 1))
         return true;
     BandPlan bp;

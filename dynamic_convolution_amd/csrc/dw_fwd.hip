@@ -240,13 +240,13 @@ int run_fwd(const Geo &g, const BandPlan &bp, const void *x, const void *w, cons
 
 enum FwdAlgo {
     kFwdRowwalk = 0, kFwdLargek, kFwdDecim, kFwdBand33s1, kFwdBand33s2, kFwdBand55s1, kFwdBand55s2d2, kFwdBandGeneric,
-    kFwdChannelGroup, kFwdLargekMfma, kFwdCount
+    kFwdChannelGroup, kFwdLargekMfma, kFwdLargekMfma32, kFwdCount
 };
 
 const char *const kFwdNames[kFwdCount] = {"rowwalk_3x3",    "largek_regtile", "decimated_s2d2",
                                           "band_3x3_s1",    "band_3x3_s2",    "band_5x5_s1",
                                           "band_5x5_s2_d2", "band_generic",   "channelgroup_small",
-                                          "largek_mfma"};
+                                          "largek_mfma",    "largek_mfma_f32"};
 
 bool band_fwd_plans(const Geo &g, int dt) {
     BandPlan bp;
@@ -263,6 +263,7 @@ bool feasible_fwd(int algo, const Geo &g, int dt) {
         case kFwdDecim: return decim_fits(g, 0);
         case kFwdChannelGroup: return small_fwd_fits(g, dt);
         case kFwdLargekMfma: return largek_mfma_fits(g, 0, dt);
+        case kFwdLargekMfma32: return largek_fwd32_fits(g, 0, dt);
         case kFwdBand33s1: return sq && g.kh == 3 && g.sh == 1 && g.dh == 1 && band_fwd_plans(g, dt);
         case kFwdBand33s2: return sq && g.kh == 3 && g.sh == 2 && g.dh == 1 && band_fwd_plans(g, dt);
         case kFwdBand55s1: return sq && g.kh == 5 && g.sh == 1 && g.dh == 1 && band_fwd_plans(g, dt);
@@ -280,6 +281,7 @@ int select_fwd(const Geo &g, int dt) {
     if (tuned >= 0 && feasible_fwd(tuned, g, dt)) return tuned;
     if (rowwalk_fits(g, dt, 0)) return kFwdRowwalk;
     if (largek_mfma_fits(g, 0, dt)) return kFwdLargekMfma;
+    if (largek_fwd32_fits(g, 0, dt) && largek_fwd32_preferred(g, 0)) return kFwdLargekMfma32;
     if (largek_fits(g, 0)) return kFwdLargek;
     if (decim_fits(g, 0)) return kFwdDecim;
     if (small_fwd_fits(g, dt)) return kFwdChannelGroup;
@@ -298,6 +300,7 @@ int dispatch_fwd(const Geo &g, const void *x, const void *w, const void *b, void
     if (algo == kFwdRowwalk) return rowwalk_fwd(g, x, w, b, y, dt, s);
     if (algo == kFwdLargek) return largek_fwd(g, x, w, b, y, dt, s);
     if (algo == kFwdLargekMfma) return largek_mfma_fwd(g, x, w, b, y, dt, s);
+    if (algo == kFwdLargekMfma32) return largek_fwd32(g, x, w, b, y, s);
     if (algo == kFwdDecim) return decim_fwd(g, x, w, b, y, dt, s);
     if (algo == kFwdChannelGroup) return small_fwd(g, x, w, b, y, dt, s);
     BandPlan bp;
@@ -320,7 +323,7 @@ const char *fwd_algo_name_of(int algo) { return algo >= 0 && algo < kFwdCount ? 
 bool fwd_algo_feasible(int algo, const Geo &g, int dtype) { return feasible_fwd(algo, g, dtype); }
 
 bool fwd_supported(const Geo &g, int dtype) {
-    if (rowwalk_fits(g, dtype, 0) || largek_mfma_fits(g, 0, dtype) || largek_fits(g, 0) || decim_fits(g, 0) ||
+    if (rowwalk_fits(g, dtype, 0) || largek_mfma_fits(g, 0, dtype) || largek_fwd32_fits(g, 0, dtype) || largek_fits(g, 0) || decim_fits(g, 0) ||
         small_fwd_fits(g, dtype))
         return true;
     BandPlan bp;

@@ -87,6 +87,13 @@ bool largek_mfma_bwdw_fits(const Geo &g, int dtype);
 int largek_mfma_bwd_weight_chunks(const Geo &g);
 int largek_mfma_bwd_weight(const Geo &g, const void *x, const void *dy, void *ws, int dtype, hipStream_t s);
 
+// Forward and grad-input of the 31 x 31 filter with fp32 I/O on the matrix
+// cores (dw_largek_fwd32.hip).  pass: 0 forward, 1 grad-input.
+bool largek_fwd32_fits(const Geo &g, int pass, int dtype);
+bool largek_fwd32_preferred(const Geo &g, int pass);
+int largek_fwd32(const Geo &g, const void *x, const void *w, const void *b, void *y, hipStream_t s);
+int largek_bwd_input32(const Geo &g, const void *dy, const void *w, void *dx, hipStream_t s);
+
 // Grad-weight pass 1 of the 31 x 31 filter with fp32 I/O on the matrix cores
 // (dw_largek_wgrad32.hip): workspace [ic][chunks][k*k + 1].
 bool largek_wgrad32_fits(const Geo &g, int dtype);

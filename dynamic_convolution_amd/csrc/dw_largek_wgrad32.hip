@@ -52,8 +52,10 @@ struct Lw32Args {
     int C, N, IH, IW, OH, OW, P;
     int NC, npc;    // image chunks, images per chunk
     int BH, nbands; // dy rows per band, bands per plane
-    int XP;         // LDS pitch of an x row (floats): iw rounded up to 8
-    int L;          // LDS pitch of a dz row: XP + 32
+    int XW;         // x columns the instructions walk: iw rounded up to 8
+    int XP;         // LDS pitch of an x row: XW + 4 (lanes read 32 different rows: the
+                    // odd multiple of 4 floats puts 16 consecutive rows in distinct banks)
+    int L;          // LDS pitch of a dz row: XW + 32
     int vx, vd;     // x / dy rows are whole aligned 16-byte vectors
 };
 
@@ -67,7 +69,7 @@ __global__ __launch_bounds__(256) void lk_wgrad32_kernel(Lw32Args a) {
     float *xs = reinterpret_cast<float *>(smem);          // [BH + K - 1][XP]
     float *dz = xs + (a.BH + K - 1) * a.XP;               // [BH][L]
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: the row loop branches on it
     const int lane = tid & 63;
     const int mj = lane & 31, h = lane >> 5;
     const int c = blockIdx.x / a.NC;
@@ -144,7 +146,7 @@ __global__ __launch_bounds__(256) void lk_wgrad32_kernel(Lw32Args a) {
                 // A: x row oh + i (staged), columns base + 4h + t; B: dz[oh][base + 4h + t - j + 31]
                 const float *xr = xs + (oh + mi) * a.XP + 4 * h;
                 const float *dr = dz + oh * a.L + kW32Off - mj + 4 * h;
-                for (int base = 0; base < a.XP; base += 8) {
+                for (int base = 0; base < a.XW; base += 8) {
                     const float4 av = *reinterpret_cast<const float4 *>(xr + base);
                     const float b0 = dr[base], b1 = dr[base + 1], b2 = dr[base + 2], b3 = dr[base + 3];
                     acc0 = mfma32(av.x, b0, acc0);
@@ -178,12 +180,13 @@ __global__ __launch_bounds__(256) void lk_wgrad32_kernel(Lw32Args a) {
 }
 
 struct Lw32Plan {
-    int NC, npc, BH, nbands, XP, L, lds_bytes;
+    int NC, npc, BH, nbands, XW, XP, L, lds_bytes;
 };
 
 bool plan_lw32(const Geo &g, Lw32Plan &p) {
-    p.XP = (g.iw + 7) & ~7;
-    p.L = p.XP + 32;
+    p.XW = (g.iw + 7) & ~7;
+    p.XP = p.XW + 4;
+    p.L = p.XW + 32;
     auto bytes = [&](int bh) {
         const int64_t stage = (static_cast<int64_t>(bh + kW32K - 1) * p.XP + static_cast<int64_t>(bh) * p.L) * 4;
         return std::max<int64_t>(stage, 4 * 64 * 17 * 4);
@@ -239,6 +242,7 @@ int largek_wgrad32(const Geo &g, const void *x, const void *dy, void *ws, hipStr
     a.npc = p.npc;
     a.BH = p.BH;
     a.nbands = p.nbands;
+    a.XW = p.XW;
     a.XP = p.XP;
     a.L = p.L;
     a.vx = g.iw % 4 == 0 && reinterpret_cast<uintptr_t>(x) % 16 == 0;

@@ -631,7 +631,7 @@ def test_large_kernel_matrix_core_deterministic(n, c, h, k, p, dt):
     (2, 3, 37, 50, 1, 7, 3, "f32"),      # ragged sizes, column tile of 4
     (1, 2, 20, 70, 1, 13, 0, "f32"),     # no padding
     (1, 2, 40, 33, 1, 13, 12, "f32"),    # pad k-1: grad-input pad 0
-    (1, 2, 64, 64, 2, 31, 15, "f32"),    # multiplier 2 (forward register tiles, others fall back)
+    (1, 2, 64, 64, 2, 31, 15, "f32"),    # multiplier 2 (forward on the matrix cores, others fall back)
     (1, 3, 48, 48, 1, 31, 15, "bf16"),
     (2, 2, 9, 9, 1, 31, 15, "f16"),      # kernel wider than the image
     (1, 1, 130, 24, 1, 7, 3, "f32"),     # several row bands
@@ -767,3 +767,51 @@ def test_large_kernel_grad_weight_f32_matrix(n, c, h, w, p):
     assert dc.dwconv2d_algo(2, *geo, dtype=torch.float32) == "largek_mfma_f32"
     x, wt, b, dy = static_case(n, c, h, w, 1, 31, 1, p, 1, torch.float32, 1500 + h + w + p)
     check_static(x, wt, b, dy, 1, p, 1, "largek-mfma32-bw n%d c%d %dx%d p%d" % (n, c, h, w, p), passes=("bwd_w",))
+
+
+# ------------------------------------------------------------------ 31 x 31 fp32 forward / grad-input on the matrix cores
+@pytest.mark.parametrize("n,c,h,w,mult,p,bin_m", [
+    (2, 2, 64, 64, 1, 15, True),      # two 32-row bands, two 32-column tiles
+    (3, 3, 64, 56, 1, 15, True),      # partial band and partial column tile
+    (2, 2, 32, 32, 1, 15, True),      # one band, one column tile
+    (2, 2, 9, 9, 1, 15, True),        # kernel wider than the image; rows not whole 16-byte vectors
+    (2, 2, 40, 36, 1, 0, True),       # no padding: 10 x 6 output; grad-input pad 30
+    (2, 2, 20, 22, 1, 30, True),      # pad k - 1: grad-input pad 0
+    (1, 2, 64, 64, 2, 15, False),     # multiplier 2: forward only
+    (1, 1, 70, 100, 1, 15, True),     # four column tiles, six bands
+    (5, 1, 33, 30, 1, 7, True),       # odd sizes
+])
+def test_large_kernel_fwd_f32_matrix(n, c, h, w, mult, p, bin_m):
+    """Forward and grad-input of the family, selected through the table (the built-in
+    rules prefer it only where its 32-column tiles are mostly input)."""
+    geo = ((n, c, h, w), (c * mult, 31, 31), 1, p, 1)
+    dt = torch.float32
+    assert "largek_mfma_f32" in dc.dwconv2d_algo_candidates(0, *geo, dtype=dt)
+    assert ("largek_mfma_f32" in dc.dwconv2d_algo_candidates(1, *geo, dtype=dt)) == bin_m
+    x, wt, b, dy = static_case(n, c, h, w, mult, 31, 1, p, 1, dt, 1550 + h + w + p)
+    try:
+        dc.dwconv2d_set_algo(0, *geo, dtype=dt, algo="largek_mfma_f32")
+        if bin_m:
+            dc.dwconv2d_set_algo(1, *geo, dtype=dt, algo="largek_mfma_f32")
+        check_static(x, wt, b, dy, 1, p, 1, "largek-mfma32 n%d c%d %dx%d m%d p%d" % (n, c, h, w, mult, p),
+                     passes=("fwd", "bwd_in"))
+    finally:
+        for pass_ in (0, 1):
+            dc.dwconv2d_set_algo(pass_, *geo, dtype=dt, algo=None)
+
+
+def test_large_kernel_f32_matrix_deterministic():
+    """The fp32 matrix-core passes give bitwise identical results run to run."""
+    x, wt, b, dy = static_case(3, 2, 40, 44, 1, 31, 1, 15, 1, torch.float32, 1590)
+    xd, wd, bd, dyd = x.to(DEV), wt.to(DEV), b.to(DEV), dy.to(DEV)
+    note("fp32 mfma determinism")
+    runs = []
+    for _ in range(3):
+        y = dc.dwconv2d_fwd(xd, wd, bd, 1, 15, 1)
+        dx = dc.dwconv2d_bwd_input(dyd, wd, xd.shape, 1, 15, 1)
+        gw, gb = dc.dwconv2d_bwd_weight(xd, dyd, wd.shape, 1, 15, 1)
+        torch.cuda.synchronize()
+        runs.append((y, dx, gw, gb))
+    for r in runs[1:]:
+        for t1, t2 in zip(runs[0], r):
+            assert torch.equal(t1, t2)
