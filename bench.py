@@ -1,75 +1,90 @@
 """Benchmark of the depthwise / dynamic-filter hot path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload mobilenet|multdil|largek|dynamic]
+    python bench.py [--steps K] [--warmup W] [--workload all|largek|mobilenet|multdil|dynamic|tiny]
 
-Prints ONE JSON line.  A step is one pass of every entry point the workload
-uses over every case of the workload, with inputs resident in HBM:
+Prints ONE JSON line.  The headline is the large-kernel workload (the largest
+configuration: N=64, C=384, H in {32,48,64}, k in {7,13,31}, fp32 and fp16,
+forward + grad-input + grad-weight; valid-tap GFLOP/s).  With the default
+``--workload all`` the same line carries the other workloads as sub-records
+under ``workloads`` (each with its own roofline, per-case table and CPU
+baseline):
 
-  mobilenet (default)  3x3 depthwise layers of MobileNet, N in {1, 64, 128},
-                       (C, H) in {(32,112), (64,112), (128,56), (256,28), (512,14),
-                       (1024,7)}, stride 1 and 2, pad 1, fp32; forward, grad-input,
-                       grad-weight (36 cases x 3 passes)
-  multdil              multiplier 2, dilation 2, stride 2, 5x5, pad 4,
-                       N=128, C=256->512, 56x56, bf16; the three passes
-  largek               N=64, C=384, H in {32,48,64}, k in {7,13,31}, pad k//2,
-                       fp32 and fp16; the three passes
-  dynamic              per-pixel 3x3 filters at dilations 1/3/5, N in {1,2}, C=64,
-                       H in {128,256}, fp32/fp16/bf16; output concatenated;
-                       forward, then backward (dx and the filter gradients)
+  largek     N=64, C=384, H in {32,48,64}, k in {7,13,31}, pad k//2, fp32 and fp16
+  mobilenet  3x3 depthwise layers of MobileNet, N in {1, 64, 128}, (C, H) in
+             {(32,112), (64,112), (128,56), (256,28), (512,14), (1024,7)}, stride 1
+             and 2, pad 1, fp32 (36 cases x 3 passes)
+  multdil    multiplier 2, dilation 2, stride 2, 5x5, pad 4, N=128, C=256->512,
+             56x56, bf16
+  dynamic    per-pixel 3x3 filters at dilations 1/3/5, N in {1,2}, C=64,
+             H in {128,256}, fp32/fp16/bf16, forward and backward
+  tiny       N=1, C=8, 16x16, 3x3, fp32: latency of each pass
 
-Passes run in pass-major order (every case's forward, then every grad-input,
-then every grad-weight) so a tensor is re-read only after gigabytes of other
-traffic, i.e. from HBM, not from the 256 MB last-level cache.
+A step is one pass of every entry point the workload uses over every case,
+pass-major (every forward, then every grad-input, then every grad-weight), with
+inputs resident in HBM.  The whole step is captured once into one HIP graph
+and replayed (--eager: call by call).  A workload whose step moves less than
+2 GiB gets identical copies of its tensors and step i uses copy i % copies, so
+no launch finds its inputs in the 256 MB last-level cache.
 
-value      whole-step algorithmic throughput: compulsory bytes (each input element
-           the result depends on once, each output once) per second for the
-           bandwidth-bound workloads; valid-tap flops (2 per in-bounds multiply-add)
-           per second for largek
-launches   the whole step is captured once into a HIP graph and the timed steps
-           replay it (--eager launches call by call instead).  A workload whose
-           step moves less than 2 GiB gets identical copies of all its tensors
-           (one graph per copy) and step i uses copy i % copies, so no launch
-           finds its inputs still in the 256 MB last-level cache
-per_kernel per kernel geometry (a "tag"): HIP events on the launch stream around
-           a replay of a graph holding that tag's calls of one step, tags in step
-           order, as many rounds as timed steps (each figure includes one
-           graph-launch gap)
-roofline   the dominant tag (most event time): its algorithmic bytes or flops per
-           launch over its average launch duration, measured with HIP events on
-           the launch stream around a graph of back-to-back rounds of its calls
-           (at least 1 GiB of traffic per replay), against the MI355X peak;
-           roofline.secondary relates it to what this machine reaches on a plain
-           device-to-device copy measured in the same run (bandwidth-bound
-           workloads) or to the unpacked v_fma_f32 rate (vector-bound ones)
-cpu_baseline  the fp64 CPU oracle on a bounded sample of the same workload
-           (a batch slice of the same host tensors), on this host's cores
+value        algorithmic work of one step per second: valid-tap flops (2 per
+             in-bounds multiply-add) for largek, compulsory bytes (each input
+             element the result depends on once, each output once) for the
+             bandwidth-bound workloads; the K timed steps after W warmup steps
+step_timing  the K-step timing repeated --repeats times (median, mean, std, min;
+             the first is the one `value` reports)
+roofline     the dominant kernel tag (most event time): algorithmic bytes or flops
+             per launch over its average launch duration (HIP events on the
+             launch stream around a graph of back-to-back rounds of its calls,
+             >= 1 GiB of traffic per replay), repeated --repeats times (median
+             reported) against the MI355X peak for that tag's arithmetic
+             (HBM 8 TB/s; fp32 157.3 TFLOP/s; fp16/bf16 matrix cores 2.5 PFLOP/s).
+             step_frac: the whole step's rate against the same peak.
+per_case     each call alone and cold (after a 512 MiB fill that evicts the last-level
+             cache): HIP events around one eager call, median of --repeats, its
+             rate and fraction of roofline, and the oracle's time for the same call
+             (scaled from the CPU sample) over it.  Calls whose roofline time is
+             under 5 us are flagged as latency-bound (their figure is a latency).
+cpu_baseline the fp64 CPU oracle on a bounded sample of the same host tensors,
+             on all host threads and on one thread (channel subset), with the
+             host CPU model
+input_sha256 SHA-256 of every input tensor (first 16 hex digits) and of their list
+gpu_clocks   shader / memory clock read from sysfs before and after the timed region
 """
 from __future__ import annotations
 
 import argparse
+import concurrent.futures as cf
+import gc
+import glob
 import hashlib
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
-FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X published fp32 vector peak
-FP32_UNPACKED_FMA_TFLOPS = 78.6  # one v_fma_f32 per lane and clock: 256 CUs x 64 lanes x 2.4 GHz x 2
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+FP32_PEAK_TFLOPS = 157.3        # MI355X published fp32 peak (vector and matrix)
+F16_MATRIX_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix-core peak
+LATENCY_US = 5.0                # calls whose roofline time is below this are latency-bound
+WORKLOADS = ["largek", "mobilenet", "multdil", "dynamic", "tiny"]
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="mobilenet", choices=["mobilenet", "multdil", "largek", "dynamic"])
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
+    ap.add_argument("--workload", default="all", choices=["all"] + WORKLOADS)
+    ap.add_argument("--repeats", type=int, default=5, help="repeats of each timed measurement")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target oracle time (all threads) for the headline's CPU baseline; sub-records use half")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline leg")
+    ap.add_argument("--no-hash", action="store_true", help="skip the SHA-256 of the inputs")
     ap.add_argument("--eager", action="store_true", help="launch call by call instead of replaying HIP graphs")
     ap.add_argument("--tune", action="store_true",
                     help="before timing, let the library time every kernel family that can run each call's "
@@ -82,7 +97,7 @@ def parse():
     ap.add_argument("--launches", type=int, default=0,
                     help="calls of the tag in the counter runs (0: the dispatch count of its kernels)")
     ap.add_argument("--cmd", default="", help="command recorded with the traffic figures")
-    return ap.parse_args()
+    return ap.parse_args(argv)
 
 
 # ---------------------------------------------------------------- accounting
@@ -107,19 +122,28 @@ def valid_taps(in_n, out_n, k, s, p, d):
     return tot
 
 
-class Call:
-    """One entry-point call of the step with its algorithmic bytes and flops; tune, when
-    given, times the kernel families that can run the call's geometry and records the
-    fastest in the library's selection table."""
+def tag_peak(tag, kind):
+    """(bound, peak, unit) of a kernel tag: HBM for bandwidth-bound workloads; for
+    flop-counted ones the matrix-core peak of 16-bit I/O on the matrix cores, else fp32."""
+    if kind == "bytes":
+        return "hbm", HBM_PEAK_GBS, "GB/s"
+    matrix16 = ".largek_mfma." in tag and not tag.endswith("_f32")
+    return ("mfma", F16_MATRIX_PEAK_TFLOPS, "TFLOP/s") if matrix16 else ("alu", FP32_PEAK_TFLOPS, "TFLOP/s")
 
-    def __init__(self, tag, fn, nbytes, flops, tune=None):
+
+class Call:
+    """One entry-point call of the step: its tag (pass.family.geometry), algorithmic
+    bytes and flops, the case it belongs to, and (static passes) a tuner."""
+
+    def __init__(self, tag, fn, nbytes, flops, case, pass_, tune=None):
         self.tag, self.fn, self.nbytes, self.flops, self.tune = tag, fn, nbytes, flops, tune
+        self.case, self.pass_ = case, pass_
 
 
 def static_calls(dc, case, dev, seed, passes=("fwd", "bwd_in", "bwd_w")):
     import torch
     from dynamic_convolution_amd import synth
-    n, c, h, M, k, s, p, d, dtype, dists, _label, with_bias = case
+    n, c, h, M, k, s, p, d, dtype, dists, label, with_bias = case
     e = torch.empty(0, dtype=dtype).element_size()
     x = synth.draw((n, c, h, h), dists["x"], seed, "x", dtype, device=dev)
     w = synth.draw((c * M, k, k), dists["w"], seed, "w", dtype, device=dev)
@@ -147,23 +171,26 @@ def static_calls(dc, case, dev, seed, passes=("fwd", "bwd_in", "bwd_w")):
 
     if "fwd" in passes:
         calls.append(Call(tag(0, "fwd"), lambda: dc.dwconv2d_fwd(x, w, b, s, p, d, out=y), sx + W + B + Y, 2 * macs,
-                          lambda: dc.dwconv2d_tune_fwd(x, w, b, s, p, d, out=y, reps=5)))
+                          label, "fwd", lambda: dc.dwconv2d_tune_fwd(x, w, b, s, p, d, out=y, reps=5)))
     if "bwd_in" in passes:
         calls.append(Call(tag(1, "bwd_input"), lambda: dc.dwconv2d_bwd_input(dy, w, x.shape, s, p, d, out=dx),
-                          Y + W + X, 2 * macs,
+                          Y + W + X, 2 * macs, label, "bwd_input",
                           lambda: dc.dwconv2d_tune_bwd_input(dy, w, x.shape, s, p, d, out=dx, reps=5)))
     if "bwd_w" in passes:
         calls.append(Call(tag(2, "bwd_weight"),
                           lambda: dc.dwconv2d_bwd_weight(x, dy, w.shape, s, p, d, with_bias=with_bias, out=gw,
                                                          out_bias=gb, workspace=ws),
-                          sx + Y + W + B, 2 * macs,
+                          sx + Y + W + B, 2 * macs, label, "bwd_weight",
                           lambda: dc.dwconv2d_tune_bwd_weight(x, dy, w.shape, s, p, d, with_bias=with_bias, reps=5)))
     tensors = dict(x=x, w=w, b=b, dy=dy, y=y, dx=dx, gw=gw, gb=gb)
-    return calls, tensors
+    inputs = {"x": x, "w": w, "dy": dy}
+    if b is not None:
+        inputs["b"] = b
+    return calls, tensors, inputs
 
 
 def build_workload(name, dc, dev):
-    """(cases, pass-major list of calls, description, dtype string, value kind)."""
+    """dict(cases, per_case=[(calls, tensors, inputs)], calls (pass-major), desc, dtype, kind, cfg)."""
     import torch
     from dynamic_convolution_amd import synth
     cases = []
@@ -174,7 +201,8 @@ def build_workload(name, dc, dev):
         for n in m["batches"]:
             for c, h in m["layers"]:
                 for s in m["strides"]:
-                    cases.append(((n, c, h, 1, 3, s, 1, 1, torch.float32, dists, "3x3_s%d_" % s, False), seed))
+                    cases.append(((n, c, h, 1, 3, s, 1, 1, torch.float32, dists,
+                                   "N%d_C%d_H%d_3x3_s%d_f32" % (n, c, h, s), False), seed))
                     seed += 1
         desc = "mobilenet_dw3x3_sweep"
         dt, kind = "f32", "bytes"
@@ -184,7 +212,7 @@ def build_workload(name, dc, dev):
         m = synth.MULT_DIL
         dists = dict(x=m["x"], w=m["w"], dy=m["dy"])
         cases.append(((m["n"], m["c"], m["h"], m["mult"], m["k"], m["stride"], m["pad"], m["dil"],
-                       torch.bfloat16, dists, "5x5_m2_d2_s2_", False), 200))
+                       torch.bfloat16, dists, "N128_C256x2_H56_5x5_s2_d2_bf16", False), 200))
         desc, dt, kind = "mult2_dil2_stride2_5x5", "bf16", "bytes"
         cfg = {"n": m["n"], "c_in": m["c"], "c_out": m["c"] * m["mult"], "hw": m["h"], "kernel": 5, "stride": 2,
                "pad": 4, "dilation": 2, "passes": ["fwd", "bwd_input", "bwd_weight"]}
@@ -196,11 +224,17 @@ def build_workload(name, dc, dev):
                 for dts in L["dtypes"]:
                     dists = dict(x=L["x"], w=("N", 0.0, 1.0 / k ** 2), dy=L["dy"])
                     cases.append(((L["n"], L["c"], h, 1, k, 1, k // 2, 1, synth.DTYPES[dts], dists,
-                                   "k%d_%s_" % (k, dts), False), seed))
+                                   "N64_C384_H%d_k%d_%s" % (h, k, dts), False), seed))
                     seed += 1
         desc, dt, kind = "large_kernel_dw_n64_c384", "f32+f16", "flops"
         cfg = {"n": L["n"], "c": L["c"], "hw": list(L["hs"]), "kernels": list(L["ks"]), "dtypes": list(L["dtypes"]),
                "passes": ["fwd", "bwd_input", "bwd_weight"]}
+    elif name == "tiny":
+        t = synth.TINY
+        cases.append(((t["n"], t["c"], t["h"], 1, t["k"], t["stride"], t["pad"], t["dil"], torch.float32,
+                       dict(x=t["x"], w=t["w"], dy=t["dy"]), "N1_C8_H16_3x3_s1_f32", True), 1))
+        desc, dt, kind = "tiny_dw3x3_n1_c8_16x16", "f32", "bytes"
+        cfg = {"n": 1, "c": 8, "hw": 16, "kernel": 3, "pad": 1, "passes": ["fwd", "bwd_input", "bwd_weight"]}
     else:
         return build_dynamic(dc, dev)
     per_case = [static_calls(dc, cs, dev, seed) for cs, seed in cases]
@@ -208,7 +242,7 @@ def build_workload(name, dc, dev):
     calls = []
     for pi in range(3):
         tags = {}
-        for cls, _t in per_case:
+        for cls, _t, _i in per_case:
             for cl in cls[pi:pi + 1]:
                 tags.setdefault(cl.tag, []).append(cl)
         for cl_list in tags.values():
@@ -244,17 +278,20 @@ def build_dynamic(dc, dev):
                 taps = sum(valid_taps(h, h, 3, 1, dd, dd) ** 2 for dd in D["dilations"])
                 X, Y, TF = x.numel() * e, y.numel() * e, n * c * taps * e
                 FF = sum(f.numel() for f in fs) * e
-                cf = Call("dyn.fused.k3_%s" % dts,
-                          (lambda x=x, fs=fs, y=y: dc.dynconv_multidil_fwd(x, fs, D["dilations"], out=y)),
-                          X + TF + Y, 2 * n * c * taps)
+                label = "N%d_C%d_H%d_%s" % (n, c, h, dts)
+                cf_ = Call("dyn.fused.k3_%s" % dts,
+                           (lambda x=x, fs=fs, y=y: dc.dynconv_multidil_fwd(x, fs, D["dilations"], out=y)),
+                           X + TF + Y, 2 * n * c * taps, label, "fwd")
                 cb = Call("dyn_bwd.fused.k3_%s" % dts,
                           (lambda x=x, fs=fs, dy=dy, dx=dx, dfs=dfs:
                            dc.dynconv_multidil_bwd(x, fs, dy, D["dilations"], out_dx=dx, out_dfilters=dfs)),
-                          X + Y + TF + X + FF, 3 * n * c * taps)
-                fwd.append(cf)
+                          X + Y + TF + X + FF, 3 * n * c * taps, label, "bwd")
+                fwd.append(cf_)
                 bwd.append(cb)
-                per_case.append(([cf, cb], dict(x=x, fs=fs, y=y, dy=dy, dx=dx, dfs=dfs)))
-                cases.append(((n, h, dts), seed))
+                inputs = {"x": x, "dy": dy}
+                inputs.update({"f%d" % i: f for i, f in enumerate(fs)})
+                per_case.append(([cf_, cb], dict(x=x, fs=fs, y=y, dy=dy, dx=dx, dfs=dfs), inputs))
+                cases.append(((n, c, h, dts), seed))
                 seed += 1
     cfg = {"batches": list(D["batches"]), "c": D["c"], "hw": list(D["hs"]), "k": 3, "dilations": list(D["dilations"]),
            "dtypes": list(D["dtypes"]), "passes": ["fwd", "bwd (dx and filter gradients)"]}
@@ -281,73 +318,172 @@ def device_copy_gbs(dev, nbytes=1 << 30, reps=5):
     return 2 * nbytes / sec / 1e9
 
 
+# ---------------------------------------------------------------- host facts
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def gpu_clocks():
+    """Current shader and memory clocks (MHz) from the amdgpu sysfs DPM tables, or None."""
+    out = {}
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+        for key, fname in (("sclk_mhz", "pp_dpm_sclk"), ("mclk_mhz", "pp_dpm_mclk")):
+            try:
+                with open(os.path.join(dev, fname)) as f:
+                    for line in f:
+                        if line.strip().endswith("*"):
+                            out.setdefault(key, []).append(int(line.split(":")[1].strip().lower()
+                                                               .split("mhz")[0]))
+            except (OSError, ValueError, IndexError):
+                continue
+    return out or None
+
+
+def input_digests(wl):
+    """SHA-256 of every input tensor of the workload (host copy of its bytes), computed on a
+    thread pool; (list of [case, tensor, first 16 hex digits], digest of the list)."""
+    import torch
+    items = []
+    for (_calls, _t, inputs), (cs, _seed) in zip(wl["per_case"], wl["cases"]):
+        label = _calls[0].case
+        for nm, t in inputs.items():
+            items.append((label, nm, t))
+
+    def digest(t):
+        a = t.detach().contiguous().view(torch.uint8).cpu().numpy()
+        return hashlib.sha256(memoryview(a)).hexdigest()
+
+    with cf.ThreadPoolExecutor(max_workers=8) as ex:
+        hexes = list(ex.map(lambda it: digest(it[2]), items))
+    rows = [[lab, nm, hx[:16]] for (lab, nm, _t), hx in zip(items, hexes)]
+    total = hashlib.sha256("".join(hexes).encode()).hexdigest()
+    return {"per_tensor": rows, "all": total[:32], "count": len(rows)}
+
+
 # ---------------------------------------------------------------- CPU baseline
-def cpu_baseline(wl, target_s):
-    """Time the oracle on a batch slice of the workload's own tensors."""
+def oracle_inputs(wl, case_idx, nimg, chans):
+    """fp64 host copies of a case's inputs restricted to images [0, nimg) and the given
+    channels (None: all); returns (arrays, fraction of the case's work they cover)."""
     import numpy as np
     import torch
-    from oracle import oracle as O
+    _calls, t, _inputs = wl["per_case"][case_idx]
+    cs = wl["cases"][case_idx][0]
 
-    def f64(t):
-        return t.detach().to("cpu", torch.float64).numpy()
+    def f64(a):
+        return np.ascontiguousarray(a.detach().to("cpu", torch.float64).numpy())
 
-    kind = wl["kind"]
+    n, c = t["x"].shape[:2]
+    sl = min(nimg, n)
+    ch = chans if chans is not None else list(range(c))
+    frac = sl / n * len(ch) / c
+    if "fs" in t:  # dynamic (channels independent)
+        nb = len(t["fs"])
+        dy = t["dy"][:sl].reshape(sl, nb, c, *t["dy"].shape[2:])[:, :, ch]
+        return dict(x=f64(t["x"][:sl][:, ch]), fs=[f64(f[:sl][:, ch]) for f in t["fs"]],
+                    dy=f64(dy.reshape(sl, nb * len(ch), *t["dy"].shape[2:]))), frac
+    M = cs[3]
+    och = [g * M + m for g in ch for m in range(M)]
+    return dict(x=f64(t["x"][:sl][:, ch]), w=f64(t["w"][och]), dy=f64(t["dy"][:sl][:, och])), frac
 
-    def run_sample(ns):
-        tot_units, tot_t = 0.0, 0.0
-        for (cs, _seed), (calls, t) in zip(wl["cases"], wl["per_case"]):
-            if "fs" in t:  # dynamic
-                n = t["x"].shape[0]
-                sl = min(ns, n)
-                x = f64(t["x"][:sl])
-                fs = [f64(f[:sl]) for f in t["fs"]]
-                dy = f64(t["dy"][:sl])
-                t0 = time.perf_counter()
-                O.dynconv_multidil_fwd(x, fs, (1, 3, 5))
-                O.dynconv_multidil_bwd(x, fs, dy, (1, 3, 5))
-                tot_t += time.perf_counter() - t0
-                tot_units += sum(cl.nbytes if kind == "bytes" else cl.flops for cl in calls) * sl / n
-                continue
-            n, c, h, M, k, s, p, d = cs[:8]
-            sl = min(ns, n)
-            x, w, dy = f64(t["x"][:sl]), f64(t["w"]), f64(t["dy"][:sl])
-            for cl in calls:
-                t0 = time.perf_counter()
-                if cl.tag.startswith("fwd."):
-                    O.dwconv2d_fwd(x, w, None, s, p, d)
-                elif cl.tag.startswith("bwd_input."):
-                    O.dwconv2d_bwd_input(dy, w, x.shape, s, p, d)
-                else:
-                    O.dwconv2d_bwd_weight(x, dy, w.shape, s, p, d, with_bias=False)
-                tot_t += time.perf_counter() - t0
-                tot_units += (cl.nbytes if kind == "bytes" else cl.flops) * sl / n
-        return tot_units, tot_t
 
-    u1, t1 = run_sample(1)
-    ns = 1
-    if t1 > 0 and t1 < target_s:
-        ns = max(1, min(128, int(target_s / t1)))
-        if ns > 1:
-            u1, t1 = run_sample(ns)
-    used = max(min(ns, t["x"].shape[0]) for _c, t in wl["per_case"])
-    whole = all(min(ns, t["x"].shape[0]) == t["x"].shape[0] for _c, t in wl["per_case"])
-    # a whole workload that the oracle finishes well inside the target is run
-    # again, so the rate comes from about target_s of oracle time
-    reps = 1
-    if whole and 0 < t1 < target_s / 2:
-        reps = min(20, max(1, int(target_s / t1)))
-        for _ in range(reps - 1):
-            u, t_ = run_sample(ns)
-            u1, t1 = u1 + u, t1 + t_
-    if kind == "bytes":
-        val, unit = u1 / t1 / 1e9, "GB/s"
+def oracle_call(O, wl, case_idx, cl, arrs):
+    """Seconds the oracle takes for one call on the given inputs."""
+    if "fs" in arrs:
+        t0 = time.perf_counter()
+        if cl.pass_ == "fwd":
+            O.dynconv_multidil_fwd(arrs["x"], arrs["fs"], (1, 3, 5))
+        else:
+            O.dynconv_multidil_bwd(arrs["x"], arrs["fs"], arrs["dy"], (1, 3, 5))
+        return time.perf_counter() - t0
+    n, c, h, M, k, s, p, d = wl["cases"][case_idx][0][:8]
+    x, w, dy = arrs["x"], arrs["w"], arrs["dy"]
+    t0 = time.perf_counter()
+    if cl.pass_ == "fwd":
+        O.dwconv2d_fwd(x, w, None, s, p, d)
+    elif cl.pass_ == "bwd_input":
+        O.dwconv2d_bwd_input(dy, w, x.shape, s, p, d)
     else:
-        val, unit = u1 / t1 / 1e9, "GFLOP/s"
+        O.dwconv2d_bwd_weight(x, dy, w.shape, s, p, d, with_bias=False)
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(wl, target_s):
+    """The oracle as it stands, timed on this host: (record, per-call full-batch time estimates).
+
+    All threads: every call on a batch slice (the whole batch when it fits target_s,
+    repeated passes when the whole workload takes under half of it).  One thread: every
+    call on one image and a channel subset that holds channels 0 and C-1 (work is linear
+    in images and channels, so rates compare directly)."""
+    from oracle import oracle as O
+    kind = wl["kind"]
+    idx = [(ci, cl) for ci, (calls, _t, _i) in enumerate(wl["per_case"]) for cl in calls]
+    threads = O.num_threads()
+
+    def units(cl):
+        return cl.nbytes if kind == "bytes" else cl.flops
+
+    def run(nimg, chans_of=None):
+        """Every call once on the sample; a call under 1 s is run three times and its
+        fastest run kept (the first run of a call also pays for first-touching the
+        oracle's freshly allocated outputs)."""
+        tot_u = tot_t = spent = 0.0
+        per = {}
+        cached = (None, None, None)
+        for ci, cl in idx:
+            if cached[0] != ci:  # one case's host copies at a time
+                cached = (None, None, None)
+                arrs, frac = oracle_inputs(wl, ci, nimg, chans_of(ci) if chans_of else None)
+                cached = (ci, arrs, frac)
+            _ci, arrs, frac = cached
+            sec = oracle_call(O, wl, ci, cl, arrs)
+            spent += sec
+            if sec < 1.0:
+                for _ in range(2):
+                    s2 = oracle_call(O, wl, ci, cl, arrs)
+                    spent += s2
+                    sec = min(sec, s2)
+            tot_t += sec
+            tot_u += units(cl) * frac
+            per[id(cl)] = sec / frac  # seconds for the whole call
+        return tot_u, tot_t, per, spent
+
+    u1, t1, per, spent = run(1)
+    ns = 1
+    if 0 < spent < target_s:
+        ns = max(1, min(128, int(target_s / spent)))
+        if ns > 1:
+            u1, t1, per, spent = run(ns)
+    whole = all(ns >= t["x"].shape[0] for _c, t, _i in wl["per_case"])
+    est = per
+    used = max(min(ns, t["x"].shape[0]) for _c, t, _i in wl["per_case"])
     what = "every case's whole batch" if whole else "first %d image(s) of every case's batch" % used
-    if reps > 1:
-        what += " (%d passes over it)" % reps
-    return {"value": round(val, 4), "unit": unit, "cores": O.num_threads(), "kind": "oracle",
-            "sample": "%s, every pass, same host tensors; %.1f s of oracle time" % (what, t1)}
+    unit = "GB/s" if kind == "bytes" else "GFLOP/s"
+    rec = {"value": round(u1 / t1 / 1e9, 4), "unit": unit, "cores": threads, "kind": "oracle",
+           "sample": "%s, every pass (a call under 1 s: fastest of 3), same host tensors; %.1f s of oracle "
+                     "time counted, %.1f s spent" % (what, t1, spent),
+           "cpu_model": cpu_model()}
+    # one thread: one image, a channel subset holding 0 and C-1
+    try:
+        O.set_threads(1)
+
+        def subset(ci):
+            c = wl["per_case"][ci][1]["x"].shape[1]
+            step = max(1, c // 16)
+            return sorted(set(list(range(0, c, step)) + [c - 1]))
+        u, t_, _, _sp = run(1, subset)
+        rec["one_thread"] = {"value": round(u / t_ / 1e9, 4), "unit": unit, "cores": 1,
+                             "sample": "first image, every 1/16th channel (and the last) of every case, every pass "
+                                       "(a call under 1 s: fastest of 3); %.1f s of oracle time" % t_}
+    finally:
+        O.set_threads(threads)
+    return rec, est
 
 
 # ---------------------------------------------------------------- traffic from committed counters
@@ -428,24 +564,15 @@ def traffic_from(fetch_csv, write_csv, tag, launches, cmd):
     print(json.dumps(out))
 
 
-def main():
-    args = parse()
-    if args.traffic_from:
-        traffic_from(args.traffic_from[0], args.traffic_from[1], args.only_tag, args.launches, args.cmd)
-        return
-    if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
-              file=sys.stderr)
-        sys.exit(2)
-    import torch
-    import dynamic_convolution_amd as dc
+# ---------------------------------------------------------------- one workload
+def stats(vals, nd=4):
+    return {"median": round(statistics.median(vals), nd), "mean": round(statistics.fmean(vals), nd),
+            "std": round(statistics.pstdev(vals), nd), "min": round(min(vals), nd), "n": len(vals)}
 
-    if not os.path.exists(dc._native.LIB_PATH):
-        from dynamic_convolution_amd import build as hb
-        hb.build()
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    wl = build_workload(args.workload, dc, dev)
+
+def run_workload(name, args, dc, dev, cpu_target):
+    import torch
+    wl = build_workload(name, dc, dev)
     if args.tune:
         # the library times the families each call's geometry allows and keeps the
         # fastest; the workload is then rebuilt so its tags name the chosen families
@@ -455,12 +582,13 @@ def main():
         torch.cuda.synchronize()
         del wl
         torch.cuda.empty_cache()
-        wl = build_workload(args.workload, dc, dev)
+        wl = build_workload(name, dc, dev)
+    kind = wl["kind"]
+    digests = None if args.no_hash else input_digests(wl)
     # rotating copies: a step whose traffic is under 2 GiB would find part of its
-    # inputs still in the 256 MB last-level cache when it runs again, so such
-    # workloads get identical copies of every tensor and step i uses copy i % ncopy
+    # inputs still in the 256 MB last-level cache when it runs again
     ncopy = int(min(8, max(1, math.ceil((2 << 30) / max(1, sum(cl.nbytes for cl in wl["calls"]))))))
-    copies = [wl] + [build_workload(args.workload, dc, dev) for _ in range(ncopy - 1)]
+    copies = [wl] + [build_workload(name, dc, dev) for _ in range(ncopy - 1)]
     calls_by_copy = [w_["calls"] for w_ in copies]
     if args.only_tag:
         calls_by_copy = [[cl for cl in cc if cl.tag == args.only_tag] for cc in calls_by_copy]
@@ -470,8 +598,6 @@ def main():
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
 
-    # one group of consecutive calls per tag (= one kernel geometry); every copy
-    # has the same calls in the same order
     def tag_groups(cc):
         gs = []
         for cl in cc:
@@ -487,6 +613,7 @@ def main():
         for cl in cc:
             cl.fn()
     torch.cuda.synchronize()
+    graphs = []
 
     def runner(fns):
         """A callable launching fns in order: replay of one HIP graph holding them (--eager: direct calls)."""
@@ -502,25 +629,24 @@ def main():
     def event_pair():
         return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
-    # the whole step is captured once into one HIP graph, so the step's launches
-    # cost no host time and no gap between graph launches, as a fixed training
-    # step would run
-    graphs = []
     step_runs = [runner([cl.fn for cl in cc]) for cc in calls_by_copy]
     torch.cuda.synchronize()
     for w_ in range(args.warmup):
         step_runs[w_ % ncopy]()
     torch.cuda.synchronize()
-
-    t0 = time.perf_counter()
-    for st in range(args.steps):
-        step_runs[st % ncopy]()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    clocks_before = gpu_clocks()
+    step_secs = []
+    for _r in range(max(1, args.repeats)):
+        t0 = time.perf_counter()
+        for st in range(args.steps):
+            step_runs[st % ncopy]()
+        torch.cuda.synchronize()
+        step_secs.append(time.perf_counter() - t0)
+    clocks_after = gpu_clocks()
+    elapsed = step_secs[0]
 
     # per-tag event times: each tag's calls replayed from a graph of their own,
-    # tags in step order, HIP events recorded on the launch stream around each
-    # replay (each figure includes one graph-launch gap)
+    # tags in step order (each figure includes one graph-launch gap)
     tag_runs = [[runner([c.fn for c in cls]) for _tag, cls in gs] for gs in groups_by_copy]
     torch.cuda.synchronize()
     ev = [[event_pair() for _ in groups] for _ in range(args.steps)]
@@ -542,23 +668,27 @@ def main():
     dom_tag = max(per_tag, key=lambda t: per_tag[t]["ms"])
 
     # the dominant tag's launch duration: HIP events around one graph of REP
-    # back-to-back rounds of its calls (at least 1 GiB of traffic per replay,
-    # so every round reads its inputs from HBM again), three replays
+    # back-to-back rounds of its calls (>= 1 GiB of traffic per replay), three
+    # replays per measurement, the measurement repeated
     dom_calls = [cl for cl in calls if cl.tag == dom_tag]
     dom_bytes = sum(cl.nbytes for cl in dom_calls)
     rep = int(min(64, max(4, math.ceil((1 << 30) / max(dom_bytes, 1)))))
     dom_run = runner([cl.fn for r in range(rep) for cl in calls_by_copy[r % ncopy] if cl.tag == dom_tag])
     dom_run()
     torch.cuda.synchronize()
-    e0, e1 = event_pair()
-    e0.record(stream)
-    for _ in range(3):
-        dom_run()
-    e1.record(stream)
-    torch.cuda.synchronize()
     dom_launches = 3 * rep * len(dom_calls)
-    avg_s = e0.elapsed_time(e1) / 1e3 / dom_launches
-    executed = len(calls) * (ncopy + args.warmup + 2 * args.steps) + len(dom_calls) * rep * 4
+    avg_list = []
+    for _r in range(max(1, args.repeats)):
+        e0, e1 = event_pair()
+        e0.record(stream)
+        for _ in range(3):
+            dom_run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        avg_list.append(e0.elapsed_time(e1) / 1e3 / dom_launches)
+    avg_s = statistics.median(avg_list)
+    executed = (len(calls) * (ncopy + args.warmup + args.steps * (max(1, args.repeats) + 1))
+                + len(dom_calls) * rep * (1 + 3 * max(1, args.repeats)))
     if args.copy_ref:
         src = torch.empty(COPY_REF_BYTES // 4, dtype=torch.float32, device=dev).normal_()
         dst = torch.empty_like(src)
@@ -566,64 +696,135 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    del graphs
+    del graphs[:]
+
+    # per call, cold: a 512 MiB fill (outside the timed window) evicts the last-level
+    # cache and keeps the GPU busy while the host enqueues the events and the call, so
+    # the window holds the call alone; median of the repeats
+    per_case = []
+    if not args.only_tag:
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        for ci, (ccalls, _t, _i) in enumerate(wl["per_case"]):
+            for cl in ccalls:
+                ts = []
+                for r_ in range(max(1, args.repeats)):
+                    scratch.fill_(r_ & 0xff)
+                    e0, e1 = event_pair()
+                    e0.record(stream)
+                    cl.fn()
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    ts.append(e0.elapsed_time(e1) / 1e3)
+                per_case.append((ci, cl, statistics.median(ts)))
+        del scratch
 
     step_bytes = sum(cl.nbytes for cl in calls)
     step_flops = sum(cl.flops for cl in calls)
     ms_step = elapsed / args.steps * 1e3
     dom_nbytes = dom_bytes / len(dom_calls)
     dom_nflops = sum(cl.flops for cl in dom_calls) / len(dom_calls)
-    if wl["kind"] == "bytes":
+    bound, peak, unit_r = tag_peak(dom_tag, kind)
+    if kind == "bytes":
         value = step_bytes / (elapsed / args.steps) / 1e9
         unit = "GB/s"
         achieved = dom_nbytes / avg_s / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+        step_peak = HBM_PEAK_GBS
     else:
         value = step_flops / (elapsed / args.steps) / 1e9
         unit = "GFLOP/s"
         achieved = dom_nflops / avg_s / 1e12
-        roof = {"bound": "alu", "achieved": round(achieved, 2), "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / FP32_VALU_PEAK_TFLOPS, 4)}
-    roof["traffic"] = committed_traffic(dom_tag)
-    # secondary ratios: the on-box device-to-device copy rate (bytes read plus
-    # bytes written, over buffers four times the last-level cache) measured in
-    # this run, and for vector-bound kernels the unpacked v_fma_f32 rate
-    if wl["kind"] == "bytes":
-        if args.copy_ref:  # counter runs: their own reference copy must stay the last copy
-            roof["secondary"] = None
-        else:
-            copy_gbs = device_copy_gbs(dev)
-            roof["secondary"] = {"copy_gbs": round(copy_gbs, 1), "frac_of_copy": round(achieved / copy_gbs, 4)}
-    else:
-        roof["secondary"] = {"unpacked_fma_tflops": FP32_UNPACKED_FMA_TFLOPS,
-                             "frac_of_unpacked": round(achieved / FP32_UNPACKED_FMA_TFLOPS, 4)}
-    roof["kernel"] = dom_tag
-    roof["avg_launch_us"] = round(avg_s * 1e6, 2)
-    roof["timed_launches"] = dom_launches
-
-    out = {
-        "metric": "dwconv fwd+bwd GFLOP/s and HBM GB/s at 1 GPU, % of roofline, vs CPU oracle",
-        "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": wl["dtype"], "data": "synthetic (seeded, shapes and distributions of the workload)",
-        "config": dict({"workload": wl["desc"], "launch": "eager" if args.eager else "hip_graph_per_step",
-                        "kernel_selection": "tuned on this device" if args.tune else "built-in rules"},
-                       **wl["cfg"]),
+        step_peak = FP32_PEAK_TFLOPS * 1e3
+    roof = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit_r,
+            "frac": round(achieved / peak, 4), "traffic": committed_traffic(dom_tag),
+            "kernel": dom_tag, "avg_launch_us": round(avg_s * 1e6, 2), "timed_launches": dom_launches,
+            "avg_launch_us_repeats": stats([a * 1e6 for a in avg_list], 2),
+            "step_frac": round(value / step_peak, 4),
+            "frac_is": "the dominant kernel tag's average launch against its peak; step_frac is the whole "
+                       "step's rate against %s" % ("8 TB/s" if kind == "bytes" else "the fp32 peak (157.3 TFLOP/s)")}
+    if kind == "bytes" and not args.copy_ref:
+        copy_gbs = device_copy_gbs(dev)
+        roof["secondary"] = {"copy_gbs": round(copy_gbs, 1), "frac_of_copy": round(achieved / copy_gbs, 4)}
+    rec = {
+        "workload": wl["desc"], "value": round(value, 2), "unit": unit, "ms_per_step": round(ms_step, 4),
+        "dtype": wl["dtype"], "config": dict({"workload": wl["desc"],
+                                              "launch": "eager" if args.eager else "hip_graph_per_step",
+                                              "kernel_selection": "tuned on this device" if args.tune
+                                              else "built-in rules"}, **wl["cfg"]),
         "step_gbytes": round(step_bytes / 1e9, 4), "step_gflop": round(step_flops / 1e9, 4),
         "gbs": round(step_bytes / (elapsed / args.steps) / 1e9, 2),
         "gflops": round(step_flops / (elapsed / args.steps) / 1e9, 2),
-        "roofline": roof,
-        "launches_executed": executed,
-        "tensor_copies": ncopy,
+        "step_timing_ms": stats([s_ / args.steps * 1e3 for s_ in step_secs]),
+        "roofline": roof, "launches_executed": executed, "tensor_copies": ncopy,
+        "gpu_clocks": {"before": clocks_before, "after": clocks_after},
         "per_kernel": {t: {"avg_us": round(r["ms"] / r["launches"] * 1e3, 2),
-                                       "share": round(r["ms"] / sum(v["ms"] for v in per_tag.values()), 4),
-                                       "gbs": round(r["bytes"] / (r["ms"] / 1e3) / 1e9, 1),
-                                       "gflops": round(r["flops"] / (r["ms"] / 1e3) / 1e9, 1)}
+                           "share": round(r["ms"] / sum(v["ms"] for v in per_tag.values()), 4),
+                           "gbs": round(r["bytes"] / (r["ms"] / 1e3) / 1e9, 1),
+                           "gflops": round(r["flops"] / (r["ms"] / 1e3) / 1e9, 1)}
                        for t, r in sorted(per_tag.items())},
     }
-    if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    if digests is not None:
+        rec["input_sha256"] = digests
+    cpu_est = {}
+    if not args.no_cpu and not args.only_tag:
+        rec["cpu_baseline"], cpu_est = cpu_baseline(wl, cpu_target)
+    rows = []
+    for ci, cl, sec in per_case:
+        b_, pk, _u = tag_peak(cl.tag, kind)
+        rate = (cl.nbytes / sec / 1e9) if kind == "bytes" else (cl.flops / sec / 1e12)
+        t_roof = max(cl.nbytes / (HBM_PEAK_GBS * 1e9), cl.flops / (pk * 1e12 if b_ != "hbm" else FP32_PEAK_TFLOPS * 1e12))
+        row = [cl.case, cl.pass_, round(sec * 1e6, 2), round(rate, 2 if kind == "bytes" else 3),
+               round(rate / pk, 4), t_roof * 1e6 < LATENCY_US]
+        est = cpu_est.get(id(cl))
+        row.append(round(est / sec, 1) if est else None)
+        rows.append(row)
+    rec["per_case"] = {"columns": ["case", "pass", "us", "GB/s" if kind == "bytes" else "TFLOP/s", "frac",
+                                   "latency_bound", "speedup_vs_oracle_all_threads"], "rows": rows,
+                       "timing": "HIP events around one eager call after a 512 MiB fill (cold), median of %d"
+                                 % max(1, args.repeats)}
+    del copies, wl, calls_by_copy, calls
+    gc.collect()
+    torch.cuda.empty_cache()
+    return rec
+
+
+def main(argv=None):
+    args = parse(argv)
+    if args.traffic_from:
+        traffic_from(args.traffic_from[0], args.traffic_from[1], args.only_tag, args.launches, args.cmd)
+        return
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.only_tag and args.workload == "all":
+        raise SystemExit("--only-tag needs one --workload")
+    import torch
+    import dynamic_convolution_amd as dc
+
+    if not os.path.exists(dc._native.LIB_PATH):
+        from dynamic_convolution_amd import build as hb
+        hb.build()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    names = WORKLOADS if args.workload == "all" else [args.workload]
+    recs = {}
+    for i, nm in enumerate(names):
+        print("[bench] %s" % nm, file=sys.stderr, flush=True)
+        recs[nm] = run_workload(nm, args, dc, dev, args.cpu_seconds if i == 0 else args.cpu_seconds / 2)
+    head = recs[names[0]]
+    out = {
+        "metric": "dwconv fwd+bwd GFLOP/s and HBM GB/s at 1 GPU, % of roofline, vs CPU oracle",
+        "value": head["value"], "unit": head["unit"], "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": head["dtype"], "data": "synthetic (seeded, shapes and distributions of the workload)",
+        "config": head["config"],
+    }
+    for k_ in ("step_gbytes", "step_gflop", "gbs", "gflops", "step_timing_ms", "roofline", "launches_executed",
+               "tensor_copies", "gpu_clocks", "per_kernel", "per_case", "input_sha256", "cpu_baseline"):
+        if k_ in head:
+            out[k_] = head[k_]
+    if len(names) > 1:
+        out["workloads"] = {nm: recs[nm] for nm in names[1:]}
     print(json.dumps(out), flush=True)
 
 

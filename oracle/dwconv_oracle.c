@@ -71,6 +71,17 @@ int oracle_num_threads(void)
 #endif
 }
 
+/* Sets the number of OpenMP threads later calls run on (timing at one thread
+ * and at all of them); results do not depend on it. */
+void oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* y[n, oc, oh, ow] = b[oc] + sum_{i<kh, j<kw} w[oc, i, j] * x[n, oc/M, oh*sh - ph + i*dh, ow*sw - pw + j*dw]
  * (out-of-image taps contribute nothing). b may be NULL. */
 void oracle_dwconv_fwd(const double *x, const double *w, const double *b, double *y,

@@ -71,6 +71,8 @@ class Oracle:
         lib.oracle_out_size.restype = _I64
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_set_threads.argtypes = [ctypes.c_int]
+        lib.oracle_set_threads.restype = None
         lib.oracle_dwconv_fwd.argtypes = [_DP, _DP, _DP, _DP] + geo
         lib.oracle_dwconv_fwd.restype = None
         lib.oracle_dwconv_bwd_input.argtypes = [_DP, _DP, _DP] + geo
@@ -96,6 +98,10 @@ class Oracle:
     def num_threads(self) -> int:
         """OpenMP threads the oracle's loops run on."""
         return int(self._lib.oracle_num_threads())
+
+    def set_threads(self, n: int) -> None:
+        """Run later calls on n OpenMP threads (results do not depend on it)."""
+        self._lib.oracle_set_threads(int(n))
 
     def geometry(self, x_shape, w_shape, stride=1, padding=0, dilation=1):
         """(13 geometry integers, oh, ow); raises ValueError on an invalid problem."""
@@ -225,6 +231,10 @@ def out_size(*a):
 
 def num_threads():
     return default().num_threads()
+
+
+def set_threads(n):
+    default().set_threads(n)
 
 
 def geometry(*a, **k):
