@@ -210,7 +210,6 @@ int dwconv2d_fwd(const void *x, const void *w, const void *bias, void *y, int64_
     if (overlap(y, yb, x, x_bytes(g, e)) || overlap(y, yb, w, w_bytes(g, e)) ||
         (bias && overlap(y, yb, bias, b_bytes(g, e))))
         return DW_EALIAS;
-    if (!dw::fwd_supported(g, dtype)) return DW_EUNSUPPORTED;
     return map_launch(dw::launch_fwd(g, x, w, bias, y, dtype, static_cast<hipStream_t>(stream)));
 }
 
@@ -226,7 +225,6 @@ int dwconv2d_bwd_input(const void *dy, const void *w, void *dx, int64_t n, int64
     if (!aligned(dy, e) || !aligned(w, e) || !aligned(dx, e)) return DW_EPTR;
     const size_t xb = x_bytes(g, e);
     if (overlap(dx, xb, dy, y_bytes(g, e)) || overlap(dx, xb, w, w_bytes(g, e))) return DW_EALIAS;
-    if (!dw::bwd_input_supported(g, dtype)) return DW_EUNSUPPORTED;
     return map_launch(dw::launch_bwd_input(g, dy, w, dx, dtype, static_cast<hipStream_t>(stream)));
 }
 
@@ -285,8 +283,6 @@ int dynconv_multidil_fwd_into(const void *x, const void *const *filters, const i
     if (overlap(y, yb, x, xb)) return DW_EALIAS;
     for (int b = 0; b < nb; ++b)
         if (overlap(y, yb, filters[b], fb)) return DW_EALIAS;
-    if (!dw::dynconv_supported(static_cast<int>(h), static_cast<int>(w), static_cast<int>(k), maxdil, dtype))
-        return DW_EUNSUPPORTED;
     return map_launch(dw::launch_dynconv(x, filters, dilations, nb, y, static_cast<int>(y_channels),
                                          static_cast<int>(y_offset), static_cast<int>(n), static_cast<int>(c),
                                          static_cast<int>(h), static_cast<int>(w), static_cast<int>(k), dtype,
@@ -337,8 +333,6 @@ int dynconv_multidil_bwd_from(const void *x, const void *const *filters, const v
         for (int q = o + 1; q < no; ++q)
             if (overlap(outs[o], osz[o], outs[q], osz[q])) return DW_EALIAS;
     }
-    if (!dw::dynconv_bwd_supported(static_cast<int>(h), static_cast<int>(w), static_cast<int>(k), maxdil, dtype))
-        return DW_EUNSUPPORTED;
     if (no == 0) return DW_OK;  // nothing requested
     return map_launch(dw::launch_dynconv_bwd(x, filters, dy, static_cast<int>(dy_channels), static_cast<int>(dy_offset),
                                              dilations, nb, dx, dfilters, static_cast<int>(n), static_cast<int>(c),
@@ -467,7 +461,7 @@ const char *dw_status_str(int status) {
         case DW_EALIAS: return "an output overlaps an input or another output";
         case DW_EHIP: return "HIP kernel launch failed";
         case DW_EDYN: return "dynamic filter: k must be odd, 1 <= nb <= 4, dilations >= 1";
-        case DW_EUNSUPPORTED: return "geometry needs more LDS per workgroup than this library stages";
+        case DW_EUNSUPPORTED: return "kernel family cannot run this geometry";
         default: return "unknown status";
     }
 }

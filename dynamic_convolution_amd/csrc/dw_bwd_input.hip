@@ -240,13 +240,13 @@ int run_bwd_input(const Geo &g, const BandPlan &bp, int seg_slots, const void *d
 
 enum BinAlgo {
     kBinRowwalk = 0, kBinLargek, kBinDecim, kBinBand33s1, kBinBand33s2, kBinBand55s1, kBinBand55s2d2, kBinBandGeneric,
-    kBinChannelGroup, kBinLargekMfma, kBinLargekMfma32, kBinCount
+    kBinChannelGroup, kBinLargekMfma, kBinLargekMfma32, kBinDirect, kBinCount
 };
 
 const char *const kBinNames[kBinCount] = {"rowwalk_3x3",    "largek_regtile", "decimated_s2d2",
                                           "band_3x3_s1",    "band_3x3_s2",    "band_5x5_s1",
                                           "band_5x5_s2_d2", "band_generic",   "channelgroup_small",
-                                          "largek_mfma",    "largek_mfma_f32"};
+                                          "largek_mfma",    "largek_mfma_f32", "direct"};
 
 bool band_bin_plans(const Geo &g, int dt) {
     BandPlan bp;
@@ -268,6 +268,7 @@ bool feasible_bin(int algo, const Geo &g, int dt) {
         case kBinBand55s1: return sq && g.kh == 5 && g.sh == 1 && g.dh == 1 && band_bin_plans(g, dt);
         case kBinBand55s2d2: return sq && g.kh == 5 && g.sh == 2 && g.dh == 2 && band_bin_plans(g, dt);
         case kBinBandGeneric: return band_bin_plans(g, dt);
+        case kBinDirect: return true;
         default: return false;
     }
 }
@@ -283,6 +284,7 @@ int select_bwd_input(const Geo &g, int dt) {
     if (largek_mfma_fits(g, 1, dt)) return kBinLargekMfma;
     if (largek_fwd32_fits(g, 1, dt) && largek_fwd32_preferred(g, 1)) return kBinLargekMfma32;
     if (largek_fits(g, 1)) return kBinLargek;
+    if (!band_bin_plans(g, dt)) return kBinDirect;  // rows too wide to stage
     const bool sq = g.kh == g.kw && g.sh == g.sw && g.dh == g.dw;
     if (sq && g.kh == 3 && g.sh == 1 && g.dh == 1) return kBinBand33s1;
     if (sq && g.kh == 3 && g.sh == 2 && g.dh == 1) return kBinBand33s2;
@@ -301,6 +303,7 @@ int dispatch_bwd_input(const Geo &g, const void *dy, const void *w, void *dx, hi
     if (algo == kBinLargekMfma32) return largek_bwd_input32(g, dy, w, dx, s);
     if (algo == kBinDecim) return decim_bwd_input(g, dy, w, dx, dt, s);
     if (algo == kBinChannelGroup) return small_bwd_input(g, dy, w, dx, dt, s);
+    if (algo == kBinDirect) return direct_bwd_input(g, dy, w, dx, dt, s);
     BandPlan bp;
     int seg_slots = 0;
     if (!plan_bwd_input<T>(g, bp, seg_slots)) return kErrUnsupported;
@@ -321,14 +324,7 @@ int bwd_input_algo_count() { return kBinCount; }
 const char *bwd_input_algo_name_of(int algo) { return algo >= 0 && algo < kBinCount ? kBinNames[algo] : nullptr; }
 bool bwd_input_algo_feasible(int algo, const Geo &g, int dtype) { return feasible_bin(algo, g, dtype); }
 
-bool bwd_input_supported(const Geo &g, int dtype) {
-    if (small_bwd_input_fits(g, dtype) || rowwalk_fits(g, dtype, 1) || largek_mfma_fits(g, 1, dtype) || largek_fwd32_fits(g, 1, dtype) ||
-        largek_fits(g, 1) || decim_fits(g, 1))
-        return true;
-    BandPlan bp;
-    int ss;
-    return dtype == 0 ? plan_bwd_input<float>(g, bp, ss) : plan_bwd_input<__half>(g, bp, ss);
-}
+bool bwd_input_supported(const Geo &, int) { return true; }  // the direct kernel serves every geometry
 
 int launch_bwd_input(const Geo &g, const void *dy, const void *w, void *dx, int dtype, hipStream_t s) {
     switch (dtype) {

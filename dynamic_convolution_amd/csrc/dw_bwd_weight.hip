@@ -426,11 +426,12 @@ int run_small(const Geo &g, const BwPlan &p, const void *x, const void *dy, void
 
 enum BwAlgo {
     kBwChannelGroup = 0, kBwLargek, kBwRowwalk, kBwDecim, kBwBandPixel, kBwBandTaps, kBwLargekMfma, kBwLargekMfma32,
-    kBwCount
+    kBwDirect, kBwCount
 };
 
 const char *const kBwNames[kBwCount] = {"channelgroup_small", "largek_regtile", "rowwalk_3x3", "decimated_s2d2",
-                                        "band_pixel",         "band_taps",      "largek_mfma",  "largek_mfma_f32"};
+                                        "band_pixel",         "band_taps",      "largek_mfma",  "largek_mfma_f32",
+                                        "direct"};
 
 bool band_bw_plans(const Geo &g, int dt) {
     BwPlan p;
@@ -449,6 +450,7 @@ bool feasible_bw(int algo, const Geo &g, int dt) {
         case kBwLargekMfma32: return largek_wgrad32_fits(g, dt);
         case kBwBandPixel: return small_variant(g) && band_bw_plans(g, dt);
         case kBwBandTaps: return !small_variant(g) && band_bw_plans(g, dt);
+        case kBwDirect: return true;
         default: return false;
     }
 }
@@ -464,6 +466,7 @@ int select_bwd_weight(const Geo &g, int dt) {
     if (largek_bwdw_fits(g)) return kBwLargek;
     if (rowwalk_fits(g, dt, 2)) return kBwRowwalk;
     if (decim_fits(g, 2)) return kBwDecim;
+    if (!band_bw_plans(g, dt)) return kBwDirect;  // rows too wide to stage
     return small_variant(g) ? kBwBandPixel : kBwBandTaps;
 }
 
@@ -475,6 +478,7 @@ int64_t ws_for(int algo, const Geo &g, int dtype) {
         case kBwLargek: return std::max<int64_t>(g.ic * largek_bwd_weight_chunks(g) * slots * 4, 16);
         case kBwLargekMfma: return std::max<int64_t>(g.ic * largek_mfma_bwd_weight_chunks(g) * slots * 4, 16);
         case kBwLargekMfma32: return std::max<int64_t>(g.ic * largek_wgrad32_chunks(g) * slots * 4, 16);
+        case kBwDirect: return std::max<int64_t>(static_cast<int64_t>(g.ic) * direct_bwd_weight_chunks(g) * slots * 4, 16);
         case kBwRowwalk: return std::max<int64_t>(g.ic * rowwalk_bwd_weight_chunks(g, dtype) * slots * 4, 16);
         case kBwDecim: return std::max<int64_t>(g.ic * decim_bwd_weight_chunks(g) * slots * 4, 16);
         default: {
@@ -499,6 +503,11 @@ int dispatch_bwd_weight(const Geo &g, const void *x, const void *dy, void *dwt, 
         rc = largek_mfma_bwd_weight(g, x, dy, ws, dt, s);
         if (rc != kOk) return rc;
         return launch_reduce<T>(g, ws, dwt, db, largek_mfma_bwd_weight_chunks(g), kk + 1, s);
+    }
+    if (algo == kBwDirect) {
+        rc = direct_bwd_weight(g, x, dy, ws, dt, s);
+        if (rc != kOk) return rc;
+        return launch_reduce<T>(g, ws, dwt, db, direct_bwd_weight_chunks(g), g.mult * (kk + 1), s);
     }
     if (algo == kBwLargekMfma32) {
         rc = largek_wgrad32(g, x, dy, ws, s);

@@ -465,6 +465,10 @@ bool dynconv_bwd_supported(int h, int w, int k, int maxdil, int dtype) {
 int launch_dynconv_bwd(const void *x, const void *const *filters, const void *dy, int dych, int dyoff,
                        const int32_t *dil, int nb, void *dx, void *const *dfilters, int n, int c, int h, int w,
                        int k, int dtype, hipStream_t s) {
+    int maxdil = 1;
+    for (int b = 0; b < nb; ++b) maxdil = std::max(maxdil, static_cast<int>(dil[b]));
+    if (!dynconv_bwd_supported(h, w, k, maxdil, dtype))  // rows too wide to stage: direct kernels
+        return direct_dynconv_bwd(x, filters, dy, dych, dyoff, dil, nb, dx, dfilters, n, c, h, w, k, dtype, s);
     switch (dtype) {
         case 0: return run_dynbwd<float>(x, filters, dy, dych, dyoff, dil, nb, dx, dfilters, n, c, h, w, k, s);
         case 1: return run_dynbwd<__half>(x, filters, dy, dych, dyoff, dil, nb, dx, dfilters, n, c, h, w, k, s);

@@ -215,6 +215,10 @@ bool dynconv_supported(int h, int w, int k, int maxdil, int dtype) {
 
 int launch_dynconv(const void *x, const void *const *filters, const int32_t *dil, int nb, void *y, int ych,
                    int yoff, int n, int c, int h, int w, int k, int dtype, hipStream_t s) {
+    int maxdil = 1;
+    for (int b = 0; b < nb; ++b) maxdil = std::max(maxdil, static_cast<int>(dil[b]));
+    if (!dynconv_supported(h, w, k, maxdil, dtype))  // rows too wide to stage: direct kernel
+        return direct_dynconv(x, filters, dil, nb, y, ych, yoff, n, c, h, w, k, dtype, s);
     switch (dtype) {
         case 0: return run_dyn<float>(x, filters, dil, nb, y, ych, yoff, n, c, h, w, k, s);
         case 1: return run_dyn<__half>(x, filters, dil, nb, y, ych, yoff, n, c, h, w, k, s);

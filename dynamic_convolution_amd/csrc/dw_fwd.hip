@@ -240,13 +240,13 @@ int run_fwd(const Geo &g, const BandPlan &bp, const void *x, const void *w, cons
 
 enum FwdAlgo {
     kFwdRowwalk = 0, kFwdLargek, kFwdDecim, kFwdBand33s1, kFwdBand33s2, kFwdBand55s1, kFwdBand55s2d2, kFwdBandGeneric,
-    kFwdChannelGroup, kFwdLargekMfma, kFwdLargekMfma32, kFwdCount
+    kFwdChannelGroup, kFwdLargekMfma, kFwdLargekMfma32, kFwdDirect, kFwdCount
 };
 
 const char *const kFwdNames[kFwdCount] = {"rowwalk_3x3",    "largek_regtile", "decimated_s2d2",
                                           "band_3x3_s1",    "band_3x3_s2",    "band_5x5_s1",
                                           "band_5x5_s2_d2", "band_generic",   "channelgroup_small",
-                                          "largek_mfma",    "largek_mfma_f32"};
+                                          "largek_mfma",    "largek_mfma_f32", "direct"};
 
 bool band_fwd_plans(const Geo &g, int dt) {
     BandPlan bp;
@@ -269,6 +269,7 @@ bool feasible_fwd(int algo, const Geo &g, int dt) {
         case kFwdBand55s1: return sq && g.kh == 5 && g.sh == 1 && g.dh == 1 && band_fwd_plans(g, dt);
         case kFwdBand55s2d2: return sq && g.kh == 5 && g.sh == 2 && g.dh == 2 && band_fwd_plans(g, dt);
         case kFwdBandGeneric: return band_fwd_plans(g, dt);
+        case kFwdDirect: return true;
         default: return false;
     }
 }
@@ -285,6 +286,7 @@ int select_fwd(const Geo &g, int dt) {
     if (largek_fits(g, 0)) return kFwdLargek;
     if (decim_fits(g, 0)) return kFwdDecim;
     if (small_fwd_fits(g, dt)) return kFwdChannelGroup;
+    if (!band_fwd_plans(g, dt)) return kFwdDirect;  // rows too wide to stage
     const bool sq = g.kh == g.kw && g.sh == g.sw && g.dh == g.dw;
     if (sq && g.kh == 3 && g.sh == 1 && g.dh == 1) return kFwdBand33s1;
     if (sq && g.kh == 3 && g.sh == 2 && g.dh == 1) return kFwdBand33s2;
@@ -303,6 +305,7 @@ int dispatch_fwd(const Geo &g, const void *x, const void *w, const void *b, void
     if (algo == kFwdLargekMfma32) return largek_fwd32(g, x, w, b, y, s);
     if (algo == kFwdDecim) return decim_fwd(g, x, w, b, y, dt, s);
     if (algo == kFwdChannelGroup) return small_fwd(g, x, w, b, y, dt, s);
+    if (algo == kFwdDirect) return direct_fwd(g, x, w, b, y, dt, s);
     BandPlan bp;
     if (!plan_fwd<T>(g, bp)) return kErrUnsupported;
     switch (algo) {
@@ -322,16 +325,7 @@ int fwd_algo_count() { return kFwdCount; }
 const char *fwd_algo_name_of(int algo) { return algo >= 0 && algo < kFwdCount ? kFwdNames[algo] : nullptr; }
 bool fwd_algo_feasible(int algo, const Geo &g, int dtype) { return feasible_fwd(algo, g, dtype); }
 
-bool fwd_supported(const Geo &g, int dtype) {
-    if (rowwalk_fits(g, dtype, 0) || largek_mfma_fits(g, 0, dtype) || largek_fwd32_fits(g, 0, dtype) || largek_fits(g, 0) || decim_fits(g, 0) ||
-        small_fwd_fits(g, dtype))
-        return true;
-    BandPlan bp;
-    switch (dtype) {
-        case 0: return plan_fwd<float>(g, bp);
-        default: return plan_fwd<__half>(g, bp);
-    }
-}
+bool fwd_supported(const Geo &, int) { return true; }  // the direct kernel serves every geometry
 
 int launch_fwd(const Geo &g, const void *x, const void *w, const void *b, void *y, int dtype,
                hipStream_t s) {

@@ -107,6 +107,19 @@ int decim_bwd_input(const Geo &g, const void *dy, const void *w, void *dx, int d
 int decim_bwd_weight_chunks(const Geo &g);
 int decim_bwd_weight(const Geo &g, const void *x, const void *dy, void *ws, int dtype, hipStream_t s);
 
+// Direct kernels for every valid geometry (dw_direct.hip): one thread per
+// output element, operands from global memory, no LDS size limit.  Grad-weight
+// pass 1 writes the chunk partials [ic][chunks][M*(k*k + 1)].
+int direct_fwd(const Geo &g, const void *x, const void *w, const void *b, void *y, int dtype, hipStream_t s);
+int direct_bwd_input(const Geo &g, const void *dy, const void *w, void *dx, int dtype, hipStream_t s);
+int direct_bwd_weight_chunks(const Geo &g);
+int direct_bwd_weight(const Geo &g, const void *x, const void *dy, void *ws, int dtype, hipStream_t s);
+int direct_dynconv(const void *x, const void *const *filters, const int32_t *dil, int nb, void *y, int ych, int yoff,
+                   int n, int c, int h, int w, int k, int dtype, hipStream_t s);
+int direct_dynconv_bwd(const void *x, const void *const *filters, const void *dy, int dych, int dyoff,
+                       const int32_t *dil, int nb, void *dx, void *const *dfilters, int n, int c, int h, int w, int k,
+                       int dtype, hipStream_t s);
+
 // Name of the kernel family each pass would launch for this geometry.
 const char *fwd_algo_name(const Geo &g, int dtype);
 const char *bwd_input_algo_name(const Geo &g, int dtype);

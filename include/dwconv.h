@@ -64,9 +64,9 @@ enum dw_status {
     DW_EALIAS = -7,     /* an output overlaps an input or another output */
     DW_EHIP = -8,       /* a HIP launch failed (hipGetLastError after the launch) */
     DW_EDYN = -9,       /* dynamic filter: k even, nb outside [1, 4], or a dilation < 1 */
-    DW_EUNSUPPORTED = -10 /* valid geometry whose minimal row band (rows one output row
-                             reads, times the row width) exceeds the 64 KiB of LDS a
-                             workgroup stages; nothing is launched */
+    DW_EUNSUPPORTED = -10 /* dwconv2d_set_algo: a kernel-family name that cannot run the
+                             geometry (the compute calls serve every valid geometry: rows
+                             too wide for a family's LDS staging run on direct kernels) */
 };
 
 /*

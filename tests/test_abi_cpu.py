@@ -301,3 +301,39 @@ def test_binding_checks_caller_buffers():
         N.dwconv2d_tune_bwd_weight(x, torch.zeros(1, 2, 5, 6), w.shape, 1, 1, 1)
     with pytest.raises(ValueError, match="bias has shape"):
         N.dwconv2d_tune_fwd(x, w, torch.zeros(5), 1, 1, 1)
+
+
+@pytest.mark.parametrize("dt", [torch.float32, torch.float16, torch.bfloat16])
+def test_every_valid_geometry_has_a_family(dt):
+    """No valid geometry is refused: each pass names a kernel family (direct kernels take rows
+    too wide for any family's LDS staging) and the grad-weight workspace is positive."""
+    import itertools
+    import random
+    rng = random.Random(7)
+    geos = [((1, 4, 64, 600), (4, 31, 31), 1, 15, 1), ((1, 4, 512, 512), (4, 31, 31), 1, 15, 1),
+            ((1, 4, 8, 8192), (4, 3, 3), 1, 1, 1), ((1, 1, 4, 16384), (1, 3, 3), 1, 1, 1),
+            ((1, 1, 4, 16400), (1, 3, 3), 1, 1, 1), ((1, 2, 24, 600), (2, 31, 31), 1, 15, 1),
+            ((1, 1, 520, 520), (1, 31, 31), 1, 15, 1), ((2, 3, 3, 20000), (6, 5, 5), (1, 2), (2, 4), (1, 3))]
+    for _ in range(300):
+        k = rng.choice([1, 2, 3, 5, 7, 9, 13, 31])
+        s = rng.choice([1, 2, 3])
+        d = rng.choice([1, 2, 3])
+        p = rng.randint(0, k)
+        h = rng.randint(1, 300)
+        w = rng.choice([rng.randint(1, 300), rng.randint(1000, 30000)])
+        m = rng.choice([1, 2, 3])
+        c = rng.randint(1, 8)
+        geos.append(((rng.randint(1, 3), c, h, w), (c * m, k, k), s, p, d))
+    checked = 0
+    for geo in geos:
+        try:
+            N.dwconv2d_out_size(*geo)
+        except N.DwconvError:
+            continue
+        for pass_ in (0, 1, 2):
+            assert N.dwconv2d_algo(pass_, *geo, dtype=dt), (pass_, geo)
+        assert N.dwconv2d_bwd_weight_workspace_bytes(*geo, dt) > 0
+        checked += 1
+    assert checked > 100
+    for geo in geos[:7]:
+        assert "direct" in {N.dwconv2d_algo(p_, *geo, dtype=dt) for p_ in (0, 1, 2)} or geo[1][1] == 31

@@ -815,3 +815,44 @@ def test_large_kernel_f32_matrix_deterministic():
     for r in runs[1:]:
         for t1, t2 in zip(runs[0], r):
             assert torch.equal(t1, t2)
+
+
+# ------------------------------------------------------------------ direct kernels: every valid geometry
+@pytest.mark.parametrize("n,c,h,w,mult,k,s,p,d,dt", [
+    (1, 2, 24, 600, 1, 31, 1, 15, 1, "f32"),      # 31 x 31 over rows of 600
+    (1, 1, 520, 520, 1, 31, 1, 15, 1, "f32"),     # 31 x 31 over a 520 x 520 plane
+    (1, 1, 4, 16400, 1, 3, 1, 1, 1, "f32"),       # 3 x 3 over rows of 16400
+    (1, 1, 4, 16400, 1, 3, 1, 1, 1, "f16"),
+    (1, 4, 8, 8192, 1, 3, 1, 1, 1, "f32"),
+    (2, 3, 3, 20000, 2, 5, (1, 2), (2, 4), (1, 3), "bf16"),  # per-axis stride, pad, dilation; multiplier 2
+])
+def test_wide_rows(n, c, h, w, mult, k, s, p, d, dt):
+    x, wt, b, dy = static_case(n, c, h, w, mult, k, s, p, d, DT[dt], 1600 + h + w + k)
+    check_static(x, wt, b, dy, s, p, d, "wide n%d c%d %dx%d m%d k%d s%s p%s d%s %s" % (n, c, h, w, mult, k, s, p, d, dt))
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("n,c,h,w,mult,k,s,p,d", [
+    (2, 3, 17, 23, 1, 3, 1, 1, 1), (2, 2, 20, 18, 2, 5, 2, 4, 2), (1, 2, 13, 29, 3, 7, (2, 1), (3, 0), (1, 2)),
+    (3, 2, 9, 9, 1, 31, 1, 15, 1), (1, 1, 1, 1, 1, 3, 1, 1, 1), (2, 2, 11, 12, 1, 4, 3, 2, 1),
+])
+def test_direct_family_forced(n, c, h, w, mult, k, s, p, d, dt):
+    """The direct kernels on ordinary geometries, selected through the table."""
+    geo = ((n, c, h, w), (c * mult, k, k), s, p, d)
+    x, wt, b, dy = static_case(n, c, h, w, mult, k, s, p, d, DT[dt], 1650 + h + w + k)
+    try:
+        for pass_ in (0, 1, 2):
+            dc.dwconv2d_set_algo(pass_, *geo, dtype=DT[dt], algo="direct")
+        check_static(x, wt, b, dy, s, p, d, "direct n%d c%d %dx%d m%d k%d %s" % (n, c, h, w, mult, k, dt))
+    finally:
+        for pass_ in (0, 1, 2):
+            dc.dwconv2d_set_algo(pass_, *geo, dtype=DT[dt], algo=None)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape,k,dils", [((1, 2, 6, 12000), 3, (1, 3, 5)), ((1, 1, 3, 20000), 5, (1, 2))])
+def test_dynamic_wide_rows(shape, k, dils, dtype):
+    """Rows too wide for the staged band run on the direct dynamic kernels."""
+    x, fs, dy = dyn_bwd_inputs(*shape, k, dils, DT[dtype], 1700 + sum(shape) + k, fdist=("N", 0.0, 1.0 / (k * k)))
+    check_dyn(x, fs, dils, "dynamic-wide %s k%d %s" % (shape, k, dtype))
+    check_dyn_bwd(x, fs, dy, dils, "dynamic-wide-bwd %s k%d %s" % (shape, k, dtype))
