@@ -8,6 +8,8 @@ ABI's names:
     dwconv2d_fwd(x, w, bias=None, stride=1, padding=0, dilation=1)
     dwconv2d_bwd_input(dy, w, x_shape, stride=1, padding=0, dilation=1)
     dwconv2d_bwd_weight(x, dy, w_shape, stride=1, padding=0, dilation=1, with_bias=True)
+    dwconv2d_bwd_weight_noalloc(x, dy, w_shape, stride=1, padding=0, dilation=1, with_bias=True)
+        (same result; partial sums in the library's fixed device scratch, no allocation)
     dynconv_multidil_fwd(x, filters, dilations=(1, 3, 5))
     dynconv_multidil_bwd(x, filters, dy, dilations=(1, 3, 5), need_dx=True, need_dfilters=True)
     dynconv_multidil_fwd_into(x, filters, y, channel_offset, dilations=(1, 3, 5))
@@ -23,6 +25,7 @@ from ._native import (  # noqa: F401
     dwconv2d_algo_candidates,
     dwconv2d_bwd_input,
     dwconv2d_bwd_weight,
+    dwconv2d_bwd_weight_noalloc,
     dwconv2d_bwd_weight_workspace_bytes,
     dwconv2d_fwd,
     dwconv2d_out_size,

@@ -18,7 +18,7 @@ DW_F32, DW_F16, DW_BF16 = 0, 1, 2
 STATUS = {
     0: "DW_OK", -1: "DW_EPTR", -2: "DW_ESHAPE", -3: "DW_EMULT", -4: "DW_EDTYPE",
     -5: "DW_EWORKSPACE", -6: "DW_ETOOLARGE", -7: "DW_EALIAS", -8: "DW_EHIP",
-    -9: "DW_EDYN", -10: "DW_EUNSUPPORTED",
+    -9: "DW_EDYN", -10: "DW_EUNSUPPORTED", -11: "DW_ESCRATCH",
 }
 # every exported symbol the header declares
 EXPORTS = (
@@ -27,8 +27,11 @@ EXPORTS = (
     "dynconv_multidil_fwd", "dynconv_multidil_bwd", "dynconv_multidil_fwd_into",
     "dynconv_multidil_bwd_from", "dwconv2d_algo", "dw_status_str",
     "dwconv2d_algo_candidates", "dwconv2d_set_algo", "dwconv2d_tune_fwd", "dwconv2d_tune_bwd_input",
-    "dwconv2d_tune_bwd_weight",
+    "dwconv2d_tune_bwd_weight", "dwconv2d_bwd_weight_noalloc",
 )
+
+# size of the device array dwconv2d_bwd_weight_noalloc keeps its partial sums in
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 _I64 = ctypes.c_int64
 _VP = ctypes.c_void_p
@@ -64,6 +67,8 @@ def lib() -> ctypes.CDLL:
     L.dwconv2d_bwd_weight_workspace_bytes.restype = ctypes.c_int
     L.dwconv2d_bwd_weight.argtypes = [_VP, _VP, _VP, _VP, _VP, ctypes.c_size_t] + _GEO + [ctypes.c_int, _VP]
     L.dwconv2d_bwd_weight.restype = ctypes.c_int
+    L.dwconv2d_bwd_weight_noalloc.argtypes = [_VP, _VP, _VP, _VP] + _GEO + [ctypes.c_int, _VP]
+    L.dwconv2d_bwd_weight_noalloc.restype = ctypes.c_int
     L.dynconv_multidil_fwd.argtypes = [_VP, ctypes.POINTER(_VP), ctypes.POINTER(ctypes.c_int32),
                                        ctypes.c_int32, _VP, _I64, _I64, _I64, _I64, _I64,
                                        ctypes.c_int, _VP]
@@ -252,6 +257,31 @@ def dwconv2d_bwd_weight(x, dy, w_shape, stride=1, padding=0, dilation=1, with_bi
                                      _dev(out_bias, "out_bias") if with_bias else None,
                                      _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
                                      *geo, code, _stream(x)), "dwconv2d_bwd_weight")
+    return out, (out_bias if with_bias else None)
+
+
+def dwconv2d_bwd_weight_noalloc(x, dy, w_shape, stride=1, padding=0, dilation=1, with_bias=True,
+                                out=None, out_bias=None):
+    """dwconv2d_bwd_weight with the partial sums in the library's fixed device scratch.
+
+    The library allocates nothing; pass `out` (and `out_bias`) to allocate nothing here either.
+    """
+    import torch
+    geo = _geo(x.shape, w_shape, stride, padding, dilation)
+    code = _dtype_code(x)
+    oh, ow = dwconv2d_out_size(x.shape, w_shape, stride, padding, dilation)
+    _match(dy, "dy", (geo[0], geo[4], oh, ow), x)
+    if out is None:
+        out = torch.empty(tuple(int(s) for s in w_shape), dtype=x.dtype, device=x.device)
+    _match(out, "out", w_shape, x)
+    if with_bias:
+        if out_bias is None:
+            out_bias = torch.empty((geo[4],), dtype=x.dtype, device=x.device)
+        _match(out_bias, "out_bias", (geo[4],), x)
+    with torch.cuda.device(x.device):  # the library resolves the scratch of the current device
+        _check(lib().dwconv2d_bwd_weight_noalloc(_dev(x, "x"), _dev(dy, "dy"), _dev(out, "out"),
+                                                 _dev(out_bias, "out_bias") if with_bias else None,
+                                                 *geo, code, _stream(x)), "dwconv2d_bwd_weight_noalloc")
     return out, (out_bias if with_bias else None)
 
 

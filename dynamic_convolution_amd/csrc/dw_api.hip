@@ -10,6 +10,7 @@
 #include <stdint.h>
 
 #include <cstring>
+#include <mutex>
 
 #include "dw_internal.hpp"
 #include "dwconv.h"
@@ -183,6 +184,44 @@ int tune_pass(int pass, const dw::Geo &g, int dtype, int reps, hipStream_t s, Ru
 
 }  // namespace
 
+// Device scratch of dwconv2d_bwd_weight_noalloc: the grad-weight's per-block
+// partial sums (pass 1) that the fixed-order reduction (pass 2) reads back.
+// Each GPU the library runs on holds its own copy until the process ends.  In
+// host code `scratch` names a host-side stand-in, never the device memory:
+// only the address hipGetSymbolAddress returns for a device is passed on.
+static __device__ __align__(256) unsigned char scratch[DWCONV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];  // device address of `scratch`, per device ordinal
+
+// The current device's copy of `scratch`, resolved once per device with that
+// device current.  Fails when the stream belongs to another device.
+int scratch_for(hipStream_t stream, void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DW_EHIP;
+    if (stream) {
+        hipDevice_t sdev = -1;
+        if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return DW_EHIP;
+        if (sdev != dev) return DW_ESCRATCH;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return DW_EHIP;
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return DW_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int dwconv2d_out_size(int64_t n, int64_t ic, int64_t ih, int64_t iw, int64_t oc, int64_t kh, int64_t kw,
@@ -264,6 +303,33 @@ int dwconv2d_bwd_weight(const void *x, const void *dy, void *dwt, void *db, void
                 overlap(db, bb, workspace, wsb))))
         return DW_EALIAS;
     return map_launch(dw::launch_bwd_weight(g, x, dy, dwt, db, workspace, dtype, static_cast<hipStream_t>(stream)));
+}
+
+int dwconv2d_bwd_weight_noalloc(const void *x, const void *dy, void *dwt, void *db, int64_t n, int64_t ic,
+                                int64_t ih, int64_t iw, int64_t oc, int64_t kh, int64_t kw, int64_t stride_h,
+                                int64_t stride_w, int64_t pad_h, int64_t pad_w, int64_t dil_h, int64_t dil_w,
+                                int dtype, void *stream) {
+    if (dtype != DW_F32 && dtype != DW_F16 && dtype != DW_BF16) return DW_EDTYPE;
+    dw::Geo g;
+    const int rc = check_geometry(n, ic, ih, iw, oc, kh, kw, stride_h, stride_w, pad_h, pad_w, dil_h, dil_w, &g);
+    if (rc != DW_OK) return rc;
+    const size_t e = elem_size(dtype);
+    if (!x || !dy || !dwt) return DW_EPTR;
+    if (!aligned(x, e) || !aligned(dy, e) || !aligned(dwt, e) || (db && !aligned(db, e))) return DW_EPTR;
+    const int64_t need = dw::bwd_weight_workspace_selected(g, dtype);
+    if (need < 0) return DW_EUNSUPPORTED;
+    if (static_cast<uint64_t>(need) > DWCONV_NOALLOC_SCRATCH_BYTES) return DW_ESCRATCH;
+    const size_t xb = x_bytes(g, e), yb = y_bytes(g, e), wb = w_bytes(g, e), bb = b_bytes(g, e);
+    if (overlap(dwt, wb, x, xb) || overlap(dwt, wb, dy, yb) ||
+        (db && (overlap(db, bb, x, xb) || overlap(db, bb, dy, yb) || overlap(db, bb, dwt, wb))))
+        return DW_EALIAS;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    void *ws = nullptr;
+    const int src = scratch_for(s, &ws);
+    if (src != DW_OK) return src;
+    // pass 1 overwrites every partial-sum slot pass 2 reads, so the scratch
+    // needs no clearing between calls
+    return map_launch(dw::launch_bwd_weight(g, x, dy, dwt, db, ws, dtype, s));
 }
 
 int dynconv_multidil_fwd_into(const void *x, const void *const *filters, const int32_t *dilations, int32_t nb,
@@ -462,6 +528,9 @@ const char *dw_status_str(int status) {
         case DW_EHIP: return "HIP kernel launch failed";
         case DW_EDYN: return "dynamic filter: k must be odd, 1 <= nb <= 4, dilations >= 1";
         case DW_EUNSUPPORTED: return "kernel family cannot run this geometry";
+        case DW_ESCRATCH:
+            return "no-alloc grad-weight: partial sums exceed the fixed device scratch, or the stream is on "
+                   "another device";
         default: return "unknown status";
     }
 }

@@ -569,6 +569,9 @@ int64_t bwd_weight_workspace(const Geo &g, int dtype) {
     return need;
 }
 
+// Workspace bytes of the family the selection picks for this geometry alone.
+int64_t bwd_weight_workspace_selected(const Geo &g, int dtype) { return ws_for(select_bwd_weight(g, dtype), g, dtype); }
+
 int launch_bwd_weight(const Geo &g, const void *x, const void *dy, void *dwt, void *db, void *ws, int dtype,
                       hipStream_t s) {
     switch (dtype) {

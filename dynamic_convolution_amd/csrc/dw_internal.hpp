@@ -32,6 +32,7 @@ int launch_bwd_input(const Geo &g, const void *dy, const void *w, void *dx, int 
                      hipStream_t s);
 // Bytes of workspace launch_bwd_weight needs; -1 when the geometry is unsupported.
 int64_t bwd_weight_workspace(const Geo &g, int dtype);
+int64_t bwd_weight_workspace_selected(const Geo &g, int dtype);
 int launch_bwd_weight(const Geo &g, const void *x, const void *dy, void *dwt, void *db,
                       void *ws, int dtype, hipStream_t s);
 // Dynamic filter forward: branch b, channel ch is written to plane

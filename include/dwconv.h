@@ -64,10 +64,16 @@ enum dw_status {
     DW_EALIAS = -7,     /* an output overlaps an input or another output */
     DW_EHIP = -8,       /* a HIP launch failed (hipGetLastError after the launch) */
     DW_EDYN = -9,       /* dynamic filter: k even, nb outside [1, 4], or a dilation < 1 */
-    DW_EUNSUPPORTED = -10 /* dwconv2d_set_algo: a kernel-family name that cannot run the
-                             geometry (the compute calls serve every valid geometry: rows
-                             too wide for a family's LDS staging run on direct kernels) */
+    DW_EUNSUPPORTED = -10, /* dwconv2d_set_algo: a kernel-family name that cannot run the
+                              geometry (the compute calls serve every valid geometry: rows
+                              too wide for a family's LDS staging run on direct kernels) */
+    DW_ESCRATCH = -11     /* dwconv2d_bwd_weight_noalloc: the partial sums need more than
+                             DWCONV_NOALLOC_SCRATCH_BYTES, or the stream belongs to a device
+                             other than the current one */
 };
+
+/* Size of the device array dwconv2d_bwd_weight_noalloc keeps its partial sums in. */
+#define DWCONV_NOALLOC_SCRATCH_BYTES (32u << 20)
 
 /*
  * Output spatial size for the geometry above.  Writes *oh and *ow (either may
@@ -150,6 +156,30 @@ int dwconv2d_bwd_weight(const void *x, const void *dy, void *dw, void *db,
                         int64_t oc, int64_t kh, int64_t kw,
                         int64_t stride_h, int64_t stride_w, int64_t pad_h, int64_t pad_w,
                         int64_t dil_h, int64_t dil_w, int dtype, void *stream);
+
+/*
+ * dwconv2d_bwd_weight without a workspace argument and without any allocation,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  Same
+ * arguments, results and kernels as dwconv2d_bwd_weight, bit for bit; the
+ * partial sums go to a fixed device array of DWCONV_NOALLOC_SCRATCH_BYTES
+ * that the library holds on each GPU it runs on until the process ends
+ * (resolved on the first call on each device, with that device current).
+ *   Succeeds whenever dwconv2d_bwd_weight_workspace_bytes reports at most
+ *   DWCONV_NOALLOC_SCRATCH_BYTES for the geometry (it needs only the selected
+ *   kernel family's part of that figure); returns DW_ESCRATCH when the
+ *   partial sums do not fit, or when `stream` is not on the current device.
+ *   Calls no hipMalloc, hipFree or hipMemset: the array keeps the last call's
+ *   contents, and the first kernel overwrites every value the second reads.
+ *   Every call on one GPU shares that GPU's array: calls that may overlap on
+ *   one GPU (different streams, different host threads) race and must be
+ *   ordered by the caller.
+ */
+int dwconv2d_bwd_weight_noalloc(const void *x, const void *dy, void *dw, void *db,
+                                int64_t n, int64_t ic, int64_t ih, int64_t iw,
+                                int64_t oc, int64_t kh, int64_t kw,
+                                int64_t stride_h, int64_t stride_w, int64_t pad_h, int64_t pad_w,
+                                int64_t dil_h, int64_t dil_w, int dtype, void *stream);
 
 /*
  * Fused per-pixel dynamic filter at several dilations, written straight into

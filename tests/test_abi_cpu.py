@@ -337,3 +337,30 @@ def test_every_valid_geometry_has_a_family(dt):
     assert checked > 100
     for geo in geos[:7]:
         assert "direct" in {N.dwconv2d_algo(p_, *geo, dtype=dt) for p_ in (0, 1, 2)} or geo[1][1] == 31
+
+
+def test_bwd_weight_noalloc_validation():
+    """The allocation-free grad-weight validates like dwconv2d_bwd_weight, and
+    refuses geometries whose partial sums exceed its fixed device scratch
+    before any HIP call."""
+    L = N.lib()
+    g = _geo()
+    f = L.dwconv2d_bwd_weight_noalloc
+    assert f(FAKE, FAKE, FAKE + 8192, None, *g, 9, None) == -4                  # dtype
+    assert f(FAKE, FAKE, None, None, *g, 0, None) == -1                         # no dw
+    assert f(FAKE, FAKE, FAKE + 8194, None, *g, 0, None) == -1                  # misaligned dw
+    assert f(FAKE, FAKE, FAKE, None, *g, 0, None) == -7                         # dw inside x
+    assert f(FAKE, FAKE, FAKE + 8192, FAKE + 8192, *g, 0, None) == -7           # db inside dw
+    assert f(FAKE, FAKE, FAKE + 8192, None, *_geo(oc=4), 0, None) == -3         # multiplier
+    assert f(FAKE, FAKE, FAKE + 8192, None, *_geo(ph=-1), 0, None) == -2        # geometry
+    # multiplier 8 at 31 x 31 over 2048 channels: some 60 MiB of partial sums
+    big = _geo(n=1, ic=2048, ih=8, iw=8, oc=16384, kh=31, kw=31, ph=15, pw=15)
+    need = ctypes.c_size_t()
+    assert L.dwconv2d_bwd_weight_workspace_bytes(*big, 0, ctypes.byref(need)) == 0
+    assert need.value > N.NOALLOC_SCRATCH_BYTES
+    dwp = FAKE + (1 << 30)
+    assert f(FAKE, FAKE + (1 << 29), dwp, None, *big, 0, None) == -11
+    assert "scratch" in N.status_str(-11)
+    hdr = open(HEADER).read()
+    m = re.search(r"#define DWCONV_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", hdr)
+    assert m and int(m.group(1)) << int(m.group(2)) == N.NOALLOC_SCRATCH_BYTES
