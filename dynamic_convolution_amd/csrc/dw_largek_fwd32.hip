@@ -168,19 +168,22 @@ __global__ __launch_bounds__(256, 4) void lk_fwd32_kernel(Lf32Args<T> a) {
                 const int r = wave + 4 * (q / NCT), ct = q % NCT;
                 // Lane (t, h) gathers, from register u of lane ((t + j) mod 32, h),
                 // D[j][(t + j) mod 32] with j = 8 (u / 4) + 4 h + u % 4: the diagonal
-                // c - j = t when t + j < 32, else t - 32.  Two fixed-order sums per lane.
-                float spos = 0.f, sneg = 0.f;
+                // c - j = t when t + j < 32, else t - 32.  j grows with u, so the
+                // registers of diagonal t are a prefix of u: one running sum in a
+                // fixed order, captured where the prefix ends; diagonal t - 32 gets
+                // the total minus that prefix (two vector instructions per register
+                // instead of four).
+                float run = 0.f, spos = 0.f;
 #pragma unroll
                 for (int u = 0; u < 16; ++u) {
                     const int j = 8 * (u >> 2) + 4 * h + (u & 3);
                     const int src = ((jl + j) & 31) + 32 * h;
                     const float v = __int_as_float(
                         __builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(acc[u])));
-                    if (jl + j < 32)
-                        spos += v;
-                    else
-                        sneg += v;
+                    run += v;
+                    spos = (jl + j < 32) ? run : spos;
                 }
+                const float sneg = run - spos;
                 // both halves' sums of a diagonal: lanes t (h = 0) and t + 32 (h = 1)
                 const float opos = __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, __float_as_int(spos)));
                 const float oneg = __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, __float_as_int(sneg)));
