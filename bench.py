@@ -39,6 +39,11 @@ roofline     the dominant kernel tag (most event time): algorithmic bytes or flo
              reported) against the MI355X peak for that tag's arithmetic
              (HBM 8 TB/s; fp32 157.3 TFLOP/s; fp16/bf16 matrix cores 2.5 PFLOP/s).
              step_frac: the whole step's rate against the same peak.
+             ceiling: the same launch against what this GPU was measured to
+             reach in the same run (libdwprobe.so): 16-byte nontemporal
+             copy / read / write streams for bandwidth-bound tags (mixed by the
+             tag's read share of its bytes), the fp32 or fp16 matrix-instruction
+             rate, or the fp32 vector FMA rate for the tag's arithmetic.
 per_case     each call alone and cold (after a 512 MiB fill that evicts the last-level
              cache): HIP events around one eager call, median of --repeats, its
              rate and fraction of roofline, and the oracle's time for the same call
@@ -135,9 +140,10 @@ class Call:
     """One entry-point call of the step: its tag (pass.family.geometry), algorithmic
     bytes and flops, the case it belongs to, and (static passes) a tuner."""
 
-    def __init__(self, tag, fn, nbytes, flops, case, pass_, tune=None):
+    def __init__(self, tag, fn, nbytes, flops, case, pass_, tune=None, rbytes=None):
         self.tag, self.fn, self.nbytes, self.flops, self.tune = tag, fn, nbytes, flops, tune
         self.case, self.pass_ = case, pass_
+        self.rbytes = nbytes if rbytes is None else rbytes  # bytes read (the rest are written)
 
 
 def static_calls(dc, case, dev, seed, passes=("fwd", "bwd_in", "bwd_w")):
@@ -171,17 +177,20 @@ def static_calls(dc, case, dev, seed, passes=("fwd", "bwd_in", "bwd_w")):
 
     if "fwd" in passes:
         calls.append(Call(tag(0, "fwd"), lambda: dc.dwconv2d_fwd(x, w, b, s, p, d, out=y), sx + W + B + Y, 2 * macs,
-                          label, "fwd", lambda: dc.dwconv2d_tune_fwd(x, w, b, s, p, d, out=y, reps=5)))
+                          label, "fwd", lambda: dc.dwconv2d_tune_fwd(x, w, b, s, p, d, out=y, reps=5),
+                          rbytes=sx + W + B))
     if "bwd_in" in passes:
         calls.append(Call(tag(1, "bwd_input"), lambda: dc.dwconv2d_bwd_input(dy, w, x.shape, s, p, d, out=dx),
                           Y + W + X, 2 * macs, label, "bwd_input",
-                          lambda: dc.dwconv2d_tune_bwd_input(dy, w, x.shape, s, p, d, out=dx, reps=5)))
+                          lambda: dc.dwconv2d_tune_bwd_input(dy, w, x.shape, s, p, d, out=dx, reps=5),
+                          rbytes=Y + W))
     if "bwd_w" in passes:
         calls.append(Call(tag(2, "bwd_weight"),
                           lambda: dc.dwconv2d_bwd_weight(x, dy, w.shape, s, p, d, with_bias=with_bias, out=gw,
                                                          out_bias=gb, workspace=ws),
                           sx + Y + W + B, 2 * macs, label, "bwd_weight",
-                          lambda: dc.dwconv2d_tune_bwd_weight(x, dy, w.shape, s, p, d, with_bias=with_bias, reps=5)))
+                          lambda: dc.dwconv2d_tune_bwd_weight(x, dy, w.shape, s, p, d, with_bias=with_bias, reps=5),
+                          rbytes=sx + Y))
     tensors = dict(x=x, w=w, b=b, dy=dy, y=y, dx=dx, gw=gw, gb=gb)
     inputs = {"x": x, "w": w, "dy": dy}
     if b is not None:
@@ -281,11 +290,11 @@ def build_dynamic(dc, dev):
                 label = "N%d_C%d_H%d_%s" % (n, c, h, dts)
                 cf_ = Call("dyn.fused.k3_%s" % dts,
                            (lambda x=x, fs=fs, y=y: dc.dynconv_multidil_fwd(x, fs, D["dilations"], out=y)),
-                           X + TF + Y, 2 * n * c * taps, label, "fwd")
+                           X + TF + Y, 2 * n * c * taps, label, "fwd", rbytes=X + TF)
                 cb = Call("dyn_bwd.fused.k3_%s" % dts,
                           (lambda x=x, fs=fs, dy=dy, dx=dx, dfs=dfs:
                            dc.dynconv_multidil_bwd(x, fs, dy, D["dilations"], out_dx=dx, out_dfilters=dfs)),
-                          X + Y + TF + X + FF, 3 * n * c * taps, label, "bwd")
+                          X + Y + TF + X + FF, 3 * n * c * taps, label, "bwd", rbytes=X + Y + TF)
                 fwd.append(cf_)
                 bwd.append(cb)
                 inputs = {"x": x, "dy": dy}
@@ -299,23 +308,92 @@ def build_dynamic(dc, dev):
                 kind="bytes", cfg=cfg)
 
 
-def device_copy_gbs(dev, nbytes=1 << 30, reps=5):
-    """Device-to-device copy rate (read + write bytes per second, GB/s) of torch's
-    copy kernel over two buffers of `nbytes`, timed with HIP events."""
+def device_ceilings(dev, nbytes=1 << 30, reps=5):
+    """What this GPU reaches in this run, measured with libdwprobe.so: GB/s of
+    16-byte nontemporal copy (read + write bytes), read-only and write-only
+    streams over `nbytes` buffers, and TFLOP/s of fp32 and fp16 matrix
+    instructions and fp32 vector FMAs; median of `reps` launches each.
+    None when the probe library is not built."""
+    import ctypes
     import torch
-    src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    from dynamic_convolution_amd import build as B
+    if not os.path.exists(B.PROBE_LIB):
+        return None
+    L = ctypes.CDLL(B.PROBE_LIB)
+    L.dw_probe_stream.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                  ctypes.c_void_p, ctypes.c_void_p]
+    L.dw_probe_stream.restype = ctypes.c_int
+    L.dw_probe_compute.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                   ctypes.POINTER(ctypes.c_double), ctypes.c_void_p]
+    L.dw_probe_compute.restype = ctypes.c_int
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
-    dst.copy_(src)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        dst.copy_(src)
-    e1.record()
-    torch.cuda.synchronize()
-    sec = e0.elapsed_time(e1) / 1e3 / reps
+    word = torch.zeros(4, dtype=torch.int32, device=dev)
+
+    def timed(launch):
+        launch()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            launch()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) / 1e3)
+        return statistics.median(ts)
+
+    out = {}
+    for name, kind, moved in (("copy_gbs", 0, 2 * nbytes), ("read_gbs", 1, nbytes), ("write_gbs", 2, nbytes)):
+        def launch(kind=kind):
+            rc = L.dw_probe_stream(kind, src.data_ptr(), dst.data_ptr(), nbytes, word.data_ptr(), sp)
+            if rc != 0:
+                raise RuntimeError("dw_probe_stream failed: %d" % rc)
+        out[name] = round(moved / timed(launch) / 1e9, 1)
     del src, dst
-    return 2 * nbytes / sec / 1e9
+    blocks, iters = 4096, 512
+    buf = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    for name, kind, it in (("mfma_f32_tflops", 0, iters), ("mfma_f16_tflops", 1, iters),
+                           ("valu_fma_f32_tflops", 2, 8 * iters)):
+        fl = ctypes.c_double()
+
+        def launch(kind=kind, it=it):
+            rc = L.dw_probe_compute(kind, buf.data_ptr(), blocks, it, ctypes.byref(fl), sp)
+            if rc != 0:
+                raise RuntimeError("dw_probe_compute failed: %d" % rc)
+        sec = timed(launch)
+        out[name] = round(fl.value / sec / 1e12, 1)
+    return out
+
+
+def ceiling_of(tag, kind, rfrac, ceil):
+    """(value, unit, basis) of the measured ceiling for a tag: bandwidth-bound
+    tags interpolate linearly in their read share between the write-only
+    (0), copy (1/2) and read-only (1) stream rates; flop-counted tags take the
+    matrix or vector rate of their arithmetic."""
+    if not ceil:
+        return None
+    if kind == "bytes":
+        if rfrac >= 0.5:
+            v = ceil["copy_gbs"] + (ceil["read_gbs"] - ceil["copy_gbs"]) * (rfrac - 0.5) / 0.5
+        else:
+            v = ceil["write_gbs"] + (ceil["copy_gbs"] - ceil["write_gbs"]) * rfrac / 0.5
+        return v, "GB/s", "stream (read share %.2f)" % rfrac
+    if ".largek_mfma." in tag and not tag.endswith("_f32"):
+        return ceil["mfma_f16_tflops"], "TFLOP/s", "fp16 matrix instructions"
+    if ".largek_mfma_f32." in tag:
+        return ceil["mfma_f32_tflops"], "TFLOP/s", "fp32 matrix instructions"
+    return ceil["valu_fma_f32_tflops"], "TFLOP/s", "fp32 vector FMA"
+
+
+def tag_ceiling(tag, r, kind, ceil):
+    """The measured ceiling of one tag's rate in the step and the fraction reached."""
+    cv = ceiling_of(tag, kind, r["rbytes"] / max(1, r["bytes"]), ceil)
+    if cv is None:
+        return {}
+    rate = (r["bytes"] / (r["ms"] / 1e3) / 1e9) if kind == "bytes" else (r["flops"] / (r["ms"] / 1e3) / 1e12)
+    return {"ceiling": round(cv[0], 1), "frac_of_ceiling": round(rate / cv[0], 4)}
 
 
 # ---------------------------------------------------------------- host facts
@@ -570,7 +648,7 @@ def stats(vals, nd=4):
             "std": round(statistics.pstdev(vals), nd), "min": round(min(vals), nd), "n": len(vals)}
 
 
-def run_workload(name, args, dc, dev, cpu_target):
+def run_workload(name, args, dc, dev, cpu_target, ceil=None):
     import torch
     wl = build_workload(name, dc, dev)
     if args.tune:
@@ -660,10 +738,11 @@ def run_workload(name, args, dc, dev, cpu_target):
     for st in range(args.steps):
         for gi, (tag, cls) in enumerate(groups):
             ms = ev[st][gi][0].elapsed_time(ev[st][gi][1])
-            r = per_tag.setdefault(tag, {"ms": 0.0, "launches": 0, "bytes": 0, "flops": 0})
+            r = per_tag.setdefault(tag, {"ms": 0.0, "launches": 0, "bytes": 0, "rbytes": 0, "flops": 0})
             r["ms"] += ms
             r["launches"] += len(cls)
             r["bytes"] += sum(c.nbytes for c in cls)
+            r["rbytes"] += sum(c.rbytes for c in cls)
             r["flops"] += sum(c.flops for c in cls)
     dom_tag = max(per_tag, key=lambda t: per_tag[t]["ms"])
 
@@ -741,9 +820,11 @@ def run_workload(name, args, dc, dev, cpu_target):
             "step_frac": round(value / step_peak, 4),
             "frac_is": "the dominant kernel tag's average launch against its peak; step_frac is the whole "
                        "step's rate against %s" % ("8 TB/s" if kind == "bytes" else "the fp32 peak (157.3 TFLOP/s)")}
-    if kind == "bytes" and not args.copy_ref:
-        copy_gbs = device_copy_gbs(dev)
-        roof["secondary"] = {"copy_gbs": round(copy_gbs, 1), "frac_of_copy": round(achieved / copy_gbs, 4)}
+    dom_rfrac = sum(cl.rbytes for cl in dom_calls) / max(1, dom_bytes)
+    cv = ceiling_of(dom_tag, kind, dom_rfrac, ceil)
+    if cv is not None:
+        roof["ceiling"] = {"value": round(cv[0], 1), "unit": cv[1], "basis": cv[2],
+                           "frac": round(achieved / cv[0], 4)}
     rec = {
         "workload": wl["desc"], "value": round(value, 2), "unit": unit, "ms_per_step": round(ms_step, 4),
         "dtype": wl["dtype"], "config": dict({"workload": wl["desc"],
@@ -756,10 +837,11 @@ def run_workload(name, args, dc, dev, cpu_target):
         "step_timing_ms": stats([s_ / args.steps * 1e3 for s_ in step_secs]),
         "roofline": roof, "launches_executed": executed, "tensor_copies": ncopy,
         "gpu_clocks": {"before": clocks_before, "after": clocks_after},
-        "per_kernel": {t: {"avg_us": round(r["ms"] / r["launches"] * 1e3, 2),
-                           "share": round(r["ms"] / sum(v["ms"] for v in per_tag.values()), 4),
-                           "gbs": round(r["bytes"] / (r["ms"] / 1e3) / 1e9, 1),
-                           "gflops": round(r["flops"] / (r["ms"] / 1e3) / 1e9, 1)}
+        "per_kernel": {t: dict({"avg_us": round(r["ms"] / r["launches"] * 1e3, 2),
+                                "share": round(r["ms"] / sum(v["ms"] for v in per_tag.values()), 4),
+                                "gbs": round(r["bytes"] / (r["ms"] / 1e3) / 1e9, 1),
+                                "gflops": round(r["flops"] / (r["ms"] / 1e3) / 1e9, 1)},
+                               **tag_ceiling(t, r, kind, ceil))
                        for t, r in sorted(per_tag.items())},
     }
     if digests is not None:
@@ -776,9 +858,11 @@ def run_workload(name, args, dc, dev, cpu_target):
                round(rate / pk, 4), t_roof * 1e6 < LATENCY_US]
         est = cpu_est.get(id(cl))
         row.append(round(est / sec, 1) if est else None)
+        cv = ceiling_of(cl.tag, kind, cl.rbytes / max(1, cl.nbytes), ceil)
+        row.append(round(rate / cv[0], 4) if cv else None)
         rows.append(row)
     rec["per_case"] = {"columns": ["case", "pass", "us", "GB/s" if kind == "bytes" else "TFLOP/s", "frac",
-                                   "latency_bound", "speedup_vs_oracle_all_threads"], "rows": rows,
+                                   "latency_bound", "speedup_vs_oracle_all_threads", "frac_of_ceiling"], "rows": rows,
                        "timing": "HIP events around one eager call after a 512 MiB fill (cold), median of %d"
                                  % max(1, args.repeats)}
     del copies, wl, calls_by_copy, calls
@@ -807,10 +891,12 @@ def main(argv=None):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     names = WORKLOADS if args.workload == "all" else [args.workload]
+    print("[bench] device ceilings", file=sys.stderr, flush=True)
+    ceil = device_ceilings(dev)
     recs = {}
     for i, nm in enumerate(names):
         print("[bench] %s" % nm, file=sys.stderr, flush=True)
-        recs[nm] = run_workload(nm, args, dc, dev, args.cpu_seconds if i == 0 else args.cpu_seconds / 2)
+        recs[nm] = run_workload(nm, args, dc, dev, args.cpu_seconds if i == 0 else args.cpu_seconds / 2, ceil)
     head = recs[names[0]]
     out = {
         "metric": "dwconv fwd+bwd GFLOP/s and HBM GB/s at 1 GPU, % of roofline, vs CPU oracle",
@@ -818,6 +904,7 @@ def main(argv=None):
         "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": head["dtype"], "data": "synthetic (seeded, shapes and distributions of the workload)",
         "config": head["config"],
+        "device_ceilings": ceil,
     }
     for k_ in ("step_gbytes", "step_gflop", "gbs", "gflops", "step_timing_ms", "roofline", "launches_executed",
                "tensor_copies", "gpu_clocks", "per_kernel", "per_case", "input_sha256", "cpu_baseline"):

@@ -20,6 +20,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdwconv.so")
+# device-ceiling probes for the benchmark's roofline; not part of the library
+PROBE_SRC = os.path.join(PKG, "probe", "dw_probe.hip")
+PROBE_LIB = os.path.join(PKG, "libdwprobe.so")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -55,9 +58,21 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s" % r.stdout)
     os.replace(tmp, LIB)
+    build_probe()
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", PROBE_LIB)
     return LIB
+
+
+def build_probe() -> str:
+    """Compile the benchmark's device-ceiling probes into libdwprobe.so."""
+    tmp = PROBE_LIB + ".tmp%d" % os.getpid()
+    cmd = [HIPCC] + [f for f in FLAGS if not f.startswith("-I")] + ["-shared", "-o", tmp, PROBE_SRC]
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed for %s:\n%s" % (PROBE_SRC, r.stdout))
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
 
 
 if __name__ == "__main__":

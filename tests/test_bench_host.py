@@ -82,3 +82,17 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_ceiling_model():
+    import bench
+    ceil = {"copy_gbs": 5000.0, "read_gbs": 6000.0, "write_gbs": 5500.0, "mfma_f32_tflops": 140.0,
+            "mfma_f16_tflops": 2000.0, "valu_fma_f32_tflops": 100.0}
+    assert bench.ceiling_of("fwd.x.k3", "bytes", 0.5, ceil)[0] == 5000.0
+    assert bench.ceiling_of("fwd.x.k3", "bytes", 1.0, ceil)[0] == 6000.0
+    assert bench.ceiling_of("fwd.x.k3", "bytes", 0.0, ceil)[0] == 5500.0
+    assert abs(bench.ceiling_of("fwd.x.k3", "bytes", 0.75, ceil)[0] - 5500.0) < 1e-9
+    assert bench.ceiling_of("bwd_weight.largek_mfma_f32.k31_s1_m1_f32", "flops", 1, ceil)[0] == 140.0
+    assert bench.ceiling_of("fwd.largek_mfma.k31_s1_m1_f16", "flops", 1, ceil)[0] == 2000.0
+    assert bench.ceiling_of("fwd.largek_regtile.k13_s1_m1_f32", "flops", 1, ceil)[0] == 100.0
+    assert bench.ceiling_of("fwd.x", "bytes", 0.5, None) is None
