@@ -26,10 +26,12 @@
 //              LDS read;
 //   D: register r of lane l is output (32 mt + l % 32, 32 nt + 8 (r / 4)
 //      + 4 (l / 32) + r % 4), so a lane stores runs of 4 adjacent outputs.
-// A workgroup serves one channel and one image per wave (4 waves, or 2 where
-// four input tiles would not fit 64 KiB of LDS): the filter table is built
-// once, each wave stages its own image's zero-padded plane in LDS and
-// accumulates its 2 x 2 (or fewer) output tiles over the k kernel rows.
+// A workgroup (4 waves) serves one channel and 4 / MT images, one wave per
+// (image, 32-row output tile): the filter table is built once, the waves stage
+// the images' zero-padded planes in LDS together, and each wave accumulates its
+// row tile's NT column tiles over the k kernel rows (one B read feeds the NT
+// tiles it overlaps).  Two 32-row tiles of a 64-row plane on two waves keep
+// three workgroups (12 waves) per CU where whole planes per wave fit one.
 // Grad-input is the same correlation of dy with the filter flipped in both
 // axes and padding k - 1 - pad.
 #include "dw_common.hpp"
@@ -85,9 +87,9 @@ template <int K, int KPS, int MT, int NT> struct LkmGeo {
     static constexpr int XP = XC + 8;                    // row pitch (halves): an odd multiple of 16 bytes mod 32
     static constexpr int table_bytes = 2 * K * QD * 4;
     static constexpr int tile_halves = XR * XP;
-    static constexpr int WPG = (kLdsCap - table_bytes) / (tile_halves * 2) >= 4 ? 4 : 2;
-    static constexpr int lds_bytes = table_bytes + WPG * tile_halves * 2;
-    static_assert(lds_bytes <= kLdsCap, "tiles of two waves exceed the LDS budget");
+    static constexpr int IPG = 4 / MT;                   // images per workgroup: one wave per (image, row tile)
+    static constexpr int lds_bytes = table_bytes + IPG * tile_halves * 2;
+    static_assert(lds_bytes <= kLdsCap, "tiles exceed the LDS budget");
 };
 
 template <typename T, int K, int KPS, int MT, int NT, bool FLIP>
@@ -97,17 +99,20 @@ __global__ __launch_bounds__(256) void lk_mfma_kernel(LkmArgs<T> a) {
     uint32_t *wtab = reinterpret_cast<uint32_t *>(smem);  // [copy][i][QD]
     uint16_t *tiles = reinterpret_cast<uint16_t *>(smem + G::table_bytes);
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
+    const int img = wave / MT;     // image of the workgroup this wave serves
+    const int mt = wave - img * MT;  // its 32-row output tile
     const int c = blockIdx.x / a.ngroups;  // output plane channel of this pass
-    const int n = (blockIdx.x - c * a.ngroups) * G::WPG + wave;
+    const int n0 = (blockIdx.x - c * a.ngroups) * G::IPG;
+    const int n = n0 + img;
     const bool active = n < a.N;
 
     // 1. filter table: copy q (0, 1) of row i holds, in dword d, the 16-bit
     //    values of padded positions 2d + q and 2d + q + 1, where padded
     //    position p is w[i][p - kZoff] (flipped for grad-input), 0 outside.
     const uint16_t *wr = reinterpret_cast<const uint16_t *>(a.w) + static_cast<int64_t>(c) * K * K;
-    for (int e = tid; e < 2 * K * G::QD; e += 64 * G::WPG) {
+    for (int e = tid; e < 2 * K * G::QD; e += 256) {
         const int q = e / (K * G::QD);
         const int rem = e - q * K * G::QD;
         const int i = rem / G::QD;
@@ -124,49 +129,56 @@ __global__ __launch_bounds__(256) void lk_mfma_kernel(LkmArgs<T> a) {
         wtab[e] = v;
     }
 
-    // 2. this wave's padded input plane: tile[r][col] = in[r - P][col - P], 0 outside
-    uint16_t *xt = tiles + wave * G::tile_halves;
+    // 2. the workgroup's padded input planes: tile[r][col] = in[r - P][col - P],
+    //    0 outside; the MT waves of an image stage its plane together
     {
-        uint4 *z = reinterpret_cast<uint4 *>(xt);
-        for (int e = lane; e < G::tile_halves / 8; e += 64) z[e] = make_uint4(0u, 0u, 0u, 0u);
-        if (active) {
-            const int cin = FLIP ? c : c / a.mult;
-            const uint16_t *src =
-                reinterpret_cast<const uint16_t *>(a.in) + (static_cast<int64_t>(n) * a.Cin + cin) * a.IH * a.IW;
-            if (a.vin) {
-                const int vpr = a.IW / 8;
-                const int nvec = a.IH * vpr;
-                for (int v = lane; v < nvec; v += 64) {
-                    const int r = v / vpr;
-                    const int c8 = (v - r * vpr) * 8;
-                    const uint4 raw = *reinterpret_cast<const uint4 *>(src + static_cast<int64_t>(r) * a.IW + c8);
-                    uint16_t *d = xt + (r + a.P) * G::XP + c8 + a.P;
-                    const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+        uint4 *z = reinterpret_cast<uint4 *>(tiles);
+        for (int e = tid; e < G::IPG * G::tile_halves / 8; e += 256) z[e] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    __syncthreads();
+    {
+        const int cin = FLIP ? c : c / a.mult;
+        const int nimg = min(G::IPG, a.N - n0);
+        if (a.vin) {
+            const int vpr = a.IW / 8;
+            const int nvec = a.IH * vpr;
+            for (int v = tid; v < nimg * nvec; v += 256) {
+                const int im = v / nvec;
+                const int vv = v - im * nvec;
+                const int r = vv / vpr;
+                const int c8 = (vv - r * vpr) * 8;
+                const uint16_t *src = reinterpret_cast<const uint16_t *>(a.in) +
+                                      (static_cast<int64_t>(n0 + im) * a.Cin + cin) * a.IH * a.IW;
+                const uint4 raw = *reinterpret_cast<const uint4 *>(src + static_cast<int64_t>(r) * a.IW + c8);
+                uint16_t *d = tiles + im * G::tile_halves + (r + a.P) * G::XP + c8 + a.P;
+                const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) d[e] = static_cast<uint16_t>(wd[e >> 1] >> ((e & 1) * 16));
-                }
-            } else {
-                for (int e = lane; e < a.IH * a.IW; e += 64) {
-                    const int r = e / a.IW;
-                    const int col = e - r * a.IW;
-                    xt[(r + a.P) * G::XP + col + a.P] = src[e];
-                }
+                for (int e = 0; e < 8; ++e) d[e] = static_cast<uint16_t>(wd[e >> 1] >> ((e & 1) * 16));
+            }
+        } else {
+            for (int e = tid; e < nimg * a.IH * a.IW; e += 256) {
+                const int im = e / (a.IH * a.IW);
+                const int ee = e - im * a.IH * a.IW;
+                const int r = ee / a.IW;
+                const int col = ee - r * a.IW;
+                const uint16_t *src = reinterpret_cast<const uint16_t *>(a.in) +
+                                      (static_cast<int64_t>(n0 + im) * a.Cin + cin) * a.IH * a.IW;
+                tiles[im * G::tile_halves + (r + a.P) * G::XP + col + a.P] = src[ee];
             }
         }
     }
     __syncthreads();
     if (!active) return;
+    const uint16_t *xt = tiles + img * G::tile_halves;
 
     // 3. k kernel rows x KPS window steps x (MT x NT) tiles of MFMAs
     const int m = lane & 31;
     const int h = lane >> 5;
-    f32x16_v acc[MT][NT];
+    f32x16_v acc[NT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[mt][nt][r] = 0.f;
+        for (int r = 0; r < 16; ++r) acc[nt][r] = 0.f;
 
 #pragma unroll 1
     for (int i = 0; i < K; ++i) {
@@ -180,14 +192,11 @@ __global__ __launch_bounds__(256) void lk_mfma_kernel(LkmArgs<T> a) {
         }
 #pragma unroll
         for (int sp = 0; sp < KPS + 2 * (NT - 1); ++sp) {
+            const u32x4_v bf = *reinterpret_cast<const u32x4_v *>(xt + (32 * mt + m + i) * G::XP + 16 * sp + 8 * h);
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const u32x4_v bf = *reinterpret_cast<const u32x4_v *>(xt + (32 * mt + m + i) * G::XP + 16 * sp + 8 * h);
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    const int s = sp - 2 * nt;
-                    if (s >= 0 && s < KPS) acc[mt][nt] = Mfma<T>::run(af[s], bf, acc[mt][nt]);
-                }
+            for (int nt = 0; nt < NT; ++nt) {
+                const int s = sp - 2 * nt;
+                if (s >= 0 && s < KPS) acc[nt] = Mfma<T>::run(af[s], bf, acc[nt]);
             }
         }
     }
@@ -195,18 +204,17 @@ __global__ __launch_bounds__(256) void lk_mfma_kernel(LkmArgs<T> a) {
     // 4. store: lane holds, per tile and r4, outputs (32 mt + m, 32 nt + 8 r4 + 4 h + 0..3)
     const float bias = (!FLIP && a.b) ? to_f32(a.b[c]) : 0.f;
     T *op = a.out + (static_cast<int64_t>(n) * a.C + c) * a.OH * a.OW;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
+    {
         const int oh = 32 * mt + m;
-        if (oh >= a.OH) continue;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
                 const int ow = 32 * nt + 8 * r4 + 4 * h;
-                const float v0 = acc[mt][nt][4 * r4] + bias, v1 = acc[mt][nt][4 * r4 + 1] + bias;
-                const float v2 = acc[mt][nt][4 * r4 + 2] + bias, v3 = acc[mt][nt][4 * r4 + 3] + bias;
+                const float v0 = acc[nt][4 * r4] + bias, v1 = acc[nt][4 * r4 + 1] + bias;
+                const float v2 = acc[nt][4 * r4 + 2] + bias, v3 = acc[nt][4 * r4 + 3] + bias;
                 T *dst = op + oh * a.OW + ow;
+                if (oh >= a.OH) continue;
                 if (a.vout && ow + 4 <= a.OW) {
                     *reinterpret_cast<uint2 *>(dst) = make_uint2(pack2<T>(v0, v1), pack2<T>(v2, v3));
                 } else {
@@ -227,9 +235,9 @@ int run_lkm_t(const LkmArgs<T> &a, hipStream_t s) {
     constexpr int KPS = kps_of(K);
     using G = LkmGeo<K, KPS, MT, NT>;
     LkmArgs<T> b = a;
-    b.ngroups = (a.N + G::WPG - 1) / G::WPG;
+    b.ngroups = (a.N + G::IPG - 1) / G::IPG;
     const dim3 grid(static_cast<unsigned>(a.C * b.ngroups));
-    hipLaunchKernelGGL((lk_mfma_kernel<T, K, KPS, MT, NT, FLIP>), grid, dim3(64 * G::WPG), G::lds_bytes, s, b);
+    hipLaunchKernelGGL((lk_mfma_kernel<T, K, KPS, MT, NT, FLIP>), grid, dim3(256), G::lds_bytes, s, b);
     return hipGetLastError() == hipSuccess ? kOk : kErrHip;
 }
 
