@@ -398,27 +398,78 @@ __global__ __launch_bounds__(256) void lk_mfma_bwdw_kernel(LkmwArgs<T> a) {
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
     float dsum = 0.f;
 
-    for (int n = n0; n < n1; ++n) {
+    // (image, band) steps; with whole 16-byte rows the next step's input and
+    // dy rows are loaded into registers while the current band is computed
+    constexpr int NXV = ((BH + K - 1) * 2 * CS + 255) / 256;  // x vectors per thread (iw <= 16 CS)
+    constexpr int NDV = (BH * 8 + 255) / 256;                 // dy vectors per thread (ow <= 64)
+    const bool vec = a.vx && a.vd;
+    const int nsteps = (n1 - n0) * a.nbands;
+    uint4 pfx[NXV], pfd[NDV];
+    auto prefetch = [&](int t) {
+        const int n = n0 + t / a.nbands, oh0 = (t % a.nbands) * BH;
+        const int rows = min(BH, a.OH - oh0);
         const uint16_t *xp = reinterpret_cast<const uint16_t *>(a.x) + (static_cast<int64_t>(n) * a.C + c) * a.IH * a.IW;
         const uint16_t *dp = reinterpret_cast<const uint16_t *>(a.dy) + (static_cast<int64_t>(n) * a.C + c) * a.OH * a.OW;
-        for (int band = 0; band < a.nbands; ++band) {
+        const int xv = a.IW / 8, dv = a.OW / 8;
+#pragma unroll
+        for (int k = 0; k < NXV; ++k) {
+            const int v = tid + 256 * k;
+            const int r = v / xv;
+            const int ih = oh0 + r - a.P;
+            pfx[k] = make_uint4(0u, 0u, 0u, 0u);
+            if (v < (rows + K - 1) * xv && ih >= 0 && ih < a.IH)
+                pfx[k] = *reinterpret_cast<const uint4 *>(xp + static_cast<int64_t>(ih) * a.IW + (v - r * xv) * 8);
+        }
+#pragma unroll
+        for (int k = 0; k < NDV; ++k) {
+            const int v = tid + 256 * k;
+            const int r = v / dv;
+            pfd[k] = make_uint4(0u, 0u, 0u, 0u);
+            if (v < rows * dv)
+                pfd[k] = *reinterpret_cast<const uint4 *>(dp + static_cast<int64_t>(oh0 + r) * a.OW + (v - r * dv) * 8);
+        }
+    };
+    if (vec && nsteps > 0) prefetch(0);
+
+    for (int t = 0; t < nsteps; ++t) {
+        const int n = n0 + t / a.nbands, band = t % a.nbands;
+        const uint16_t *xp = reinterpret_cast<const uint16_t *>(a.x) + (static_cast<int64_t>(n) * a.C + c) * a.IH * a.IW;
+        const uint16_t *dp = reinterpret_cast<const uint16_t *>(a.dy) + (static_cast<int64_t>(n) * a.C + c) * a.OH * a.OW;
+        {
             const int oh0 = band * BH;
             const int rows = min(BH, a.OH - oh0);
             __syncthreads();  // the previous band's reads are done
             // input rows oh0 .. oh0 + rows + k - 2 of the padded plane (image row = that - P)
             const int xrows = rows + K - 1;
-            if (a.vx) {
-                const int vpr = a.IW / 8;
-                for (int v = tid; v < xrows * vpr; v += 256) {
-                    const int r = v / vpr;
-                    const int c8 = (v - r * vpr) * 8;
-                    const int ih = oh0 + r - a.P;
-                    uint4 raw = make_uint4(0u, 0u, 0u, 0u);
-                    if (ih >= 0 && ih < a.IH) raw = *reinterpret_cast<const uint4 *>(xp + static_cast<int64_t>(ih) * a.IW + c8);
-                    uint16_t *d = xt + r * G::XP + a.P + c8;
-                    const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+            if (vec) {
+                const int xv = a.IW / 8, dv = a.OW / 8;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) d[e] = static_cast<uint16_t>(wd[e >> 1] >> ((e & 1) * 16));
+                for (int k = 0; k < NXV; ++k) {
+                    const int v = tid + 256 * k;
+                    if (v < xrows * xv) {
+                        const int r = v / xv;
+                        uint16_t *d = xt + r * G::XP + a.P + (v - r * xv) * 8;
+                        const uint32_t wd[4] = {pfx[k].x, pfx[k].y, pfx[k].z, pfx[k].w};
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) d[e] = static_cast<uint16_t>(wd[e >> 1] >> ((e & 1) * 16));
+                    }
+                }
+#pragma unroll
+                for (int k = 0; k < NDV; ++k) {
+                    const int v = tid + 256 * k;
+                    if (v < rows * dv) {
+                        const int r = v / dv;
+                        const int c8 = (v - r * dv) * 8;
+                        *reinterpret_cast<uint4 *>(dz + r * G::QD + (kDzOff + c8) / 2) = pfd[k];
+                        const uint32_t wd[4] = {pfd[k].x, pfd[k].y, pfd[k].z, pfd[k].w};
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const uint16_t bits = static_cast<uint16_t>(wd[e >> 1] >> ((e & 1) * 16));
+                            T tv;
+                            __builtin_memcpy(&tv, &bits, 2);
+                            dsum += to_f32(tv);
+                        }
+                    }
                 }
             } else {
                 for (int e = tid; e < xrows * a.IW; e += 256) {
@@ -427,34 +478,16 @@ __global__ __launch_bounds__(256) void lk_mfma_bwdw_kernel(LkmwArgs<T> a) {
                     const int ih = oh0 + r - a.P;
                     xt[r * G::XP + a.P + col] = (ih >= 0 && ih < a.IH) ? xp[static_cast<int64_t>(ih) * a.IW + col] : 0;
                 }
-            }
-            // dy rows oh0 .. oh0 + rows - 1 into copy 0: dword d holds columns 2d - kDzOff, 2d + 1 - kDzOff
-            if (a.vd) {
-                const int vpr = a.OW / 8;
-                for (int v = tid; v < rows * vpr; v += 256) {
-                    const int r = v / vpr;
-                    const int c8 = (v - r * vpr) * 8;
-                    const uint4 raw = *reinterpret_cast<const uint4 *>(dp + static_cast<int64_t>(oh0 + r) * a.OW + c8);
-                    *reinterpret_cast<uint4 *>(dz + r * G::QD + (kDzOff + c8) / 2) = raw;
-                    const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const uint16_t bits = static_cast<uint16_t>(wd[e >> 1] >> ((e & 1) * 16));
-                        T t;
-                        __builtin_memcpy(&t, &bits, 2);
-                        dsum += to_f32(t);
-                    }
-                }
-            } else {
+                // dy rows oh0 .. oh0 + rows - 1 into copy 0: dword d holds columns 2d - kDzOff, 2d + 1 - kDzOff
                 uint16_t *dz16 = reinterpret_cast<uint16_t *>(dz);
                 for (int e = tid; e < rows * a.OW; e += 256) {
                     const int r = e / a.OW;
                     const int col = e - r * a.OW;
                     const uint16_t bits = dp[static_cast<int64_t>(oh0 + r) * a.OW + col];
                     dz16[2 * r * G::QD + kDzOff + col] = bits;
-                    T t;
-                    __builtin_memcpy(&t, &bits, 2);
-                    dsum += to_f32(t);
+                    T tv;
+                    __builtin_memcpy(&tv, &bits, 2);
+                    dsum += to_f32(tv);
                 }
             }
             __syncthreads();
@@ -468,6 +501,7 @@ __global__ __launch_bounds__(256) void lk_mfma_bwdw_kernel(LkmwArgs<T> a) {
                 dz1[r * G::QD + d] = (lo >> 16) | (hi << 16);
             }
             __syncthreads();
+            if (vec && t + 1 < nsteps) prefetch(t + 1);
             // kernel rows i >= k (lanes m >= k) are not part of dw: they read row k - 1
             // instead, so every read stays inside the staged rows
             const int mi = min(m, K - 1);
