@@ -48,7 +48,9 @@ per_case     each call alone and cold (after a 512 MiB fill that evicts the last
              cache): HIP events around one eager call, median of --repeats, its
              rate and fraction of roofline, and the oracle's time for the same call
              (scaled from the CPU sample) over it.  Calls whose roofline time is
-             under 5 us are flagged as latency-bound (their figure is a latency).
+             under 5 us are flagged as latency-bound (their figure is a latency);
+             their kernel tags carry a ".lat" suffix, so per_kernel and the
+             dominant-tag roofline keep them apart from the batched launches.
 cpu_baseline the fp64 CPU oracle on a bounded sample of the same host tensors,
              on all host threads and on one thread (channel subset), with the
              host CPU model
@@ -169,23 +171,29 @@ def static_calls(dc, case, dev, seed, passes=("fwd", "bwd_in", "bwd_w")):
     calls = []
     dts = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}[dtype]
 
-    def tag(pi, name):
+    def tag(pi, name, nbytes=None):
         # one tag = one kernel instantiation: the library's algorithm for this geometry,
-        # plus the template parameters it is specialised on
+        # plus the template parameters it is specialised on; calls whose HBM time at
+        # the peak is under LATENCY_US get their own ".lat" tag (a latency, not a rate)
         algo = dc.dwconv2d_algo(pi, x.shape, w.shape, s, p, d, dtype)
-        return "%s.%s.k%d_s%d_m%d_%s" % (name, algo, k, s, M, dts)
+        t = "%s.%s.k%d_s%d_m%d_%s" % (name, algo, k, s, M, dts)
+        if nbytes is not None and nbytes / (HBM_PEAK_GBS * 1e9) * 1e6 < LATENCY_US and 2 * macs < 1e9:
+            t += ".lat"
+        return t
 
     if "fwd" in passes:
-        calls.append(Call(tag(0, "fwd"), lambda: dc.dwconv2d_fwd(x, w, b, s, p, d, out=y), sx + W + B + Y, 2 * macs,
+        calls.append(Call(tag(0, "fwd", sx + W + B + Y), lambda: dc.dwconv2d_fwd(x, w, b, s, p, d, out=y),
+                          sx + W + B + Y, 2 * macs,
                           label, "fwd", lambda: dc.dwconv2d_tune_fwd(x, w, b, s, p, d, out=y, reps=5),
                           rbytes=sx + W + B))
     if "bwd_in" in passes:
-        calls.append(Call(tag(1, "bwd_input"), lambda: dc.dwconv2d_bwd_input(dy, w, x.shape, s, p, d, out=dx),
+        calls.append(Call(tag(1, "bwd_input", Y + W + X),
+                          lambda: dc.dwconv2d_bwd_input(dy, w, x.shape, s, p, d, out=dx),
                           Y + W + X, 2 * macs, label, "bwd_input",
                           lambda: dc.dwconv2d_tune_bwd_input(dy, w, x.shape, s, p, d, out=dx, reps=5),
                           rbytes=Y + W))
     if "bwd_w" in passes:
-        calls.append(Call(tag(2, "bwd_weight"),
+        calls.append(Call(tag(2, "bwd_weight", sx + Y + W + B),
                           lambda: dc.dwconv2d_bwd_weight(x, dy, w.shape, s, p, d, with_bias=with_bias, out=gw,
                                                          out_bias=gb, workspace=ws),
                           sx + Y + W + B, 2 * macs, label, "bwd_weight",
