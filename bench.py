@@ -390,7 +390,7 @@ def ceiling_of(tag, kind, rfrac, ceil):
         return v, "GB/s", "stream (read share %.2f)" % rfrac
     if ".largek_mfma." in tag and not tag.endswith("_f32"):
         return ceil["mfma_f16_tflops"], "TFLOP/s", "fp16 matrix instructions"
-    if ".largek_mfma_f32." in tag:
+    if ".largek_mfma_f32." in tag or ".largek_mfma_t16." in tag:
         return ceil["mfma_f32_tflops"], "TFLOP/s", "fp32 matrix instructions"
     return ceil["valu_fma_f32_tflops"], "TFLOP/s", "fp32 vector FMA"
 

@@ -426,12 +426,12 @@ int run_small(const Geo &g, const BwPlan &p, const void *x, const void *dy, void
 
 enum BwAlgo {
     kBwChannelGroup = 0, kBwLargek, kBwRowwalk, kBwDecim, kBwBandPixel, kBwBandTaps, kBwLargekMfma, kBwLargekMfma32,
-    kBwDirect, kBwCount
+    kBwDirect, kBwLargekMfma16, kBwCount
 };
 
 const char *const kBwNames[kBwCount] = {"channelgroup_small", "largek_regtile", "rowwalk_3x3", "decimated_s2d2",
                                         "band_pixel",         "band_taps",      "largek_mfma",  "largek_mfma_f32",
-                                        "direct"};
+                                        "direct",             "largek_mfma_t16"};
 
 bool band_bw_plans(const Geo &g, int dt) {
     BwPlan p;
@@ -451,6 +451,7 @@ bool feasible_bw(int algo, const Geo &g, int dt) {
         case kBwBandPixel: return small_variant(g) && band_bw_plans(g, dt);
         case kBwBandTaps: return !small_variant(g) && band_bw_plans(g, dt);
         case kBwDirect: return true;
+        case kBwLargekMfma16: return largek_wgrad16_fits(g, dt);
         default: return false;
     }
 }
@@ -461,7 +462,8 @@ int select_bwd_weight(const Geo &g, int dt) {
     const int tuned = tuned_algo(2, g, dt);
     if (tuned >= 0 && feasible_bw(tuned, g, dt)) return tuned;
     if (small_fits(g, dt, 2)) return kBwChannelGroup;
-    if (largek_mfma_bwdw_fits(g, dt)) return kBwLargekMfma;
+    if (largek_mfma_bwdw_fits(g, dt)) return kBwLargekMfma;  // 16-bit: measured faster than 16 x 16 fp32 tiles
+    if (largek_wgrad16_fits(g, dt)) return kBwLargekMfma16;
     if (largek_wgrad32_fits(g, dt)) return kBwLargekMfma32;
     if (largek_bwdw_fits(g)) return kBwLargek;
     if (rowwalk_fits(g, dt, 2)) return kBwRowwalk;
@@ -478,6 +480,7 @@ int64_t ws_for(int algo, const Geo &g, int dtype) {
         case kBwLargek: return std::max<int64_t>(g.ic * largek_bwd_weight_chunks(g) * slots * 4, 16);
         case kBwLargekMfma: return std::max<int64_t>(g.ic * largek_mfma_bwd_weight_chunks(g) * slots * 4, 16);
         case kBwLargekMfma32: return std::max<int64_t>(g.ic * largek_wgrad32_chunks(g) * slots * 4, 16);
+        case kBwLargekMfma16: return std::max<int64_t>(g.ic * largek_wgrad16_chunks(g) * slots * 4, 16);
         case kBwDirect: return std::max<int64_t>(static_cast<int64_t>(g.ic) * direct_bwd_weight_chunks(g) * slots * 4, 16);
         case kBwRowwalk: return std::max<int64_t>(g.ic * rowwalk_bwd_weight_chunks(g, dtype) * slots * 4, 16);
         case kBwDecim: return std::max<int64_t>(g.ic * decim_bwd_weight_chunks(g) * slots * 4, 16);
@@ -508,6 +511,11 @@ int dispatch_bwd_weight(const Geo &g, const void *x, const void *dy, void *dwt, 
         rc = direct_bwd_weight(g, x, dy, ws, dt, s);
         if (rc != kOk) return rc;
         return launch_reduce<T>(g, ws, dwt, db, direct_bwd_weight_chunks(g), g.mult * (kk + 1), s);
+    }
+    if (algo == kBwLargekMfma16) {
+        rc = largek_wgrad16(g, x, dy, ws, dt, s);
+        if (rc != kOk) return rc;
+        return launch_reduce<T>(g, ws, dwt, db, largek_wgrad16_chunks(g), kk + 1, s);
     }
     if (algo == kBwLargekMfma32) {
         rc = largek_wgrad32(g, x, dy, ws, s);

@@ -100,6 +100,11 @@ int largek_bwd_input32(const Geo &g, const void *dy, const void *w, void *dx, hi
 bool largek_wgrad32_fits(const Geo &g, int dtype);
 int largek_wgrad32_chunks(const Geo &g);
 int largek_wgrad32(const Geo &g, const void *x, const void *dy, void *ws, hipStream_t s);
+// Grad-weight of 13 x 13 filters on the matrix cores with 16 x 16 tiles, any
+// dtype (dw_largek_wgrad16.hip): workspace [ic][chunks][k*k + 1].
+bool largek_wgrad16_fits(const Geo &g, int dtype);
+int largek_wgrad16_chunks(const Geo &g);
+int largek_wgrad16(const Geo &g, const void *x, const void *dy, void *ws, int dtype, hipStream_t s);
 
 // Stride 2, dilation 2, pad k-1 (k = 3, 5) as stride-1 passes on the even grid (dw_decim.hip).
 bool decim_fits(const Geo &g, int pass);

@@ -856,3 +856,25 @@ def test_dynamic_wide_rows(shape, k, dils, dtype):
     x, fs, dy = dyn_bwd_inputs(*shape, k, dils, DT[dtype], 1700 + sum(shape) + k, fdist=("N", 0.0, 1.0 / (k * k)))
     check_dyn(x, fs, dils, "dynamic-wide %s k%d %s" % (shape, k, dtype))
     check_dyn_bwd(x, fs, dy, dils, "dynamic-wide-bwd %s k%d %s" % (shape, k, dtype))
+
+
+# ------------------------------------------------------------------ 13 x 13 grad-weight on 16 x 16 matrix tiles
+@pytest.mark.parametrize("n,c,h,w,p,dt", [
+    (3, 2, 64, 64, 6, "f32"),     # two bands of 32 dy rows, register prefetch
+    (2, 3, 48, 48, 6, "f32"),     # a full and a partial band
+    (4, 2, 32, 32, 6, "f16"),
+    (2, 2, 40, 72, 6, "bf16"),    # rows of 72: staged without prefetch
+    (2, 2, 33, 30, 0, "f32"),     # no padding, ragged width: element staging
+    (2, 2, 20, 22, 12, "f32"),    # pad k - 1
+    (2, 2, 9, 9, 6, "f32"),       # filter wider than the image
+    (1, 2, 70, 64, 3, "f32"),     # 70 dy rows: three bands
+])
+def test_grad_weight_13_matrix_tiles(n, c, h, w, p, dt):
+    geo = ((n, c, h, w), (c, 13, 13), 1, p, 1)
+    assert "largek_mfma_t16" in dc.dwconv2d_algo_candidates(2, *geo, dtype=DT[dt])
+    x, wt, b, dy = static_case(n, c, h, w, 1, 13, 1, p, 1, DT[dt], 1750 + h + w + p)
+    try:
+        dc.dwconv2d_set_algo(2, *geo, dtype=DT[dt], algo="largek_mfma_t16")
+        check_static(x, wt, b, dy, 1, p, 1, "wgrad16 n%d c%d %dx%d p%d %s" % (n, c, h, w, p, dt), passes=("bwd_w",))
+    finally:
+        dc.dwconv2d_set_algo(2, *geo, dtype=DT[dt], algo=None)
