@@ -199,6 +199,130 @@ __global__ __launch_bounds__(kThreads) void dec_fwd_kernel(DcArgs<T> a) {
     }
 }
 
+// ---------------------------------------------------------------- forward, 16-bit pairs
+// The forward with 16-bit whole-vector rows: two taps per instruction.  The
+// decimated values of a lane's raw x segment are the low halves of its four
+// words, so the window is kept as words W[k] (low half = decimated column
+// c0 - HH + k) and as pairs P[k] = (W[k].lo, W[k+1].lo) built with one byte
+// permute each; each output q then sums, per kernel row i and multiplier m,
+// the dot products of P[q + 2p] with the tap pairs (w[i][2p], w[i][2p+1])
+// (the last pair of an odd k is (w[i][k-1], 0)).  v_dot2c_f32_{bf16,f16}
+// multiplies the 16-bit values exactly and adds in fp32.
+template <typename T> struct Dot2;
+template <> struct Dot2<bf16_t> {
+    static __device__ __forceinline__ float run(uint32_t a, uint32_t b, float c) {
+        typedef __bf16 v2 __attribute__((ext_vector_type(2)));
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2, a), __builtin_bit_cast(v2, b), c, false);
+    }
+};
+template <> struct Dot2<__half> {
+    static __device__ __forceinline__ float run(uint32_t a, uint32_t b, float c) {
+        typedef _Float16 v2 __attribute__((ext_vector_type(2)));
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(v2, a), __builtin_bit_cast(v2, b), c, false);
+    }
+};
+
+// Pairs of a window row from a raw x segment (zeros outside the plane / image).
+template <typename T, int HH>
+__device__ __forceinline__ void xrow_pairs(const uint32_t (&w)[kXWords<T>], bool ok, int lane, bool hl, bool hr,
+                                           uint32_t (&P)[RO + 2 * HH]) {
+    static_assert(kXWords<T> == RO, "16-bit segment: one word per decimated column");
+    constexpr int WW = RO + 2 * HH;
+    uint32_t W[WW];
+    uint32_t v[RO];
+#pragma unroll
+    for (int e = 0; e < RO; ++e) v[e] = ok ? w[e] : 0u;
+#pragma unroll
+    for (int e = 0; e < HH; ++e) {
+        const uint32_t l = static_cast<uint32_t>(__shfl(static_cast<int>(v[RO - HH + e]), lane - 1, 64));
+        W[e] = hl ? l : 0u;
+        const uint32_t r = static_cast<uint32_t>(__shfl(static_cast<int>(v[e]), lane + 1, 64));
+        W[HH + RO + e] = hr ? r : 0u;
+    }
+#pragma unroll
+    for (int e = 0; e < RO; ++e) W[HH + e] = v[e];
+#pragma unroll
+    for (int k = 0; k + 1 < WW; ++k) P[k] = __builtin_amdgcn_perm(W[k + 1], W[k], 0x05040100u);
+    P[WW - 1] = W[WW - 1] & 0xffffu;
+}
+
+template <typename T, int K, int MM>
+__global__ __launch_bounds__(kThreads) void dec_fwd_dot2_kernel(DcArgs<T> a) {
+    constexpr int HH = (K - 1) / 2, WW = RO + 2 * HH, NX = kXWords<T>, ND = kDWords<T>, KP = (K + 1) / 2;
+    const Geo &g = a.g;
+    const WaveUnit u = wave_unit(a.wpc, a.NS, a.SPW, a.nunits, a.nbands, g.ic);
+    // tap pairs (w[i][2p], w[i][2p+1]) as 16-bit pairs, wave-uniform
+    uint32_t wp[MM][K][KP];
+    float bias[MM];
+    const uint16_t *wr = reinterpret_cast<const uint16_t *>(a.w);
+#pragma unroll
+    for (int m = 0; m < MM; ++m) {
+#pragma unroll
+        for (int i = 0; i < K; ++i)
+#pragma unroll
+            for (int p = 0; p < KP; ++p) {
+                const int t = (u.ic * MM + m) * K * K + i * K + 2 * p;
+                const uint32_t lo = wr[t], hi = 2 * p + 1 < K ? wr[t + 1] : 0u;
+                wp[m][i][p] = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(lo | (hi << 16))));
+            }
+        bias[m] = a.b ? uniform(to_f32(a.b[u.ic * MM + m])) : 0.f;
+    }
+    const int P = u.n * g.ic + u.ic;  // input plane (n, ic)
+    const T *xp = a.in + static_cast<int64_t>(P) * g.ih * g.iw;
+    const int c0 = u.s * RO;
+    const bool hl = u.s > 0, hr = u.s < a.NS - 1;
+    const int oh0 = u.band * a.BH, oh_end = min(oh0 + a.BH, g.oh);
+    // relative row j (absolute decimated row oh0 - HH + j) lives in window slot j % K
+    uint32_t win[K][WW];
+    uint32_t rq[K][NX];
+    bool rk[K];
+#pragma unroll
+    for (int j = 0; j < K - 1; ++j) {
+        uint32_t w[NX];
+        bool ok;
+        load_xrow<T, true>(xp, oh0 - HH + j, a.XH, g.iw, c0, u.act, w, ok);
+        xrow_pairs<T, HH>(w, ok, u.lane, hl, hr, win[j]);
+    }
+#pragma unroll
+    for (int f = 0; f < K; ++f) load_xrow<T, true>(xp, oh0 - HH + K - 1 + f, a.XH, g.iw, c0, u.act, rq[f], rk[f]);
+    for (int t0 = 0; t0 < a.BH; t0 += K) {  // BH is a multiple of K
+        uint32_t ybuf[K][MM][ND];
+#pragma unroll
+        for (int uu = 0; uu < K; ++uu) {
+            const int t = t0 + uu;
+            {
+                uint32_t cw[NX];
+                take_words<T>(rq[uu], cw);
+                xrow_pairs<T, HH>(cw, rk[uu], u.lane, hl, hr, win[(uu + K - 1) % K]);
+            }
+            load_xrow<T, true>(xp, oh0 - HH + t + 2 * K - 1, a.XH, g.iw, c0, u.act, rq[uu], rk[uu]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int m = 0; m < MM; ++m) {
+                float acc[RO];
+#pragma unroll
+                for (int q = 0; q < RO; ++q) acc[q] = bias[m];
+#pragma unroll
+                for (int i = 0; i < K; ++i)
+#pragma unroll
+                    for (int p = 0; p < KP; ++p)
+#pragma unroll
+                        for (int q = 0; q < RO; ++q)
+                            acc[q] = Dot2<T>::run(win[(uu + i) % K][q + 2 * p], wp[m][i][p], acc[q]);
+                pack_words<T, ND>(acc, ybuf[uu][m]);
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < MM; ++m)
+#pragma unroll
+            for (int uu = 0; uu < K; ++uu) {
+                const int oh = oh0 + t0 + uu;
+                if (u.act && oh < oh_end)
+                    store_words<ND>(a.out + ((static_cast<int64_t>(P) * MM + m) * g.oh + oh) * g.ow + c0, ybuf[uu][m]);
+            }
+    }
+}
+
 // ---------------------------------------------------------------- grad-input
 template <typename T, int K, int MM, bool FULL>
 __global__ __launch_bounds__(kThreads) void dec_bwdin_kernel(DcArgs<T> a) {
@@ -475,8 +599,12 @@ bool aligned16(const void *p) { return p == nullptr || reinterpret_cast<uintptr_
 
 template <typename T, int K, int MM, bool FULL>
 void launch_dec(int pass, int grid, const DcArgs<T> &a, hipStream_t s) {
-    if (pass == 0)
-        hipLaunchKernelGGL((dec_fwd_kernel<T, K, MM, FULL>), dim3(grid), dim3(kThreads), 0, s, a);
+    if (pass == 0) {
+        if constexpr (sizeof(T) == 2 && FULL)
+            hipLaunchKernelGGL((dec_fwd_dot2_kernel<T, K, MM>), dim3(grid), dim3(kThreads), 0, s, a);
+        else
+            hipLaunchKernelGGL((dec_fwd_kernel<T, K, MM, FULL>), dim3(grid), dim3(kThreads), 0, s, a);
+    }
     else if (pass == 1)
         hipLaunchKernelGGL((dec_bwdin_kernel<T, K, MM, FULL>), dim3(grid), dim3(kThreads), 0, s, a);
     else
