@@ -207,21 +207,7 @@ __global__ __launch_bounds__(kThreads) void dec_fwd_kernel(DcArgs<T> a) {
 // permute each; each output q then sums, per kernel row i and multiplier m,
 // the dot products of P[q + 2p] with the tap pairs (w[i][2p], w[i][2p+1])
 // (the last pair of an odd k is (w[i][k-1], 0)).  v_dot2c_f32_{bf16,f16}
-// multiplies the 16-bit values exactly and adds in fp32.
-template <typename T> struct Dot2;
-template <> struct Dot2<bf16_t> {
-    static __device__ __forceinline__ float run(uint32_t a, uint32_t b, float c) {
-        typedef __bf16 v2 __attribute__((ext_vector_type(2)));
-        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2, a), __builtin_bit_cast(v2, b), c, false);
-    }
-};
-template <> struct Dot2<__half> {
-    static __device__ __forceinline__ float run(uint32_t a, uint32_t b, float c) {
-        typedef _Float16 v2 __attribute__((ext_vector_type(2)));
-        return __builtin_amdgcn_fdot2(__builtin_bit_cast(v2, a), __builtin_bit_cast(v2, b), c, false);
-    }
-};
-
+// multiplies the 16-bit values exactly and adds in fp32 (Dot2).
 // Pairs of a window row from a raw x segment (zeros outside the plane / image).
 template <typename T, int HH>
 __device__ __forceinline__ void xrow_pairs(const uint32_t (&w)[kXWords<T>], bool ok, int lane, bool hl, bool hr,

@@ -105,6 +105,11 @@ int largek_wgrad32(const Geo &g, const void *x, const void *dy, void *ws, hipStr
 bool largek_wgrad16_fits(const Geo &g, int dtype);
 int largek_wgrad16_chunks(const Geo &g);
 int largek_wgrad16(const Geo &g, const void *x, const void *dy, void *ws, int dtype, hipStream_t s);
+// Grad-weight of 7 x 7 filters as a register row stream, any dtype
+// (dw_largek_wgrad7.hip): workspace [ic][chunks][k*k + 1].
+bool stream7_bwdw_fits(const Geo &g);
+int stream7_bwdw_chunks(const Geo &g);
+int stream7_bwdw(const Geo &g, const void *x, const void *dy, void *ws, int dtype, hipStream_t s);
 
 // Stride 2, dilation 2, pad k-1 (k = 3, 5) as stride-1 passes on the even grid (dw_decim.hip).
 bool decim_fits(const Geo &g, int pass);

@@ -119,6 +119,22 @@ __device__ __forceinline__ void store_words_tail(T *p, int avail, const uint32_t
             if (k * PW + e < avail) p[k * PW + e] = from_bits<T>(PW == 1 ? w[k] : (w[k] >> (16 * e)) & 0xffffu);
 }
 
+// acc + a.lo * b.lo + a.hi * b.hi for two packed 16-bit pairs
+// (v_dot2c_f32_{f16,bf16}: the products are exact, the sums fp32).
+template <typename T> struct Dot2;
+template <> struct Dot2<bf16_t> {
+    static __device__ __forceinline__ float run(uint32_t a, uint32_t b, float c) {
+        typedef __bf16 v2 __attribute__((ext_vector_type(2)));
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2, a), __builtin_bit_cast(v2, b), c, false);
+    }
+};
+template <> struct Dot2<__half> {
+    static __device__ __forceinline__ float run(uint32_t a, uint32_t b, float c) {
+        typedef _Float16 v2 __attribute__((ext_vector_type(2)));
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(v2, a), __builtin_bit_cast(v2, b), c, false);
+    }
+};
+
 // Wave-uniform value kept in a scalar register (the filter taps of a channel).
 __device__ __forceinline__ float uniform(float v) {
     return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));

@@ -878,3 +878,26 @@ def test_grad_weight_13_matrix_tiles(n, c, h, w, p, dt):
         check_static(x, wt, b, dy, 1, p, 1, "wgrad16 n%d c%d %dx%d p%d %s" % (n, c, h, w, p, dt), passes=("bwd_w",))
     finally:
         dc.dwconv2d_set_algo(2, *geo, dtype=DT[dt], algo=None)
+
+
+# ------------------------------------------------------------------ 7 x 7 grad-weight as a register row stream
+@pytest.mark.parametrize("n,c,h,w,dt", [
+    (2, 3, 64, 64, "f32"),     # 16 lanes a row, 4 planes a wave, 16-byte rows
+    (2, 3, 48, 48, "f16"),     # plane rows of 12 lanes across the wave's 16-lane rows
+    (4, 2, 17, 100, "bf16"),   # 25 lanes a row, 2 planes a wave
+    (3, 2, 30, 45, "f16"),     # ragged rows: element loads
+    (2, 2, 20, 22, "bf16"),
+    (2, 2, 33, 32, "f32"),     # a ragged band
+    (2, 2, 5, 5, "f32"),       # filter wider than the image
+    (1, 2, 100, 256, "f32"),   # rows of 256: one plane a wave, several bands
+    (32, 520, 2, 132, "f32"),  # two rounds of units a chunk, bands of 2 rows
+])
+def test_grad_weight_7_row_stream(n, c, h, w, dt):
+    geo = ((n, c, h, w), (c, 7, 7), 1, 3, 1)
+    assert "stream_7x7" in dc.dwconv2d_algo_candidates(2, *geo, dtype=DT[dt])
+    x, wt, b, dy = static_case(n, c, h, w, 1, 7, 1, 3, 1, DT[dt], 1800 + h + w)
+    try:
+        dc.dwconv2d_set_algo(2, *geo, dtype=DT[dt], algo="stream_7x7")
+        check_static(x, wt, b, dy, 1, 3, 1, "stream7 n%d c%d %dx%d %s" % (n, c, h, w, dt), passes=("bwd_w",))
+    finally:
+        dc.dwconv2d_set_algo(2, *geo, dtype=DT[dt], algo=None)
