@@ -73,8 +73,11 @@ template <typename T> struct LkmArgs {
     int C;         // output channels of this pass (planes per image)
     int Cin;       // input channels of this pass
     int mult;      // output channels per input channel
-    int ngroups;   // image groups (one image per wave of a workgroup)
+    int ngroups;   // workgroups per channel, each walking gpc image groups
+    int gpc;       // image groups (one image per wave of a workgroup) per workgroup
+    int ngtot;     // image groups per channel
     int vin;       // input rows are whole 16-byte vectors (and aligned)
+    int pre;       // vin, and a group's planes fit the prefetch registers (2 NT vectors a thread)
     int vout;      // output rows are whole 4-element runs (and 8-byte aligned)
 };
 
@@ -101,12 +104,11 @@ __global__ __launch_bounds__(256) void lk_mfma_kernel(LkmArgs<T> a) {
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
-    const int img = wave / MT;     // image of the workgroup this wave serves
+    const int img = wave / MT;     // image of the workgroup's group this wave serves
     const int mt = wave - img * MT;  // its 32-row output tile
     const int c = blockIdx.x / a.ngroups;  // output plane channel of this pass
-    const int n0 = (blockIdx.x - c * a.ngroups) * G::IPG;
-    const int n = n0 + img;
-    const bool active = n < a.N;
+    const int g0 = (blockIdx.x - c * a.ngroups) * a.gpc;
+    const int g1 = min(g0 + a.gpc, a.ngtot);
 
     // 1. filter table: copy q (0, 1) of row i holds, in dword d, the 16-bit
     //    values of padded positions 2d + q and 2d + q + 1, where padded
@@ -129,101 +131,144 @@ __global__ __launch_bounds__(256) void lk_mfma_kernel(LkmArgs<T> a) {
         wtab[e] = v;
     }
 
-    // 2. the workgroup's padded input planes: tile[r][col] = in[r - P][col - P],
-    //    0 outside; the MT waves of an image stage its plane together
+    // 2. per image group, the padded input planes: tile[r][col] = in[r - P][col - P],
+    //    0 outside (the zeros are written once: every group writes the same
+    //    interior positions); the MT waves of an image stage its plane together.
+    //    With whole 16-byte rows that fit the registers (planes no larger than
+    //    the output tiles) the next group's planes are loaded into registers
+    //    while the matrix cores work on this one.
     {
         uint4 *z = reinterpret_cast<uint4 *>(tiles);
         for (int e = tid; e < G::IPG * G::tile_halves / 8; e += 256) z[e] = make_uint4(0u, 0u, 0u, 0u);
     }
-    __syncthreads();
-    {
-        const int cin = FLIP ? c : c / a.mult;
+    __syncthreads();  // zeros before any plane data
+    const int cin = FLIP ? c : c / a.mult;
+    const int64_t plane = static_cast<int64_t>(a.IH) * a.IW;
+    const int64_t istride = static_cast<int64_t>(a.Cin) * plane;  // one image
+    const uint16_t *ib = reinterpret_cast<const uint16_t *>(a.in) + cin * plane;
+    // vector v = tid + 256 k of a group: image v / nvec, row, 8-column run; its
+    // offset from the group's first plane and its place in the tiles
+    constexpr int NV = 2 * NT;  // IPG * 32 MT * 32 NT halves / 8 per vector / 256 threads
+    const int vpr = a.IW / 8, nvec = a.IH * vpr;
+    int64_t goff[NV];
+    int loff[NV], vidx[NV];
+    if (a.pre) {
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            const int v = tid + 256 * k;
+            const int im = v / nvec;
+            const int vv = v - im * nvec;
+            const int r = vv / vpr;
+            const int c8 = (vv - r * vpr) * 8;
+            vidx[k] = v;
+            goff[k] = im * istride + static_cast<int64_t>(r) * a.IW + c8;
+            loff[k] = im * G::tile_halves + (r + a.P) * G::XP + c8 + a.P;
+        }
+    }
+    uint4 raw[NV];
+    auto load_group = [&](int gi) {
+        const int nv = min(G::IPG, a.N - gi * G::IPG) * nvec;
+        const uint16_t *src = ib + static_cast<int64_t>(gi) * G::IPG * istride;
+#pragma unroll
+        for (int k = 0; k < NV; ++k)
+            if (vidx[k] < nv) raw[k] = *reinterpret_cast<const uint4 *>(src + goff[k]);
+    };
+    if (a.pre && g0 < g1) load_group(g0);
+
+    const int m = lane & 31;
+    const int h = lane >> 5;
+    const float bias = (!FLIP && a.b) ? to_f32(a.b[c]) : 0.f;
+    const uint16_t *xt = tiles + img * G::tile_halves;
+    for (int gi = g0; gi < g1; ++gi) {
+        const int n0 = gi * G::IPG;
         const int nimg = min(G::IPG, a.N - n0);
-        if (a.vin) {
-            const int vpr = a.IW / 8;
-            const int nvec = a.IH * vpr;
+        if (a.pre) {
+            const int nv = nimg * nvec;
+#pragma unroll
+            for (int k = 0; k < NV; ++k)
+                if (vidx[k] < nv) {
+                    uint16_t *d = tiles + loff[k];
+                    const uint32_t wd[4] = {raw[k].x, raw[k].y, raw[k].z, raw[k].w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) d[e] = static_cast<uint16_t>(wd[e >> 1] >> ((e & 1) * 16));
+                }
+        } else if (a.vin) {
+            const uint16_t *src = ib + static_cast<int64_t>(n0) * istride;
             for (int v = tid; v < nimg * nvec; v += 256) {
                 const int im = v / nvec;
                 const int vv = v - im * nvec;
                 const int r = vv / vpr;
                 const int c8 = (vv - r * vpr) * 8;
-                const uint16_t *src = reinterpret_cast<const uint16_t *>(a.in) +
-                                      (static_cast<int64_t>(n0 + im) * a.Cin + cin) * a.IH * a.IW;
-                const uint4 raw = *reinterpret_cast<const uint4 *>(src + static_cast<int64_t>(r) * a.IW + c8);
+                const uint4 rv = *reinterpret_cast<const uint4 *>(src + im * istride + static_cast<int64_t>(r) * a.IW + c8);
                 uint16_t *d = tiles + im * G::tile_halves + (r + a.P) * G::XP + c8 + a.P;
-                const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+                const uint32_t wd[4] = {rv.x, rv.y, rv.z, rv.w};
 #pragma unroll
                 for (int e = 0; e < 8; ++e) d[e] = static_cast<uint16_t>(wd[e >> 1] >> ((e & 1) * 16));
             }
         } else {
+            const uint16_t *src = ib + static_cast<int64_t>(n0) * istride;
             for (int e = tid; e < nimg * a.IH * a.IW; e += 256) {
                 const int im = e / (a.IH * a.IW);
                 const int ee = e - im * a.IH * a.IW;
                 const int r = ee / a.IW;
                 const int col = ee - r * a.IW;
-                const uint16_t *src = reinterpret_cast<const uint16_t *>(a.in) +
-                                      (static_cast<int64_t>(n0 + im) * a.Cin + cin) * a.IH * a.IW;
-                tiles[im * G::tile_halves + (r + a.P) * G::XP + col + a.P] = src[ee];
+                tiles[im * G::tile_halves + (r + a.P) * G::XP + col + a.P] = src[im * istride + ee];
             }
         }
-    }
-    __syncthreads();
-    if (!active) return;
-    const uint16_t *xt = tiles + img * G::tile_halves;
-
-    // 3. k kernel rows x KPS window steps x (MT x NT) tiles of MFMAs
-    const int m = lane & 31;
-    const int h = lane >> 5;
-    f32x16_v acc[NT];
+        __syncthreads();
+        if (a.pre && gi + 1 < g1) load_group(gi + 1);
+        const int n = n0 + img;
+        if (n < a.N) {
+            // 3. k kernel rows x KPS window steps x (MT x NT) tiles of MFMAs
+            f32x16_v acc[NT];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+            for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[nt][r] = 0.f;
-
+                for (int r = 0; r < 16; ++r) acc[nt][r] = 0.f;
 #pragma unroll 1
-    for (int i = 0; i < K; ++i) {
-        u32x4_v af[KPS];
+            for (int i = 0; i < K; ++i) {
+                u32x4_v af[KPS];
 #pragma unroll
-        for (int s = 0; s < KPS; ++s) {
-            const int t = 16 * s + 8 * h - m + kZoff;  // first padded position of this lane's run
-            const int q = t & 1;
-            const uint32_t *p = wtab + (q * K + i) * G::QD + ((t - q) >> 1);
-            af[s] = u32x4_v{p[0], p[1], p[2], p[3]};
-        }
+                for (int s = 0; s < KPS; ++s) {
+                    const int t = 16 * s + 8 * h - m + kZoff;  // first padded position of this lane's run
+                    const int q = t & 1;
+                    const uint32_t *p = wtab + (q * K + i) * G::QD + ((t - q) >> 1);
+                    af[s] = u32x4_v{p[0], p[1], p[2], p[3]};
+                }
 #pragma unroll
-        for (int sp = 0; sp < KPS + 2 * (NT - 1); ++sp) {
-            const u32x4_v bf = *reinterpret_cast<const u32x4_v *>(xt + (32 * mt + m + i) * G::XP + 16 * sp + 8 * h);
+                for (int sp = 0; sp < KPS + 2 * (NT - 1); ++sp) {
+                    const u32x4_v bf =
+                        *reinterpret_cast<const u32x4_v *>(xt + (32 * mt + m + i) * G::XP + 16 * sp + 8 * h);
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                const int s = sp - 2 * nt;
-                if (s >= 0 && s < KPS) acc[nt] = Mfma<T>::run(af[s], bf, acc[nt]);
-            }
-        }
-    }
-
-    // 4. store: lane holds, per tile and r4, outputs (32 mt + m, 32 nt + 8 r4 + 4 h + 0..3)
-    const float bias = (!FLIP && a.b) ? to_f32(a.b[c]) : 0.f;
-    T *op = a.out + (static_cast<int64_t>(n) * a.C + c) * a.OH * a.OW;
-    {
-        const int oh = 32 * mt + m;
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const int ow = 32 * nt + 8 * r4 + 4 * h;
-                const float v0 = acc[nt][4 * r4] + bias, v1 = acc[nt][4 * r4 + 1] + bias;
-                const float v2 = acc[nt][4 * r4 + 2] + bias, v3 = acc[nt][4 * r4 + 3] + bias;
-                T *dst = op + oh * a.OW + ow;
-                if (oh >= a.OH) continue;
-                if (a.vout && ow + 4 <= a.OW) {
-                    *reinterpret_cast<uint2 *>(dst) = make_uint2(pack2<T>(v0, v1), pack2<T>(v2, v3));
-                } else {
-                    const float vv[4] = {v0, v1, v2, v3};
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        if (ow + q < a.OW) dst[q] = from_f32<T>(vv[q]);
+                    for (int nt = 0; nt < NT; ++nt) {
+                        const int s = sp - 2 * nt;
+                        if (s >= 0 && s < KPS) acc[nt] = Mfma<T>::run(af[s], bf, acc[nt]);
+                    }
                 }
             }
+            // 4. store: lane holds, per tile and r4, outputs (32 mt + m, 32 nt + 8 r4 + 4 h + 0..3)
+            T *op = a.out + (static_cast<int64_t>(n) * a.C + c) * a.OH * a.OW;
+            const int oh = 32 * mt + m;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const int ow = 32 * nt + 8 * r4 + 4 * h;
+                    const float v0 = acc[nt][4 * r4] + bias, v1 = acc[nt][4 * r4 + 1] + bias;
+                    const float v2 = acc[nt][4 * r4 + 2] + bias, v3 = acc[nt][4 * r4 + 3] + bias;
+                    T *dst = op + oh * a.OW + ow;
+                    if (oh >= a.OH) continue;
+                    if (a.vout && ow + 4 <= a.OW) {
+                        *reinterpret_cast<uint2 *>(dst) = make_uint2(pack2<T>(v0, v1), pack2<T>(v2, v3));
+                    } else {
+                        const float vv[4] = {v0, v1, v2, v3};
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            if (ow + q < a.OW) dst[q] = from_f32<T>(vv[q]);
+                    }
+                }
+        }
+        __syncthreads();  // the tiles are read before the next group overwrites them
     }
 }
 
@@ -235,7 +280,15 @@ int run_lkm_t(const LkmArgs<T> &a, hipStream_t s) {
     constexpr int KPS = kps_of(K);
     using G = LkmGeo<K, KPS, MT, NT>;
     LkmArgs<T> b = a;
-    b.ngroups = (a.N + G::IPG - 1) / G::IPG;
+    // image groups per channel, walked by about 2048 workgroups in all where the
+    // matrix work per group is short (k = 7, 13: the next group's loads then
+    // overlap it); at k = 31 one group per workgroup measured faster
+    b.ngtot = (a.N + G::IPG - 1) / G::IPG;
+    const int64_t all = static_cast<int64_t>(a.C) * b.ngtot;
+    const int gpc = K > 13 ? 1 : static_cast<int>(std::max<int64_t>(1, all / 2048));
+    b.ngroups = (b.ngtot + gpc - 1) / gpc;
+    b.gpc = (b.ngtot + b.ngroups - 1) / b.ngroups;
+    b.pre = a.vin && G::IPG * a.IH * (a.IW / 8) <= 256 * 2 * NT;
     const dim3 grid(static_cast<unsigned>(a.C * b.ngroups));
     hipLaunchKernelGGL((lk_mfma_kernel<T, K, KPS, MT, NT, FLIP>), grid, dim3(256), G::lds_bytes, s, b);
     return hipGetLastError() == hipSuccess ? kOk : kErrHip;

@@ -665,6 +665,20 @@ def test_large_kernel_mfma(n, c, h, w, mult, k, p, dt, fwd_mfma, bin_mfma):
                  passes=("fwd", "bwd_in"))
 
 
+@pytest.mark.parametrize("n,c,h,w,k,p,dt", [
+    (7, 2048, 16, 16, 7, 3, "f16"),    # four images a group, two groups a workgroup, the last one partial
+    (7, 1200, 40, 40, 7, 3, "bf16"),   # 2 x 2 tiles, two images a group, two groups a workgroup
+])
+def test_large_kernel_mfma_group_chunks(n, c, h, w, k, p, dt):
+    """Workgroups that walk several image groups load the next group's planes during the matrix work."""
+    geo = ((n, c, h, w), (c, k, k), 1, p, 1)
+    assert dc.dwconv2d_algo(0, *geo, dtype=DT[dt]) == "largek_mfma"
+    assert dc.dwconv2d_algo(1, *geo, dtype=DT[dt]) == "largek_mfma"
+    x, wt, b, dy = static_case(n, c, h, w, 1, k, 1, p, 1, DT[dt], 690 + h + w + k)
+    check_static(x, wt, b, dy, 1, p, 1, "largek-mfma-chunks n%d c%d %dx%d k%d %s" % (n, c, h, w, k, dt),
+                 passes=("fwd", "bwd_in"))
+
+
 @pytest.mark.parametrize("n,c,h,w,k,p,dt,bw_mfma", [
     (5, 2, 64, 64, 31, 15, "f16", True),     # two 32-row bands, chunks of images
     (3, 3, 48, 48, 31, 15, "bf16", True),    # a full band and a partial band
