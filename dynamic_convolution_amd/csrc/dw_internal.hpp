@@ -87,6 +87,10 @@ int largek_mfma_bwd_input(const Geo &g, const void *dy, const void *w, void *dx,
 bool largek_mfma_bwdw_fits(const Geo &g, int dtype);
 int largek_mfma_bwd_weight_chunks(const Geo &g);
 int largek_mfma_bwd_weight(const Geo &g, const void *x, const void *dy, void *ws, int dtype, hipStream_t s);
+// The same on 16 x 16 tiles for k = 7, 13 (dw_largek_mfma.hip): workspace
+// [ic][chunks][k*k + 1], chunks as largek_mfma_bwd_weight_chunks.
+bool largek_mfma_bwdw16_fits(const Geo &g, int dtype);
+int largek_mfma_bwd_weight16(const Geo &g, const void *x, const void *dy, void *ws, int dtype, hipStream_t s);
 
 // Forward and grad-input of the 31 x 31 filter with fp32 I/O on the matrix
 // cores (dw_largek_fwd32.hip).  pass: 0 forward, 1 grad-input.

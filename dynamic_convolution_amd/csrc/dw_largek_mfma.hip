@@ -644,6 +644,242 @@ int run_lkmw(const Geo &g, const LkmwPlan &p, const void *x, const void *dy, voi
     }
 }
 
+// ---------------------------------------------------------------- grad-weight, 16 x 16 tiles
+// The same contraction for k <= 16 on v_mfma_f32_16x16x32_{f16,bf16}: one
+// 16 x 16 output tile (M = kernel row i, N = kernel column j) holds the k x k
+// filter, 13 x 13 of 16 x 16 at k = 13 against 13 x 13 of 32 x 32 in the 32 x 32
+// tile, so the matrix cores execute a quarter of the multiply-adds.  Per dy
+// row and window step of 32 columns one instruction:
+//   A[i][kk] = X[oh + i][32 s + kk]: lane l reads 8 adjacent columns
+//              (kk = 8 (l / 16) ..) of input row oh + l % 16 -- one aligned
+//              16-byte LDS read;
+//   B[kk][j] = dz[oh][32 s + kk - j]: lane l reads the run of 8 dy values
+//              starting at column 32 s + 8 (l / 16) - l % 16 from the two
+//              shifted copies of the dy row (copy 1 placed 17 dwords further
+//              in the bank order, so the lanes reading either copy use
+//              distinct banks);
+//   D: register r of lane l is dw[4 (l / 16) + r][l % 16].
+typedef float f32x4_v __attribute__((ext_vector_type(4)));
+
+template <typename T> struct Mfma16;
+template <> struct Mfma16<__half> {
+    static __device__ __forceinline__ f32x4_v run(u32x4_v a, u32x4_v b, f32x4_v c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_v, a), __builtin_bit_cast(f16x8_v, b),
+                                                      c, 0, 0, 0);
+    }
+};
+template <> struct Mfma16<bf16_t> {
+    static __device__ __forceinline__ f32x4_v run(u32x4_v a, u32x4_v b, f32x4_v c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, a),
+                                                       __builtin_bit_cast(bf16x8_v, b), c, 0, 0, 0);
+    }
+};
+
+template <int K, int CS, int BH> struct Lkmw16Geo {
+    static constexpr int QD = 16 * CS + 20;         // dwords per copy of a dy row
+    static constexpr int D1 = BH * QD + 17;         // dword offset of copy 1
+    static constexpr int XR = BH + K - 1;           // staged input rows
+    static constexpr int XP = 32 * CS + 8;          // input row pitch (halves)
+    static constexpr int dz_bytes = ((D1 + BH * QD) * 4 + 15) / 16 * 16;
+    static constexpr int x_bytes = XR * XP * 2;
+    static constexpr int red_bytes = 4 * 64 * 5 * 4;  // per-wave tiles and dy sums for the final sum
+    static constexpr int lds_bytes = (dz_bytes + x_bytes) > red_bytes ? dz_bytes + x_bytes : red_bytes;
+    static_assert(lds_bytes <= kLdsCap, "band tiles exceed the LDS budget");
+};
+
+template <typename T, int K, int CS, int BH>
+__global__ __launch_bounds__(256) void lk_mfma_bwdw16_kernel(LkmwArgs<T> a) {
+    using G = Lkmw16Geo<K, CS, BH>;
+    static_assert(K <= 16, "one 16 x 16 tile holds the filter");
+    extern __shared__ __align__(16) unsigned char smem[];
+    uint32_t *dz = reinterpret_cast<uint32_t *>(smem);                    // copy 0 [BH][QD], copy 1 at D1
+    uint16_t *xt = reinterpret_cast<uint16_t *>(smem + G::dz_bytes);      // [XR][XP]
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int jl = lane & 15, g4 = lane >> 4;
+    const int c = blockIdx.x / a.NC;
+    const int chunk = blockIdx.x - c * a.NC;
+    const int n0 = chunk * a.npc, n1 = min(n0 + a.npc, a.N);
+
+    for (int e = tid; e < G::x_bytes / 16; e += 256) reinterpret_cast<uint4 *>(xt)[e] = make_uint4(0u, 0u, 0u, 0u);
+    for (int e = tid; e < G::dz_bytes / 16; e += 256) reinterpret_cast<uint4 *>(dz)[e] = make_uint4(0u, 0u, 0u, 0u);
+
+    f32x4_v acc0, acc1;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc0[r] = acc1[r] = 0.f;
+    float dsum = 0.f;
+
+    constexpr int NXV = ((BH + K - 1) * 4 * CS + 255) / 256;  // x vectors per thread (iw <= 32 CS)
+    constexpr int NDV = (BH * 8 + 255) / 256;                 // dy vectors per thread (ow <= 64)
+    const bool vec = a.vx && a.vd;
+    const int nsteps = (n1 - n0) * a.nbands;
+    uint4 pfx[NXV], pfd[NDV];
+    auto prefetch = [&](int t) {
+        const int n = n0 + t / a.nbands, oh0 = (t % a.nbands) * BH;
+        const int rows = min(BH, a.OH - oh0);
+        const uint16_t *xp = reinterpret_cast<const uint16_t *>(a.x) + (static_cast<int64_t>(n) * a.C + c) * a.IH * a.IW;
+        const uint16_t *dp = reinterpret_cast<const uint16_t *>(a.dy) + (static_cast<int64_t>(n) * a.C + c) * a.OH * a.OW;
+        const int xv = a.IW / 8, dv = a.OW / 8;
+#pragma unroll
+        for (int k = 0; k < NXV; ++k) {
+            const int v = tid + 256 * k;
+            const int r = v / xv;
+            const int ih = oh0 + r - a.P;
+            pfx[k] = make_uint4(0u, 0u, 0u, 0u);
+            if (v < (rows + K - 1) * xv && ih >= 0 && ih < a.IH)
+                pfx[k] = *reinterpret_cast<const uint4 *>(xp + static_cast<int64_t>(ih) * a.IW + (v - r * xv) * 8);
+        }
+#pragma unroll
+        for (int k = 0; k < NDV; ++k) {
+            const int v = tid + 256 * k;
+            const int r = v / dv;
+            pfd[k] = make_uint4(0u, 0u, 0u, 0u);
+            if (v < rows * dv)
+                pfd[k] = *reinterpret_cast<const uint4 *>(dp + static_cast<int64_t>(oh0 + r) * a.OW + (v - r * dv) * 8);
+        }
+    };
+    if (vec && nsteps > 0) prefetch(0);
+
+    for (int t = 0; t < nsteps; ++t) {
+        const int n = n0 + t / a.nbands, band = t % a.nbands;
+        const uint16_t *xp = reinterpret_cast<const uint16_t *>(a.x) + (static_cast<int64_t>(n) * a.C + c) * a.IH * a.IW;
+        const uint16_t *dp = reinterpret_cast<const uint16_t *>(a.dy) + (static_cast<int64_t>(n) * a.C + c) * a.OH * a.OW;
+        const int oh0 = band * BH;
+        const int rows = min(BH, a.OH - oh0);
+        __syncthreads();  // the previous band's reads are done
+        const int xrows = rows + K - 1;
+        if (vec) {
+            const int xv = a.IW / 8, dv = a.OW / 8;
+#pragma unroll
+            for (int k = 0; k < NXV; ++k) {
+                const int v = tid + 256 * k;
+                if (v < xrows * xv) {
+                    const int r = v / xv;
+                    uint16_t *d = xt + r * G::XP + a.P + (v - r * xv) * 8;
+                    const uint32_t wd[4] = {pfx[k].x, pfx[k].y, pfx[k].z, pfx[k].w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) d[e] = static_cast<uint16_t>(wd[e >> 1] >> ((e & 1) * 16));
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < NDV; ++k) {
+                const int v = tid + 256 * k;
+                if (v < rows * dv) {
+                    const int r = v / dv;
+                    const int c8 = (v - r * dv) * 8;
+                    *reinterpret_cast<uint4 *>(dz + r * G::QD + (kDzOff + c8) / 2) = pfd[k];
+                    const uint32_t wd[4] = {pfd[k].x, pfd[k].y, pfd[k].z, pfd[k].w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const uint16_t bits = static_cast<uint16_t>(wd[e >> 1] >> ((e & 1) * 16));
+                        T tv;
+                        __builtin_memcpy(&tv, &bits, 2);
+                        dsum += to_f32(tv);
+                    }
+                }
+            }
+        } else {
+            for (int e = tid; e < xrows * a.IW; e += 256) {
+                const int r = e / a.IW;
+                const int col = e - r * a.IW;
+                const int ih = oh0 + r - a.P;
+                xt[r * G::XP + a.P + col] = (ih >= 0 && ih < a.IH) ? xp[static_cast<int64_t>(ih) * a.IW + col] : 0;
+            }
+            uint16_t *dz16 = reinterpret_cast<uint16_t *>(dz);
+            for (int e = tid; e < rows * a.OW; e += 256) {
+                const int r = e / a.OW;
+                const int col = e - r * a.OW;
+                const uint16_t bits = dp[static_cast<int64_t>(oh0 + r) * a.OW + col];
+                dz16[2 * r * G::QD + kDzOff + col] = bits;
+                T tv;
+                __builtin_memcpy(&tv, &bits, 2);
+                dsum += to_f32(tv);
+            }
+        }
+        __syncthreads();
+        // copy 1: dword d holds copy-0 positions 2d + 1 and 2d + 2
+        for (int e = tid; e < rows * G::QD; e += 256) {
+            const int r = e / G::QD;
+            const int d = e - r * G::QD;
+            const uint32_t lo = dz[r * G::QD + d];
+            const uint32_t hi = d + 1 < G::QD ? dz[r * G::QD + d + 1] : 0u;
+            dz[G::D1 + r * G::QD + d] = (lo >> 16) | (hi << 16);
+        }
+        __syncthreads();
+        if (vec && t + 1 < nsteps) prefetch(t + 1);
+        // kernel rows i >= k (lanes with l % 16 >= k) are not part of dw: they read
+        // row k - 1 instead, so every read stays inside the staged rows
+        const int mi = min(jl, K - 1);
+        for (int oh = wave; oh < rows; oh += 4) {
+#pragma unroll
+            for (int s2 = 0; s2 < CS; ++s2) {
+                const u32x4_v af = *reinterpret_cast<const u32x4_v *>(xt + (oh + mi) * G::XP + 32 * s2 + 8 * g4);
+                const int tp = 32 * s2 + 8 * g4 - jl + kDzOff;  // first padded position of this lane's dy run
+                const int q = tp & 1;
+                const uint32_t *p = dz + q * G::D1 + oh * G::QD + ((tp - q) >> 1);
+                const u32x4_v bf = u32x4_v{p[0], p[1], p[2], p[3]};
+                if (s2 & 1)
+                    acc1 = Mfma16<T>::run(af, bf, acc1);
+                else
+                    acc0 = Mfma16<T>::run(af, bf, acc0);
+            }
+        }
+    }
+
+    // fixed-order sum of the 4 waves' tiles and of the 256 dy partial sums
+    __syncthreads();
+    float *red = reinterpret_cast<float *>(smem);  // [wave][lane][5]
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[(wave * 64 + lane) * 5 + r] = acc0[r] + acc1[r];
+    red[(wave * 64 + lane) * 5 + 4] = dsum;
+    __syncthreads();
+    float *dst = a.ws + (static_cast<int64_t>(c) * a.NC + chunk) * (K * K + 1);
+    for (int e = tid; e < K * K + 1; e += 256) {
+        float v = 0.f;
+        if (e < K * K) {
+            const int i = e / K, j = e - (e / K) * K;
+            const int ln = 16 * (i >> 2) + j, r = i & 3;
+            for (int w = 0; w < 4; ++w) v += red[(w * 64 + ln) * 5 + r];
+        } else {
+            for (int t2 = 0; t2 < 256; ++t2) v += red[t2 * 5 + 4];
+        }
+        dst[e] = v;
+    }
+}
+
+template <typename T, int K, int CS>
+int run_lkmw16_cs(const Geo &g, const LkmwPlan &p, const void *x, const void *dy, void *ws, hipStream_t s) {
+    using G = Lkmw16Geo<K, CS, kBwBH>;
+    LkmwArgs<T> a{};
+    a.x = static_cast<const T *>(x);
+    a.dy = static_cast<const T *>(dy);
+    a.ws = static_cast<float *>(ws);
+    a.C = g.ic;
+    a.N = g.n;
+    a.IH = g.ih;
+    a.IW = g.iw;
+    a.OH = g.oh;
+    a.OW = g.ow;
+    a.P = g.ph;
+    a.NC = p.NC;
+    a.npc = p.npc;
+    a.nbands = p.nbands;
+    a.vx = g.iw % 8 == 0 && reinterpret_cast<uintptr_t>(x) % 16 == 0;
+    a.vd = g.ow % 8 == 0 && reinterpret_cast<uintptr_t>(dy) % 16 == 0;
+    hipLaunchKernelGGL((lk_mfma_bwdw16_kernel<T, K, CS, kBwBH>), dim3(g.ic * p.NC), dim3(256), G::lds_bytes, s, a);
+    return hipGetLastError() == hipSuccess ? kOk : kErrHip;
+}
+
+template <typename T, int K>
+int run_lkmw16(const Geo &g, const LkmwPlan &p, const void *x, const void *dy, void *ws, hipStream_t s) {
+    switch ((g.ow + K - 1 + 31) / 32) {
+        case 1: return run_lkmw16_cs<T, K, 1>(g, p, x, dy, ws, s);
+        case 2: return run_lkmw16_cs<T, K, 2>(g, p, x, dy, ws, s);
+        default: return run_lkmw16_cs<T, K, 3>(g, p, x, dy, ws, s);
+    }
+}
+
 }  // namespace
 
 // 16-bit I/O, k = 13 or 31 square, stride 1, dilation 1, multiplier 1,
@@ -663,6 +899,25 @@ int largek_mfma_bwd_weight_chunks(const Geo &g) {
     LkmwPlan p;
     plan_lkmw(g, p);
     return p.NC;
+}
+
+// 16-bit I/O, k = 7 or 13 square, stride 1, dilation 1, multiplier 1,
+// symmetric padding, dy rows of at most 64 (the window, ow + k - 1 <= 76
+// columns, is at most three 32-column steps) and an input that fits them.
+bool largek_mfma_bwdw16_fits(const Geo &g, int dtype) {
+    if (dtype == 0) return false;
+    if (g.kh != g.kw || (g.kh != 7 && g.kh != 13)) return false;
+    if (g.sh != 1 || g.sw != 1 || g.dh != 1 || g.dw != 1 || g.ph != g.pw || g.mult != 1) return false;
+    if (g.ow > 64) return false;
+    const int XC = 32 * ((g.ow + g.kh - 1 + 31) / 32);
+    return g.iw + g.ph <= XC;
+}
+
+int largek_mfma_bwd_weight16(const Geo &g, const void *x, const void *dy, void *ws, int dtype, hipStream_t s) {
+    LkmwPlan p;
+    plan_lkmw(g, p);
+    if (dtype == 1) return g.kh == 7 ? run_lkmw16<__half, 7>(g, p, x, dy, ws, s) : run_lkmw16<__half, 13>(g, p, x, dy, ws, s);
+    return g.kh == 7 ? run_lkmw16<bf16_t, 7>(g, p, x, dy, ws, s) : run_lkmw16<bf16_t, 13>(g, p, x, dy, ws, s);
 }
 
 int largek_mfma_bwd_weight(const Geo &g, const void *x, const void *dy, void *ws, int dtype, hipStream_t s) {

@@ -694,11 +694,21 @@ def test_large_kernel_mfma_group_chunks(n, c, h, w, k, p, dt):
     (1, 2, 40, 100, 13, 6, "f16", False),    # rows of 100: register tiles
 ])
 def test_large_kernel_mfma_grad_weight(n, c, h, w, k, p, dt, bw_mfma):
+    """The 32 x 32-tile family (the default at k = 31; at k = 13 the 16 x 16 tiles are, so it is forced)."""
     geo = ((n, c, h, w), (c, k, k), 1, p, 1)
-    assert (dc.dwconv2d_algo(2, *geo, dtype=DT[dt]) == "largek_mfma") == bw_mfma
+    default = dc.dwconv2d_algo(2, *geo, dtype=DT[dt])
+    if bw_mfma and k == 13:
+        assert default == "largek_mfma_h16"
+    else:
+        assert (default == "largek_mfma") == bw_mfma
     x, wt, b, dy = static_case(n, c, h, w, 1, k, 1, p, 1, DT[dt], 690 + h + w + k)
-    check_static(x, wt, b, dy, 1, p, 1, "largek-mfma-bw n%d c%d %dx%d k%d p%d %s" % (n, c, h, w, k, p, dt),
-                 passes=("bwd_w",))
+    try:
+        if bw_mfma:
+            dc.dwconv2d_set_algo(2, *geo, dtype=DT[dt], algo="largek_mfma")
+        check_static(x, wt, b, dy, 1, p, 1, "largek-mfma-bw n%d c%d %dx%d k%d p%d %s" % (n, c, h, w, k, p, dt),
+                     passes=("bwd_w",))
+    finally:
+        dc.dwconv2d_set_algo(2, *geo, dtype=DT[dt], algo=None)
 
 # ------------------------------------------------------------------ stride 2 / dilation 2 / pad k-1 (even-grid) path
 @pytest.mark.parametrize("n,c,h,w,mult,k,dt", [
@@ -913,5 +923,28 @@ def test_grad_weight_7_row_stream(n, c, h, w, dt):
     try:
         dc.dwconv2d_set_algo(2, *geo, dtype=DT[dt], algo="stream_7x7")
         check_static(x, wt, b, dy, 1, 3, 1, "stream7 n%d c%d %dx%d %s" % (n, c, h, w, dt), passes=("bwd_w",))
+    finally:
+        dc.dwconv2d_set_algo(2, *geo, dtype=DT[dt], algo=None)
+
+
+# ------------------------------------------------------------------ 16-bit grad-weight of k <= 16 on 16 x 16 matrix tiles
+@pytest.mark.parametrize("n,c,h,w,k,p,dt", [
+    (3, 2, 64, 64, 13, 6, "f16"),     # two bands, three 32-column window steps
+    (2, 3, 48, 48, 13, 6, "bf16"),    # a full and a partial band, two steps
+    (4, 2, 32, 32, 7, 3, "f16"),
+    (5, 2, 64, 64, 7, 3, "bf16"),
+    (2, 2, 20, 22, 13, 12, "bf16"),   # pad k - 1, rows of 22: element staging
+    (2, 2, 9, 9, 13, 6, "f16"),       # kernel wider than the image, one step
+    (3, 2, 70, 40, 13, 6, "f16"),     # 70 dy rows: three bands
+    (2, 2, 33, 30, 7, 0, "bf16"),     # no padding
+])
+def test_grad_weight_16bit_small_matrix_tiles(n, c, h, w, k, p, dt):
+    geo = ((n, c, h, w), (c, k, k), 1, p, 1)
+    assert "largek_mfma_h16" in dc.dwconv2d_algo_candidates(2, *geo, dtype=DT[dt])
+    x, wt, b, dy = static_case(n, c, h, w, 1, k, 1, p, 1, DT[dt], 1850 + h + w + k + p)
+    try:
+        dc.dwconv2d_set_algo(2, *geo, dtype=DT[dt], algo="largek_mfma_h16")
+        check_static(x, wt, b, dy, 1, p, 1, "wgrad-h16 n%d c%d %dx%d k%d p%d %s" % (n, c, h, w, k, p, dt),
+                     passes=("bwd_w",))
     finally:
         dc.dwconv2d_set_algo(2, *geo, dtype=DT[dt], algo=None)
