@@ -85,10 +85,11 @@ template <typename T> struct LkmArgs {
 // input tile per wave, as many waves (up to 4) as fit the LDS budget.
 template <int K, int KPS, int MT, int NT> struct LkmGeo {
     static constexpr int QD = 8 * KPS + 20;              // dwords per copy of a filter row (even)
+    static constexpr int W1 = K * QD + 17;               // dword offset of copy 1 (17 banks from copy 0)
     static constexpr int XR = 32 * MT + K - 1;           // staged input rows
     static constexpr int XC = 32 * (NT - 1) + 16 * KPS;  // staged input columns
     static constexpr int XP = XC + 8;                    // row pitch (halves): an odd multiple of 16 bytes mod 32
-    static constexpr int table_bytes = 2 * K * QD * 4;
+    static constexpr int table_bytes = ((W1 + K * QD) * 4 + 15) / 16 * 16;
     static constexpr int tile_halves = XR * XP;
     static constexpr int IPG = 4 / MT;                   // images per workgroup: one wave per (image, row tile)
     static constexpr int lds_bytes = table_bytes + IPG * tile_halves * 2;
@@ -99,7 +100,7 @@ template <typename T, int K, int KPS, int MT, int NT, bool FLIP>
 __global__ __launch_bounds__(256) void lk_mfma_kernel(LkmArgs<T> a) {
     using G = LkmGeo<K, KPS, MT, NT>;
     extern __shared__ __align__(16) unsigned char smem[];
-    uint32_t *wtab = reinterpret_cast<uint32_t *>(smem);  // [copy][i][QD]
+    uint32_t *wtab = reinterpret_cast<uint32_t *>(smem);  // copy 0 [i][QD], copy 1 at W1
     uint16_t *tiles = reinterpret_cast<uint16_t *>(smem + G::table_bytes);
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -128,7 +129,7 @@ __global__ __launch_bounds__(256) void lk_mfma_kernel(LkmArgs<T> a) {
                 v |= static_cast<uint32_t>(bits) << (16 * u);
             }
         }
-        wtab[e] = v;
+        wtab[q * G::W1 + rem] = v;
     }
 
     // 2. per image group, the padded input planes: tile[r][col] = in[r - P][col - P],
@@ -232,7 +233,7 @@ __global__ __launch_bounds__(256) void lk_mfma_kernel(LkmArgs<T> a) {
                 for (int s = 0; s < KPS; ++s) {
                     const int t = 16 * s + 8 * h - m + kZoff;  // first padded position of this lane's run
                     const int q = t & 1;
-                    const uint32_t *p = wtab + (q * K + i) * G::QD + ((t - q) >> 1);
+                    const uint32_t *p = wtab + q * G::W1 + i * G::QD + ((t - q) >> 1);
                     af[s] = u32x4_v{p[0], p[1], p[2], p[3]};
                 }
 #pragma unroll
@@ -418,9 +419,10 @@ template <typename T> struct LkmwArgs {
 
 template <int K, int CS, int BH> struct LkmwGeo {
     static constexpr int QD = 8 * CS + 20;          // dwords per copy of a dy row (multiple of 4)
+    static constexpr int D1 = BH * QD + 17;         // dword offset of copy 1 (17 banks from copy 0)
     static constexpr int XR = BH + K - 1;           // staged input rows
     static constexpr int XP = 16 * CS + 8;          // input row pitch (halves)
-    static constexpr int dz_bytes = 2 * BH * QD * 4;
+    static constexpr int dz_bytes = ((D1 + BH * QD) * 4 + 15) / 16 * 16;
     static constexpr int x_bytes = XR * XP * 2;
     static constexpr int red_bytes = 4 * 64 * 17 * 4;  // per-wave tiles and dy sums for the final sum
     static constexpr int lds_bytes = (dz_bytes + x_bytes) > red_bytes ? dz_bytes + x_bytes : red_bytes;
@@ -431,7 +433,7 @@ template <typename T, int K, int CS, int BH>
 __global__ __launch_bounds__(256) void lk_mfma_bwdw_kernel(LkmwArgs<T> a) {
     using G = LkmwGeo<K, CS, BH>;
     extern __shared__ __align__(16) unsigned char smem[];
-    uint32_t *dz = reinterpret_cast<uint32_t *>(smem);                    // [copy][BH][QD]
+    uint32_t *dz = reinterpret_cast<uint32_t *>(smem);                    // copy 0 [BH][QD], copy 1 at D1
     uint16_t *xt = reinterpret_cast<uint16_t *>(smem + G::dz_bytes);      // [XR][XP]
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -545,7 +547,7 @@ __global__ __launch_bounds__(256) void lk_mfma_bwdw_kernel(LkmwArgs<T> a) {
             }
             __syncthreads();
             // copy 1: dword d holds copy-0 positions 2d + 1 and 2d + 2
-            uint32_t *dz1 = dz + BH * G::QD;
+            uint32_t *dz1 = dz + G::D1;
             for (int e = tid; e < rows * G::QD; e += 256) {
                 const int r = e / G::QD;
                 const int d = e - r * G::QD;
@@ -564,7 +566,7 @@ __global__ __launch_bounds__(256) void lk_mfma_bwdw_kernel(LkmwArgs<T> a) {
                     const u32x4_v af = *reinterpret_cast<const u32x4_v *>(xt + (oh + mi) * G::XP + 16 * s + 8 * h);
                     const int t = 16 * s + 8 * h - m + kDzOff;  // first padded position of this lane's dy run
                     const int q = t & 1;
-                    const uint32_t *p = dz + (q * BH + oh) * G::QD + ((t - q) >> 1);
+                    const uint32_t *p = dz + q * G::D1 + oh * G::QD + ((t - q) >> 1);
                     const u32x4_v bf = u32x4_v{p[0], p[1], p[2], p[3]};
                     acc = Mfma<T>::run(af, bf, acc);
                 }
