@@ -39,6 +39,7 @@ namespace dw {
 namespace {
 
 typedef float f32x16_f __attribute__((ext_vector_type(16)));
+typedef float f32x4_f __attribute__((ext_vector_type(4)));
 
 constexpr int kF32K = 31;            // filter size this family serves
 constexpr int kF32TargetWG = 6144;
@@ -215,14 +216,193 @@ __global__ __launch_bounds__(256, 4) void lk_fwd32_kernel(Lf32Args<T> a) {
     }
 }
 
+// The same split on 16 x 16 x 4 fp32 tiles (v_mfma_f32_16x16x4_f32), for rows
+// whose width leaves at most half of a last 32-column tile used (48 = 32 + 16
+// columns: 32-column tiles execute 64 columns' work, 16-column tiles 48).  A
+// 16-column tile of one output row is two instructions per 4 kernel rows:
+//   D_h[j][c] = sum_i w[i][16 h + j] X[oh + i - P][c0 + c],  h = 0, 1,
+// A lane l holding j = l % 16, i = 4 u + l / 16 (16 filter registers per lane
+// for the whole kernel); B lane l holding c = l % 16, i = 4 u + l / 16 (one
+// 4-byte LDS read feeds both instructions); D register r of lane l holding
+// j = 4 (l / 16) + r, c = l % 16 (layout checked on the MI355X).  Diagonal
+// sums: lane (t, g) = (l % 16, l / 16) gathers D[j][(t + j) mod 16] for its 4
+// rows j = 4 g + r (one ds_bpermute each within its 16-lane row, j growing
+// with r so the diagonal-t terms are a prefix: running sum, captured), then
+// the 4 rows of lanes are summed with v_permlane16_swap / v_permlane32_swap
+// (both halves added in the same order in every lane).  Lane t then holds
+// local diagonals t and t - 16 of each tile half; the three output columns a
+// lane adds (diagonals t, t - 16, t - 32 of the 47 a tile touches) go to the
+// wave's LDS row accumulator from lane rows 0, 1 and 2.
+__device__ __forceinline__ f32x4_f mfma_f32x16(float a, float b, f32x4_f c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// sum of v over the lanes l ^ 16, l ^ 32, l ^ 48 and l (fixed order, same in every lane)
+__device__ __forceinline__ float rowsum4(float v) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    const float s = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+template <typename T, int K, int NCT, bool FLIP>
+__global__ __launch_bounds__(256, 4) void lk_fwd16t_kernel(Lf32Args<T> a) {
+    constexpr int XP = 16 * NCT;  // LDS pitch of a staged input row
+    constexpr int NU = 8;          // instructions per tile half: kernel rows 4u .. 4u + 3
+    static_assert(K <= 4 * NU, "one 32-row contraction covers the filter");
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int xrows = a.BH + K;
+    float *xs = reinterpret_cast<float *>(smem);                  // [xrows][XP]
+    float *yacc = xs + xrows * XP;                                // [4][OWP]
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int t = lane & 15, g = lane >> 4;
+    const int c = blockIdx.x / a.NC;
+    const int chunk = blockIdx.x - c * a.NC;
+    const int n0 = chunk * a.npc, n1 = min(n0 + a.npc, a.N);
+    const int cin = FLIP ? c : c / a.mult;
+    float *ya = yacc + wave * a.OWP;
+
+    // A operands: w[i][j] at i = 4u + g, j = 16 h + t (flipped for grad-input), zero outside
+    float wreg[2][NU];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            const int i = 4 * u + g, j = 16 * hh + t;
+            float v = 0.f;
+            if (i < K && j < K) {
+                const int si = FLIP ? K - 1 - i : i, sj = FLIP ? K - 1 - j : j;
+                v = to_f32(a.w[(static_cast<int64_t>(c) * K + si) * K + sj]);
+            }
+            wreg[hh][u] = v;
+        }
+    __builtin_amdgcn_s_waitcnt(0);
+    const float bias = (!FLIP && a.b) ? to_f32(a.b[c]) : 0.f;
+    for (int e = tid; e < xrows * XP; e += 256) xs[e] = 0.f;
+    for (int e = tid; e < 4 * a.OWP; e += 256) yacc[e] = 0.f;
+
+    for (int n = n0; n < n1; ++n) {
+        const T *ip = a.in + (static_cast<int64_t>(n) * a.Cin + cin) * a.IH * a.IW;
+        T *op = a.out + (static_cast<int64_t>(n) * a.C + c) * a.OH * a.OW;
+        for (int band = 0; band < a.nbands; ++band) {
+            const int oh0 = band * a.BH;
+            const int rows = min(a.BH, a.OH - oh0);
+            const int srows = rows + K;
+            __syncthreads();
+            if (a.vin) {
+                constexpr int VE = Vec<T>::N;
+                const int vpr = a.IW / VE;
+                for (int v = tid; v < srows * vpr; v += 256) {
+                    const int r = v / vpr;
+                    const int c0 = (v - r * vpr) * VE;
+                    const int ih = oh0 + r - a.P;
+                    union {
+                        uint4 u;
+                        T t[VE];
+                    } raw;
+                    raw.u = make_uint4(0u, 0u, 0u, 0u);
+                    if (ih >= 0 && ih < a.IH) raw.u = *reinterpret_cast<const uint4 *>(ip + static_cast<int64_t>(ih) * a.IW + c0);
+                    float *d = xs + r * XP + c0;
+#pragma unroll
+                    for (int e = 0; e < VE; ++e) d[e] = to_f32(raw.t[e]);
+                }
+            } else {
+                for (int e = tid; e < srows * a.IW; e += 256) {
+                    const int r = e / a.IW;
+                    const int col = e - r * a.IW;
+                    const int ih = oh0 + r - a.P;
+                    xs[r * XP + col] = (ih >= 0 && ih < a.IH) ? to_f32(ip[static_cast<int64_t>(ih) * a.IW + col]) : 0.f;
+                }
+            }
+            __syncthreads();
+            // items: output row wave + 4 (q / NCT), 16-column tile q % NCT; item q + 1's
+            // instructions are issued before item q's diagonal sums
+            const int nq = (rows > wave ? (rows - wave + 3) / 4 : 0) * NCT;
+            auto issue = [&](f32x4_f &d0, f32x4_f &d1, int q) {
+                const int r = wave + 4 * (q / NCT), ct = q % NCT;
+                const int oh = oh0 + r;
+                const int i_lo = max(0, a.P - oh), i_hi = min(K, a.IH + a.P - oh);
+                const int u_lo = i_lo >> 2, u_hi = (i_hi + 3) >> 2;
+                const float *bp = xs + (r + g) * XP + 16 * ct + t;
+                float bv[NU];
+#pragma unroll
+                for (int u = 0; u < NU; ++u) bv[u] = bp[4 * u * XP];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) d0[e] = d1[e] = 0.f;
+#pragma unroll
+                for (int u = 0; u < NU; ++u)
+                    if (u >= u_lo && u < u_hi) {
+                        d0 = mfma_f32x16(wreg[0][u], bv[u], d0);
+                        d1 = mfma_f32x16(wreg[1][u], bv[u], d1);
+                    }
+            };
+            auto reduce = [&](const f32x4_f &d0, const f32x4_f &d1, int q) {
+                const int r = wave + 4 * (q / NCT), ct = q % NCT;
+                // per tile half: lane (t, g) gathers D[4g + e][(t + 4g + e) mod 16] from
+                // register e of lane 16 g + ((t + 4 g + e) & 15); the terms with
+                // t + 4g + e < 16 are diagonal t (a prefix of e), the others t - 16
+                float pos[2], neg[2];
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    float run = 0.f, sp = 0.f;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int jj = 4 * g + e;
+                        const int src = 16 * g + ((t + jj) & 15);
+                        const float dv = hh == 0 ? d0[e] : d1[e];
+                        const float v = __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(dv)));
+                        run += v;
+                        sp = (t + jj < 16) ? run : sp;
+                    }
+                    pos[hh] = rowsum4(sp);
+                    neg[hh] = rowsum4(run - sp);
+                }
+                // diagonals t (half 0 pos), t - 16 (half 0 neg + half 1 pos), t - 32 (half 1 neg)
+                const float v = g == 0 ? pos[0] : g == 1 ? neg[0] + pos[1] : neg[1];
+                const int ow = 16 * ct + t - 16 * g + a.P;
+                if (g < 3 && ow >= 0 && ow < a.OW) ya[ow] += v;
+                if (ct == NCT - 1) {
+                    wave_lds_sync();
+                    T *yr = op + static_cast<int64_t>(oh0 + r) * a.OW;
+                    for (int u = lane; u < a.OW; u += 64) {
+                        yr[u] = from_f32<T>(ya[u] + bias);
+                        ya[u] = 0.f;
+                    }
+                    wave_lds_sync();
+                }
+            };
+            f32x4_f a0, a1, b0, b1;
+            if (nq > 0) issue(a0, a1, 0);
+            for (int q = 0; q < nq; q += 2) {
+                if (q + 1 < nq) issue(b0, b1, q + 1);
+                reduce(a0, a1, q);
+                if (q + 1 < nq) {
+                    if (q + 2 < nq) issue(a0, a1, q + 2);
+                    reduce(b0, b1, q + 1);
+                }
+            }
+        }
+    }
+}
+
 struct Lf32Plan {
-    int NC, npc, BH, nbands, XP, OWP, lds_bytes;
+    int NC, npc, BH, nbands, XP, OWP, lds_bytes, tile;
 };
+
+// Column tile of the input rows: 16 where a last 32-column tile would be at
+// most half used.
+inline int lf32_tile(int IW) {
+    const int r = IW % 32;
+    return (r != 0 && r <= 16) ? 16 : 32;
+}
 
 // ih x iw: input plane of this pass, oh x ow: its output plane
 bool plan_lf32(int N, int C, int IH, int IW, int OH, int OW, Lf32Plan &p) {
     (void)IH;
-    p.XP = (IW + 31) / 32 * 32;
+    p.tile = lf32_tile(IW);
+    p.XP = (IW + p.tile - 1) / p.tile * p.tile;
     p.OWP = (OW + 63) / 64 * 64;
     const int64_t fixed = 4LL * p.OWP * 4;
     auto bytes = [&](int bh) { return static_cast<int64_t>(bh + kF32K) * p.XP * 4 + fixed; };
@@ -246,10 +426,24 @@ int run_lf32(Lf32Args<T> a, const Lf32Plan &p, hipStream_t s) {
     a.npc = p.npc;
     a.BH = p.BH;
     a.nbands = p.nbands;
-    a.NCT = p.XP / 32;
+    a.NCT = p.XP / p.tile;
     a.OWP = p.OWP;
     a.vin = a.IW % Vec<T>::N == 0 && reinterpret_cast<uintptr_t>(a.in) % 16 == 0;
     const dim3 grid(a.C * p.NC), block(256);
+    if (p.tile == 16) {
+        // an odd count of 16-column tiles (the width leaves the last 32-column tile half used)
+        switch (a.NCT) {
+            case 1: hipLaunchKernelGGL((lk_fwd16t_kernel<T, kF32K, 1, FLIP>), grid, block, p.lds_bytes, s, a); break;
+            case 3: hipLaunchKernelGGL((lk_fwd16t_kernel<T, kF32K, 3, FLIP>), grid, block, p.lds_bytes, s, a); break;
+            case 5: hipLaunchKernelGGL((lk_fwd16t_kernel<T, kF32K, 5, FLIP>), grid, block, p.lds_bytes, s, a); break;
+            case 7: hipLaunchKernelGGL((lk_fwd16t_kernel<T, kF32K, 7, FLIP>), grid, block, p.lds_bytes, s, a); break;
+            case 9: hipLaunchKernelGGL((lk_fwd16t_kernel<T, kF32K, 9, FLIP>), grid, block, p.lds_bytes, s, a); break;
+            case 11: hipLaunchKernelGGL((lk_fwd16t_kernel<T, kF32K, 11, FLIP>), grid, block, p.lds_bytes, s, a); break;
+            case 13: hipLaunchKernelGGL((lk_fwd16t_kernel<T, kF32K, 13, FLIP>), grid, block, p.lds_bytes, s, a); break;
+            default: hipLaunchKernelGGL((lk_fwd16t_kernel<T, kF32K, 15, FLIP>), grid, block, p.lds_bytes, s, a); break;
+        }
+        return hipGetLastError() == hipSuccess ? kOk : kErrHip;
+    }
     switch (a.NCT) {
         case 1: hipLaunchKernelGGL((lk_fwd32_kernel<T, kF32K, 1, FLIP>), grid, block, p.lds_bytes, s, a); break;
         case 2: hipLaunchKernelGGL((lk_fwd32_kernel<T, kF32K, 2, FLIP>), grid, block, p.lds_bytes, s, a); break;
@@ -280,13 +474,14 @@ bool largek_fwd32_fits(const Geo &g, int pass, int dtype) {
     return plan_lf32(g.n, g.oc, g.ih, g.iw, g.oh, g.ow, p);
 }
 
-// Whether the family is the better default: its 32-column tiles must be
-// mostly input (48-column rows leave a quarter of the second tile empty and
+// Whether the family is the better default: its tiles must be mostly input
+// (32-column tiles on 48-column rows leave a quarter of the work empty and
 // measured slower than the register-tile kernels: 1.49 against 1.44 ms at
-// N64 C384 48 x 48).
+// N64 C384 48 x 48; those rows take 16-column tiles).
 bool largek_fwd32_preferred(const Geo &g, int pass) {
     const int iw = pass == 1 ? g.ow : g.iw;
-    return 5 * iw >= 4 * 32 * ((iw + 31) / 32);
+    const int tile = lf32_tile(iw);
+    return tile == 16 || 5 * iw >= 4 * tile * ((iw + tile - 1) / tile);
 }
 
 int largek_fwd32(const Geo &g, const void *x, const void *w, const void *b, void *y, hipStream_t s) {

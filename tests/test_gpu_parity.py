@@ -804,6 +804,10 @@ def test_large_kernel_grad_weight_f32_matrix(n, c, h, w, p):
     (1, 2, 64, 64, 2, 15, False),     # multiplier 2: forward only
     (1, 1, 70, 100, 1, 15, True),     # four column tiles, six bands
     (5, 1, 33, 30, 1, 7, True),       # odd sizes
+    (2, 3, 48, 48, 1, 15, True),      # 16-column tiles: three a row
+    (2, 2, 40, 80, 1, 15, True),      # five 16-column tiles, two bands
+    (1, 1, 20, 144, 1, 15, True),     # nine 16-column tiles
+    (2, 2, 48, 48, 2, 15, False),     # 16-column tiles, multiplier 2
 ])
 def test_large_kernel_fwd_f32_matrix(n, c, h, w, mult, p, bin_m):
     """Forward and grad-input of the family, selected through the table (the built-in
