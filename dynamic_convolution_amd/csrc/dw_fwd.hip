@@ -240,13 +240,14 @@ int run_fwd(const Geo &g, const BandPlan &bp, const void *x, const void *w, cons
 
 enum FwdAlgo {
     kFwdRowwalk = 0, kFwdLargek, kFwdDecim, kFwdBand33s1, kFwdBand33s2, kFwdBand55s1, kFwdBand55s2d2, kFwdBandGeneric,
-    kFwdChannelGroup, kFwdLargekMfma, kFwdLargekMfma32, kFwdDirect, kFwdCount
+    kFwdChannelGroup, kFwdLargekMfma, kFwdLargekMfma32, kFwdDirect, kFwdLargekMfmaH16, kFwdCount
 };
 
 const char *const kFwdNames[kFwdCount] = {"rowwalk_3x3",    "largek_regtile", "decimated_s2d2",
                                           "band_3x3_s1",    "band_3x3_s2",    "band_5x5_s1",
                                           "band_5x5_s2_d2", "band_generic",   "channelgroup_small",
-                                          "largek_mfma",    "largek_mfma_f32", "direct"};
+                                          "largek_mfma",    "largek_mfma_f32", "direct",
+                                          "largek_mfma_h16"};
 
 bool band_fwd_plans(const Geo &g, int dt) {
     BandPlan bp;
@@ -264,6 +265,7 @@ bool feasible_fwd(int algo, const Geo &g, int dt) {
         case kFwdChannelGroup: return small_fwd_fits(g, dt);
         case kFwdLargekMfma: return largek_mfma_fits(g, 0, dt);
         case kFwdLargekMfma32: return largek_fwd32_fits(g, 0, dt);
+        case kFwdLargekMfmaH16: return largek_mfma16_fits(g, 0, dt);
         case kFwdBand33s1: return sq && g.kh == 3 && g.sh == 1 && g.dh == 1 && band_fwd_plans(g, dt);
         case kFwdBand33s2: return sq && g.kh == 3 && g.sh == 2 && g.dh == 1 && band_fwd_plans(g, dt);
         case kFwdBand55s1: return sq && g.kh == 5 && g.sh == 1 && g.dh == 1 && band_fwd_plans(g, dt);
@@ -281,6 +283,8 @@ int select_fwd(const Geo &g, int dt) {
     const int tuned = tuned_algo(0, g, dt);
     if (tuned >= 0 && feasible_fwd(tuned, g, dt)) return tuned;
     if (rowwalk_fits(g, dt, 0)) return kFwdRowwalk;
+    // 16-bit k = 7 planes wider or taller than 32: 16 x 16 tiles measured ~10 % faster
+    if (g.kh == 7 && (g.oh > 32 || g.ow > 32) && largek_mfma16_fits(g, 0, dt)) return kFwdLargekMfmaH16;
     if (largek_mfma_fits(g, 0, dt)) return kFwdLargekMfma;
     if (largek_fwd32_fits(g, 0, dt) && largek_fwd32_preferred(g, 0)) return kFwdLargekMfma32;
     if (largek_fits(g, 0)) return kFwdLargek;
@@ -303,6 +307,7 @@ int dispatch_fwd(const Geo &g, const void *x, const void *w, const void *b, void
     if (algo == kFwdLargek) return largek_fwd(g, x, w, b, y, dt, s);
     if (algo == kFwdLargekMfma) return largek_mfma_fwd(g, x, w, b, y, dt, s);
     if (algo == kFwdLargekMfma32) return largek_fwd32(g, x, w, b, y, s);
+    if (algo == kFwdLargekMfmaH16) return largek_mfma16_fwd(g, x, w, b, y, dt, s);
     if (algo == kFwdDecim) return decim_fwd(g, x, w, b, y, dt, s);
     if (algo == kFwdChannelGroup) return small_fwd(g, x, w, b, y, dt, s);
     if (algo == kFwdDirect) return direct_fwd(g, x, w, b, y, dt, s);

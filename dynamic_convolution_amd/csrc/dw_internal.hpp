@@ -82,6 +82,10 @@ int largek_bwd_weight(const Geo &g, const void *x, const void *dy, void *ws, int
 bool largek_mfma_fits(const Geo &g, int pass, int dtype);
 int largek_mfma_fwd(const Geo &g, const void *x, const void *w, const void *b, void *y, int dtype, hipStream_t s);
 int largek_mfma_bwd_input(const Geo &g, const void *dy, const void *w, void *dx, int dtype, hipStream_t s);
+// The same on 16 x 16 output tiles (dw_largek_mfma.hip).
+bool largek_mfma16_fits(const Geo &g, int pass, int dtype);
+int largek_mfma16_fwd(const Geo &g, const void *x, const void *w, const void *b, void *y, int dtype, hipStream_t s);
+int largek_mfma16_bwd_input(const Geo &g, const void *dy, const void *w, void *dx, int dtype, hipStream_t s);
 // Grad-weight pass 1 of the same family (k = 13, 31; multiplier 1; dy rows <= 64):
 // workspace [ic][chunks][k*k + 1].
 bool largek_mfma_bwdw_fits(const Geo &g, int dtype);

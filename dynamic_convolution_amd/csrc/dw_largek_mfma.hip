@@ -385,6 +385,319 @@ int largek_mfma_bwd_input(const Geo &g, const void *dy, const void *w, void *dx,
     return dtype == 1 ? lkm_bwdin_t<__half>(g, dy, w, dx, s) : lkm_bwdin_t<bf16_t>(g, dy, w, dx, s);
 }
 
+namespace {
+
+typedef float f32x4_v __attribute__((ext_vector_type(4)));
+
+template <typename T> struct Mfma16;
+template <> struct Mfma16<__half> {
+    static __device__ __forceinline__ f32x4_v run(u32x4_v a, u32x4_v b, f32x4_v c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_v, a), __builtin_bit_cast(f16x8_v, b),
+                                                      c, 0, 0, 0);
+    }
+};
+template <> struct Mfma16<bf16_t> {
+    static __device__ __forceinline__ f32x4_v run(u32x4_v a, u32x4_v b, f32x4_v c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, a),
+                                                       __builtin_bit_cast(bf16x8_v, b), c, 0, 0, 0);
+    }
+};
+
+// ---------------------------------------------------------------- forward, 16 x 16 tiles
+// The same Toeplitz product on v_mfma_f32_16x16x32_{f16,bf16}: 16 x 16 output
+// tiles (M = 16 output columns, N = 16 output rows, K = 32 window columns per
+// instruction).  A 16-column tile reads 16 + k - 1 window columns, padded to
+// 32 KPS: 32 for k = 7, 13 (4.6x and 2.5x the useful multiply-adds against
+// 6.9x and 3.7x with 32-column tiles) and 64 for k = 31 (2.06x, the same), and
+// 48-wide planes take 3 x 3 tiles instead of four 32 x 32 ones that are 44 %
+// empty.  Measured on N64 C384: ~10 % faster than the 32 x 32 tiles at k = 7
+// on 48 and 64 planes, about even at k = 13 and 2.5-3x slower at k = 31 (twice
+// the LDS reads per multiply-add), so the default only at k = 7.
+//   A[m][kk] = T_i[m][kk]: lane l reads the 8 filter values of window columns
+//              32 s + 8 (l / 16) .. for output column l % 16 from the table;
+//   B[kk][n] = X[16 mt + n + i][16 nt + 32 s + kk]: lane l reads 8 adjacent
+//              columns of input row 16 mt + l % 16 + i (one 16-byte LDS read;
+//              tiles whose windows start at the same column share it);
+//   D: register r of lane l is output (16 mt + l % 16, 16 nt + 4 (l / 16) + r).
+// A workgroup serves one channel and IPG images, one wave per (image, 16-row
+// tile), and walks several image groups, loading the next group's planes into
+// registers during the matrix work.
+template <int K> constexpr int kps16_of() { return (16 + K - 1 + 31) / 32; }
+
+template <typename T> struct Lkm16Args {
+    const T *in, *w, *b;
+    T *out;
+    int N, IH, IW, OH, OW, P, C, Cin, mult;
+    int MT, NT;          // 16-row / 16-column output tiles of a plane (NT <= 4)
+    int IPG;             // images per group (one wave per image and row tile)
+    int XR, XP;          // staged rows, row pitch (halves) of an input plane
+    int ngroups, gpc, ngtot;
+    int vin, vout, pre;
+};
+
+template <typename T, int K, bool FLIP>
+__global__ __launch_bounds__(256) void lk_mfma16_kernel(Lkm16Args<T> a) {
+    constexpr int KPS = kps16_of<K>();
+    constexpr int QD = 16 * KPS + 20;   // dwords per copy of a filter row (even)
+    constexpr int W1 = K * QD + 17;     // dword offset of copy 1 (17 banks from copy 0)
+    constexpr int table_bytes = ((W1 + K * QD) * 4 + 15) / 16 * 16;
+    constexpr int NTM = 4;              // largest column-tile count (planes up to 64 wide)
+    constexpr int NV = 2;               // prefetch vectors per thread: IPG * 16 MT * 16 NT / 8 <= 2 * threads
+    extern __shared__ __align__(16) unsigned char smem[];
+    uint32_t *wtab = reinterpret_cast<uint32_t *>(smem);  // copy 0 [i][QD], copy 1 at W1
+    uint16_t *tiles = reinterpret_cast<uint16_t *>(smem + table_bytes);
+    const int tid = threadIdx.x;
+    const int nthr = blockDim.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int img = wave / a.MT;
+    const int mt = wave - img * a.MT;
+    const int c = blockIdx.x / a.ngroups;
+    const int g0 = (blockIdx.x - c * a.ngroups) * a.gpc;
+    const int g1 = min(g0 + a.gpc, a.ngtot);
+    const int tile_halves = a.XR * a.XP;
+
+    // 1. filter table: copy q holds, in dword d of row i, padded positions
+    //    2d + q and 2d + q + 1 (position p is w[i][p - kZoff], flipped for grad-input)
+    const uint16_t *wr = reinterpret_cast<const uint16_t *>(a.w) + static_cast<int64_t>(c) * K * K;
+    for (int e = tid; e < 2 * K * QD; e += nthr) {
+        const int q = e / (K * QD);
+        const int rem = e - q * K * QD;
+        const int i = rem / QD;
+        const int d = rem - i * QD;
+        uint32_t v = 0;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int j = 2 * d + q + u - kZoff;
+            if (j >= 0 && j < K) {
+                const uint16_t bits = FLIP ? wr[(K - 1 - i) * K + (K - 1 - j)] : wr[i * K + j];
+                v |= static_cast<uint32_t>(bits) << (16 * u);
+            }
+        }
+        wtab[q * W1 + rem] = v;
+    }
+    // 2. zero planes once; every group writes the same interior positions
+    for (int e = tid; e < a.IPG * tile_halves / 8; e += nthr)
+        reinterpret_cast<uint4 *>(tiles)[e] = make_uint4(0u, 0u, 0u, 0u);
+    __syncthreads();
+    const int cin = FLIP ? c : c / a.mult;
+    const int64_t plane = static_cast<int64_t>(a.IH) * a.IW;
+    const int64_t istride = static_cast<int64_t>(a.Cin) * plane;
+    const uint16_t *ib = reinterpret_cast<const uint16_t *>(a.in) + cin * plane;
+    const int vpr = a.IW / 8, nvec = a.IH * vpr;
+    int64_t goff[NV];
+    int loff[NV], vidx[NV];
+    if (a.pre) {
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            const int v = tid + nthr * k;
+            const int im = v / nvec;
+            const int vv = v - im * nvec;
+            const int r = vv / vpr;
+            const int c8 = (vv - r * vpr) * 8;
+            vidx[k] = v;
+            goff[k] = im * istride + static_cast<int64_t>(r) * a.IW + c8;
+            loff[k] = im * tile_halves + (r + a.P) * a.XP + c8 + a.P;
+        }
+    }
+    uint4 raw[NV];
+    auto load_group = [&](int gi) {
+        const int nv = min(a.IPG, a.N - gi * a.IPG) * nvec;
+        const uint16_t *src = ib + static_cast<int64_t>(gi) * a.IPG * istride;
+#pragma unroll
+        for (int k = 0; k < NV; ++k)
+            if (vidx[k] < nv) raw[k] = *reinterpret_cast<const uint4 *>(src + goff[k]);
+    };
+    if (a.pre && g0 < g1) load_group(g0);
+
+    const int m = lane & 15, g4 = lane >> 4;
+    const float bias = (!FLIP && a.b) ? to_f32(a.b[c]) : 0.f;
+    const uint16_t *xt = tiles + img * tile_halves;
+    for (int gi = g0; gi < g1; ++gi) {
+        const int n0 = gi * a.IPG;
+        const int nimg = min(a.IPG, a.N - n0);
+        if (a.pre) {
+            const int nv = nimg * nvec;
+#pragma unroll
+            for (int k = 0; k < NV; ++k)
+                if (vidx[k] < nv) {
+                    uint16_t *d = tiles + loff[k];
+                    const uint32_t wd[4] = {raw[k].x, raw[k].y, raw[k].z, raw[k].w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) d[e] = static_cast<uint16_t>(wd[e >> 1] >> ((e & 1) * 16));
+                }
+        } else {
+            const uint16_t *src = ib + static_cast<int64_t>(n0) * istride;
+            for (int e = tid; e < nimg * a.IH * a.IW; e += nthr) {
+                const int im = e / (a.IH * a.IW);
+                const int ee = e - im * a.IH * a.IW;
+                const int r = ee / a.IW;
+                const int col = ee - r * a.IW;
+                tiles[im * tile_halves + (r + a.P) * a.XP + col + a.P] = src[im * istride + ee];
+            }
+        }
+        __syncthreads();
+        if (a.pre && gi + 1 < g1) load_group(gi + 1);
+        const int n = n0 + img;
+        if (img < nimg) {
+            // 3. kernel rows x window positions x column tiles
+            f32x4_v acc[NTM];
+#pragma unroll
+            for (int nt = 0; nt < NTM; ++nt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[nt][r] = 0.f;
+#pragma unroll 1
+            for (int i = 0; i < K; ++i) {
+                u32x4_v af[KPS];
+#pragma unroll
+                for (int s2 = 0; s2 < KPS; ++s2) {
+                    const int t = 32 * s2 + 8 * g4 - m + kZoff;  // first padded position of this lane's run
+                    const int q = t & 1;
+                    const uint32_t *p = wtab + q * W1 + i * QD + ((t - q) >> 1);
+                    af[s2] = u32x4_v{p[0], p[1], p[2], p[3]};
+                }
+                // window position p (16 columns): tile nt, step s with nt + 2 s = p
+#pragma unroll
+                for (int p = 0; p < NTM + 2 * (KPS - 1); ++p) {
+                    if (p >= a.NT + 2 * (KPS - 1)) break;
+                    const u32x4_v bf =
+                        *reinterpret_cast<const u32x4_v *>(xt + (16 * mt + m + i) * a.XP + 16 * p + 8 * g4);
+#pragma unroll
+                    for (int nt = 0; nt < NTM; ++nt) {
+                        const int d = p - nt;
+                        if (nt < a.NT && d >= 0 && (d & 1) == 0 && (d >> 1) < KPS)
+                            acc[nt] = Mfma16<T>::run(af[d >> 1], bf, acc[nt]);
+                    }
+                }
+            }
+            // 4. store: lane holds outputs (16 mt + m, 16 nt + 4 g4 + 0..3)
+            T *op = a.out + (static_cast<int64_t>(n) * a.C + c) * a.OH * a.OW;
+            const int oh = 16 * mt + m;
+            if (oh < a.OH) {
+#pragma unroll
+                for (int nt = 0; nt < NTM; ++nt) {
+                    if (nt >= a.NT) break;
+                    const int ow = 16 * nt + 4 * g4;
+                    const float v0 = acc[nt][0] + bias, v1 = acc[nt][1] + bias;
+                    const float v2 = acc[nt][2] + bias, v3 = acc[nt][3] + bias;
+                    T *dst = op + oh * a.OW + ow;
+                    if (a.vout && ow + 4 <= a.OW) {
+                        *reinterpret_cast<uint2 *>(dst) = make_uint2(pack2<T>(v0, v1), pack2<T>(v2, v3));
+                    } else {
+                        const float vv[4] = {v0, v1, v2, v3};
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            if (ow + q < a.OW) dst[q] = from_f32<T>(vv[q]);
+                    }
+                }
+            }
+        }
+        __syncthreads();  // the planes are read before the next group overwrites them
+    }
+}
+
+template <typename T, int K, bool FLIP>
+int run_lkm16(Lkm16Args<T> a, hipStream_t s) {
+    constexpr int KPS = kps16_of<K>();
+    constexpr int QD = 16 * KPS + 20;
+    constexpr int table_bytes = ((K * QD + 17 + K * QD) * 4 + 15) / 16 * 16;
+    a.MT = (a.OH + 15) / 16;
+    a.NT = (a.OW + 15) / 16;
+    a.IPG = std::max(1, 4 / a.MT);
+    a.XR = 16 * a.MT + K - 1;
+    a.XP = 16 * (a.NT - 1) + 32 * KPS + 8;
+    const int threads = 64 * a.MT * a.IPG;
+    const int lds = table_bytes + a.IPG * a.XR * a.XP * 2;
+    if (a.NT > 4 || a.MT > 4 || lds > kLdsCap) return kErrUnsupported;
+    a.ngtot = (a.N + a.IPG - 1) / a.IPG;
+    const int64_t all = static_cast<int64_t>(a.C) * a.ngtot;
+    const int gpc = K > 13 ? 1 : static_cast<int>(std::max<int64_t>(1, all / 2048));
+    a.ngroups = (a.ngtot + gpc - 1) / gpc;
+    a.gpc = (a.ngtot + a.ngroups - 1) / a.ngroups;
+    a.pre = a.vin && a.IPG * a.IH * (a.IW / 8) <= 2 * threads;
+    hipLaunchKernelGGL((lk_mfma16_kernel<T, K, FLIP>), dim3(static_cast<unsigned>(a.C * a.ngroups)), dim3(threads), lds, s,
+                       a);
+    return hipGetLastError() == hipSuccess ? kOk : kErrHip;
+}
+
+template <typename T, bool FLIP>
+int run_lkm16_k(const Lkm16Args<T> &a, int K, hipStream_t s) {
+    if (K == 7) return run_lkm16<T, 7, FLIP>(a, s);
+    if (K == 13) return run_lkm16<T, 13, FLIP>(a, s);
+    return run_lkm16<T, 31, FLIP>(a, s);
+}
+
+template <typename T>
+void fill_io16(Lkm16Args<T> &a) {
+    a.vin = a.IW % 8 == 0 && reinterpret_cast<uintptr_t>(a.in) % 16 == 0;
+    a.vout = a.OW % 4 == 0 && reinterpret_cast<uintptr_t>(a.out) % 8 == 0;
+}
+
+template <typename T>
+int lkm16_fwd_t(const Geo &g, const void *x, const void *w, const void *b, void *y, hipStream_t s) {
+    Lkm16Args<T> a{};
+    a.in = static_cast<const T *>(x);
+    a.w = static_cast<const T *>(w);
+    a.b = static_cast<const T *>(b);
+    a.out = static_cast<T *>(y);
+    a.N = g.n;
+    a.IH = g.ih;
+    a.IW = g.iw;
+    a.OH = g.oh;
+    a.OW = g.ow;
+    a.P = g.ph;
+    a.C = g.oc;
+    a.Cin = g.ic;
+    a.mult = g.mult;
+    fill_io16(a);
+    return run_lkm16_k<T, false>(a, g.kh, s);
+}
+
+template <typename T>
+int lkm16_bwdin_t(const Geo &g, const void *dy, const void *w, void *dx, hipStream_t s) {
+    Lkm16Args<T> a{};
+    a.in = static_cast<const T *>(dy);
+    a.w = static_cast<const T *>(w);
+    a.out = static_cast<T *>(dx);
+    a.N = g.n;
+    a.IH = g.oh;
+    a.IW = g.ow;
+    a.OH = g.ih;
+    a.OW = g.iw;
+    a.P = g.kh - 1 - g.ph;
+    a.C = g.ic;
+    a.Cin = g.oc;
+    a.mult = 1;
+    fill_io16(a);
+    return run_lkm16_k<T, true>(a, g.kh, s);
+}
+
+}  // namespace
+
+// The same conditions on 16 x 16 tiles (16-row / 16-column tiles of an output
+// plane of at most 64 x 64, the input inside the staged window).
+bool largek_mfma16_fits(const Geo &g, int pass, int dtype) {
+    if (dtype == 0) return false;
+    if (g.kh != g.kw || (g.kh != 7 && g.kh != 13 && g.kh != 31)) return false;
+    if (g.sh != 1 || g.sw != 1 || g.dh != 1 || g.dw != 1 || g.ph != g.pw) return false;
+    if (pass == 1 && (g.mult != 1 || g.ph > g.kh - 1)) return false;
+    const int OH = pass == 1 ? g.ih : g.oh, OW = pass == 1 ? g.iw : g.ow;
+    const int IH = pass == 1 ? g.oh : g.ih, IW = pass == 1 ? g.ow : g.iw;
+    const int P = pass == 1 ? g.kh - 1 - g.ph : g.ph;
+    if (OH < 1 || OW < 1 || OH > 64 || OW > 64) return false;
+    const int MT = (OH + 15) / 16, NT = (OW + 15) / 16;
+    const int kps = (16 + g.kh - 1 + 31) / 32;
+    const int XR = 16 * MT + g.kh - 1, XC = 16 * (NT - 1) + 32 * kps;
+    return IH + P <= XR && IW + P <= XC;
+}
+
+int largek_mfma16_fwd(const Geo &g, const void *x, const void *w, const void *b, void *y, int dtype, hipStream_t s) {
+    return dtype == 1 ? lkm16_fwd_t<__half>(g, x, w, b, y, s) : lkm16_fwd_t<bf16_t>(g, x, w, b, y, s);
+}
+
+int largek_mfma16_bwd_input(const Geo &g, const void *dy, const void *w, void *dx, int dtype, hipStream_t s) {
+    return dtype == 1 ? lkm16_bwdin_t<__half>(g, dy, w, dx, s) : lkm16_bwdin_t<bf16_t>(g, dy, w, dx, s);
+}
 
 // ---------------------------------------------------------------- grad-weight
 // dw[i][j] = sum_{n, oh, c} X[oh + i][c] * dz[oh][c - j], with X the
@@ -661,22 +974,6 @@ int run_lkmw(const Geo &g, const LkmwPlan &p, const void *x, const void *dy, voi
 //              in the bank order, so the lanes reading either copy use
 //              distinct banks);
 //   D: register r of lane l is dw[4 (l / 16) + r][l % 16].
-typedef float f32x4_v __attribute__((ext_vector_type(4)));
-
-template <typename T> struct Mfma16;
-template <> struct Mfma16<__half> {
-    static __device__ __forceinline__ f32x4_v run(u32x4_v a, u32x4_v b, f32x4_v c) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_v, a), __builtin_bit_cast(f16x8_v, b),
-                                                      c, 0, 0, 0);
-    }
-};
-template <> struct Mfma16<bf16_t> {
-    static __device__ __forceinline__ f32x4_v run(u32x4_v a, u32x4_v b, f32x4_v c) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, a),
-                                                       __builtin_bit_cast(bf16x8_v, b), c, 0, 0, 0);
-    }
-};
-
 template <int K, int CS, int BH> struct Lkmw16Geo {
     static constexpr int QD = 16 * CS + 20;         // dwords per copy of a dy row
     static constexpr int D1 = BH * QD + 17;         // dword offset of copy 1

@@ -657,12 +657,22 @@ def test_large_kernel_shapes(n, c, h, w, mult, k, p, dt):
     (1, 2, 100, 64, 1, 13, 6, "f16", False, False),   # more than 64 rows: register-tile kernels
 ])
 def test_large_kernel_mfma(n, c, h, w, mult, k, p, dt, fwd_mfma, bin_mfma):
+    """The 32 x 32-tile family (at k = 7 on planes over 32 the 16 x 16 tiles are the default, so it is forced)."""
     geo = ((n, c, h, w), (c * mult, k, k), 1, p, 1)
-    assert (dc.dwconv2d_algo(0, *geo, dtype=DT[dt]) == "largek_mfma") == fwd_mfma
-    assert (dc.dwconv2d_algo(1, *geo, dtype=DT[dt]) == "largek_mfma") == bin_mfma
+    mfma = ("largek_mfma", "largek_mfma_h16")
+    assert (dc.dwconv2d_algo(0, *geo, dtype=DT[dt]) in mfma) == fwd_mfma
+    assert (dc.dwconv2d_algo(1, *geo, dtype=DT[dt]) in mfma) == bin_mfma
     x, wt, b, dy = static_case(n, c, h, w, mult, k, 1, p, 1, DT[dt], 680 + h + w + k)
-    check_static(x, wt, b, dy, 1, p, 1, "largek-mfma n%d c%d %dx%d m%d k%d p%d %s" % (n, c, h, w, mult, k, p, dt),
-                 passes=("fwd", "bwd_in"))
+    try:
+        if fwd_mfma:
+            dc.dwconv2d_set_algo(0, *geo, dtype=DT[dt], algo="largek_mfma")
+        if bin_mfma:
+            dc.dwconv2d_set_algo(1, *geo, dtype=DT[dt], algo="largek_mfma")
+        check_static(x, wt, b, dy, 1, p, 1, "largek-mfma n%d c%d %dx%d m%d k%d p%d %s" % (n, c, h, w, mult, k, p, dt),
+                     passes=("fwd", "bwd_in"))
+    finally:
+        dc.dwconv2d_set_algo(0, *geo, dtype=DT[dt], algo=None)
+        dc.dwconv2d_set_algo(1, *geo, dtype=DT[dt], algo=None)
 
 
 @pytest.mark.parametrize("n,c,h,w,k,p,dt", [
@@ -672,11 +682,15 @@ def test_large_kernel_mfma(n, c, h, w, mult, k, p, dt, fwd_mfma, bin_mfma):
 def test_large_kernel_mfma_group_chunks(n, c, h, w, k, p, dt):
     """Workgroups that walk several image groups load the next group's planes during the matrix work."""
     geo = ((n, c, h, w), (c, k, k), 1, p, 1)
-    assert dc.dwconv2d_algo(0, *geo, dtype=DT[dt]) == "largek_mfma"
-    assert dc.dwconv2d_algo(1, *geo, dtype=DT[dt]) == "largek_mfma"
     x, wt, b, dy = static_case(n, c, h, w, 1, k, 1, p, 1, DT[dt], 690 + h + w + k)
-    check_static(x, wt, b, dy, 1, p, 1, "largek-mfma-chunks n%d c%d %dx%d k%d %s" % (n, c, h, w, k, dt),
-                 passes=("fwd", "bwd_in"))
+    try:
+        for pass_ in (0, 1):
+            dc.dwconv2d_set_algo(pass_, *geo, dtype=DT[dt], algo="largek_mfma")
+        check_static(x, wt, b, dy, 1, p, 1, "largek-mfma-chunks n%d c%d %dx%d k%d %s" % (n, c, h, w, k, dt),
+                     passes=("fwd", "bwd_in"))
+    finally:
+        for pass_ in (0, 1):
+            dc.dwconv2d_set_algo(pass_, *geo, dtype=DT[dt], algo=None)
 
 
 @pytest.mark.parametrize("n,c,h,w,k,p,dt,bw_mfma", [
@@ -952,3 +966,33 @@ def test_grad_weight_16bit_small_matrix_tiles(n, c, h, w, k, p, dt):
                      passes=("bwd_w",))
     finally:
         dc.dwconv2d_set_algo(2, *geo, dtype=DT[dt], algo=None)
+
+
+# ------------------------------------------------------------------ 16-bit large kernels on 16 x 16 matrix tiles
+@pytest.mark.parametrize("n,c,h,w,mult,k,p,dt,bin_h", [
+    (5, 2, 64, 64, 1, 31, 15, "f16", True),     # four 16-row tiles a plane, one image a group
+    (3, 3, 48, 48, 1, 31, 15, "bf16", True),    # 3 x 3 tiles
+    (6, 2, 32, 32, 1, 31, 15, "bf16", True),    # two images a group, the last group partial
+    (2, 2, 64, 64, 2, 31, 15, "f16", False),    # multiplier 2: forward only
+    (3, 2, 64, 40, 1, 13, 6, "f16", True),      # 4 x 3 tiles
+    (2, 3, 33, 36, 1, 13, 0, "bf16", True),     # no padding, rows of 36: element staging
+    (2, 2, 20, 22, 1, 13, 12, "f16", True),     # pad k - 1: grad-input pad 0
+    (4, 2, 47, 47, 1, 7, 2, "bf16", True),      # k = 7, odd sizes
+    (2, 2, 9, 9, 1, 31, 15, "f16", True),       # kernel wider than the image
+    (7, 2048, 16, 16, 1, 7, 3, "f16", True),    # two groups a workgroup: the next group's planes prefetched
+])
+def test_large_kernel_16bit_small_tiles(n, c, h, w, mult, k, p, dt, bin_h):
+    geo = ((n, c, h, w), (c * mult, k, k), 1, p, 1)
+    assert "largek_mfma_h16" in dc.dwconv2d_algo_candidates(0, *geo, dtype=DT[dt])
+    assert ("largek_mfma_h16" in dc.dwconv2d_algo_candidates(1, *geo, dtype=DT[dt])) == bin_h
+    x, wt, b, dy = static_case(n, c, h, w, mult, k, 1, p, 1, DT[dt], 1900 + h + w + k + p)
+    try:
+        dc.dwconv2d_set_algo(0, *geo, dtype=DT[dt], algo="largek_mfma_h16")
+        if bin_h:
+            dc.dwconv2d_set_algo(1, *geo, dtype=DT[dt], algo="largek_mfma_h16")
+        check_static(x, wt, b, dy, 1, p, 1, "largek-h16 n%d c%d %dx%d m%d k%d p%d %s" % (n, c, h, w, mult, k, p, dt),
+                     passes=("fwd", "bwd_in") if bin_h else ("fwd",))
+    finally:
+        dc.dwconv2d_set_algo(0, *geo, dtype=DT[dt], algo=None)
+        if bin_h:
+            dc.dwconv2d_set_algo(1, *geo, dtype=DT[dt], algo=None)
