@@ -94,6 +94,9 @@ def test_ceiling_model():
     assert abs(bench.ceiling_of("fwd.x.k3", "bytes", 0.75, ceil)[0] - 5500.0) < 1e-9
     assert bench.ceiling_of("bwd_weight.largek_mfma_f32.k31_s1_m1_f32", "flops", 1, ceil)[0] == 140.0
     assert bench.ceiling_of("fwd.largek_mfma.k31_s1_m1_f16", "flops", 1, ceil)[0] == 2000.0
+    assert bench.ceiling_of("bwd_weight.largek_mfma_h16.k13_s1_m1_f16", "flops", 1, ceil)[0] == 2000.0
+    assert bench.ceiling_of("fwd.largek_mfma_h16.k7_s1_m1_bf16", "flops", 1, ceil)[0] == 2000.0
+    assert bench.ceiling_of("bwd_weight.stream_7x7.k7_s1_m1_f16", "flops", 1, ceil)[0] == 100.0
     assert bench.ceiling_of("fwd.largek_regtile.k13_s1_m1_f32", "flops", 1, ceil)[0] == 100.0
     assert bench.ceiling_of("bwd_weight.largek_mfma_t16.k13_s1_m1_f32", "flops", 1, ceil)[0] == 140.0
     assert bench.ceiling_of("fwd.x", "bytes", 0.5, None) is None
