@@ -34,7 +34,7 @@ namespace {
 
 typedef float f32x4_w __attribute__((ext_vector_type(4)));
 
-constexpr int kW16Off = 15;      // dz column of dy column -P (so m - j + 15 indexes dz directly)
+constexpr int kW16Off = 15;      // largest kernel column reach left of a dy column
 constexpr int kW16TargetWG = 6144;
 
 template <typename T> struct Lw16Args {
@@ -46,7 +46,9 @@ template <typename T> struct Lw16Args {
     int BH, nbands; // dy rows per band, bands per plane
     int XW;         // x columns the instructions walk: iw rounded up to 16
     int XP;         // LDS pitch of an x row: XW + 4 (the 16 rows a read touches in distinct banks)
-    int L;          // LDS pitch of a dz row: XW + 16
+    int L;          // LDS pitch of a dz row: XW + 20
+    int D0;         // dz column of dy column 0: 15 - P rounded up to a multiple of 4
+                    // (16-byte stores; the B reads start at D0 + P - 15 >= 0)
     int vx, vd;     // x / dy rows are whole aligned 16-byte vectors
 };
 
@@ -73,9 +75,11 @@ __device__ __forceinline__ void stage_f32(float *dst, int pitch, const T *src, i
             } raw;
             raw.u = make_uint4(0u, 0u, 0u, 0u);
             if (ih >= 0 && ih < h) raw.u = *reinterpret_cast<const uint4 *>(src + static_cast<int64_t>(ih) * w + c0);
-            float *d = dst + r * pitch + c0;
+            float4 *d = reinterpret_cast<float4 *>(dst + r * pitch + c0);
 #pragma unroll
-            for (int e = 0; e < VE; ++e) d[e] = to_f32(raw.t[e]);
+            for (int e = 0; e < VE / 4; ++e)
+                d[e] = make_float4(to_f32(raw.t[4 * e]), to_f32(raw.t[4 * e + 1]), to_f32(raw.t[4 * e + 2]),
+                                   to_f32(raw.t[4 * e + 3]));
         }
     } else {
         for (int e = tid; e < nrows * w; e += 256) {
@@ -158,7 +162,7 @@ __global__ __launch_bounds__(256) void lk_wgrad16_kernel(Lw16Args<T> a) {
             const int oh0 = band * a.BH;
             const int rows = min(a.BH, a.OH - oh0);
             __syncthreads();  // the previous band's reads are done
-            // staged x row r is image row oh0 + r - P; dy row r sits at dz column kW16Off - P
+            // staged x row r is image row oh0 + r - P; dy row r sits at dz column D0
             if constexpr (PF) {
                 const int xv = a.IW / VE, dv = a.OW / VE;
 #pragma unroll
@@ -171,9 +175,11 @@ __global__ __launch_bounds__(256) void lk_wgrad16_kernel(Lw16Args<T> a) {
                             T t[VE];
                         } raw;
                         raw.u = pfx[k];
-                        float *d = xs + r * a.XP + (v - r * xv) * VE;
+                        float4 *d = reinterpret_cast<float4 *>(xs + r * a.XP + (v - r * xv) * VE);
 #pragma unroll
-                        for (int e = 0; e < VE; ++e) d[e] = to_f32(raw.t[e]);
+                        for (int e = 0; e < VE / 4; ++e)
+                            d[e] = make_float4(to_f32(raw.t[4 * e]), to_f32(raw.t[4 * e + 1]), to_f32(raw.t[4 * e + 2]),
+                                               to_f32(raw.t[4 * e + 3]));
                     }
                 }
 #pragma unroll
@@ -186,26 +192,28 @@ __global__ __launch_bounds__(256) void lk_wgrad16_kernel(Lw16Args<T> a) {
                             T t[VE];
                         } raw;
                         raw.u = pfd[k];
-                        float *d = dz + kW16Off - a.P + r * a.L + (v - r * dv) * VE;
+                        float4 *d = reinterpret_cast<float4 *>(dz + a.D0 + r * a.L + (v - r * dv) * VE);
 #pragma unroll
-                        for (int e = 0; e < VE; ++e) d[e] = to_f32(raw.t[e]);
+                        for (int e = 0; e < VE / 4; ++e)
+                            d[e] = make_float4(to_f32(raw.t[4 * e]), to_f32(raw.t[4 * e + 1]), to_f32(raw.t[4 * e + 2]),
+                                               to_f32(raw.t[4 * e + 3]));
                     }
                 }
             } else {
                 stage_f32<T>(xs, a.XP, xp, oh0 - a.P, rows + K - 1, a.IH, a.IW, a.vx != 0, tid);
-                stage_f32<T>(dz + kW16Off - a.P, a.L, dp, oh0, rows, a.OH, a.OW, a.vd != 0, tid);
+                stage_f32<T>(dz + a.D0, a.L, dp, oh0, rows, a.OH, a.OW, a.vd != 0, tid);
             }
             __syncthreads();
             if (PF && t + 1 < nsteps) prefetch(t + 1);
             // bias gradient: the band's dy values, summed per thread in a fixed order
             for (int e = tid; e < rows * a.OW; e += 256) {
                 const int r = e / a.OW;
-                dsum += dz[r * a.L + kW16Off - a.P + (e - r * a.OW)];
+                dsum += dz[r * a.L + a.D0 + (e - r * a.OW)];
             }
             for (int oh = wave; oh < rows; oh += 4) {
                 // A: x row oh + i, column base + 4 kq + t; B: dz[oh][base + 4 kq + t - j + 15]
                 const float *xr = xs + (oh + mi) * a.XP + 4 * kq;
-                const float *dr = dz + oh * a.L + kW16Off - mj + 4 * kq;
+                const float *dr = dz + oh * a.L + a.D0 + a.P - mj + 4 * kq;
                 for (int base = 0; base < a.XW; base += 16) {
                     const float4 av = *reinterpret_cast<const float4 *>(xr + base);
                     const float b0 = dr[base], b1 = dr[base + 1], b2 = dr[base + 2], b3 = dr[base + 3];
@@ -246,7 +254,7 @@ struct Lw16Plan {
 bool plan_lw16(const Geo &g, Lw16Plan &p) {
     p.XW = (g.iw + 15) & ~15;
     p.XP = p.XW + 4;
-    p.L = p.XW + 16;
+    p.L = p.XW + 20;
     const int K = g.kh;
     auto bytes = [&](int bh) {
         const int64_t stage = (static_cast<int64_t>(bh + K - 1) * p.XP + static_cast<int64_t>(bh) * p.L) * 4;
@@ -287,6 +295,7 @@ int run_lw16(const Geo &g, const Lw16Plan &p, const void *x, const void *dy, voi
     a.XW = p.XW;
     a.XP = p.XP;
     a.L = p.L;
+    a.D0 = (kW16Off - g.ph + 3) & ~3;
     a.vx = g.iw % Vec<T>::N == 0 && reinterpret_cast<uintptr_t>(x) % 16 == 0;
     a.vd = g.ow % Vec<T>::N == 0 && reinterpret_cast<uintptr_t>(dy) % 16 == 0;
     // register prefetch for whole-vector rows of at most kW16PfCols elements
