@@ -71,7 +71,7 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 template <typename T, int K, int NCT, bool FLIP>
-__global__ __launch_bounds__(256, 4) void lk_fwd32_kernel(Lf32Args<T> a) {
+__global__ __launch_bounds__(256, 6) void lk_fwd32_kernel(Lf32Args<T> a) {
     constexpr int XP = 32 * NCT;  // LDS pitch of a staged input row
     constexpr int NS = 16;  // instructions per 32-column tile: kernel rows 2s, 2s + 1
     static_assert(K <= 2 * NS, "one 32-row contraction covers the filter");
@@ -144,9 +144,11 @@ __global__ __launch_bounds__(256, 4) void lk_fwd32_kernel(Lf32Args<T> a) {
                 }
             }
             __syncthreads();
-            // this wave's items: output row wave + 4 (q / NCT), column tile q % NCT.
-            // Item q + 1's instructions are issued before item q's diagonal sums,
-            // so the matrix cores work while the vector units and LDS reduce.
+            // this wave's items: output row wave + 4 (q / NCT), column tile q % NCT,
+            // each issued and then reduced: one accumulator and B operands read
+            // four at a time keep the kernel at 71 VGPRs, seven waves per SIMD,
+            // whose matrix work covers the others' reductions (8-10 % faster than
+            // issuing item q + 1 before reducing item q at four waves per SIMD).
             const int nq = (rows > wave ? (rows - wave + 3) / 4 : 0) * NCT;
             auto issue = [&](f32x16_f &acc, int q) {
                 const int r = wave + 4 * (q / NCT), ct = q % NCT;
@@ -154,16 +156,20 @@ __global__ __launch_bounds__(256, 4) void lk_fwd32_kernel(Lf32Args<T> a) {
                 // kernel rows whose input row is inside the image; pairs with neither are skipped
                 const int i_lo = max(0, a.P - oh), i_hi = min(K, a.IH + a.P - oh);
                 const int s_lo = i_lo >> 1, s_hi = (i_hi + 1) >> 1;
-                // B operands of all 16 instructions read first (every row is in the staged band)
+                // every B operand row is in the staged band
                 const float *bp = xs + (r + h) * XP + 32 * ct + jl;
-                float bv[NS];
-#pragma unroll
-                for (int u = 0; u < NS; ++u) bv[u] = bp[2 * u * XP];
 #pragma unroll
                 for (int u = 0; u < 16; ++u) acc[u] = 0.f;
+                // B operands read four at a time (fewer live registers)
 #pragma unroll
-                for (int u = 0; u < NS; ++u)
-                    if (u >= s_lo && u < s_hi) acc = mfma_f32(wreg[u], bv[u], acc);
+                for (int u0 = 0; u0 < NS; u0 += 4) {
+                    float bv[4];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) bv[k] = bp[2 * (u0 + k) * XP];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        if (u0 + k >= s_lo && u0 + k < s_hi) acc = mfma_f32(wreg[u0 + k], bv[k], acc);
+                }
             };
             auto reduce = [&](const f32x16_f &acc, int q) {
                 const int r = wave + 4 * (q / NCT), ct = q % NCT;
@@ -202,15 +208,10 @@ __global__ __launch_bounds__(256, 4) void lk_fwd32_kernel(Lf32Args<T> a) {
                     wave_lds_sync();
                 }
             };
-            f32x16_f acc_a, acc_b;
-            if (nq > 0) issue(acc_a, 0);
-            for (int q = 0; q < nq; q += 2) {
-                if (q + 1 < nq) issue(acc_b, q + 1);
+            f32x16_f acc_a;
+            for (int q = 0; q < nq; ++q) {
+                issue(acc_a, q);
                 reduce(acc_a, q);
-                if (q + 1 < nq) {
-                    if (q + 2 < nq) issue(acc_a, q + 2);
-                    reduce(acc_b, q + 1);
-                }
             }
         }
     }
@@ -246,7 +247,7 @@ __device__ __forceinline__ float rowsum4(float v) {
 }
 
 template <typename T, int K, int NCT, bool FLIP>
-__global__ __launch_bounds__(256, 4) void lk_fwd16t_kernel(Lf32Args<T> a) {
+__global__ __launch_bounds__(256, 8) void lk_fwd16t_kernel(Lf32Args<T> a) {
     constexpr int XP = 16 * NCT;  // LDS pitch of a staged input row
     constexpr int NU = 8;          // instructions per tile half: kernel rows 4u .. 4u + 3
     static_assert(K <= 4 * NU, "one 32-row contraction covers the filter");
@@ -317,8 +318,8 @@ __global__ __launch_bounds__(256, 4) void lk_fwd16t_kernel(Lf32Args<T> a) {
                 }
             }
             __syncthreads();
-            // items: output row wave + 4 (q / NCT), 16-column tile q % NCT; item q + 1's
-            // instructions are issued before item q's diagonal sums
+            // items: output row wave + 4 (q / NCT), 16-column tile q % NCT, each
+            // issued and then reduced (53 VGPRs: eight waves per SIMD)
             const int nq = (rows > wave ? (rows - wave + 3) / 4 : 0) * NCT;
             auto issue = [&](f32x4_f &d0, f32x4_f &d1, int q) {
                 const int r = wave + 4 * (q / NCT), ct = q % NCT;
@@ -326,17 +327,20 @@ __global__ __launch_bounds__(256, 4) void lk_fwd16t_kernel(Lf32Args<T> a) {
                 const int i_lo = max(0, a.P - oh), i_hi = min(K, a.IH + a.P - oh);
                 const int u_lo = i_lo >> 2, u_hi = (i_hi + 3) >> 2;
                 const float *bp = xs + (r + g) * XP + 16 * ct + t;
-                float bv[NU];
-#pragma unroll
-                for (int u = 0; u < NU; ++u) bv[u] = bp[4 * u * XP];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) d0[e] = d1[e] = 0.f;
 #pragma unroll
-                for (int u = 0; u < NU; ++u)
-                    if (u >= u_lo && u < u_hi) {
-                        d0 = mfma_f32x16(wreg[0][u], bv[u], d0);
-                        d1 = mfma_f32x16(wreg[1][u], bv[u], d1);
-                    }
+                for (int u0 = 0; u0 < NU; u0 += 4) {
+                    float bv[4];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) bv[k] = bp[4 * (u0 + k) * XP];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        if (u0 + k >= u_lo && u0 + k < u_hi) {
+                            d0 = mfma_f32x16(wreg[0][u0 + k], bv[k], d0);
+                            d1 = mfma_f32x16(wreg[1][u0 + k], bv[k], d1);
+                        }
+                }
             };
             auto reduce = [&](const f32x4_f &d0, const f32x4_f &d1, int q) {
                 const int r = wave + 4 * (q / NCT), ct = q % NCT;
@@ -373,15 +377,10 @@ __global__ __launch_bounds__(256, 4) void lk_fwd16t_kernel(Lf32Args<T> a) {
                     wave_lds_sync();
                 }
             };
-            f32x4_f a0, a1, b0, b1;
-            if (nq > 0) issue(a0, a1, 0);
-            for (int q = 0; q < nq; q += 2) {
-                if (q + 1 < nq) issue(b0, b1, q + 1);
+            f32x4_f a0, a1;
+            for (int q = 0; q < nq; ++q) {
+                issue(a0, a1, q);
                 reduce(a0, a1, q);
-                if (q + 1 < nq) {
-                    if (q + 2 < nq) issue(a0, a1, q + 2);
-                    reduce(b0, b1, q + 1);
-                }
             }
         }
     }
