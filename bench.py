@@ -129,12 +129,16 @@ def valid_taps(in_n, out_n, k, s, p, d):
     return tot
 
 
+# kernel families that run 16-bit I/O on the matrix cores (tag infixes)
+MATRIX16_FAMILIES = (".largek_mfma.", ".largek_mfma_h16.", ".largek_roll16.")
+
+
 def tag_peak(tag, kind):
     """(bound, peak, unit) of a kernel tag: HBM for bandwidth-bound workloads; for
     flop-counted ones the matrix-core peak of 16-bit I/O on the matrix cores, else fp32."""
     if kind == "bytes":
         return "hbm", HBM_PEAK_GBS, "GB/s"
-    matrix16 = (".largek_mfma." in tag or ".largek_mfma_h16." in tag) and not tag.endswith("_f32")
+    matrix16 = any(f in tag for f in MATRIX16_FAMILIES) and not tag.endswith("_f32")
     return ("mfma", F16_MATRIX_PEAK_TFLOPS, "TFLOP/s") if matrix16 else ("alu", FP32_PEAK_TFLOPS, "TFLOP/s")
 
 
@@ -388,7 +392,7 @@ def ceiling_of(tag, kind, rfrac, ceil):
         else:
             v = ceil["write_gbs"] + (ceil["copy_gbs"] - ceil["write_gbs"]) * rfrac / 0.5
         return v, "GB/s", "stream (read share %.2f)" % rfrac
-    if (".largek_mfma." in tag or ".largek_mfma_h16." in tag) and not tag.endswith("_f32"):
+    if any(f in tag for f in MATRIX16_FAMILIES) and not tag.endswith("_f32"):
         return ceil["mfma_f16_tflops"], "TFLOP/s", "fp16 matrix instructions"
     if ".largek_mfma_f32." in tag or ".largek_mfma_t16." in tag:
         return ceil["mfma_f32_tflops"], "TFLOP/s", "fp32 matrix instructions"

@@ -33,13 +33,21 @@ FLAGS = [
 ]
 
 
+# Per-source code generation options: the row-streaming 16-bit kernels keep
+# their matrix accumulators in ordinary VGPRs (their bookkeeping moves single
+# accumulator elements, which the AGPR form turns into register copies).
+EXTRA_FLAGS = {
+    "dw_largek_roll16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC] + FLAGS + ["-c", src, "-o", obj]
+    cmd = [HIPCC] + FLAGS + EXTRA_FLAGS.get(os.path.basename(src), []) + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s" % (src, r.stdout))

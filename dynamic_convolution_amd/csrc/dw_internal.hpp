@@ -86,6 +86,11 @@ int largek_mfma_bwd_input(const Geo &g, const void *dy, const void *w, void *dx,
 bool largek_mfma16_fits(const Geo &g, int pass, int dtype);
 int largek_mfma16_fwd(const Geo &g, const void *x, const void *w, const void *b, void *y, int dtype, hipStream_t s);
 int largek_mfma16_bwd_input(const Geo &g, const void *dy, const void *w, void *dx, int dtype, hipStream_t s);
+// 16-bit k = 31 forward / grad-input streaming input rows through rotating
+// filter rows on the matrix cores (dw_largek_roll16.hip); any plane size.
+bool largek_roll16_fits(const Geo &g, int pass, int dtype);
+int largek_roll16_fwd(const Geo &g, const void *x, const void *w, const void *b, void *y, int dtype, hipStream_t s);
+int largek_roll16_bwd_input(const Geo &g, const void *dy, const void *w, void *dx, int dtype, hipStream_t s);
 // Grad-weight pass 1 of the same family (k = 13, 31; multiplier 1; dy rows <= 64):
 // workspace [ic][chunks][k*k + 1].
 bool largek_mfma_bwdw_fits(const Geo &g, int dtype);

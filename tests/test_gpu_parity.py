@@ -659,7 +659,7 @@ def test_large_kernel_shapes(n, c, h, w, mult, k, p, dt):
 def test_large_kernel_mfma(n, c, h, w, mult, k, p, dt, fwd_mfma, bin_mfma):
     """The 32 x 32-tile family (at k = 7 on planes over 32 the 16 x 16 tiles are the default, so it is forced)."""
     geo = ((n, c, h, w), (c * mult, k, k), 1, p, 1)
-    mfma = ("largek_mfma", "largek_mfma_h16")
+    mfma = ("largek_mfma", "largek_mfma_h16", "largek_roll16")
     assert (dc.dwconv2d_algo(0, *geo, dtype=DT[dt]) in mfma) == fwd_mfma
     assert (dc.dwconv2d_algo(1, *geo, dtype=DT[dt]) in mfma) == bin_mfma
     x, wt, b, dy = static_case(n, c, h, w, mult, k, 1, p, 1, DT[dt], 680 + h + w + k)
@@ -995,4 +995,43 @@ def test_large_kernel_16bit_small_tiles(n, c, h, w, mult, k, p, dt, bin_h):
     finally:
         dc.dwconv2d_set_algo(0, *geo, dtype=DT[dt], algo=None)
         if bin_h:
+            dc.dwconv2d_set_algo(1, *geo, dtype=DT[dt], algo=None)
+
+
+# 16-bit 31 x 31 forward / grad-input streaming input rows through rotating
+# filter rows (forced family): the large-kernel workload's planes, odd and
+# element-staged widths, several column chunks with a ragged last one, pad 0
+# and pad k - 1, a multiplier, a kernel wider than the image, input heights
+# that are not a multiple of 4, and enough planes that each wave walks two images.
+@pytest.mark.gpu
+@pytest.mark.parametrize("n,c,h,w,mult,p,dt,bin_ok", [
+    (2, 3, 32, 32, 1, 15, "f16", True),
+    (2, 2, 48, 48, 1, 15, "bf16", True),
+    (2, 2, 64, 64, 1, 15, "f16", True),
+    (1, 2, 47, 47, 1, 15, "f16", True),     # element staging, ragged 16-column tile
+    (2, 1, 33, 29, 1, 15, "bf16", True),
+    (1, 2, 21, 150, 1, 15, "f16", True),    # three column chunks, the last ragged
+    (1, 1, 12, 264, 1, 15, "bf16", True),   # five chunks, vector staging
+    (2, 2, 40, 40, 1, 0, "f16", True),      # pad 0: grad-input pad 30
+    (2, 2, 26, 22, 1, 30, "bf16", True),    # pad k - 1: grad-input pad 0
+    (2, 2, 30, 34, 2, 15, "f16", False),    # multiplier 2 (forward only)
+    (2, 2, 9, 9, 1, 15, "bf16", True),      # kernel wider than the image
+    (1, 2, 5, 70, 1, 15, "f16", True),      # fewer input rows than one batch of four
+    (8, 2048, 16, 16, 1, 15, "f16", True),  # two images a wave
+])
+def test_large_kernel_row_stream_16bit(n, c, h, w, mult, p, dt, bin_ok):
+    k = 31
+    geo = ((n, c, h, w), (c * mult, k, k), 1, p, 1)
+    assert "largek_roll16" in dc.dwconv2d_algo_candidates(0, *geo, dtype=DT[dt])
+    assert ("largek_roll16" in dc.dwconv2d_algo_candidates(1, *geo, dtype=DT[dt])) == bin_ok
+    x, wt, b, dy = static_case(n, c, h, w, mult, k, 1, p, 1, DT[dt], 2300 + h + w + p + mult)
+    try:
+        dc.dwconv2d_set_algo(0, *geo, dtype=DT[dt], algo="largek_roll16")
+        if bin_ok:
+            dc.dwconv2d_set_algo(1, *geo, dtype=DT[dt], algo="largek_roll16")
+        check_static(x, wt, b, dy, 1, p, 1, "largek-roll16 n%d c%d %dx%d m%d p%d %s" % (n, c, h, w, mult, p, dt),
+                     passes=("fwd", "bwd_in") if bin_ok else ("fwd",))
+    finally:
+        dc.dwconv2d_set_algo(0, *geo, dtype=DT[dt], algo=None)
+        if bin_ok:
             dc.dwconv2d_set_algo(1, *geo, dtype=DT[dt], algo=None)
