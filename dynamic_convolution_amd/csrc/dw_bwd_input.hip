@@ -287,7 +287,7 @@ int select_bwd_input(const Geo &g, int dt) {
     // 16-bit k = 7 planes wider or taller than 32: 16 x 16 tiles measured ~5 % faster
     if (g.kh == 7 && (g.ih > 32 || g.iw > 32) && largek_mfma16_fits(g, 1, dt)) return kBinLargekMfmaH16;
     // 16-bit 31 x 31: input rows streamed through rotating filter rows
-    if (largek_roll16_fits(g, 1, dt)) return kBinLargekRoll16;
+    if (g.kh == 31 && largek_roll16_fits(g, 1, dt)) return kBinLargekRoll16;
     if (largek_mfma_fits(g, 1, dt)) return kBinLargekMfma;
     if (largek_fwd32_fits(g, 1, dt) && largek_fwd32_preferred(g, 1)) return kBinLargekMfma32;
     if (largek_fits(g, 1)) return kBinLargek;

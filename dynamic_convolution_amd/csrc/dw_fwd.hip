@@ -287,7 +287,7 @@ int select_fwd(const Geo &g, int dt) {
     // 16-bit k = 7 planes wider or taller than 32: 16 x 16 tiles measured ~10 % faster
     if (g.kh == 7 && (g.oh > 32 || g.ow > 32) && largek_mfma16_fits(g, 0, dt)) return kFwdLargekMfmaH16;
     // 16-bit 31 x 31: input rows streamed through rotating filter rows
-    if (largek_roll16_fits(g, 0, dt)) return kFwdLargekRoll16;
+    if (g.kh == 31 && largek_roll16_fits(g, 0, dt)) return kFwdLargekRoll16;
     if (largek_mfma_fits(g, 0, dt)) return kFwdLargekMfma;
     if (largek_fwd32_fits(g, 0, dt) && largek_fwd32_preferred(g, 0)) return kFwdLargekMfma32;
     if (largek_fits(g, 0)) return kFwdLargek;

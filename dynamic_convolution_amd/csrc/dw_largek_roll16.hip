@@ -62,7 +62,6 @@ template <> struct RollMfma<bf16_t> {
 };
 
 constexpr int kR16K = 31;     // filter size this family serves
-constexpr int kR16Slots = 8;  // ring rows per wave: two batches of four
 
 template <typename T> struct Lr16Args {
     const T *in;  // forward: x; grad-input: dy
@@ -88,43 +87,47 @@ template <typename T> struct Lr16Args {
 // d - d' = D1 mod 32; 32 lanes whose runs start at 32 consecutive positions
 // give d - d' in [-15, 15] (even first position) or [-14, 16] (odd), so copy 1
 // starts at a dword = 16 mod 32, one dword later for an odd first position.
-template <int K, int NT> struct Lr16Geo {
+template <int K, int NT, int NSLOT> struct Lr16Geo {
+    static constexpr int SLOTS = NSLOT;   // ring rows (input rows in flight)
+    static constexpr int RS = SLOTS + 1;  // ring stride: dword d of slot k at RS d + k (RS odd)
+    static_assert(SLOTS == 8 || SLOTS == 16, "two or four batches of four rows");
     static constexpr int XW = 16 * NT + K - 1;
     static constexpr int XP = (XW + 23 + 7) / 8 * 8;
     static constexpr int D1 = (XP / 2 + 1 + 15) / 32 * 32 + 16;  // copy 1's first dword (+1 for an odd start)
     static constexpr int ROWD = D1 + 1 + XP / 2;  // dwords of a staged row, both copies
-    static constexpr int RING = 9 * ROWD;     // dwords of a wave's ring
+    static constexpr int RING = RS * ROWD;    // dwords of a wave's ring
     static constexpr int NVEC = (XW + 7 + 7) / 8;  // 8-column vectors a row may need
     static_assert(NVEC <= 16, "a staged row is loaded by 16 lanes");
-    static_assert(kR16Slots <= 9, "slots interleave within 9 dwords");
     static constexpr int lds_bytes = 4 * RING * 4;
 };
 
 // Ring dword of the lane's B-operand run starting at staged position s0
 // (copy 1 from dword d1).
-__device__ __forceinline__ int ring_run(int s0, int d1) { return 9 * ((s0 & 1) ? d1 + ((s0 - 1) >> 1) : (s0 >> 1)); }
+template <int RS> __device__ __forceinline__ int ring_run(int s0, int d1) {
+    return RS * ((s0 & 1) ? d1 + ((s0 - 1) >> 1) : (s0 >> 1));
+}
 
 // Stages one 8-value vector (raw, staged positions 8 sk .. 8 sk + 7) of slot k:
 // copy 0, and copy 1 from dword d1 (its position q holds copy-0 position q + 1).
-__device__ __forceinline__ void ring_put_vec(uint32_t *ring, int d1, int k, int sk, const uint4 &raw) {
-    uint32_t *p0 = ring + 9 * (4 * sk) + k;
+template <int RS> __device__ __forceinline__ void ring_put_vec(uint32_t *ring, int d1, int k, int sk, const uint4 &raw) {
+    uint32_t *p0 = ring + RS * (4 * sk) + k;
     p0[0] = raw.x;
-    p0[9] = raw.y;
-    p0[18] = raw.z;
-    p0[27] = raw.w;
-    uint32_t *p1 = ring + 9 * (d1 + 4 * sk) + k;
-    reinterpret_cast<uint16_t *>(p1 - 9)[1] = static_cast<uint16_t>(raw.x);  // position 8 sk - 1
+    p0[RS] = raw.y;
+    p0[2 * RS] = raw.z;
+    p0[3 * RS] = raw.w;
+    uint32_t *p1 = ring + RS * (d1 + 4 * sk) + k;
+    reinterpret_cast<uint16_t *>(p1 - RS)[1] = static_cast<uint16_t>(raw.x);  // position 8 sk - 1
     p1[0] = __builtin_amdgcn_alignbit(raw.y, raw.x, 16);
-    p1[9] = __builtin_amdgcn_alignbit(raw.z, raw.y, 16);
-    p1[18] = __builtin_amdgcn_alignbit(raw.w, raw.z, 16);
-    reinterpret_cast<uint16_t *>(p1 + 27)[0] = static_cast<uint16_t>(raw.w >> 16);  // position 8 sk + 6
+    p1[RS] = __builtin_amdgcn_alignbit(raw.z, raw.y, 16);
+    p1[2 * RS] = __builtin_amdgcn_alignbit(raw.w, raw.z, 16);
+    reinterpret_cast<uint16_t *>(p1 + 3 * RS)[0] = static_cast<uint16_t>(raw.w >> 16);  // position 8 sk + 6
 }
 
 // Stages one value at staged position p of slot k (both copies).
-__device__ __forceinline__ void ring_put_one(uint32_t *ring, int d1, int k, int p, uint16_t v) {
-    reinterpret_cast<uint16_t *>(ring + 9 * (p >> 1) + k)[p & 1] = v;
+template <int RS> __device__ __forceinline__ void ring_put_one(uint32_t *ring, int d1, int k, int p, uint16_t v) {
+    reinterpret_cast<uint16_t *>(ring + RS * (p >> 1) + k)[p & 1] = v;
     const int q = 2 * d1 + p - 1;
-    reinterpret_cast<uint16_t *>(ring + 9 * (q >> 1) + k)[q & 1] = v;
+    reinterpret_cast<uint16_t *>(ring + RS * (q >> 1) + k)[q & 1] = v;
 }
 
 // Orders this wave's LDS accesses: its earlier LDS operations complete before
@@ -153,7 +156,7 @@ __device__ __forceinline__ uint16_t bits16(float v, bf16_t *) { return from_f32<
 
 template <typename T, int K, int NT, bool FLIP, bool VIN>
 __global__ __launch_bounds__(256) void lk_roll16_kernel(Lr16Args<T> a) {
-    using G = Lr16Geo<K, NT>;
+    using G = Lr16Geo<K, NT, 8>;
     constexpr int NB = (K + 15) / 16;  // 16-row blocks of kernel rows
     extern __shared__ __align__(16) unsigned char smem[];
     const int tid = threadIdx.x;
@@ -180,7 +183,7 @@ __global__ __launch_bounds__(256) void lk_roll16_kernel(Lr16Args<T> a) {
     // B operand: staged position s = AL + 16 t + n + 8 g; odd runs read copy 1
     const int s0 = AL + n + 8 * g;
     const int d1 = G::D1 + (AL & 1);  // copy 1's first dword
-    const int boff = ring_run(s0, d1);
+    const int boff = ring_run<G::RS>(s0, d1);
     // staging: lane = (row of the batch, 8-column vector)
     const int sk = lane & 15;
     const int gc = cb8 + 8 * sk;
@@ -242,7 +245,7 @@ __global__ __launch_bounds__(256) void lk_roll16_kernel(Lr16Args<T> a) {
             raw = make_uint4(v[0], v[1], v[2], v[3]);
         };
         auto write_batch = [&](int qb) {
-            if (vk) ring_put_vec(ring, d1, (4 * qb + (lane >> 4)) & (kR16Slots - 1), sk, raw);
+            if (vk) ring_put_vec<G::RS>(ring, d1, (4 * qb + (lane >> 4)) & (G::SLOTS - 1), sk, raw);
         };
         // element-wise staging (rows that are not whole aligned vectors)
         auto stage_scalar = [&](int qb) {
@@ -254,7 +257,7 @@ __global__ __launch_bounds__(256) void lk_roll16_kernel(Lr16Args<T> a) {
                 const int col = cb8 + p;
                 if (col < 0 || col >= a.IW) continue;
                 const uint16_t v = r < a.IH ? ip[static_cast<int64_t>(r) * a.IW + col] : uint16_t{0};
-                ring_put_one(ring, d1, (4 * qb + q) & (kR16Slots - 1), p, v);
+                ring_put_one<G::RS>(ring, d1, (4 * qb + q) & (G::SLOTS - 1), p, v);
             }
         };
 
@@ -269,12 +272,12 @@ __global__ __launch_bounds__(256) void lk_roll16_kernel(Lr16Args<T> a) {
         auto step = [&](auto rr_c, int v) {
             constexpr int rr = decltype(rr_c)::value;
             // B operands first: their LDS latency overlaps the accumulator bookkeeping
-            const uint32_t *bp = ring + boff + (v & (kR16Slots - 1));
+            const uint32_t *bp = ring + boff + (v & (G::SLOTS - 1));
             u32x4_r bv[NT];
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
-                const uint32_t *q = bp + 9 * 8 * t;
-                bv[t] = u32x4_r{q[0], q[9], q[18], q[27]};
+                const uint32_t *q = bp + G::RS * 8 * t;
+                bv[t] = u32x4_r{q[0], q[G::RS], q[2 * G::RS], q[3 * G::RS]};
             }
             // accumulator row v mod 16 (register rr of lane row (v / 4) mod 4): the
             // last block's output row v + P - 16 NB is complete, each block takes
@@ -376,7 +379,7 @@ template <> struct RollMfma32<bf16_t> {
 template <typename T, int K, int NT, bool FLIP, bool VIN>
 __global__ __launch_bounds__(256) void lk_roll32_kernel(Lr16Args<T> a) {
     static_assert(K > 16 && K <= 32, "two 16-row blocks of kernel rows");
-    using G = Lr16Geo<K, 2 * NT>;
+    using G = Lr16Geo<K, 2 * NT, 8>;
     extern __shared__ __align__(16) unsigned char smem[];
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -402,7 +405,7 @@ __global__ __launch_bounds__(256) void lk_roll32_kernel(Lr16Args<T> a) {
     // B operand of instruction s: staged position AL + 32 t + 16 s + n + 8 h
     const int s0 = AL + n + 8 * h;
     const int d1 = G::D1 + (AL & 1);  // copy 1's first dword
-    const int boff = ring_run(s0, d1);
+    const int boff = ring_run<G::RS>(s0, d1);
     const int sk = lane & 15;
     const int gc = cb8 + 8 * sk;
     const bool vk = sk < G::NVEC && gc >= 0 && gc + 8 <= a.IW;
@@ -455,15 +458,14 @@ __global__ __launch_bounds__(256) void lk_roll32_kernel(Lr16Args<T> a) {
         // batch is written to the ring
         const __amdgpu_buffer_rsrc_t irsrc =
             __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(ip), 0, static_cast<int>(iplane * 2), 0x00020000);
-        uint4 raw = make_uint4(0u, 0u, 0u, 0u);
-        auto load_batch = [&](int qb) {
+        auto load_batch = [&](int qb) -> uint4 {
             const int r = 4 * qb + (lane >> 4);
             const int off = (vk && r < a.IH) ? (r * a.IW + gc) * 2 : kR16Skip;
             const u32x4_r v = __builtin_amdgcn_raw_buffer_load_b128(irsrc, off, 0, 0);
-            raw = make_uint4(v[0], v[1], v[2], v[3]);
+            return make_uint4(v[0], v[1], v[2], v[3]);
         };
-        auto write_batch = [&](int qb) {
-            if (vk) ring_put_vec(ring, d1, (4 * qb + (lane >> 4)) & (kR16Slots - 1), sk, raw);
+        auto write_batch = [&](int qb, const uint4 &raw) {
+            if (vk) ring_put_vec<G::RS>(ring, d1, (4 * qb + (lane >> 4)) & (G::SLOTS - 1), sk, raw);
         };
         auto stage_scalar = [&](int qb) {
             const int span = AL + G::XW;
@@ -474,13 +476,13 @@ __global__ __launch_bounds__(256) void lk_roll32_kernel(Lr16Args<T> a) {
                 const int col = cb8 + p;
                 if (col < 0 || col >= a.IW) continue;
                 const uint16_t v = r < a.IH ? ip[static_cast<int64_t>(r) * a.IW + col] : uint16_t{0};
-                ring_put_one(ring, d1, (4 * qb + q) & (kR16Slots - 1), p, v);
+                ring_put_one<G::RS>(ring, d1, (4 * qb + q) & (G::SLOTS - 1), p, v);
             }
         };
+        uint4 raw = make_uint4(0u, 0u, 0u, 0u);
         if constexpr (VIN) {
-            load_batch(0);
-            write_batch(0);
-            load_batch(1);
+            write_batch(0, load_batch(0));
+            raw = load_batch(1);
         } else {
             stage_scalar(0);
         }
@@ -491,14 +493,14 @@ __global__ __launch_bounds__(256) void lk_roll32_kernel(Lr16Args<T> a) {
             constexpr int MM = decltype(mm_c)::value;
             constexpr int HH = (MM >> 2) & 1;
             constexpr int R0 = 4 * (MM >> 3) + (MM & 3), R1 = R0 + 8;
-            const uint32_t *bp = ring + boff + (v & (kR16Slots - 1));
+            const uint32_t *bp = ring + boff + (v & (G::SLOTS - 1));
             u32x4_r bv[NT][2];
 #pragma unroll
             for (int t = 0; t < NT; ++t)
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
-                    const uint32_t *q = bp + 9 * (16 * t + 8 * s);
-                    bv[t][s] = u32x4_r{q[0], q[9], q[18], q[27]};
+                    const uint32_t *q = bp + G::RS * (16 * t + 8 * s);
+                    bv[t][s] = u32x4_r{q[0], q[G::RS], q[2 * G::RS], q[3 * G::RS]};
                 }
             const bool sel = h == HH;
             float e[NT];
@@ -535,8 +537,8 @@ __global__ __launch_bounds__(256) void lk_roll32_kernel(Lr16Args<T> a) {
             roll_lds_sync();
             if (q + 1 < nq) {
                 if constexpr (VIN) {
-                    write_batch(q + 1);
-                    if (q + 2 < nq) load_batch(q + 2);
+                    write_batch(q + 1, raw);
+                    if (q + 2 < nq) raw = load_batch(q + 2);
                 } else {
                     stage_scalar(q + 1);
                 }
@@ -570,9 +572,267 @@ __global__ __launch_bounds__(256) void lk_roll32_kernel(Lr16Args<T> a) {
     }
 }
 
+// The same streaming for k <= 16 on 16 x 16 x 32 tiles, the contraction
+// covering several input rows: RPS = 4 rows of 8 kernel columns (k <= 8) or
+// 2 rows of 16 (k <= 16) per instruction, lane k-group g holding 8 adjacent
+// values of input row RPS p + delta(g).  One 16-row block of accumulator
+// slots: the output row whose kernel row 0 is input row rho lives in slot
+// s = rho mod 16 while input rows rho .. rho + 15 stream past; at step p slot s
+// holds kernel rows i0 + delta with i0 = RPS p - rho, so from one step to the
+// next the slots' filter rows move by RPS slots.  Slot s sits in accumulator
+// row sigma(s): for RPS = 4 the transpose 4 (s mod 4) + s / 4, so the four
+// slots a step finishes are one whole register (all four lane rows) and the
+// move of filter rows is a rotation inside each quad of lanes (DPP quad_perm);
+// for RPS = 2 the identity (two registers of one lane row finish, the filter
+// rows rotate by two lanes, DPP row_ror:2).
+template <typename T, int K, int NT, bool FLIP, bool VIN>
+__global__ __launch_bounds__(256) void lk_rolls_kernel(Lr16Args<T> a) {
+    constexpr int RPS = K <= 8 ? 4 : 2;  // input rows per step
+    // a slot restarts while the rows of its step still stream past: the
+    // finishing output's kernel rows 16 - RPS + 1 .. 15 must be zero
+    static_assert(K <= 17 - RPS, "one 16-row block of slots");
+    constexpr int JW = 32 / RPS;         // kernel columns per input row of the contraction
+    constexpr int SPB = 4 / RPS;         // steps per batch of four rows
+    using G = Lr16Geo<K, NT, 8>;
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int wid = blockIdx.x * 4 + wave;
+    if (wid >= a.nwaves) return;  // whole waves; the kernel has no workgroup barrier
+    uint32_t *ring = reinterpret_cast<uint32_t *>(smem) + wave * G::RING;
+
+    const int per_c = a.nchunk * a.nimgw;
+    const int c = wid / per_c;
+    const int rem = wid - c * per_c;
+    const int chunk = rem / a.nimgw;
+    const int ig = rem - chunk * a.nimgw;
+    const int n0 = ig * a.ipw, n1 = min(n0 + a.ipw, a.N);
+    const int cin = FLIP ? c : c / a.mult;
+    const int c_lo = chunk * 16 * NT;
+    const int cb = c_lo - a.P;
+    const int cb8 = cb & ~7;
+    const int AL = cb - cb8;
+
+    const int n = lane & 15, g = lane >> 4;
+    const int n2 = n * static_cast<int>(sizeof(T));
+    const int dl = (8 * g) / JW;        // this lane row's input row within a step
+    const int j0 = (8 * g) % JW;        // its first kernel column
+    const int s0 = AL + n + j0;
+    const int d1 = G::D1 + (AL & 1);
+    const int boff = ring_run<G::RS>(s0, d1) + dl;  // + slot of the step's first row
+    const int sk = lane & 15;
+    const int gc = cb8 + 8 * sk;
+    const bool vk = sk < G::NVEC && gc >= 0 && gc + 8 <= a.IW;
+
+    for (int e = lane; e < G::RING; e += 64) ring[e] = 0u;
+    roll_lds_sync();
+
+    const float bias = (!FLIP && a.b) ? to_f32(a.b[c]) : 0.f;
+    const uint16_t *wc = reinterpret_cast<const uint16_t *>(a.w) + static_cast<int64_t>(c) * K * K;
+    const int64_t iplane = static_cast<int64_t>(a.IH) * a.IW;
+    const int nq = ((a.IH + 15) >> 4) << 2;  // batches of four rows, whole groups of 16
+    const bool colfull = c_lo + 16 * NT <= a.OW;
+    // slot of accumulator row m = n (A lane row) and i0 - (RPS - 1) at step 0
+    const int slot = RPS == 4 ? 4 * (n & 3) + (n >> 2) : n;
+    const int i00 = ((RPS - 1 - slot) & 15) - (RPS - 1);
+
+    for (int nimg = n0; nimg < n1; ++nimg) {
+        const uint16_t *ip = reinterpret_cast<const uint16_t *>(a.in) + (static_cast<int64_t>(nimg) * a.Cin + cin) * iplane;
+        T *op = a.out + (static_cast<int64_t>(nimg) * a.C + c) * a.OH * a.OW;
+        const __amdgpu_buffer_rsrc_t orsrc =
+            __builtin_amdgcn_make_buffer_rsrc(op, 0, a.OH * a.OW * static_cast<int>(sizeof(T)), 0x00020000);
+        const __amdgpu_buffer_rsrc_t irsrc =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(ip), 0, static_cast<int>(iplane * 2), 0x00020000);
+
+        // A: lane (m, g) holds w[i0 + dl][j0 .. j0 + 7] (zero outside the filter)
+        u32x4_r A;
+#pragma unroll
+        for (int k2 = 0; k2 < 4; ++k2) {
+            uint32_t v = 0;
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int i = i00 + dl, j = j0 + 2 * k2 + hh;
+                if (i >= 0 && i < K && j < K) {
+                    const uint16_t bits = FLIP ? wc[(K - 1 - i) * K + (K - 1 - j)] : wc[i * K + j];
+                    v |= static_cast<uint32_t>(bits) << (16 * hh);
+                }
+            }
+            A[k2] = v;
+        }
+        f32x4_r d[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) d[t] = f32x4_r{bias, bias, bias, bias};
+
+        auto load_batch = [&](int qb) -> uint4 {
+            const int r = 4 * qb + (lane >> 4);
+            const int off = (vk && r < a.IH) ? (r * a.IW + gc) * 2 : kR16Skip;
+            const u32x4_r v = __builtin_amdgcn_raw_buffer_load_b128(irsrc, off, 0, 0);
+            return make_uint4(v[0], v[1], v[2], v[3]);
+        };
+        auto write_batch = [&](int qb, const uint4 &raw) {
+            if (vk) ring_put_vec<G::RS>(ring, d1, (4 * qb + (lane >> 4)) & (G::SLOTS - 1), sk, raw);
+        };
+        auto stage_scalar = [&](int qb) {
+            const int span = AL + G::XW;
+            for (int e = lane; e < 4 * span; e += 64) {
+                const int q = e / span;
+                const int p = e - q * span;
+                const int r = 4 * qb + q;
+                const int col = cb8 + p;
+                if (col < 0 || col >= a.IW) continue;
+                const uint16_t v = r < a.IH ? ip[static_cast<int64_t>(r) * a.IW + col] : uint16_t{0};
+                ring_put_one<G::RS>(ring, d1, (4 * qb + q) & (G::SLOTS - 1), p, v);
+            }
+        };
+        uint4 raw = make_uint4(0u, 0u, 0u, 0u);
+        if constexpr (VIN) {
+            write_batch(0, load_batch(0));
+            raw = load_batch(1);
+        } else {
+            stage_scalar(0);
+        }
+
+        // step p (PP = p mod 16 / RPS): input rows RPS p .. RPS p + RPS - 1
+        auto step = [&](auto pp_c, int p) {
+            constexpr int PP = decltype(pp_c)::value;
+            const uint32_t *bp = ring + boff + ((RPS * PP) & (G::SLOTS - 1));
+            u32x4_r bv[NT];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const uint32_t *q = bp + G::RS * 8 * t;
+                bv[t] = u32x4_r{q[0], q[G::RS], q[2 * G::RS], q[3 * G::RS]};
+            }
+            // the RPS slots RPS PP .. finish the output rows rho = RPS p + e - 16
+            // and start rho + 16 (at its bias)
+            float e0[NT], e1[NT];
+            if constexpr (RPS == 4) {
+                constexpr int R = PP & 3;  // register of sigma(4 PP + e) = 4 e + PP
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    e0[t] = d[t][R];
+                    d[t][R] = bias;
+                }
+                const int oh = RPS * p + g - 16 + a.P;
+                const int off = (oh >= 0 && oh < a.OH) ? (oh * a.OW + c_lo) * static_cast<int>(sizeof(T)) + n2 : kR16Skip;
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+                    __builtin_amdgcn_raw_buffer_store_b16(bits16(e0[t], static_cast<T *>(nullptr)), orsrc,
+                                                          (colfull || c_lo + 16 * t + n < a.OW) ? off + 32 * t : kR16Skip, 0, 0);
+            } else {
+                constexpr int M0 = (2 * PP) & 15;        // slots M0, M0 + 1: lane row M0 / 4, registers M0 % 4, + 1
+                constexpr int R = M0 & 3;
+                const bool sel = g == (M0 >> 2);
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    e0[t] = d[t][R];
+                    e1[t] = d[t][R + 1];
+                    d[t][R] = sel ? bias : d[t][R];
+                    d[t][R + 1] = sel ? bias : d[t][R + 1];
+                }
+                const int oh = RPS * p - 16 + a.P;
+                const int ub0 = (oh >= 0 && oh < a.OH) ? (oh * a.OW + c_lo) * static_cast<int>(sizeof(T)) : kR16Skip;
+                const int ub1 = (oh + 1 >= 0 && oh + 1 < a.OH) ? ((oh + 1) * a.OW + c_lo) * static_cast<int>(sizeof(T)) : kR16Skip;
+                const int off0 = sel ? ub0 + n2 : kR16Skip;
+                const int off1 = sel ? ub1 + n2 : kR16Skip;
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    const bool cok = colfull || c_lo + 16 * t + n < a.OW;
+                    __builtin_amdgcn_raw_buffer_store_b16(bits16(e0[t], static_cast<T *>(nullptr)), orsrc,
+                                                          cok ? off0 + 32 * t : kR16Skip, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b16(bits16(e1[t], static_cast<T *>(nullptr)), orsrc,
+                                                          cok ? off1 + 32 * t : kR16Skip, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < NT; ++t) d[t] = RollMfma<T>::run(A, bv[t], d[t]);
+            // filter rows of the slots RPS behind: quad rotation (RPS 4) or two lanes (RPS 2)
+#pragma unroll
+            for (int k2 = 0; k2 < 4; ++k2) {
+                uint32_t r;
+                if constexpr (RPS == 4)
+                    r = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(A[k2]), 0x93, 0xf, 0xf, true));
+                else
+                    r = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(A[k2]), 0x122, 0xf, 0xf, true));
+                asm volatile("" : "+v"(r));
+                A[k2] = r;
+            }
+        };
+        auto batch = [&](auto jb_c, int q) {
+            constexpr int JB = decltype(jb_c)::value;
+            roll_lds_sync();
+            if (q + 1 < nq) {
+                if constexpr (VIN) {
+                    write_batch(q + 1, raw);
+                    if (q + 2 < nq) raw = load_batch(q + 2);
+                } else {
+                    stage_scalar(q + 1);
+                }
+            }
+            const int p = SPB * q;
+            if constexpr (RPS == 4) {
+                step(std::integral_constant<int, JB>{}, p);
+            } else {
+                step(std::integral_constant<int, 2 * JB>{}, p);
+                step(std::integral_constant<int, 2 * JB + 1>{}, p + 1);
+            }
+        };
+        for (int q = 0; q < nq; q += 4) {
+            batch(std::integral_constant<int, 0>{}, q);
+            batch(std::integral_constant<int, 1>{}, q + 1);
+            batch(std::integral_constant<int, 2>{}, q + 2);
+            batch(std::integral_constant<int, 3>{}, q + 3);
+        }
+        roll_lds_sync();
+
+        // every output row still in a slot is complete
+        const int pl = SPB * nq - 1;  // last step
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = 4 * g + r;
+            const int sl = RPS == 4 ? 4 * (m & 3) + (m >> 2) : m;
+            const int i0 = ((RPS * pl - sl + RPS - 1) & 15) - (RPS - 1);
+            const int oh = RPS * pl - i0 + a.P;
+            if (oh < 0 || oh >= a.OH) continue;
+            T *orow = op + static_cast<int64_t>(oh) * a.OW + c_lo + n;
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                if (c_lo + 16 * t + n < a.OW) orow[16 * t] = from_f32<T>(d[t][r]);
+        }
+    }
+}
+
+template <typename T, int K, int NT, bool FLIP>
+int run_lrs_t(Lr16Args<T> a, hipStream_t s) {
+    using G = Lr16Geo<K, NT, 8>;
+    a.nchunk = (a.OW + 16 * NT - 1) / (16 * NT);
+    const int64_t items = static_cast<int64_t>(a.C) * a.nchunk;
+    const int64_t want = std::max<int64_t>(1, (static_cast<int64_t>(a.N) * items) >> 18);
+    a.ipw = static_cast<int>(std::min<int64_t>(want, a.N));
+    a.nimgw = (a.N + a.ipw - 1) / a.ipw;
+    const int64_t nw = items * a.nimgw;
+    if (nw > (int64_t{1} << 30)) return kErrUnsupported;
+    a.nwaves = static_cast<int>(nw);
+    const dim3 grid(static_cast<unsigned>((nw + 3) / 4));
+    if (a.vin)
+        hipLaunchKernelGGL((lk_rolls_kernel<T, K, NT, FLIP, true>), grid, dim3(256), G::lds_bytes, s, a);
+    else
+        hipLaunchKernelGGL((lk_rolls_kernel<T, K, NT, FLIP, false>), grid, dim3(256), G::lds_bytes, s, a);
+    return hipGetLastError() == hipSuccess ? kOk : kErrHip;
+}
+
+template <typename T, int K, bool FLIP>
+int run_lrs(const Lr16Args<T> &a, hipStream_t s) {
+    const int nt = std::min(4, (a.OW + 15) / 16);
+    if (nt == 1) return run_lrs_t<T, K, 1, FLIP>(a, s);
+    if (nt == 2) return run_lrs_t<T, K, 2, FLIP>(a, s);
+    if (nt == 3) return run_lrs_t<T, K, 3, FLIP>(a, s);
+    return run_lrs_t<T, K, 4, FLIP>(a, s);
+}
+
 template <typename T, int NT, bool FLIP>
 int run_lr32_t(Lr16Args<T> a, hipStream_t s) {
-    using G = Lr16Geo<kR16K, 2 * NT>;
+    using G = Lr16Geo<kR16K, 2 * NT, 8>;
     a.nchunk = (a.OW + 32 * NT - 1) / (32 * NT);
     const int64_t items = static_cast<int64_t>(a.C) * a.nchunk;
     const int64_t want = std::max<int64_t>(1, (static_cast<int64_t>(a.N) * items) >> 18);
@@ -591,7 +851,7 @@ int run_lr32_t(Lr16Args<T> a, hipStream_t s) {
 
 template <typename T, int NT, bool FLIP>
 int run_lr16_t(Lr16Args<T> a, hipStream_t s) {
-    using G = Lr16Geo<kR16K, NT>;
+    using G = Lr16Geo<kR16K, NT, 8>;
     a.nchunk = (a.OW + 16 * NT - 1) / (16 * NT);
     // one image a wave (many short waves leave no partial last round of
     // resident waves), a few where there are more than 2^18 of them
@@ -611,7 +871,9 @@ int run_lr16_t(Lr16Args<T> a, hipStream_t s) {
 }
 
 template <typename T, bool FLIP>
-int run_lr16(const Lr16Args<T> &a, hipStream_t s) {
+int run_lr16(const Lr16Args<T> &a, int K, hipStream_t s) {
+    if (K == 7) return run_lrs<T, 7, FLIP>(a, s);
+    if (K == 13) return run_lrs<T, 13, FLIP>(a, s);
     // rows a multiple of 32 wide: 32-column tiles
     if (a.OW % 32 == 0) return a.OW == 32 ? run_lr32_t<T, 1, FLIP>(a, s) : run_lr32_t<T, 2, FLIP>(a, s);
     const int nt = std::min(4, (a.OW + 15) / 16);
@@ -638,7 +900,7 @@ int lr16_fwd_t(const Geo &g, const void *x, const void *w, const void *b, void *
     a.OW = g.ow;
     a.P = g.ph;
     a.vin = a.IW % 8 == 0 && reinterpret_cast<uintptr_t>(x) % 16 == 0;
-    return run_lr16<T, false>(a, s);
+    return run_lr16<T, false>(a, g.kh, s);
 }
 
 template <typename T>
@@ -657,16 +919,16 @@ int lr16_bwdin_t(const Geo &g, const void *dy, const void *w, void *dx, hipStrea
     a.OW = g.iw;
     a.P = g.kh - 1 - g.ph;
     a.vin = a.IW % 8 == 0 && reinterpret_cast<uintptr_t>(dy) % 16 == 0;
-    return run_lr16<T, true>(a, s);
+    return run_lr16<T, true>(a, g.kh, s);
 }
 
 }  // namespace
 
-// 16-bit, k = 31 square, stride 1, dilation 1, equal paddings below k; the
-// grad-input pass with multiplier 1.  Any plane size.
+// 16-bit, k = 7, 13 or 31 square, stride 1, dilation 1, equal paddings below
+// k; the grad-input pass with multiplier 1.  Any plane size.
 bool largek_roll16_fits(const Geo &g, int pass, int dtype) {
     if (dtype == 0) return false;
-    if (g.kh != kR16K || g.kw != kR16K) return false;
+    if (g.kh != g.kw || (g.kh != 7 && g.kh != 13 && g.kh != kR16K)) return false;
     if (g.sh != 1 || g.sw != 1 || g.dh != 1 || g.dw != 1 || g.ph != g.pw || g.ph > g.kh - 1) return false;
     if (pass == 1 && g.mult != 1) return false;
     // input and output planes addressed by 32-bit buffer offsets below 1 GiB

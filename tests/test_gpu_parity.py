@@ -1020,7 +1020,34 @@ def test_large_kernel_16bit_small_tiles(n, c, h, w, mult, k, p, dt, bin_h):
     (8, 2048, 16, 16, 1, 15, "f16", True),  # two images a wave
 ])
 def test_large_kernel_row_stream_16bit(n, c, h, w, mult, p, dt, bin_ok):
-    k = 31
+    run_row_stream_16bit(n, c, h, w, mult, 31, p, dt, bin_ok)
+
+
+# k = 7 and 13 on the same streaming: four input rows (k = 7) or two (k = 13)
+# per contraction; odd heights, element staging, chunks, pad 0 and k - 1, a
+# multiplier, kernels wider than the image.
+@pytest.mark.gpu
+@pytest.mark.parametrize("n,c,h,w,mult,k,p,dt,bin_ok", [
+    (2, 3, 32, 32, 1, 7, 3, "f16", True),
+    (2, 2, 48, 48, 1, 7, 3, "bf16", True),
+    (2, 2, 64, 64, 1, 13, 6, "f16", True),
+    (2, 2, 48, 48, 1, 13, 6, "bf16", True),
+    (1, 2, 47, 45, 1, 7, 3, "f16", True),     # element staging, ragged tiles
+    (2, 1, 33, 29, 1, 13, 6, "bf16", True),
+    (1, 2, 21, 150, 1, 13, 6, "f16", True),   # three column chunks
+    (1, 1, 14, 264, 1, 7, 3, "bf16", True),   # five chunks, vector staging
+    (2, 2, 40, 40, 1, 7, 0, "f16", True),     # pad 0: grad-input pad 6
+    (2, 2, 26, 22, 1, 13, 12, "bf16", True),  # pad k - 1: grad-input pad 0
+    (2, 2, 20, 24, 1, 7, 6, "f16", True),     # pad k - 1
+    (2, 2, 30, 34, 2, 13, 6, "f16", False),   # multiplier 2 (forward only)
+    (2, 2, 5, 9, 1, 13, 6, "bf16", True),     # kernel wider than the image
+    (1, 2, 3, 70, 1, 7, 3, "f16", True),      # fewer input rows than one step
+])
+def test_small_kernel_row_stream_16bit(n, c, h, w, mult, k, p, dt, bin_ok):
+    run_row_stream_16bit(n, c, h, w, mult, k, p, dt, bin_ok)
+
+
+def run_row_stream_16bit(n, c, h, w, mult, k, p, dt, bin_ok):
     geo = ((n, c, h, w), (c * mult, k, k), 1, p, 1)
     assert "largek_roll16" in dc.dwconv2d_algo_candidates(0, *geo, dtype=DT[dt])
     assert ("largek_roll16" in dc.dwconv2d_algo_candidates(1, *geo, dtype=DT[dt])) == bin_ok
@@ -1029,7 +1056,7 @@ def test_large_kernel_row_stream_16bit(n, c, h, w, mult, p, dt, bin_ok):
         dc.dwconv2d_set_algo(0, *geo, dtype=DT[dt], algo="largek_roll16")
         if bin_ok:
             dc.dwconv2d_set_algo(1, *geo, dtype=DT[dt], algo="largek_roll16")
-        check_static(x, wt, b, dy, 1, p, 1, "largek-roll16 n%d c%d %dx%d m%d p%d %s" % (n, c, h, w, mult, p, dt),
+        check_static(x, wt, b, dy, 1, p, 1, "largek-roll16 n%d c%d %dx%d m%d k%d p%d %s" % (n, c, h, w, mult, k, p, dt),
                      passes=("fwd", "bwd_in") if bin_ok else ("fwd",))
     finally:
         dc.dwconv2d_set_algo(0, *geo, dtype=DT[dt], algo=None)
