@@ -38,6 +38,7 @@ FLAGS = [
 # accumulator elements, which the AGPR form turns into register copies).
 EXTRA_FLAGS = {
     "dw_largek_roll16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "dw_largek_wroll16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

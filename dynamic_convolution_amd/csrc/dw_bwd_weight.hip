@@ -426,12 +426,12 @@ int run_small(const Geo &g, const BwPlan &p, const void *x, const void *dy, void
 
 enum BwAlgo {
     kBwChannelGroup = 0, kBwLargek, kBwRowwalk, kBwDecim, kBwBandPixel, kBwBandTaps, kBwLargekMfma, kBwLargekMfma32,
-    kBwDirect, kBwLargekMfma16, kBwStream7, kBwLargekMfmaH16, kBwCount
+    kBwDirect, kBwLargekMfma16, kBwStream7, kBwLargekMfmaH16, kBwRoll16, kBwCount
 };
 
 const char *const kBwNames[kBwCount] = {"channelgroup_small", "largek_regtile", "rowwalk_3x3", "decimated_s2d2",
                                         "band_pixel",         "band_taps",      "largek_mfma",  "largek_mfma_f32",
-                                        "direct",             "largek_mfma_t16", "stream_7x7",     "largek_mfma_h16"};
+                                        "direct",             "largek_mfma_t16", "stream_7x7",     "largek_mfma_h16", "largek_roll16"};
 
 bool band_bw_plans(const Geo &g, int dt) {
     BwPlan p;
@@ -454,6 +454,7 @@ bool feasible_bw(int algo, const Geo &g, int dt) {
         case kBwLargekMfma16: return largek_wgrad16_fits(g, dt);
         case kBwStream7: return stream7_bwdw_fits(g);
         case kBwLargekMfmaH16: return largek_mfma_bwdw16_fits(g, dt);
+        case kBwRoll16: return largek_wroll16_fits(g, dt);
         default: return false;
     }
 }
@@ -465,6 +466,9 @@ int select_bwd_weight(const Geo &g, int dt) {
     if (tuned >= 0 && feasible_bw(tuned, g, dt)) return tuned;
     if (small_fits(g, dt, 2)) return kBwChannelGroup;
     // 16-bit, k = 13: 16 x 16 tiles measured 1.45-1.75x faster than 32 x 32 ones
+    // 16-bit 13 x 13 and 31 x 31: input rows streamed past the dy rows held in
+    // the filter-row slots, measured 1.25-1.55x faster than the tile kernels
+    if (largek_wroll16_fits(g, dt)) return kBwRoll16;
     if (g.kh == 13 && largek_mfma_bwdw16_fits(g, dt)) return kBwLargekMfmaH16;
     if (largek_mfma_bwdw_fits(g, dt)) return kBwLargekMfma;  // 16-bit: measured faster than 16 x 16 fp32 tiles
     if (largek_wgrad16_fits(g, dt)) return kBwLargekMfma16;
@@ -488,6 +492,7 @@ int64_t ws_for(int algo, const Geo &g, int dtype) {
         case kBwLargekMfma16: return std::max<int64_t>(g.ic * largek_wgrad16_chunks(g) * slots * 4, 16);
         case kBwStream7: return std::max<int64_t>(g.ic * stream7_bwdw_chunks(g) * slots * 4, 16);
         case kBwLargekMfmaH16: return std::max<int64_t>(g.ic * largek_mfma_bwd_weight_chunks(g) * slots * 4, 16);
+        case kBwRoll16: return std::max<int64_t>(static_cast<int64_t>(g.ic) * largek_wroll16_chunks(g) * slots * 4, 16);
         case kBwDirect: return std::max<int64_t>(static_cast<int64_t>(g.ic) * direct_bwd_weight_chunks(g) * slots * 4, 16);
         case kBwRowwalk: return std::max<int64_t>(g.ic * rowwalk_bwd_weight_chunks(g, dtype) * slots * 4, 16);
         case kBwDecim: return std::max<int64_t>(g.ic * decim_bwd_weight_chunks(g) * slots * 4, 16);
@@ -528,6 +533,11 @@ int dispatch_bwd_weight(const Geo &g, const void *x, const void *dy, void *dwt, 
         rc = largek_mfma_bwd_weight16(g, x, dy, ws, dt, s);
         if (rc != kOk) return rc;
         return launch_reduce<T>(g, ws, dwt, db, largek_mfma_bwd_weight_chunks(g), kk + 1, s);
+    }
+    if (algo == kBwRoll16) {
+        rc = largek_wroll16(g, x, dy, ws, dt, s);
+        if (rc != kOk) return rc;
+        return launch_reduce<T>(g, ws, dwt, db, largek_wroll16_chunks(g), kk + 1, s);
     }
     if (algo == kBwStream7) {
         rc = stream7_bwdw(g, x, dy, ws, dt, s);

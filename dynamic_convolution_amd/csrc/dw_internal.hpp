@@ -91,6 +91,11 @@ int largek_mfma16_bwd_input(const Geo &g, const void *dy, const void *w, void *d
 bool largek_roll16_fits(const Geo &g, int pass, int dtype);
 int largek_roll16_fwd(const Geo &g, const void *x, const void *w, const void *b, void *y, int dtype, hipStream_t s);
 int largek_roll16_bwd_input(const Geo &g, const void *dy, const void *w, void *dx, int dtype, hipStream_t s);
+// 16-bit k = 13 / 31 grad-weight streaming input rows, the dy rows moving
+// through the filter-row slots (dw_largek_wroll16.hip); output rows <= 64.
+bool largek_wroll16_fits(const Geo &g, int dtype);
+int largek_wroll16_chunks(const Geo &g);
+int largek_wroll16(const Geo &g, const void *x, const void *dy, void *ws, int dtype, hipStream_t s);
 // Grad-weight pass 1 of the same family (k = 13, 31; multiplier 1; dy rows <= 64):
 // workspace [ic][chunks][k*k + 1].
 bool largek_mfma_bwdw_fits(const Geo &g, int dtype);

@@ -215,7 +215,7 @@ def test_dynconv_into_validation():
     (2, ((128, 1024, 7, 7), (1024, 3, 3), 2, 1, 1), torch.float32, {"channelgroup_small"}),
     (0, ((64, 384, 64, 64), (384, 31, 31), 1, 15, 1), torch.float16, {"largek_roll16", "largek_mfma", "largek_regtile"}),
     (1, ((64, 384, 48, 48), (384, 31, 31), 1, 15, 1), torch.bfloat16, {"largek_roll16", "largek_mfma", "largek_regtile"}),
-    (2, ((64, 384, 64, 64), (384, 31, 31), 1, 15, 1), torch.bfloat16, {"largek_mfma", "largek_regtile"}),
+    (2, ((64, 384, 64, 64), (384, 31, 31), 1, 15, 1), torch.bfloat16, {"largek_roll16", "largek_mfma", "largek_regtile"}),
     (2, ((64, 384, 48, 48), (384, 7, 7), 1, 3, 1), torch.float32, {"stream_7x7", "largek_regtile"}),
     (1, ((128, 256, 56, 56), (512, 5, 5), 2, 4, 2), torch.bfloat16, {"decimated_s2d2", "band_generic"}),
 ])

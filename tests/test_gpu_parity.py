@@ -708,13 +708,14 @@ def test_large_kernel_mfma_group_chunks(n, c, h, w, k, p, dt):
     (1, 2, 40, 100, 13, 6, "f16", False),    # rows of 100: register tiles
 ])
 def test_large_kernel_mfma_grad_weight(n, c, h, w, k, p, dt, bw_mfma):
-    """The 32 x 32-tile family (the default at k = 31; at k = 13 the 16 x 16 tiles are, so it is forced)."""
+    """The 32 x 32-tile family (forced: the row-streaming family is the 16-bit default at k = 13 and 31)."""
     geo = ((n, c, h, w), (c, k, k), 1, p, 1)
     default = dc.dwconv2d_algo(2, *geo, dtype=DT[dt])
-    if bw_mfma and k == 13:
-        assert default == "largek_mfma_h16"
+    if bw_mfma:
+        assert default == "largek_roll16"
+        assert "largek_mfma" in dc.dwconv2d_algo_candidates(2, *geo, dtype=DT[dt])
     else:
-        assert (default == "largek_mfma") == bw_mfma
+        assert default not in ("largek_mfma", "largek_roll16")
     x, wt, b, dy = static_case(n, c, h, w, 1, k, 1, p, 1, DT[dt], 690 + h + w + k)
     try:
         if bw_mfma:
@@ -1062,3 +1063,33 @@ def run_row_stream_16bit(n, c, h, w, mult, k, p, dt, bin_ok):
         dc.dwconv2d_set_algo(0, *geo, dtype=DT[dt], algo=None)
         if bin_ok:
             dc.dwconv2d_set_algo(1, *geo, dtype=DT[dt], algo=None)
+
+
+# 16-bit grad-weight streaming input rows, the dy rows moving through the
+# filter-row slots (forced family): the workload's planes, element-staged
+# widths, pad 0 and pad k - 1, a kernel wider than the image, dy rows shorter
+# than 32 (one contraction step), and enough planes that each wave walks two images.
+@pytest.mark.gpu
+@pytest.mark.parametrize("n,c,h,w,k,p,dt", [
+    (3, 2, 64, 64, 31, 15, "f16"),
+    (2, 3, 48, 48, 31, 15, "bf16"),
+    (3, 2, 32, 32, 31, 15, "f16"),
+    (3, 2, 64, 64, 13, 6, "bf16"),
+    (2, 3, 48, 48, 13, 6, "f16"),
+    (2, 2, 47, 45, 31, 15, "bf16"),   # element staging
+    (2, 2, 33, 30, 13, 0, "f16"),     # no padding
+    (2, 2, 20, 24, 31, 30, "bf16"),   # pad k - 1 (output rows of 54)
+    (2, 2, 9, 9, 31, 15, "f16"),      # kernel wider than the image
+    (3, 2, 70, 20, 13, 6, "bf16"),    # 70 rows, one contraction step
+    (8, 2048, 16, 16, 31, 15, "f16"),  # two images a wave
+])
+def test_grad_weight_row_stream_16bit(n, c, h, w, k, p, dt):
+    geo = ((n, c, h, w), (c, k, k), 1, p, 1)
+    assert "largek_roll16" in dc.dwconv2d_algo_candidates(2, *geo, dtype=DT[dt])
+    x, wt, b, dy = static_case(n, c, h, w, 1, k, 1, p, 1, DT[dt], 2500 + h + w + k + p)
+    try:
+        dc.dwconv2d_set_algo(2, *geo, dtype=DT[dt], algo="largek_roll16")
+        check_static(x, wt, b, dy, 1, p, 1, "wgrad-roll16 n%d c%d %dx%d k%d p%d %s" % (n, c, h, w, k, p, dt),
+                     passes=("bwd_w",))
+    finally:
+        dc.dwconv2d_set_algo(2, *geo, dtype=DT[dt], algo=None)
