@@ -572,35 +572,54 @@ __global__ __launch_bounds__(256) void lk_roll32_kernel(Lr16Args<T> a) {
     }
 }
 
-// The same streaming for k <= 16 on 16 x 16 x 32 tiles, the contraction
+// The same streaming for k <= 13 on 16 x 16 x 32 tiles, the contraction
 // covering several input rows: RPS = 4 rows of 8 kernel columns (k <= 8) or
-// 2 rows of 16 (k <= 16) per instruction, lane k-group g holding 8 adjacent
+// 2 rows of 16 (k <= 13) per instruction, lane k-group g holding 8 adjacent
 // values of input row RPS p + delta(g).  One 16-row block of accumulator
 // slots: the output row whose kernel row 0 is input row rho lives in slot
 // s = rho mod 16 while input rows rho .. rho + 15 stream past; at step p slot s
-// holds kernel rows i0 + delta with i0 = RPS p - rho, so from one step to the
-// next the slots' filter rows move by RPS slots.  Slot s sits in accumulator
-// row sigma(s): for RPS = 4 the transpose 4 (s mod 4) + s / 4, so the four
-// slots a step finishes are one whole register (all four lane rows) and the
-// move of filter rows is a rotation inside each quad of lanes (DPP quad_perm);
-// for RPS = 2 the identity (two registers of one lane row finish, the filter
-// rows rotate by two lanes, DPP row_ror:2).
+// holds kernel rows i0 + delta with i0 = RPS p - rho (mod 16), so the filter
+// rows a lane needs repeat every 16 / RPS steps: all of those phases are held
+// in registers (no data movement between steps).  Slot s sits in accumulator
+// row 4 (s mod 4) + s / 4, so slots 4 R .. 4 R + 3 are register R of all four
+// lane rows.  With RPS = 4 a step finishes exactly those four slots; with
+// RPS = 2 a step finishes two of them, and the other two are already complete
+// (their last two kernel rows, 14 and 15 or 13 and 14, are zero for k <= 13),
+// so every second step emits one whole register.
+//
+// Output rows are collected in LDS (32 rows of the chunk) and leave in a
+// fixed number of stores once per 32 rows: with no stores between, the waits on
+// vector memory are for the oldest input loads only, so the inputs can be
+// loaded several batches (a few hundred cycles of matrix work each) ahead.
+template <int K, int NT> struct RsOut {
+    static constexpr int ROWS = 32;
+    static constexpr int PITCH = 8 * NT + 4;   // dwords of a buffered output row (16 NT halves, padded)
+    static constexpr int DW = ROWS * PITCH;    // dwords of the buffer
+    static constexpr int RINGA = (Lr16Geo<K, NT, 8>::RING + 3) / 4 * 4;  // ring, 16-byte aligned
+    static constexpr int WAVE = RINGA + DW;    // dwords of LDS a wave
+};
+
 template <typename T, int K, int NT, bool FLIP, bool VIN>
 __global__ __launch_bounds__(256) void lk_rolls_kernel(Lr16Args<T> a) {
     constexpr int RPS = K <= 8 ? 4 : 2;  // input rows per step
-    // a slot restarts while the rows of its step still stream past: the
-    // finishing output's kernel rows 16 - RPS + 1 .. 15 must be zero
-    static_assert(K <= 17 - RPS, "one 16-row block of slots");
+    // a slot restarts while the rows of its step still stream past, and with
+    // RPS = 2 a register is emitted one step before half of its slots restart:
+    // kernel rows 13 .. 15 must be zero
+    static_assert(K <= 13, "one 16-row block of slots");
+    constexpr int NPH = 16 / RPS;        // filter phases
     constexpr int JW = 32 / RPS;         // kernel columns per input row of the contraction
     constexpr int SPB = 4 / RPS;         // steps per batch of four rows
+    constexpr int PD = 4;                // batches loaded ahead
     using G = Lr16Geo<K, NT, 8>;
+    using O = RsOut<K, NT>;
     extern __shared__ __align__(16) unsigned char smem[];
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int wid = blockIdx.x * 4 + wave;
     if (wid >= a.nwaves) return;  // whole waves; the kernel has no workgroup barrier
-    uint32_t *ring = reinterpret_cast<uint32_t *>(smem) + wave * G::RING;
+    uint32_t *ring = reinterpret_cast<uint32_t *>(smem) + wave * O::WAVE;
+    uint16_t *obuf = reinterpret_cast<uint16_t *>(ring + O::RINGA);
 
     const int per_c = a.nchunk * a.nimgw;
     const int c = wid / per_c;
@@ -615,27 +634,53 @@ __global__ __launch_bounds__(256) void lk_rolls_kernel(Lr16Args<T> a) {
     const int AL = cb - cb8;
 
     const int n = lane & 15, g = lane >> 4;
-    const int n2 = n * static_cast<int>(sizeof(T));
     const int dl = (8 * g) / JW;        // this lane row's input row within a step
     const int j0 = (8 * g) % JW;        // its first kernel column
     const int s0 = AL + n + j0;
     const int d1 = G::D1 + (AL & 1);
     const int boff = ring_run<G::RS>(s0, d1) + dl;  // + slot of the step's first row
-    const int sk = lane & 15;
+    // lanes past the last vector repeat it (same load, same LDS writes), so
+    // every lane stages without a branch; vectors outside the plane, and rows
+    // past it, load zeros (offsets past the buffer's range)
+    const int sk = min(lane & 15, G::NVEC - 1);
     const int gc = cb8 + 8 * sk;
-    const bool vk = sk < G::NVEC && gc >= 0 && gc + 8 <= a.IW;
+    const bool vk = gc >= 0 && gc + 8 <= a.IW;
+    const int lbase = vk ? ((lane >> 4) * a.IW + gc) * 2 : kR16Skip;  // batch 0's offset
+    const int bstep = 8 * a.IW;                                        // bytes of four rows
 
-    for (int e = lane; e < G::RING; e += 64) ring[e] = 0u;
-    roll_lds_sync();
+    for (int e = lane; e < O::RINGA / 4; e += 64) reinterpret_cast<uint4 *>(ring)[e] = make_uint4(0u, 0u, 0u, 0u);
 
     const float bias = (!FLIP && a.b) ? to_f32(a.b[c]) : 0.f;
     const uint16_t *wc = reinterpret_cast<const uint16_t *>(a.w) + static_cast<int64_t>(c) * K * K;
+    // the filter (flipped for grad-input), staged in the output buffer's place
+    // as rows i = -4 .. 15 of 16 values, zero outside the k x k filter: each
+    // phase's 8 values of a lane are one 16-byte LDS read
+    constexpr int FO = 4;  // rows of zeros before kernel row 0
+    static_assert(RPS - 1 <= FO && (FO + 16) * 8 <= O::DW, "staged filter fits");
+    for (int e = lane; e < (FO + 16) * 16; e += 64) {
+        const int i = e / 16 - FO, j = e % 16;
+        uint16_t v = 0;
+        if (i >= 0 && i < K && j < K) v = FLIP ? wc[(K - 1 - i) * K + (K - 1 - j)] : wc[i * K + j];
+        obuf[e] = v;
+    }
+    roll_lds_sync();
     const int64_t iplane = static_cast<int64_t>(a.IH) * a.IW;
     const int nq = ((a.IH + 15) >> 4) << 2;  // batches of four rows, whole groups of 16
-    const bool colfull = c_lo + 16 * NT <= a.OW;
-    // slot of accumulator row m = n (A lane row) and i0 - (RPS - 1) at step 0
-    const int slot = RPS == 4 ? 4 * (n & 3) + (n >> 2) : n;
-    const int i00 = ((RPS - 1 - slot) & 15) - (RPS - 1);
+    // A of phase f: lane (m, g) holds w[i0 + dl][j0 .. j0 + 7] (zero outside
+    // the filter), i0 = (RPS (f + 1) - 1 - s mod 16) - (RPS - 1) for the slot
+    // s = 4 (m mod 4) + m / 4 of accumulator row m
+    const int slot = 4 * (n & 3) + (n >> 2);
+    u32x4_r A[NPH];
+#pragma unroll
+    for (int f = 0; f < NPH; ++f) {
+        const int i = (((RPS * (f + 1) - 1 - slot) & 15) - (RPS - 1)) + dl;
+        const uint4 v = *reinterpret_cast<const uint4 *>(obuf + (i + FO) * 16 + j0);
+        A[f] = u32x4_r{v.x, v.y, v.z, v.w};
+    }
+    // output row oh sits in buffer row (oh - oh0) mod 32, oh0 = P - 16 the first
+    // row a step finishes, so a group of 32 buffer rows is whole steps
+    const int oh0 = a.P - 16;
+    const bool vout = a.OW % 8 == 0 && reinterpret_cast<uintptr_t>(a.out) % 16 == 0;
 
     for (int nimg = n0; nimg < n1; ++nimg) {
         const uint16_t *ip = reinterpret_cast<const uint16_t *>(a.in) + (static_cast<int64_t>(nimg) * a.Cin + cin) * iplane;
@@ -645,33 +690,48 @@ __global__ __launch_bounds__(256) void lk_rolls_kernel(Lr16Args<T> a) {
         const __amdgpu_buffer_rsrc_t irsrc =
             __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(ip), 0, static_cast<int>(iplane * 2), 0x00020000);
 
-        // A: lane (m, g) holds w[i0 + dl][j0 .. j0 + 7] (zero outside the filter)
-        u32x4_r A;
+        // buffered rows gb .. gb + 31 (those inside the plane) to memory, in the
+        // same number of stores every time
+        auto flush = [&](int gb) {
+            roll_lds_sync();  // the rows' LDS writes are done
+            if (vout) {
+                // 16-byte runs: 2 NT a row
 #pragma unroll
-        for (int k2 = 0; k2 < 4; ++k2) {
-            uint32_t v = 0;
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                const int i = i00 + dl, j = j0 + 2 * k2 + hh;
-                if (i >= 0 && i < K && j < K) {
-                    const uint16_t bits = FLIP ? wc[(K - 1 - i) * K + (K - 1 - j)] : wc[i * K + j];
-                    v |= static_cast<uint32_t>(bits) << (16 * hh);
+                for (int it = 0; it < O::ROWS * 2 * NT / 64; ++it) {
+                    const int e = lane + 64 * it;
+                    const int rl = e / (2 * NT);
+                    const int v8 = e % (2 * NT);
+                    const int rr = gb + rl;
+                    const int col = c_lo + 8 * v8;
+                    const uint4 val = *reinterpret_cast<const uint4 *>(obuf + 2 * ((rr - oh0) & (O::ROWS - 1)) * O::PITCH + 8 * v8);
+                    const int off = (rr >= 0 && rr < a.OH && col < a.OW) ? (rr * a.OW + col) * static_cast<int>(sizeof(T)) : kR16Skip;
+                    __builtin_amdgcn_raw_buffer_store_b128(u32x4_r{val.x, val.y, val.z, val.w}, orsrc, off, 0, 0);
+                }
+            } else {
+#pragma unroll 1
+                for (int it = 0; it < O::ROWS * 16 * NT / 64; ++it) {
+                    const int e = lane + 64 * it;
+                    const int rl = e / (16 * NT);
+                    const int cc = e % (16 * NT);
+                    const int rr = gb + rl;
+                    const uint16_t val = obuf[2 * ((rr - oh0) & (O::ROWS - 1)) * O::PITCH + cc];
+                    const int off = (rr >= 0 && rr < a.OH && c_lo + cc < a.OW) ? (rr * a.OW + c_lo + cc) * static_cast<int>(sizeof(T)) : kR16Skip;
+                    __builtin_amdgcn_raw_buffer_store_b16(val, orsrc, off, 0, 0);
                 }
             }
-            A[k2] = v;
-        }
+            roll_lds_sync();  // the rows are read before the buffer is reused
+        };
+
         f32x4_r d[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) d[t] = f32x4_r{bias, bias, bias, bias};
 
         auto load_batch = [&](int qb) -> uint4 {
-            const int r = 4 * qb + (lane >> 4);
-            const int off = (vk && r < a.IH) ? (r * a.IW + gc) * 2 : kR16Skip;
-            const u32x4_r v = __builtin_amdgcn_raw_buffer_load_b128(irsrc, off, 0, 0);
+            const u32x4_r v = __builtin_amdgcn_raw_buffer_load_b128(irsrc, lbase + qb * bstep, 0, 0);
             return make_uint4(v[0], v[1], v[2], v[3]);
         };
         auto write_batch = [&](int qb, const uint4 &raw) {
-            if (vk) ring_put_vec<G::RS>(ring, d1, (4 * qb + (lane >> 4)) & (G::SLOTS - 1), sk, raw);
+            ring_put_vec<G::RS>(ring, d1, (4 * qb + (lane >> 4)) & (G::SLOTS - 1), sk, raw);
         };
         auto stage_scalar = [&](int qb) {
             const int span = AL + G::XW;
@@ -685,89 +745,61 @@ __global__ __launch_bounds__(256) void lk_rolls_kernel(Lr16Args<T> a) {
                 ring_put_one<G::RS>(ring, d1, (4 * qb + q) & (G::SLOTS - 1), p, v);
             }
         };
-        uint4 raw = make_uint4(0u, 0u, 0u, 0u);
+        // every batch loads the same way (rows past the plane read zeros): the
+        // waits then count loads exactly
+        uint4 raw[PD];
         if constexpr (VIN) {
             write_batch(0, load_batch(0));
-            raw = load_batch(1);
+#pragma unroll
+            for (int b = 0; b < PD; ++b) raw[b] = load_batch(b + 1);
         } else {
             stage_scalar(0);
         }
 
-        // step p (PP = p mod 16 / RPS): input rows RPS p .. RPS p + RPS - 1
+        // step p (PP = p mod 16 / RPS, the filter phase): input rows RPS p .. RPS p + RPS - 1
         auto step = [&](auto pp_c, int p) {
             constexpr int PP = decltype(pp_c)::value;
-            const uint32_t *bp = ring + boff + ((RPS * PP) & (G::SLOTS - 1));
+            // a base of its own per step: the reads of two steps are not paired
+            // into one ds_read2 (which would scatter each operand's registers)
+            int boffs = boff + ((RPS * PP) & (G::SLOTS - 1));
+            asm volatile("" : "+v"(boffs));
+            const uint32_t *bp = ring + boffs;
             u32x4_r bv[NT];
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 const uint32_t *q = bp + G::RS * 8 * t;
                 bv[t] = u32x4_r{q[0], q[G::RS], q[2 * G::RS], q[3 * G::RS]};
             }
-            // the RPS slots RPS PP .. finish the output rows rho = RPS p + e - 16
-            // and start rho + 16 (at its bias)
-            float e0[NT], e1[NT];
-            if constexpr (RPS == 4) {
-                constexpr int R = PP & 3;  // register of sigma(4 PP + e) = 4 e + PP
+            // register R's four slots finish the output rows RPS p + g + oh0 (buffer
+            // row (RPS p + g) mod 32) and start the rows 16 later at the bias:
+            // every step (RPS 4) or every even step (RPS 2)
+            if constexpr (RPS == 4 || PP % 2 == 0) {
+                constexpr int R = RPS == 4 ? PP : PP / 2;
+                uint16_t *orow = obuf + 2 * ((RPS * p + g) & (O::ROWS - 1)) * O::PITCH + n;
 #pragma unroll
-                for (int t = 0; t < NT; ++t) {
-                    e0[t] = d[t][R];
-                    d[t][R] = bias;
+                for (int t = 0; t < NT; t += 2) {
+                    if (t + 1 < NT) {
+                        const uint32_t w2 = pack2<T>(d[t][R], d[t + 1][R]);
+                        orow[16 * t] = static_cast<uint16_t>(w2);
+                        orow[16 * t + 16] = static_cast<uint16_t>(w2 >> 16);
+                    } else {
+                        orow[16 * t] = bits16(d[t][R], static_cast<T *>(nullptr));
+                    }
                 }
-                const int oh = RPS * p + g - 16 + a.P;
-                const int off = (oh >= 0 && oh < a.OH) ? (oh * a.OW + c_lo) * static_cast<int>(sizeof(T)) + n2 : kR16Skip;
 #pragma unroll
-                for (int t = 0; t < NT; ++t)
-                    __builtin_amdgcn_raw_buffer_store_b16(bits16(e0[t], static_cast<T *>(nullptr)), orsrc,
-                                                          (colfull || c_lo + 16 * t + n < a.OW) ? off + 32 * t : kR16Skip, 0, 0);
-            } else {
-                constexpr int M0 = (2 * PP) & 15;        // slots M0, M0 + 1: lane row M0 / 4, registers M0 % 4, + 1
-                constexpr int R = M0 & 3;
-                const bool sel = g == (M0 >> 2);
-#pragma unroll
-                for (int t = 0; t < NT; ++t) {
-                    e0[t] = d[t][R];
-                    e1[t] = d[t][R + 1];
-                    d[t][R] = sel ? bias : d[t][R];
-                    d[t][R + 1] = sel ? bias : d[t][R + 1];
-                }
-                const int oh = RPS * p - 16 + a.P;
-                const int ub0 = (oh >= 0 && oh < a.OH) ? (oh * a.OW + c_lo) * static_cast<int>(sizeof(T)) : kR16Skip;
-                const int ub1 = (oh + 1 >= 0 && oh + 1 < a.OH) ? ((oh + 1) * a.OW + c_lo) * static_cast<int>(sizeof(T)) : kR16Skip;
-                const int off0 = sel ? ub0 + n2 : kR16Skip;
-                const int off1 = sel ? ub1 + n2 : kR16Skip;
-#pragma unroll
-                for (int t = 0; t < NT; ++t) {
-                    const bool cok = colfull || c_lo + 16 * t + n < a.OW;
-                    __builtin_amdgcn_raw_buffer_store_b16(bits16(e0[t], static_cast<T *>(nullptr)), orsrc,
-                                                          cok ? off0 + 32 * t : kR16Skip, 0, 0);
-                    __builtin_amdgcn_raw_buffer_store_b16(bits16(e1[t], static_cast<T *>(nullptr)), orsrc,
-                                                          cok ? off1 + 32 * t : kR16Skip, 0, 0);
-                }
+                for (int t = 0; t < NT; ++t) d[t][R] = bias;
             }
 #pragma unroll
-            for (int t = 0; t < NT; ++t) d[t] = RollMfma<T>::run(A, bv[t], d[t]);
-            // filter rows of the slots RPS behind: quad rotation (RPS 4) or two lanes (RPS 2)
-#pragma unroll
-            for (int k2 = 0; k2 < 4; ++k2) {
-                uint32_t r;
-                if constexpr (RPS == 4)
-                    r = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(A[k2]), 0x93, 0xf, 0xf, true));
-                else
-                    r = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(A[k2]), 0x122, 0xf, 0xf, true));
-                asm volatile("" : "+v"(r));
-                A[k2] = r;
-            }
+            for (int t = 0; t < NT; ++t) d[t] = RollMfma<T>::run(A[PP], bv[t], d[t]);
         };
         auto batch = [&](auto jb_c, int q) {
             constexpr int JB = decltype(jb_c)::value;
             roll_lds_sync();
-            if (q + 1 < nq) {
-                if constexpr (VIN) {
-                    write_batch(q + 1, raw);
-                    if (q + 2 < nq) raw = load_batch(q + 2);
-                } else {
-                    stage_scalar(q + 1);
-                }
+            if constexpr (VIN) {
+                write_batch(q + 1, raw[JB]);
+                raw[JB] = load_batch(q + 1 + PD);
+            } else {
+                if (q + 1 < nq) stage_scalar(q + 1);
             }
             const int p = SPB * q;
             if constexpr (RPS == 4) {
@@ -782,32 +814,40 @@ __global__ __launch_bounds__(256) void lk_rolls_kernel(Lr16Args<T> a) {
             batch(std::integral_constant<int, 1>{}, q + 1);
             batch(std::integral_constant<int, 2>{}, q + 2);
             batch(std::integral_constant<int, 3>{}, q + 3);
+            // 16 rows a pass: after every second pass 32 buffer rows are whole
+            if (((q + 4) & 7) == 0) flush(oh0 + 4 * (q + 4) - O::ROWS);
         }
-        roll_lds_sync();
 
         // every output row still in a slot is complete
         const int pl = SPB * nq - 1;  // last step
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int m = 4 * g + r;
-            const int sl = RPS == 4 ? 4 * (m & 3) + (m >> 2) : m;
+            const int sl = 4 * r + g;  // slot of accumulator row 4 g + r
+            // the last step is odd for RPS 2: no slot is between its early
+            // emission and its restart
             const int i0 = ((RPS * pl - sl + RPS - 1) & 15) - (RPS - 1);
             const int oh = RPS * pl - i0 + a.P;
-            if (oh < 0 || oh >= a.OH) continue;
-            T *orow = op + static_cast<int64_t>(oh) * a.OW + c_lo + n;
+            uint16_t *orow = obuf + 2 * ((oh - oh0) & (O::ROWS - 1)) * O::PITCH + n;
 #pragma unroll
-            for (int t = 0; t < NT; ++t)
-                if (c_lo + 16 * t + n < a.OW) orow[16 * t] = from_f32<T>(d[t][r]);
+            for (int t = 0; t < NT; ++t) orow[16 * t] = bits16(d[t][r], static_cast<T *>(nullptr));
         }
+        // the slots held relative rows 4 nq .. 4 nq + 15; with the 0 or 16 rows
+        // since the last whole group (4 nq is a multiple of 16) they fill at most
+        // one group, so none overwrote a row still to go out
+        flush(oh0 + 4 * nq - ((4 * nq) & (O::ROWS - 1)));
     }
 }
 
 template <typename T, int K, int NT, bool FLIP>
 int run_lrs_t(Lr16Args<T> a, hipStream_t s) {
     using G = Lr16Geo<K, NT, 8>;
+    constexpr int lds = 4 * 4 * RsOut<K, NT>::WAVE;
     a.nchunk = (a.OW + 16 * NT - 1) / (16 * NT);
     const int64_t items = static_cast<int64_t>(a.C) * a.nchunk;
-    const int64_t want = std::max<int64_t>(1, (static_cast<int64_t>(a.N) * items) >> 18);
+    // two images a wave on planes of at most 32 rows (the wave's set-up, its
+    // filter phases and first loads, then covers two planes: measured 6-12 %
+    // faster at 32 x 32, 3-15 % slower at 64 x 64), more past 2^18 waves
+    const int64_t want = std::max<int64_t>(a.IH <= 32 ? 2 : 1, (static_cast<int64_t>(a.N) * items) >> 18);
     a.ipw = static_cast<int>(std::min<int64_t>(want, a.N));
     a.nimgw = (a.N + a.ipw - 1) / a.ipw;
     const int64_t nw = items * a.nimgw;
@@ -815,9 +855,9 @@ int run_lrs_t(Lr16Args<T> a, hipStream_t s) {
     a.nwaves = static_cast<int>(nw);
     const dim3 grid(static_cast<unsigned>((nw + 3) / 4));
     if (a.vin)
-        hipLaunchKernelGGL((lk_rolls_kernel<T, K, NT, FLIP, true>), grid, dim3(256), G::lds_bytes, s, a);
+        hipLaunchKernelGGL((lk_rolls_kernel<T, K, NT, FLIP, true>), grid, dim3(256), lds, s, a);
     else
-        hipLaunchKernelGGL((lk_rolls_kernel<T, K, NT, FLIP, false>), grid, dim3(256), G::lds_bytes, s, a);
+        hipLaunchKernelGGL((lk_rolls_kernel<T, K, NT, FLIP, false>), grid, dim3(256), lds, s, a);
     return hipGetLastError() == hipSuccess ? kOk : kErrHip;
 }
 

@@ -238,6 +238,23 @@ def test_algo_candidates_and_selection_table(pass_, geo, dtype, must):
     assert N.dwconv2d_algo(pass_, *geo, dtype=dtype) == default
 
 
+@pytest.mark.parametrize("pass_,geo,dtype,want", [
+    (0, ((64, 384, 48, 48), (384, 13, 13), 1, 6, 1), torch.float16, "largek_roll16"),
+    (1, ((64, 384, 64, 64), (384, 7, 7), 1, 3, 1), torch.bfloat16, "largek_roll16"),
+    (0, ((64, 384, 32, 32), (384, 7, 7), 1, 3, 1), torch.bfloat16, "largek_roll16"),
+    (1, ((8, 64, 16, 16), (64, 13, 13), 1, 6, 1), torch.float16, None),   # below 32 x 32: the tiles
+    (0, ((8, 64, 100, 24), (64, 13, 13), 1, 6, 1), torch.float16, None),  # rows under 32 columns
+])
+def test_default_16bit_row_streaming(pass_, geo, dtype, want):
+    """16-bit 7 x 7 and 13 x 13 stream input rows on planes of at least 32 x 32."""
+    default = N.dwconv2d_algo(pass_, *geo, dtype=dtype)
+    if want:
+        assert default == want
+    else:
+        assert default != "largek_roll16"
+        assert "largek_roll16" in N.dwconv2d_algo_candidates(pass_, *geo, dtype=dtype)
+
+
 def test_algo_candidates_validation():
     L = N.lib()
     names = (ctypes.c_char_p * 4)()

@@ -654,7 +654,7 @@ def test_large_kernel_shapes(n, c, h, w, mult, k, p, dt):
     (2, 2, 20, 22, 1, 13, 12, "f16", True, True),     # pad k - 1: grad-input pad 0
     (4, 2, 47, 47, 1, 7, 2, "bf16", True, True),      # k = 7, odd sizes
     (2, 2, 9, 9, 1, 31, 15, "f16", True, True),       # kernel wider than the image
-    (1, 2, 100, 64, 1, 13, 6, "f16", False, False),   # more than 64 rows: register-tile kernels
+    (1, 2, 100, 24, 1, 13, 6, "f16", False, False),   # more than 64 rows, under 32 columns: register-tile kernels
 ])
 def test_large_kernel_mfma(n, c, h, w, mult, k, p, dt, fwd_mfma, bin_mfma):
     """The 32 x 32-tile family (at k = 7 on planes over 32 the 16 x 16 tiles are the default, so it is forced)."""
