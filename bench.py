@@ -131,15 +131,21 @@ def valid_taps(in_n, out_n, k, s, p, d):
 
 # kernel families that run 16-bit I/O on the matrix cores (tag infixes)
 MATRIX16_FAMILIES = (".largek_mfma.", ".largek_mfma_h16.", ".largek_roll16.")
+MATRIX32_FAMILIES = (".largek_mfma_f32.", ".largek_mfma_t16.", ".largek_roll_f32.")
 
 
 def tag_peak(tag, kind):
     """(bound, peak, unit) of a kernel tag: HBM for bandwidth-bound workloads; for
-    flop-counted ones the matrix-core peak of 16-bit I/O on the matrix cores, else fp32."""
+    flop-counted ones the matrix-core peak of 16-bit I/O on the matrix cores, the
+    fp32 matrix peak of fp32 matrix families, else the fp32 vector peak (the two
+    fp32 peaks are the same figure)."""
     if kind == "bytes":
         return "hbm", HBM_PEAK_GBS, "GB/s"
-    matrix16 = any(f in tag for f in MATRIX16_FAMILIES) and not tag.endswith("_f32")
-    return ("mfma", F16_MATRIX_PEAK_TFLOPS, "TFLOP/s") if matrix16 else ("alu", FP32_PEAK_TFLOPS, "TFLOP/s")
+    if any(f in tag for f in MATRIX16_FAMILIES) and not tag.endswith("_f32"):
+        return "mfma", F16_MATRIX_PEAK_TFLOPS, "TFLOP/s"
+    if any(f in tag for f in MATRIX32_FAMILIES):
+        return "mfma", FP32_PEAK_TFLOPS, "TFLOP/s"
+    return "alu", FP32_PEAK_TFLOPS, "TFLOP/s"
 
 
 class Call:
@@ -394,7 +400,7 @@ def ceiling_of(tag, kind, rfrac, ceil):
         return v, "GB/s", "stream (read share %.2f)" % rfrac
     if any(f in tag for f in MATRIX16_FAMILIES) and not tag.endswith("_f32"):
         return ceil["mfma_f16_tflops"], "TFLOP/s", "fp16 matrix instructions"
-    if ".largek_mfma_f32." in tag or ".largek_mfma_t16." in tag:
+    if any(f in tag for f in MATRIX32_FAMILIES):
         return ceil["mfma_f32_tflops"], "TFLOP/s", "fp32 matrix instructions"
     return ceil["valu_fma_f32_tflops"], "TFLOP/s", "fp32 vector FMA"
 

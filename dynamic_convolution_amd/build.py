@@ -39,6 +39,7 @@ FLAGS = [
 EXTRA_FLAGS = {
     "dw_largek_roll16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "dw_largek_wroll16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "dw_largek_rollf32.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -240,14 +240,14 @@ int run_bwd_input(const Geo &g, const BandPlan &bp, int seg_slots, const void *d
 
 enum BinAlgo {
     kBinRowwalk = 0, kBinLargek, kBinDecim, kBinBand33s1, kBinBand33s2, kBinBand55s1, kBinBand55s2d2, kBinBandGeneric,
-    kBinChannelGroup, kBinLargekMfma, kBinLargekMfma32, kBinDirect, kBinLargekMfmaH16, kBinLargekRoll16, kBinCount
+    kBinChannelGroup, kBinLargekMfma, kBinLargekMfma32, kBinDirect, kBinLargekMfmaH16, kBinLargekRoll16, kBinLargekRollF32, kBinCount
 };
 
 const char *const kBinNames[kBinCount] = {"rowwalk_3x3",    "largek_regtile", "decimated_s2d2",
                                           "band_3x3_s1",    "band_3x3_s2",    "band_5x5_s1",
                                           "band_5x5_s2_d2", "band_generic",   "channelgroup_small",
                                           "largek_mfma",    "largek_mfma_f32", "direct",
-                                          "largek_mfma_h16", "largek_roll16"};
+                                          "largek_mfma_h16", "largek_roll16",  "largek_roll_f32"};
 
 bool band_bin_plans(const Geo &g, int dt) {
     BandPlan bp;
@@ -266,6 +266,7 @@ bool feasible_bin(int algo, const Geo &g, int dt) {
         case kBinLargekMfma32: return largek_fwd32_fits(g, 1, dt);
         case kBinLargekMfmaH16: return largek_mfma16_fits(g, 1, dt);
         case kBinLargekRoll16: return largek_roll16_fits(g, 1, dt);
+        case kBinLargekRollF32: return largek_rollf32_fits(g, 1, dt);
         case kBinBand33s1: return sq && g.kh == 3 && g.sh == 1 && g.dh == 1 && band_bin_plans(g, dt);
         case kBinBand33s2: return sq && g.kh == 3 && g.sh == 2 && g.dh == 1 && band_bin_plans(g, dt);
         case kBinBand55s1: return sq && g.kh == 5 && g.sh == 1 && g.dh == 1 && band_bin_plans(g, dt);
@@ -292,6 +293,10 @@ int select_bwd_input(const Geo &g, int dt) {
     if (g.kh == 7 && (g.ih > 32 || g.iw > 32) && largek_mfma16_fits(g, 1, dt)) return kBinLargekMfmaH16;
     // 16-bit 31 x 31: input rows streamed through rotating filter rows
     if (g.kh == 31 && largek_roll16_fits(g, 1, dt)) return kBinLargekRoll16;
+    // fp32 31 x 31 on planes of at least 32 x 32: input rows streamed past
+    // rotating filter rows, measured 1.05-1.27x faster than the kernel-row
+    // contraction, whose anti-diagonal sums add vector work to the matrix time
+    if (g.kh == 31 && g.ih >= 32 && g.ow >= 32 && largek_rollf32_fits(g, 1, dt)) return kBinLargekRollF32;
     if (largek_mfma_fits(g, 1, dt)) return kBinLargekMfma;
     if (largek_fwd32_fits(g, 1, dt) && largek_fwd32_preferred(g, 1)) return kBinLargekMfma32;
     if (largek_fits(g, 1)) return kBinLargek;
@@ -314,6 +319,7 @@ int dispatch_bwd_input(const Geo &g, const void *dy, const void *w, void *dx, hi
     if (algo == kBinLargekMfma32) return largek_bwd_input32(g, dy, w, dx, s);
     if (algo == kBinLargekMfmaH16) return largek_mfma16_bwd_input(g, dy, w, dx, dt, s);
     if (algo == kBinLargekRoll16) return largek_roll16_bwd_input(g, dy, w, dx, dt, s);
+    if (algo == kBinLargekRollF32) return largek_rollf32_bwd_input(g, dy, w, dx, s);
     if (algo == kBinDecim) return decim_bwd_input(g, dy, w, dx, dt, s);
     if (algo == kBinChannelGroup) return small_bwd_input(g, dy, w, dx, dt, s);
     if (algo == kBinDirect) return direct_bwd_input(g, dy, w, dx, dt, s);

@@ -91,6 +91,11 @@ int largek_mfma16_bwd_input(const Geo &g, const void *dy, const void *w, void *d
 bool largek_roll16_fits(const Geo &g, int pass, int dtype);
 int largek_roll16_fwd(const Geo &g, const void *x, const void *w, const void *b, void *y, int dtype, hipStream_t s);
 int largek_roll16_bwd_input(const Geo &g, const void *dy, const void *w, void *dx, int dtype, hipStream_t s);
+// fp32 31 x 31 forward / grad-input streaming input rows through rotating
+// filter rows on the matrix cores (dw_largek_rollf32.hip); any plane size.
+bool largek_rollf32_fits(const Geo &g, int pass, int dtype);
+int largek_rollf32_fwd(const Geo &g, const void *x, const void *w, const void *b, void *y, hipStream_t s);
+int largek_rollf32_bwd_input(const Geo &g, const void *dy, const void *w, void *dx, hipStream_t s);
 // 16-bit k = 13 / 31 grad-weight streaming input rows, the dy rows moving
 // through the filter-row slots (dw_largek_wroll16.hip); output rows <= 64.
 bool largek_wroll16_fits(const Geo &g, int dtype);

@@ -244,15 +244,19 @@ def test_algo_candidates_and_selection_table(pass_, geo, dtype, must):
     (0, ((64, 384, 32, 32), (384, 7, 7), 1, 3, 1), torch.bfloat16, "largek_roll16"),
     (1, ((8, 64, 16, 16), (64, 13, 13), 1, 6, 1), torch.float16, None),   # below 32 x 32: the tiles
     (0, ((8, 64, 100, 24), (64, 13, 13), 1, 6, 1), torch.float16, None),  # rows under 32 columns
+    (0, ((64, 384, 48, 48), (384, 31, 31), 1, 15, 1), torch.float32, "largek_roll_f32"),
+    (1, ((64, 384, 32, 32), (384, 31, 31), 1, 15, 1), torch.float32, "largek_roll_f32"),
+    (1, ((8, 64, 16, 16), (64, 31, 31), 1, 15, 1), torch.float32, None),   # below 32 x 32
 ])
-def test_default_16bit_row_streaming(pass_, geo, dtype, want):
-    """16-bit 7 x 7 and 13 x 13 stream input rows on planes of at least 32 x 32."""
+def test_default_row_streaming(pass_, geo, dtype, want):
+    """16-bit 7 x 7 and 13 x 13, and fp32 31 x 31, stream input rows on planes of at least 32 x 32."""
+    fam = "largek_roll16" if dtype != torch.float32 else "largek_roll_f32"
     default = N.dwconv2d_algo(pass_, *geo, dtype=dtype)
     if want:
         assert default == want
     else:
-        assert default != "largek_roll16"
-        assert "largek_roll16" in N.dwconv2d_algo_candidates(pass_, *geo, dtype=dtype)
+        assert default != fam
+        assert fam in N.dwconv2d_algo_candidates(pass_, *geo, dtype=dtype)
 
 
 def test_algo_candidates_validation():

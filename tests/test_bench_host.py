@@ -98,6 +98,9 @@ def test_ceiling_model():
     assert bench.ceiling_of("fwd.largek_mfma_h16.k7_s1_m1_bf16", "flops", 1, ceil)[0] == 2000.0
     assert bench.ceiling_of("bwd_input.largek_roll16.k31_s1_m1_f16", "flops", 1, ceil)[0] == 2000.0
     assert bench.tag_peak("fwd.largek_roll16.k31_s1_m1_bf16", "flops")[0] == "mfma"
+    assert bench.tag_peak("fwd.largek_roll_f32.k31_s1_m1_f32", "flops") == ("mfma", bench.FP32_PEAK_TFLOPS, "TFLOP/s")
+    assert bench.tag_peak("bwd_weight.largek_regtile.k7_s1_m1_f32", "flops")[0] == "alu"
+    assert bench.ceiling_of("bwd_input.largek_roll_f32.k31_s1_m1_f32", "flops", 1, ceil)[1:] == ("TFLOP/s", "fp32 matrix instructions")
     assert bench.ceiling_of("bwd_weight.stream_7x7.k7_s1_m1_f16", "flops", 1, ceil)[0] == 100.0
     assert bench.ceiling_of("fwd.largek_regtile.k13_s1_m1_f32", "flops", 1, ceil)[0] == 100.0
     assert bench.ceiling_of("bwd_weight.largek_mfma_t16.k13_s1_m1_f32", "flops", 1, ceil)[0] == 140.0

@@ -1024,6 +1024,42 @@ def test_large_kernel_row_stream_16bit(n, c, h, w, mult, p, dt, bin_ok):
     run_row_stream_16bit(n, c, h, w, mult, 31, p, dt, bin_ok)
 
 
+# fp32 31 x 31 forward / grad-input on the same streaming (forced family): the
+# workload's planes, element-staged widths (not a multiple of 4), column chunks
+# with a ragged last one, pad 0 and pad k - 1, a multiplier, a kernel wider
+# than the image, and fewer input rows than one batch.
+@pytest.mark.gpu
+@pytest.mark.parametrize("n,c,h,w,mult,p,bin_ok", [
+    (2, 3, 32, 32, 1, 15, True),
+    (2, 2, 48, 48, 1, 15, True),
+    (2, 2, 64, 64, 1, 15, True),
+    (1, 2, 47, 47, 1, 15, True),     # element staging, ragged 16-column tile
+    (2, 1, 33, 29, 1, 15, True),
+    (1, 2, 21, 150, 1, 15, True),    # three column chunks, the last ragged
+    (1, 1, 12, 264, 1, 15, True),    # five chunks, vector staging
+    (2, 2, 40, 40, 1, 0, True),      # pad 0: grad-input pad 30
+    (2, 2, 26, 22, 1, 30, True),     # pad k - 1: grad-input pad 0
+    (2, 2, 30, 34, 2, 15, False),    # multiplier 2 (forward only)
+    (2, 2, 9, 9, 1, 15, True),       # kernel wider than the image
+    (1, 2, 5, 70, 1, 15, True),      # fewer input rows than one batch
+])
+def test_large_kernel_row_stream_f32(n, c, h, w, mult, p, bin_ok):
+    geo = ((n, c, h, w), (c * mult, 31, 31), 1, p, 1)
+    assert "largek_roll_f32" in dc.dwconv2d_algo_candidates(0, *geo, dtype=torch.float32)
+    assert ("largek_roll_f32" in dc.dwconv2d_algo_candidates(1, *geo, dtype=torch.float32)) == bin_ok
+    x, wt, b, dy = static_case(n, c, h, w, mult, 31, 1, p, 1, torch.float32, 2400 + h + w + p + mult)
+    try:
+        dc.dwconv2d_set_algo(0, *geo, dtype=torch.float32, algo="largek_roll_f32")
+        if bin_ok:
+            dc.dwconv2d_set_algo(1, *geo, dtype=torch.float32, algo="largek_roll_f32")
+        check_static(x, wt, b, dy, 1, p, 1, "largek-roll-f32 n%d c%d %dx%d m%d p%d" % (n, c, h, w, mult, p),
+                     passes=("fwd", "bwd_in") if bin_ok else ("fwd",))
+    finally:
+        dc.dwconv2d_set_algo(0, *geo, dtype=torch.float32, algo=None)
+        if bin_ok:
+            dc.dwconv2d_set_algo(1, *geo, dtype=torch.float32, algo=None)
+
+
 # k = 7 and 13 on the same streaming: four input rows (k = 7) or two (k = 13)
 # per contraction; odd heights, element staging, chunks, pad 0 and k - 1, a
 # multiplier, kernels wider than the image.
