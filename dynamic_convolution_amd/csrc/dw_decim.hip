@@ -71,9 +71,9 @@ __device__ __forceinline__ void halo_window(const float (&v)[RO], int lane, bool
                                             float (&win)[RO + 2 * HH]) {
 #pragma unroll
     for (int e = 0; e < HH; ++e) {
-        const float l = __shfl(v[RO - HH + e], lane - 1, 64);
+        const float l = lane_left(v[RO - HH + e]);
         win[e] = has_left ? l : 0.f;
-        const float r = __shfl(v[e], lane + 1, 64);
+        const float r = lane_right(v[e]);
         win[HH + RO + e] = has_right ? r : 0.f;
     }
 #pragma unroll
@@ -220,9 +220,9 @@ __device__ __forceinline__ void xrow_pairs(const uint32_t (&w)[kXWords<T>], bool
     for (int e = 0; e < RO; ++e) v[e] = ok ? w[e] : 0u;
 #pragma unroll
     for (int e = 0; e < HH; ++e) {
-        const uint32_t l = static_cast<uint32_t>(__shfl(static_cast<int>(v[RO - HH + e]), lane - 1, 64));
+        const uint32_t l = static_cast<uint32_t>(lane_left(static_cast<uint32_t>(v[RO - HH + e])));
         W[e] = hl ? l : 0u;
-        const uint32_t r = static_cast<uint32_t>(__shfl(static_cast<int>(v[e]), lane + 1, 64));
+        const uint32_t r = static_cast<uint32_t>(lane_right(static_cast<uint32_t>(v[e])));
         W[HH + RO + e] = hr ? r : 0u;
     }
 #pragma unroll

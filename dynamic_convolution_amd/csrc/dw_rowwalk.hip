@@ -55,12 +55,12 @@ template <typename T> struct RwArgs {
 template <int IRW, int S>
 __device__ __forceinline__ void make_window(const float (&v)[IRW], int lane, bool has_left, bool has_right,
                                             float (&win)[IRW + (S == 1 ? 2 : 1)]) {
-    const float l = __shfl(v[IRW - 1], lane - 1, 64);
+    const float l = lane_left(v[IRW - 1]);
     win[0] = has_left ? l : 0.f;
 #pragma unroll
     for (int e = 0; e < IRW; ++e) win[1 + e] = v[e];
     if constexpr (S == 1) {
-        const float r = __shfl(v[0], lane + 1, 64);
+        const float r = lane_right(v[0]);
         win[IRW + 1] = has_right ? r : 0.f;
     }
 }
@@ -249,7 +249,7 @@ __global__ __launch_bounds__(kThreads) void rw_bwdin3_s2_kernel(RwArgs<T> a) {
         float v[DRW];
         load_row<T, ND, VD>(dp[m], r0, g.oh, g.ow, c0, u.act, w, ok);
         row_values<T>(w, ok, nd, v);
-        const float rr = __shfl(v[0], u.lane + 1, 64);
+        const float rr = lane_right(v[0]);
 #pragma unroll
         for (int e = 0; e < DRW; ++e) cur[m][e] = v[e];
         cur[m][DRW] = has_right ? rr : 0.f;
@@ -264,7 +264,7 @@ __global__ __launch_bounds__(kThreads) void rw_bwdin3_s2_kernel(RwArgs<T> a) {
             row_values<T>(rq[m][0], rk[m][0], nd, v);
             ring_pop<R, ND>(rq[m], rk[m]);
             load_row<T, ND, VD>(dp[m], min(r + 1 + R, rlast), g.oh, g.ow, c0, u.act, rq[m][R - 1], rk[m][R - 1]);
-            const float rr = __shfl(v[0], u.lane + 1, 64);
+            const float rr = lane_right(v[0]);
 #pragma unroll
             for (int e = 0; e < DRW; ++e) nxt[m][e] = v[e];
             nxt[m][DRW] = has_right ? rr : 0.f;

@@ -140,26 +140,80 @@ __device__ __forceinline__ float uniform(float v) {
     return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
 }
 
+// Value of lane - 1 (DPP wave_shr:1) and of lane + 1 (wave_shl:1), 0 past the
+// wave's ends, without LDS traffic.  A DPP move reads a lane that EXEC
+// disables as zero, so callers run it with every lane enabled; the empty
+// volatile asm keeps the compiler from sinking it under a later branch.
+__device__ __forceinline__ float lane_left(float v) {
+    int r = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x138, 0xf, 0xf, true);
+    asm volatile("" : "+v"(r));
+    return __int_as_float(r);
+}
+__device__ __forceinline__ float lane_right(float v) {
+    int r = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x130, 0xf, 0xf, true);
+    asm volatile("" : "+v"(r));
+    return __int_as_float(r);
+}
+__device__ __forceinline__ uint32_t lane_left(uint32_t v) {
+    return __float_as_uint(lane_left(__uint_as_float(v)));
+}
+__device__ __forceinline__ uint32_t lane_right(uint32_t v) {
+    return __float_as_uint(lane_right(__uint_as_float(v)));
+}
+
+// Partner value of the lane paired with this one inside its 16-lane row at
+// halving step o <= 8 (DPP, no LDS): row_mirror (lane i ^ 15) for o = 8,
+// row_half_mirror (i ^ 7) for o = 4, quad_perm (i ^ 2, i ^ 1) for o = 2, 1.
+// Each partner differs from the lane in bit o and agrees on every bit above
+// it, which is all the halving below needs.
+template <int O> __device__ __forceinline__ float row_partner(float v) {
+    constexpr int ctrl = O == 8 ? 0x140 : O == 4 ? 0x141 : O == 2 ? 0x4e : 0xb1;
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), ctrl, 0xf, 0xf, true));
+}
+
 // Sums of N <= 64 per-lane values over the wave, by recursive halving: at the
 // step with lane offset o every lane keeps one half of its current vector,
-// sends the other half to lane ^ o and adds what it receives, so after six
-// steps lane l holds the total of value l (63 shuffles instead of 6 per value).
+// sends the other half to its partner (a lane that differs in bit o) and adds
+// what it receives, so after six steps lane l holds the total of value l
+// (63 exchanges instead of 6 per value).  The exchanges across 32 and 16
+// lanes are v_permlane32_swap / v_permlane16_swap of the two halves (one swap
+// leaves each lane its kept value and its partner's sent one, the sum of the
+// two results), the ones inside 16-lane rows are DPP moves: no LDS traffic.
 template <int N>
 __device__ __forceinline__ float wave_transpose_sum(const float (&v)[N], int lane) {
     static_assert(N <= 64, "one value per lane");
     float c[64];
 #pragma unroll
     for (int i = 0; i < 64; ++i) c[i] = i < N ? v[i] : 0.f;
+    auto swap_step = [&](auto o_c) {
+        constexpr int o = decltype(o_c)::value;
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
+        for (int i = 0; i < o; ++i) {
+            // lower lanes keep c[i], upper lanes c[i + o]: after the swap the
+            // first result holds the lower lanes' c[i] and the upper lanes'
+            // partner c[i + o], the second the partner c[i] and own c[i + o]
+            const uint32_t x = __float_as_uint(c[i]), y = __float_as_uint(c[i + o]);
+            auto r = o == 32 ? __builtin_amdgcn_permlane32_swap(x, y, false, false)
+                             : __builtin_amdgcn_permlane16_swap(x, y, false, false);
+            c[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+        }
+    };
+    auto row_step = [&](auto o_c) {
+        constexpr int o = decltype(o_c)::value;
         const bool upper = (lane & o) != 0;  // this lane keeps indices [o, 2o) of the current vector
 #pragma unroll
         for (int i = 0; i < o; ++i) {
             const float keep = upper ? c[i + o] : c[i];
             const float send = upper ? c[i] : c[i + o];
-            c[i] = keep + __shfl_xor(send, o, 64);
+            c[i] = keep + row_partner<o>(send);
         }
-    }
+    };
+    swap_step(std::integral_constant<int, 32>{});
+    swap_step(std::integral_constant<int, 16>{});
+    row_step(std::integral_constant<int, 8>{});
+    row_step(std::integral_constant<int, 4>{});
+    row_step(std::integral_constant<int, 2>{});
+    row_step(std::integral_constant<int, 1>{});
     return c[0];
 }
 
