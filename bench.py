@@ -102,7 +102,9 @@ def parse(argv=None):
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
                     help="write profiles/traffic_<--only-tag>.json from two rocprofv3 --pmc runs and exit")
     ap.add_argument("--launches", type=int, default=0,
-                    help="calls of the tag in the counter runs (0: the dispatch count of its kernels)")
+                    help="calls of the tag in the counter runs (0: the largest dispatch count of one of "
+                         "its kernels, right when every call launches each kernel once; give it when the "
+                         "tag's cases launch different instantiations)")
     ap.add_argument("--cmd", default="", help="command recorded with the traffic figures")
     return ap.parse_args(argv)
 
