@@ -128,28 +128,39 @@ __global__ __launch_bounds__(256) void lk_wgrad16_kernel(Lw16Args<T> a) {
     constexpr int NXV = PF ? kW16Nx<T> : 1, NDV = PF ? kW16Nd<T> : 1;
     const int nsteps = (n1 - n0) * a.nbands;
     uint4 pfx[NXV], pfd[NDV];
+    // each thread's vectors (row, element column) are the same for every band:
+    // divided once here, not per band
+    const int xv = PF ? a.IW / VE : 1, dv = PF ? a.OW / VE : 1;
+    int xr_[NXV], xc_[NXV], dr_[NDV], dc_[NDV];
+#pragma unroll
+    for (int k = 0; k < NXV; ++k) {
+        const int v = tid + 256 * k;
+        xr_[k] = v / xv;
+        xc_[k] = (v - xr_[k] * xv) * VE;
+    }
+#pragma unroll
+    for (int k = 0; k < NDV; ++k) {
+        const int v = tid + 256 * k;
+        dr_[k] = v / dv;
+        dc_[k] = (v - dr_[k] * dv) * VE;
+    }
     auto prefetch = [&](int t) {
         const int n = n0 + t / a.nbands, oh0 = (t % a.nbands) * a.BH;
         const int rows = min(a.BH, a.OH - oh0);
         const T *xp = a.x + (static_cast<int64_t>(n) * a.C + c) * a.IH * a.IW;
         const T *dp = a.dy + (static_cast<int64_t>(n) * a.C + c) * a.OH * a.OW;
-        const int xv = a.IW / VE, dv = a.OW / VE;
 #pragma unroll
         for (int k = 0; k < NXV; ++k) {
-            const int v = tid + 256 * k;
-            const int r = v / xv;
-            const int ih = oh0 + r - a.P;
+            const int ih = oh0 + xr_[k] - a.P;
             pfx[k] = make_uint4(0u, 0u, 0u, 0u);
-            if (v < (rows + K - 1) * xv && ih >= 0 && ih < a.IH)
-                pfx[k] = *reinterpret_cast<const uint4 *>(xp + static_cast<int64_t>(ih) * a.IW + (v - r * xv) * VE);
+            if (xr_[k] < rows + K - 1 && ih >= 0 && ih < a.IH)
+                pfx[k] = *reinterpret_cast<const uint4 *>(xp + static_cast<int64_t>(ih) * a.IW + xc_[k]);
         }
 #pragma unroll
         for (int k = 0; k < NDV; ++k) {
-            const int v = tid + 256 * k;
-            const int r = v / dv;
             pfd[k] = make_uint4(0u, 0u, 0u, 0u);
-            if (v < rows * dv)
-                pfd[k] = *reinterpret_cast<const uint4 *>(dp + static_cast<int64_t>(oh0 + r) * a.OW + (v - r * dv) * VE);
+            if (dr_[k] < rows)
+                pfd[k] = *reinterpret_cast<const uint4 *>(dp + static_cast<int64_t>(oh0 + dr_[k]) * a.OW + dc_[k]);
         }
     };
     if (PF && nsteps > 0) prefetch(0);
@@ -167,15 +178,13 @@ __global__ __launch_bounds__(256) void lk_wgrad16_kernel(Lw16Args<T> a) {
                 const int xv = a.IW / VE, dv = a.OW / VE;
 #pragma unroll
                 for (int k = 0; k < NXV; ++k) {
-                    const int v = tid + 256 * k;
-                    if (v < (rows + K - 1) * xv) {
-                        const int r = v / xv;
+                    if (xr_[k] < rows + K - 1) {
                         union {
                             uint4 u;
                             T t[VE];
                         } raw;
                         raw.u = pfx[k];
-                        float4 *d = reinterpret_cast<float4 *>(xs + r * a.XP + (v - r * xv) * VE);
+                        float4 *d = reinterpret_cast<float4 *>(xs + xr_[k] * a.XP + xc_[k]);
 #pragma unroll
                         for (int e = 0; e < VE / 4; ++e)
                             d[e] = make_float4(to_f32(raw.t[4 * e]), to_f32(raw.t[4 * e + 1]), to_f32(raw.t[4 * e + 2]),
@@ -184,19 +193,20 @@ __global__ __launch_bounds__(256) void lk_wgrad16_kernel(Lw16Args<T> a) {
                 }
 #pragma unroll
                 for (int k = 0; k < NDV; ++k) {
-                    const int v = tid + 256 * k;
-                    if (v < rows * dv) {
-                        const int r = v / dv;
+                    if (dr_[k] < rows) {
                         union {
                             uint4 u;
                             T t[VE];
                         } raw;
                         raw.u = pfd[k];
-                        float4 *d = reinterpret_cast<float4 *>(dz + a.D0 + r * a.L + (v - r * dv) * VE);
+                        float4 *d = reinterpret_cast<float4 *>(dz + a.D0 + dr_[k] * a.L + dc_[k]);
 #pragma unroll
-                        for (int e = 0; e < VE / 4; ++e)
-                            d[e] = make_float4(to_f32(raw.t[4 * e]), to_f32(raw.t[4 * e + 1]), to_f32(raw.t[4 * e + 2]),
-                                               to_f32(raw.t[4 * e + 3]));
+                        for (int e = 0; e < VE / 4; ++e) {
+                            const float4 q = make_float4(to_f32(raw.t[4 * e]), to_f32(raw.t[4 * e + 1]),
+                                                         to_f32(raw.t[4 * e + 2]), to_f32(raw.t[4 * e + 3]));
+                            d[e] = q;
+                            dsum += (q.x + q.y) + (q.z + q.w);  // bias gradient, this thread's vectors in order
+                        }
                     }
                 }
             } else {
@@ -205,10 +215,13 @@ __global__ __launch_bounds__(256) void lk_wgrad16_kernel(Lw16Args<T> a) {
             }
             __syncthreads();
             if (PF && t + 1 < nsteps) prefetch(t + 1);
-            // bias gradient: the band's dy values, summed per thread in a fixed order
-            for (int e = tid; e < rows * a.OW; e += 256) {
-                const int r = e / a.OW;
-                dsum += dz[r * a.L + a.D0 + (e - r * a.OW)];
+            // bias gradient (the prefetching variant sums the dy vectors as it
+            // stages them): the band's dy values, summed per thread in a fixed order
+            if constexpr (!PF) {
+                for (int e = tid; e < rows * a.OW; e += 256) {
+                    const int r = e / a.OW;
+                    dsum += dz[r * a.L + a.D0 + (e - r * a.OW)];
+                }
             }
             for (int oh = wave; oh < rows; oh += 4) {
                 // A: x row oh + i, column base + 4 kq + t; B: dz[oh][base + 4 kq + t - j + 15]
