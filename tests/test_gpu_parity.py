@@ -1018,7 +1018,8 @@ def test_large_kernel_16bit_small_tiles(n, c, h, w, mult, k, p, dt, bin_h):
     (2, 2, 30, 34, 2, 15, "f16", False),    # multiplier 2 (forward only)
     (2, 2, 9, 9, 1, 15, "bf16", True),      # kernel wider than the image
     (1, 2, 5, 70, 1, 15, "f16", True),      # fewer input rows than one batch of four
-    (8, 2048, 16, 16, 1, 15, "f16", True),  # two images a wave
+    (8, 2048, 16, 16, 1, 15, "f16", True),  # many waves of few rows
+    (4, 131073, 1, 1, 1, 15, "bf16", True),  # over 2^19 planes: two images a wave
 ])
 def test_large_kernel_row_stream_16bit(n, c, h, w, mult, p, dt, bin_ok):
     run_row_stream_16bit(n, c, h, w, mult, 31, p, dt, bin_ok)
@@ -1027,7 +1028,8 @@ def test_large_kernel_row_stream_16bit(n, c, h, w, mult, p, dt, bin_ok):
 # fp32 31 x 31 forward / grad-input on the same streaming (forced family): the
 # workload's planes, element-staged widths (not a multiple of 4), column chunks
 # with a ragged last one, pad 0 and pad k - 1, a multiplier, a kernel wider
-# than the image, and fewer input rows than one batch.
+# than the image, fewer input rows than one batch, and more than 2^19 planes
+# (each wave then walks two images).
 @pytest.mark.gpu
 @pytest.mark.parametrize("n,c,h,w,mult,p,bin_ok", [
     (2, 3, 32, 32, 1, 15, True),
@@ -1042,6 +1044,7 @@ def test_large_kernel_row_stream_16bit(n, c, h, w, mult, p, dt, bin_ok):
     (2, 2, 30, 34, 2, 15, False),    # multiplier 2 (forward only)
     (2, 2, 9, 9, 1, 15, True),       # kernel wider than the image
     (1, 2, 5, 70, 1, 15, True),      # fewer input rows than one batch
+    (4, 131073, 1, 1, 1, 15, True),  # over 2^19 planes: two images a wave
 ])
 def test_large_kernel_row_stream_f32(n, c, h, w, mult, p, bin_ok):
     geo = ((n, c, h, w), (c * mult, 31, 31), 1, p, 1)
