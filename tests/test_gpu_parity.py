@@ -1045,6 +1045,9 @@ def test_large_kernel_row_stream_16bit(n, c, h, w, mult, p, dt, bin_ok):
     (2, 2, 9, 9, 1, 15, True),       # kernel wider than the image
     (1, 2, 5, 70, 1, 15, True),      # fewer input rows than one batch
     (4, 131073, 1, 1, 1, 15, True),  # over 2^19 planes: two images a wave
+    (2, 2, 64, 40, 1, 7, True),      # pad 7 (grad-input pad 23), H != W
+    (1, 3, 37, 61, 3, 15, False),    # multiplier 3, element staging
+    (2, 2, 50, 33, 1, 20, True),     # pad 20: output 60 x 43
 ])
 def test_large_kernel_row_stream_f32(n, c, h, w, mult, p, bin_ok):
     geo = ((n, c, h, w), (c * mult, 31, 31), 1, p, 1)
@@ -1061,6 +1064,20 @@ def test_large_kernel_row_stream_f32(n, c, h, w, mult, p, bin_ok):
         dc.dwconv2d_set_algo(0, *geo, dtype=torch.float32, algo=None)
         if bin_ok:
             dc.dwconv2d_set_algo(1, *geo, dtype=torch.float32, algo=None)
+
+
+@pytest.mark.gpu
+def test_large_kernel_row_stream_f32_no_bias():
+    """The fp32 stream's forward without a bias starts every output row at zero."""
+    n, c, h, w, p = 2, 3, 48, 48, 15
+    geo = ((n, c, h, w), (c, 31, 31), 1, p, 1)
+    x, wt, b, dy = static_case(n, c, h, w, 1, 31, 1, p, 1, torch.float32, 2490, bias=False)
+    assert b is None
+    try:
+        dc.dwconv2d_set_algo(0, *geo, dtype=torch.float32, algo="largek_roll_f32")
+        check_static(x, wt, b, dy, 1, p, 1, "largek-roll-f32 no bias", passes=("fwd",))
+    finally:
+        dc.dwconv2d_set_algo(0, *geo, dtype=torch.float32, algo=None)
 
 
 # k = 7 and 13 on the same streaming: four input rows (k = 7) or two (k = 13)
