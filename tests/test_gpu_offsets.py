@@ -58,7 +58,9 @@ STATIC = [
     (4, 40, 14, 14, 1, 3, 2, 1, 1, "f16"),        # small-plane channel groups, stride 2
     (1, 2, 40, 40, 1, 13, 1, 6, 1, "f32"),        # large-kernel register tiles
     (2, 2, 32, 32, 1, 31, 1, 15, 1, "f16"),       # large kernels on the matrix cores
-    (2, 2, 32, 36, 1, 31, 1, 15, 1, "f32"),       # 31 x 31 fp32 on the matrix cores
+    (2, 2, 32, 36, 1, 31, 1, 15, 1, "f32"),       # 31 x 31 fp32 on the matrix cores (input-row stream)
+    (2, 2, 40, 40, 1, 13, 1, 6, 1, "bf16"),       # 16-bit 13 x 13 input-row stream (and its grad-weight)
+    (2, 2, 33, 34, 1, 7, 1, 3, 1, "f16"),         # 16-bit 7 x 7 input-row stream
 ]
 
 
